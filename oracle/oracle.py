@@ -1,0 +1,176 @@
+"""ctypes front end of the float64 CPU oracle (``ssm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the product package.
+
+What the oracle computes is documented in ``ssm_oracle.c`` (the pages: the
+PaddleNLP Kernel operator-library guide, sections 4.1 selective_scan and 4.2
+causal_conv1d).  This module only marshals numpy arrays: io tensors are passed
+as their stored bits (float32 arrays, or uint16 arrays holding bf16 bits), and
+results come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ssm_oracle.c")
+LIB = os.path.join(HERE, "libssm_oracle.so")
+
+F32, BF16 = 0, 1
+BC_FIXED, BC_VARYING = 0, 1
+ACT_NONE, ACT_SILU = 0, 1
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def use_library(path: Optional[str]) -> None:
+    """Point this module at another build of the oracle source (None: the
+    default build).  Used only by the mutation test, which plants mistakes in
+    a copy of the source to show the pins catch them."""
+    global _lib, _lib_path
+    _lib, _lib_path = None, path
+
+
+_lib_path: Optional[str] = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _lib_path is None:
+            build()
+        lib = ctypes.CDLL(_lib_path or LIB)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_selective_scan.argtypes = [
+            i64, i64, i64, i64, i64, i32,
+            p, p, p, p, i32, p, i32, p, p, p, i32, p,
+            p, p, p, i32, i32,
+            p, i64, p, p, i32]
+        lib.oracle_selective_scan.restype = i32
+        lib.oracle_causal_conv1d.argtypes = [
+            i64, i64, i64, i32, i32, p, p, p, i32, p, i64, p, i32]
+        lib.oracle_causal_conv1d.restype = i32
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16.restype = ctypes.c_double
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _io(a: Optional[np.ndarray], dtype: int):
+    """Check an io tensor holds the stored bits of the stated dtype."""
+    if a is None:
+        return None
+    want = np.uint16 if dtype == BF16 else np.float32
+    if a.dtype != want:
+        raise TypeError(f"io tensor must be {want.__name__}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _f32(a: Optional[np.ndarray]):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def round_bf16(v: float) -> float:
+    return float(_load().oracle_round_bf16(float(v)))
+
+
+def softplus(v: float) -> float:
+    return float(_load().oracle_softplus(float(v)))
+
+
+def silu(v: float) -> float:
+    return float(_load().oracle_silu(float(v)))
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus=False, *, io_dtype=F32, ngroups=1,
+                   B_kind=BC_VARYING, C_kind=BC_VARYING, initial_state=None,
+                   conv_x=None, conv_weight=None, conv_bias=None, conv_act=ACT_SILU,
+                   rows=None, nthreads=0, shape=None):
+    """Oracle selective scan.
+
+    u, delta, z: (batch, dim, seqlen) io bits; A: (dim, dstate) float32;
+    B/C: (dim, dstate) when fixed, (batch, ngroups, dstate, seqlen) when varying;
+    D, delta_bias: (dim,) float32; initial_state: (batch, dim, dstate) float64.
+    With conv_weight given, u is ignored and computed from conv_x.
+    rows: optional int64 array of row ids b*dim + d.
+    Returns (out (nrows, seqlen) float64, last_state (nrows, dstate) float64).
+    """
+    lib = _load()
+    delta = _io(delta, io_dtype)
+    batch, dim, seqlen = shape if shape is not None else delta.shape
+    A = _f32(A)
+    dstate = A.shape[1]
+    u = _io(u, io_dtype)
+    B = _io(B, io_dtype)
+    C = _io(C, io_dtype)
+    z = _io(z, io_dtype)
+    conv_x = _io(conv_x, io_dtype)
+    D, delta_bias = _f32(D), _f32(delta_bias)
+    conv_weight, conv_bias = _f32(conv_weight), _f32(conv_bias)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = batch * dim if rows_a is None else rows_a.shape[0]
+    out = np.empty((nrows, seqlen), dtype=np.float64)
+    last = np.empty((nrows, dstate), dtype=np.float64)
+    width = 0 if conv_weight is None else conv_weight.shape[1]
+    rc = lib.oracle_selective_scan(
+        batch, dim, seqlen, dstate, ngroups, io_dtype,
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), B_kind, _ptr(C), C_kind,
+        _ptr(D), _ptr(delta_bias), _ptr(z), int(bool(delta_softplus)), _ptr(init),
+        _ptr(conv_x), _ptr(conv_weight), _ptr(conv_bias), width, conv_act,
+        _ptr(rows_a), nrows, _ptr(out), _ptr(last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan failed with status {rc}")
+    return out, last
+
+
+def causal_conv1d(x, weight, bias=None, act=ACT_NONE, *, io_dtype=F32, rows=None,
+                  nthreads=0):
+    """Oracle causal depthwise conv: x (batch, dim, seqlen) io bits, weight
+    (dim, width) float32, bias (dim,) float32.  Returns (nrows, seqlen) float64
+    (not rounded to the io dtype)."""
+    lib = _load()
+    x = _io(x, io_dtype)
+    batch, dim, seqlen = x.shape
+    weight, bias = _f32(weight), _f32(bias)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = batch * dim if rows_a is None else rows_a.shape[0]
+    out = np.empty((nrows, seqlen), dtype=np.float64)
+    rc = lib.oracle_causal_conv1d(batch, dim, seqlen, weight.shape[1], io_dtype,
+                                  _ptr(x), _ptr(weight), _ptr(bias), act,
+                                  _ptr(rows_a), nrows, _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_causal_conv1d failed with status {rc}")
+    return out

@@ -1,0 +1,267 @@
+/*
+ * ssm_oracle.c -- plain float64 CPU reference for the selective-scan forward
+ * operator and its width-W causal depthwise conv prologue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load it.  It shares no code, header or constant with the HIP
+ * kernels.
+ *
+ * Sources (the pages are the authority for what is computed):
+ *   - "PaddleNLP Kernel operator library: CUDA and Triton dual-implementation
+ *     guide", section 4.1 (selective_scan): the argument list of
+ *     selective_scan_fn, the shapes of u/delta (batch,dim,seqlen), A
+ *     (dim,dstate), B/C fixed (dim,dstate), time-varying (batch,dstate,seqlen)
+ *     or grouped (batch,groups,dstate,seqlen), D and delta_bias (dim,), z
+ *     (batch,dim,seqlen) multiplied into the output through silu(z), the
+ *     softplus flag on delta, and last_state (batch,dim,dstate).
+ *   - same page, section 4.2 (causal_conv1d): depthwise weight (dim,width),
+ *     optional bias (dim,), activation None / silu / swish.
+ *   - The recurrence itself is not printed on the pages.  The reading used is
+ *     the standard zero-order-hold discretisation named by the benchmark spec:
+ *       dA = exp(delta'*A),  x_t = dA*x_{t-1} + delta'*B_t*u_t,  x_{-1} = 0,
+ *       y_t = C_t . x_t,  out = (y + D*u) * silu(z).
+ *
+ * Readings of open points (each is listed with its reason in the design notes):
+ *   - delta' = softplus(delta + delta_bias): the bias is a bias of the step,
+ *     softplus is applied to the (biased) step.
+ *   - the D skip term is added before the gate.
+ *   - grouped B/C: channel d uses group d / (dim/groups) (contiguous blocks).
+ *     PARITY UNPINNED for this group-assignment convention; everything else
+ *     about grouping is pinned by invariants.
+ *   - conv orientation: cross-correlation with left zero padding, so
+ *     w[d][W-1] multiplies the current sample.  PARITY UNPINNED for the
+ *     orientation (symmetric kernels pin padding, bias and activation).
+ *   - "swish" is silu.
+ *
+ * Numbers: every input is read from its stored bits (fp32, or bf16 as the top
+ * 16 bits of an fp32) and widened to double; all arithmetic is double; results
+ * are double.  Rows are independent, so the optional thread split over rows
+ * gives bit-identical results for any thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <stdlib.h>
+#include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_BC_FIXED = 0, OR_BC_VARYING = 1 };
+enum { OR_ACT_NONE = 0, OR_ACT_SILU = 1 };
+
+/* ---- element access ---------------------------------------------------- */
+
+/* bf16 is the upper half of an IEEE binary32: widening is a 16-bit shift. */
+static double bf16_bits_to_double(uint16_t h) {
+    uint32_t w = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+static double load_io(const void *p, int dtype, int64_t i) {
+    if (dtype == OR_BF16) return bf16_bits_to_double(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+/* Round a double to the nearest bfloat16 value, ties to even, and return it
+ * as a double.  bfloat16: 8 significant bits, exponent range of binary32,
+ * subnormal spacing 2^-133, largest finite (2 - 2^-7) * 2^127. */
+double oracle_round_bf16(double v) {
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int e = ilogb(v);                 /* |v| in [2^e, 2^(e+1)) */
+    if (e < -126) e = -126;           /* subnormal range keeps the fixed spacing */
+    int q = e - 7;                    /* exponent of one unit in the last place */
+    double r = nearbyint(ldexp(v, -q));   /* default rounding mode: ties to even */
+    double out = ldexp(r, q);
+    const double maxf = ldexp(2.0 - ldexp(1.0, -7), 127);
+    if (fabs(out) > maxf) return copysign(INFINITY, v);
+    return out;
+}
+
+/* Round a double to the io dtype (fp32 cast rounds to nearest even). */
+static double round_io(double v, int dtype) {
+    if (dtype == OR_BF16) return oracle_round_bf16(v);
+    return (double)(float)v;
+}
+
+/* softplus(v) = log(1 + e^v), in the overflow-free form. */
+double oracle_softplus(double v) {
+    if (v > 0.0) return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v); "swish" with beta = 1. */
+double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* ---- causal depthwise conv ---------------------------------------------- */
+
+/* One channel row: out[t] = act(bias + sum_k w[k] * x[t - (W-1) + k]),
+ * x[t<0] = 0.  xrow/out are length l; the input is read through load_io. */
+static void conv_row(const void *x, int dtype, int64_t base, int64_t l,
+                     const float *w, int W, double bias, int act, double *out) {
+    for (int64_t t = 0; t < l; ++t) {
+        double acc = bias;
+        for (int k = 0; k < W; ++k) {
+            int64_t src = t - (W - 1) + k;
+            if (src >= 0) acc += (double)w[k] * load_io(x, dtype, base + src);
+        }
+        if (act == OR_ACT_SILU) acc = oracle_silu(acc);
+        out[t] = acc;
+    }
+}
+
+/* causal_conv1d forward over selected rows (row id = b*dim + d).
+ * rows == NULL means every row in order.  out is (nrows, l) double, not
+ * rounded to the io dtype (callers round when they model a stored result). */
+int oracle_causal_conv1d(int64_t batch, int64_t dim, int64_t seqlen, int width,
+                         int io_dtype, const void *x, const float *weight,
+                         const float *bias, int act,
+                         const int64_t *rows, int64_t nrows, double *out,
+                         int nthreads) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || width <= 0) return 2;
+    if (!x || !weight || !out) return 1;
+    int64_t total = rows ? nrows : batch * dim;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+    for (int64_t r = 0; r < total; ++r) {
+        int64_t row = rows ? rows[r] : r;
+        int64_t d = row % dim;
+        conv_row(x, io_dtype, row * seqlen, seqlen, weight + d * width, width,
+                 bias ? (double)bias[d] : 0.0, act, out + r * seqlen);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* ---- selective scan ------------------------------------------------------ */
+
+typedef struct {
+    int64_t batch, dim, seqlen, dstate, ngroups;
+    int io_dtype;
+    const void *u, *delta;
+    const float *A;
+    const void *B; int B_kind;
+    const void *C; int C_kind;
+    const float *D, *delta_bias;
+    const void *z;
+    int delta_softplus;
+    const double *initial_state;     /* (batch, dim, dstate) or NULL */
+    /* optional conv prologue: if conv_weight != NULL, u is replaced by
+     * round_io(act(conv(conv_x) + conv_bias)) */
+    const void *conv_x; const float *conv_weight, *conv_bias;
+    int conv_width, conv_act;
+} oracle_scan_args;
+
+/* B or C at (b, d, s, t) for the given layout kind. */
+static double bc_at(const void *p, int kind, int dtype, const oracle_scan_args *a,
+                    int64_t b, int64_t d, int64_t s, int64_t t) {
+    if (kind == OR_BC_FIXED) return load_io(p, dtype, d * a->dstate + s);
+    int64_t per_group = a->dim / a->ngroups;
+    int64_t g = d / per_group;
+    return load_io(p, dtype, ((b * a->ngroups + g) * a->dstate + s) * a->seqlen + t);
+}
+
+static void scan_row(const oracle_scan_args *a, int64_t row, double *out,
+                     double *last, double *x, double *urow) {
+    const int64_t l = a->seqlen, n = a->dstate;
+    const int64_t b = row / a->dim, d = row % a->dim;
+    const int64_t base = row * l;
+
+    if (a->conv_weight) {
+        conv_row(a->conv_x, a->io_dtype, base, l, a->conv_weight + d * a->conv_width,
+                 a->conv_width, a->conv_bias ? (double)a->conv_bias[d] : 0.0,
+                 a->conv_act, urow);
+        for (int64_t t = 0; t < l; ++t) urow[t] = round_io(urow[t], a->io_dtype);
+    } else {
+        for (int64_t t = 0; t < l; ++t) urow[t] = load_io(a->u, a->io_dtype, base + t);
+    }
+
+    for (int64_t s = 0; s < n; ++s)
+        x[s] = a->initial_state ? a->initial_state[row * n + s] : 0.0;
+
+    for (int64_t t = 0; t < l; ++t) {
+        double dt = load_io(a->delta, a->io_dtype, base + t);
+        if (a->delta_bias) dt += (double)a->delta_bias[d];
+        if (a->delta_softplus) dt = oracle_softplus(dt);
+        const double ut = urow[t];
+        double y = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            const double dA = exp(dt * (double)a->A[d * n + s]);
+            const double Bv = bc_at(a->B, a->B_kind, a->io_dtype, a, b, d, s, t);
+            x[s] = dA * x[s] + dt * Bv * ut;
+            y += bc_at(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s];
+        }
+        if (a->D) y += (double)a->D[d] * ut;
+        if (a->z) y *= oracle_silu(load_io(a->z, a->io_dtype, base + t));
+        out[t] = y;
+    }
+    if (last)
+        for (int64_t s = 0; s < n; ++s) last[s] = x[s];
+}
+
+/* Selective-scan forward over selected rows (row id = b*dim + d; NULL = all).
+ * out: (nrows, seqlen) double; last_state: (nrows, dstate) double or NULL.
+ * Returns 0, 1 (null required pointer), 2 (bad shape). */
+int oracle_selective_scan(int64_t batch, int64_t dim, int64_t seqlen,
+                          int64_t dstate, int64_t ngroups, int io_dtype,
+                          const void *u, const void *delta, const float *A,
+                          const void *B, int B_kind, const void *C, int C_kind,
+                          const float *D, const float *delta_bias, const void *z,
+                          int delta_softplus, const double *initial_state,
+                          const void *conv_x, const float *conv_weight,
+                          const float *conv_bias, int conv_width, int conv_act,
+                          const int64_t *rows, int64_t nrows,
+                          double *out, double *last_state, int nthreads) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!delta || !A || !B || !C || !out) return 1;
+    if (!conv_weight && !u) return 1;
+    if (conv_weight && (!conv_x || conv_width <= 0)) return 1;
+
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, D, delta_bias, z, delta_softplus,
+                          initial_state, conv_x, conv_weight, conv_bias, conv_width,
+                          conv_act};
+    const int64_t total = rows ? nrows : batch * dim;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(|:failed)
+#endif
+    {
+        double *x = (double *)malloc(sizeof(double) * (size_t)dstate);
+        double *urow = (double *)malloc(sizeof(double) * (size_t)seqlen);
+        if (!x || !urow) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t r = 0; r < total; ++r) {
+                const int64_t row = rows ? rows[r] : r;
+                scan_row(&a, row, out + r * seqlen,
+                         last_state ? last_state + r * dstate : NULL, x, urow);
+            }
+        }
+        free(x);
+        free(urow);
+    }
+    (void)nthreads;
+    return failed ? 5 : 0;
+}
+
+/* Number of threads an OpenMP region would use (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the selective-scan forward workloads.
+
+This module only draws random numbers and stores them in the io dtype; it holds
+none of the operator's arithmetic.  Both the oracle side and the HIP side get
+their inputs from here and nowhere else.
+
+Workloads (shapes and distributions follow the page's selective_scan_fn
+argument list: u/delta/z (batch, dim, seqlen), A (dim, dstate), B/C fixed
+(dim, dstate), time-varying (batch, dstate, seqlen) or grouped
+(batch, groups, dstate, seqlen), D/delta_bias (dim,)):
+
+  tiny        b=1  d=16   l=64    n=4   fp32  varying B/C (g=1)  seed 0
+  mamba130m   b=4  d=1536 l=2048  n=16  bf16  varying B/C (g=1)  seed 1
+  mamba2p8b   b=8  d=5120 l=2048  n=16  bf16  grouped B/C g=4    seed 2
+              A = -exp(N(0, 0.5))
+  longseq     b=1  d=2560 l=65536 n=16  fp32  varying B/C, no z,  seed 3
+              raw delta ~ N(-3, 0.5)
+  convfixed   b=16 d=2048 l=4096  n=16  bf16  fixed B/C (d, n), conv prologue
+              (width 4, weight ~ N(0, 0.5), bias ~ N(0, 1), silu), seed 4
+
+Unless a workload says otherwise: u (or the conv input x), z, B, C, D ~ N(0, 1);
+raw delta ~ N(-2, 0.5); delta_bias ~ U(-0.1, 0.1); softplus on;
+A[d, s] = -(s + 1); D, z, delta_bias present; last_state requested.
+N(mu, sigma) names the standard deviation.
+
+Draw order from ``numpy.random.default_rng(seed)``, all in float32:
+u (or x), delta, z, B, C, D, delta_bias, A-noise, conv weight, conv bias.
+Large tensors are drawn in fixed chunks of CHUNK values, in order.
+bf16 storage rounds the float32 draw to nearest, ties to even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Dict, Optional
+
+import numpy as np
+
+CHUNK = 1 << 24
+
+F32, BF16 = 0, 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    io_dtype: int             # F32 or BF16
+    bc_kind: str              # "varying" or "fixed"
+    ngroups: int = 1
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    softplus: bool = True
+    delta_mean: float = -2.0
+    delta_std: float = 0.5
+    A_mode: str = "s4d"        # "s4d": A = -(s+1);  "lognormal": A = -exp(N(0, 0.5))
+    conv: bool = False
+    seed: int = 0
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", 1, 16, 64, 4, F32, "varying", seed=0),
+    "mamba130m": Workload("mamba130m", 4, 1536, 2048, 16, BF16, "varying", seed=1),
+    "mamba2p8b": Workload("mamba2p8b", 8, 5120, 2048, 16, BF16, "varying", ngroups=4,
+                          A_mode="lognormal", seed=2),
+    "longseq": Workload("longseq", 1, 2560, 65536, 16, F32, "varying", has_z=False,
+                        delta_mean=-3.0, seed=3),
+    "convfixed": Workload("convfixed", 16, 2048, 4096, 16, BF16, "fixed", conv=True, seed=4),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, mean=0.0, std=1.0) -> np.ndarray:
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.float32)
+    for i in range(0, total, CHUNK):
+        j = min(total, i + CHUNK)
+        out[i:j] = rng.standard_normal(j - i, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    if mean != 0.0:
+        out += np.float32(mean)
+    return out.reshape(shape)
+
+
+def _uniform(rng: np.random.Generator, shape, lo, hi) -> np.ndarray:
+    return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def _store(a: np.ndarray, io_dtype: int) -> np.ndarray:
+    return f32_to_bf16_bits(a) if io_dtype == BF16 else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw every tensor of workload ``w``.
+
+    io tensors come back as their stored bits (uint16 for bf16, float32 for fp32);
+    parameters (A, D, delta_bias, conv weight/bias) are float32.  Absent optional
+    tensors are ``None``.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, d, l, n, g = w.batch, w.dim, w.seqlen, w.dstate, w.ngroups
+    io = w.io_dtype
+    t: Dict[str, Optional[np.ndarray]] = {}
+    first = _store(_normal(rng, (b, d, l)), io)
+    if w.conv:
+        t["conv_x"], t["u"] = first, None
+    else:
+        t["u"], t["conv_x"] = first, None
+    t["delta"] = _store(_normal(rng, (b, d, l), w.delta_mean, w.delta_std), io)
+    t["z"] = _store(_normal(rng, (b, d, l)), io) if w.has_z else None
+    bc_shape = (d, n) if w.bc_kind == "fixed" else (b, g, n, l)
+    t["B"] = _store(_normal(rng, bc_shape), io)
+    t["C"] = _store(_normal(rng, bc_shape), io)
+    t["D"] = _normal(rng, (d,)) if w.has_D else None
+    t["delta_bias"] = _uniform(rng, (d,), -0.1, 0.1) if w.has_bias else None
+    if w.A_mode == "lognormal":
+        t["A"] = (-np.exp(_normal(rng, (d, n), 0.0, 0.5).astype(np.float64))).astype(np.float32)
+    else:
+        t["A"] = np.ascontiguousarray(
+            np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (d, n)))
+    if w.conv:
+        t["conv_weight"] = _normal(rng, (d, 4), 0.0, 0.5)
+        t["conv_bias"] = _normal(rng, (d,))
+    else:
+        t["conv_weight"] = t["conv_bias"] = None
+    return t
+
+
+def sha256(a: Optional[np.ndarray]) -> Optional[str]:
+    if a is None:
+        return None
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:
+    """A fixed spread of row ids (b*dim + d) for spot checks at full size:
+    the first and last rows, group and block boundaries, plus random rows."""
+    total = w.batch * w.dim
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, 63, 64, 65, w.dim - 1, w.dim, total - 1, total - 64}
+    per_group = w.dim // w.ngroups
+    for gi in range(w.ngroups):
+        fixed.update({gi * per_group, gi * per_group + per_group - 1})
+    fixed = {r for r in fixed if 0 <= r < total}
+    extra = rng.choice(total, size=min(total, max(0, count - len(fixed))), replace=False)
+    return np.array(sorted(fixed.union(int(r) for r in extra)), dtype=np.int64)

@@ -1,0 +1,80 @@
+"""Mutation check of the oracle's pins.
+
+Each case plants one plausible mistake in a copy of the oracle source (on the
+CPU, in a temporary directory), builds it, and runs the pin suite against it:
+at least one pin must fail.  This shows the pins constrain every term of the
+recurrence, the epilogue, the layouts and the conv prologue.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle import oracle as orc
+import tests.test_oracle_pins as pins
+
+MUTANTS = {
+    "drop_delta_bias": ("if (a->delta_bias) dt += (double)a->delta_bias[d];", ""),
+    "softplus_sign": ("return v + log1p(exp(-v));", "return v + log1p(exp(v));"),
+    "decay_sign": ("exp(dt * (double)a->A[d * n + s])", "exp(-dt * (double)a->A[d * n + s])"),
+    "drop_dt_in_input": ("dt * Bv * ut", "Bv * ut"),
+    "C_reads_B": ("bc_at(a->C, a->C_kind", "bc_at(a->B, a->B_kind"),
+    "A_state_reversed": ("(double)a->A[d * n + s]", "(double)a->A[d * n + (n - 1 - s)]"),
+    "D_after_gate": ("if (a->D) y += (double)a->D[d] * ut;\n        if (a->z) y *= oracle_silu(load_io(a->z, a->io_dtype, base + t));",
+                     "if (a->z) y *= oracle_silu(load_io(a->z, a->io_dtype, base + t));\n        if (a->D) y += (double)a->D[d] * ut;"),
+    "group_interleaved": ("int64_t g = d / per_group;", "int64_t g = d % a->ngroups; (void)per_group;"),
+    "contract_old_state": ("x[s] = dA * x[s] + dt * Bv * ut;\n            y += bc_at(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s];",
+                           "y += bc_at(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s];\n            x[s] = dA * x[s] + dt * Bv * ut;"),
+    "fixed_BC_transposed": ("if (kind == OR_BC_FIXED) return load_io(p, dtype, d * a->dstate + s);",
+                            "if (kind == OR_BC_FIXED) return load_io(p, dtype, (s * a->dim + d) % (a->dim * a->dstate));"),
+    "time_index_shift": ("* a->seqlen + t);", "* a->seqlen + (t + 1) % a->seqlen);"),
+    "ignore_initial_state": ("a->initial_state ? a->initial_state[row * n + s] : 0.0", "0.0"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "conv_flipped": ("acc += (double)w[k] * load_io(x, dtype, base + src);",
+                     "acc += (double)w[W - 1 - k] * load_io(x, dtype, base + src);"),
+    "conv_pad_off_by_one": ("int64_t src = t - (W - 1) + k;", "int64_t src = t - W + k;"),
+    "conv_drop_bias": ("double acc = bias;", "double acc = 0.0; (void)bias;"),
+    "bf16_ties_away": ("double r = nearbyint(ldexp(v, -q));", "double r = round(ldexp(v, -q));"),
+    "bf16_truncate": ("double r = nearbyint(ldexp(v, -q));", "double r = trunc(ldexp(v, -q));"),
+    "last_state_stale": ("for (int64_t s = 0; s < n; ++s) last[s] = x[s];",
+                         "for (int64_t s = 0; s < n; ++s) last[s] = 0.5 * x[s];"),
+}
+
+
+def _pin_calls():
+    calls = []
+    for name in dir(pins):
+        fn = getattr(pins, name)
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        if name == "test_brute_force_tiny":
+            for fixed in (False, True):
+                for sp in (True, False):
+                    calls.append((f"{name}[{fixed},{sp}]", lambda f=fn, a=fixed, b=sp: f(a, b)))
+        else:
+            calls.append((name, fn))
+    return calls
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
