@@ -1,0 +1,228 @@
+"""Benchmark of the selective-scan forward (ssm_scan_fwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ssm_scan_fwd call over the whole workload (discretisation,
+recurrence, contraction, D skip, gate, last_state -- and the conv prologue for
+the workload that has one), with every input already resident in HBM.  W
+untimed steps, then K steps timed between two device synchronisations.  Prints
+one JSON line.
+
+Default workload: mamba2p8b (b=8, d=5120, l=2048, n=16, g=4, bf16 io, fp32
+state), the Mamba-2.8B-shaped layer the throughput target is quoted on.
+
+Roofline of the scan kernel (the only kernel of that workload):
+  * alu: algorithmic fp32 VALU operations per launch / measured launch time,
+    against 78.6 T lane-ops/s (256 CUs x 128 fp32 lanes x 2.4 GHz, i.e. the
+    157.3 TFLOP/s vector figure with an FMA counted once).  The method needs,
+    per (timestep, state), 4 plain ops (delta'*A, delta'u*B, state FMA, C.x FMA)
+    and one exp; per element 10 plain ops and 4 transcendentals (softplus:
+    exp, log; silu: exp, rcp).  A transcendental issues at a quarter of the
+    plain rate, so it is weighted 4: ops = E * (8 n + 26).
+  * hbm: algorithmic bytes (every input read once, every output written once)
+    / launch time, against 8 TB/s.
+The launch time is measured live with HIP events on the stream the kernel runs
+on.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE,
+scaled by the same counters on a copy of known size) is read from
+profiles/traffic_<workload>.json when that file was taken from the current
+kernel source, else null.
+
+cpu_baseline: the float64 oracle (test infrastructure) timed on this host's
+cores over a bounded sample of the workload's rows, scaled to elements/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "selective-scan fwd elements/s (b·d·l) and HBM GB/s as % of MI355X peak"
+HBM_PEAK_GBS = 8000.0
+ALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12       # 78.64 T fp32 lane-ops/s
+CSRC = os.path.join(ROOT, "state_space_model_scan_amd", "csrc")
+KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip", "ssm_scan.hip")
+
+
+def algorithmic_bytes(w) -> int:
+    """Every input read once, every output written once (the fused minimum for
+    the conv workload: the conv input replaces u, u never touches memory)."""
+    es = 2 if w.io_dtype == 1 else 4
+    E = w.elements
+    n = w.dstate
+    io_tensors = 2 + (1 if w.has_z else 0) + 1          # u or conv x, delta, z, out
+    total = io_tensors * E * es
+    bc = 2 * (w.dim * n if w.bc_kind == "fixed" else w.batch * w.ngroups * n * w.seqlen) * es
+    params = w.dim * n * 4 + (w.dim * 4 if w.has_D else 0) + (w.dim * 4 if w.has_bias else 0)
+    if w.conv:
+        params += w.dim * 4 * 4 + w.dim * 4
+    last = w.batch * w.dim * n * 4
+    return total + bc + params + last
+
+
+def algorithmic_alu_ops(w) -> float:
+    return float(w.elements) * (8 * w.dstate + 26)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic(name: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha256") != kernel_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(w, t, budget_s: float):
+    """Oracle throughput on a bounded sample of rows (all host threads)."""
+    from oracle import oracle as orc
+    from tests.harness import run_oracle
+    threads = orc.max_threads()
+    total_rows = w.batch * w.dim
+    rng = np.random.default_rng(0)
+    # calibrate on a few rows, then size the sample for ~budget_s of CPU work
+    probe = np.sort(rng.choice(total_rows, size=min(total_rows, max(threads, 16)), replace=False))
+    t0 = time.perf_counter()
+    run_oracle(w, t, rows=probe, nthreads=threads)
+    dt = time.perf_counter() - t0
+    per_row = dt / len(probe)
+    nrows = int(min(total_rows, max(len(probe), budget_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(total_rows, size=nrows, replace=False))
+    t0 = time.perf_counter()
+    run_oracle(w, t, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": nrows * w.seqlen / dt, "unit": "elements/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nrows} of {total_rows} (b,d) rows x full seqlen {w.seqlen}, "
+                      f"{dt:.1f} s float64 on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2p8b")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one 512 MiB device copy (for rocprofv3 counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the operator shards with no communication along batch and channels", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, WORKLOADS, make_inputs
+
+    def to_dev(a, io_dtype, param=False):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and io_dtype == BF16 and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16)
+        return x.cuda()
+
+    _lib.lib()  # fail loudly when the HIP library is missing
+    w = WORKLOADS[args.workload]
+    t = make_inputs(w)
+    io = w.io_dtype
+    dev = {k: (to_dev(v, io, param=k in ("A", "D", "delta_bias", "conv_weight", "conv_bias"))
+               if v is not None else None) for k, v in t.items()}
+    out = torch.empty_like(dev["delta"])
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+    conv = {}
+    if w.conv:
+        conv = dict(conv_x=dev["conv_x"], conv_weight=dev["conv_weight"], conv_bias=dev["conv_bias"])
+
+    def step():
+        binding.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                             dev["delta_bias"], w.softplus, out=out, last_state=last, **conv)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    elems = w.elements
+    value = elems * args.steps / wall
+
+    abytes = algorithmic_bytes(w)
+    aops = algorithmic_alu_ops(w)
+    alu_tops = aops / avg_launch_s / 1e12
+    hbm_gbs = abytes / avg_launch_s / 1e9
+    traffic = load_traffic(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} "
+                        f"B/C {w.bc_kind}, {'bf16' if io == BF16 else 'fp32'} io, fp32 state"
+                        f"{', conv prologue' if w.conv else ''}{', z gate' if w.has_z else ''}",
+            "io_dtype": "bf16" if io == BF16 else "fp32",
+            "elements_per_step": elems,
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": alu_tops,
+            "peak": ALU_PEAK_TOPS,
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)",
+            "frac": alu_tops / ALU_PEAK_TOPS,
+            "traffic": traffic,
+            "kernel_avg_ms": avg_launch_s * 1e3,
+            "hbm": {"achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": abytes},
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, t, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

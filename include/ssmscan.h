@@ -1,0 +1,151 @@
+/*
+ * ssmscan.h -- C ABI of libssmscan.so: the Mamba selective-scan forward
+ * operator and its width-4 causal depthwise conv prologue, for AMD MI355X
+ * (gfx950).
+ *
+ * Operation (PaddleNLP Kernel operator-library guide, section 4.1
+ * "selective_scan": selective_scan_fn(u, delta, A, B, C, D, z, delta_bias,
+ * delta_softplus, return_last_state)).  For every batch b, channel d and
+ * state s, with delta' = softplus(delta + delta_bias) when delta_softplus is
+ * set (otherwise delta + delta_bias):
+ *
+ *     x_t[s] = exp(delta'_t * A[d,s]) * x_{t-1}[s] + delta'_t * B_t[s] * u_t
+ *     y_t    = sum_s C_t[s] * x_t[s]
+ *     out_t  = (y_t + D[d] * u_t) * silu(z_t)          (D, z optional)
+ *     last_state[b,d,s] = x_{seqlen-1}[s]              (optional)
+ *
+ * with x_{-1} = initial_state (zero when not given).  The recurrence is not
+ * printed on the pages; it is the standard zero-order-hold discretisation.
+ *
+ * Shapes (same section): u, delta, z, out: (batch, dim, seqlen); A: (dim,
+ * dstate), real; B and C each either fixed (dim, dstate) or time-varying
+ * grouped (batch, ngroups, dstate, seqlen) -- the page's 3-D (batch, dstate,
+ * seqlen) form is ngroups = 1; D, delta_bias: (dim,); last_state and
+ * initial_state: (batch, dim, dstate).  Grouped channel d uses group
+ * d / (dim / ngroups).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers to dense row-major tensors (innermost
+ *    stride 1).  The caller owns and allocates every buffer, including the
+ *    outputs.  `out` must not alias an input.
+ *  - "io" tensors (u, delta, z, B, C, out, conv x) all have the dtype
+ *    io_dtype: SSM_F32 (IEEE binary32) or SSM_BF16 (bfloat16, stored as the
+ *    upper 16 bits of a binary32).  A, D, delta_bias, conv weight and bias,
+ *    initial_state and last_state are always binary32; the state is binary32.
+ *    bf16 outputs are rounded to nearest, ties to even.
+ *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *    the default stream).  Nothing synchronises.
+ *  - Errors: arguments are checked on the host before anything is enqueued.
+ *    Status 1-3 and 5 leave all memory untouched.  Status 4 means a HIP call
+ *    failed while enqueueing (ssm_last_hip_error() gives the hipError_t).
+ *  - The library keeps no state between calls except a cached device
+ *    property query; calls from several host threads are safe.
+ */
+#ifndef SSMSCAN_H
+#define SSMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
+#define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
+
+/* io dtype */
+enum { SSM_F32 = 0, SSM_BF16 = 1 };
+/* layout of B and C (one kind per tensor) */
+enum { SSM_BC_FIXED = 0,    /* (dim, dstate) */
+       SSM_BC_VARYING = 1   /* (batch, ngroups, dstate, seqlen) */ };
+/* conv activation ("swish" on the page is silu) */
+enum { SSM_ACT_NONE = 0, SSM_ACT_SILU = 1 };
+/* status codes */
+enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,         /* a required pointer is NULL */
+  SSM_ERR_SHAPE = 2,        /* a size <= 0, dim % ngroups != 0, or overflow */
+  SSM_ERR_UNSUPPORTED = 3,  /* dtype, dstate > 16, conv width != 4, bad enum */
+  SSM_ERR_HIP = 4,          /* a HIP runtime call failed */
+  SSM_ERR_WORKSPACE = 5     /* workspace given but smaller than required */
+};
+
+/* Arguments of ssm_scan_fwd.  Every pointer is a device pointer. */
+typedef struct ssm_scan_args {
+  int64_t batch, dim, seqlen, dstate, ngroups;  /* ngroups: 1 unless grouped */
+  int32_t io_dtype;                             /* SSM_F32 or SSM_BF16 */
+  const void *u;                                /* (b,d,l) io; ignored with conv */
+  const void *delta;                            /* (b,d,l) io, required */
+  const float *A;                               /* (d,n) fp32, required */
+  const void *B; int32_t B_kind;                /* io, SSM_BC_* */
+  const void *C; int32_t C_kind;                /* io, SSM_BC_* */
+  const float *D;                               /* (d) fp32 or NULL */
+  const float *delta_bias;                      /* (d) fp32 or NULL */
+  const void *z;                                /* (b,d,l) io or NULL */
+  int32_t delta_softplus;                       /* 0 or 1 */
+  void *out;                                    /* (b,d,l) io, required */
+  float *last_state;                            /* (b,d,n) fp32 or NULL */
+  const float *initial_state;                   /* (b,d,n) fp32 or NULL (zero) */
+  /* Optional fused conv prologue (same page, section 4.2 causal_conv1d):
+   * when conv_weight != NULL, u is not read and is replaced by
+   *   u = round_io(act(conv_bias[d] + sum_k conv_weight[d,k] * conv_x[b,d,t-3+k]))
+   * with conv_x[t<0] = 0 -- exactly what causal_conv1d_fwd stores. */
+  const void *conv_x;                           /* (b,d,l) io */
+  const float *conv_weight;                     /* (d, conv_width) fp32 */
+  const float *conv_bias;                       /* (d) fp32 or NULL */
+  int32_t conv_width;                           /* must be 4 */
+  int32_t conv_act;                             /* SSM_ACT_* */
+  /* Scratch for the sequence-split plan (see ssm_scan_workspace_size).  When
+   * NULL and scratch is needed, the library takes it from the stream-ordered
+   * allocator (hipMallocAsync/hipFreeAsync on hip_stream). */
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_scan_args_t;
+
+/* Selective-scan forward.  Enqueues the scan on hip_stream and returns a
+ * status code (SSM_OK on success). */
+int ssm_scan_fwd(const ssm_scan_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssm_scan_fwd: the same status the call would
+ * return before enqueueing anything.  Touches no device memory and makes no
+ * HIP call, so it is usable on a machine without a GPU. */
+int ssm_scan_validate(const ssm_scan_args_t *args);
+
+/* Scratch bytes ssm_scan_fwd needs for these arguments (0 when the plan keeps
+ * the whole sequence in one pass).  Host-only, no HIP call except a cached
+ * query of the device's compute-unit count. */
+int ssm_scan_workspace_size(const ssm_scan_args_t *args, size_t *bytes);
+
+/* Causal depthwise conv forward (PaddleNLP Kernel operator-library guide,
+ * section 4.2 "causal_conv1d": causal_conv1d_fn(x, weight, bias, ...,
+ * activation)).  x, out: (batch, dim, seqlen) io, device pointers; weight:
+ * (dim, width) fp32; bias: (dim) fp32 or NULL; act: SSM_ACT_NONE or
+ * SSM_ACT_SILU.
+ *   out[b,d,t] = round_io(act(bias[d] + sum_k weight[d,k] * x[b,d,t-(width-1)+k]))
+ * with x[t<0] = 0 (cross-correlation with left zero padding).  width must be
+ * 4.  Asynchronous on hip_stream; returns a status code. */
+int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, void *out,
+                      int64_t batch, int64_t dim, int64_t seqlen, int32_t width,
+                      int32_t io_dtype, int32_t act, void *hip_stream);
+
+/* Host-only argument check of causal_conv1d_fwd (no HIP call). */
+int causal_conv1d_validate(const void *x, const float *weight, const void *out,
+                           int64_t batch, int64_t dim, int64_t seqlen, int32_t width,
+                           int32_t io_dtype, int32_t act);
+
+/* Static text for a status code. */
+const char *ssm_status_str(int status);
+
+/* The hipError_t of the last SSM_ERR_HIP returned on this thread (0 if none). */
+int ssm_last_hip_error(void);
+
+/* SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMSCAN_H */

@@ -1,0 +1,64 @@
+"""Builds libssmscan.so in-tree with hipcc for gfx950 (MI355X).
+
+Every HIP source is compiled with the packed-FP32 feature switched off
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``): hipcc then emits only
+scalar fp32 VALU instructions.  hipcc's host pass warns that it does not know
+the feature; that warning is harmless.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libssmscan.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", "-Wall"]
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fno-gpu-rdc"]
+
+SOURCES = [
+    ("scan_bf16.hip", True),
+    ("scan_f32.hip", True),
+    ("ssm_scan.hip", True),
+    ("validate.cpp", False),
+]
+
+
+def _compile(src: str, is_hip: bool) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + (HIP_FLAGS if is_hip else ["-x", "c++"]) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libssmscan.so (always rebuilds)."""
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("linking libssmscan.so failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

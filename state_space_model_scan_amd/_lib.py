@@ -1,0 +1,91 @@
+"""ctypes view of libssmscan.so (include/ssmscan.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_BC_FIXED, SSM_BC_VARYING = 0, 1
+SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
+SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_WORKSPACE = range(6)
+SSM_MAX_DSTATE = 16
+SSM_CONV_WIDTH = 4
+
+# Every symbol include/ssmscan.h declares.
+EXPORTS = (
+    "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size",
+    "causal_conv1d_fwd", "causal_conv1d_validate",
+    "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
+)
+
+_vp = ctypes.c_void_p
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ssm_scan_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("u", _vp), ("delta", _vp), ("A", _vp),
+        ("B", _vp), ("B_kind", ctypes.c_int32),
+        ("C", _vp), ("C_kind", ctypes.c_int32),
+        ("D", _vp), ("delta_bias", _vp), ("z", _vp),
+        ("delta_softplus", ctypes.c_int32),
+        ("out", _vp), ("last_state", _vp), ("initial_state", _vp),
+        ("conv_x", _vp), ("conv_weight", _vp), ("conv_bias", _vp),
+        ("conv_width", ctypes.c_int32), ("conv_act", ctypes.c_int32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SsmError(ValueError):
+    """A non-zero status from libssmscan."""
+
+    def __init__(self, status: int, text: str):
+        super().__init__(f"libssmscan status {status}: {text}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssmscan.so; raises with a clear message when it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python -m state_space_model_scan_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_validate.argtypes = [ctypes.POINTER(ScanArgs)]
+        L.ssm_scan_validate.restype = ctypes.c_int
+        L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_scan_workspace_size.restype = ctypes.c_int
+        L.causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, i64, i64, i64, i32, i32, i32, _vp]
+        L.causal_conv1d_fwd.restype = ctypes.c_int
+        L.causal_conv1d_validate.argtypes = [_vp, _vp, _vp, i64, i64, i64, i32, i32, i32]
+        L.causal_conv1d_validate.restype = ctypes.c_int
+        L.ssm_status_str.argtypes = [ctypes.c_int]
+        L.ssm_status_str.restype = ctypes.c_char_p
+        L.ssm_last_hip_error.argtypes = []
+        L.ssm_last_hip_error.restype = ctypes.c_int
+        L.ssm_abi_version.argtypes = []
+        L.ssm_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != SSM_OK:
+        text = lib().ssm_status_str(status).decode()
+        if status == SSM_ERR_HIP:
+            text += f" (hipError_t {lib().ssm_last_hip_error()})"
+        raise SsmError(status, text)

@@ -1,0 +1,182 @@
+"""Python binding of libssmscan.so.  Argument marshalling only: every step of
+the operator runs in the HIP kernels behind the C ABI; torch provides device
+memory and the current stream.
+
+``ssm_scan_fwd`` / ``causal_conv1d_fwd`` mirror the C entry points.
+``selective_scan_fn`` / ``causal_conv1d_fn`` keep the signatures the page
+gives (PaddleNLP Kernel operator-library guide, sections 4.1 and 4.2),
+forward only: tensors whose last stride is not 1 are made contiguous, a 3-D
+B/C (batch, dstate, seqlen) is the grouped form with one group, and an
+activation other than None / "silu" / "swish" raises NotImplementedError.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import _lib
+from ._lib import ScanArgs, check
+
+_IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dense(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _stream(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bc_kind(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    """(kind, ngroups) of a B or C tensor from its rank."""
+    if t.dim() == 2:
+        return _lib.SSM_BC_FIXED, 0
+    if t.dim() == 3:
+        return _lib.SSM_BC_VARYING, 1
+    if t.dim() == 4:
+        return _lib.SSM_BC_VARYING, t.shape[1]
+    raise ValueError(f"{name} must be (dim, dstate), (batch, dstate, seqlen) or "
+                     f"(batch, groups, dstate, seqlen); got shape {tuple(t.shape)}")
+
+
+def _act_code(activation) -> int:
+    if activation is None:
+        return _lib.SSM_ACT_NONE
+    if activation in ("silu", "swish"):
+        return _lib.SSM_ACT_SILU
+    raise NotImplementedError("activation must be None, silu, or swish")
+
+
+def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
+                 B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                 delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                 last_state: Optional[torch.Tensor] = None,
+                 initial_state: Optional[torch.Tensor] = None,
+                 conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
+                 conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Enqueue ssm_scan_fwd on the current stream; returns ``out``.
+
+    Shapes as in include/ssmscan.h.  ``out`` (same dtype as delta) and
+    ``last_state`` (float32, optional) are written in place; ``out`` is
+    allocated when not given.  With ``conv_weight`` the conv prologue computes
+    u from ``conv_x`` and ``u`` may be None.
+    """
+    delta = _dense(delta)
+    io = _IO.get(delta.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32 or bfloat16, got {delta.dtype}")
+    batch, dim, seqlen = delta.shape
+    dstate = A.shape[1]
+    B, C = _dense(B), _dense(C)
+    bk, bg = _bc_kind(B, "B")
+    ck, cg = _bc_kind(C, "C")
+    if bk == _lib.SSM_BC_VARYING and ck == _lib.SSM_BC_VARYING and bg != cg:
+        raise ValueError("B and C must have the same number of groups")
+    ngroups = max(bg, cg, 1)
+    for name, t in (("u", u), ("z", z), ("B", B), ("C", C), ("conv_x", conv_x)):
+        if t is not None and t.dtype != delta.dtype:
+            raise ValueError(f"{name} must have the io dtype {delta.dtype}, got {t.dtype}")
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("initial_state", initial_state),
+                    ("conv_weight", conv_weight), ("conv_bias", conv_bias)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if out is None:
+        out = torch.empty_like(delta)
+    args = ScanArgs()
+    args.batch, args.dim, args.seqlen, args.dstate, args.ngroups = batch, dim, seqlen, dstate, ngroups
+    args.io_dtype = io
+    u, A, D, z, delta_bias = _dense(u), _dense(A), _dense(D), _dense(z), _dense(delta_bias)
+    initial_state, conv_x = _dense(initial_state), _dense(conv_x)
+    conv_weight, conv_bias = _dense(conv_weight), _dense(conv_bias)
+    args.u, args.delta, args.A = _ptr(u), _ptr(delta), _ptr(A)
+    args.B, args.B_kind, args.C, args.C_kind = _ptr(B), bk, _ptr(C), ck
+    args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
+    args.delta_softplus = int(bool(delta_softplus))
+    args.out, args.last_state, args.initial_state = _ptr(out), _ptr(last_state), _ptr(initial_state)
+    args.conv_x, args.conv_weight, args.conv_bias = _ptr(conv_x), _ptr(conv_weight), _ptr(conv_bias)
+    args.conv_width = 0 if conv_weight is None else conv_weight.shape[1]
+    args.conv_act = conv_act
+    L = _lib.lib()
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        check(L.ssm_scan_workspace_size(ctypes.byref(args), ctypes.byref(need)))
+        if need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=delta.device)
+    if workspace is not None:
+        args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    check(L.ssm_scan_fwd(ctypes.byref(args), _stream(delta.device, stream)))
+    return out
+
+
+def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, act: int = _lib.SSM_ACT_NONE,
+                      stream=None) -> torch.Tensor:
+    """Enqueue causal_conv1d_fwd on the current stream; returns ``out``."""
+    x = _dense(x)
+    io = _IO.get(x.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+    weight, bias = _dense(weight), _dense(bias)
+    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("conv weight and bias must be float32")
+    if out is None:
+        out = torch.empty_like(x)
+    batch, dim, seqlen = x.shape
+    check(_lib.lib().causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out),
+                                       batch, dim, seqlen, weight.shape[1], io, act,
+                                       _stream(x.device, stream)))
+    return out
+
+
+def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                      delta_softplus=False, return_last_state=False
+                      ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """Forward of selective_scan_fn with the page's signature and returns."""
+    if B.dim() == 3:
+        B = B.unsqueeze(1)
+    if C.dim() == 3:
+        C = C.unsqueeze(1)
+    last = None
+    if return_last_state:
+        last = torch.empty((delta.shape[0], delta.shape[1], A.shape[1]), dtype=torch.float32,
+                           device=delta.device)
+    out = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, last_state=last)
+    return (out, last) if return_last_state else out
+
+
+def causal_conv1d_fn(x, weight, bias=None, activation=None) -> torch.Tensor:
+    """Forward of causal_conv1d_fn (x, weight, bias, activation)."""
+    return causal_conv1d_fwd(x, weight, bias, act=_act_code(activation))
+
+
+def conv1d_selective_scan_fn(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,
+                             delta_bias=None, delta_softplus=False, return_last_state=False,
+                             activation="silu"):
+    """causal_conv1d_fn followed by selective_scan_fn, fused into one pass:
+    u = causal_conv1d_fn(x, conv_weight, conv_bias, activation) is computed in
+    registers (rounded to the io dtype exactly as the stored conv output) and
+    never written to memory."""
+    if B.dim() == 3:
+        B = B.unsqueeze(1)
+    if C.dim() == 3:
+        C = C.unsqueeze(1)
+    last = None
+    if return_last_state:
+        last = torch.empty((delta.shape[0], delta.shape[1], A.shape[1]), dtype=torch.float32,
+                           device=delta.device)
+    out = ssm_scan_fwd(None, delta, A, B, C, D, z, delta_bias, delta_softplus, last_state=last,
+                       conv_x=x, conv_weight=conv_weight, conv_bias=conv_bias,
+                       conv_act=_act_code(activation))
+    return (out, last) if return_last_state else out

@@ -1,0 +1,237 @@
+// ssm_scan.hip -- host side of libssmscan.so: planning, dispatch and the
+// C-ABI entry points, plus the standalone causal depthwise conv kernel.
+//
+// Operation: PaddleNLP Kernel operator-library guide, section 4.1
+// (selective_scan_fn) and section 4.2 (causal_conv1d_fn); see
+// include/ssmscan.h.  The scan kernel itself is in scan_kernel.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "scan_kernel.h"
+#include "ssmscan.h"
+
+using namespace ssm;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// standalone causal depthwise conv: one thread per 8 consecutive outputs
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
+            int64_t rows, int64_t dim, int64_t seqlen, int silu, int vec) {
+  const int64_t nt8 = (seqlen + 7) / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * nt8) return;
+  const int64_t row = idx / nt8;
+  const int64_t t0 = (idx - row * nt8) * 8;
+  const int64_t d = row % dim;
+  const int64_t rb = row * seqlen;
+  const int cnt = static_cast<int>((seqlen - t0 < 8) ? seqlen - t0 : 8);
+  Raw8<BF16> cur, prev;
+  cur.load(x, rb + t0, cnt, vec != 0);
+  if (t0 >= 8 && vec) prev.load_vec(x, rb + t0 - 8);
+  else prev.load_elems(x, rb + t0 - 8, t0 >= 8 ? 8 : 0);
+  const float w0 = wgt[d * 4 + 0], w1 = wgt[d * 4 + 1], w2 = wgt[d * 4 + 2], w3 = wgt[d * 4 + 3];
+  const float bb = bias ? bias[d] : 0.0f;
+  float xv[11];
+  xv[0] = prev.get(5); xv[1] = prev.get(6); xv[2] = prev.get(7);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i + 3] = cur.get(i);
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float acc = bb;
+    acc = fmaf(w0, xv[i], acc);
+    acc = fmaf(w1, xv[i + 1], acc);
+    acc = fmaf(w2, xv[i + 2], acc);
+    acc = fmaf(w3, xv[i + 3], acc);
+    if (silu) acc = silu_f(acc);
+    o[i] = acc;
+  }
+  store8<BF16>(out, rb + t0, o, cnt, vec != 0);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return SSM_ERR_HIP;
+}
+
+int cu_count_cached() {
+  static std::mutex mu;
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (counts[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    counts[dev] = v;
+  }
+  return counts[dev];
+}
+
+struct Plan {
+  int n_pad, nsw, lpc, T;
+  int groups_eff, nblk, nblocks, nseg;
+  int64_t cpg, seg_len;
+  size_t ws_bytes;
+};
+
+int pow2ceil(int v) {
+  int r = 1;
+  while (r < v) r <<= 1;
+  return r;
+}
+
+// A channel's states are spread over lpc lanes of nsw states each (four
+// lanes of four at dstate 16): enough waves to fill the GPU at the Mamba
+// shapes, and each lane still runs several independent state chains.
+Plan make_plan(const ssm_scan_args_t *a, int cus) {
+  Plan pl{};
+  pl.n_pad = pow2ceil(static_cast<int>(a->dstate));
+  switch (pl.n_pad) {
+    case 16: pl.nsw = 4; pl.lpc = 4; break;
+    case 8: pl.nsw = 4; pl.lpc = 2; break;
+    case 4: pl.nsw = 4; pl.lpc = 1; break;
+    case 2: pl.nsw = 2; pl.lpc = 1; break;
+    default: pl.nsw = 1; pl.lpc = 1; break;
+  }
+  pl.T = chunk_of(pl.lpc);
+  const bool any_varying = a->B_kind == SSM_BC_VARYING || a->C_kind == SSM_BC_VARYING;
+  pl.groups_eff = any_varying ? static_cast<int>(a->ngroups) : 1;
+  pl.cpg = a->dim / pl.groups_eff;
+  const int cpb = channels_per_block(pl.lpc);
+  pl.nblk = static_cast<int>((pl.cpg + cpb - 1) / cpb);
+  pl.nblocks = static_cast<int>(a->batch * pl.groups_eff * pl.nblk);
+  const int64_t waves = static_cast<int64_t>(pl.nblocks) * kWavesPerBlock;
+  const int64_t target = 8LL * cus;     // two waves per SIMD
+  int nseg = 1;
+  if (waves < target) {
+    const int64_t want = (3 * target + 2 * waves - 1) / (2 * waves);
+    const int64_t cap = a->seqlen / (4 * pl.T);
+    nseg = static_cast<int>(want < cap ? want : cap);
+    if (nseg < 1) nseg = 1;
+  }
+  if (const char *env = std::getenv("SSMSCAN_NSEG")) {
+    const int v = std::atoi(env);
+    if (v >= 1) nseg = v;
+  }
+  int64_t seg_len = (a->seqlen + nseg - 1) / nseg;
+  seg_len = (seg_len + pl.T - 1) / pl.T * pl.T;
+  pl.seg_len = seg_len;
+  pl.nseg = static_cast<int>((a->seqlen + seg_len - 1) / seg_len);
+  pl.ws_bytes = pl.nseg > 1
+                    ? static_cast<size_t>(pl.nseg - 1) * (pl.n_pad + 1) * a->batch * a->dim * sizeof(float)
+                    : 0;
+  return pl;
+}
+
+ScanFn pick(bool bf16, int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
+  return bf16 ? pick_scan_bf16(nsw, lpc, bv, cv, conv, mode) : pick_scan_f32(nsw, lpc, bv, cv, conv, mode);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int ssm_scan_workspace_size(const ssm_scan_args_t *a, size_t *bytes) {
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  if (!bytes) return SSM_ERR_NULL;
+  *bytes = make_plan(a, cu_count_cached()).ws_bytes;
+  return SSM_OK;
+}
+
+extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  const Plan pl = make_plan(a, cu_count_cached());
+  if (a->workspace && a->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+  const bool bf16 = a->io_dtype == SSM_BF16;
+  const bool conv = a->conv_weight != nullptr;
+  ScanParams p{};
+  p.u = a->u; p.delta = a->delta; p.B = a->B; p.C = a->C; p.z = a->z;
+  p.cx = a->conv_x; p.A = a->A; p.D = a->D; p.dbias = a->delta_bias;
+  p.init = a->initial_state; p.cw = a->conv_weight; p.cb = a->conv_bias;
+  p.out = a->out; p.last = a->last_state;
+  p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
+  p.seg_len = pl.seg_len; p.cpg = pl.cpg;
+  p.n = static_cast<int>(a->dstate); p.n_pad = pl.n_pad; p.ngroups = static_cast<int>(a->ngroups);
+  p.groups_eff = pl.groups_eff; p.nblk = pl.nblk; p.nseg = pl.nseg; p.nblocks = pl.nblocks;
+  p.softplus = a->delta_softplus; p.conv_silu = a->conv_act == SSM_ACT_SILU;
+  p.vec = (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
+          (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z));
+  p.xcd_swizzle = (pl.nblocks % 8 == 0);
+
+  void *ws = a->workspace;
+  bool owned = false;
+  if (pl.ws_bytes > 0 && !ws) {
+    const hipError_t e = hipMallocAsync(&ws, pl.ws_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    owned = true;
+  }
+  if (pl.nseg > 1) {
+    float *wsf = static_cast<float *>(ws);
+    p.ws_state = wsf;
+    p.ws_sumdt = wsf + static_cast<size_t>(pl.nseg - 1) * pl.n_pad * a->batch * a->dim;
+  }
+  const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
+  int rc = SSM_OK;
+  const ScanFn f_state = pl.nseg > 1 ? pick(bf16, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE) : nullptr;
+  const ScanFn f_full = pick(bf16, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL);
+  if (!f_full || (pl.nseg > 1 && !f_state)) rc = SSM_ERR_UNSUPPORTED;
+  if (rc == SSM_OK && pl.nseg > 1) {
+    hipLaunchKernelGGL(f_state, dim3(pl.nblocks, pl.nseg - 1), dim3(64 * kWavesPerBlock), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e);
+  }
+  if (rc == SSM_OK) {
+    hipLaunchKernelGGL(f_full, dim3(pl.nblocks, pl.nseg), dim3(64 * kWavesPerBlock), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e);
+  }
+  if (owned) {
+    const hipError_t e = hipFreeAsync(ws, stream);
+    if (e != hipSuccess && rc == SSM_OK) rc = hip_fail(e);
+  }
+  return rc;
+}
+
+extern "C" int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, void *out,
+                                 int64_t batch, int64_t dim, int64_t seqlen, int32_t width,
+                                 int32_t io_dtype, int32_t act, void *stream_ptr) {
+  const int st = causal_conv1d_validate(x, weight, out, batch, dim, seqlen, width, io_dtype, act);
+  if (st != SSM_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int64_t rows = batch * dim;
+  const int64_t threads = rows * ((seqlen + 7) / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  const int vec = (seqlen % 8 == 0) && aligned16(x) && aligned16(out);
+  const int silu = act == SSM_ACT_SILU;
+  if (io_dtype == SSM_BF16)
+    hipLaunchKernelGGL(conv_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       x, weight, bias, out, rows, dim, seqlen, silu, vec);
+  else
+    hipLaunchKernelGGL(conv_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       x, weight, bias, out, rows, dim, seqlen, silu, vec);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+extern "C" int ssm_last_hip_error(void) { return g_last_hip_error; }

@@ -1,0 +1,78 @@
+// Host-side argument checks of the C ABI.  Plain C++: no HIP header, no device
+// access, so every error path can be exercised on a machine without a GPU.
+//
+// What is checked follows the argument list of selective_scan_fn and
+// causal_conv1d_fn (PaddleNLP Kernel operator-library guide, sections 4.1 and
+// 4.2): required tensors present, positive sizes, dim divisible by the number
+// of B/C groups, one of the supported io dtypes, dstate within the compiled
+// range, and the conv width and activation the kernels are built for.
+#include "ssmscan.h"
+
+#include <cstdint>
+#include <limits>
+
+namespace {
+
+bool positive(int64_t v) { return v > 0; }
+
+// b*d*l (and friends) must fit comfortably in int64 element counts.
+bool product_fits(int64_t a, int64_t b, int64_t c) {
+  const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
+  if (a > lim / b) return false;
+  const int64_t ab = a * b;
+  return ab <= lim / c;
+}
+
+}  // namespace
+
+extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  if (!positive(a->batch) || !positive(a->dim) || !positive(a->seqlen) ||
+      !positive(a->dstate) || !positive(a->ngroups))
+    return SSM_ERR_SHAPE;
+  if (a->dim % a->ngroups != 0) return SSM_ERR_SHAPE;
+  if (!product_fits(a->batch, a->dim, a->seqlen) ||
+      !product_fits(a->batch, a->ngroups * a->dstate, a->seqlen))
+    return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  if ((a->B_kind != SSM_BC_FIXED && a->B_kind != SSM_BC_VARYING) ||
+      (a->C_kind != SSM_BC_FIXED && a->C_kind != SSM_BC_VARYING))
+    return SSM_ERR_UNSUPPORTED;
+  if (a->delta_softplus != 0 && a->delta_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (!a->delta || !a->A || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
+  if (a->conv_weight) {
+    if (!a->conv_x) return SSM_ERR_NULL;
+    if (a->conv_width != SSM_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
+    if (a->conv_act != SSM_ACT_NONE && a->conv_act != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  } else if (!a->u) {
+    return SSM_ERR_NULL;
+  }
+  return SSM_OK;
+}
+
+extern "C" int causal_conv1d_validate(const void *x, const float *weight, const void *out,
+                                      int64_t batch, int64_t dim, int64_t seqlen,
+                                      int32_t width, int32_t io_dtype, int32_t act) {
+  if (!positive(batch) || !positive(dim) || !positive(seqlen)) return SSM_ERR_SHAPE;
+  if (!product_fits(batch, dim, seqlen)) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (width != SSM_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
+  if (act != SSM_ACT_NONE && act != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!x || !weight || !out) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
+extern "C" const char *ssm_status_str(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "bad shape (size <= 0, dim not divisible by ngroups, or too large)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported argument (dtype, dstate > 16, conv width != 4, or enum value)";
+    case SSM_ERR_HIP: return "HIP runtime error";
+    case SSM_ERR_WORKSPACE: return "workspace smaller than required";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int ssm_abi_version(void) { return SSM_ABI_VERSION; }

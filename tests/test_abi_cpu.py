@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ssmscan.h declares, and rejects bad arguments on the host (status
+codes 1-3) before any HIP call.  No compute entry point is called with valid
+arguments here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_model_scan_amd import _lib
+from state_space_model_scan_amd._lib import ScanArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssmscan.h")
+
+FAKE = 0x1000  # a non-null pointer value; validation never dereferences it
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = _lib.lib()
+    funcs = _header_functions()
+    assert set(funcs) == set(_lib.EXPORTS), funcs
+    for name in funcs:
+        assert hasattr(L, name), f"{name} not exported"
+    assert L.ssm_abi_version() == 1
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in range(6):
+        assert L.ssm_status_str(code)
+    assert L.ssm_status_str(99) == b"unknown status"
+
+
+def _good_args(**kw):
+    a = ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate, a.ngroups = 2, 64, 128, 16, 1
+    a.io_dtype = _lib.SSM_BF16
+    a.u = a.delta = a.A = a.B = a.C = a.out = FAKE
+    a.B_kind = a.C_kind = _lib.SSM_BC_VARYING
+    a.delta_softplus = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _validate(a):
+    return _lib.lib().ssm_scan_validate(ctypes.byref(a))
+
+
+def test_valid_arguments_pass():
+    assert _validate(_good_args()) == _lib.SSM_OK
+    assert _validate(_good_args(u=None, conv_x=FAKE, conv_weight=FAKE, conv_width=4,
+                                conv_act=_lib.SSM_ACT_SILU)) == _lib.SSM_OK
+    assert _validate(_good_args(ngroups=4, dim=256)) == _lib.SSM_OK
+    assert _validate(_good_args(dstate=1)) == _lib.SSM_OK
+
+
+@pytest.mark.parametrize("field", ["delta", "A", "B", "C", "out", "u"])
+def test_null_required_pointer(field):
+    assert _validate(_good_args(**{field: None})) == _lib.SSM_ERR_NULL
+
+
+def test_null_conv_input():
+    a = _good_args(u=None, conv_weight=FAKE, conv_width=4)
+    assert _validate(a) == _lib.SSM_ERR_NULL
+
+
+@pytest.mark.parametrize("field,val", [("batch", 0), ("dim", -1), ("seqlen", 0), ("dstate", 0),
+                                       ("ngroups", 0), ("ngroups", 3)])
+def test_bad_shapes(field, val):
+    assert _validate(_good_args(**{field: val})) == _lib.SSM_ERR_SHAPE
+
+
+def test_overflowing_sizes():
+    assert _validate(_good_args(batch=1 << 40, dim=1 << 20, seqlen=1 << 20)) == _lib.SSM_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(io_dtype=2), dict(dstate=17), dict(B_kind=2), dict(C_kind=-1),
+                                dict(delta_softplus=2),
+                                dict(conv_weight=FAKE, conv_x=FAKE, conv_width=3),
+                                dict(conv_weight=FAKE, conv_x=FAKE, conv_width=4, conv_act=7)])
+def test_unsupported(kw):
+    assert _validate(_good_args(**kw)) == _lib.SSM_ERR_UNSUPPORTED
+
+
+def test_fwd_rejects_before_any_hip_call():
+    """Invalid arguments return their status from ssm_scan_fwd itself, without
+    touching HIP (this runs on a machine with no GPU)."""
+    L = _lib.lib()
+    assert L.ssm_scan_fwd(ctypes.byref(_good_args(delta=None)), None) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_fwd(ctypes.byref(_good_args(dstate=33)), None) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssm_scan_fwd(None, None) == _lib.SSM_ERR_NULL
+    size = ctypes.c_size_t(0)
+    assert L.ssm_scan_workspace_size(ctypes.byref(_good_args(seqlen=0)), ctypes.byref(size)) == _lib.SSM_ERR_SHAPE
+
+
+def test_conv_validation():
+    L = _lib.lib()
+    v = L.causal_conv1d_validate
+    assert v(FAKE, FAKE, FAKE, 2, 8, 16, 4, _lib.SSM_F32, _lib.SSM_ACT_SILU) == _lib.SSM_OK
+    assert v(None, FAKE, FAKE, 2, 8, 16, 4, _lib.SSM_F32, 0) == _lib.SSM_ERR_NULL
+    assert v(FAKE, FAKE, FAKE, 0, 8, 16, 4, _lib.SSM_F32, 0) == _lib.SSM_ERR_SHAPE
+    assert v(FAKE, FAKE, FAKE, 2, 8, 16, 5, _lib.SSM_F32, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, 2, 8, 16, 4, 9, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, 2, 8, 16, 4, _lib.SSM_BF16, 3) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.causal_conv1d_fwd(None, FAKE, None, FAKE, 2, 8, 16, 4, 0, 0, None) == _lib.SSM_ERR_NULL
+
+
+def test_python_binding_errors():
+    import torch
+    from state_space_model_scan_amd import binding
+    with pytest.raises(NotImplementedError):
+        binding._act_code("gelu")
+    assert binding._act_code("swish") == binding._act_code("silu") == _lib.SSM_ACT_SILU
+    assert binding._act_code(None) == _lib.SSM_ACT_NONE
+    with pytest.raises(ValueError):
+        binding._bc_kind(torch.zeros(2, 3, 4, 5, 6), "B")
+    assert binding._bc_kind(torch.zeros(4, 16), "B") == (_lib.SSM_BC_FIXED, 0)
+    assert binding._bc_kind(torch.zeros(2, 16, 8), "B") == (_lib.SSM_BC_VARYING, 1)
+    assert binding._bc_kind(torch.zeros(2, 4, 16, 8), "B") == (_lib.SSM_BC_VARYING, 4)
