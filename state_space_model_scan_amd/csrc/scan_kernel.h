@@ -16,9 +16,12 @@
 //     timesteps [8q, 8q+8) of each chunk: it loads them as one 16-byte bf16
 //     vector, computes delta' = softplus(delta + bias), delta'*u and D*u in
 //     registers, and after the chunk gates and stores its 8 outputs;
-//   * inside the chunk the other lanes of the quad read delta' and delta'*u of
-//     timestep t from the owner through a DPP quad broadcast, and the partial
-//     C.x of the LPC lanes are summed with DPP adds;
+//   * the owner writes delta' and delta'*u of its timesteps to the wave's LDS
+//     slice, where the whole quad reads them (one broadcast load per step);
+//     each lane writes its partial C.x of every timestep there too, and after
+//     the chunk the owner sums the LPC partials of its timesteps.  (Measured
+//     on gfx950, DPP forms issue at ~60% of the plain VALU rate and stall the
+//     dual issue, so the quad talks through LDS rather than DPP.);
 //   * time-varying B/C are the same for every channel of a wave: the wave
 //     stages the chunk's B/C tile (all states) in its own LDS slice, and lane
 //     q reads its NSW states of timestep t with one LDS vector load each;
@@ -50,7 +53,9 @@ struct ScanParams {
 
 enum { MODE_STATE = 0, MODE_FULL = 1 };
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 1;   // every wave is independent
+constexpr bool kDtViaDpp = true;    // delta' to the quad: DPP broadcast (else LDS)
+constexpr bool kYBatched = false;   // partial C.x: reduced once per chunk (else per step)
 constexpr int kKP = 8;                                   // timesteps each lane owns per chunk
 constexpr int chunk_of(int lpc) { return kKP * lpc; }    // chunk length
 constexpr int channels_per_block(int lpc) { return kWavesPerBlock * 64 / lpc; }
@@ -98,6 +103,12 @@ scan_kernel(const ScanParams p) {
   static_assert(NSW == 1 || NSW == 2 || NSW == 4, "states per lane");
 
   __shared__ float s_bc[ANYV ? kWavesPerBlock : 1][ANYV ? 2 : 1][ANYV ? T : 1][ANYV ? NP : 1];
+  constexpr bool XCH = LPC > 1;          // lanes of a channel exchange data
+  constexpr bool DT_DPP = kDtViaDpp && XCH;     // delta' reaches the quad by DPP (else LDS)
+  constexpr bool Y_BATCH = kYBatched && XCH;    // partial C.x kept for the chunk, reduced once
+  __shared__ float2 s_dt[(XCH && !DT_DPP) ? T : 1][(XCH && !DT_DPP) ? CPW : 1];   // (delta', delta'*u)
+  // partial C.x: [t][channel][lane] per step, or [channel][lane][t] per chunk
+  __shared__ float s_yp[(XCH && FULL) ? T * CPW * LPC : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -262,6 +273,46 @@ scan_kernel(const ScanParams p) {
       duv[i] = Dd * uu[i];
     }
   };
+  auto publish_dt = [&]() {   // this lane's timesteps to the quad
+    if constexpr (XCH && !DT_DPP) {
+#pragma unroll
+      for (int i = 0; i < kKP; ++i)
+        s_dt[(XCH && !DT_DPP) ? own + i : 0][(XCH && !DT_DPP) ? cw_idx : 0] = make_float2(dtv[i], dtuv[i]);
+    }
+  };
+  float yc[Y_BATCH ? T : 1];  // partial C.x of the chunk (batched reduction)
+  auto gather_y = [&]() {     // sum of the quad's partial C.x of this lane's timesteps
+    if constexpr (XCH && FULL) {
+      if constexpr (Y_BATCH) {
+        float *mine = &s_yp[(cw_idx * LPC + q) * T];
+#pragma unroll
+        for (int t = 0; t < T; t += 4)
+          *reinterpret_cast<float4 *>(mine + t) = make_float4(yc[t], yc[t + 1], yc[t + 2], yc[t + 3]);
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < kKP; ++i) yv[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < LPC; ++k) {
+          const float *theirs = &s_yp[(cw_idx * LPC + k) * T + own];
+#pragma unroll
+          for (int i = 0; i < kKP; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(theirs + i);
+            yv[i] += v.x; yv[i + 1] += v.y; yv[i + 2] += v.z; yv[i + 3] += v.w;
+          }
+        }
+      } else {
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < kKP; ++i) {
+          const float *yp = &s_yp[((own + i) * CPW + cw_idx) * LPC];
+          float y = yp[0];
+#pragma unroll
+          for (int k = 1; k < LPC; ++k) y += yp[k];
+          yv[i] = y;
+        }
+      }
+    }
+  };
 
   auto epilogue = [&](int64_t c) {
     const int cnt = count(c);
@@ -277,49 +328,55 @@ scan_kernel(const ScanParams p) {
   };
 
   float sumdt = 0.0f;   // summed delta' of the segment (MODE_STATE)
-  bool owner[LPC];      // owner[s]: this lane owns the timesteps of slot s
-#pragma unroll
-  for (int k = 0; k < LPC; ++k) owner[k] = q == k;
 
-  // one timestep t (0 <= t < T) of the chunk
-  auto step = [&](auto TT) {
+  // operands of timestep t of the chunk: (delta', delta'*u) and this lane's
+  // B/C values (LDS, registers or fixed)
+  struct StepIn {
+    float dt, dtu, Bv[NSW], Cv[NSW];
+  };
+  auto load_in = [&](auto TT, StepIn &in) {
     constexpr int t = decltype(TT)::value;
-    constexpr int src = t / kKP;      // lane of the quad that owns timestep t
-    constexpr int i = t % kKP;
-    float dt, dtu;
-    if constexpr (LPC == 1) {
-      dt = dtv[i];
-      dtu = dtuv[i];
+    if constexpr (DT_DPP) {
+      in.dt = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtv[t % kKP]);
+      in.dtu = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtuv[t % kKP]);
+    } else if constexpr (XCH) {
+      const float2 q2 = s_dt[(XCH && !DT_DPP) ? t : 0][(XCH && !DT_DPP) ? cw_idx : 0];
+      in.dt = q2.x;
+      in.dtu = q2.y;
     } else {
-      dt = dpp_bcast_reg<quad_bcast_ctrl<LPC, src>()>(dtv[i]);
-      dtu = dpp_bcast_reg<quad_bcast_ctrl<LPC, src>()>(dtuv[i]);
+      in.dt = dtv[t % kKP];
+      in.dtu = dtuv[t % kKP];
     }
-    if constexpr (!FULL) sumdt += dt;
-    float Bv[NSW], Cv[NSW];
     if constexpr (ANYV) {
       const float *rowB = &s_bc[ANYV ? w : 0][0][t][s0];
       const float *rowC = &s_bc[ANYV ? w : 0][ANYV ? 1 : 0][t][s0];
 #pragma unroll
       for (int k = 0; k < NSW; ++k) {
-        Bv[k] = BV ? rowB[k] : Bf[k];
-        Cv[k] = (CV && FULL) ? rowC[k] : Cf[k];
+        in.Bv[k] = BV ? rowB[k] : Bf[k];
+        in.Cv[k] = (CV && FULL) ? rowC[k] : Cf[k];
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < NSW; ++k) { Bv[k] = Bf[k]; Cv[k] = Cf[k]; }
+      for (int k = 0; k < NSW; ++k) { in.Bv[k] = Bf[k]; in.Cv[k] = Cf[k]; }
     }
+  };
+
+  // one timestep t (0 <= t < T) of the chunk
+  auto step = [&](auto TT, const StepIn &in) {
+    constexpr int t = decltype(TT)::value;
+    if constexpr (!FULL) sumdt += in.dt;
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
-      const float e = fast_exp2(dt * Ap[k]);
-      x[k] = fmaf(e, x[k], Bv[k] * dtu);
+      const float e = fast_exp2(in.dt * Ap[k]);
+      x[k] = fmaf(e, x[k], in.Bv[k] * in.dtu);
     }
     if constexpr (FULL) {
-      float y = Cv[0] * x[0];
+      float y = in.Cv[0] * x[0];
 #pragma unroll
-      for (int k = 1; k < NSW; ++k) y = fmaf(Cv[k], x[k], y);
-      if constexpr (LPC >= 2) y += dpp_mov<0xB1>(y);   // quad_perm [1,0,3,2]
-      if constexpr (LPC >= 4) y += dpp_mov<0x4E>(y);   // quad_perm [2,3,0,1]
-      yv[i] = owner[src] ? y : yv[i];                   // kept by the owning lane
+      for (int k = 1; k < NSW; ++k) y = fmaf(in.Cv[k], x[k], y);
+      if constexpr (Y_BATCH) yc[Y_BATCH ? t : 0] = y;
+      else if constexpr (XCH) s_yp[(t * CPW + cw_idx) * LPC + q] = y;
+      else yv[t % kKP] = y;
     }
   };
 
@@ -329,10 +386,11 @@ scan_kernel(const ScanParams p) {
   for (int64_t c = t_begin; c < t_end; c += T) {
     const int len = static_cast<int>((t_end - c < T) ? t_end - c : T);
     prep(c);
-    if constexpr (ANYV) {
-      wave_lds_sync();          // the previous chunk's reads of the tile are done
-      stage_bc();
-      wave_lds_sync();          // the tile is written before any lane reads it
+    if constexpr (ANYV || (XCH && !DT_DPP)) {
+      wave_lds_sync();          // the previous chunk's reads of the slice are done
+      if constexpr (ANYV) stage_bc();
+      publish_dt();
+      wave_lds_sync();          // the slice is written before any lane reads it
     }
     const RawV<BF16, kKP> z_cur = r_z;
     if (c + T < t_end) {
@@ -340,14 +398,28 @@ scan_kernel(const ScanParams p) {
       if constexpr (ANYV) fetch_bc(c + T);
     }
     if (len == T) {
-      static_for(std::make_integer_sequence<int, T>{}, [&](auto TT) { step(TT); });
-    } else {
-      // ragged last chunk: timesteps past the end have delta' = 0 and only
-      // leave the state unchanged if they also skip the update
+      // whole chunk, fully unrolled; operands read from LDS two timesteps
+      // ahead of their use so the LDS latency hides behind the recurrence
+      constexpr int AH = 2;
+      StepIn in[AH + 1];
+      load_in(std::integral_constant<int, 0>{}, in[0]);
+      load_in(std::integral_constant<int, 1>{}, in[1]);
       static_for(std::make_integer_sequence<int, T>{}, [&](auto TT) {
-        if (decltype(TT)::value < len) step(TT);
+        constexpr int t = decltype(TT)::value;
+        if constexpr (t + AH < T) load_in(std::integral_constant<int, t + AH>{}, in[(t + AH) % (AH + 1)]);
+        step(TT, in[t % (AH + 1)]);
+      });
+    } else {
+      // ragged last chunk of a segment: timesteps past the end are skipped
+      static_for(std::make_integer_sequence<int, T>{}, [&](auto TT) {
+        if (decltype(TT)::value < len) {
+          StepIn in1;
+          load_in(TT, in1);
+          step(TT, in1);
+        }
       });
     }
+    if constexpr (XCH && FULL) gather_y();   // sum of the quad's partial C.x
     if constexpr (FULL) {
       const RawV<BF16, kKP> z_next = r_z;
       r_z = z_cur;

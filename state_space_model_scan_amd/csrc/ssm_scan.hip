@@ -116,9 +116,12 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   pl.nblk = static_cast<int>((pl.cpg + cpb - 1) / cpb);
   pl.nblocks = static_cast<int>(a->batch * pl.groups_eff * pl.nblk);
   const int64_t waves = static_cast<int64_t>(pl.nblocks) * kWavesPerBlock;
-  const int64_t target = 8LL * cus;     // two waves per SIMD
+  // Split when the waves would leave the SIMDs short of work: the state pass
+  // of a split costs more than it gains once a pass has >= ~2 waves per SIMD,
+  // and narrow workloads keep gaining up to ~4-6 waves per SIMD.
+  const int64_t target = 16LL * cus;
   int nseg = 1;
-  if (waves < target) {
+  if (waves < 8LL * cus) {
     const int64_t want = (3 * target + 2 * waves - 1) / (2 * waves);
     const int64_t cap = a->seqlen / (4 * pl.T);
     nseg = static_cast<int>(want < cap ? want : cap);
