@@ -13,18 +13,17 @@
 //     for delta'*A, one multiply for delta'*u*B, one FMA for the state and
 //     one FMA for C.x, the plain recurrence with no parallel-scan overhead;
 //   * the sequence is walked in chunks of T = 8*LPC timesteps.  Lane q owns
-//     timesteps [8q, 8q+8) of each chunk: it loads them as one 16-byte bf16
-//     vector, computes delta' = softplus(delta + bias), delta'*u and D*u in
+//     timesteps [8q, 8q+8) of each chunk: it loads them as one vector per
+//     input, computes delta' = softplus(delta + bias), delta'*u and D*u in
 //     registers, and after the chunk gates and stores its 8 outputs;
-//   * the owner writes delta' and delta'*u of its timesteps to the wave's LDS
-//     slice, where the whole quad reads them (one broadcast load per step);
-//     each lane writes its partial C.x of every timestep there too, and after
-//     the chunk the owner sums the LPC partials of its timesteps.  (Measured
-//     on gfx950, DPP forms issue at ~60% of the plain VALU rate and stall the
-//     dual issue, so the quad talks through LDS rather than DPP.);
+//   * per timestep the owner's delta' and delta'*u reach the other lanes of
+//     the quad by one DPP quad broadcast each; every lane writes its partial
+//     C.x to the wave's LDS slice, and after the chunk the owner sums the LPC
+//     partials of its timesteps;
 //   * time-varying B/C are the same for every channel of a wave: the wave
 //     stages the chunk's B/C tile (all states) in its own LDS slice, and lane
-//     q reads its NSW states of timestep t with one LDS vector load each;
+//     q reads its NSW states of timestep t with one LDS vector load each, two
+//     timesteps ahead of their use;
 //   * the global loads of chunk c+1 are issued before the recurrence of chunk
 //     c, so their latency hides behind it;
 //   * when batch*dim is too small to fill the GPU the sequence is cut into
@@ -54,8 +53,6 @@ struct ScanParams {
 enum { MODE_STATE = 0, MODE_FULL = 1 };
 
 constexpr int kWavesPerBlock = 1;   // every wave is independent
-constexpr bool kDtViaDpp = true;    // delta' to the quad: DPP broadcast (else LDS)
-constexpr bool kYBatched = false;   // partial C.x: reduced once per chunk (else per step)
 constexpr int kKP = 8;                                   // timesteps each lane owns per chunk
 constexpr int chunk_of(int lpc) { return kKP * lpc; }    // chunk length
 constexpr int channels_per_block(int lpc) { return kWavesPerBlock * 64 / lpc; }
@@ -104,10 +101,7 @@ scan_kernel(const ScanParams p) {
 
   __shared__ float s_bc[ANYV ? kWavesPerBlock : 1][ANYV ? 2 : 1][ANYV ? T : 1][ANYV ? NP : 1];
   constexpr bool XCH = LPC > 1;          // lanes of a channel exchange data
-  constexpr bool DT_DPP = kDtViaDpp && XCH;     // delta' reaches the quad by DPP (else LDS)
-  constexpr bool Y_BATCH = kYBatched && XCH;    // partial C.x kept for the chunk, reduced once
-  __shared__ float2 s_dt[(XCH && !DT_DPP) ? T : 1][(XCH && !DT_DPP) ? CPW : 1];   // (delta', delta'*u)
-  // partial C.x: [t][channel][lane] per step, or [channel][lane][t] per chunk
+  // partial C.x of every (timestep, channel, lane) of the chunk
   __shared__ float s_yp[(XCH && FULL) ? T * CPW * LPC : 1];
 
   const int lane = threadIdx.x & 63;
@@ -241,7 +235,9 @@ scan_kernel(const ScanParams p) {
 #pragma unroll
   for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
 
-  auto prep = [&](int64_t c) {
+  // CSc: silu after the conv (a compile-time constant, chosen once per chunk)
+  auto prep = [&](int64_t c, auto CSc) {
+    constexpr bool CS = decltype(CSc)::value;
     float uu[kKP];
     if constexpr (CONV) {
       float xv[kKP + 3];
@@ -255,7 +251,7 @@ scan_kernel(const ScanParams p) {
         acc = fmaf(cw1, xv[i + 1], acc);
         acc = fmaf(cw2, xv[i + 2], acc);
         acc = fmaf(cw3, xv[i + 3], acc);
-        if (p.conv_silu) acc = silu_f(acc);
+        if constexpr (CS) acc = silu_f(acc);
         uu[i] = round_io<BF16>(acc);
       }
     } else {
@@ -273,43 +269,16 @@ scan_kernel(const ScanParams p) {
       duv[i] = Dd * uu[i];
     }
   };
-  auto publish_dt = [&]() {   // this lane's timesteps to the quad
-    if constexpr (XCH && !DT_DPP) {
-#pragma unroll
-      for (int i = 0; i < kKP; ++i)
-        s_dt[(XCH && !DT_DPP) ? own + i : 0][(XCH && !DT_DPP) ? cw_idx : 0] = make_float2(dtv[i], dtuv[i]);
-    }
-  };
-  float yc[Y_BATCH ? T : 1];  // partial C.x of the chunk (batched reduction)
   auto gather_y = [&]() {     // sum of the quad's partial C.x of this lane's timesteps
     if constexpr (XCH && FULL) {
-      if constexpr (Y_BATCH) {
-        float *mine = &s_yp[(cw_idx * LPC + q) * T];
+      wave_lds_sync();
 #pragma unroll
-        for (int t = 0; t < T; t += 4)
-          *reinterpret_cast<float4 *>(mine + t) = make_float4(yc[t], yc[t + 1], yc[t + 2], yc[t + 3]);
-        wave_lds_sync();
+      for (int i = 0; i < kKP; ++i) {
+        const float *yp = &s_yp[((own + i) * CPW + cw_idx) * LPC];
+        float y = yp[0];
 #pragma unroll
-        for (int i = 0; i < kKP; ++i) yv[i] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < LPC; ++k) {
-          const float *theirs = &s_yp[(cw_idx * LPC + k) * T + own];
-#pragma unroll
-          for (int i = 0; i < kKP; i += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(theirs + i);
-            yv[i] += v.x; yv[i + 1] += v.y; yv[i + 2] += v.z; yv[i + 3] += v.w;
-          }
-        }
-      } else {
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < kKP; ++i) {
-          const float *yp = &s_yp[((own + i) * CPW + cw_idx) * LPC];
-          float y = yp[0];
-#pragma unroll
-          for (int k = 1; k < LPC; ++k) y += yp[k];
-          yv[i] = y;
-        }
+        for (int k = 1; k < LPC; ++k) y += yp[k];
+        yv[i] = y;
       }
     }
   };
@@ -336,13 +305,9 @@ scan_kernel(const ScanParams p) {
   };
   auto load_in = [&](auto TT, StepIn &in) {
     constexpr int t = decltype(TT)::value;
-    if constexpr (DT_DPP) {
+    if constexpr (XCH) {
       in.dt = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtv[t % kKP]);
       in.dtu = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtuv[t % kKP]);
-    } else if constexpr (XCH) {
-      const float2 q2 = s_dt[(XCH && !DT_DPP) ? t : 0][(XCH && !DT_DPP) ? cw_idx : 0];
-      in.dt = q2.x;
-      in.dtu = q2.y;
     } else {
       in.dt = dtv[t % kKP];
       in.dtu = dtuv[t % kKP];
@@ -374,8 +339,7 @@ scan_kernel(const ScanParams p) {
       float y = in.Cv[0] * x[0];
 #pragma unroll
       for (int k = 1; k < NSW; ++k) y = fmaf(in.Cv[k], x[k], y);
-      if constexpr (Y_BATCH) yc[Y_BATCH ? t : 0] = y;
-      else if constexpr (XCH) s_yp[(t * CPW + cw_idx) * LPC + q] = y;
+      if constexpr (XCH) s_yp[(t * CPW + cw_idx) * LPC + q] = y;
       else yv[t % kKP] = y;
     }
   };
@@ -385,11 +349,10 @@ scan_kernel(const ScanParams p) {
 
   for (int64_t c = t_begin; c < t_end; c += T) {
     const int len = static_cast<int>((t_end - c < T) ? t_end - c : T);
-    prep(c);
-    if constexpr (ANYV || (XCH && !DT_DPP)) {
+    if (CONV && p.conv_silu) prep(c, std::true_type{}); else prep(c, std::false_type{});
+    if constexpr (ANYV) {
       wave_lds_sync();          // the previous chunk's reads of the slice are done
-      if constexpr (ANYV) stage_bc();
-      publish_dt();
+      stage_bc();
       wave_lds_sync();          // the slice is written before any lane reads it
     }
     const RawV<BF16, kKP> z_cur = r_z;
@@ -408,6 +371,9 @@ scan_kernel(const ScanParams p) {
         constexpr int t = decltype(TT)::value;
         if constexpr (t + AH < T) load_in(std::integral_constant<int, t + AH>{}, in[(t + AH) % (AH + 1)]);
         step(TT, in[t % (AH + 1)]);
+        // keep the lookahead loads where they are written: without the fence
+        // the scheduler sinks them next to their use and every step waits on LDS
+        __builtin_amdgcn_sched_barrier(0);
       });
     } else {
       // ragged last chunk of a segment: timesteps past the end are skipped

@@ -177,7 +177,8 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   p.groups_eff = pl.groups_eff; p.nblk = pl.nblk; p.nseg = pl.nseg; p.nblocks = pl.nblocks;
   p.softplus = a->delta_softplus; p.conv_silu = a->conv_act == SSM_ACT_SILU;
   p.vec = (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
-          (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z));
+          (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z)) &&
+          (a->B_kind != SSM_BC_VARYING || aligned16(a->B)) && (a->C_kind != SSM_BC_VARYING || aligned16(a->C));
   p.xcd_swizzle = (pl.nblocks % 8 == 0);
 
   void *ws = a->workspace;
