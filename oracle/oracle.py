@@ -73,6 +73,12 @@ def _load():
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_selective_state_update.argtypes = [
+            i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, p, i32, p, p]
+        lib.oracle_selective_state_update.restype = i32
+        lib.oracle_causal_conv1d_update.argtypes = [
+            i64, i64, i64, i32, i64, i32, p, p, p, p, i32, p, p, p]
+        lib.oracle_causal_conv1d_update.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -174,3 +180,56 @@ def causal_conv1d(x, weight, bias=None, act=ACT_NONE, *, io_dtype=F32, rows=None
     if rc != 0:
         raise ValueError(f"oracle_causal_conv1d failed with status {rc}")
     return out
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           dt_softplus=False, *, io_dtype=F32):
+    """Oracle single decode step against a cached state.
+
+    state: (batch, dim, dstate) float (the cached fp32 state, widened);
+    x, dt, z: (batch, dim) io bits; A: (dim, dstate) float32;
+    B, C: (batch, ngroups, dstate) io bits; D, dt_bias: (dim,) float32.
+    Returns (out (batch, dim) float64, new state (batch, dim, dstate) float64).
+    """
+    lib = _load()
+    x, dt, z = _io(x, io_dtype), _io(dt, io_dtype), _io(z, io_dtype)
+    B, C = _io(B, io_dtype), _io(C, io_dtype)
+    A, D, dt_bias = _f32(A), _f32(D), _f32(dt_bias)
+    st = np.ascontiguousarray(state, dtype=np.float64)
+    batch, dim = x.shape
+    dstate = A.shape[1]
+    ngroups = B.shape[1]
+    out = np.empty((batch, dim), dtype=np.float64)
+    new = np.empty((batch, dim, dstate), dtype=np.float64)
+    rc = lib.oracle_selective_state_update(
+        batch, dim, dstate, ngroups, io_dtype, _ptr(st), _ptr(x), _ptr(dt), _ptr(A),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(z), int(bool(dt_softplus)),
+        _ptr(out), _ptr(new))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_state_update failed with status {rc}")
+    return out, new
+
+
+def causal_conv1d_update(x, conv_state, weight, bias=None, act=ACT_NONE, cache_seqlens=None,
+                         *, io_dtype=F32):
+    """Oracle conv continued from a cache of earlier inputs.
+
+    x: (batch, dim, seqlen) io bits; conv_state: (batch, dim, state_len) io bits
+    (not modified); weight (dim, width) float32; bias (dim,) float32;
+    cache_seqlens: None (shift mode) or (batch,) int32 ring-buffer positions.
+    Returns (out (batch, dim, seqlen) float64, new conv_state (io bits)).
+    """
+    lib = _load()
+    x, conv_state = _io(x, io_dtype), _io(conv_state, io_dtype)
+    batch, dim, seqlen = x.shape
+    state_len = conv_state.shape[2]
+    weight, bias = _f32(weight), _f32(bias)
+    cs = None if cache_seqlens is None else np.ascontiguousarray(cache_seqlens, dtype=np.int32)
+    out = np.empty((batch, dim, seqlen), dtype=np.float64)
+    new = np.empty_like(conv_state)
+    rc = lib.oracle_causal_conv1d_update(
+        batch, dim, seqlen, weight.shape[1], state_len, io_dtype, _ptr(x), _ptr(conv_state),
+        _ptr(weight), _ptr(bias), act, _ptr(cs), _ptr(out), _ptr(new))
+    if rc != 0:
+        raise ValueError(f"oracle_causal_conv1d_update failed with status {rc}")
+    return out, new

@@ -8,6 +8,11 @@
  * kernels.
  *
  * Sources (the pages are the authority for what is computed):
+ *   - the same guide, section 4.4, lists selective_state_update among the
+ *     mamba operators, and section 4.2 names causal_conv1d_update (single-step
+ *     incremental inference over a conv_state cache with an optional ring
+ *     buffer); neither is printed, so both are read as one more step of the
+ *     operators above applied to a cache (see each function).
  *   - "PaddleNLP Kernel operator library: CUDA and Triton dual-implementation
  *     guide", section 4.1 (selective_scan): the argument list of
  *     selective_scan_fn, the shapes of u/delta (batch,dim,seqlen), A
@@ -255,6 +260,145 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t seqlen,
     }
     (void)nthreads;
     return failed ? 5 : 0;
+}
+
+/* ---- single-step decode -------------------------------------------------- */
+
+/* selective_state_update: one timestep of the recurrence above applied to a
+ * cached state (the decode step named in the mamba operator list of the
+ * PaddleNLP Kernel guide, section 4.4).  Per (b, d):
+ *   dt' = softplus(dt + dt_bias) (or dt + dt_bias without the flag)
+ *   state[s] <- exp(dt' * A[d,s]) * state[s] + dt' * B[b,g,s] * x
+ *   out = (sum_s C[b,g,s] * state[s] + D[d] * x) * silu(z)
+ * with g = d / (dim/ngroups).  Mamba-2 heads are flattened into dim (head h,
+ * element p -> d = h*headdim + p), which is the same computation.
+ * state_in: (batch, dim, dstate) double; x, dt, z: (batch, dim) io bits;
+ * B, C: (batch, ngroups, dstate) io bits; out: (batch*dim) double;
+ * state_out: (batch, dim, dstate) double (may equal state_in). */
+int oracle_selective_state_update(int64_t batch, int64_t dim, int64_t dstate,
+                                  int64_t ngroups, int io_dtype,
+                                  const double *state_in, const void *x,
+                                  const void *dt, const float *A, const void *B,
+                                  const void *C, const float *D,
+                                  const float *dt_bias, const void *z,
+                                  int dt_softplus, double *out, double *state_out) {
+    if (batch <= 0 || dim <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!state_in || !x || !dt || !A || !B || !C || !out || !state_out) return 1;
+    const int64_t per_group = dim / ngroups;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            const int64_t grp = d / per_group;
+            double step = load_io(dt, io_dtype, row);
+            if (dt_bias) step += (double)dt_bias[d];
+            if (dt_softplus) step = oracle_softplus(step);
+            const double xv = load_io(x, io_dtype, row);
+            double y = 0.0;
+            for (int64_t s = 0; s < dstate; ++s) {
+                const int64_t bc = (b * ngroups + grp) * dstate + s;
+                const double dA = exp(step * (double)A[d * dstate + s]);
+                const double h = dA * state_in[row * dstate + s]
+                                 + step * load_io(B, io_dtype, bc) * xv;
+                state_out[row * dstate + s] = h;
+                y += load_io(C, io_dtype, bc) * h;
+            }
+            if (D) y += (double)D[d] * xv;
+            if (z) y *= oracle_silu(load_io(z, io_dtype, row));
+            out[row] = y;
+        }
+    }
+    return 0;
+}
+
+/* causal_conv1d_update: the causal conv of section 4.2 continued from a
+ * cache of earlier inputs (the single-step incremental form the same section
+ * names, with its conv_state cache and optional ring buffer).  Per (b, d) and
+ * new token t of seqlen:
+ *   window = the width-1 inputs before t, then x[t]
+ *   out[t] = act(bias[d] + sum_k w[d,k] * window[k])
+ * The cache holds state_len >= width-1 earlier inputs.
+ *   - cache_seqlens == NULL: the cache is ordered oldest first; the inputs
+ *     before the first new token are its last width-1 entries, and after the
+ *     call it holds the last state_len inputs (cache and new tokens together,
+ *     shifted left).
+ *   - cache_seqlens given (one int32 per batch): the cache is a ring buffer;
+ *     token t is written at slot (cache_seqlens[b] + t) % state_len, and the
+ *     inputs before it are the width-1 slots before that one, circularly.
+ *     The other slots are left as they are; the caller advances cache_seqlens.
+ * x: (batch, dim, seqlen) io bits; conv_state: (batch, dim, state_len) io
+ * bits, read; out: (batch*dim*seqlen) double; state_out: (batch, dim,
+ * state_len) io bits, written (may equal conv_state: each row is read whole
+ * before it is written). */
+int oracle_causal_conv1d_update(int64_t batch, int64_t dim, int64_t seqlen,
+                                int width, int64_t state_len, int io_dtype,
+                                const void *x, const void *conv_state,
+                                const float *weight, const float *bias, int act,
+                                const int32_t *cache_seqlens, double *out,
+                                void *state_out) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || width <= 0) return 2;
+    if (state_len < width - 1 || state_len <= 0) return 2;
+    if (!x || !conv_state || !weight || !out || !state_out) return 1;
+    const size_t es = io_dtype == OR_BF16 ? 2 : 4;
+    /* one row of raw io words: the cache followed by the new tokens */
+    unsigned char *buf = (unsigned char *)malloc(es * (size_t)(state_len + seqlen));
+    double *win = (double *)malloc(sizeof(double) * (size_t)width);
+    if (!buf || !win) { free(buf); free(win); return 5; }
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            const unsigned char *st = (const unsigned char *)conv_state + es * (size_t)(row * state_len);
+            const unsigned char *xr = (const unsigned char *)x + es * (size_t)(row * seqlen);
+            memcpy(buf, st, es * (size_t)state_len);
+            const double bv = bias ? (double)bias[d] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                /* gather the window: width-1 earlier inputs, then x[t] */
+                for (int k = 0; k < width - 1; ++k) {
+                    const int64_t back = (width - 1) - k;   /* steps before token t */
+                    if (!cache_seqlens) {
+                        /* linear history: cache entries then new tokens */
+                        const int64_t pos = state_len + t - back;
+                        win[k] = pos < state_len ? load_io(st, io_dtype, pos)
+                                                 : load_io(xr, io_dtype, pos - state_len);
+                    } else {
+                        if (back <= t) {
+                            win[k] = load_io(xr, io_dtype, t - back);
+                        } else {
+                            int64_t slot = ((int64_t)cache_seqlens[b] + t - back) % state_len;
+                            if (slot < 0) slot += state_len;
+                            win[k] = load_io(st, io_dtype, slot);
+                        }
+                    }
+                }
+                win[width - 1] = load_io(xr, io_dtype, t);
+                double acc = bv;
+                for (int k = 0; k < width; ++k) acc += (double)weight[d * width + k] * win[k];
+                if (act == OR_ACT_SILU) acc = oracle_silu(acc);
+                out[row * seqlen + t] = acc;
+            }
+            /* the cache after the call */
+            unsigned char *so = (unsigned char *)state_out + es * (size_t)(row * state_len);
+            if (!cache_seqlens) {
+                /* the last state_len inputs of (cache, new tokens) */
+                unsigned char *hist = (unsigned char *)malloc(es * (size_t)(state_len + seqlen));
+                if (!hist) { free(buf); free(win); return 5; }
+                memcpy(hist, buf, es * (size_t)state_len);
+                memcpy(hist + es * (size_t)state_len, xr, es * (size_t)seqlen);
+                memcpy(so, hist + es * (size_t)seqlen, es * (size_t)state_len);
+                free(hist);
+            } else {
+                memcpy(so, buf, es * (size_t)state_len);
+                for (int64_t t = 0; t < seqlen; ++t) {
+                    int64_t slot = ((int64_t)cache_seqlens[b] + t) % state_len;
+                    if (slot < 0) slot += state_len;
+                    memcpy(so + es * (size_t)slot, xr + es * (size_t)t, es);
+                }
+            }
+        }
+    }
+    free(buf);
+    free(win);
+    return 0;
 }
 
 /* Number of threads an OpenMP region would use (1 without OpenMP). */

@@ -78,3 +78,69 @@ def test_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the decode functions against their own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_decode_pins as dpins  # noqa: E402
+
+DECODE_MUTANTS = {
+    "su_contract_old_state": ("y += load_io(C, io_dtype, bc) * h;",
+                              "y += load_io(C, io_dtype, bc) * state_in[row * dstate + s];"),
+    "su_drop_dt_in_input": ("+ step * load_io(B, io_dtype, bc) * xv;", "+ load_io(B, io_dtype, bc) * xv;"),
+    "su_group_interleaved": ("const int64_t grp = d / per_group;",
+                             "const int64_t grp = d % ngroups; (void)per_group;"),
+    "su_bias_after_softplus": ("if (dt_bias) step += (double)dt_bias[d];\n            if (dt_softplus) step = oracle_softplus(step);",
+                               "if (dt_softplus) step = oracle_softplus(step);\n            if (dt_bias) step += (double)dt_bias[d];"),
+    "su_drop_D": ("if (D) y += (double)D[d] * xv;", ""),
+    "cu_ring_read_off_by_one": ("int64_t slot = ((int64_t)cache_seqlens[b] + t - back) % state_len;",
+                                "int64_t slot = ((int64_t)cache_seqlens[b] + t - back + 1) % state_len;"),
+    "cu_ring_write_off_by_one": ("int64_t slot = ((int64_t)cache_seqlens[b] + t) % state_len;",
+                                 "int64_t slot = ((int64_t)cache_seqlens[b] + t + 1) % state_len;"),
+    "cu_shift_stale": ("memcpy(so, hist + es * (size_t)seqlen, es * (size_t)state_len);",
+                       "memcpy(so, hist, es * (size_t)state_len);"),
+    "cu_window_reversed": ("acc += (double)weight[d * width + k] * win[k];",
+                           "acc += (double)weight[d * width + k] * win[width - 1 - k];"),
+}
+
+
+def _decode_pin_calls():
+    F32, BF16 = orc.F32, orc.BF16
+    return [
+        ("chain_scan_f32", lambda: dpins.test_state_update_chain_equals_scan(F32, 2, True)),
+        ("chain_scan_bf16_nosp", lambda: dpins.test_state_update_chain_equals_scan(BF16, 1, False)),
+        ("a_zero", dpins.test_state_update_a_zero_is_accumulation),
+        ("zero_step", dpins.test_state_update_zero_step_keeps_state),
+        ("one_hot_c", dpins.test_state_update_one_hot_c_reads_one_state),
+        ("groups", dpins.test_state_update_groups_broadcast),
+        ("conv_chain", lambda: dpins.test_conv_update_chain_equals_conv(F32, orc.ACT_SILU, 4)),
+        ("conv_multi_shift", lambda: dpins.test_conv_update_multi_token_equals_single_steps(False)),
+        ("conv_multi_ring", lambda: dpins.test_conv_update_multi_token_equals_single_steps(True)),
+        ("conv_identity", dpins.test_conv_update_identity_kernel_and_history),
+        ("conv_ring_slots", dpins.test_conv_update_ring_reads_the_slots_before_the_position),
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(DECODE_MUTANTS))
+def test_decode_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = DECODE_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _decode_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
