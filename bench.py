@@ -29,6 +29,14 @@ kernel source, else null.
 
 cpu_baseline: the float64 oracle (test infrastructure) timed on this host's
 cores over a bounded sample of the workload's rows, scaled to elements/s.
+
+Decode workloads (--workload decode2p8b): a step is one decode step of one
+layer, causal_conv1d_update (one new token against the conv cache) then
+ssm_state_update (one timestep against the cached fp32 state), both in place.
+The value is channel-steps/s (b*d per step); the roofline is HBM for the
+state update, the dominant kernel: the state read and written once, x, dt,
+z, out, B, C once, A/D/dt_bias once (d*n*4 + 2*d*4 bytes, shared by the
+batch), against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -88,6 +96,23 @@ def load_traffic(name: str):
     return rec.get("traffic_bytes")
 
 
+def decode_state_update_bytes(w) -> int:
+    es = 2 if w.io_dtype == 1 else 4
+    bd = w.batch * w.dim
+    state = 2 * bd * w.dstate * 4
+    vecs = (3 + (1 if w.has_z else 0)) * bd * es            # x, dt, out (+ z)
+    bc = 2 * w.batch * w.ngroups * w.dstate * es
+    params = w.dim * w.dstate * 4 + (w.dim * 4 if w.has_D else 0) + (w.dim * 4 if w.has_bias else 0)
+    return state + vecs + bc + params
+
+
+def decode_conv_update_bytes(w) -> int:
+    es = 2 if w.io_dtype == 1 else 4
+    bd = w.batch * w.dim
+    return (2 * bd * w.conv_tokens * es + 2 * bd * w.conv_state_len * es
+            + w.dim * w.conv_width * 4 + w.dim * 4)
+
+
 def cpu_baseline(w, t, budget_s: float):
     """Oracle throughput on a bounded sample of rows (all host threads)."""
     from oracle import oracle as orc
@@ -136,7 +161,9 @@ def main():
 
     import torch
     from state_space_model_scan_amd import _lib, binding
-    from state_space_model_scan_amd.inputs import BF16, WORKLOADS, make_inputs
+    from state_space_model_scan_amd.inputs import BF16, DECODE_WORKLOADS, WORKLOADS, make_inputs
+    if args.workload in DECODE_WORKLOADS:
+        return decode_main(args)
 
     def to_dev(a, io_dtype, param=False):
         x = torch.from_numpy(np.ascontiguousarray(a))
@@ -230,6 +257,129 @@ def main():
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
+
+
+
+def decode_main(args):
+    """One decode step per timed step: conv update, then state update."""
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, DECODE_WORKLOADS, make_decode_inputs
+
+    _lib.lib()
+    w = DECODE_WORKLOADS[args.workload]
+    t = make_decode_inputs(w)
+    io = w.io_dtype
+
+    def dev(a, param=False):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and io == BF16 and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16)
+        return x.cuda()
+
+    x, dt = dev(t["x"]), dev(t["dt"])
+    z = dev(t["z"]) if t["z"] is not None else None
+    B, C = dev(t["B"]), dev(t["C"])
+    A = dev(t["A"], True)
+    D = dev(t["D"], True) if t["D"] is not None else None
+    bias = dev(t["dt_bias"], True) if t["dt_bias"] is not None else None
+    state = dev(t["state"], True)
+    conv_x, conv_state = dev(t["conv_x"]), dev(t["conv_state"])
+    cw, cb = dev(t["conv_weight"], True), dev(t["conv_bias"], True)
+    u = torch.empty_like(conv_x)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def conv_step():
+        binding.causal_conv1d_update(conv_x, conv_state, cw, cb, "silu", None, out=u)
+
+    def state_step():
+        binding.selective_state_update(state, x, dt, A, B, C, D, z, bias, w.softplus, out=out)
+
+    for _ in range(args.warmup):
+        conv_step()
+        state_step()
+    torch.cuda.synchronize()
+    cs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ss = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    se = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        cs[i].record(stream)
+        conv_step()
+        ce[i].record(stream)
+        ss[i].record(stream)
+        state_step()
+        se[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    conv_ms = [a.elapsed_time(b) for a, b in zip(cs, ce)]
+    su_ms = [a.elapsed_time(b) for a, b in zip(ss, se)]
+    su_s = float(np.mean(su_ms)) / 1e3
+    conv_s = float(np.mean(conv_ms)) / 1e3
+    su_bytes = decode_state_update_bytes(w)
+    cv_bytes = decode_conv_update_bytes(w)
+    su_gbs = su_bytes / su_s / 1e9
+    rec = {
+        "metric": "decode step (conv update + selective_state_update) channel-steps/s (b·d)",
+        "value": w.channels * args.steps / wall,
+        "unit": "channel-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: b={w.batch} d={w.dim} n={w.dstate} g={w.ngroups} "
+                        f"{'bf16' if io == BF16 else 'fp32'} io, fp32 state, conv width {w.conv_width} "
+                        f"cache {w.conv_state_len}, {w.conv_tokens} token(s)",
+            "io_dtype": "bf16" if io == BF16 else "fp32",
+            "channels_per_step": w.channels,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": su_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": su_gbs / HBM_PEAK_GBS,
+            "traffic": load_traffic(w.name),
+            "kernel": "state_update_kernel",
+            "kernel_avg_ms": su_s * 1e3,
+            "kernel_median_ms": float(np.median(su_ms)),
+            "algorithmic_bytes": su_bytes,
+            "conv_update": {"avg_ms": conv_s * 1e3, "algorithmic_bytes": cv_bytes,
+                            "GBs": cv_bytes / conv_s / 1e9},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = decode_cpu_baseline(w, t, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+def decode_cpu_baseline(w, t, budget_s: float):
+    """The oracle's state update (single-threaded C) on a batch slice."""
+    from oracle import oracle as orc
+    nb = min(w.batch, 16)
+    while True:
+        sl = slice(0, nb)
+        t0 = time.perf_counter()
+        orc.selective_state_update(t["state"][sl].astype(np.float64), t["x"][sl], t["dt"][sl], t["A"],
+                                   t["B"][sl], t["C"][sl], t["D"], t["z"][sl] if t["z"] is not None else None,
+                                   t["dt_bias"], w.softplus, io_dtype=w.io_dtype)
+        dt = time.perf_counter() - t0
+        if dt >= min(budget_s, 2.0) or nb == w.batch:
+            break
+        nb = min(w.batch, nb * 4)
+    return {"value": nb * w.dim / dt, "unit": "channel-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"state update of {nb} of {w.batch} batch rows (d={w.dim}, n={w.dstate}), "
+                      f"{dt:.2f} s float64 on 1 thread"}
 
 
 if __name__ == "__main__":

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
 
@@ -134,6 +134,85 @@ int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, voi
 int causal_conv1d_validate(const void *x, const float *weight, const void *out,
                            int64_t batch, int64_t dim, int64_t seqlen, int32_t width,
                            int32_t io_dtype, int32_t act);
+
+/* ---------------------------------------------------------------------------
+ * Single-step decode.
+ * ------------------------------------------------------------------------- */
+
+#define SSM_MAX_CONV_STATE 256  /* largest conv cache length causal_conv1d_update takes */
+
+/* Arguments of ssm_state_update.  Every pointer is a device pointer. */
+typedef struct ssm_state_update_args {
+  int64_t batch, dim, dstate, ngroups;          /* ngroups: 1 unless grouped */
+  int32_t io_dtype;                             /* SSM_F32 or SSM_BF16 */
+  float *state;                                 /* (b,d,n) fp32: read, then overwritten */
+  const void *x;                                /* (b,d) io, required */
+  const void *dt;                               /* (b,d) io, required */
+  const float *A;                               /* (d,n) fp32, required */
+  const void *B;                                /* (b,g,n) io, required */
+  const void *C;                                /* (b,g,n) io, required */
+  const float *D;                               /* (d) fp32 or NULL */
+  const float *dt_bias;                         /* (d) fp32 or NULL */
+  const void *z;                                /* (b,d) io or NULL */
+  int32_t dt_softplus;                          /* 0 or 1 */
+  void *out;                                    /* (b,d) io, required */
+} ssm_state_update_args_t;
+
+/* selective_state_update: one decode step of the recurrence above against a
+ * cached state (the PaddleNLP Kernel operator-library guide lists
+ * selective_state_update among its mamba operators, section 4.4; it is not
+ * printed there, and is read as one timestep of section 4.1's scan applied
+ * to a cache).  For every (b, d), with dt' = softplus(dt + dt_bias) when
+ * dt_softplus is set (otherwise dt + dt_bias) and g = d / (dim / ngroups):
+ *
+ *     state[b,d,s] <- exp(dt' * A[d,s]) * state[b,d,s] + dt' * B[b,g,s] * x[b,d]
+ *     out[b,d]      = (sum_s C[b,g,s] * state[b,d,s] + D[d] * x[b,d]) * silu(z[b,d])
+ *
+ * (the contraction uses the updated state).  A Mamba-2 style state
+ * (batch, nheads, headdim, dstate) is this call with dim = nheads * headdim
+ * and every per-head tensor expanded over headdim.  The state is updated in
+ * place and must not overlap any other argument; `out` must not alias an
+ * input.  dstate <= SSM_MAX_DSTATE.  Same conventions and status codes as
+ * ssm_scan_fwd; the update is a pure function of its inputs, so calls on one
+ * stream compose into a sequence of decode steps. */
+int ssm_state_update(const ssm_state_update_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssm_state_update (no HIP call). */
+int ssm_state_update_validate(const ssm_state_update_args_t *args);
+
+/* causal_conv1d_update: the causal conv of causal_conv1d_fwd continued from a
+ * cache of earlier inputs (same guide, section 4.2: single-step incremental
+ * inference over a conv_state cache, with an optional ring buffer indexed by
+ * cache_seqlens).  x: (batch, dim, seqlen) io, the new tokens; conv_state:
+ * (batch, dim, state_len) io, state_len >= width - 1, read and updated in
+ * place; weight: (dim, width) fp32; bias: (dim) fp32 or NULL; out: (batch,
+ * dim, seqlen) io.  For every new token t,
+ *
+ *     out[b,d,t] = round_io(act(bias[d] + sum_k weight[d,k] * h[t - (width-1) + k]))
+ *
+ * where h is the input history: the inputs before the first new token come
+ * from the cache, the rest are x.
+ *  - cache_seqlens == NULL: the cache is ordered oldest first (its last
+ *    width-1 entries precede x[.,.,0]); afterwards it holds the last state_len
+ *    inputs of (cache, x).
+ *  - cache_seqlens != NULL (device pointer, one int32 >= 0 per batch): the
+ *    cache is a ring buffer; token t is written at slot
+ *    (cache_seqlens[b] + t) % state_len and the inputs before it are the
+ *    width-1 slots before that one, circularly.  Other slots are untouched
+ *    and cache_seqlens is not advanced (the caller adds seqlen).
+ * 2 <= width <= SSM_CONV_WIDTH, state_len <= SSM_MAX_CONV_STATE.  x, out and
+ * conv_state must not overlap.  Asynchronous on hip_stream; returns a status
+ * code. */
+int causal_conv1d_update(const void *x, void *conv_state, const float *weight,
+                         const float *bias, const int32_t *cache_seqlens, void *out,
+                         int64_t batch, int64_t dim, int64_t seqlen, int64_t state_len,
+                         int32_t width, int32_t io_dtype, int32_t act, void *hip_stream);
+
+/* Host-only argument check of causal_conv1d_update (no HIP call). */
+int causal_conv1d_update_validate(const void *x, const void *conv_state, const float *weight,
+                                  const void *out, int64_t batch, int64_t dim, int64_t seqlen,
+                                  int64_t state_len, int32_t width, int32_t io_dtype,
+                                  int32_t act);
 
 /* Static text for a status code. */
 const char *ssm_status_str(int status);

@@ -29,6 +29,7 @@ SOURCES = [
     ("scan_bf16.hip", True),
     ("scan_f32.hip", True),
     ("ssm_scan.hip", True),
+    ("decode.hip", True),
     ("validate.cpp", False),
 ]
 

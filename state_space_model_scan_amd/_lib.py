@@ -13,11 +13,14 @@ SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
 SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_WORKSPACE = range(6)
 SSM_MAX_DSTATE = 16
 SSM_CONV_WIDTH = 4
+SSM_MAX_CONV_STATE = 256
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
     "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size",
     "causal_conv1d_fwd", "causal_conv1d_validate",
+    "ssm_state_update", "ssm_state_update_validate",
+    "causal_conv1d_update", "causal_conv1d_update_validate",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
 )
 
@@ -39,6 +42,19 @@ class ScanArgs(ctypes.Structure):
         ("conv_x", _vp), ("conv_weight", _vp), ("conv_bias", _vp),
         ("conv_width", ctypes.c_int32), ("conv_act", ctypes.c_int32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class StateUpdateArgs(ctypes.Structure):
+    """Mirror of ssm_state_update_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("state", _vp), ("x", _vp), ("dt", _vp), ("A", _vp), ("B", _vp), ("C", _vp),
+        ("D", _vp), ("dt_bias", _vp), ("z", _vp),
+        ("dt_softplus", ctypes.c_int32),
+        ("out", _vp),
     ]
 
 
@@ -73,6 +89,16 @@ def lib() -> ctypes.CDLL:
         L.causal_conv1d_fwd.restype = ctypes.c_int
         L.causal_conv1d_validate.argtypes = [_vp, _vp, _vp, i64, i64, i64, i32, i32, i32]
         L.causal_conv1d_validate.restype = ctypes.c_int
+        L.ssm_state_update.argtypes = [ctypes.POINTER(StateUpdateArgs), _vp]
+        L.ssm_state_update.restype = ctypes.c_int
+        L.ssm_state_update_validate.argtypes = [ctypes.POINTER(StateUpdateArgs)]
+        L.ssm_state_update_validate.restype = ctypes.c_int
+        L.causal_conv1d_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, i64, i64, i64, i64,
+                                           i32, i32, i32, _vp]
+        L.causal_conv1d_update.restype = ctypes.c_int
+        L.causal_conv1d_update_validate.argtypes = [_vp, _vp, _vp, _vp, i64, i64, i64, i64,
+                                                    i32, i32, i32]
+        L.causal_conv1d_update_validate.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_hip_error.argtypes = []

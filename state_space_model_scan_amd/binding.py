@@ -180,3 +180,81 @@ def conv1d_selective_scan_fn(x, conv_weight, conv_bias, delta, A, B, C, D=None, 
                        conv_x=x, conv_weight=conv_weight, conv_bias=conv_bias,
                        conv_act=_act_code(activation))
     return (out, last) if return_last_state else out
+
+
+# ---------------------------------------------------------------------------
+# single-step decode
+# ---------------------------------------------------------------------------
+
+def selective_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                           B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                           z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                           dt_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """One decode step (ssm_state_update): updates ``state`` (batch, dim, dstate)
+    float32 in place and returns ``out`` (batch, dim).  x, dt, z: (batch, dim);
+    A: (dim, dstate); B, C: (batch, dstate) or (batch, ngroups, dstate);
+    D, dt_bias: (dim,).  ``state`` must be contiguous: it is written in place."""
+    if not state.is_contiguous() or state.dtype != torch.float32 or state.dim() != 3:
+        raise ValueError("state must be a contiguous float32 (batch, dim, dstate) tensor")
+    x, dt = _dense(x), _dense(dt)
+    io = _IO.get(x.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+    if B.dim() == 2:
+        B = B.unsqueeze(1)
+    if C.dim() == 2:
+        C = C.unsqueeze(1)
+    if B.dim() != 3 or C.dim() != 3 or B.shape[1] != C.shape[1]:
+        raise ValueError("B and C must be (batch, dstate) or (batch, ngroups, dstate) with equal groups")
+    B, C, A, D, z, dt_bias = _dense(B), _dense(C), _dense(A), _dense(D), _dense(z), _dense(dt_bias)
+    for name, t in (("dt", dt), ("z", z), ("B", B), ("C", C)):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError(f"{name} must have the io dtype {x.dtype}, got {t.dtype}")
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {t.dtype}")
+    batch, dim, dstate = state.shape
+    if out is None:
+        out = torch.empty_like(x)
+    a = _lib.StateUpdateArgs()
+    a.batch, a.dim, a.dstate, a.ngroups = batch, dim, dstate, B.shape[1]
+    a.io_dtype = io
+    a.state, a.x, a.dt, a.A, a.B, a.C = _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
+    a.D, a.dt_bias, a.z = _ptr(D), _ptr(dt_bias), _ptr(z)
+    a.dt_softplus = int(bool(dt_softplus))
+    a.out = _ptr(out)
+    check(_lib.lib().ssm_state_update(ctypes.byref(a), _stream(state.device, stream)))
+    return out
+
+
+def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, activation=None,
+                         cache_seqlens: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Conv over new tokens against a cache (causal_conv1d_update): x is
+    (batch, dim) or (batch, dim, seqlen); conv_state (batch, dim, state_len) is
+    updated in place; cache_seqlens (batch,) int32 selects ring-buffer mode.
+    Returns ``out`` shaped like x."""
+    if not conv_state.is_contiguous() or conv_state.dim() != 3:
+        raise ValueError("conv_state must be a contiguous (batch, dim, state_len) tensor")
+    squeeze = x.dim() == 2
+    x = _dense(x.unsqueeze(-1) if squeeze else x)
+    io = _IO.get(x.dtype)
+    if io is None or conv_state.dtype != x.dtype:
+        raise ValueError("x and conv_state must share the io dtype (float32 or bfloat16)")
+    weight, bias = _dense(weight), _dense(bias)
+    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("conv weight and bias must be float32")
+    if cache_seqlens is not None:
+        if cache_seqlens.dtype != torch.int32:
+            raise ValueError("cache_seqlens must be int32")
+        cache_seqlens = _dense(cache_seqlens)
+    batch, dim, seqlen = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    check(_lib.lib().causal_conv1d_update(
+        _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias), _ptr(cache_seqlens), _ptr(out),
+        batch, dim, seqlen, conv_state.shape[2], weight.shape[1], io, _act_code(activation),
+        _stream(x.device, stream)))
+    return out.squeeze(-1) if squeeze else out

@@ -132,6 +132,17 @@ __device__ __forceinline__ void store_n(void *base, int64_t idx, const float (&v
   }
 }
 
+// One io element (bf16: rounded to nearest, ties to even).
+template <bool BF16>
+__device__ __forceinline__ void store_one(void *base, int64_t idx, float v) {
+  if constexpr (BF16) {
+    const __bf16 h = static_cast<__bf16>(v);
+    static_cast<uint16_t *>(base)[idx] = __builtin_bit_cast(uint16_t, h);
+  } else {
+    static_cast<float *>(base)[idx] = v;
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store8(void *base, int64_t idx, const float (&v)[8], int cnt, bool vec) {
   store_n<BF16, 8>(base, idx, v, cnt, vec);

@@ -1,0 +1,15 @@
+// host_util.h -- host helpers shared by the entry points of libssmscan.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ssm {
+
+// Records a failed HIP call for ssm_last_hip_error() and returns SSM_ERR_HIP.
+int hip_fail(hipError_t e);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace ssm

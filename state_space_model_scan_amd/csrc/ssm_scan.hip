@@ -10,10 +10,22 @@
 #include <cstdlib>
 #include <mutex>
 
+#include "host_util.h"
 #include "scan_kernel.h"
 #include "ssmscan.h"
 
 using namespace ssm;
+
+namespace ssm {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return SSM_ERR_HIP;
+}
+
+}  // namespace ssm
 
 namespace {
 
@@ -60,13 +72,6 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-
-thread_local int g_last_hip_error = 0;
-
-int hip_fail(hipError_t e) {
-  g_last_hip_error = static_cast<int>(e);
-  return SSM_ERR_HIP;
-}
 
 int cu_count_cached() {
   static std::mutex mu;
@@ -144,8 +149,6 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
 ScanFn pick(bool bf16, int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
   return bf16 ? pick_scan_bf16(nsw, lpc, bv, cv, conv, mode) : pick_scan_f32(nsw, lpc, bv, cv, conv, mode);
 }
-
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 

@@ -63,12 +63,45 @@ extern "C" int causal_conv1d_validate(const void *x, const float *weight, const 
   return SSM_OK;
 }
 
+// selective_state_update (guide section 4.4 operator list) and
+// causal_conv1d_update (section 4.2): the decode forms of the two operators.
+extern "C" int ssm_state_update_validate(const ssm_state_update_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  if (!positive(a->batch) || !positive(a->dim) || !positive(a->dstate) || !positive(a->ngroups))
+    return SSM_ERR_SHAPE;
+  if (a->dim % a->ngroups != 0) return SSM_ERR_SHAPE;
+  if (!product_fits(a->batch, a->dim, a->dstate) || !product_fits(a->batch, a->ngroups, a->dstate))
+    return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_softplus != 0 && a->dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (!a->state || !a->x || !a->dt || !a->A || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
+extern "C" int causal_conv1d_update_validate(const void *x, const void *conv_state,
+                                             const float *weight, const void *out,
+                                             int64_t batch, int64_t dim, int64_t seqlen,
+                                             int64_t state_len, int32_t width,
+                                             int32_t io_dtype, int32_t act) {
+  if (!positive(batch) || !positive(dim) || !positive(seqlen) || !positive(state_len))
+    return SSM_ERR_SHAPE;
+  if (!product_fits(batch, dim, seqlen) || !product_fits(batch, dim, state_len)) return SSM_ERR_SHAPE;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (width < 2 || width > SSM_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
+  if (state_len < width - 1) return SSM_ERR_SHAPE;
+  if (state_len > SSM_MAX_CONV_STATE) return SSM_ERR_UNSUPPORTED;
+  if (act != SSM_ACT_NONE && act != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!x || !conv_state || !weight || !out) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
 extern "C" const char *ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
     case SSM_ERR_SHAPE: return "bad shape (size <= 0, dim not divisible by ngroups, or too large)";
-    case SSM_ERR_UNSUPPORTED: return "unsupported argument (dtype, dstate > 16, conv width != 4, or enum value)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported argument (dtype, dstate > 16, conv width or cache length out of range, or enum value)";
     case SSM_ERR_HIP: return "HIP runtime error";
     case SSM_ERR_WORKSPACE: return "workspace smaller than required";
     default: return "unknown status";

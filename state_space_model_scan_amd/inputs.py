@@ -80,6 +80,43 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: selective_state_update against a cached fp32 state
+    (batch, dim, dstate) and causal_conv1d_update against a conv cache
+    (batch, dim, conv_state_len) with conv_tokens new tokens."""
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    io_dtype: int
+    ngroups: int = 1
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    softplus: bool = True
+    conv_width: int = 4
+    conv_state_len: int = 3
+    conv_tokens: int = 1
+    seed: int = 0
+
+    @property
+    def channels(self) -> int:
+        return self.batch * self.dim
+
+    def scaled(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# decode2p8b: the Mamba-2.8B-shaped layer of mamba2p8b (d=5120, n=16, g=4,
+# bf16) at a decode batch of 1024, whose 335 MB state exceeds the 256 MB
+# last-level cache, so a step streams the state from HBM.
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    "decode_tiny": DecodeWorkload("decode_tiny", 2, 16, 4, F32, seed=10),
+    "decode2p8b": DecodeWorkload("decode2p8b", 1024, 5120, 16, BF16, ngroups=4, seed=12),
+}
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
     bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
@@ -166,3 +203,31 @@ def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:
     fixed = {r for r in fixed if 0 <= r < total}
     extra = rng.choice(total, size=min(total, max(0, count - len(fixed))), replace=False)
     return np.array(sorted(fixed.union(int(r) for r in extra)), dtype=np.int64)
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw every tensor of decode workload ``w``, in this order:
+    x, dt (N(-2, 0.5)), z, B, C (b, g, n), D, dt_bias (U(-0.1, 0.1)), A
+    (-exp(N(0, 0.5))), state (b, d, n) fp32 N(0, 1), conv x (b, d, conv_tokens),
+    conv state (b, d, conv_state_len), conv weight (N(0, 0.5)), conv bias,
+    cache_seqlens (b,) int32 uniform in [0, 4096).  Same storage rules as
+    ``make_inputs``."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, d, n, g = w.batch, w.dim, w.dstate, w.ngroups
+    io = w.io_dtype
+    t: Dict[str, Optional[np.ndarray]] = {}
+    t["x"] = _store(_normal(rng, (b, d)), io)
+    t["dt"] = _store(_normal(rng, (b, d), -2.0, 0.5), io)
+    t["z"] = _store(_normal(rng, (b, d)), io) if w.has_z else None
+    t["B"] = _store(_normal(rng, (b, g, n)), io)
+    t["C"] = _store(_normal(rng, (b, g, n)), io)
+    t["D"] = _normal(rng, (d,)) if w.has_D else None
+    t["dt_bias"] = _uniform(rng, (d,), -0.1, 0.1) if w.has_bias else None
+    t["A"] = (-np.exp(_normal(rng, (d, n), 0.0, 0.5).astype(np.float64))).astype(np.float32)
+    t["state"] = _normal(rng, (b, d, n))
+    t["conv_x"] = _store(_normal(rng, (b, d, w.conv_tokens)), io)
+    t["conv_state"] = _store(_normal(rng, (b, d, w.conv_state_len)), io)
+    t["conv_weight"] = _normal(rng, (d, w.conv_width), 0.0, 0.5)
+    t["conv_bias"] = _normal(rng, (d,))
+    t["cache_seqlens"] = rng.integers(0, 4096, size=(b,), dtype=np.int32)
+    return t

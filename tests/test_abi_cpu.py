@@ -9,7 +9,7 @@ import re
 import pytest
 
 from state_space_model_scan_amd import _lib
-from state_space_model_scan_amd._lib import ScanArgs
+from state_space_model_scan_amd._lib import ScanArgs, StateUpdateArgs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssmscan.h")
@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 1
+    assert L.ssm_abi_version() == 2
 
 
 def test_status_strings():
@@ -126,3 +126,82 @@ def test_python_binding_errors():
     assert binding._bc_kind(torch.zeros(4, 16), "B") == (_lib.SSM_BC_FIXED, 0)
     assert binding._bc_kind(torch.zeros(2, 16, 8), "B") == (_lib.SSM_BC_VARYING, 1)
     assert binding._bc_kind(torch.zeros(2, 4, 16, 8), "B") == (_lib.SSM_BC_VARYING, 4)
+
+
+# --------------------------------------------------------------------------
+# decode entry points
+# --------------------------------------------------------------------------
+
+def _good_su(**kw):
+    a = StateUpdateArgs()
+    a.batch, a.dim, a.dstate, a.ngroups = 4, 64, 16, 2
+    a.io_dtype = _lib.SSM_BF16
+    a.state = a.x = a.dt = a.A = a.B = a.C = a.out = FAKE
+    a.dt_softplus = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _su(a):
+    return _lib.lib().ssm_state_update_validate(ctypes.byref(a))
+
+
+def test_state_update_validation():
+    L = _lib.lib()
+    assert _su(_good_su()) == _lib.SSM_OK
+    assert _su(_good_su(dstate=1, ngroups=1)) == _lib.SSM_OK
+    assert _su(_good_su(D=FAKE, z=FAKE, dt_bias=FAKE)) == _lib.SSM_OK
+    for field in ("state", "x", "dt", "A", "B", "C", "out"):
+        assert _su(_good_su(**{field: None})) == _lib.SSM_ERR_NULL, field
+    for field, val in (("batch", 0), ("dim", -3), ("dstate", 0), ("ngroups", 0), ("ngroups", 3)):
+        assert _su(_good_su(**{field: val})) == _lib.SSM_ERR_SHAPE, (field, val)
+    assert _su(_good_su(batch=1 << 40, dim=1 << 22)) == _lib.SSM_ERR_SHAPE
+    for kw in (dict(io_dtype=5), dict(dstate=17), dict(dt_softplus=3)):
+        assert _su(_good_su(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
+    assert L.ssm_state_update_validate(None) == _lib.SSM_ERR_NULL
+    # the compute entry point returns the same status before any HIP call
+    assert L.ssm_state_update(ctypes.byref(_good_su(out=None)), None) == _lib.SSM_ERR_NULL
+    assert L.ssm_state_update(None, None) == _lib.SSM_ERR_NULL
+
+
+def test_conv_update_validation():
+    L = _lib.lib()
+    v = L.causal_conv1d_update_validate
+    F32, BF16 = _lib.SSM_F32, _lib.SSM_BF16
+    # x, conv_state, weight, out, batch, dim, seqlen, state_len, width, io, act
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 3, 4, BF16, 1) == _lib.SSM_OK
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 5, 7, 2, F32, 0) == _lib.SSM_OK
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 256, 4, F32, 0) == _lib.SSM_OK
+    for i in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[i] = None
+        assert v(*ptrs, 2, 8, 1, 3, 4, F32, 0) == _lib.SSM_ERR_NULL
+    assert v(FAKE, FAKE, FAKE, FAKE, 0, 8, 1, 3, 4, F32, 0) == _lib.SSM_ERR_SHAPE
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 0, 3, 4, F32, 0) == _lib.SSM_ERR_SHAPE
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 2, 4, F32, 0) == _lib.SSM_ERR_SHAPE    # cache < width-1
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 257, 4, F32, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 3, 5, F32, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 3, 1, F32, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 3, 4, 7, 0) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 3, 4, F32, 2) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.causal_conv1d_update(None, FAKE, FAKE, None, None, FAKE, 2, 8, 1, 3, 4, F32, 0,
+                                  None) == _lib.SSM_ERR_NULL
+
+
+def test_decode_binding_errors():
+    import torch
+    from state_space_model_scan_amd import binding
+    st = torch.zeros(2, 4, 8)
+    x = torch.zeros(2, 4)
+    with pytest.raises(ValueError):   # state must be contiguous float32
+        binding.selective_state_update(st.transpose(1, 2), x, x, torch.zeros(4, 8),
+                                       torch.zeros(2, 8), torch.zeros(2, 8))
+    with pytest.raises(ValueError):   # mismatched B/C groups
+        binding.selective_state_update(st, x, x, torch.zeros(4, 8), torch.zeros(2, 2, 8),
+                                       torch.zeros(2, 4, 8))
+    with pytest.raises(ValueError):   # cache_seqlens must be int32
+        binding.causal_conv1d_update(x, torch.zeros(2, 4, 3), torch.zeros(4, 4),
+                                     cache_seqlens=torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(NotImplementedError):
+        binding.causal_conv1d_update(x, torch.zeros(2, 4, 3), torch.zeros(4, 4), activation="relu")
