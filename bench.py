@@ -57,6 +57,7 @@ HBM_PEAK_GBS = 8000.0
 ALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12       # 78.64 T fp32 lane-ops/s
 CSRC = os.path.join(ROOT, "state_space_model_scan_amd", "csrc")
 KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip", "ssm_scan.hip")
+DECODE_SRCS = ("decode.hip", "device_util.h")
 
 
 def algorithmic_bytes(w) -> int:
@@ -79,19 +80,19 @@ def algorithmic_alu_ops(w) -> float:
     return float(w.elements) * (8 * w.dstate + 26)
 
 
-def kernel_sha() -> str:
+def kernel_sha(srcs=KERNEL_SRCS) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SRCS:
+    for name in srcs:
         h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()
 
 
-def load_traffic(name: str):
+def load_traffic(name: str, srcs=KERNEL_SRCS):
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha256") != kernel_sha():
+    if rec.get("kernel_sha256") != kernel_sha(srcs):
         return None
     return rec.get("traffic_bytes")
 
@@ -290,6 +291,12 @@ def decode_main(args):
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
 
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
     def conv_step():
         binding.causal_conv1d_update(conv_x, conv_state, cw, cb, "silu", None, out=u)
 
@@ -348,7 +355,7 @@ def decode_main(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": su_gbs / HBM_PEAK_GBS,
-            "traffic": load_traffic(w.name),
+            "traffic": load_traffic(w.name, DECODE_SRCS),
             "kernel": "state_update_kernel",
             "kernel_avg_ms": su_s * 1e3,
             "kernel_median_ms": float(np.median(su_ms)),
