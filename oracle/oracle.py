@@ -79,6 +79,9 @@ def _load():
         lib.oracle_causal_conv1d_update.argtypes = [
             i64, i64, i64, i32, i64, i32, p, p, p, p, i32, p, p, p]
         lib.oracle_causal_conv1d_update.restype = i32
+        lib.oracle_ssd_scan.argtypes = [
+            i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, i32, p, p, i32, p, p, p, i32]
+        lib.oracle_ssd_scan.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -233,3 +236,32 @@ def causal_conv1d_update(x, conv_state, weight, bias=None, act=ACT_NONE, cache_s
     if rc != 0:
         raise ValueError(f"oracle_causal_conv1d_update failed with status {rc}")
     return out, new
+
+
+def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, *,
+             io_dtype=F32, initial_states=None, nthreads=0):
+    """Oracle Mamba-2 scan (scalar decay per head), sequential in time.
+
+    x, z: (batch, seqlen, nheads, headdim) io bits; dt: (batch, seqlen, nheads)
+    io bits; A, dt_bias: (nheads,) float32; B, C: (batch, seqlen, ngroups,
+    dstate) io bits; D: (nheads,) or (nheads, headdim) float32;
+    initial_states: (batch, nheads, headdim, dstate) float.
+    Returns (out (batch, seqlen, nheads, headdim) float64,
+             final_states (batch, nheads, headdim, dstate) float64).
+    """
+    lib = _load()
+    x, dt, z = _io(x, io_dtype), _io(dt, io_dtype), _io(z, io_dtype)
+    B, C = _io(B, io_dtype), _io(C, io_dtype)
+    A, D, dt_bias = _f32(A), _f32(D), _f32(dt_bias)
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    init = None if initial_states is None else np.ascontiguousarray(initial_states, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    fin = np.empty((batch, nheads, headdim, dstate), dtype=np.float64)
+    rc = lib.oracle_ssd_scan(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype,
+                             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             int(D is not None and D.ndim == 2), _ptr(z), _ptr(dt_bias),
+                             int(bool(dt_softplus)), _ptr(init), _ptr(out), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_scan failed with status {rc}")
+    return out, fin

@@ -12,7 +12,9 @@
  *     mamba operators, and section 4.2 names causal_conv1d_update (single-step
  *     incremental inference over a conv_state cache with an optional ring
  *     buffer); neither is printed, so both are read as one more step of the
- *     operators above applied to a cache (see each function).
+ *     operators above applied to a cache (see each function); section 4.4
+ *     also lists the Mamba-2 chunk-scan operators, read as the same
+ *     recurrence with a scalar decay per head (oracle_ssd_scan).
  *   - "PaddleNLP Kernel operator library: CUDA and Triton dual-implementation
  *     guide", section 4.1 (selective_scan): the argument list of
  *     selective_scan_fn, the shapes of u/delta (batch,dim,seqlen), A
@@ -399,6 +401,84 @@ int oracle_causal_conv1d_update(int64_t batch, int64_t dim, int64_t seqlen,
     free(buf);
     free(win);
     return 0;
+}
+
+/* ---- Mamba-2 state-space-duality scan ------------------------------------ */
+
+/* The SSD scan of the mamba2 operators listed in section 4.4 of the guide
+ * (mamba_chunk_scan_combined with chunk_state / state_passing).  The pages
+ * name it without printing it; it is read as the recurrence of
+ * selective_scan with a scalar decay per head and a step shared by the
+ * head's channels (the Mamba-2 form), in the layout of those operators:
+ *   x, z, out: (batch, seqlen, nheads, headdim);  dt: (batch, seqlen, nheads)
+ *   A, dt_bias: (nheads);  B, C: (batch, seqlen, ngroups, dstate)
+ *   D: (nheads) or (nheads, headdim);  states: (batch, nheads, headdim, dstate)
+ * Per (b, h), head h in group g = h / (nheads / ngroups), for t in order:
+ *   dt' = softplus(dt + dt_bias) (or dt + dt_bias)
+ *   H[p][n] <- exp(dt' * A[h]) * H[p][n] + dt' * B[b,t,g,n] * x[b,t,h,p]
+ *   y[p]     = sum_n C[b,t,g,n] * H[p][n]
+ *   out      = (y[p] + D * x[b,t,h,p]) * silu(z[b,t,h,p])
+ * H starts at initial_states (zero when NULL); final_states gets the last H.
+ * The chunked evaluation is a reassociation of this sum; the oracle runs the
+ * recurrence in order.  out: (batch*seqlen*nheads*headdim) double;
+ * final_states: (batch*nheads*headdim*dstate) double or NULL. */
+int oracle_ssd_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                    int64_t dstate, int64_t ngroups, int io_dtype, const void *x,
+                    const void *dt, const float *A, const void *B, const void *C,
+                    const float *D, int D_per_channel, const void *z,
+                    const float *dt_bias, int dt_softplus, const double *initial_states,
+                    double *out, double *final_states, int nthreads) {
+    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return 2;
+    if (nheads % ngroups != 0) return 2;
+    if (!x || !dt || !A || !B || !C || !out) return 1;
+    const int64_t hpg = nheads / ngroups;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(|:failed)
+#endif
+    {
+        double *H = (double *)malloc(sizeof(double) * (size_t)(headdim * dstate));
+        if (!H) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t bh = 0; bh < batch * nheads; ++bh) {
+                const int64_t b = bh / nheads, h = bh % nheads, g = h / hpg;
+                const int64_t sbase = bh * headdim * dstate;
+                for (int64_t i = 0; i < headdim * dstate; ++i)
+                    H[i] = initial_states ? initial_states[sbase + i] : 0.0;
+                for (int64_t t = 0; t < seqlen; ++t) {
+                    double step = load_io(dt, io_dtype, (b * seqlen + t) * nheads + h);
+                    if (dt_bias) step += (double)dt_bias[h];
+                    if (dt_softplus) step = oracle_softplus(step);
+                    const double dA = exp(step * (double)A[h]);
+                    const int64_t bcb = ((b * seqlen + t) * ngroups + g) * dstate;
+                    const int64_t xb = ((b * seqlen + t) * nheads + h) * headdim;
+                    for (int64_t pp = 0; pp < headdim; ++pp) {
+                        const double xv = load_io(x, io_dtype, xb + pp);
+                        double y = 0.0;
+                        for (int64_t s = 0; s < dstate; ++s) {
+                            double *hs = &H[pp * dstate + s];
+                            *hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;
+                            y += load_io(C, io_dtype, bcb + s) * *hs;
+                        }
+                        if (D) y += (double)(D_per_channel ? D[h * headdim + pp] : D[h]) * xv;
+                        if (z) y *= oracle_silu(load_io(z, io_dtype, xb + pp));
+                        out[xb + pp] = y;
+                    }
+                }
+                if (final_states)
+                    for (int64_t i = 0; i < headdim * dstate; ++i) final_states[sbase + i] = H[i];
+            }
+        }
+        free(H);
+    }
+    (void)nthreads;
+    return failed ? 5 : 0;
 }
 
 /* Number of threads an OpenMP region would use (1 without OpenMP). */

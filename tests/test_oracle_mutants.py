@@ -144,3 +144,59 @@ def test_decode_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the Mamba-2 scan against its own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_ssd_pins as spins  # noqa: E402
+
+SSD_MUTANTS = {
+    "ssd_group_interleaved": ("h = bh % nheads, g = h / hpg;", "h = bh % nheads, g = h % ngroups;"),
+    "ssd_decay_sign": ("const double dA = exp(step * (double)A[h]);",
+                       "const double dA = exp(-step * (double)A[h]);"),
+    "ssd_contract_old_state": (
+        "*hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;\n"
+        "                            y += load_io(C, io_dtype, bcb + s) * *hs;",
+        "y += load_io(C, io_dtype, bcb + s) * *hs;\n"
+        "                            *hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;"),
+    "ssd_drop_dt_in_input": ("*hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;",
+                             "*hs = dA * *hs + load_io(B, io_dtype, bcb + s) * xv;"),
+    "ssd_D_channel_index": ("D[h * headdim + pp]", "D[pp % nheads * headdim + h % headdim]"),
+    "ssd_ignore_initial": ("H[i] = initial_states ? initial_states[sbase + i] : 0.0;", "H[i] = 0.0;"),
+}
+
+
+def _ssd_pin_calls():
+    F32, BF16 = orc.F32, orc.BF16
+    return [
+        ("flattened_f32", lambda: spins.test_ssd_equals_selective_scan_flattened(F32, 2, True)),
+        ("flattened_bf16", lambda: spins.test_ssd_equals_selective_scan_flattened(BF16, 1, False)),
+        ("dual", lambda: spins.test_ssd_dual_quadratic_form(True)),
+        ("split", spins.test_ssd_split_continuation),
+        ("D_forms", spins.test_ssd_D_per_head_equals_per_channel),
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(SSD_MUTANTS))
+def test_ssd_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = SSD_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _ssd_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
