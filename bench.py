@@ -37,6 +37,13 @@ The value is channel-steps/s (b*d per step); the roofline is HBM for the
 state update, the dominant kernel: the state read and written once, x, dt,
 z, out, B, C once, A/D/dt_bias once (d*n*4 + 2*d*4 bytes, shared by the
 batch), against 8 TB/s.
+
+Mamba-2 workloads (--workload ssd2p7b): a step is one ssd_scan_fwd call.
+The value is elements/s (b*l*h*p).  The roofline is HBM (x, z, out, dt, B, C
+read or written once, plus the small per-head vectors), with the matrix-core
+rate beside it: the chunked form's minimal work per (chunk, head) is
+Q^2 n / 2 + Q^2 p / 2 + 2 Q p n multiply-adds (causal halves of C B^T and
+M X, then C S^T and the state update), against 2.5 PFLOP/s bf16.
 """
 from __future__ import annotations
 
@@ -58,6 +65,8 @@ ALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12       # 78.64 T fp32 lane-ops/s
 CSRC = os.path.join(ROOT, "state_space_model_scan_amd", "csrc")
 KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip", "ssm_scan.hip")
 DECODE_SRCS = ("decode.hip", "device_util.h")
+SSD_SRCS = ("ssd.hip", "device_util.h")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def algorithmic_bytes(w) -> int:
@@ -165,6 +174,9 @@ def main():
     from state_space_model_scan_amd.inputs import BF16, DECODE_WORKLOADS, WORKLOADS, make_inputs
     if args.workload in DECODE_WORKLOADS:
         return decode_main(args)
+    from state_space_model_scan_amd.inputs import SSD_WORKLOADS
+    if args.workload in SSD_WORKLOADS:
+        return ssd_main(args)
 
     def to_dev(a, io_dtype, param=False):
         x = torch.from_numpy(np.ascontiguousarray(a))
@@ -387,6 +399,134 @@ def decode_cpu_baseline(w, t, budget_s: float):
     return {"value": nb * w.dim / dt, "unit": "channel-steps/s", "cores": 1, "kind": "oracle",
             "sample": f"state update of {nb} of {w.batch} batch rows (d={w.dim}, n={w.dstate}), "
                       f"{dt:.2f} s float64 on 1 thread"}
+
+
+
+def ssd_bytes(w) -> int:
+    es = 2
+    xs = w.batch * w.seqlen * w.nheads * w.headdim * es
+    total = xs * (3 if w.has_z else 2)                     # x, out (+ z)
+    total += w.batch * w.seqlen * w.nheads * es             # dt
+    total += 2 * w.batch * w.seqlen * w.ngroups * w.dstate * es   # B, C
+    total += w.nheads * 4 * 3                               # A, D, dt_bias
+    if w.init_state:
+        total += w.batch * w.nheads * w.headdim * w.dstate * 4
+    return total
+
+
+def ssd_flops(w, Q=64) -> float:
+    chunks = -(-w.seqlen // Q)
+    n, p = w.dstate, w.headdim
+    macs = Q * Q * n / 2 + Q * Q * p / 2 + 2 * Q * p * n
+    return 2.0 * macs * chunks * w.batch * w.nheads
+
+
+def ssd_main(args):
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import SSD_WORKLOADS, make_ssd_inputs
+
+    _lib.lib()
+    w = SSD_WORKLOADS[args.workload]
+    t = make_ssd_inputs(w)
+
+    def dev(a, param=False):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16)
+        return x.cuda()
+
+    x, dt, z, B, C = dev(t["x"]), dev(t["dt"]), dev(t["z"]), dev(t["B"]), dev(t["C"])
+    A, D, bias, init = dev(t["A"], True), dev(t["D"], True), dev(t["dt_bias"], True), dev(t["initial_states"], True)
+    out = torch.empty_like(x)
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+
+    def step():
+        binding.ssd_scan_fwd(x, dt, A, B, C, D, z, bias, w.softplus, initial_states=init, out=out,
+                             final_states=fin)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    k_s = float(np.mean(ms)) / 1e3
+    nbytes = ssd_bytes(w) + w.batch * w.nheads * w.headdim * w.dstate * 4   # + final states
+    gbs = nbytes / k_s / 1e9
+    tflops = ssd_flops(w) / k_s / 1e12
+    rec = {
+        "metric": "Mamba-2 chunked scan elements/s (b·l·h·p)",
+        "value": w.elements * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: b={w.batch} l={w.seqlen} h={w.nheads} p={w.headdim} n={w.dstate} "
+                        f"g={w.ngroups}, bf16 io, fp32 state, chunk 64",
+            "elements_per_step": w.elements,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": load_traffic(w.name, SSD_SRCS),
+            "kernel": "ssd_kernel",
+            "kernel_avg_ms": k_s * 1e3,
+            "kernel_median_ms": float(np.median(ms)),
+            "algorithmic_bytes": nbytes,
+            "mfma": {"achieved_TFLOPs": tflops, "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": ssd_flops(w)},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else ssd_cpu_baseline(w, t, args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def ssd_cpu_baseline(w, t, budget_s: float):
+    """The oracle's sequential Mamba-2 scan (all host threads) on a batch slice."""
+    from oracle import oracle as orc
+    nb = 1
+    threads = orc.max_threads()
+    while True:
+        sl = slice(0, nb)
+        t0 = time.perf_counter()
+        orc.ssd_scan(t["x"][sl], t["dt"][sl], t["A"], t["B"][sl], t["C"][sl], t["D"],
+                     None if t["z"] is None else t["z"][sl], t["dt_bias"], w.softplus, io_dtype=w.io_dtype,
+                     nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= min(budget_s, 4.0) or nb == w.batch:
+            break
+        nb = min(w.batch, nb * 2)
+    return {"value": nb * w.seqlen * w.nheads * w.headdim / dt, "unit": "elements/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nb} of {w.batch} batch rows x all {w.nheads} heads x {w.seqlen} tokens, "
+                      f"{dt:.1f} s float64 on {threads} threads"}
 
 
 if __name__ == "__main__":

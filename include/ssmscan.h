@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
 
@@ -213,6 +213,55 @@ int causal_conv1d_update_validate(const void *x, const void *conv_state, const f
                                   const void *out, int64_t batch, int64_t dim, int64_t seqlen,
                                   int64_t state_len, int32_t width, int32_t io_dtype,
                                   int32_t act);
+
+/* ---------------------------------------------------------------------------
+ * Mamba-2 chunked scan (state-space duality form).
+ * ------------------------------------------------------------------------- */
+
+#define SSD_HEADDIM 64     /* the head width the kernel is built for */
+#define SSD_CHUNK 64       /* tokens per chunk of the chunked evaluation */
+
+/* Arguments of ssd_scan_fwd.  Every pointer is a device pointer; x, z, out,
+ * B and C must be 16-byte aligned. */
+typedef struct ssd_scan_args {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups;
+  int32_t io_dtype;               /* SSM_BF16 */
+  const void *x;                  /* (b,l,h,p) io, required */
+  const void *dt;                 /* (b,l,h) io, required */
+  const float *A;                 /* (h) fp32, required */
+  const void *B;                  /* (b,l,g,n) io, required */
+  const void *C;                  /* (b,l,g,n) io, required */
+  const float *D;                 /* (h) or (h,p) fp32, or NULL */
+  int32_t D_per_channel;          /* 1: D is (h,p) */
+  const void *z;                  /* (b,l,h,p) io or NULL */
+  const float *dt_bias;           /* (h) fp32 or NULL */
+  int32_t dt_softplus;            /* 0 or 1 */
+  const float *initial_states;    /* (b,h,p,n) fp32 or NULL (zero) */
+  void *out;                      /* (b,l,h,p) io, required */
+  float *final_states;            /* (b,h,p,n) fp32 or NULL */
+} ssd_scan_args_t;
+
+/* ssd_scan_fwd: the Mamba-2 chunked scan (the guide's section 4.4 lists
+ * mamba_chunk_scan_combined, chunk_state and state_passing among its mamba
+ * operators without printing them; they are read as the selective-scan
+ * recurrence with a scalar decay per head, evaluated chunk by chunk).  For
+ * every (b, h), head h in group g = h / (nheads / ngroups), and token t:
+ *
+ *     dt'          = softplus(dt[b,t,h] + dt_bias[h])   (or without softplus)
+ *     H[p][n]     <- exp(dt' * A[h]) * H[p][n] + dt' * B[b,t,g,n] * x[b,t,h,p]
+ *     out[b,t,h,p] = (sum_n C[b,t,g,n] * H[p][n] + D * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ * with H starting at initial_states and its last value stored to
+ * final_states.  The kernel evaluates each chunk of SSD_CHUNK tokens in the
+ * quadratic (dual) form on the matrix cores -- products of bf16 operands
+ * accumulated in fp32 -- and carries the fp32 state from chunk to chunk.
+ * Supported: io_dtype SSM_BF16, headdim SSD_HEADDIM, dstate 32, 64 or 128;
+ * other values return SSM_ERR_UNSUPPORTED.  Same conventions and status
+ * codes as ssm_scan_fwd. */
+int ssd_scan_fwd(const ssd_scan_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssd_scan_fwd (no HIP call). */
+int ssd_scan_validate(const ssd_scan_args_t *args);
 
 /* Static text for a status code. */
 const char *ssm_status_str(int status);

@@ -30,6 +30,7 @@ SOURCES = [
     ("scan_f32.hip", True),
     ("ssm_scan.hip", True),
     ("decode.hip", True),
+    ("ssd.hip", True),
     ("validate.cpp", False),
 ]
 

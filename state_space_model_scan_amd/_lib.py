@@ -14,6 +14,8 @@ SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_W
 SSM_MAX_DSTATE = 16
 SSM_CONV_WIDTH = 4
 SSM_MAX_CONV_STATE = 256
+SSD_HEADDIM = 64
+SSD_CHUNK = 64
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
@@ -21,6 +23,7 @@ EXPORTS = (
     "causal_conv1d_fwd", "causal_conv1d_validate",
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
+    "ssd_scan_fwd", "ssd_scan_validate",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
 )
 
@@ -55,6 +58,19 @@ class StateUpdateArgs(ctypes.Structure):
         ("D", _vp), ("dt_bias", _vp), ("z", _vp),
         ("dt_softplus", ctypes.c_int32),
         ("out", _vp),
+    ]
+
+
+class SsdArgs(ctypes.Structure):
+    """Mirror of ssd_scan_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("x", _vp), ("dt", _vp), ("A", _vp), ("B", _vp), ("C", _vp),
+        ("D", _vp), ("D_per_channel", ctypes.c_int32),
+        ("z", _vp), ("dt_bias", _vp), ("dt_softplus", ctypes.c_int32),
+        ("initial_states", _vp), ("out", _vp), ("final_states", _vp),
     ]
 
 
@@ -99,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.causal_conv1d_update_validate.argtypes = [_vp, _vp, _vp, _vp, i64, i64, i64, i64,
                                                     i32, i32, i32]
         L.causal_conv1d_update_validate.restype = ctypes.c_int
+        L.ssd_scan_fwd.argtypes = [ctypes.POINTER(SsdArgs), _vp]
+        L.ssd_scan_fwd.restype = ctypes.c_int
+        L.ssd_scan_validate.argtypes = [ctypes.POINTER(SsdArgs)]
+        L.ssd_scan_validate.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_hip_error.argtypes = []

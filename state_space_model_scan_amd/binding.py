@@ -258,3 +258,45 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
         batch, dim, seqlen, conv_state.shape[2], weight.shape[1], io, _act_code(activation),
         _stream(x.device, stream)))
     return out.squeeze(-1) if squeeze else out
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 chunked scan
+# ---------------------------------------------------------------------------
+
+def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                 initial_states: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 final_states: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Enqueue ssd_scan_fwd; returns ``out`` (batch, seqlen, nheads, headdim).
+
+    x, z: (batch, seqlen, nheads, headdim) bf16; dt: (batch, seqlen, nheads) bf16;
+    A, dt_bias: (nheads,) float32; B, C: (batch, seqlen, ngroups, dstate) bf16;
+    D: (nheads,) or (nheads, headdim) float32; initial_states / final_states:
+    (batch, nheads, headdim, dstate) float32."""
+    x, dt, B, C = _dense(x), _dense(dt), _dense(B), _dense(C)
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"ssd_scan_fwd takes bfloat16 io, got {x.dtype}")
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError(f"{name} must have the io dtype {x.dtype}, got {t.dtype}")
+    A, D, z, dt_bias, initial_states = _dense(A), _dense(D), _dense(z), _dense(dt_bias), _dense(initial_states)
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias), ("initial_states", initial_states)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {t.dtype}")
+    batch, seqlen, nheads, headdim = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    a = _lib.SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim = batch, seqlen, nheads, headdim
+    a.dstate, a.ngroups = B.shape[3], B.shape[2]
+    a.io_dtype = _lib.SSM_BF16
+    a.x, a.dt, a.A, a.B, a.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
+    a.D = _ptr(D)
+    a.D_per_channel = int(D is not None and D.dim() == 2)
+    a.z, a.dt_bias = _ptr(z), _ptr(dt_bias)
+    a.dt_softplus = int(bool(dt_softplus))
+    a.initial_states, a.out, a.final_states = _ptr(initial_states), _ptr(out), _ptr(final_states)
+    check(_lib.lib().ssd_scan_fwd(ctypes.byref(a), _stream(x.device, stream)))
+    return out

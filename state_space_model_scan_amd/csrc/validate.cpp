@@ -96,6 +96,30 @@ extern "C" int causal_conv1d_update_validate(const void *x, const void *conv_sta
   return SSM_OK;
 }
 
+// Mamba-2 chunked scan (guide section 4.4 operator list).
+extern "C" int ssd_scan_validate(const ssd_scan_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  if (!positive(a->batch) || !positive(a->seqlen) || !positive(a->nheads) ||
+      !positive(a->headdim) || !positive(a->dstate) || !positive(a->ngroups))
+    return SSM_ERR_SHAPE;
+  if (a->nheads % a->ngroups != 0) return SSM_ERR_SHAPE;
+  if (!product_fits(a->batch * a->seqlen, a->nheads, a->headdim) ||
+      !product_fits(a->batch * a->seqlen, a->ngroups, a->dstate) ||
+      !product_fits(a->batch, a->nheads, a->headdim * a->dstate))
+    return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->headdim != SSD_HEADDIM) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate != 32 && a->dstate != 64 && a->dstate != 128) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_softplus != 0 && a->dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->D_per_channel != 0 && a->D_per_channel != 1) return SSM_ERR_UNSUPPORTED;
+  if (!a->x || !a->dt || !a->A || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
+  const uintptr_t mis = (reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->B) |
+                         reinterpret_cast<uintptr_t>(a->C) | reinterpret_cast<uintptr_t>(a->out) |
+                         reinterpret_cast<uintptr_t>(a->z)) & 15u;
+  if (mis) return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
 extern "C" const char *ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";

@@ -117,6 +117,48 @@ DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    """The Mamba-2 chunked scan: x, z (batch, seqlen, nheads, headdim), dt
+    (batch, seqlen, nheads), B, C (batch, seqlen, ngroups, dstate), A, dt_bias
+    (nheads), D (nheads) or (nheads, headdim), states (batch, nheads, headdim,
+    dstate)."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    io_dtype: int = 1
+    has_z: bool = True
+    has_D: bool = True
+    D_per_channel: bool = False
+    has_bias: bool = True
+    softplus: bool = True
+    init_state: bool = False
+    seed: int = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+    def scaled(self, **kw) -> "SsdWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# ssd2p7b: a Mamba-2 2.7B-shaped layer (d_inner 5120 = 80 heads of 64, dstate
+# 128, one B/C group) at batch 8 and 2048 tokens, bf16.
+SSD_WORKLOADS: Dict[str, "SsdWorkload"] = {
+    "ssd_tiny": SsdWorkload("ssd_tiny", 1, 100, 4, 64, 32, 2, init_state=True, seed=20),
+    "ssd2p7b": SsdWorkload("ssd2p7b", 8, 2048, 80, 64, 128, 1, seed=22),
+}
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
     bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
@@ -230,4 +272,29 @@ def make_decode_inputs(w: DecodeWorkload, seed: Optional[int] = None) -> Dict[st
     t["conv_weight"] = _normal(rng, (d, w.conv_width), 0.0, 0.5)
     t["conv_bias"] = _normal(rng, (d,))
     t["cache_seqlens"] = rng.integers(0, 4096, size=(b,), dtype=np.int32)
+    return t
+
+
+def make_ssd_inputs(w: SsdWorkload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw every tensor of the Mamba-2 workload ``w``, in this order:
+    x, dt (N(-3, 0.5): with softplus and the bias a step near 0.05), z, B, C,
+    D (N(0, 1), per head or per channel), dt_bias (U(-0.1, 0.1)), A
+    (-U(1, 16) per head), initial states (N(0, 1), when the workload has
+    them).  Same storage rules as ``make_inputs``."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, l, h, p, n, g = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    io = w.io_dtype
+    t: Dict[str, Optional[np.ndarray]] = {}
+    t["x"] = _store(_normal(rng, (b, l, h, p)), io)
+    t["dt"] = _store(_normal(rng, (b, l, h), -3.0, 0.5), io)
+    t["z"] = _store(_normal(rng, (b, l, h, p)), io) if w.has_z else None
+    t["B"] = _store(_normal(rng, (b, l, g, n)), io)
+    t["C"] = _store(_normal(rng, (b, l, g, n)), io)
+    if w.has_D:
+        t["D"] = _normal(rng, (h, p) if w.D_per_channel else (h,))
+    else:
+        t["D"] = None
+    t["dt_bias"] = _uniform(rng, (h,), -0.1, 0.1) if w.has_bias else None
+    t["A"] = -_uniform(rng, (h,), 1.0, 16.0)
+    t["initial_states"] = _normal(rng, (b, h, p, n)) if w.init_state else None
     return t

@@ -9,7 +9,7 @@ import re
 import pytest
 
 from state_space_model_scan_amd import _lib
-from state_space_model_scan_amd._lib import ScanArgs, StateUpdateArgs
+from state_space_model_scan_amd._lib import ScanArgs, SsdArgs, StateUpdateArgs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssmscan.h")
@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 2
+    assert L.ssm_abi_version() == 3
 
 
 def test_status_strings():
@@ -205,3 +205,30 @@ def test_decode_binding_errors():
                                      cache_seqlens=torch.zeros(2, dtype=torch.int64))
     with pytest.raises(NotImplementedError):
         binding.causal_conv1d_update(x, torch.zeros(2, 4, 3), torch.zeros(4, 4), activation="relu")
+
+
+def _good_ssd(**kw):
+    a = SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.ngroups = 2, 128, 8, 64, 128, 2
+    a.io_dtype = _lib.SSM_BF16
+    a.x = a.dt = a.A = a.B = a.C = a.out = 0x1000
+    a.dt_softplus = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_ssd_validation():
+    L = _lib.lib()
+    v = lambda a: L.ssd_scan_validate(ctypes.byref(a))
+    assert v(_good_ssd()) == _lib.SSM_OK
+    assert v(_good_ssd(dstate=32, ngroups=1, z=0x2000, D=0x3000, D_per_channel=1)) == _lib.SSM_OK
+    for field in ("x", "dt", "A", "B", "C", "out"):
+        assert v(_good_ssd(**{field: None})) == _lib.SSM_ERR_NULL, field
+    for field, val in (("batch", 0), ("seqlen", -1), ("nheads", 0), ("ngroups", 3), ("dstate", 0)):
+        assert v(_good_ssd(**{field: val})) == _lib.SSM_ERR_SHAPE, (field, val)
+    for kw in (dict(io_dtype=_lib.SSM_F32), dict(headdim=32), dict(dstate=16), dict(dstate=96),
+               dict(dt_softplus=2), dict(D_per_channel=5), dict(x=0x1002), dict(z=0x1008)):
+        assert v(_good_ssd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
+    assert L.ssd_scan_fwd(ctypes.byref(_good_ssd(B=None)), None) == _lib.SSM_ERR_NULL
+    assert L.ssd_scan_validate(None) == _lib.SSM_ERR_NULL

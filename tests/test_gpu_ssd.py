@@ -1,0 +1,122 @@
+"""GPU parity of the Mamba-2 chunked scan (ssd_scan_fwd) against the float64
+oracle's sequential recurrence, through the C ABI.
+
+The kernel evaluates each 64-token chunk in the quadratic form on the matrix
+cores (bf16 operands, fp32 accumulation), so the bar is the bf16 io
+tolerance of the harness: |gpu - ref| <= 2e-2 * (1 + |ref|) for out and for
+the final states.  At full size the oracle runs on a sample of heads (each
+head is an independent scan of its group's B and C).
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from state_space_model_scan_amd.inputs import BF16, SSD_WORKLOADS, make_ssd_inputs
+from tests.harness import TOL, log, max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(w, t, final=True):
+    import torch
+    from state_space_model_scan_amd import binding
+    x = to_dev(t["x"], BF16)
+    out = torch.empty_like(x).fill_(float("nan"))
+    fin = None
+    if final:
+        fin = torch.full((w.batch, w.nheads, w.headdim, w.dstate), float("nan"), dtype=torch.float32,
+                         device="cuda")
+    binding.ssd_scan_fwd(x, to_dev(t["dt"], BF16), to_dev(t["A"], param=True), to_dev(t["B"], BF16),
+                         to_dev(t["C"], BF16), to_dev(t["D"], param=True), to_dev(t["z"], BF16),
+                         to_dev(t["dt_bias"], param=True), w.softplus,
+                         initial_states=to_dev(t["initial_states"], param=True), out=out,
+                         final_states=fin)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    f = None if fin is None else fin.cpu().numpy().astype(np.float64)
+    return o, f
+
+
+def _oracle(w, t, heads=None):
+    """Oracle on all heads, or on the listed heads only (returned in that order
+    along the head axis)."""
+    if heads is None:
+        return orc.ssd_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"],
+                            w.softplus, io_dtype=BF16, initial_states=t["initial_states"])
+    hpg = w.nheads // w.ngroups
+    outs, fins = [], []
+    for h in heads:
+        g = h // hpg
+        sl = lambda a, ax: None if a is None else np.ascontiguousarray(np.take(a, [h], axis=ax))
+        D = t["D"]
+        Dh = None if D is None else np.ascontiguousarray(D[[h]])
+        o, f = orc.ssd_scan(sl(t["x"], 2), sl(t["dt"], 2), t["A"][[h]],
+                            np.ascontiguousarray(t["B"][:, :, [g]]), np.ascontiguousarray(t["C"][:, :, [g]]),
+                            Dh, sl(t["z"], 2), None if t["dt_bias"] is None else t["dt_bias"][[h]],
+                            w.softplus, io_dtype=BF16,
+                            initial_states=None if t["initial_states"] is None else sl(t["initial_states"], 1),
+                            nthreads=0)
+        outs.append(o)
+        fins.append(f)
+    return np.concatenate(outs, axis=2), np.concatenate(fins, axis=1)
+
+
+def _check(w, t, what, heads=None):
+    log(f"[ssd] {what}: b={w.batch} l={w.seqlen} h={w.nheads} p={w.headdim} n={w.dstate} g={w.ngroups}")
+    out, fin = _gpu(w, t)
+    ref, ref_fin = _oracle(w, t, heads)
+    if heads is not None:
+        out, fin = out[:, :, heads], fin[:, heads]
+    tol = TOL[BF16]
+    eo, ef = max_err(out, ref), max_err(fin, ref_fin)
+    assert eo <= tol, f"{what} out: {eo:.3e} > {tol:.0e}"
+    assert ef <= tol, f"{what} final states: {ef:.3e} > {tol:.0e}"
+    return eo, ef
+
+
+def test_ssd_tiny():
+    w = SSD_WORKLOADS["ssd_tiny"]
+    _check(w, make_ssd_inputs(w), "ssd_tiny")
+
+
+@pytest.mark.parametrize("n", [32, 64, 128])
+@pytest.mark.parametrize("seqlen", [1, 63, 64, 65, 200])
+def test_ssd_sizes(n, seqlen):
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=2, seqlen=seqlen, nheads=4, dstate=n, ngroups=2,
+                                         seed=200 + n + seqlen)
+    _check(w, make_ssd_inputs(w), f"n={n} l={seqlen}")
+
+
+@pytest.mark.parametrize("flags", [dict(has_z=False), dict(has_D=False), dict(D_per_channel=True),
+                                   dict(has_bias=False), dict(softplus=False), dict(init_state=False),
+                                   dict(has_z=False, has_D=False, has_bias=False, init_state=False)])
+def test_ssd_optional_inputs(flags):
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=1, seqlen=130, nheads=4, dstate=64, ngroups=1, seed=7,
+                                         **flags)
+    t = make_ssd_inputs(w)
+    if not w.softplus:   # keep dt' = dt + bias a positive step
+        import state_space_model_scan_amd.inputs as inp
+        t["dt"] = inp.f32_to_bf16_bits(0.11 + np.abs(inp.bf16_bits_to_f32(t["dt"])) * 0.02)
+    _check(w, t, f"flags={flags}")
+
+
+@pytest.mark.parametrize("groups", [1, 2, 4])
+def test_ssd_groups(groups):
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=2, seqlen=96, nheads=8, dstate=32, ngroups=groups,
+                                         seed=30 + groups)
+    _check(w, make_ssd_inputs(w), f"groups={groups}")
+
+
+def test_ssd_long_decay_carry():
+    # small |A| and steps: the state carries across many chunks
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=1, seqlen=1024, nheads=2, dstate=64, ngroups=1,
+                                         init_state=True, seed=41)
+    t = make_ssd_inputs(w)
+    t["A"] = np.array([-0.01, -0.05], np.float32)
+    _check(w, t, "slow decay")
+
+
+def test_ssd_full_size_sampled_heads():
+    w = SSD_WORKLOADS["ssd2p7b"]
+    t = make_ssd_inputs(w)
+    _check(w, t, "ssd2p7b", heads=[0, 37, 79])
