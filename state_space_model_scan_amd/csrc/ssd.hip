@@ -23,14 +23,17 @@
 // across chunks, with its hi/lo copy in LDS as the operand of C S^T.
 //
 // Work decomposition: one 256-thread workgroup (four waves) per (batch,
-// head), walking the chunks in order.  Wave w owns rows [16w, 16w+16) of the
-// chunk's tokens for M and Y, and rows [16w, 16w+16) of the head's channels
-// for the state.  Operand layout of the 16x16x32 instruction (checked on the
+// head), walking the chunks in order.  Wave w owns the chunk's tokens
+// [16w, 16w+16) for M and Y, and the head's channels [16w, 16w+16) for the
+// state.  Operand layout of the 16x16x32 instruction (checked on the
 // device): lane l holds A[l%16][8(l/16)+i] and B[8(l/16)+i][l%16] for
-// i < 8, and accumulator i is D[4(l/16)+i][l%16].  LDS matrices are stored
-// row-major with each row's 16-byte groups XOR-swizzled by the row index, so
-// the operand reads (8 consecutive elements of 16 different rows) spread
-// over the banks without padding.
+// i < 8, and accumulator i is D[4(l/16)+i][l%16].  The products are taken
+// transposed (G^T = B C^T, Y^T, S^T) so that each lane's four accumulators
+// are consecutive elements of one LDS row and go out in one store.  LDS
+// matrices are row-major with each row's 16-byte groups permuted by the row
+// index, so the operand reads and the transposed staging stores of X and B
+// spread over the banks without padding (measured: bank conflicts were the
+// largest stall before this layout).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -58,10 +61,15 @@ struct SsdParams {
 };
 
 // element offset of (row, col) in a row-major LDS matrix whose rows hold
-// row_len elements, 16-byte groups swizzled by the row
+// ROW_LEN bf16 elements: the row's 16-byte groups are permuted by
+// (row ^ row / 8) mod 8, so that both the operand reads (16 rows, one group
+// each) and the transposed stores (8 rows 8 apart, 8 consecutive columns)
+// spread over the banks
 template <int ROW_LEN>
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * ROW_LEN + (col ^ (((row & 7) << 3) & (ROW_LEN - 1)));
+  constexpr int GROUPS = ROW_LEN / 8;
+  const int gsw = ((row ^ (row >> 3)) & 7) & (GROUPS - 1);
+  return row * ROW_LEN + (col ^ (gsw << 3));
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
@@ -116,52 +124,64 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   const uint16_t *dtb = p.dt + b * L * p.nheads + h;
   const bf16x8 zero8 = {};
 
-  // D of the channels this thread stores (8 * (tid % 8) + 0..7)
+  // Token pairs and channel groups this thread stages and stores:
+  // tokens 2 (tid / 8) + {0, 1}, channels 8 (tid % 8) + 0..7.
+  const int xt0 = 2 * (tid >> 3), xp0 = (tid & 7) * 8;
+  // D of those channels
   float Dv8[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int pp = (tid & 7) * 8 + i;
+    const int pp = xp0 + i;
     Dv8[i] = p.D ? (p.D_per_channel ? p.D[h * kP + pp] : p.D[h]) : 0.0f;
   }
+  float *sY = reinterpret_cast<float *>(&sM[0][0]);   // Y [t][p] (fp32), 16-byte groups permuted by t
 
-  // state: wave w holds S[16w + 4kq + i][16 nt + r]
+  // state, transposed: wave w holds S[p = 16w + r][n = 16 nt + 4kq + i]
   f32x4 accs[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    const int pp = 16 * w + r;
+    uint16_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pp = 16 * w + 4 * kq + i, n = 16 * nt + r;
+      const int n = 16 * nt + 4 * kq + i;
       const float v = p.init ? p.init[(bh * kP + pp) * N + n] : 0.0f;
       accs[nt][i] = v;
-      split_bf(v, sS[0][swz<N>(pp, n)], sS[1][swz<N>(pp, n)]);
+      split_bf(v, hi[i], lo[i]);
     }
+    const int o = swz<N>(pp, 16 * nt + 4 * kq);
+    *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   }
   __syncthreads();
 
   const int64_t nchunks = (L + kQ - 1) / kQ;
-  constexpr int BSEG = kQ * (N / 8) / 256;   // 16-byte pieces of the B tile per thread
+  constexpr int G8 = N / 8;                      // 16-byte groups per B row
+  constexpr int BPIECES = (kQ / 2) * G8;        // (token pair, 16-byte group) pieces of a B tile
+  constexpr int BPAIRS = (BPIECES + 255) / 256;  // pieces per thread
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>((L - t0 < kQ) ? L - t0 : kQ);
 
-    // ---- every global load of the chunk first, so their latencies overlap:
-    // x and z (thread: tokens tid/8 and tid/8 + 32, channels 8*(tid%8)..+7),
-    // the B tile, this wave's C rows (tokens 16w + r), and the steps
-    uint4 xr[2], zr[2], br[BSEG];
+    // ---- every global load of the chunk first, so their latencies overlap
+    uint4 xr[2], zr[2], br[BPAIRS][2];
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int t = (tid >> 3) + 32 * rep, p0 = (tid & 7) * 8;
-      const int64_t e = (t0 + t) * xrow + p0;
-      xr[rep] = t < len ? ld8_raw(xb + e) : make_uint4(0, 0, 0, 0);
-      zr[rep] = (zb && t < len) ? ld8_raw(zb + e) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < 2; ++k) {
+      const int t = xt0 + k;
+      const int64_t e = (t0 + t) * xrow + xp0;
+      xr[k] = t < len ? ld8_raw(xb + e) : make_uint4(0, 0, 0, 0);
+      zr[k] = (zb && t < len) ? ld8_raw(zb + e) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < BSEG; ++j) {
-      const int seg = tid + 256 * j;
-      const int t = seg / (N / 8), n0 = (seg % (N / 8)) * 8;
-      br[j] = t < len ? ld8_raw(Bb + (t0 + t) * bcrow + n0) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < BPAIRS; ++j) {
+      const int piece = tid + 256 * j;
+      const int t = 2 * (piece / G8), n0 = (piece % G8) * 8;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        br[j][k] = (piece < BPIECES && t + k < len) ? ld8_raw(Bb + (t0 + t + k) * bcrow + n0)
+                                                     : make_uint4(0, 0, 0, 0);
     }
-    bf16x8 cop[KN];
+    bf16x8 cop[KN];   // this wave's C rows (tokens 16w + r)
     {
       const int t = 16 * w + r;
 #pragma unroll
@@ -170,21 +190,25 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     float dtraw = 0.0f;
     if (w == 0 && l < len) dtraw = bf2f(dtb[(t0 + l) * p.nheads]);
 
-    // ---- X^T and B^T into LDS; the steps and their running sum inside the
-    // chunk (padding: dt' = 0)
+    // ---- X^T and B^T into LDS, two tokens per 32-bit store
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int t = (tid >> 3) + 32 * rep, p0 = (tid & 7) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sXT[swz<kQ>(p0 + i, t)] = raw_bits(xr[rep], i);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = static_cast<uint32_t>(raw_bits(xr[0], i)) | (static_cast<uint32_t>(raw_bits(xr[1], i)) << 16);
+      *reinterpret_cast<uint32_t *>(&sXT[swz<kQ>(xp0 + i, xt0)]) = v;
     }
 #pragma unroll
-    for (int j = 0; j < BSEG; ++j) {
-      const int seg = tid + 256 * j;
-      const int t = seg / (N / 8), n0 = (seg % (N / 8)) * 8;
+    for (int j = 0; j < BPAIRS; ++j) {
+      const int piece = tid + 256 * j;
+      if (piece >= BPIECES) break;
+      const int t = 2 * (piece / G8), n0 = (piece % G8) * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sBT[swz<kQ>(n0 + i, t)] = raw_bits(br[j], i);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t v = static_cast<uint32_t>(raw_bits(br[j][0], i)) |
+                           (static_cast<uint32_t>(raw_bits(br[j][1], i)) << 16);
+        *reinterpret_cast<uint32_t *>(&sBT[swz<kQ>(n0 + i, t)]) = v;
+      }
     }
+    // ---- the steps and their running sum inside the chunk (padding: dt' = 0)
     if (w == 0) {
       float dtp = 0.0f;
       if (l < len) {
@@ -205,31 +229,38 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     const float csl = sCs[kQ - 1];
     // the state-update weights w_t = exp(cs_last - cs_t) * dt'_t
     if (tid < kQ) sW[tid] = fast_exp2((csl - sCs[tid]) * kLog2e) * sDt[tid];
-    // ---- M: this wave's rows of C B^T, masked to tau <= t and decayed (the
-    // B operand rows were just read into L2 by the tile load)
+    // ---- M, from G^T = B C^T: lane holds G[t = 16w + r][tau = 16 tb + 4kq + i],
+    // masked to tau <= t, decayed, split, stored as 4 consecutive tau
+    {
+      const int t = 16 * w + r;
+      const float cst = sCs[t];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int tau = 16 * tb + r;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (tb <= w) {
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (tb <= w) {
+          const int tau_row = 16 * tb + r;   // the B row this lane feeds as A operand
 #pragma unroll
-        for (int kk = 0; kk < KN; ++kk) {
-          const bf16x8 bop = tau < len ? ld8(Bb + (t0 + tau) * bcrow + 32 * kk + 8 * kq) : zero8;
-          acc = mfma(cop[kk], bop, acc);
+          for (int kk = 0; kk < KN; ++kk) {
+            const bf16x8 bop = tau_row < len ? ld8(Bb + (t0 + tau_row) * bcrow + 32 * kk + 8 * kq) : zero8;
+            acc = mfma(bop, cop[kk], acc);
+          }
         }
-      }
-      const float cst = sCs[tau], dtt = sDt[tau];
+        uint16_t hi[4], lo[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * w + 4 * kq + i;
-        float m = 0.0f;
-        if (tb <= w && tau <= t) m = acc[i] * fast_exp2((sCs[t] - cst) * kLog2e) * dtt;
-        split_bf(m, sM[0][swz<kQ>(t, tau)], sM[1][swz<kQ>(t, tau)]);
+        for (int i = 0; i < 4; ++i) {
+          const int tau = 16 * tb + 4 * kq + i;
+          float m = 0.0f;
+          if (tb <= w && tau <= t) m = acc[i] * fast_exp2((cst - sCs[tau]) * kLog2e) * sDt[tau];
+          split_bf(m, hi[i], lo[i]);
+        }
+        const int o = swz<kQ>(t, 16 * tb + 4 * kq);
+        *reinterpret_cast<uint2 *>(&sM[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+        *reinterpret_cast<uint2 *>(&sM[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
       }
     }
     __syncthreads();
 
-    // ---- Y = diag(exp(cs)) C S^T + M X for this wave's tokens
+    // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T: lane holds Y[t = 16w + r][p = 16 pb + 4kq + i]
     f32x4 accy[4];
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
@@ -237,15 +268,14 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
         const int o = swz<N>(16 * pb + r, 32 * kk + 8 * kq);
-        accy[pb] = mfma(cop[kk], ld8(&sS[0][o]), accy[pb]);
-        accy[pb] = mfma(cop[kk], ld8(&sS[1][o]), accy[pb]);
+        accy[pb] = mfma(ld8(&sS[0][o]), cop[kk], accy[pb]);
+        accy[pb] = mfma(ld8(&sS[1][o]), cop[kk], accy[pb]);
       }
     }
+    {
+      const float e = fast_exp2(sCs[16 * w + r] * kLog2e);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = fast_exp2(sCs[16 * w + 4 * kq + i] * kLog2e);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) accy[pb][i] *= e;
+      for (int pb = 0; pb < 4; ++pb) accy[pb] *= e;
     }
     const int kkmax = (16 * (w + 1) + 31) / 32;   // tau blocks at or before this wave's tokens
     for (int kk = 0; kk < kkmax; ++kk) {
@@ -254,26 +284,29 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         const bf16x8 xop = ld8(&sXT[swz<kQ>(16 * pb + r, 32 * kk + 8 * kq)]);
-        accy[pb] = mfma(mhi, xop, accy[pb]);
-        accy[pb] = mfma(mlo, xop, accy[pb]);
+        accy[pb] = mfma(xop, mhi, accy[pb]);
+        accy[pb] = mfma(xop, mlo, accy[pb]);
       }
     }
     __syncthreads();   // every read of M and of the old state is done
 
-    // ---- Y into LDS (over M) for a coalesced epilogue
-    float *sY = reinterpret_cast<float *>(&sM[0][0]);
+    // ---- Y into LDS (over M), four consecutive channels per store
+    {
+      const int t = 16 * w + r;
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sY[(16 * w + 4 * kq + i) * kP + 16 * pb + r] = accy[pb][i];
+      for (int pb = 0; pb < 4; ++pb) {
+        const int grp = (4 * pb + kq) ^ (t & 15);   // 16-byte group of channels 16pb + 4kq, permuted by t
+        *reinterpret_cast<float4 *>(&sY[t * kP + 4 * grp]) =
+            make_float4(accy[pb][0], accy[pb][1], accy[pb][2], accy[pb][3]);
+      }
     }
-    // ---- S <- exp(cs_last) S + (X w)^T B
+    // ---- S^T <- exp(cs_last) S^T + B^T (X w)
     const float dec = fast_exp2(csl * kLog2e);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) accs[nt] *= dec;
 #pragma unroll
     for (int kk = 0; kk < kQ / 32; ++kk) {
-      // A operand: this wave's rows of (X w)^T, split into hi / lo
+      // B operand: (X w) at tokens 32kk + 8kq + i, channel 16w + r, split hi / lo
       const uint4 xt = ld8_raw(&sXT[swz<kQ>(16 * w + r, 32 * kk + 8 * kq)]);
       bf16x8 xhi, xlo;
 #pragma unroll
@@ -286,42 +319,44 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8 bop = ld8(&sBT[swz<kQ>(16 * nt + r, 32 * kk + 8 * kq)]);
-        accs[nt] = mfma(xhi, bop, accs[nt]);
-        accs[nt] = mfma(xlo, bop, accs[nt]);
+        accs[nt] = mfma(bop, xhi, accs[nt]);
+        accs[nt] = mfma(bop, xlo, accs[nt]);
       }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      uint16_t hi[4], lo[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = swz<N>(16 * w + 4 * kq + i, 16 * nt + r);
-        split_bf(accs[nt][i], sS[0][o], sS[1][o]);
-      }
+      for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
+      const int o = swz<N>(16 * w + r, 16 * nt + 4 * kq);
+      *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
     __syncthreads();
 
     // ---- out = (Y + D x) * silu(z): this thread's x / z pieces, 16-byte stores
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int t = (tid >> 3) + 32 * rep, p0 = (tid & 7) * 8;
+    for (int k = 0; k < 2; ++k) {
+      const int t = xt0 + k;
       if (t < len) {
-        const float4 y0 = *reinterpret_cast<const float4 *>(&sY[t * kP + p0]);
-        const float4 y1 = *reinterpret_cast<const float4 *>(&sY[t * kP + p0 + 4]);
+        const int g0 = (xp0 >> 2) ^ (t & 15), g1 = ((xp0 >> 2) + 1) ^ (t & 15);
+        const float4 y0 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g0]);
+        const float4 y1 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g1]);
         const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           float o2[2];
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            float y = yv[i + k];
-            if (p.D) y = fmaf(Dv8[i + k], bf2f(raw_bits(xr[rep], i + k)), y);
-            if (zb) y *= silu_f(bf2f(raw_bits(zr[rep], i + k)));
-            o2[k] = y;
+          for (int q2 = 0; q2 < 2; ++q2) {
+            float y = yv[i + q2];
+            if (p.D) y = fmaf(Dv8[i + q2], bf2f(raw_bits(xr[k], i + q2)), y);
+            if (zb) y *= silu_f(bf2f(raw_bits(zr[k], i + q2)));
+            o2[q2] = y;
           }
           pk[i / 2] = static_cast<uint32_t>(f2bf(o2[0])) | (static_cast<uint32_t>(f2bf(o2[1])) << 16);
         }
-        *reinterpret_cast<uint4 *>(ob + (t0 + t) * xrow + p0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *reinterpret_cast<uint4 *>(ob + (t0 + t) * xrow + xp0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
   }
@@ -330,7 +365,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p.fin[(bh * kP + 16 * w + 4 * kq + i) * N + 16 * nt + r] = accs[nt][i];
+      for (int i = 0; i < 4; ++i)
+        p.fin[(bh * kP + 16 * w + r) * N + 16 * nt + 4 * kq + i] = accs[nt][i];
     }
   }
 }
