@@ -264,6 +264,120 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t seqlen,
     return failed ? 5 : 0;
 }
 
+/* ---- selective-scan backward ---------------------------------------------- */
+
+/* Gradients of the selective-scan forward (no conv prologue) with respect to
+ * every input, given dout = dL/dout (the guide's section 4.1 says the
+ * operator's backward is selective_scan_cuda.bwd and that last_state carries
+ * no gradient).  The backward of the recurrence is its adjoint, run in
+ * reverse time: with h the gradient of the loss with respect to x_t,
+ *   h_t = dy_t C_t + exp(dt'_{t+1} A) h_{t+1},   h_l = 0,
+ * and every input's gradient follows by the chain rule from
+ *   x_t = exp(dt'_t A) x_{t-1} + dt'_t B_t u_t,  y_t = C_t . x_t,
+ *   out_t = (y_t + D u_t) silu(z_t).
+ * Per row the forward states are kept (seqlen * dstate doubles).
+ * Outputs (all double, caller-allocated, zero-filled by this function):
+ *   du, ddelta, dz: (batch, dim, seqlen) (dz only when z is given);
+ *   dA: (dim, dstate); dB, dC: the layout of B, C (fixed (dim, dstate) or
+ *   (batch, ngroups, dstate, seqlen)); dD, ddelta_bias: (dim) (when given);
+ *   dinit: (batch, dim, dstate), the gradient with respect to initial_state. */
+int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen,
+                              int64_t dstate, int64_t ngroups, int io_dtype,
+                              const void *u, const void *delta, const float *A,
+                              const void *B, int B_kind, const void *C, int C_kind,
+                              const float *D, const float *delta_bias, const void *z,
+                              int delta_softplus, const double *initial_state,
+                              const double *dout,
+                              double *du, double *ddelta, double *dA, double *dB,
+                              double *dC, double *dD, double *dz, double *ddelta_bias,
+                              double *dinit) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC) return 1;
+    const int64_t l = seqlen, n = dstate;
+    const int64_t bsz = B_kind == OR_BC_FIXED ? dim * n : batch * ngroups * n * l;
+    const int64_t csz = C_kind == OR_BC_FIXED ? dim * n : batch * ngroups * n * l;
+    memset(du, 0, sizeof(double) * (size_t)(batch * dim * l));
+    memset(ddelta, 0, sizeof(double) * (size_t)(batch * dim * l));
+    memset(dA, 0, sizeof(double) * (size_t)(dim * n));
+    memset(dB, 0, sizeof(double) * (size_t)bsz);
+    memset(dC, 0, sizeof(double) * (size_t)csz);
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)dim);
+    if (dz) memset(dz, 0, sizeof(double) * (size_t)(batch * dim * l));
+    if (ddelta_bias) memset(ddelta_bias, 0, sizeof(double) * (size_t)dim);
+    if (dinit) memset(dinit, 0, sizeof(double) * (size_t)(batch * dim * n));
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, D, delta_bias, z, delta_softplus,
+                          initial_state, NULL, NULL, NULL, 0, 0};
+    double *xs = (double *)malloc(sizeof(double) * (size_t)((l + 1) * n));
+    double *h = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!xs || !h) { free(xs); free(h); return 5; }
+    const int64_t per_group = dim / ngroups;
+    for (int64_t row = 0; row < batch * dim; ++row) {
+        const int64_t b = row / dim, d = row % dim, g = d / per_group;
+        const int64_t base = row * l;
+        /* forward: xs[(t+1)*n + s] = x_t[s], xs[s] = x_{-1}[s] */
+        for (int64_t s = 0; s < n; ++s) xs[s] = initial_state ? initial_state[row * n + s] : 0.0;
+        for (int64_t t = 0; t < l; ++t) {
+            double dt = load_io(delta, io_dtype, base + t);
+            if (delta_bias) dt += (double)delta_bias[d];
+            if (delta_softplus) dt = oracle_softplus(dt);
+            const double ut = load_io(u, io_dtype, base + t);
+            for (int64_t s = 0; s < n; ++s)
+                xs[(t + 1) * n + s] = exp(dt * (double)A[d * n + s]) * xs[t * n + s]
+                                      + dt * bc_at(B, B_kind, io_dtype, &a, b, d, s, t) * ut;
+        }
+        /* reverse */
+        for (int64_t s = 0; s < n; ++s) h[s] = 0.0;
+        for (int64_t t = l - 1; t >= 0; --t) {
+            const double raw = load_io(delta, io_dtype, base + t) + (delta_bias ? (double)delta_bias[d] : 0.0);
+            const double dt = delta_softplus ? oracle_softplus(raw) : raw;
+            const double dsp = delta_softplus ? 1.0 / (1.0 + exp(-raw)) : 1.0;   /* softplus' */
+            const double ut = load_io(u, io_dtype, base + t);
+            double y = 0.0;
+            for (int64_t s = 0; s < n; ++s)
+                y += bc_at(C, C_kind, io_dtype, &a, b, d, s, t) * xs[(t + 1) * n + s];
+            const double pre = y + (D ? (double)D[d] * ut : 0.0);
+            double dy = dout[base + t];
+            if (z) {
+                const double zt = load_io(z, io_dtype, base + t);
+                const double sg = 1.0 / (1.0 + exp(-zt));
+                dz[base + t] = dy * pre * sg * (1.0 + zt * (1.0 - sg));   /* silu' = sg (1 + z (1 - sg)) */
+                dy *= zt * sg;
+            }
+            if (D) dD[d] += dy * ut;
+            double dut = D ? dy * (double)D[d] : 0.0;
+            double ddt = 0.0;
+            for (int64_t s = 0; s < n; ++s) {
+                const double Cv = bc_at(C, C_kind, io_dtype, &a, b, d, s, t);
+                const double Bv = bc_at(B, B_kind, io_dtype, &a, b, d, s, t);
+                const double As = (double)A[d * n + s];
+                const double aa = exp(dt * As);
+                h[s] += dy * Cv;                          /* h_t */
+                const double dCv = dy * xs[(t + 1) * n + s];
+                const double da = h[s] * xs[t * n + s];   /* dL/d(exp(dt' A)) */
+                ddt += da * As * aa + h[s] * Bv * ut;
+                dA[d * n + s] += da * dt * aa;
+                const double dBv = h[s] * dt * ut;
+                dut += h[s] * dt * Bv;
+                if (B_kind == OR_BC_FIXED) dB[d * n + s] += dBv;
+                else dB[((b * ngroups + g) * n + s) * l + t] += dBv;
+                if (C_kind == OR_BC_FIXED) dC[d * n + s] += dCv;
+                else dC[((b * ngroups + g) * n + s) * l + t] += dCv;
+                h[s] *= aa;                               /* carried to t-1 */
+            }
+            du[base + t] = dut;
+            ddelta[base + t] = ddt * dsp;
+            if (ddelta_bias) ddelta_bias[d] += ddt * dsp;
+        }
+        if (dinit)
+            for (int64_t s = 0; s < n; ++s) dinit[row * n + s] = h[s];
+    }
+    free(xs);
+    free(h);
+    return 0;
+}
+
 /* ---- single-step decode -------------------------------------------------- */
 
 /* selective_state_update: one timestep of the recurrence above applied to a

@@ -200,3 +200,58 @@ def test_ssd_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the selective-scan backward against its own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_bwd_pins as bpins  # noqa: E402
+
+BWD_MUTANTS = {
+    "bwd_softplus_derivative_sign": ("const double dsp = delta_softplus ? 1.0 / (1.0 + exp(-raw)) : 1.0;",
+                                     "const double dsp = delta_softplus ? 1.0 / (1.0 + exp(raw)) : 1.0;"),
+    "bwd_dA_drops_step": ("dA[d * n + s] += da * dt * aa;", "dA[d * n + s] += da * aa;"),
+    "bwd_silu_derivative": ("dz[base + t] = dy * pre * sg * (1.0 + zt * (1.0 - sg));",
+                            "dz[base + t] = dy * pre * sg * (1.0 + zt * sg);"),
+    "bwd_dC_old_state": ("const double dCv = dy * xs[(t + 1) * n + s];",
+                         "const double dCv = dy * xs[t * n + s];"),
+    "bwd_adjoint_not_decayed": ("h[s] *= aa;                               /* carried to t-1 */", ""),
+    "bwd_bias_grad_skips_softplus": ("if (ddelta_bias) ddelta_bias[d] += ddt * dsp;",
+                                     "if (ddelta_bias) ddelta_bias[d] += ddt;"),
+    "bwd_dB_group_zero": ("else dB[((b * ngroups + g) * n + s) * l + t] += dBv;",
+                          "else dB[((b * ngroups + 0 * g) * n + s) * l + t] += dBv;"),
+    "bwd_du_misses_input_path": ("dut += h[s] * dt * Bv;", ""),
+    "bwd_dD_ungated": ("if (D) dD[d] += dy * ut;\n", "if (D) dD[d] += dout[base + t] * ut;\n"),
+}
+
+
+def _bwd_pin_calls():
+    calls = [(f"fd_{c}_{sp}", lambda c=c, sp=sp: bpins.test_backward_matches_finite_differences(c, sp))
+             for c in sorted(bpins.CASES) for sp in (True, False)]
+    calls += [("euler", lambda: bpins.test_backward_euler_identities(True)),
+              ("init_closed_form", bpins.test_backward_initial_state_gradient_closed_form)]
+    return calls
+
+
+@pytest.mark.parametrize("mutant", sorted(BWD_MUTANTS))
+def test_bwd_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = BWD_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _bwd_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
