@@ -51,7 +51,8 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
+#define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
 
@@ -102,6 +103,11 @@ typedef struct ssm_scan_args {
    * allocator (hipMallocAsync/hipFreeAsync on hip_stream). */
   void *workspace;
   size_t workspace_bytes;
+  /* Optional output for the backward (ssm_scan_bwd): the state before every
+   * SSM_CKPT_INTERVAL-th timestep, (batch, dim, nck, dstate) fp32 with
+   * nck = ceil(seqlen / SSM_CKPT_INTERVAL); entry k is x_{k*32-1}, so entry 0
+   * is initial_state (zero when not given).  NULL: not written. */
+  float *checkpoints;
 } ssm_scan_args_t;
 
 /* Selective-scan forward.  Enqueues the scan on hip_stream and returns a
@@ -117,6 +123,70 @@ int ssm_scan_validate(const ssm_scan_args_t *args);
  * the whole sequence in one pass).  Host-only, no HIP call except a cached
  * query of the device's compute-unit count. */
 int ssm_scan_workspace_size(const ssm_scan_args_t *args, size_t *bytes);
+
+/* Arguments of ssm_scan_bwd.  Every pointer is a device pointer.  The inputs
+ * are those of the forward call (same shapes, dtypes and layout kinds);
+ * checkpoints are the ones that forward call wrote. */
+typedef struct ssm_scan_bwd_args {
+  int64_t batch, dim, seqlen, dstate, ngroups;
+  int32_t io_dtype;
+  const void *u;                                /* (b,d,l) io, required */
+  const void *delta;                            /* (b,d,l) io, required */
+  const float *A;                               /* (d,n) fp32, required */
+  const void *B; int32_t B_kind;                /* io, SSM_BC_* */
+  const void *C; int32_t C_kind;                /* io, SSM_BC_* */
+  const float *D;                               /* (d) fp32 or NULL */
+  const float *delta_bias;                      /* (d) fp32 or NULL */
+  const void *z;                                /* (b,d,l) io or NULL */
+  int32_t delta_softplus;                       /* 0 or 1 */
+  const float *checkpoints;                     /* (b,d,nck,n) fp32 from ssm_scan_fwd, required */
+  const void *dout;                             /* (b,d,l) io: dL/d out, required */
+  /* gradients, caller-allocated and fully overwritten */
+  void *du;                                     /* (b,d,l) io, required */
+  void *ddelta;                                 /* (b,d,l) io, required */
+  void *dz;                                     /* (b,d,l) io, required iff z */
+  float *dA;                                    /* (d,n) fp32, required */
+  float *dB;                                    /* fp32, B's layout ((d,n) or (b,g,n,l)), required */
+  float *dC;                                    /* fp32, C's layout, required */
+  float *dD;                                    /* (d) fp32, required iff D */
+  float *ddelta_bias;                           /* (d) fp32, required iff delta_bias */
+  float *dinitial_state;                        /* (b,d,n) fp32 or NULL */
+  /* Scratch for the per-workgroup partial sums (ssm_scan_bwd_workspace_size).
+   * When NULL the library takes it from the stream-ordered allocator. */
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_scan_bwd_args_t;
+
+/* Selective-scan backward (the same page, section 4.1: the operator's
+ * backward is the extension's bwd entry; last_state carries no gradient).
+ * Given dout = dL/d out, writes the gradient of L with respect to every input
+ * of the forward:  with h_t = dL/dx_t, the adjoint of the recurrence,
+ *
+ *     g_t     = dout_t * silu(z_t)                     (dL/d(y_t + D u_t))
+ *     h_t[s]  = g_t * C_t[s] + exp(delta'_{t+1} A[d,s]) * h_{t+1}[s],  h_l = 0
+ *     du_t    = g_t D[d] + delta'_t sum_s h_t[s] B_t[s]
+ *     ddelta_t = softplus'(delta_t + delta_bias[d]) *
+ *                sum_s h_t[s] (A[d,s] exp(delta'_t A[d,s]) x_{t-1}[s] + B_t[s] u_t)
+ *     dA[d,s] = sum_{b,t} h_t[s] delta'_t exp(delta'_t A[d,s]) x_{t-1}[s]
+ *     dB_t[s] = sum over the group's channels of h_t[s] delta'_t u_t   (fixed: summed over b, t)
+ *     dC_t[s] = sum over the group's channels of g_t x_t[s]           (fixed: summed over b, t)
+ *     dD[d]   = sum_{b,t} g_t u_t,   ddelta_bias[d] = sum_{b,t} ddelta_t
+ *     dz_t    = dout_t (y_t + D u_t) silu'(z_t),  dinitial_state = exp(delta'_0 A) h_0
+ *
+ * (softplus' = 1 without delta_softplus).  Every chunk of SSM_CKPT_INTERVAL
+ * timesteps is re-run forward from its checkpoint, then walked in reverse.
+ * Sums over batches, and over the workgroups of a group, are combined in a
+ * fixed order; inside a workgroup the time-varying dB/dC terms of its waves
+ * are added with LDS atomics, so those two can differ between runs in the
+ * last bits (fp32 rounding), every other output is bit-for-bit repeatable.
+ * Same conventions and status codes as ssm_scan_fwd. */
+int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssm_scan_bwd (no HIP call). */
+int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *args);
+
+/* Scratch bytes ssm_scan_bwd needs for these arguments (host-only). */
+int ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *args, size_t *bytes);
 
 /* Causal depthwise conv forward (PaddleNLP Kernel operator-library guide,
  * section 4.2 "causal_conv1d": causal_conv1d_fn(x, weight, bias, ...,

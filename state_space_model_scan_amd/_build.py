@@ -31,6 +31,7 @@ SOURCES = [
     ("ssm_scan.hip", True),
     ("decode.hip", True),
     ("ssd.hip", True),
+    ("bwd.hip", True),
     ("validate.cpp", False),
 ]
 

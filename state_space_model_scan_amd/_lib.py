@@ -16,6 +16,7 @@ SSM_CONV_WIDTH = 4
 SSM_MAX_CONV_STATE = 256
 SSD_HEADDIM = 64
 SSD_CHUNK = 64
+SSM_CKPT_INTERVAL = 32
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
@@ -24,6 +25,7 @@ EXPORTS = (
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
     "ssd_scan_fwd", "ssd_scan_validate",
+    "ssm_scan_bwd", "ssm_scan_bwd_validate", "ssm_scan_bwd_workspace_size",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
 )
 
@@ -44,6 +46,25 @@ class ScanArgs(ctypes.Structure):
         ("out", _vp), ("last_state", _vp), ("initial_state", _vp),
         ("conv_x", _vp), ("conv_weight", _vp), ("conv_bias", _vp),
         ("conv_width", ctypes.c_int32), ("conv_act", ctypes.c_int32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("checkpoints", _vp),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of ssm_scan_bwd_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("u", _vp), ("delta", _vp), ("A", _vp),
+        ("B", _vp), ("B_kind", ctypes.c_int32),
+        ("C", _vp), ("C_kind", ctypes.c_int32),
+        ("D", _vp), ("delta_bias", _vp), ("z", _vp),
+        ("delta_softplus", ctypes.c_int32),
+        ("checkpoints", _vp), ("dout", _vp),
+        ("du", _vp), ("ddelta", _vp), ("dz", _vp), ("dA", _vp), ("dB", _vp), ("dC", _vp),
+        ("dD", _vp), ("ddelta_bias", _vp), ("dinitial_state", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -119,6 +140,12 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_fwd.restype = ctypes.c_int
         L.ssd_scan_validate.argtypes = [ctypes.POINTER(SsdArgs)]
         L.ssd_scan_validate.restype = ctypes.c_int
+        L.ssm_scan_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+        L.ssm_scan_bwd.restype = ctypes.c_int
+        L.ssm_scan_bwd_validate.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.ssm_scan_bwd_validate.restype = ctypes.c_int
+        L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_scan_bwd_workspace_size.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_hip_error.argtypes = []

@@ -17,7 +17,7 @@ from typing import Optional, Tuple, Union
 import torch
 
 from . import _lib
-from ._lib import ScanArgs, check
+from ._lib import BwdArgs, ScanArgs, check
 
 _IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
 
@@ -65,13 +65,16 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
                  initial_state: Optional[torch.Tensor] = None,
                  conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
                  conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 checkpoints: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Enqueue ssm_scan_fwd on the current stream; returns ``out``.
 
     Shapes as in include/ssmscan.h.  ``out`` (same dtype as delta) and
     ``last_state`` (float32, optional) are written in place; ``out`` is
     allocated when not given.  With ``conv_weight`` the conv prologue computes
-    u from ``conv_x`` and ``u`` may be None.
+    u from ``conv_x`` and ``u`` may be None.  ``checkpoints`` (float32,
+    (batch, dim, ceil(seqlen / 32), dstate), optional) receives the states the
+    backward starts its chunks from.
     """
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
@@ -108,6 +111,11 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     args.conv_x, args.conv_weight, args.conv_bias = _ptr(conv_x), _ptr(conv_weight), _ptr(conv_bias)
     args.conv_width = 0 if conv_weight is None else conv_weight.shape[1]
     args.conv_act = conv_act
+    if checkpoints is not None:
+        want = (batch, dim, checkpoint_count(seqlen), dstate)
+        if tuple(checkpoints.shape) != want or checkpoints.dtype != torch.float32 or not checkpoints.is_contiguous():
+            raise ValueError(f"checkpoints must be a contiguous float32 tensor of shape {want}")
+        args.checkpoints = _ptr(checkpoints)
     L = _lib.lib()
     if workspace is None:
         need = ctypes.c_size_t(0)
@@ -118,6 +126,77 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
         args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     check(L.ssm_scan_fwd(ctypes.byref(args), _stream(delta.device, stream)))
     return out
+
+
+def checkpoint_count(seqlen: int) -> int:
+    """Saved states per channel: one every SSM_CKPT_INTERVAL timesteps."""
+    return (seqlen + _lib.SSM_CKPT_INTERVAL - 1) // _lib.SSM_CKPT_INTERVAL
+
+
+def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 C: torch.Tensor, dout: torch.Tensor, checkpoints: torch.Tensor,
+                 D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                 want_dinitial_state: bool = False, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> dict:
+    """Enqueue ssm_scan_bwd; returns the gradients in a dict.
+
+    Inputs as for ``ssm_scan_fwd`` (B/C 2-D fixed or 4-D grouped), ``dout`` in
+    the io dtype and the ``checkpoints`` that forward call wrote.  du, ddelta
+    and dz come back in the io dtype; dA, dB, dC, dD, ddelta_bias and
+    dinitial_state in float32 (dB/dC in B's/C's layout).
+    """
+    delta = _dense(delta)
+    io = _IO.get(delta.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32 or bfloat16, got {delta.dtype}")
+    batch, dim, seqlen = delta.shape
+    dstate = A.shape[1]
+    u, B, C, z, dout = _dense(u), _dense(B), _dense(C), _dense(z), _dense(dout)
+    bk, bg = _bc_kind(B, "B")
+    ck, cg = _bc_kind(C, "C")
+    if bk == _lib.SSM_BC_VARYING and ck == _lib.SSM_BC_VARYING and bg != cg:
+        raise ValueError("B and C must have the same number of groups")
+    ngroups = max(bg, cg, 1)
+    for name, t in (("u", u), ("z", z), ("B", B), ("C", C), ("dout", dout)):
+        if t is not None and t.dtype != delta.dtype:
+            raise ValueError(f"{name} must have the io dtype {delta.dtype}, got {t.dtype}")
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("checkpoints", checkpoints)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {t.dtype}")
+    want = (batch, dim, checkpoint_count(seqlen), dstate)
+    if tuple(checkpoints.shape) != want:
+        raise ValueError(f"checkpoints must have shape {want}, got {tuple(checkpoints.shape)}")
+    A, D, delta_bias, checkpoints = _dense(A), _dense(D), _dense(delta_bias), _dense(checkpoints)
+    dev = delta.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {
+        "du": torch.empty_like(delta), "ddelta": torch.empty_like(delta),
+        "dz": None if z is None else torch.empty_like(delta),
+        "dA": torch.empty((dim, dstate), **f32),
+        "dB": torch.empty(B.shape, **f32), "dC": torch.empty(C.shape, **f32),
+        "dD": None if D is None else torch.empty((dim,), **f32),
+        "ddelta_bias": None if delta_bias is None else torch.empty((dim,), **f32),
+        "dinitial_state": torch.empty((batch, dim, dstate), **f32) if want_dinitial_state else None,
+    }
+    args = BwdArgs()
+    args.batch, args.dim, args.seqlen, args.dstate, args.ngroups = batch, dim, seqlen, dstate, ngroups
+    args.io_dtype = io
+    args.u, args.delta, args.A = _ptr(u), _ptr(delta), _ptr(A)
+    args.B, args.B_kind, args.C, args.C_kind = _ptr(B), bk, _ptr(C), ck
+    args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
+    args.delta_softplus = int(bool(delta_softplus))
+    args.checkpoints, args.dout = _ptr(checkpoints), _ptr(dout)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
+        setattr(args, k, _ptr(g[k]))
+    L = _lib.lib()
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        check(L.ssm_scan_bwd_workspace_size(ctypes.byref(args), ctypes.byref(need)))
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    check(L.ssm_scan_bwd(ctypes.byref(args), _stream(dev, stream)))
+    return g
 
 
 def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,

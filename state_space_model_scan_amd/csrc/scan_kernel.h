@@ -36,6 +36,7 @@
 #pragma once
 
 #include "device_util.h"
+#include "ssmscan.h"
 
 namespace ssm {
 
@@ -45,7 +46,8 @@ struct ScanParams {
   void *out;
   float *last;
   float *ws_state, *ws_sumdt;
-  int64_t batch, dim, seqlen, seg_len, cpg;
+  float *ckpt;           // saved states for the backward, or null
+  int64_t batch, dim, seqlen, seg_len, cpg, nck;
   int n, n_pad, ngroups, groups_eff, nblk, nseg, nblocks;
   int softplus, conv_silu, vec, xcd_swizzle;
 };
@@ -349,6 +351,15 @@ scan_kernel(const ScanParams p) {
 
   for (int64_t c = t_begin; c < t_end; c += T) {
     const int len = static_cast<int>((t_end - c < T) ? t_end - c : T);
+    if constexpr (FULL) {
+      // the state before timestep c, every SSM_CKPT_INTERVAL timesteps
+      if (p.ckpt && valid && (c % SSM_CKPT_INTERVAL) == 0) {
+        float *dst = p.ckpt + (row * p.nck + c / SSM_CKPT_INTERVAL) * n;
+#pragma unroll
+        for (int k = 0; k < NSW; ++k)
+          if (s0 + k < n) dst[s0 + k] = x[k];
+      }
+    }
     if (CONV && p.conv_silu) prep(c, std::true_type{}); else prep(c, std::false_type{});
     if constexpr (ANYV) {
       wave_lds_sync();          // the previous chunk's reads of the slice are done

@@ -137,7 +137,10 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
     if (v >= 1) nseg = v;
   }
   int64_t seg_len = (a->seqlen + nseg - 1) / nseg;
-  seg_len = (seg_len + pl.T - 1) / pl.T * pl.T;
+  // checkpoints sit at multiples of SSM_CKPT_INTERVAL, which every chunk
+  // length divides: segments then start on a checkpoint too
+  const int64_t align = a->checkpoints ? SSM_CKPT_INTERVAL : pl.T;
+  seg_len = (seg_len + align - 1) / align * align;
   pl.seg_len = seg_len;
   pl.nseg = static_cast<int>((a->seqlen + seg_len - 1) / seg_len);
   pl.ws_bytes = pl.nseg > 1
@@ -176,6 +179,8 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   p.out = a->out; p.last = a->last_state;
   p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
   p.seg_len = pl.seg_len; p.cpg = pl.cpg;
+  p.ckpt = a->checkpoints;
+  p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
   p.n = static_cast<int>(a->dstate); p.n_pad = pl.n_pad; p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = pl.groups_eff; p.nblk = pl.nblk; p.nseg = pl.nseg; p.nblocks = pl.nblocks;
   p.softplus = a->delta_softplus; p.conv_silu = a->conv_act == SSM_ACT_SILU;

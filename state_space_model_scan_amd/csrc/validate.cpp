@@ -51,6 +51,29 @@ extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
   return SSM_OK;
 }
 
+extern "C" int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  if (!positive(a->batch) || !positive(a->dim) || !positive(a->seqlen) ||
+      !positive(a->dstate) || !positive(a->ngroups))
+    return SSM_ERR_SHAPE;
+  if (a->dim % a->ngroups != 0) return SSM_ERR_SHAPE;
+  // the per-workgroup partial sums hold up to (batch*ngroups, dim, dstate, seqlen) floats
+  if (!product_fits(a->batch, a->dim, a->seqlen) ||
+      !product_fits(a->batch * a->dim, a->dstate, a->seqlen))
+    return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
+  if ((a->B_kind != SSM_BC_FIXED && a->B_kind != SSM_BC_VARYING) ||
+      (a->C_kind != SSM_BC_FIXED && a->C_kind != SSM_BC_VARYING))
+    return SSM_ERR_UNSUPPORTED;
+  if (a->delta_softplus != 0 && a->delta_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (!a->u || !a->delta || !a->A || !a->B || !a->C || !a->checkpoints || !a->dout ||
+      !a->du || !a->ddelta || !a->dA || !a->dB || !a->dC)
+    return SSM_ERR_NULL;
+  if ((a->z && !a->dz) || (a->D && !a->dD) || (a->delta_bias && !a->ddelta_bias)) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
 extern "C" int causal_conv1d_validate(const void *x, const float *weight, const void *out,
                                       int64_t batch, int64_t dim, int64_t seqlen,
                                       int32_t width, int32_t io_dtype, int32_t act) {

@@ -227,6 +227,13 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray
     return t
 
 
+def make_dout(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """The output gradient of the backward: N(0, 1) of shape (batch, dim,
+    seqlen) in the io dtype, from its own stream (seed + 1000)."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 1000)
+    return _store(_normal(rng, (w.batch, w.dim, w.seqlen)), w.io_dtype)
+
+
 def sha256(a: Optional[np.ndarray]) -> Optional[str]:
     if a is None:
         return None

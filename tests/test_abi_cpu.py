@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 3
+    assert L.ssm_abi_version() == 4
 
 
 def test_status_strings():
@@ -232,3 +232,59 @@ def test_ssd_validation():
         assert v(_good_ssd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
     assert L.ssd_scan_fwd(ctypes.byref(_good_ssd(B=None)), None) == _lib.SSM_ERR_NULL
     assert L.ssd_scan_validate(None) == _lib.SSM_ERR_NULL
+
+
+def _good_bwd(**kw):
+    a = _lib.BwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate, a.ngroups = 2, 64, 100, 16, 2
+    a.io_dtype = _lib.SSM_BF16
+    a.u = a.delta = a.A = a.B = a.C = a.checkpoints = a.dout = FAKE
+    a.du = a.ddelta = a.dA = a.dB = a.dC = FAKE
+    a.B_kind = a.C_kind = _lib.SSM_BC_VARYING
+    a.delta_softplus = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_bwd_validation():
+    L = _lib.lib()
+    v = lambda a: L.ssm_scan_bwd_validate(ctypes.byref(a))
+    assert v(_good_bwd()) == _lib.SSM_OK
+    assert v(_good_bwd(z=FAKE, dz=FAKE, D=FAKE, dD=FAKE, delta_bias=FAKE, ddelta_bias=FAKE,
+                       B_kind=_lib.SSM_BC_FIXED)) == _lib.SSM_OK
+    for field in ("u", "delta", "A", "B", "C", "checkpoints", "dout", "du", "ddelta", "dA", "dB", "dC"):
+        assert v(_good_bwd(**{field: None})) == _lib.SSM_ERR_NULL, field
+    # an optional input asks for its gradient
+    for inp, grad in (("z", "dz"), ("D", "dD"), ("delta_bias", "ddelta_bias")):
+        assert v(_good_bwd(**{inp: FAKE})) == _lib.SSM_ERR_NULL, inp
+    for field, val in (("batch", 0), ("dim", -1), ("seqlen", 0), ("dstate", 0), ("ngroups", 3)):
+        assert v(_good_bwd(**{field: val})) == _lib.SSM_ERR_SHAPE, (field, val)
+    for kw in (dict(io_dtype=7), dict(dstate=17), dict(B_kind=5), dict(delta_softplus=3)):
+        assert v(_good_bwd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
+    assert v(_good_bwd(batch=1 << 40, dim=1 << 20)) == _lib.SSM_ERR_SHAPE
+    assert L.ssm_scan_bwd_validate(None) == _lib.SSM_ERR_NULL
+    # rejected before any HIP call: usable without a GPU
+    assert L.ssm_scan_bwd(ctypes.byref(_good_bwd(dout=None)), None) == _lib.SSM_ERR_NULL
+    need = ctypes.c_size_t(0)
+    assert L.ssm_scan_bwd_workspace_size(ctypes.byref(_good_bwd()), ctypes.byref(need)) == _lib.SSM_OK
+    # partial dB/dC per 32-channel workgroup, dA per batch, dD and ddelta_bias per batch
+    nblk = (64 // 2 + 31) // 32
+    up = lambda e: (e * 4 + 255) // 256 * 256
+    assert need.value == 2 * up(2 * 2 * nblk * 16 * 100) + up(2 * 64 * 16) + 2 * up(2 * 64)
+
+
+def test_bwd_binding_errors():
+    import torch
+    from state_space_model_scan_amd import binding
+    b, d, l, n = 1, 4, 10, 3
+    u = torch.zeros(b, d, l)
+    A = torch.zeros(d, n)
+    B = torch.zeros(b, 1, n, l)
+    ck = torch.zeros(b, d, 1, n)
+    with pytest.raises(ValueError, match="checkpoints must have shape"):
+        binding.ssm_scan_bwd(u, u, A, B, B, u, torch.zeros(b, d, 2, n))
+    with pytest.raises(ValueError, match="io dtype"):
+        binding.ssm_scan_bwd(u, u, A, B, B, u.to(torch.bfloat16), ck)
+    with pytest.raises(ValueError, match="checkpoints must be a contiguous float32"):
+        binding.ssm_scan_fwd(u, u, A, B, B, checkpoints=torch.zeros(b, d, 2, n))

@@ -1,0 +1,240 @@
+"""GPU parity of the selective-scan backward (ssm_scan_bwd) and of the
+forward's checkpoint output, against the float64 oracle, through the C ABI.
+
+The forward runs on the GPU with checkpoints, then the backward; the oracle
+computes every gradient from the same input bits and dout.  Bar, per element:
+|gpu - ref| <= tol * (1 + |ref|), tol 1e-4 for fp32 io and 2e-2 for bf16 io
+(du, ddelta, dz are stored in the io dtype; dA, dB, dC, dD, ddelta_bias and
+dinitial_state in fp32).  At full size the oracle runs on one (batch, group)
+slice -- every channel of the group, so dB and dC of that slice are complete
+sums -- and on every batch of three channels for dA, dD and ddelta_bias.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from state_space_model_scan_amd.inputs import (BF16, F32, WORKLOADS, bf16_bits_to_f32, make_dout,
+                                               make_inputs)
+from tests.harness import TOL, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BASE = WORKLOADS["tiny"].scaled(batch=2, dim=32, seqlen=100, dstate=16, A_mode="lognormal",
+                                delta_mean=-1.0)
+
+
+def _as_f64(a, io):
+    if a is None:
+        return None
+    return bf16_bits_to_f32(a).astype(np.float64) if io == BF16 else a.astype(np.float64)
+
+
+def _kinds(t):
+    bk = orc.BC_FIXED if t["B"].ndim == 2 else orc.BC_VARYING
+    ck = orc.BC_FIXED if t["C"].ndim == 2 else orc.BC_VARYING
+    return bk, ck
+
+
+def _gpu(w, t, dout, init=None, want_dinit=True, ret_ckpt=False):
+    import torch
+    from state_space_model_scan_amd import binding
+    io = w.io_dtype
+    dev = lambda a: to_dev(a, io)
+    par = lambda a: to_dev(a, param=True)
+    ck = torch.full((w.batch, w.dim, binding.checkpoint_count(w.seqlen), w.dstate), float("nan"),
+                    dtype=torch.float32, device="cuda")
+    u, delta, B, C, z = dev(t["u"]), dev(t["delta"]), dev(t["B"]), dev(t["C"]), dev(t["z"])
+    A, D, bias = par(t["A"]), par(t["D"]), par(t["delta_bias"])
+    init_t = None if init is None else par(init.astype(np.float32))
+    binding.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, w.softplus, initial_state=init_t, checkpoints=ck)
+    g = binding.ssm_scan_bwd(u, delta, A, B, C, dev(dout), ck, D=D, z=z, delta_bias=bias,
+                             delta_softplus=w.softplus, want_dinitial_state=want_dinit)
+    torch.cuda.synchronize()
+    res = {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
+    if ret_ckpt:
+        res["ckpt"] = ck.cpu().numpy().astype(np.float64)
+    return res
+
+
+def _oracle(w, t, dout, init=None):
+    bk, ck = _kinds(t)
+    return orc.selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], _as_f64(dout, w.io_dtype),
+                                  t["D"], t["z"], t["delta_bias"], w.softplus, io_dtype=w.io_dtype,
+                                  ngroups=w.ngroups, B_kind=bk, C_kind=ck,
+                                  initial_state=None if init is None else init.astype(np.float32).astype(np.float64))
+
+
+def _err(gpu, ref):
+    if gpu.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(gpu)):
+        return float("inf")
+    return float(np.max(np.abs(gpu - ref) / (1.0 + np.abs(ref))))
+
+
+def _compare(w, got, want, what, names=None):
+    tol = TOL[w.io_dtype]
+    errs = {}
+    for k in names or ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
+        if want.get(k) is None or got.get(k) is None:
+            continue
+        e = _err(got[k], want[k].reshape(got[k].shape))
+        errs[k] = e
+        assert e <= tol, f"{what} {k}: max normalised error {e:.3e} > {tol:.0e}"
+    return errs
+
+
+def _run(w, what, init=None, t=None):
+    log(f"[bwd] {what}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} io={w.io_dtype} "
+        f"bc={w.bc_kind} z={w.has_z} D={w.has_D} bias={w.has_bias} sp={w.softplus}")
+    t = make_inputs(w) if t is None else t
+    dout = make_dout(w)
+    got = _gpu(w, t, dout, init)
+    want = _oracle(w, t, dout, init)
+    return _compare(w, got, want, what)
+
+
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_bwd_base(io):
+    _run(BASE.scaled(io_dtype=io, seed=500 + io), f"base io={io}")
+
+
+@pytest.mark.parametrize("n", [1, 4, 9, 16])
+@pytest.mark.parametrize("seqlen", [1, 31, 32, 33, 130])
+def test_bwd_sizes(n, seqlen):
+    w = BASE.scaled(dstate=n, seqlen=seqlen, io_dtype=F32, seed=510 + n * 7 + seqlen)
+    _run(w, f"n={n} l={seqlen}")
+
+
+@pytest.mark.parametrize("bc", ["varying", "fixed", "Bfixed", "Cfixed"])
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_bwd_bc_layouts(bc, io):
+    w = BASE.scaled(io_dtype=io, bc_kind="fixed" if bc == "fixed" else "varying", seed=530 + len(bc) + io)
+    t = make_inputs(w)
+    if bc in ("Bfixed", "Cfixed"):
+        fixed = make_inputs(w.scaled(bc_kind="fixed"))
+        key = bc[0]
+        t[key] = fixed[key]
+    _run(w, f"bc={bc}", t=t)
+
+
+@pytest.mark.parametrize("groups,dim", [(1, 96), (2, 96), (4, 256), (3, 24)])
+def test_bwd_groups_and_partial_blocks(groups, dim):
+    # 96 / g channels per group: workgroups of 32 channels end part-filled
+    w = BASE.scaled(dim=dim, ngroups=groups, io_dtype=F32, seed=540 + groups + dim)
+    _run(w, f"groups={groups} dim={dim}")
+
+
+@pytest.mark.parametrize("flags", [dict(has_z=False), dict(has_D=False), dict(has_bias=False),
+                                   dict(softplus=False, delta_mean=0.3, delta_std=0.1),
+                                   dict(has_z=False, has_D=False, has_bias=False)])
+def test_bwd_optional_inputs(flags):
+    w = BASE.scaled(io_dtype=F32, seed=550, **flags)
+    t = make_inputs(w)
+    if not w.softplus:   # keep the step positive without softplus
+        t["delta"] = (np.abs(t["delta"]) + 0.05).astype(np.float32)
+    _run(w, f"flags={flags}", t=t)
+
+
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_bwd_initial_state(io):
+    w = BASE.scaled(io_dtype=io, seqlen=70, seed=560 + io)
+    init = np.random.default_rng(561).standard_normal((w.batch, w.dim, w.dstate))
+    _run(w, f"initial state io={io}", init=init)
+
+
+def test_checkpoints_are_the_forward_states():
+    """Entry k of the checkpoints is the state before timestep 32k: the
+    oracle's last state of the prefix [0, 32k), and entry 0 the initial state."""
+    w = BASE.scaled(seqlen=100, io_dtype=F32, seed=570)
+    t = make_inputs(w)
+    init = np.random.default_rng(571).standard_normal((w.batch, w.dim, w.dstate))
+    got = _gpu(w, t, make_dout(w), init, ret_ckpt=True)["ckpt"]
+    np.testing.assert_array_equal(got[:, :, 0], init.astype(np.float32).astype(np.float64))
+    for k in range(1, got.shape[2]):
+        L = 32 * k
+        sl = {key: (None if v is None else np.ascontiguousarray(v[..., :L]))
+              for key, v in t.items() if key in ("u", "delta", "z")}
+        B = np.ascontiguousarray(t["B"][..., :L])
+        C = np.ascontiguousarray(t["C"][..., :L])
+        _, last = orc.selective_scan(sl["u"], sl["delta"], t["A"], B, C, t["D"], sl["z"], t["delta_bias"],
+                                     w.softplus, io_dtype=w.io_dtype, ngroups=w.ngroups,
+                                     initial_state=init.astype(np.float32).astype(np.float64))
+        e = _err(got[:, :, k].reshape(-1, w.dstate), last)
+        assert e <= TOL[F32], f"checkpoint {k}: {e:.3e}"
+
+
+def test_bwd_repeatable():
+    """Two runs agree bit for bit except time-varying dB/dC, whose sum over the
+    waves of a workgroup is taken with LDS atomics in arrival order: there the
+    runs differ by fp32 rounding only."""
+    w = BASE.scaled(io_dtype=BF16, dim=64, ngroups=2, seed=580)
+    t = make_inputs(w)
+    dout = make_dout(w)
+    a = _gpu(w, t, dout)
+    b = _gpu(w, t, dout)
+    for k, v in a.items():
+        if v is None:
+            continue
+        if k in ("dB", "dC"):
+            assert np.max(np.abs(v - b[k]) / (1.0 + np.abs(v))) <= 1e-5, k
+        else:
+            np.testing.assert_array_equal(v, b[k], err_msg=k)
+
+
+def test_bwd_full_size_slices():
+    """mamba2p8b (b=8 d=5120 l=2048 n=16 g=4 bf16) through the GPU; the oracle
+    on batch 3 / group 2 (all 1280 channels: complete dB and dC sums) and on
+    every batch of channels 0, 2777 and 5119 (dA, dD, ddelta_bias)."""
+    import torch
+    from state_space_model_scan_amd import binding
+    w = WORKLOADS["mamba2p8b"]
+    log(f"[bwd] full size {w.name}")
+    t = make_inputs(w)
+    dout = make_dout(w)
+    io = w.io_dtype
+    dev = lambda a: to_dev(a, io)
+    par = lambda a: to_dev(a, param=True)
+    ck = torch.empty((w.batch, w.dim, binding.checkpoint_count(w.seqlen), w.dstate), dtype=torch.float32,
+                     device="cuda")
+    u, delta, B, C, z = dev(t["u"]), dev(t["delta"]), dev(t["B"]), dev(t["C"]), dev(t["z"])
+    A, D, bias = par(t["A"]), par(t["D"]), par(t["delta_bias"])
+    binding.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, w.softplus, checkpoints=ck)
+    g = binding.ssm_scan_bwd(u, delta, A, B, C, dev(dout), ck, D=D, z=z, delta_bias=bias,
+                             delta_softplus=w.softplus)
+    torch.cuda.synchronize()
+
+    bb, gg = 3, 2
+    cpg = w.dim // w.ngroups
+    ch = slice(gg * cpg, (gg + 1) * cpg)
+    sub = w.scaled(batch=1, dim=cpg, ngroups=1)
+    ts = {k: (None if v is None else v) for k, v in t.items()}
+    for k in ("u", "delta", "z"):
+        ts[k] = np.ascontiguousarray(t[k][bb:bb + 1, ch])
+    ts["B"] = np.ascontiguousarray(t["B"][bb:bb + 1, gg:gg + 1])
+    ts["C"] = np.ascontiguousarray(t["C"][bb:bb + 1, gg:gg + 1])
+    ts["A"] = np.ascontiguousarray(t["A"][ch])
+    ts["D"] = np.ascontiguousarray(t["D"][ch])
+    ts["delta_bias"] = np.ascontiguousarray(t["delta_bias"][ch])
+    want = _oracle(sub, ts, np.ascontiguousarray(dout[bb:bb + 1, ch]))
+    got = {k: g[k][bb:bb + 1, ch].float().cpu().numpy().astype(np.float64) for k in ("du", "ddelta", "dz")}
+    got["dB"] = g["dB"][bb:bb + 1, gg:gg + 1].cpu().numpy().astype(np.float64)
+    got["dC"] = g["dC"][bb:bb + 1, gg:gg + 1].cpu().numpy().astype(np.float64)
+    _compare(w, got, want, "full size (b=3, g=2)", names=("du", "ddelta", "dz", "dB", "dC"))
+
+    for d in (0, 2777, 5119):
+        gi = d // cpg
+        one = w.scaled(dim=1, ngroups=1)
+        t1 = dict(t)
+        for k in ("u", "delta", "z"):
+            t1[k] = np.ascontiguousarray(t[k][:, d:d + 1])
+        t1["B"] = np.ascontiguousarray(t["B"][:, gi:gi + 1])
+        t1["C"] = np.ascontiguousarray(t["C"][:, gi:gi + 1])
+        t1["A"] = np.ascontiguousarray(t["A"][d:d + 1])
+        t1["D"] = np.ascontiguousarray(t["D"][d:d + 1])
+        t1["delta_bias"] = np.ascontiguousarray(t["delta_bias"][d:d + 1])
+        want1 = _oracle(one, t1, np.ascontiguousarray(dout[:, d:d + 1]))
+        got1 = {"dA": g["dA"][d:d + 1].cpu().numpy().astype(np.float64),
+                "dD": g["dD"][d:d + 1].cpu().numpy().astype(np.float64),
+                "ddelta_bias": g["ddelta_bias"][d:d + 1].cpu().numpy().astype(np.float64)}
+        _compare(w, got1, want1, f"full size channel {d}", names=("dA", "dD", "ddelta_bias"))
