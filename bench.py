@@ -38,6 +38,14 @@ state update, the dominant kernel: the state read and written once, x, dt,
 z, out, B, C once, A/D/dt_bias once (d*n*4 + 2*d*4 bytes, shared by the
 batch), against 8 TB/s.
 
+Backward (--backward, with a selective-scan workload): a step is one
+ssm_scan_bwd call (every input gradient: du, ddelta, dz, dA, dB, dC, dD,
+d(delta_bias)) from the checkpoints a forward call wrote before timing.  The
+value is elements/s (b*d*l).  The roofline is the VALU rate (bwd_alu_ops per
+step over the step's event time, which brackets the backward kernel and the
+short partial-sum kernels after it), with the HBM rate of the algorithmic
+bytes beside it.
+
 Mamba-2 workloads (--workload ssd2p7b): a step is one ssd_scan_fwd call.
 The value is elements/s (b*l*h*p).  The roofline is HBM (x, z, out, dt, B, C
 read or written once, plus the small per-head vectors), with the matrix-core
@@ -66,6 +74,7 @@ CSRC = os.path.join(ROOT, "state_space_model_scan_amd", "csrc")
 KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip", "ssm_scan.hip")
 DECODE_SRCS = ("decode.hip", "device_util.h")
 SSD_SRCS = ("ssd.hip", "device_util.h")
+BWD_SRCS = ("bwd.hip", "device_util.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -163,6 +172,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 512 MiB device copy (for rocprofv3 counter scaling)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time ssm_scan_bwd (all gradients) on the selective-scan workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -177,6 +188,8 @@ def main():
     from state_space_model_scan_amd.inputs import SSD_WORKLOADS
     if args.workload in SSD_WORKLOADS:
         return ssd_main(args)
+    if args.backward:
+        return bwd_main(args)
 
     def to_dev(a, io_dtype, param=False):
         x = torch.from_numpy(np.ascontiguousarray(a))
@@ -527,6 +540,156 @@ def ssd_cpu_baseline(w, t, budget_s: float):
             "kind": "oracle",
             "sample": f"{nb} of {w.batch} batch rows x all {w.nheads} heads x {w.seqlen} tokens, "
                       f"{dt:.1f} s float64 on {threads} threads"}
+
+
+def bwd_bytes(w) -> int:
+    """Backward minimum: u, delta, z, dout, B, C and the checkpoints read once;
+    du, ddelta, dz (io) and dA, dB, dC, dD, d(delta_bias) (fp32) written once."""
+    es = 2 if w.io_dtype == 1 else 4
+    E = w.elements
+    n = w.dstate
+    zed = 1 if w.has_z else 0
+    bcn = w.dim * n if w.bc_kind == "fixed" else w.batch * w.ngroups * n * w.seqlen
+    nck = -(-w.seqlen // 32)
+    reads = (3 + zed) * E * es + 2 * bcn * es + w.batch * w.dim * nck * n * 4 + w.dim * n * 4 + 2 * w.dim * 4
+    writes = (2 + zed) * E * es + 2 * bcn * 4 + w.dim * n * 4 + 2 * w.dim * 4
+    return reads + writes
+
+
+def bwd_alu_ops(w) -> float:
+    """Per (timestep, state): the forward re-run (delta'*A, delta'u*B, the
+    state FMA, C.x for dz, one exp weighted 4) = 8, and the adjoint (h FMA,
+    carry multiply, a*x, h*a*x, dA FMA, h*B, A*hax FMA with u*hB, the two sums
+    over states, dB and dC products and their sums over channels) = 14, plus
+    the sum of C.x over states = 1: 23.  Per element: softplus (exp, log),
+    its derivative (exp, rcp), silu and its derivative (exp, rcp) -- six
+    transcendentals weighted 4 -- and about 16 plain ops: 40."""
+    return float(w.elements) * (23 * w.dstate + 40)
+
+
+def bwd_main(args):
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, WORKLOADS, make_dout, make_inputs
+
+    _lib.lib()
+    w = WORKLOADS[args.workload]
+    if w.conv:
+        raise SystemExit("the backward covers the scan; pick a workload without the conv prologue")
+    t = make_inputs(w)
+    dout_np = make_dout(w)
+    io = w.io_dtype
+
+    def dev(a, param=False):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and io == BF16 and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16)
+        return x.cuda()
+
+    u, delta, z, B, C = dev(t["u"]), dev(t["delta"]), dev(t["z"]), dev(t["B"]), dev(t["C"])
+    A, D, bias = dev(t["A"], True), dev(t["D"], True), dev(t["delta_bias"], True)
+    dout = dev(dout_np)
+    ck = torch.empty((w.batch, w.dim, binding.checkpoint_count(w.seqlen), w.dstate), dtype=torch.float32,
+                     device="cuda")
+    binding.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, w.softplus, checkpoints=ck)
+
+    def step():
+        binding.ssm_scan_bwd(u, delta, A, B, C, dout, ck, D=D, z=z, delta_bias=bias,
+                             delta_softplus=w.softplus)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    k_s = float(np.mean(ms)) / 1e3
+    ops = bwd_alu_ops(w)
+    tops = ops / k_s / 1e12
+    nbytes = bwd_bytes(w)
+    gbs = nbytes / k_s / 1e9
+    rec = {
+        "metric": "selective-scan bwd elements/s (b·d·l), all input gradients",
+        "value": w.elements * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} backward: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} "
+                        f"B/C {w.bc_kind}, {'bf16' if io == BF16 else 'fp32'} io, fp32 state, checkpoints "
+                        f"every 32 timesteps from the forward",
+            "elements_per_step": w.elements,
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": tops,
+            "peak": ALU_PEAK_TOPS,
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)",
+            "frac": tops / ALU_PEAK_TOPS,
+            "traffic": load_traffic(f"{w.name}_bwd", BWD_SRCS),
+            "kernel": "scan_bwd_kernel (+ the partial-sum kernels: the step's events bracket both)",
+            "kernel_avg_ms": k_s * 1e3,
+            "kernel_median_ms": float(np.median(ms)),
+            "hbm": {"achieved_GBs": gbs, "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": nbytes},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else bwd_cpu_baseline(w, t, dout_np, args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bwd_cpu_baseline(w, t, dout, budget_s: float):
+    """The oracle's backward (one thread: it has no parallel loop) on the first
+    channels of batch 0's first group, grown until it takes about budget_s."""
+    from oracle import oracle as orc
+    cpg = w.dim // w.ngroups
+    nch = 8
+    while True:
+        ch = slice(0, nch)
+        sub = {k: v for k, v in t.items()}
+        for k in ("u", "delta", "z"):
+            sub[k] = None if t[k] is None else np.ascontiguousarray(t[k][0:1, ch])
+        for k in ("B", "C"):
+            sub[k] = np.ascontiguousarray(t[k][ch] if t[k].ndim == 2 else t[k][0:1, 0:1])
+        for k in ("A", "D", "delta_bias"):
+            sub[k] = None if t[k] is None else np.ascontiguousarray(t[k][ch])
+        d64 = dout[0:1, ch]
+        d64 = (d64.astype(np.uint32) << 16).view(np.float32) if d64.dtype == np.uint16 else d64
+        t0 = time.perf_counter()
+        orc.selective_scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], d64.astype(np.float64),
+                               sub["D"], sub["z"], sub["delta_bias"], w.softplus, io_dtype=w.io_dtype,
+                               ngroups=1, B_kind=orc.BC_FIXED if t["B"].ndim == 2 else orc.BC_VARYING,
+                               C_kind=orc.BC_FIXED if t["C"].ndim == 2 else orc.BC_VARYING)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or nch >= cpg:
+            break
+        nch = min(cpg, nch * 4)
+    return {"value": nch * w.seqlen / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nch} channels of batch 0 x full seqlen {w.seqlen} (backward), {dt:.1f} s float64 "
+                      f"on 1 thread"}
 
 
 if __name__ == "__main__":

@@ -175,11 +175,9 @@ typedef struct ssm_scan_bwd_args {
  *
  * (softplus' = 1 without delta_softplus).  Every chunk of SSM_CKPT_INTERVAL
  * timesteps is re-run forward from its checkpoint, then walked in reverse.
- * Sums over batches, and over the workgroups of a group, are combined in a
- * fixed order; inside a workgroup the time-varying dB/dC terms of its waves
- * are added with LDS atomics, so those two can differ between runs in the
- * last bits (fp32 rounding), every other output is bit-for-bit repeatable.
- * Same conventions and status codes as ssm_scan_fwd. */
+ * Every sum over channels, batches and timesteps is taken in a fixed order,
+ * so results are bit-for-bit repeatable.  Same conventions and status codes
+ * as ssm_scan_fwd. */
 int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssm_scan_bwd (no HIP call). */

@@ -10,27 +10,34 @@
 //
 // Work decomposition.  A channel (b, d) is one 16-lane row of a wave; lane s
 // of the row owns state s (dstate <= 16, padded states are inert zeros), so
-// a wave holds 4 channels and a 512-thread workgroup 32 channels of one
-// (batch, group).  The sequence is walked in chunks of SSM_CKPT_INTERVAL = 32
-// timesteps from the last to the first:
+// a wave holds 4 channels and a 768-thread workgroup (3 waves per SIMD) 48
+// channels of one (batch, group).  The sequence is walked in chunks of
+// SSM_CKPT_INTERVAL = 32 timesteps from the last to the first:
 //   * per chunk every row re-runs the forward recurrence from the state the
-//     forward saved at the chunk's start, keeping x_{t-1} and a_t of each
-//     timestep in registers (64 VGPRs), then walks the chunk backwards;
+//     forward saved at the chunk's start, keeping x_{t-1} of each timestep in
+//     registers (32 VGPRs), then walks the chunk backwards, recomputing the
+//     decay a_t = exp(delta'_t A) (cheaper than 32 more live registers);
+//   * the owned timesteps' inputs and the checkpoint of the next chunk are
+//     loaded one chunk ahead;
 //   * the per-(channel, timestep) scalars -- delta', delta'*u, g, u -- are
 //     computed once by the lane that owns the timestep (lane j of a row owns
-//     timesteps j and j+16) and handed to the row through a small per-wave
-//     LDS array read 4 timesteps per vector load;
-//   * sums over the states (y for dz; sum_s h B and the delta' gradient) go
-//     through a per-wave LDS transpose in batches of 8 timesteps and are
-//     finished by the owning lanes, which also store du, ddelta and dz;
+//     timesteps j and j+16) and stay in its registers; the row reads them by
+//     DPP row broadcast (row_newbcast), mostly folded into the multiply that
+//     consumes them;
+//   * sums over the states (y for dz; sum_s h B and the delta' gradient) are
+//     a DPP reduce-scatter over the row in batches of 16 timesteps, which
+//     leaves the sum of timestep 16H + j on lane j -- its owner, which
+//     stores du, ddelta and dz.  No LDS traffic and no waits inside a chunk
+//     apart from the B/C tile reads and the dB/dC accumulator;
 //   * dB/dC of time-varying B/C are sums over every channel of the group:
 //     the wave folds its 4 rows with the gfx950 row-swap instructions
 //     (v_permlane32_swap, v_permlane16_swap) so that each lane ends with one
-//     (state, timestep) value, adds it to the workgroup's LDS accumulator of
-//     the chunk (an LDS atomic: the 8 waves' terms land in arrival order, so
-//     dB/dC may differ between runs by rounding), and after the chunk's
-//     barrier the workgroup writes its partial sums; a second kernel adds the
-//     workgroups' partials in a fixed order;
+//     (state, timestep) value, and stores it to the wave's own LDS slot of
+//     the chunk; after the chunk's barrier the workgroup adds its waves'
+//     slots in wave order and writes its partial sums, and a second kernel
+//     adds the workgroups' partials in a fixed order (no atomics anywhere:
+//     every output is bit-for-bit repeatable; LDS float atomics cost more
+//     than half the kernel's time when measured);
 //   * dA, fixed-B/C gradients, dD and d(delta_bias) are accumulated per lane
 //     over the whole sequence and written as per-batch partials, summed over
 //     the batch by the same second kernel.
@@ -46,13 +53,12 @@ namespace ssm {
 namespace {
 
 constexpr int kT = SSM_CKPT_INTERVAL;   // timesteps per chunk (= checkpoint spacing)
-constexpr int kWaves = 8;               // waves per workgroup
+constexpr int kWaves = 12;              // waves per workgroup (3 per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCPW = 4;                 // channels per wave (one 16-lane row each)
 constexpr int kCPB = kWaves * kCPW;     // channels per workgroup
 constexpr int kNP = 16;                 // lanes (states) per channel
 constexpr int kRow = 36;                // padded LDS row, in floats
-constexpr int kRB = 8;                  // timesteps per reduction batch
 static_assert(kT == 32, "the chunk layout assumes 32 timesteps");
 
 struct BwdParams {
@@ -82,20 +88,60 @@ __device__ __forceinline__ void swap16(float &x, float &y) {
   y = __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void lds_add(float *p, float v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+template <int I>
+__device__ __forceinline__ float f4get(const float4 &v) {
+  if constexpr (I == 0) return v.x;
+  else if constexpr (I == 1) return v.y;
+  else if constexpr (I == 2) return v.z;
+  else return v.w;
 }
 
-// LDS handoff between the lanes of one wave (see scan_kernel.h).
-__device__ __forceinline__ void wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// Lane K of the row broadcast to the row, kept in a register (for operands
+// the compiler cannot fold a DPP source into).
+template <int K>
+__device__ __forceinline__ float row_bcast_reg(float v) {
+  float r = row_bcast<K>(v);
+  asm volatile("" : "+v"(r));
+  return r;
+}
 
-template <bool BF16, bool BV, bool CV>
-__global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
+// v[j] is this lane's term for timestep j of a 16-timestep batch; returns the
+// sum of v[s] over the row's 16 lanes for s = lane & 15.  Recursive halving:
+// each step pairs lanes that differ in one lane bit (8: row_ror:8, 4:
+// row_half_mirror, 2 and 1: quad permutes), every lane keeps the half of its
+// values its bit selects and adds the partner's copy of that half.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int s) {
+  const bool b3 = s & 8, b2 = s & 4, b1 = s & 2, b0 = s & 1;
+  float r8[8], r4[4], r2[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = b3 ? v[k + 8] : v[k], send = b3 ? v[k] : v[k + 8];
+    r8[k] = keep + dpp<0x128>(send);          // row_ror:8
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b2 ? r8[k + 4] : r8[k], send = b2 ? r8[k] : r8[k + 4];
+    r4[k] = keep + dpp<0x141>(send);          // row_half_mirror
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b1 ? r4[k + 2] : r4[k], send = b1 ? r4[k] : r4[k + 2];
+    r2[k] = keep + dpp<0x4E>(send);           // quad_perm [2,3,0,1]
+  }
+  const float keep = b0 ? r2[1] : r2[0], send = b0 ? r2[0] : r2[1];
+  return keep + dpp<0xB1>(send);              // quad_perm [1,0,3,2]
+}
+
+template <bool BF16, bool BV, bool CV, bool HZ>
+__global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p) {
   constexpr bool ANYV = BV || CV;
   __shared__ __align__(16) float s_bc[2][2][kNP][kRow];               // B/C tiles, double-buffered
-  __shared__ __align__(16) float s_acc[ANYV ? 2 : 1][2][kNP][kT];     // dB/dC of a chunk, double-buffered
-  __shared__ __align__(16) float s_cast[kWaves][4][kCPW][kT];         // delta', delta'*u, g, u
-  __shared__ __align__(16) float s_red[kWaves][kCPW][kRB][kRow];      // state-sum transpose
+  // each wave's dB/dC terms of a chunk (its 4 channels summed), double-buffered
+  __shared__ float s_slot[ANYV ? 2 : 1][ANYV ? kWaves : 1][2][kNP][kT + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -121,13 +167,13 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
   const float Cf = (!CV && sv) ? load_io<BF16>(p.C, dl * n + s) : 0.0f;
   const float bias = p.dbias ? p.dbias[dl] : 0.0f;
   const float Dd = p.D ? p.D[dl] : 0.0f;
-  const bool hz = p.z != nullptr;
 
   // ---- B/C tile of a chunk: thread -> (tensor, state, 2 timesteps)
-  const int tq = tid >> 8;
+  const bool t_thr = tid < 2 * kNP * kT / 2;     // 512 threads move a tile, 2 elements each
+  const int tq = (tid >> 8) & 1;
   const int ts = (tid >> 4) & 15;
   const int tt = (tid & 15) * 2;
-  const bool t_on = (tq == 0 ? BV : CV) && ts < n;
+  const bool t_on = t_thr && (tq == 0 ? BV : CV) && ts < n;
   float tile0 = 0.0f, tile1 = 0.0f;
   auto fetch_tile = [&](int ci) {
     tile0 = tile1 = 0.0f;
@@ -140,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
     }
   };
   auto store_tile = [&](int buf) {
-    *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(tile0, tile1);
+    if (t_thr) *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(tile0, tile1);
   };
 
   // ---- running state of this lane
@@ -148,11 +194,26 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
   float dA_acc = 0.0f, dBf_acc = 0.0f, dCf_acc = 0.0f;
   float accD = 0.0f, accBias = 0.0f;          // owner sums over its timesteps
 
+  // this lane's two owned timesteps (s, s + 16) of a chunk, and the lane's
+  // checkpoint: loaded one chunk ahead of their use
+  float r_u[2], r_d[2], r_go[2], r_z[2], r_x;
+  auto fetch_own = [&](int ci) {
+    const int64_t t0 = static_cast<int64_t>(ci) * kT;
+    r_x = sv ? p.ckpt[(row * p.nck + ci) * n + s] : 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t t = t0 + s + 16 * h;
+      const bool on = valid && t < L;
+      r_u[h] = on ? load_io<BF16>(p.u, rbase + t) : 0.0f;
+      r_d[h] = on ? load_io<BF16>(p.delta, rbase + t) : 0.0f;
+      r_go[h] = on ? load_io<BF16>(p.dout, rbase + t) : 0.0f;
+      r_z[h] = (HZ && on) ? load_io<BF16>(p.z, rbase + t) : 0.0f;
+    }
+  };
+
+  fetch_own(p.nck - 1);
   fetch_tile(p.nck - 1);
   store_tile(0);
-  if constexpr (ANYV) {
-    for (int i = tid; i < 2 * 2 * kNP * kT; i += kThreads) (&s_acc[0][0][0][0])[i] = 0.0f;
-  }
   __syncthreads();
 
   for (int k = 0; k < p.nck; ++k) {
@@ -161,118 +222,100 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
     const int64_t t0 = static_cast<int64_t>(ci) * kT;
     const int len = static_cast<int>((L - t0 < kT) ? L - t0 : kT);
 
-    // state at the chunk's start, and the next-earlier chunk's B/C tile
-    const float xck = sv ? p.ckpt[(row * p.nck + ci) * n + s] : 0.0f;
-    if (ci > 0) fetch_tile(ci - 1);
+    // this chunk's owned inputs and checkpoint (loaded during the previous
+    // chunk); then the next-earlier chunk's loads
+    const float xck = r_x;
+    float c_u[2], c_d[2], c_go[2], c_z[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) { c_u[h] = r_u[h]; c_d[h] = r_d[h]; c_go[h] = r_go[h]; c_z[h] = r_z[h]; }
+    if (ci > 0) {
+      fetch_own(ci - 1);
+      fetch_tile(ci - 1);
+    }
 
-    // ---- owner prologue: timesteps s and s + 16 of this row
-    float o_u[2], o_dout[2], o_dsp[2], o_z[2], o_dt[2], o_g[2];
+    // ---- owner prologue: timesteps s and s + 16 of this row.  The results
+    // stay in the owner's registers; the row reads them by DPP broadcast.
+    float o_dt[2], o_dtu[2], o_g[2], o_u[2], o_dsp[2], o_dzf[2], o_Du[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = s + 16 * h;
       const bool on = valid && t < len;
-      const int64_t e = rbase + t0 + t;
-      float uu = 0.0f, dd = 0.0f, zz = 0.0f, go = 0.0f;
-      if (on) {
-        uu = load_io<BF16>(p.u, e);
-        dd = load_io<BF16>(p.delta, e);
-        go = load_io<BF16>(p.dout, e);
-        if (hz) zz = load_io<BF16>(p.z, e);
-      }
+      float uu = c_u[h];
+      const float dd = c_d[h], go = c_go[h], zz = c_z[h];
       const float raw = dd + bias;
       float dt = p.softplus ? softplus_f(raw) : raw;
       const float dsp = p.softplus ? sigmoid_f(raw) : 1.0f;
-      const float gate = hz ? silu_f(zz) : 1.0f;
-      float gg = go * gate;
+      float gg = go;
+      if constexpr (HZ) {
+        const float sg = sigmoid_f(zz);
+        gg = go * zz * sg;                                  // dout * silu(z)
+        o_dzf[h] = go * sg * (1.0f + zz * (1.0f - sg));     // dout * silu'(z)
+      }
       if (!on) { dt = 0.0f; gg = 0.0f; uu = 0.0f; }   // inert timestep
-      o_u[h] = uu; o_dout[h] = go; o_dsp[h] = dsp; o_z[h] = zz; o_dt[h] = dt; o_g[h] = gg;
-      s_cast[w][0][c][t] = dt;
-      s_cast[w][1][c][t] = dt * uu;
-      s_cast[w][2][c][t] = gg;
-      s_cast[w][3][c][t] = uu;
+      o_dt[h] = dt;
+      o_dtu[h] = dt * uu;
+      o_g[h] = gg;
+      o_u[h] = uu;
+      o_dsp[h] = dsp;
+      o_Du[h] = Dd * uu;
+      accD = fmaf(gg, uu, accD);
     }
-    wave_sync();
 
     const float(*bt)[kRow] = s_bc[kb][0];
     const float(*ct)[kRow] = s_bc[kb][1];
 
     // ---- forward re-run of the chunk
-    float xs[kT], as[kT];
+    float xs[kT];
     float x = xck;
     float Y[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int t4 = 0; t4 < kT; t4 += 4) {
-      const float4 dt4 = *reinterpret_cast<const float4 *>(&s_cast[w][0][c][t4]);
-      const float4 du4 = *reinterpret_cast<const float4 *>(&s_cast[w][1][c][t4]);
-      float4 B4 = make_float4(Bf, Bf, Bf, Bf), C4 = make_float4(Cf, Cf, Cf, Cf);
-      if constexpr (BV) B4 = *reinterpret_cast<const float4 *>(&bt[s][t4]);
-      if constexpr (CV) { if (hz) C4 = *reinterpret_cast<const float4 *>(&ct[s][t4]); }
-      const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
-      const float duv[4] = {du4.x, du4.y, du4.z, du4.w};
-      const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
-      const float Cv[4] = {C4.x, C4.y, C4.z, C4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t4 + i;
-        const float a = fast_exp2(dtv[i] * Ap);
-        xs[t] = x;
-        as[t] = a;
-        x = fmaf(a, x, duv[i] * Bv[i]);
-        if (hz) s_red[w][c][t % kRB][s] = Cv[i] * x;
+    float cx[16];
+    float4 B4, C4;
+    static_for(std::make_integer_sequence<int, kT>{}, [&](auto TT) {
+      constexpr int t = decltype(TT)::value;
+      constexpr int K = t & 15, H = t >> 4;
+      if constexpr ((t & 3) == 0) {
+        B4 = make_float4(Bf, Bf, Bf, Bf);
+        C4 = make_float4(Cf, Cf, Cf, Cf);
+        if constexpr (BV) B4 = *reinterpret_cast<const float4 *>(&bt[s][t]);
+        if constexpr (CV && HZ) C4 = *reinterpret_cast<const float4 *>(&ct[s][t]);
       }
-      if (hz && (t4 % kRB) == kRB - 4) {
-        // y of the batch's 8 timesteps, summed by their owners
-        wave_sync();
-        const int tb = t4 / kRB;
-        if ((s >> 3) == (tb & 1)) {
-          const float4 *r = reinterpret_cast<const float4 *>(&s_red[w][c][s & 7][0]);
-          const float4 r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3];
-          Y[tb >> 1] = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w)) +
-                       ((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w));
-        }
-        wave_sync();
+      const float Bv = f4get<t & 3>(B4), Cv = f4get<t & 3>(C4);
+      const float a = fast_exp2(row_bcast<K>(o_dt[H]) * Ap);
+      xs[t] = x;
+      x = fmaf(a, x, row_bcast<K>(o_dtu[H]) * Bv);
+      if constexpr (HZ) {
+        cx[K] = Cv * x;
+        if constexpr (K == 15) Y[H] = row_reduce_scatter16(cx, s);   // y of timestep 16H + s
       }
-    }
+      if constexpr ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    });
     const float x_end = x;
 
     // ---- dz (needs only the forward)
-    if (hz) {
+    if constexpr (HZ) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = s + 16 * h;
-        if (valid && t < len) {
-          const float pre = Y[h] + Dd * o_u[h];
-          const float sg = sigmoid_f(o_z[h]);
-          const float dsilu = sg * (1.0f + o_z[h] * (1.0f - sg));
-          store_one<BF16>(p.dz, rbase + t0 + t, o_dout[h] * pre * dsilu);
-        }
+        if (valid && t < len) store_one<BF16>(p.dz, rbase + t0 + t, o_dzf[h] * (Y[h] + o_Du[h]));
       }
     }
 
     // ---- reverse walk of the chunk
     float pb_hi = 0.0f, pc_hi = 0.0f;   // dB/dC values of the odd timestep of a pair
-    float4 dt4, du4, g4, u4, B4, C4;
-#pragma unroll
-    for (int t = kT - 1; t >= 0; --t) {
-      const int i = t & 3;
-      if (i == 3) {
-        const int t4 = t - 3;
-        dt4 = *reinterpret_cast<const float4 *>(&s_cast[w][0][c][t4]);
-        du4 = *reinterpret_cast<const float4 *>(&s_cast[w][1][c][t4]);
-        g4 = *reinterpret_cast<const float4 *>(&s_cast[w][2][c][t4]);
-        u4 = *reinterpret_cast<const float4 *>(&s_cast[w][3][c][t4]);
+    float hb[16], qv[16];
+    static_for(std::make_integer_sequence<int, kT>{}, [&](auto RR) {
+      constexpr int t = kT - 1 - decltype(RR)::value;
+      constexpr int K = t & 15, H = t >> 4;
+      if constexpr ((t & 3) == 3) {
         B4 = make_float4(Bf, Bf, Bf, Bf);
         C4 = make_float4(Cf, Cf, Cf, Cf);
-        if constexpr (BV) B4 = *reinterpret_cast<const float4 *>(&bt[s][t4]);
-        if constexpr (CV) C4 = *reinterpret_cast<const float4 *>(&ct[s][t4]);
+        if constexpr (BV) B4 = *reinterpret_cast<const float4 *>(&bt[s][t - 3]);
+        if constexpr (CV) C4 = *reinterpret_cast<const float4 *>(&ct[s][t - 3]);
       }
-      const float dt = i == 0 ? dt4.x : i == 1 ? dt4.y : i == 2 ? dt4.z : dt4.w;
-      const float dtu = i == 0 ? du4.x : i == 1 ? du4.y : i == 2 ? du4.z : du4.w;
-      const float gg = i == 0 ? g4.x : i == 1 ? g4.y : i == 2 ? g4.z : g4.w;
-      const float uu = i == 0 ? u4.x : i == 1 ? u4.y : i == 2 ? u4.z : u4.w;
-      const float Bv = i == 0 ? B4.x : i == 1 ? B4.y : i == 2 ? B4.z : B4.w;
-      const float Cv = i == 0 ? C4.x : i == 1 ? C4.y : i == 2 ? C4.z : C4.w;
-      const float a = as[t];
+      const float Bv = f4get<t & 3>(B4), Cv = f4get<t & 3>(C4);
+      const float dt = row_bcast_reg<K>(o_dt[H]);
+      const float gg = row_bcast_reg<K>(o_g[H]);
+      const float a = fast_exp2(dt * Ap);
       const float xp = xs[t];
       const float xt = t + 1 < kT ? xs[t + 1] : x_end;
 
@@ -280,15 +323,15 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
       const float hax = h * (a * xp);
       dA_acc = fmaf(hax, dt, dA_acc);
       const float hB = h * Bv;
-      const float q = fmaf(Av, hax, uu * hB);
-      *reinterpret_cast<float2 *>(&s_red[w][c][t % kRB][2 * s]) = make_float2(hB, q);
+      hb[K] = hB;
+      qv[K] = fmaf(Av, hax, row_bcast<K>(o_u[H]) * hB);
       gcar = h * a;
 
       float vb = 0.0f, vc = 0.0f;
-      if constexpr (BV) vb = h * dtu; else dBf_acc = fmaf(h, dtu, dBf_acc);
+      if constexpr (BV) vb = h * row_bcast<K>(o_dtu[H]); else dBf_acc = fmaf(h, row_bcast<K>(o_dtu[H]), dBf_acc);
       if constexpr (CV) vc = gg * xt; else dCf_acc = fmaf(gg, xt, dCf_acc);
       if constexpr (ANYV) {
-        if (t & 1) {
+        if constexpr (t & 1) {
           pb_hi = vb;
           pc_hi = vc;
         } else {
@@ -303,49 +346,38 @@ __global__ void __launch_bounds__(kThreads) scan_bwd_kernel(const BwdParams p) {
           swap16(r1, r2);
           const float v = r1 + r2;   // rows: dB(t+1), dB(t), dC(t+1), dC(t)
           const int rw = lane >> 4;
-          lds_add(&s_acc[kb][rw >> 1][s][t + 1 - (rw & 1)], v);
+          s_slot[kb][w][rw >> 1][s][t + 1 - (rw & 1)] = v;
         }
       }
 
-      if ((t % kRB) == 0) {
-        // sum over states of the batch [t, t+8): owners finish du, ddelta
-        wave_sync();
-        const int tb = t / kRB;
-        if ((s >> 3) == (tb & 1)) {
-          const int hh = tb >> 1;
-          const int to = s + 16 * hh;
-          const float4 *r = reinterpret_cast<const float4 *>(&s_red[w][c][s & 7][0]);
-          float S1 = 0.0f, Q = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float4 v = r[j];
-            S1 += v.x + v.z;
-            Q += v.y + v.w;
-          }
-          if (valid && to < len) {
-            const float ddl = Q * o_dsp[hh];
-            store_one<BF16>(p.du, rbase + t0 + to, fmaf(o_dt[hh], S1, Dd * o_g[hh]));
-            store_one<BF16>(p.ddelta, rbase + t0 + to, ddl);
-            accD = fmaf(o_g[hh], o_u[hh], accD);
-            accBias += ddl;
-          }
+      if constexpr (K == 0) {
+        // sums over the states of timesteps [16H, 16H+16): lane s gets 16H + s
+        const float S1 = row_reduce_scatter16(hb, s);
+        const float Q = row_reduce_scatter16(qv, s);
+        const int to = s + 16 * H;
+        if (valid && to < len) {
+          const float ddl = Q * o_dsp[H];
+          store_one<BF16>(p.du, rbase + t0 + to, fmaf(o_dt[H], S1, Dd * o_g[H]));
+          store_one<BF16>(p.ddelta, rbase + t0 + to, ddl);
+          accBias += ddl;
         }
-        wave_sync();
       }
-    }
+      if constexpr ((t & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+    });
 
     // next tile into the other buffer; after the barrier the chunk's dB/dC
     // accumulator is complete
     if (ci > 0) store_tile(kb ^ 1);
     __syncthreads();
-    if constexpr (ANYV) {
-      const int fq = tid >> 8;
-      const int fs = (tid >> 4) & 15;
-      const int ft = (tid & 15) * 2;
-      float *acc = &s_acc[kb][fq][fs][ft];
-      const float v0 = acc[0], v1 = acc[1];
-      acc[0] = 0.0f;
-      acc[1] = 0.0f;
+    if (ANYV && t_thr) {
+      // the workgroup's sum: its waves' slots added in wave order
+      const int fq = tq, fs = ts, ft = tt;
+      float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        v0 += s_slot[kb][ww][fq][fs][ft];
+        v1 += s_slot[kb][ww][fq][fs][ft + 1];
+      }
       if ((fq == 0 ? BV : CV) && fs < n) {
         float *dst = (fq == 0 ? p.pB : p.pC) + ((static_cast<int64_t>(bg) * p.nblk + blk) * n + fs) * L + t0 + ft;
         if (ft < len) dst[0] = v0;
@@ -387,12 +419,16 @@ __global__ void __launch_bounds__(256) sum_mid_kernel(const float *in, float *ou
 
 using BwdFn = void (*)(const BwdParams);
 
+template <bool BF16, bool HZ>
+BwdFn pick_bc(bool bv, bool cv) {
+  if (bv && cv) return scan_bwd_kernel<BF16, true, true, HZ>;
+  if (bv) return scan_bwd_kernel<BF16, true, false, HZ>;
+  if (cv) return scan_bwd_kernel<BF16, false, true, HZ>;
+  return scan_bwd_kernel<BF16, false, false, HZ>;
+}
 template <bool BF16>
-BwdFn pick_bwd(bool bv, bool cv) {
-  if (bv && cv) return scan_bwd_kernel<BF16, true, true>;
-  if (bv) return scan_bwd_kernel<BF16, true, false>;
-  if (cv) return scan_bwd_kernel<BF16, false, true>;
-  return scan_bwd_kernel<BF16, false, false>;
+BwdFn pick_bwd(bool bv, bool cv, bool hz) {
+  return hz ? pick_bc<BF16, true>(bv, cv) : pick_bc<BF16, false>(bv, cv);
 }
 
 struct BwdPlan {
@@ -471,7 +507,8 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   p.nblk = static_cast<int>(pl.nblk); p.nck = static_cast<int>(pl.nck);
   p.softplus = a->delta_softplus;
 
-  const BwdFn f = bf16 ? pick_bwd<true>(bv, cv) : pick_bwd<false>(bv, cv);
+  const bool hz = a->z != nullptr;
+  const BwdFn f = bf16 ? pick_bwd<true>(bv, cv, hz) : pick_bwd<false>(bv, cv, hz);
   hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(pl.blocks)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
 

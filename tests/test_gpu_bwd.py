@@ -164,21 +164,15 @@ def test_checkpoints_are_the_forward_states():
         assert e <= TOL[F32], f"checkpoint {k}: {e:.3e}"
 
 
-def test_bwd_repeatable():
-    """Two runs agree bit for bit except time-varying dB/dC, whose sum over the
-    waves of a workgroup is taken with LDS atomics in arrival order: there the
-    runs differ by fp32 rounding only."""
+def test_bwd_deterministic():
+    """Every sum is taken in a fixed order: two runs agree bit for bit."""
     w = BASE.scaled(io_dtype=BF16, dim=64, ngroups=2, seed=580)
     t = make_inputs(w)
     dout = make_dout(w)
     a = _gpu(w, t, dout)
     b = _gpu(w, t, dout)
     for k, v in a.items():
-        if v is None:
-            continue
-        if k in ("dB", "dC"):
-            assert np.max(np.abs(v - b[k]) / (1.0 + np.abs(v))) <= 1e-5, k
-        else:
+        if v is not None:
             np.testing.assert_array_equal(v, b[k], err_msg=k)
 
 
