@@ -88,6 +88,17 @@ __device__ __forceinline__ void swap16(float &x, float &y) {
   y = __uint_as_float(r[1]);
 }
 
+// One io element as stored (bf16: zero-extended 16 bits), and its value.
+template <bool BF16>
+__device__ __forceinline__ uint32_t raw_load(const void *p, int64_t i) {
+  if constexpr (BF16) return static_cast<const uint16_t *>(p)[i];
+  else return static_cast<const uint32_t *>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ float raw_float(uint32_t r) {
+  return __uint_as_float(BF16 ? r << 16 : r);
+}
+
 template <int I>
 __device__ __forceinline__ float f4get(const float4 &v) {
   if constexpr (I == 0) return v.x;
@@ -103,8 +114,10 @@ __device__ __forceinline__ float dpp(float v) {
 // Lane K of the row broadcast to the row, kept in a register (for operands
 // the compiler cannot fold a DPP source into).
 template <int K>
+__device__ __forceinline__ float bc(float v) { return dpp<0x150 + K>(v); }   // row_newbcast:K
+template <int K>
 __device__ __forceinline__ float row_bcast_reg(float v) {
-  float r = row_bcast<K>(v);
+  float r = bc<K>(v);
   asm volatile("" : "+v"(r));
   return r;
 }
@@ -174,19 +187,22 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
   const int ts = (tid >> 4) & 15;
   const int tt = (tid & 15) * 2;
   const bool t_on = t_thr && (tq == 0 ? BV : CV) && ts < n;
-  float tile0 = 0.0f, tile1 = 0.0f;
+  // Loads keep the raw io bits and convert at the point of use, so that no
+  // wait for them lands inside the guarded load.
+  uint32_t tile0 = 0, tile1 = 0;
   auto fetch_tile = [&](int ci) {
-    tile0 = tile1 = 0.0f;
+    tile0 = tile1 = 0;
     if (t_on) {
       const int64_t t0 = static_cast<int64_t>(ci) * kT + tt;
       const void *src = tq == 0 ? p.B : p.C;
       const int64_t e = bc_base + ts * L + t0;
-      if (t0 < L) tile0 = load_io<BF16>(src, e);
-      if (t0 + 1 < L) tile1 = load_io<BF16>(src, e + 1);
+      if (t0 < L) tile0 = raw_load<BF16>(src, e);
+      if (t0 + 1 < L) tile1 = raw_load<BF16>(src, e + 1);
     }
   };
   auto store_tile = [&](int buf) {
-    if (t_thr) *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(tile0, tile1);
+    if (t_thr)
+      *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(raw_float<BF16>(tile0), raw_float<BF16>(tile1));
   };
 
   // ---- running state of this lane
@@ -196,18 +212,22 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
 
   // this lane's two owned timesteps (s, s + 16) of a chunk, and the lane's
   // checkpoint: loaded one chunk ahead of their use
-  float r_u[2], r_d[2], r_go[2], r_z[2], r_x;
+  uint32_t r_u[2], r_d[2], r_go[2], r_z[2];
+  float r_x;
   auto fetch_own = [&](int ci) {
     const int64_t t0 = static_cast<int64_t>(ci) * kT;
-    r_x = sv ? p.ckpt[(row * p.nck + ci) * n + s] : 0.0f;
+    r_x = 0.0f;
+    if (sv) r_x = p.ckpt[(row * p.nck + ci) * n + s];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t t = t0 + s + 16 * h;
-      const bool on = valid && t < L;
-      r_u[h] = on ? load_io<BF16>(p.u, rbase + t) : 0.0f;
-      r_d[h] = on ? load_io<BF16>(p.delta, rbase + t) : 0.0f;
-      r_go[h] = on ? load_io<BF16>(p.dout, rbase + t) : 0.0f;
-      r_z[h] = (HZ && on) ? load_io<BF16>(p.z, rbase + t) : 0.0f;
+      r_u[h] = r_d[h] = r_go[h] = r_z[h] = 0;
+      if (valid && t < L) {
+        r_u[h] = raw_load<BF16>(p.u, rbase + t);
+        r_d[h] = raw_load<BF16>(p.delta, rbase + t);
+        r_go[h] = raw_load<BF16>(p.dout, rbase + t);
+        if constexpr (HZ) r_z[h] = raw_load<BF16>(p.z, rbase + t);
+      }
     }
   };
 
@@ -227,7 +247,12 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
     const float xck = r_x;
     float c_u[2], c_d[2], c_go[2], c_z[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) { c_u[h] = r_u[h]; c_d[h] = r_d[h]; c_go[h] = r_go[h]; c_z[h] = r_z[h]; }
+    for (int h = 0; h < 2; ++h) {
+      c_u[h] = raw_float<BF16>(r_u[h]);
+      c_d[h] = raw_float<BF16>(r_d[h]);
+      c_go[h] = raw_float<BF16>(r_go[h]);
+      c_z[h] = raw_float<BF16>(r_z[h]);
+    }
     if (ci > 0) {
       fetch_own(ci - 1);
       fetch_tile(ci - 1);
@@ -280,9 +305,9 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
         if constexpr (CV && HZ) C4 = *reinterpret_cast<const float4 *>(&ct[s][t]);
       }
       const float Bv = f4get<t & 3>(B4), Cv = f4get<t & 3>(C4);
-      const float a = fast_exp2(row_bcast<K>(o_dt[H]) * Ap);
+      const float a = fast_exp2(bc<K>(o_dt[H]) * Ap);
       xs[t] = x;
-      x = fmaf(a, x, row_bcast<K>(o_dtu[H]) * Bv);
+      x = fmaf(a, x, bc<K>(o_dtu[H]) * Bv);
       if constexpr (HZ) {
         cx[K] = Cv * x;
         if constexpr (K == 15) Y[H] = row_reduce_scatter16(cx, s);   // y of timestep 16H + s
@@ -324,11 +349,11 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
       dA_acc = fmaf(hax, dt, dA_acc);
       const float hB = h * Bv;
       hb[K] = hB;
-      qv[K] = fmaf(Av, hax, row_bcast<K>(o_u[H]) * hB);
+      qv[K] = fmaf(Av, hax, bc<K>(o_u[H]) * hB);
       gcar = h * a;
 
       float vb = 0.0f, vc = 0.0f;
-      if constexpr (BV) vb = h * row_bcast<K>(o_dtu[H]); else dBf_acc = fmaf(h, row_bcast<K>(o_dtu[H]), dBf_acc);
+      if constexpr (BV) vb = h * bc<K>(o_dtu[H]); else dBf_acc = fmaf(h, bc<K>(o_dtu[H]), dBf_acc);
       if constexpr (CV) vc = gg * xt; else dCf_acc = fmaf(gg, xt, dCf_acc);
       if constexpr (ANYV) {
         if constexpr (t & 1) {
