@@ -86,6 +86,8 @@ def _load():
             i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
             p, p, p, p, p, p, p, p, p]
         lib.oracle_selective_scan_bwd.restype = i32
+        lib.oracle_causal_conv1d_ex.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, p, p, p, p]
+        lib.oracle_causal_conv1d_ex.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -306,3 +308,29 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise ValueError(f"oracle_selective_scan_bwd failed with status {rc}")
     return out
+
+
+def causal_conv1d_ex(x, weight, bias=None, act=ACT_NONE, *, io_dtype=F32, seq_idx=None,
+                     initial_states=None, want_final=False):
+    """Oracle causal_conv1d with seq_idx / initial_states / final states.
+
+    x: (batch, dim, seqlen) io bits; weight (dim, width) float32; seq_idx
+    (batch, seqlen) int32; initial_states (batch, dim, width-1) io bits.
+    Returns (out (batch, dim, seqlen) float64, final_states (batch, dim,
+    width-1) float64 or None).
+    """
+    lib = _load()
+    x = _io(x, io_dtype)
+    batch, dim, seqlen = x.shape
+    weight = _f32(weight)
+    width = weight.shape[1]
+    bias = _f32(bias)
+    init = _io(initial_states, io_dtype)
+    sq = None if seq_idx is None else np.ascontiguousarray(seq_idx, dtype=np.int32)
+    out = np.empty((batch, dim, seqlen))
+    fin = np.empty((batch, dim, width - 1)) if want_final else None
+    rc = lib.oracle_causal_conv1d_ex(batch, dim, seqlen, width, io_dtype, _ptr(x), _ptr(weight), _ptr(bias),
+                                     act, _ptr(sq), _ptr(init), _ptr(out), _ptr(fin))
+    if rc != 0:
+        raise ValueError(f"oracle_causal_conv1d_ex failed with status {rc}")
+    return out, fin

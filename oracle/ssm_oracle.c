@@ -147,6 +147,48 @@ int oracle_causal_conv1d(int64_t batch, int64_t dim, int64_t seqlen, int width,
     return 0;
 }
 
+/* causal_conv1d with the optional inputs of the same page section
+ * (causal_conv1d_fn's seq_idx, initial_states, return_final_states):
+ *   the input is extended to the left by initial_states[b,d,0..W-2] (oldest
+ *   first; zeros when not given), xe[t] for t in [-(W-1), l);
+ *   out[b,d,t] = act(bias[d] + sum_k w[d,k] * xe[t-(W-1)+k]), where with
+ *   seq_idx a tap contributes only if its position is >= 0 and carries the
+ *   same sequence id as t (each packed sequence restarts from zero);
+ *   final_states[b,d,j] = xe[l-(W-1)+j], the last W-1 inputs (raw values).
+ * seq_idx: (batch, seqlen) int32 or NULL; initial_states: (b,d,W-1) io or
+ * NULL; out: (b,d,l) double; final_states: (b,d,W-1) double or NULL. */
+int oracle_causal_conv1d_ex(int64_t batch, int64_t dim, int64_t seqlen, int width,
+                            int io_dtype, const void *x, const float *weight,
+                            const float *bias, int act, const int32_t *seq_idx,
+                            const void *initial_states, double *out, double *final_states) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || width <= 0) return 2;
+    if (!x || !weight || !out) return 1;
+    const int H = width - 1;
+    for (int64_t row = 0; row < batch * dim; ++row) {
+        const int64_t b = row / dim, d = row % dim;
+        const int64_t base = row * seqlen;
+        /* the value at extended position src in [-(W-1), l) */
+#define XE(src) ((src) >= 0 ? load_io(x, io_dtype, base + (src)) \
+                 : (initial_states ? load_io(initial_states, io_dtype, row * H + H + (src)) : 0.0))
+        for (int64_t t = 0; t < seqlen; ++t) {
+            double acc = bias ? (double)bias[d] : 0.0;
+            for (int k = 0; k < width; ++k) {
+                const int64_t src = t - H + k;
+                if (seq_idx) {
+                    if (src < 0 || seq_idx[b * seqlen + src] != seq_idx[b * seqlen + t]) continue;
+                }
+                acc += (double)weight[d * width + k] * XE(src);
+            }
+            if (act == OR_ACT_SILU) acc = oracle_silu(acc);
+            out[base + t] = acc;
+        }
+        if (final_states)
+            for (int j = 0; j < H; ++j) final_states[row * H + j] = XE(seqlen - H + j);
+#undef XE
+    }
+    return 0;
+}
+
 /* ---- selective scan ------------------------------------------------------ */
 
 typedef struct {

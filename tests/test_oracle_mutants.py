@@ -255,3 +255,55 @@ def test_bwd_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the conv's optional inputs against their own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_conv_ex_pins as cpins  # noqa: E402
+
+CONV_EX_MUTANTS = {
+    "cx_seq_mask_ignored": ("if (src < 0 || seq_idx[b * seqlen + src] != seq_idx[b * seqlen + t]) continue;",
+                            "if (src < 0) continue;"),
+    "cx_initial_shifted": ("load_io(initial_states, io_dtype, row * H + H + (src))",
+                           "load_io(initial_states, io_dtype, row * H + H - 1 + (src) + ((src) == -H))"),
+    "cx_final_off_by_one": ("final_states[row * H + j] = XE(seqlen - H + j);",
+                            "final_states[row * H + j] = XE(seqlen - H + j - 1);"),
+    "cx_seq_compare_previous": ("seq_idx[b * seqlen + src] != seq_idx[b * seqlen + t]",
+                                "seq_idx[b * seqlen + src] != seq_idx[b * seqlen + (t > 0 ? t - 1 : 0)]"),
+}
+
+
+def _conv_ex_pin_calls():
+    F32, BF16 = orc.F32, orc.BF16
+    return [
+        ("plain", lambda: cpins.test_no_options_is_the_plain_conv(F32, 4)),
+        ("states_9", lambda: cpins.test_initial_and_final_states(F32, 9)),
+        ("states_2", lambda: cpins.test_initial_and_final_states(BF16, 2)),
+        ("split", cpins.test_split_continuation_through_states),
+        ("seq", lambda: cpins.test_seq_idx_packed_sequences(F32)),
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(CONV_EX_MUTANTS))
+def test_conv_ex_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = CONV_EX_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _conv_ex_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
