@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -197,6 +197,36 @@ int ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *args, size_t *bytes);
 int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, void *out,
                       int64_t batch, int64_t dim, int64_t seqlen, int32_t width,
                       int32_t io_dtype, int32_t act, void *hip_stream);
+
+/* causal_conv1d_fwd with the optional inputs of causal_conv1d_fn (same page
+ * section 4.2: seq_idx, initial_states, return_final_states /
+ * final_states_out).  Every pointer is a device pointer.
+ *  - initial_states (batch, dim, width-1) io: the inputs before t = 0, oldest
+ *    first (replacing the zero padding);
+ *  - final_states (batch, dim, width-1) io, written: the last width-1 inputs
+ *    of the row (with initial_states / zeros in front when seqlen < width-1),
+ *    copied bit for bit -- the conv cache for continuing the sequence;
+ *  - seq_idx (batch, seqlen) int32: packed sequences; a tap contributes only
+ *    when its position carries the output's id, so each sequence restarts
+ *    from zero.  Ids are expected to be contiguous per sequence.  seq_idx
+ *    with initial_states or final_states returns SSM_ERR_UNSUPPORTED (the
+ *    page: they cannot be used together).
+ * width must be 4.  Same status codes as causal_conv1d_fwd. */
+typedef struct causal_conv1d_args {
+  int64_t batch, dim, seqlen;
+  int32_t width, io_dtype, act;
+  const void *x;                                /* (b,d,l) io, required */
+  const float *weight;                          /* (d, width) fp32, required */
+  const float *bias;                            /* (d) fp32 or NULL */
+  const int32_t *seq_idx;                       /* (b,l) int32 or NULL */
+  const void *initial_states;                   /* (b,d,width-1) io or NULL */
+  void *out;                                    /* (b,d,l) io, required */
+  void *final_states;                           /* (b,d,width-1) io or NULL */
+} causal_conv1d_args_t;
+int causal_conv1d_fwd_ex(const causal_conv1d_args_t *args, void *hip_stream);
+
+/* Host-only argument check of causal_conv1d_fwd_ex (no HIP call). */
+int causal_conv1d_ex_validate(const causal_conv1d_args_t *args);
 
 /* Host-only argument check of causal_conv1d_fwd (no HIP call). */
 int causal_conv1d_validate(const void *x, const float *weight, const void *out,

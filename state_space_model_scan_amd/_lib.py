@@ -21,7 +21,7 @@ SSM_CKPT_INTERVAL = 32
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
     "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size",
-    "causal_conv1d_fwd", "causal_conv1d_validate",
+    "causal_conv1d_fwd", "causal_conv1d_validate", "causal_conv1d_fwd_ex", "causal_conv1d_ex_validate",
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
     "ssd_scan_fwd", "ssd_scan_validate",
@@ -48,6 +48,16 @@ class ScanArgs(ctypes.Structure):
         ("conv_width", ctypes.c_int32), ("conv_act", ctypes.c_int32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("checkpoints", _vp),
+    ]
+
+
+class ConvArgs(ctypes.Structure):
+    """Mirror of causal_conv1d_args_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("width", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("x", _vp), ("weight", _vp), ("bias", _vp), ("seq_idx", _vp), ("initial_states", _vp),
+        ("out", _vp), ("final_states", _vp),
     ]
 
 
@@ -140,6 +150,10 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_fwd.restype = ctypes.c_int
         L.ssd_scan_validate.argtypes = [ctypes.POINTER(SsdArgs)]
         L.ssd_scan_validate.restype = ctypes.c_int
+        L.causal_conv1d_fwd_ex.argtypes = [ctypes.POINTER(ConvArgs), _vp]
+        L.causal_conv1d_fwd_ex.restype = ctypes.c_int
+        L.causal_conv1d_ex_validate.argtypes = [ctypes.POINTER(ConvArgs)]
+        L.causal_conv1d_ex_validate.restype = ctypes.c_int
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
         L.ssm_scan_bwd.restype = ctypes.c_int
         L.ssm_scan_bwd_validate.argtypes = [ctypes.POINTER(BwdArgs)]

@@ -17,7 +17,7 @@ from typing import Optional, Tuple, Union
 import torch
 
 from . import _lib
-from ._lib import BwdArgs, ScanArgs, check
+from ._lib import BwdArgs, ConvArgs, ScanArgs, check
 
 _IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
 
@@ -235,9 +235,59 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return (out, last) if return_last_state else out
 
 
-def causal_conv1d_fn(x, weight, bias=None, activation=None) -> torch.Tensor:
-    """Forward of causal_conv1d_fn (x, weight, bias, activation)."""
-    return causal_conv1d_fwd(x, weight, bias, act=_act_code(activation))
+def causal_conv1d_fwd_ex(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                         seq_idx: Optional[torch.Tensor] = None,
+                         initial_states: Optional[torch.Tensor] = None,
+                         final_states: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, act: int = _lib.SSM_ACT_NONE,
+                         stream=None) -> torch.Tensor:
+    """Enqueue causal_conv1d_fwd_ex; returns ``out``.  ``final_states``
+    (batch, dim, width-1) in the io dtype is written when given."""
+    x = _dense(x)
+    io = _IO.get(x.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+    weight, bias = _dense(weight), _dense(bias)
+    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise ValueError("conv weight and bias must be float32")
+    batch, dim, seqlen = x.shape
+    width = weight.shape[1]
+    if seq_idx is not None:
+        seq_idx = _dense(seq_idx)
+        if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (batch, seqlen):
+            raise ValueError(f"seq_idx must be int32 of shape {(batch, seqlen)}")
+    for name, t in (("initial_states", initial_states), ("final_states", final_states)):
+        if t is not None and (t.dtype != x.dtype or tuple(t.shape) != (batch, dim, width - 1)
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {x.dtype} tensor of shape {(batch, dim, width - 1)}")
+    if out is None:
+        out = torch.empty_like(x)
+    a = ConvArgs()
+    a.batch, a.dim, a.seqlen, a.width, a.io_dtype, a.act = batch, dim, seqlen, width, io, act
+    a.x, a.weight, a.bias, a.seq_idx = _ptr(x), _ptr(weight), _ptr(bias), _ptr(seq_idx)
+    a.initial_states, a.out, a.final_states = _ptr(initial_states), _ptr(out), _ptr(final_states)
+    check(_lib.lib().causal_conv1d_fwd_ex(ctypes.byref(a), _stream(x.device, stream)))
+    return out
+
+
+def causal_conv1d_fn(x, weight, bias=None, seq_idx=None, initial_states=None, return_final_states=False,
+                     final_states_out=None, activation=None):
+    """causal_conv1d_fn with the page's signature (section 4.2): returns out,
+    or (out, final_states) with return_final_states.  seq_idx cannot be used
+    with initial_states or return_final_states."""
+    act = _act_code(activation)
+    if seq_idx is not None and (initial_states is not None or return_final_states):
+        raise ValueError("seq_idx cannot be used with initial_states or return_final_states")
+    if seq_idx is None and initial_states is None and not return_final_states:
+        return causal_conv1d_fwd(x, weight, bias, act=act)
+    fin = None
+    if return_final_states:
+        fin = final_states_out
+        if fin is None:
+            fin = torch.empty((x.shape[0], x.shape[1], weight.shape[1] - 1), dtype=x.dtype, device=x.device)
+    out = causal_conv1d_fwd_ex(x, weight, bias, seq_idx=seq_idx, initial_states=initial_states,
+                               final_states=fin, act=act)
+    return (out, fin) if return_final_states else out
 
 
 def conv1d_selective_scan_fn(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None,

@@ -30,13 +30,18 @@ int hip_fail(hipError_t e) {
 namespace {
 
 // ---------------------------------------------------------------------------
-// standalone causal depthwise conv: one thread per 8 consecutive outputs
+// standalone causal depthwise conv: one thread per 8 consecutive outputs.
+// Optional (causal_conv1d_fn's seq_idx / initial_states / final states):
+// init (b, d, 3) io prepends the three inputs before t = 0; with SEQ a tap
+// contributes only when its position carries the output's sequence id; the
+// thread holding the row's last output writes the last three inputs to fin.
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
+template <bool BF16, bool SEQ>
 __global__ void __launch_bounds__(256)
 conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
-            int64_t rows, int64_t dim, int64_t seqlen, int silu, int vec) {
+            int64_t rows, int64_t dim, int64_t seqlen, int silu, int vec,
+            const int32_t *seq_idx, const void *init, void *fin) {
   const int64_t nt8 = (seqlen + 7) / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= rows * nt8) return;
@@ -53,20 +58,48 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
   const float bb = bias ? bias[d] : 0.0f;
   float xv[11];
   xv[0] = prev.get(5); xv[1] = prev.get(6); xv[2] = prev.get(7);
+  if (t0 == 0 && init) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) xv[j] = load_io<BF16>(init, row * 3 + j);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) xv[i + 3] = cur.get(i);
+  // sequence ids of positions t0-3 .. t0+7 (positions outside [0, seqlen)
+  // hold zero inputs, so their ids do not matter)
+  int32_t sid[11];
+  if constexpr (SEQ) {
+    const int64_t sb = (row / dim) * seqlen;
+#pragma unroll
+    for (int j = 0; j < 11; ++j) {
+      const int64_t pos = t0 - 3 + j;
+      sid[j] = (pos >= 0 && pos < seqlen) ? seq_idx[sb + pos] : 0;
+    }
+  }
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    float v0 = xv[i], v1 = xv[i + 1], v2 = xv[i + 2];
+    if constexpr (SEQ) {
+      const int32_t me = sid[i + 3];
+      if (sid[i] != me) v0 = 0.0f;
+      if (sid[i + 1] != me) v1 = 0.0f;
+      if (sid[i + 2] != me) v2 = 0.0f;
+    }
     float acc = bb;
-    acc = fmaf(w0, xv[i], acc);
-    acc = fmaf(w1, xv[i + 1], acc);
-    acc = fmaf(w2, xv[i + 2], acc);
+    acc = fmaf(w0, v0, acc);
+    acc = fmaf(w1, v1, acc);
+    acc = fmaf(w2, v2, acc);
     acc = fmaf(w3, xv[i + 3], acc);
     if (silu) acc = silu_f(acc);
     o[i] = acc;
   }
   store8<BF16>(out, rb + t0, o, cnt, vec != 0);
+  if (fin && t0 + 8 >= seqlen) {
+    // the extended input at seqlen-3+j sits at xv[seqlen - t0 + j]
+    const int e = static_cast<int>(seqlen - t0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) store_one<BF16>(fin, row * 3 + j, xv[e + j]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -236,11 +269,32 @@ extern "C" int causal_conv1d_fwd(const void *x, const float *weight, const float
   const int vec = (seqlen % 8 == 0) && aligned16(x) && aligned16(out);
   const int silu = act == SSM_ACT_SILU;
   if (io_dtype == SSM_BF16)
-    hipLaunchKernelGGL(conv_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       x, weight, bias, out, rows, dim, seqlen, silu, vec);
+    hipLaunchKernelGGL((conv_kernel<true, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       x, weight, bias, out, rows, dim, seqlen, silu, vec, nullptr, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(conv_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       x, weight, bias, out, rows, dim, seqlen, silu, vec);
+    hipLaunchKernelGGL((conv_kernel<false, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       x, weight, bias, out, rows, dim, seqlen, silu, vec, nullptr, nullptr, nullptr);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+extern "C" int causal_conv1d_fwd_ex(const causal_conv1d_args_t *a, void *stream_ptr) {
+  const int st = causal_conv1d_ex_validate(a);
+  if (st != SSM_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int64_t rows = a->batch * a->dim;
+  const int64_t threads = rows * ((a->seqlen + 7) / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  const int vec = (a->seqlen % 8 == 0) && aligned16(a->x) && aligned16(a->out);
+  const int silu = a->act == SSM_ACT_SILU;
+  const bool seq = a->seq_idx != nullptr;
+  const bool bf16 = a->io_dtype == SSM_BF16;
+  auto f = bf16 ? (seq ? conv_kernel<true, true> : conv_kernel<true, false>)
+                : (seq ? conv_kernel<false, true> : conv_kernel<false, false>);
+  hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a->x, a->weight, a->bias,
+                     a->out, rows, a->dim, a->seqlen, silu, vec, a->seq_idx, a->initial_states, a->final_states);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;

@@ -51,6 +51,16 @@ extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
   return SSM_OK;
 }
 
+extern "C" int causal_conv1d_ex_validate(const causal_conv1d_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  const int st = causal_conv1d_validate(a->x, a->weight, a->out, a->batch, a->dim, a->seqlen, a->width,
+                                        a->io_dtype, a->act);
+  if (st != SSM_OK) return st;
+  // the page: seq_idx excludes initial_states and the final states
+  if (a->seq_idx && (a->initial_states || a->final_states)) return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
 extern "C" int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *a) {
   if (!a) return SSM_ERR_NULL;
   if (!positive(a->batch) || !positive(a->dim) || !positive(a->seqlen) ||

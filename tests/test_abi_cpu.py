@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 4
+    assert L.ssm_abi_version() == 5
 
 
 def test_status_strings():
@@ -288,3 +288,45 @@ def test_bwd_binding_errors():
         binding.ssm_scan_bwd(u, u, A, B, B, u.to(torch.bfloat16), ck)
     with pytest.raises(ValueError, match="checkpoints must be a contiguous float32"):
         binding.ssm_scan_fwd(u, u, A, B, B, checkpoints=torch.zeros(b, d, 2, n))
+
+
+def _good_conv(**kw):
+    a = _lib.ConvArgs()
+    a.batch, a.dim, a.seqlen, a.width = 2, 8, 33, 4
+    a.io_dtype, a.act = _lib.SSM_BF16, _lib.SSM_ACT_SILU
+    a.x = a.weight = a.out = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_conv_ex_validation():
+    L = _lib.lib()
+    v = lambda a: L.causal_conv1d_ex_validate(ctypes.byref(a))
+    assert v(_good_conv()) == _lib.SSM_OK
+    assert v(_good_conv(initial_states=FAKE, final_states=FAKE, bias=FAKE)) == _lib.SSM_OK
+    assert v(_good_conv(seq_idx=FAKE)) == _lib.SSM_OK
+    for field in ("x", "weight", "out"):
+        assert v(_good_conv(**{field: None})) == _lib.SSM_ERR_NULL, field
+    assert v(_good_conv(seqlen=0)) == _lib.SSM_ERR_SHAPE
+    assert v(_good_conv(width=3)) == _lib.SSM_ERR_UNSUPPORTED
+    # the page: seq_idx excludes initial_states and the final states
+    assert v(_good_conv(seq_idx=FAKE, initial_states=FAKE)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_conv(seq_idx=FAKE, final_states=FAKE)) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.causal_conv1d_ex_validate(None) == _lib.SSM_ERR_NULL
+    assert L.causal_conv1d_fwd_ex(ctypes.byref(_good_conv(x=None)), None) == _lib.SSM_ERR_NULL
+
+
+def test_conv_fn_binding_errors():
+    import torch
+    from state_space_model_scan_amd import binding
+    x = torch.zeros(1, 2, 8)
+    w = torch.zeros(2, 4)
+    with pytest.raises(ValueError, match="seq_idx cannot be used"):
+        binding.causal_conv1d_fn(x, w, seq_idx=torch.zeros(1, 8, dtype=torch.int32), return_final_states=True)
+    with pytest.raises(ValueError, match="seq_idx must be int32"):
+        binding.causal_conv1d_fwd_ex(x, w, seq_idx=torch.zeros(1, 8, dtype=torch.int64))
+    with pytest.raises(ValueError, match="initial_states must be"):
+        binding.causal_conv1d_fwd_ex(x, w, initial_states=torch.zeros(1, 2, 4))
+    with pytest.raises(NotImplementedError):
+        binding.causal_conv1d_fn(x, w, activation="relu")
