@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ssm_oracle.c")
 LIB = os.path.join(HERE, "libssm_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 BC_FIXED, BC_VARYING = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
 
@@ -88,6 +88,10 @@ def _load():
         lib.oracle_selective_scan_bwd.restype = i32
         lib.oracle_causal_conv1d_ex.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, p, p, p, p]
         lib.oracle_causal_conv1d_ex.restype = i32
+        lib.oracle_round_f16.argtypes = [ctypes.c_double]
+        lib.oracle_round_f16.restype = ctypes.c_double
+        lib.oracle_f16_bits_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_bits_to_double.restype = ctypes.c_double
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -102,7 +106,7 @@ def _io(a: Optional[np.ndarray], dtype: int):
     """Check an io tensor holds the stored bits of the stated dtype."""
     if a is None:
         return None
-    want = np.uint16 if dtype == BF16 else np.float32
+    want = np.uint16 if dtype in (BF16, F16) else np.float32
     if a.dtype != want:
         raise TypeError(f"io tensor must be {want.__name__}, got {a.dtype}")
     return np.ascontiguousarray(a)
@@ -118,6 +122,14 @@ def max_threads() -> int:
 
 def round_bf16(v: float) -> float:
     return float(_load().oracle_round_bf16(float(v)))
+
+
+def round_f16(v: float) -> float:
+    return float(_load().oracle_round_f16(float(v)))
+
+
+def f16_bits_to_double(h: int) -> float:
+    return float(_load().oracle_f16_bits_to_double(int(h)))
 
 
 def softplus(v: float) -> float:

@@ -56,7 +56,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 enum { OR_BC_FIXED = 0, OR_BC_VARYING = 1 };
 enum { OR_ACT_NONE = 0, OR_ACT_SILU = 1 };
 
@@ -70,8 +70,20 @@ static double bf16_bits_to_double(uint16_t h) {
     return (double)f;
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;
+ * exponent 0 is zero or subnormal (fraction * 2^-24), 31 is inf or NaN. */
+double oracle_f16_bits_to_double(uint16_t h) {
+    const int sign = h >> 15, ex = (h >> 10) & 31, fr = h & 1023;
+    double v;
+    if (ex == 0) v = ldexp((double)fr, -24);
+    else if (ex == 31) v = fr ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + fr), ex - 25);
+    return sign ? -v : v;
+}
+
 static double load_io(const void *p, int dtype, int64_t i) {
     if (dtype == OR_BF16) return bf16_bits_to_double(((const uint16_t *)p)[i]);
+    if (dtype == OR_F16) return oracle_f16_bits_to_double(((const uint16_t *)p)[i]);
     return (double)((const float *)p)[i];
 }
 
@@ -90,9 +102,23 @@ double oracle_round_bf16(double v) {
     return out;
 }
 
+/* Round a double to the nearest binary16 value, ties to even: 11
+ * significant bits, smallest normal 2^-14, subnormal spacing 2^-24, largest
+ * finite 65504; beyond it (after rounding) infinity. */
+double oracle_round_f16(double v) {
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int e = ilogb(v);
+    if (e < -14) e = -14;
+    int q = e - 10;
+    double out = ldexp(nearbyint(ldexp(v, -q)), q);
+    if (fabs(out) > 65504.0) return copysign(INFINITY, v);
+    return out;
+}
+
 /* Round a double to the io dtype (fp32 cast rounds to nearest even). */
 static double round_io(double v, int dtype) {
     if (dtype == OR_BF16) return oracle_round_bf16(v);
+    if (dtype == OR_F16) return oracle_round_f16(v);
     return (double)(float)v;
 }
 

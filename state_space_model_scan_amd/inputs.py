@@ -38,7 +38,7 @@ import numpy as np
 
 CHUNK = 1 << 24
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -170,6 +170,25 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (h.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy: nearest, ties to even);
+    return the bits."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def io_bits_to_f64(a: np.ndarray, io_dtype: int) -> np.ndarray:
+    """The values of stored io bits (any io dtype) as float64."""
+    if io_dtype == BF16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    if io_dtype == F16:
+        return f16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
 def _normal(rng: np.random.Generator, shape, mean=0.0, std=1.0) -> np.ndarray:
     total = int(np.prod(shape))
     out = np.empty(total, dtype=np.float32)
@@ -188,7 +207,11 @@ def _uniform(rng: np.random.Generator, shape, lo, hi) -> np.ndarray:
 
 
 def _store(a: np.ndarray, io_dtype: int) -> np.ndarray:
-    return f32_to_bf16_bits(a) if io_dtype == BF16 else np.ascontiguousarray(a, dtype=np.float32)
+    if io_dtype == BF16:
+        return f32_to_bf16_bits(a)
+    if io_dtype == F16:
+        return f32_to_f16_bits(a)
+    return np.ascontiguousarray(a, dtype=np.float32)
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:

@@ -307,3 +307,43 @@ def test_conv_ex_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# fp16 io against its own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_f16_pins as fpins  # noqa: E402
+
+F16_MUTANTS = {
+    "f16_ties_away": ("double out = ldexp(nearbyint(ldexp(v, -q)), q);", "double out = ldexp(round(ldexp(v, -q)), q);"),
+    "f16_exponent_bias": ("else v = ldexp((double)(1024 + fr), ex - 25);", "else v = ldexp((double)(1024 + fr), ex - 24);"),
+    "f16_min_normal": ("if (e < -14) e = -14;", "if (e < -15) e = -15;"),
+    "f16_read_as_bf16": ("if (dtype == OR_F16) return oracle_f16_bits_to_double(((const uint16_t *)p)[i]);",
+                         "if (dtype == OR_F16) return bf16_bits_to_double(((const uint16_t *)p)[i]);"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(F16_MUTANTS))
+def test_f16_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = F16_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in (("decode", fpins.test_decode_every_bit_pattern),
+                           ("round", fpins.test_rounding_matches_numpy),
+                           ("scan", fpins.test_scan_f16_io_equals_f32_io_of_the_same_values)):
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
