@@ -28,6 +28,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
 SOURCES = [
     ("scan_bf16.hip", True),
     ("scan_f32.hip", True),
+    ("scan_f16.hip", True),
     ("ssm_scan.hip", True),
     ("decode.hip", True),
     ("ssd.hip", True),

@@ -7,7 +7,7 @@ from typing import Optional
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.so")
 
-SSM_F32, SSM_BF16 = 0, 1
+SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_BC_FIXED, SSM_BC_VARYING = 0, 1
 SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
 SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_WORKSPACE = range(6)

@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import BwdArgs, ConvArgs, ScanArgs, check
 
-_IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
+_IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16, torch.float16: _lib.SSM_F16}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -79,7 +79,7 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
     if io is None:
-        raise ValueError(f"io dtype must be float32 or bfloat16, got {delta.dtype}")
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
     batch, dim, seqlen = delta.shape
     dstate = A.shape[1]
     B, C = _dense(B), _dense(C)
@@ -149,7 +149,7 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
     if io is None:
-        raise ValueError(f"io dtype must be float32 or bfloat16, got {delta.dtype}")
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
     batch, dim, seqlen = delta.shape
     dstate = A.shape[1]
     u, B, C, z, dout = _dense(u), _dense(B), _dense(C), _dense(z), _dense(dout)
@@ -206,7 +206,7 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
     x = _dense(x)
     io = _IO.get(x.dtype)
     if io is None:
-        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {x.dtype}")
     weight, bias = _dense(weight), _dense(bias)
     if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("conv weight and bias must be float32")
@@ -246,7 +246,7 @@ def causal_conv1d_fwd_ex(x: torch.Tensor, weight: torch.Tensor, bias: Optional[t
     x = _dense(x)
     io = _IO.get(x.dtype)
     if io is None:
-        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {x.dtype}")
     weight, bias = _dense(weight), _dense(bias)
     if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("conv weight and bias must be float32")
@@ -329,7 +329,7 @@ def selective_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tenso
     x, dt = _dense(x), _dense(dt)
     io = _IO.get(x.dtype)
     if io is None:
-        raise ValueError(f"io dtype must be float32 or bfloat16, got {x.dtype}")
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {x.dtype}")
     if B.dim() == 2:
         B = B.unsqueeze(1)
     if C.dim() == 2:

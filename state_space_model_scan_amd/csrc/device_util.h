@@ -13,19 +13,37 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// io element access.  bf16 is the upper half of a binary32.
+// io element access.  The io dtype is a template value IO: 0 = fp32, 1 =
+// bf16 (the upper half of a binary32), 2 = fp16 (IEEE binary16).  A bool
+// argument converts to 0 / 1.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int NV>
+// 16 stored bits -> float (bf16: a shift; fp16: the hardware conversion).
+template <int IO>
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  if constexpr (IO == 1) return __uint_as_float(h << 16);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+// float -> 16 stored bits, rounded to nearest, ties to even.
+template <int IO>
+__device__ __forceinline__ uint32_t float_to_half_bits(float v) {
+  if constexpr (IO == 1) return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  else return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+template <int IO, int NV>
 struct RawV {  // NV consecutive io elements as loaded from memory (NV = 4 or 8)
   static_assert(NV == 4 || NV == 8, "vector width");
-  static constexpr int kWords = BF16 ? NV / 2 : NV;
+  static constexpr int kWords = IO ? NV / 2 : NV;
   uint32_t w[kWords];
 
   __device__ __forceinline__ float get(int i) const {
-    if constexpr (BF16) {
+    if constexpr (IO == 1) {
       const uint32_t v = w[i >> 1];
       return __uint_as_float((i & 1) ? (v & 0xffff0000u) : (v << 16));
+    } else if constexpr (IO == 2) {
+      const uint32_t v = w[i >> 1];
+      return half_bits_to_float<2>((i & 1) ? (v >> 16) : (v & 0xffffu));
     } else {
       return __uint_as_float(w[i]);
     }
@@ -36,7 +54,7 @@ struct RawV {  // NV consecutive io elements as loaded from memory (NV = 4 or 8)
   }
   // Aligned vector load of elements [idx, idx+NV).
   __device__ __forceinline__ void load_vec(const void *base, int64_t idx) {
-    const uint32_t *p = BF16 ? reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx)
+    const uint32_t *p = IO ? reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx)
                              : reinterpret_cast<const uint32_t *>(static_cast<const float *>(base) + idx);
     if constexpr (kWords == 2) {
       const uint2 q = *reinterpret_cast<const uint2 *>(p);
@@ -62,7 +80,7 @@ struct RawV {  // NV consecutive io elements as loaded from memory (NV = 4 or 8)
   }
   // Element load into slot i (slot assumed zero).
   __device__ __forceinline__ void load_one(const void *base, int64_t idx, int i) {
-    if constexpr (BF16) {
+    if constexpr (IO != 0) {
       const uint32_t h = static_cast<const uint16_t *>(base)[idx];
       w[i >> 1] |= (i & 1) ? (h << 16) : h;
     } else {
@@ -71,44 +89,36 @@ struct RawV {  // NV consecutive io elements as loaded from memory (NV = 4 or 8)
   }
 };
 
-template <bool BF16>
-using Raw8 = RawV<BF16, 8>;
+template <int IO>
+using Raw8 = RawV<IO, 8>;
 
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ float load_io(const void *p, int64_t i) {
-  if constexpr (BF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+  if constexpr (IO != 0) return half_bits_to_float<IO>(static_cast<const uint16_t *>(p)[i]);
   else return static_cast<const float *>(p)[i];
 }
 
-// Raw io bits -> float (bf16 bits in the low half of the word).
-template <bool BF16>
+// An io element's value as the bits of a binary32.
+template <int IO>
 __device__ __forceinline__ uint32_t load_io_bits(const void *p, int64_t i) {
-  if constexpr (BF16) return static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16;
-  else return __float_as_uint(static_cast<const float *>(p)[i]);
+  return __float_as_uint(load_io<IO>(p, i));
 }
 
-// Round to the io dtype (bf16: hardware round-to-nearest-even convert).
-template <bool BF16>
+// Round to the io dtype (hardware round-to-nearest-even convert).
+template <int IO>
 __device__ __forceinline__ float round_io(float v) {
-  if constexpr (BF16) {
-    const __bf16 h = static_cast<__bf16>(v);
-    return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
-  } else {
-    return v;
-  }
+  if constexpr (IO != 0) return half_bits_to_float<IO>(float_to_half_bits<IO>(v));
+  else return v;
 }
 
-template <bool BF16, int NV>
+template <int IO, int NV>
 __device__ __forceinline__ void store_n(void *base, int64_t idx, const float (&v)[NV], int cnt, bool vec) {
   static_assert(NV == 4 || NV == 8, "vector width");
-  if constexpr (BF16) {
+  if constexpr (IO != 0) {
     uint32_t pk[NV / 2];
 #pragma unroll
-    for (int i = 0; i < NV / 2; ++i) {
-      const __bf16 lo = static_cast<__bf16>(v[2 * i]), hi = static_cast<__bf16>(v[2 * i + 1]);
-      pk[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-    }
+    for (int i = 0; i < NV / 2; ++i)
+      pk[i] = float_to_half_bits<IO>(v[2 * i]) | (float_to_half_bits<IO>(v[2 * i + 1]) << 16);
     if (vec && cnt >= NV) {
       uint16_t *p = static_cast<uint16_t *>(base) + idx;
       if constexpr (NV == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
@@ -132,20 +142,16 @@ __device__ __forceinline__ void store_n(void *base, int64_t idx, const float (&v
   }
 }
 
-// One io element (bf16: rounded to nearest, ties to even).
-template <bool BF16>
+// One io element (16-bit dtypes: rounded to nearest, ties to even).
+template <int IO>
 __device__ __forceinline__ void store_one(void *base, int64_t idx, float v) {
-  if constexpr (BF16) {
-    const __bf16 h = static_cast<__bf16>(v);
-    static_cast<uint16_t *>(base)[idx] = __builtin_bit_cast(uint16_t, h);
-  } else {
-    static_cast<float *>(base)[idx] = v;
-  }
+  if constexpr (IO != 0) static_cast<uint16_t *>(base)[idx] = static_cast<uint16_t>(float_to_half_bits<IO>(v));
+  else static_cast<float *>(base)[idx] = v;
 }
 
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void store8(void *base, int64_t idx, const float (&v)[8], int cnt, bool vec) {
-  store_n<BF16, 8>(base, idx, v, cnt, vec);
+  store_n<IO, 8>(base, idx, v, cnt, vec);
 }
 
 // ---------------------------------------------------------------------------

@@ -3,6 +3,6 @@
 
 namespace ssm {
 ScanFn pick_scan_bf16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  return pick_scan<true>(nsw, lpc, bv, cv, conv, mode);
+  return pick_scan<1>(nsw, lpc, bv, cv, conv, mode);
 }
 }  // namespace ssm

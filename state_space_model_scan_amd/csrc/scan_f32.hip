@@ -3,6 +3,6 @@
 
 namespace ssm {
 ScanFn pick_scan_f32(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  return pick_scan<false>(nsw, lpc, bv, cv, conv, mode);
+  return pick_scan<0>(nsw, lpc, bv, cv, conv, mode);
 }
 }  // namespace ssm

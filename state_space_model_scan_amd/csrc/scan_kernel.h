@@ -88,7 +88,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <bool BF16, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE>
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 scan_kernel(const ScanParams p) {
   constexpr bool FULL = MODE == MODE_FULL;
@@ -141,8 +141,8 @@ scan_kernel(const ScanParams p) {
     const int s = s0 + k;
     const bool sv = s < n;
     Ap[k] = sv ? p.A[dl * n + s] * kLog2e : 0.0f;
-    Bf[k] = (!BV && sv) ? load_io<BF16>(p.B, dl * n + s) : 0.0f;
-    Cf[k] = (!CV && sv) ? load_io<BF16>(p.C, dl * n + s) : 0.0f;
+    Bf[k] = (!BV && sv) ? load_io<IO>(p.B, dl * n + s) : 0.0f;
+    Cf[k] = (!CV && sv) ? load_io<IO>(p.C, dl * n + s) : 0.0f;
     x[k] = 0.0f;
   }
   const float bias = p.dbias ? p.dbias[dl] : 0.0f;
@@ -182,7 +182,7 @@ scan_kernel(const ScanParams p) {
   };
 
   // global inputs of the next chunk, loaded before the current recurrence
-  RawV<BF16, kKP> r_a, r_dl, r_z, r_h;   // u (or conv x), delta, z, conv halo
+  RawV<IO, kKP> r_a, r_dl, r_z, r_h;   // u (or conv x), delta, z, conv halo
   r_a.zero(); r_dl.zero(); r_z.zero(); r_h.zero();
   auto fetch = [&](int64_t c) {
     const int64_t tp0 = c + own;
@@ -211,7 +211,7 @@ scan_kernel(const ScanParams p) {
   const int bc_t0 = (lane % (T / 8)) * 8;
   const bool bc_lane = ANYV && lane < PIECES;
   const bool bc_real = bc_lane && bc_s < n;
-  RawV<BF16, 8> r_B, r_C;
+  RawV<IO, 8> r_B, r_C;
   r_B.zero(); r_C.zero();
   auto fetch_bc = [&](int64_t c) {
     if (bc_real) {
@@ -254,7 +254,7 @@ scan_kernel(const ScanParams p) {
         acc = fmaf(cw2, xv[i + 2], acc);
         acc = fmaf(cw3, xv[i + 3], acc);
         if constexpr (CS) acc = silu_f(acc);
-        uu[i] = round_io<BF16>(acc);
+        uu[i] = round_io<IO>(acc);
       }
     } else {
 #pragma unroll
@@ -295,7 +295,7 @@ scan_kernel(const ScanParams p) {
       if (p.z) y *= silu_f(r_z.get(i));
       o[i] = y;
     }
-    store_n<BF16, kKP>(p.out, rbase + c + own, o, cnt, vec);
+    store_n<IO, kKP>(p.out, rbase + c + own, o, cnt, vec);
   };
 
   float sumdt = 0.0f;   // summed delta' of the segment (MODE_STATE)
@@ -366,7 +366,7 @@ scan_kernel(const ScanParams p) {
       stage_bc();
       wave_lds_sync();          // the slice is written before any lane reads it
     }
-    const RawV<BF16, kKP> z_cur = r_z;
+    const RawV<IO, kKP> z_cur = r_z;
     if (c + T < t_end) {
       fetch(c + T);
       if constexpr (ANYV) fetch_bc(c + T);
@@ -398,7 +398,7 @@ scan_kernel(const ScanParams p) {
     }
     if constexpr (XCH && FULL) gather_y();   // sum of the quad's partial C.x
     if constexpr (FULL) {
-      const RawV<BF16, kKP> z_next = r_z;
+      const RawV<IO, kKP> z_next = r_z;
       r_z = z_cur;
       epilogue(c);
       r_z = z_next;
@@ -425,34 +425,36 @@ using ScanFn = void (*)(const ScanParams);
 
 // Kernel instance for a plan.  (nsw, lpc) is one of (4,4), (4,2), (4,1),
 // (2,1), (1,1): n_pad = nsw * lpc states.
-template <bool BF16, int NSW, int LPC, bool BV, bool CV, bool CONV>
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV>
 ScanFn pick_mode(int mode) {
-  return mode == MODE_FULL ? scan_kernel<BF16, NSW, LPC, BV, CV, CONV, MODE_FULL>
-                           : scan_kernel<BF16, NSW, LPC, BV, CV, CONV, MODE_STATE>;
+  return mode == MODE_FULL ? scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_FULL>
+                           : scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_STATE>;
 }
-template <bool BF16, int NSW, int LPC, bool BV, bool CV>
+template <int IO, int NSW, int LPC, bool BV, bool CV>
 ScanFn pick_conv(bool conv, int mode) {
-  return conv ? pick_mode<BF16, NSW, LPC, BV, CV, true>(mode) : pick_mode<BF16, NSW, LPC, BV, CV, false>(mode);
+  return conv ? pick_mode<IO, NSW, LPC, BV, CV, true>(mode) : pick_mode<IO, NSW, LPC, BV, CV, false>(mode);
 }
-template <bool BF16, int NSW, int LPC>
+template <int IO, int NSW, int LPC>
 ScanFn pick_bc(bool bv, bool cv, bool conv, int mode) {
-  if (bv && cv) return pick_conv<BF16, NSW, LPC, true, true>(conv, mode);
-  if (bv) return pick_conv<BF16, NSW, LPC, true, false>(conv, mode);
-  if (cv) return pick_conv<BF16, NSW, LPC, false, true>(conv, mode);
-  return pick_conv<BF16, NSW, LPC, false, false>(conv, mode);
+  if (bv && cv) return pick_conv<IO, NSW, LPC, true, true>(conv, mode);
+  if (bv) return pick_conv<IO, NSW, LPC, true, false>(conv, mode);
+  if (cv) return pick_conv<IO, NSW, LPC, false, true>(conv, mode);
+  return pick_conv<IO, NSW, LPC, false, false>(conv, mode);
 }
-template <bool BF16>
+template <int IO>
 ScanFn pick_scan(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  if (nsw == 4 && lpc == 4) return pick_bc<BF16, 4, 4>(bv, cv, conv, mode);
-  if (nsw == 4 && lpc == 2) return pick_bc<BF16, 4, 2>(bv, cv, conv, mode);
-  if (nsw == 4 && lpc == 1) return pick_bc<BF16, 4, 1>(bv, cv, conv, mode);
-  if (nsw == 2 && lpc == 1) return pick_bc<BF16, 2, 1>(bv, cv, conv, mode);
-  if (nsw == 1 && lpc == 1) return pick_bc<BF16, 1, 1>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 4) return pick_bc<IO, 4, 4>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 2) return pick_bc<IO, 4, 2>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 1) return pick_bc<IO, 4, 1>(bv, cv, conv, mode);
+  if (nsw == 2 && lpc == 1) return pick_bc<IO, 2, 1>(bv, cv, conv, mode);
+  if (nsw == 1 && lpc == 1) return pick_bc<IO, 1, 1>(bv, cv, conv, mode);
   return nullptr;
 }
 
-// Defined in scan_f32.hip / scan_bf16.hip (one translation unit per io dtype).
+// Defined in scan_f32.hip / scan_bf16.hip / scan_f16.hip (one translation
+// unit per io dtype).
 ScanFn pick_scan_f32(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
+ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
 ScanFn pick_scan_bf16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
 
 }  // namespace ssm

@@ -37,7 +37,7 @@ namespace {
 // thread holding the row's last output writes the last three inputs to fin.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, bool SEQ>
+template <int IO, bool SEQ>
 __global__ void __launch_bounds__(256)
 conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
             int64_t rows, int64_t dim, int64_t seqlen, int silu, int vec,
@@ -50,7 +50,7 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
   const int64_t d = row % dim;
   const int64_t rb = row * seqlen;
   const int cnt = static_cast<int>((seqlen - t0 < 8) ? seqlen - t0 : 8);
-  Raw8<BF16> cur, prev;
+  Raw8<IO> cur, prev;
   cur.load(x, rb + t0, cnt, vec != 0);
   if (t0 >= 8 && vec) prev.load_vec(x, rb + t0 - 8);
   else prev.load_elems(x, rb + t0 - 8, t0 >= 8 ? 8 : 0);
@@ -60,7 +60,7 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
   xv[0] = prev.get(5); xv[1] = prev.get(6); xv[2] = prev.get(7);
   if (t0 == 0 && init) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) xv[j] = load_io<BF16>(init, row * 3 + j);
+    for (int j = 0; j < 3; ++j) xv[j] = load_io<IO>(init, row * 3 + j);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) xv[i + 3] = cur.get(i);
@@ -93,12 +93,12 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
     if (silu) acc = silu_f(acc);
     o[i] = acc;
   }
-  store8<BF16>(out, rb + t0, o, cnt, vec != 0);
+  store8<IO>(out, rb + t0, o, cnt, vec != 0);
   if (fin && t0 + 8 >= seqlen) {
     // the extended input at seqlen-3+j sits at xv[seqlen - t0 + j]
     const int e = static_cast<int>(seqlen - t0);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) store_one<BF16>(fin, row * 3 + j, xv[e + j]);
+    for (int j = 0; j < 3; ++j) store_one<IO>(fin, row * 3 + j, xv[e + j]);
   }
 }
 
@@ -182,8 +182,10 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   return pl;
 }
 
-ScanFn pick(bool bf16, int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  return bf16 ? pick_scan_bf16(nsw, lpc, bv, cv, conv, mode) : pick_scan_f32(nsw, lpc, bv, cv, conv, mode);
+ScanFn pick(int io, int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
+  if (io == SSM_BF16) return pick_scan_bf16(nsw, lpc, bv, cv, conv, mode);
+  if (io == SSM_F16) return pick_scan_f16(nsw, lpc, bv, cv, conv, mode);
+  return pick_scan_f32(nsw, lpc, bv, cv, conv, mode);
 }
 
 }  // namespace
@@ -203,7 +205,7 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   if (a->workspace && a->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
-  const bool bf16 = a->io_dtype == SSM_BF16;
+  const int io = a->io_dtype;
   const bool conv = a->conv_weight != nullptr;
   ScanParams p{};
   p.u = a->u; p.delta = a->delta; p.B = a->B; p.C = a->C; p.z = a->z;
@@ -236,8 +238,8 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   }
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
   int rc = SSM_OK;
-  const ScanFn f_state = pl.nseg > 1 ? pick(bf16, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE) : nullptr;
-  const ScanFn f_full = pick(bf16, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL);
+  const ScanFn f_state = pl.nseg > 1 ? pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE) : nullptr;
+  const ScanFn f_full = pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL);
   if (!f_full || (pl.nseg > 1 && !f_state)) rc = SSM_ERR_UNSUPPORTED;
   if (rc == SSM_OK && pl.nseg > 1) {
     hipLaunchKernelGGL(f_state, dim3(pl.nblocks, pl.nseg - 1), dim3(64 * kWavesPerBlock), 0, stream, p);
@@ -268,12 +270,10 @@ extern "C" int causal_conv1d_fwd(const void *x, const float *weight, const float
   if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
   const int vec = (seqlen % 8 == 0) && aligned16(x) && aligned16(out);
   const int silu = act == SSM_ACT_SILU;
-  if (io_dtype == SSM_BF16)
-    hipLaunchKernelGGL((conv_kernel<true, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       x, weight, bias, out, rows, dim, seqlen, silu, vec, nullptr, nullptr, nullptr);
-  else
-    hipLaunchKernelGGL((conv_kernel<false, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       x, weight, bias, out, rows, dim, seqlen, silu, vec, nullptr, nullptr, nullptr);
+  auto f = io_dtype == SSM_BF16 ? conv_kernel<1, false> : io_dtype == SSM_F16 ? conv_kernel<2, false>
+                                                                                : conv_kernel<0, false>;
+  hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     x, weight, bias, out, rows, dim, seqlen, silu, vec, nullptr, nullptr, nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
@@ -290,9 +290,9 @@ extern "C" int causal_conv1d_fwd_ex(const causal_conv1d_args_t *a, void *stream_
   const int vec = (a->seqlen % 8 == 0) && aligned16(a->x) && aligned16(a->out);
   const int silu = a->act == SSM_ACT_SILU;
   const bool seq = a->seq_idx != nullptr;
-  const bool bf16 = a->io_dtype == SSM_BF16;
-  auto f = bf16 ? (seq ? conv_kernel<true, true> : conv_kernel<true, false>)
-                : (seq ? conv_kernel<false, true> : conv_kernel<false, false>);
+  auto f = a->io_dtype == SSM_BF16 ? (seq ? conv_kernel<1, true> : conv_kernel<1, false>)
+         : a->io_dtype == SSM_F16  ? (seq ? conv_kernel<2, true> : conv_kernel<2, false>)
+                                   : (seq ? conv_kernel<0, true> : conv_kernel<0, false>);
   hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a->x, a->weight, a->bias,
                      a->out, rows, a->dim, a->seqlen, silu, vec, a->seq_idx, a->initial_states, a->final_states);
   const hipError_t e = hipGetLastError();

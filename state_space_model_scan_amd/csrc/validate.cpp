@@ -34,7 +34,7 @@ extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
   if (!product_fits(a->batch, a->dim, a->seqlen) ||
       !product_fits(a->batch, a->ngroups * a->dstate, a->seqlen))
     return SSM_ERR_SHAPE;
-  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16 && a->io_dtype != SSM_F16) return SSM_ERR_UNSUPPORTED;
   if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   if ((a->B_kind != SSM_BC_FIXED && a->B_kind != SSM_BC_VARYING) ||
       (a->C_kind != SSM_BC_FIXED && a->C_kind != SSM_BC_VARYING))
@@ -89,7 +89,7 @@ extern "C" int causal_conv1d_validate(const void *x, const float *weight, const 
                                       int32_t width, int32_t io_dtype, int32_t act) {
   if (!positive(batch) || !positive(dim) || !positive(seqlen)) return SSM_ERR_SHAPE;
   if (!product_fits(batch, dim, seqlen)) return SSM_ERR_SHAPE;
-  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16 && io_dtype != SSM_F16) return SSM_ERR_UNSUPPORTED;
   if (width != SSM_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
   if (act != SSM_ACT_NONE && act != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
   if (!x || !weight || !out) return SSM_ERR_NULL;

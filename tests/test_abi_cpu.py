@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 5
+    assert L.ssm_abi_version() == 6
 
 
 def test_status_strings():
@@ -83,7 +83,7 @@ def test_overflowing_sizes():
     assert _validate(_good_args(batch=1 << 40, dim=1 << 20, seqlen=1 << 20)) == _lib.SSM_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(io_dtype=2), dict(dstate=17), dict(B_kind=2), dict(C_kind=-1),
+@pytest.mark.parametrize("kw", [dict(io_dtype=3), dict(dstate=17), dict(B_kind=2), dict(C_kind=-1),
                                 dict(delta_softplus=2),
                                 dict(conv_weight=FAKE, conv_x=FAKE, conv_width=3),
                                 dict(conv_weight=FAKE, conv_x=FAKE, conv_width=4, conv_act=7)])
@@ -330,3 +330,12 @@ def test_conv_fn_binding_errors():
         binding.causal_conv1d_fwd_ex(x, w, initial_states=torch.zeros(1, 2, 4))
     with pytest.raises(NotImplementedError):
         binding.causal_conv1d_fn(x, w, activation="relu")
+
+
+def test_fp16_io_is_taken_by_the_scan_and_conv_only():
+    L = _lib.lib()
+    assert _validate(_good_args(io_dtype=_lib.SSM_F16)) == _lib.SSM_OK
+    assert L.causal_conv1d_validate(FAKE, FAKE, FAKE, 1, 4, 8, 4, _lib.SSM_F16, 0) == _lib.SSM_OK
+    assert L.causal_conv1d_ex_validate(ctypes.byref(_good_conv(io_dtype=_lib.SSM_F16))) == _lib.SSM_OK
+    assert L.ssm_scan_bwd_validate(ctypes.byref(_good_bwd(io_dtype=_lib.SSM_F16))) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssd_scan_validate(ctypes.byref(_good_ssd(io_dtype=_lib.SSM_F16))) == _lib.SSM_ERR_UNSUPPORTED
