@@ -126,20 +126,48 @@ __device__ __forceinline__ float row_bcast_reg(float v) {
 // sum of v[s] over the row's 16 lanes for s = lane & 15.  Recursive halving:
 // each step pairs lanes that differ in one lane bit (8: row_ror:8, 4:
 // row_half_mirror, 2 and 1: quad permutes), every lane keeps the half of its
-// values its bit selects and adds the partner's copy of that half.
+// values its bit selects and adds the partner's copy of that half.  In the
+// first two steps the lanes of one half are whole DPP banks (bit 3: banks
+// 0-1 / 2-3; bit 2: banks 0,2 / 1,3), so each kept value is two bank-masked
+// DPP adds writing one register -- no selects.  The leading s_nop gives the
+// two wait states a DPP source read needs after a VALU write.
 __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int s) {
-  const bool b3 = s & 8, b2 = s & 4, b1 = s & 2, b0 = s & 1;
   float r8[8], r4[4], r2[2];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float keep = b3 ? v[k + 8] : v[k], send = b3 ? v[k] : v[k + 8];
-    r8[k] = keep + dpp<0x128>(send);          // row_ror:8
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = b2 ? r8[k + 4] : r8[k], send = b2 ? r8[k] : r8[k + 4];
-    r4[k] = keep + dpp<0x141>(send);          // row_half_mirror
-  }
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(r8[0]), "=&v"(r8[1]), "=&v"(r8[2]), "=&v"(r8[3]),
+        "=&v"(r8[4]), "=&v"(r8[5]), "=&v"(r8[6]), "=&v"(r8[7])
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+        "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(r4[0]), "=&v"(r4[1]), "=&v"(r4[2]), "=&v"(r4[3])
+      : "v"(r8[0]), "v"(r8[1]), "v"(r8[2]), "v"(r8[3]), "v"(r8[4]), "v"(r8[5]), "v"(r8[6]), "v"(r8[7]));
+  const bool b1 = s & 2, b0 = s & 1;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const float keep = b1 ? r4[k + 2] : r4[k], send = b1 ? r4[k] : r4[k + 2];
