@@ -523,7 +523,7 @@ int oracle_causal_conv1d_update(int64_t batch, int64_t dim, int64_t seqlen,
     if (batch <= 0 || dim <= 0 || seqlen <= 0 || width <= 0) return 2;
     if (state_len < width - 1 || state_len <= 0) return 2;
     if (!x || !conv_state || !weight || !out || !state_out) return 1;
-    const size_t es = io_dtype == OR_BF16 ? 2 : 4;
+    const size_t es = io_dtype == OR_F32 ? 4 : 2;   /* bytes per io element */
     /* one row of raw io words: the cache followed by the new tokens */
     unsigned char *buf = (unsigned char *)malloc(es * (size_t)(state_len + seqlen));
     double *win = (double *)malloc(sizeof(double) * (size_t)width);

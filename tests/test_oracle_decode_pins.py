@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as orc
-from state_space_model_scan_amd.inputs import f32_to_bf16_bits
+from state_space_model_scan_amd.inputs import f32_to_bf16_bits, f32_to_f16_bits
 
 TOL = 1e-12
 
@@ -141,7 +141,7 @@ def test_state_update_groups_broadcast():
 # causal_conv1d_update
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("io", [orc.F32, orc.BF16])
+@pytest.mark.parametrize("io", [orc.F32, orc.BF16, orc.F16])
 @pytest.mark.parametrize("act", [orc.ACT_NONE, orc.ACT_SILU])
 @pytest.mark.parametrize("width", [2, 4])
 def test_conv_update_chain_equals_conv(io, act, width):
@@ -153,6 +153,8 @@ def test_conv_update_chain_equals_conv(io, act, width):
     x = _rand(rng, (b, d, l))
     if io == orc.BF16:
         x = f32_to_bf16_bits(x)
+    elif io == orc.F16:
+        x = f32_to_f16_bits(x)
     w = _rand(rng, (d, width), 0.0, 0.5)
     bias = _rand(rng, (d,))
     ref = orc.causal_conv1d(x, w, bias, act, io_dtype=io).reshape(b, d, l)
