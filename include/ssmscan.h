@@ -30,8 +30,7 @@
  *    outputs.  `out` must not alias an input.
  *  - "io" tensors (u, delta, z, B, C, out, conv x) all have the dtype
  *    io_dtype: SSM_F32 (IEEE binary32), SSM_BF16 (bfloat16, stored as the
- *    upper 16 bits of a binary32) or, for the scan and conv forward,
- *    SSM_F16 (IEEE binary16).  A, D, delta_bias, conv weight and bias,
+ *    upper 16 bits of a binary32) or SSM_F16 (IEEE binary16).  A, D, delta_bias, conv weight and bias,
  *    initial_state and last_state are always binary32; the state is binary32.
  *    bf16 and fp16 outputs are rounded to nearest, ties to even.
  *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
@@ -57,9 +56,8 @@ extern "C" {
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
 
-/* io dtype.  SSM_F16 (IEEE binary16) is taken by ssm_scan_fwd,
- * causal_conv1d_fwd and causal_conv1d_fwd_ex; the other entry points return
- * SSM_ERR_UNSUPPORTED for it. */
+/* io dtype.  SSM_F16 (IEEE binary16) is taken by every entry point except
+ * ssd_scan_fwd (bf16 only), which returns SSM_ERR_UNSUPPORTED for it. */
 enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 };
 /* layout of B and C (one kind per tensor) */
 enum { SSM_BC_FIXED = 0,    /* (dim, dstate) */

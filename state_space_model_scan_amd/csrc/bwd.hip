@@ -89,14 +89,15 @@ __device__ __forceinline__ void swap16(float &x, float &y) {
 }
 
 // One io element as stored (bf16: zero-extended 16 bits), and its value.
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ uint32_t raw_load(const void *p, int64_t i) {
-  if constexpr (BF16) return static_cast<const uint16_t *>(p)[i];
+  if constexpr (IO) return static_cast<const uint16_t *>(p)[i];
   else return static_cast<const uint32_t *>(p)[i];
 }
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ float raw_float(uint32_t r) {
-  return __uint_as_float(BF16 ? r << 16 : r);
+  if constexpr (IO != 0) return half_bits_to_float<IO>(r);
+  else return __uint_as_float(r);
 }
 
 template <int I>
@@ -177,7 +178,7 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int 
   return keep + dpp<0xB1>(send);              // quad_perm [1,0,3,2]
 }
 
-template <bool BF16, bool BV, bool CV, bool HZ>
+template <int IO, bool BV, bool CV, bool HZ>
 __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p) {
   constexpr bool ANYV = BV || CV;
   __shared__ __align__(16) float s_bc[2][2][kNP][kRow];               // B/C tiles, double-buffered
@@ -204,8 +205,8 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
 
   const float Av = sv ? p.A[dl * n + s] : 0.0f;
   const float Ap = Av * kLog2e;
-  const float Bf = (!BV && sv) ? load_io<BF16>(p.B, dl * n + s) : 0.0f;
-  const float Cf = (!CV && sv) ? load_io<BF16>(p.C, dl * n + s) : 0.0f;
+  const float Bf = (!BV && sv) ? load_io<IO>(p.B, dl * n + s) : 0.0f;
+  const float Cf = (!CV && sv) ? load_io<IO>(p.C, dl * n + s) : 0.0f;
   const float bias = p.dbias ? p.dbias[dl] : 0.0f;
   const float Dd = p.D ? p.D[dl] : 0.0f;
 
@@ -224,13 +225,13 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
       const int64_t t0 = static_cast<int64_t>(ci) * kT + tt;
       const void *src = tq == 0 ? p.B : p.C;
       const int64_t e = bc_base + ts * L + t0;
-      if (t0 < L) tile0 = raw_load<BF16>(src, e);
-      if (t0 + 1 < L) tile1 = raw_load<BF16>(src, e + 1);
+      if (t0 < L) tile0 = raw_load<IO>(src, e);
+      if (t0 + 1 < L) tile1 = raw_load<IO>(src, e + 1);
     }
   };
   auto store_tile = [&](int buf) {
     if (t_thr)
-      *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(raw_float<BF16>(tile0), raw_float<BF16>(tile1));
+      *reinterpret_cast<float2 *>(&s_bc[buf][tq][ts][tt]) = make_float2(raw_float<IO>(tile0), raw_float<IO>(tile1));
   };
 
   // ---- running state of this lane
@@ -251,10 +252,10 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
       const int64_t t = t0 + s + 16 * h;
       r_u[h] = r_d[h] = r_go[h] = r_z[h] = 0;
       if (valid && t < L) {
-        r_u[h] = raw_load<BF16>(p.u, rbase + t);
-        r_d[h] = raw_load<BF16>(p.delta, rbase + t);
-        r_go[h] = raw_load<BF16>(p.dout, rbase + t);
-        if constexpr (HZ) r_z[h] = raw_load<BF16>(p.z, rbase + t);
+        r_u[h] = raw_load<IO>(p.u, rbase + t);
+        r_d[h] = raw_load<IO>(p.delta, rbase + t);
+        r_go[h] = raw_load<IO>(p.dout, rbase + t);
+        if constexpr (HZ) r_z[h] = raw_load<IO>(p.z, rbase + t);
       }
     }
   };
@@ -276,10 +277,10 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
     float c_u[2], c_d[2], c_go[2], c_z[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      c_u[h] = raw_float<BF16>(r_u[h]);
-      c_d[h] = raw_float<BF16>(r_d[h]);
-      c_go[h] = raw_float<BF16>(r_go[h]);
-      c_z[h] = raw_float<BF16>(r_z[h]);
+      c_u[h] = raw_float<IO>(r_u[h]);
+      c_d[h] = raw_float<IO>(r_d[h]);
+      c_go[h] = raw_float<IO>(r_go[h]);
+      c_z[h] = raw_float<IO>(r_z[h]);
     }
     if (ci > 0) {
       fetch_own(ci - 1);
@@ -349,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = s + 16 * h;
-        if (valid && t < len) store_one<BF16>(p.dz, rbase + t0 + t, o_dzf[h] * (Y[h] + o_Du[h]));
+        if (valid && t < len) store_one<IO>(p.dz, rbase + t0 + t, o_dzf[h] * (Y[h] + o_Du[h]));
       }
     }
 
@@ -410,8 +411,8 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
         const int to = s + 16 * H;
         if (valid && to < len) {
           const float ddl = Q * o_dsp[H];
-          store_one<BF16>(p.du, rbase + t0 + to, fmaf(o_dt[H], S1, Dd * o_g[H]));
-          store_one<BF16>(p.ddelta, rbase + t0 + to, ddl);
+          store_one<IO>(p.du, rbase + t0 + to, fmaf(o_dt[H], S1, Dd * o_g[H]));
+          store_one<IO>(p.ddelta, rbase + t0 + to, ddl);
           accBias += ddl;
         }
       }
@@ -472,16 +473,16 @@ __global__ void __launch_bounds__(256) sum_mid_kernel(const float *in, float *ou
 
 using BwdFn = void (*)(const BwdParams);
 
-template <bool BF16, bool HZ>
+template <int IO, bool HZ>
 BwdFn pick_bc(bool bv, bool cv) {
-  if (bv && cv) return scan_bwd_kernel<BF16, true, true, HZ>;
-  if (bv) return scan_bwd_kernel<BF16, true, false, HZ>;
-  if (cv) return scan_bwd_kernel<BF16, false, true, HZ>;
-  return scan_bwd_kernel<BF16, false, false, HZ>;
+  if (bv && cv) return scan_bwd_kernel<IO, true, true, HZ>;
+  if (bv) return scan_bwd_kernel<IO, true, false, HZ>;
+  if (cv) return scan_bwd_kernel<IO, false, true, HZ>;
+  return scan_bwd_kernel<IO, false, false, HZ>;
 }
-template <bool BF16>
+template <int IO>
 BwdFn pick_bwd(bool bv, bool cv, bool hz) {
-  return hz ? pick_bc<BF16, true>(bv, cv) : pick_bc<BF16, false>(bv, cv);
+  return hz ? pick_bc<IO, true>(bv, cv) : pick_bc<IO, false>(bv, cv);
 }
 
 struct BwdPlan {
@@ -528,7 +529,6 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   if (pl.blocks > 0x7fffffffLL || static_cast<int64_t>(pl.nB / 256) > 0x7fffffffLL) return SSM_ERR_SHAPE;
   if (a->workspace && a->workspace_bytes < pl.bytes) return SSM_ERR_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const bool bf16 = a->io_dtype == SSM_BF16;
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
 
   void *ws = a->workspace;
@@ -561,7 +561,9 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   p.softplus = a->delta_softplus;
 
   const bool hz = a->z != nullptr;
-  const BwdFn f = bf16 ? pick_bwd<true>(bv, cv, hz) : pick_bwd<false>(bv, cv, hz);
+  const BwdFn f = a->io_dtype == SSM_BF16  ? pick_bwd<1>(bv, cv, hz)
+                 : a->io_dtype == SSM_F16 ? pick_bwd<2>(bv, cv, hz)
+                                          : pick_bwd<0>(bv, cv, hz);
   hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(pl.blocks)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
 

@@ -78,7 +78,7 @@ __device__ __forceinline__ void store_stream(float *p, const float (&v)[NSW]) {
 
 // A block covers kSuChannels channels of one batch row (the batch index is
 // uniform over the block: no per-lane 64-bit division).
-template <bool BF16, int NSW>
+template <int IO, int NSW>
 __global__ void __launch_bounds__(256) state_update_kernel(const StateUpdateParams p) {
   const uint32_t b = blockIdx.x / p.dblocks;
   const uint32_t dblk = blockIdx.x - b * p.dblocks;
@@ -93,8 +93,8 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StateUpdatePara
   const int n = p.n;
   const int s0 = q * NSW;
 
-  float step = load_io<BF16>(p.dt, row);
-  const float xv = load_io<BF16>(p.x, row);
+  float step = load_io<IO>(p.dt, row);
+  const float xv = load_io<IO>(p.x, row);
   float h[NSW], a[NSW], Bv[NSW], Cv[NSW];
   float *srow = p.state + row * n + s0;
   const float *arow = p.A + d * n + s0;
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StateUpdatePara
   bool bc_done = false;
   if constexpr (NSW == 4) {
     if (p.bcvec) {   // a lane's four io elements of B and of C, one vector load each
-      RawV<BF16, 4> rb, rc;
+      RawV<IO, 4> rb, rc;
       rb.load_vec(p.B, bc);
       rc.load_vec(p.C, bc);
 #pragma unroll
@@ -131,8 +131,8 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StateUpdatePara
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
       const bool sv = s0 + k < n;
-      Bv[k] = sv ? load_io<BF16>(p.B, bc + k) : 0.0f;
-      Cv[k] = sv ? load_io<BF16>(p.C, bc + k) : 0.0f;
+      Bv[k] = sv ? load_io<IO>(p.B, bc + k) : 0.0f;
+      Cv[k] = sv ? load_io<IO>(p.C, bc + k) : 0.0f;
     }
   }
 
@@ -160,8 +160,8 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StateUpdatePara
   y += quad_dpp<0x4E>(y);
   if (valid && q == 0) {
     if (p.D) y = fmaf(p.D[d], xv, y);
-    if (p.z) y *= silu_f(load_io<BF16>(p.z, row));
-    store_one<BF16>(p.out, row, y);
+    if (p.z) y *= silu_f(load_io<IO>(p.z, row));
+    store_one<IO>(p.out, row, y);
   }
 }
 
@@ -181,19 +181,20 @@ struct ConvUpdateParams {
 };
 
 // raw io element copy (exact: the cache stores inputs unchanged)
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ uint32_t raw_get(const void *p, int64_t i) {
-  if constexpr (BF16) return static_cast<const uint16_t *>(p)[i];
+  if constexpr (IO) return static_cast<const uint16_t *>(p)[i];
   else return static_cast<const uint32_t *>(p)[i];
 }
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void raw_put(void *p, int64_t i, uint32_t v) {
-  if constexpr (BF16) static_cast<uint16_t *>(p)[i] = static_cast<uint16_t>(v);
+  if constexpr (IO) static_cast<uint16_t *>(p)[i] = static_cast<uint16_t>(v);
   else static_cast<uint32_t *>(p)[i] = v;
 }
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ float raw_float(uint32_t v) {
-  return __uint_as_float(BF16 ? (v << 16) : v);
+  if constexpr (IO != 0) return half_bits_to_float<IO>(v);
+  else return __uint_as_float(v);
 }
 
 __device__ __forceinline__ int64_t ring_slot(int64_t pos, int64_t S) {
@@ -202,7 +203,7 @@ __device__ __forceinline__ int64_t ring_slot(int64_t pos, int64_t S) {
 }
 
 // A block covers 256 channels of one batch row.
-template <bool BF16, int W>
+template <int IO, int W>
 __global__ void __launch_bounds__(256) conv_update_kernel(const ConvUpdateParams p) {
   const uint32_t b = blockIdx.x / p.dblocks;
   const uint32_t dblk = blockIdx.x - b * p.dblocks;
@@ -223,36 +224,36 @@ __global__ void __launch_bounds__(256) conv_update_kernel(const ConvUpdateParams
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) {
     const int64_t slot = p.cache_seqlens ? ring_slot(pos - (W - 1) + k, S) : S - (W - 1) + k;
-    hist[k] = raw_get<BF16>(p.state, sbase + slot);
-    win[k] = raw_float<BF16>(hist[k]);
+    hist[k] = raw_get<IO>(p.state, sbase + slot);
+    win[k] = raw_float<IO>(hist[k]);
   }
-  hist[W - 1] = raw_get<BF16>(p.x, xbase);
+  hist[W - 1] = raw_get<IO>(p.x, xbase);
   for (int64_t t = 0; t < L; ++t) {
-    win[W - 1] = raw_float<BF16>(t == 0 ? hist[W - 1] : raw_get<BF16>(p.x, xbase + t));
+    win[W - 1] = raw_float<IO>(t == 0 ? hist[W - 1] : raw_get<IO>(p.x, xbase + t));
     float acc = bias;
 #pragma unroll
     for (int k = 0; k < W; ++k) acc = fmaf(w[k], win[k], acc);
     if (p.silu) acc = silu_f(acc);
-    store_one<BF16>(p.out, xbase + t, acc);
+    store_one<IO>(p.out, xbase + t, acc);
 #pragma unroll
     for (int k = 0; k < W - 1; ++k) win[k] = win[k + 1];
   }
 
   if (p.cache_seqlens) {
     for (int64_t t = 0; t < L; ++t)
-      raw_put<BF16>(p.state, sbase + ring_slot(pos + t, S), raw_get<BF16>(p.x, xbase + t));
+      raw_put<IO>(p.state, sbase + ring_slot(pos + t, S), raw_get<IO>(p.x, xbase + t));
   } else if (S == W - 1 && L == 1) {
     // one new token into a cache of exactly the window: the new cache is the
     // window's last W-1 inputs, already in registers
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) raw_put<BF16>(p.state, sbase + k, hist[k + 1]);
+    for (int k = 0; k < W - 1; ++k) raw_put<IO>(p.state, sbase + k, hist[k + 1]);
   } else {
     // the last S inputs of (cache, x); ascending, so every cache entry is read
     // before its slot is overwritten
     for (int64_t j = 0; j < S; ++j) {
       const int64_t src = j + L;
-      const uint32_t v = src < S ? raw_get<BF16>(p.state, sbase + src) : raw_get<BF16>(p.x, xbase + src - S);
-      raw_put<BF16>(p.state, sbase + j, v);
+      const uint32_t v = src < S ? raw_get<IO>(p.state, sbase + src) : raw_get<IO>(p.x, xbase + src - S);
+      raw_put<IO>(p.state, sbase + j, v);
     }
   }
 }
@@ -263,18 +264,18 @@ int64_t pow2ceil64(int64_t v) {
   return r;
 }
 
-template <bool BF16>
+template <int IO>
 void launch_state_update(int nsw, dim3 grid, hipStream_t s, const StateUpdateParams &p) {
-  if (nsw == 4) hipLaunchKernelGGL((state_update_kernel<BF16, 4>), grid, dim3(256), 0, s, p);
-  else if (nsw == 2) hipLaunchKernelGGL((state_update_kernel<BF16, 2>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((state_update_kernel<BF16, 1>), grid, dim3(256), 0, s, p);
+  if (nsw == 4) hipLaunchKernelGGL((state_update_kernel<IO, 4>), grid, dim3(256), 0, s, p);
+  else if (nsw == 2) hipLaunchKernelGGL((state_update_kernel<IO, 2>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((state_update_kernel<IO, 1>), grid, dim3(256), 0, s, p);
 }
 
-template <bool BF16>
+template <int IO>
 void launch_conv_update(int width, dim3 grid, hipStream_t s, const ConvUpdateParams &p) {
-  if (width == 4) hipLaunchKernelGGL((conv_update_kernel<BF16, 4>), grid, dim3(256), 0, s, p);
-  else if (width == 3) hipLaunchKernelGGL((conv_update_kernel<BF16, 3>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((conv_update_kernel<BF16, 2>), grid, dim3(256), 0, s, p);
+  if (width == 4) hipLaunchKernelGGL((conv_update_kernel<IO, 4>), grid, dim3(256), 0, s, p);
+  else if (width == 3) hipLaunchKernelGGL((conv_update_kernel<IO, 3>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((conv_update_kernel<IO, 2>), grid, dim3(256), 0, s, p);
 }
 
 }  // namespace
@@ -306,8 +307,9 @@ extern "C" int ssm_state_update(const ssm_state_update_args_t *a, void *stream_p
   if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (a->io_dtype == SSM_BF16) launch_state_update<true>(nsw, grid, stream, p);
-  else launch_state_update<false>(nsw, grid, stream, p);
+  if (a->io_dtype == SSM_BF16) launch_state_update<1>(nsw, grid, stream, p);
+  else if (a->io_dtype == SSM_F16) launch_state_update<2>(nsw, grid, stream, p);
+  else launch_state_update<0>(nsw, grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
@@ -330,8 +332,9 @@ extern "C" int causal_conv1d_update(const void *x, void *conv_state, const float
   if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (io_dtype == SSM_BF16) launch_conv_update<true>(width, grid, stream, p);
-  else launch_conv_update<false>(width, grid, stream, p);
+  if (io_dtype == SSM_BF16) launch_conv_update<1>(width, grid, stream, p);
+  else if (io_dtype == SSM_F16) launch_conv_update<2>(width, grid, stream, p);
+  else launch_conv_update<0>(width, grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;

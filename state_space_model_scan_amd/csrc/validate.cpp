@@ -71,7 +71,7 @@ extern "C" int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *a) {
   if (!product_fits(a->batch, a->dim, a->seqlen) ||
       !product_fits(a->batch * a->dim, a->dstate, a->seqlen))
     return SSM_ERR_SHAPE;
-  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16 && a->io_dtype != SSM_F16) return SSM_ERR_UNSUPPORTED;
   if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   if ((a->B_kind != SSM_BC_FIXED && a->B_kind != SSM_BC_VARYING) ||
       (a->C_kind != SSM_BC_FIXED && a->C_kind != SSM_BC_VARYING))
@@ -105,7 +105,7 @@ extern "C" int ssm_state_update_validate(const ssm_state_update_args_t *a) {
   if (a->dim % a->ngroups != 0) return SSM_ERR_SHAPE;
   if (!product_fits(a->batch, a->dim, a->dstate) || !product_fits(a->batch, a->ngroups, a->dstate))
     return SSM_ERR_SHAPE;
-  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16 && a->io_dtype != SSM_F16) return SSM_ERR_UNSUPPORTED;
   if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   if (a->dt_softplus != 0 && a->dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
   if (!a->state || !a->x || !a->dt || !a->A || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
@@ -120,7 +120,7 @@ extern "C" int causal_conv1d_update_validate(const void *x, const void *conv_sta
   if (!positive(batch) || !positive(dim) || !positive(seqlen) || !positive(state_len))
     return SSM_ERR_SHAPE;
   if (!product_fits(batch, dim, seqlen) || !product_fits(batch, dim, state_len)) return SSM_ERR_SHAPE;
-  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16 && io_dtype != SSM_F16) return SSM_ERR_UNSUPPORTED;
   if (width < 2 || width > SSM_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
   if (state_len < width - 1) return SSM_ERR_SHAPE;
   if (state_len > SSM_MAX_CONV_STATE) return SSM_ERR_UNSUPPORTED;

@@ -332,10 +332,10 @@ def test_conv_fn_binding_errors():
         binding.causal_conv1d_fn(x, w, activation="relu")
 
 
-def test_fp16_io_is_taken_by_the_scan_and_conv_only():
+def test_fp16_io_is_taken_by_all_but_the_mamba2_scan():
     L = _lib.lib()
     assert _validate(_good_args(io_dtype=_lib.SSM_F16)) == _lib.SSM_OK
     assert L.causal_conv1d_validate(FAKE, FAKE, FAKE, 1, 4, 8, 4, _lib.SSM_F16, 0) == _lib.SSM_OK
     assert L.causal_conv1d_ex_validate(ctypes.byref(_good_conv(io_dtype=_lib.SSM_F16))) == _lib.SSM_OK
-    assert L.ssm_scan_bwd_validate(ctypes.byref(_good_bwd(io_dtype=_lib.SSM_F16))) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssm_scan_bwd_validate(ctypes.byref(_good_bwd(io_dtype=_lib.SSM_F16))) == _lib.SSM_OK
     assert L.ssd_scan_validate(ctypes.byref(_good_ssd(io_dtype=_lib.SSM_F16))) == _lib.SSM_ERR_UNSUPPORTED

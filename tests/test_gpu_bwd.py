@@ -4,7 +4,7 @@ forward's checkpoint output, against the float64 oracle, through the C ABI.
 The forward runs on the GPU with checkpoints, then the backward; the oracle
 computes every gradient from the same input bits and dout.  Bar, per element:
 |gpu - ref| <= tol * (1 + |ref|), tol 1e-4 for fp32 io and 2e-2 for bf16 io
-(du, ddelta, dz are stored in the io dtype; dA, dB, dC, dD, ddelta_bias and
+(5e-3 for fp16 io; du, ddelta, dz are stored in the io dtype; dA, dB, dC, dD, ddelta_bias and
 dinitial_state in fp32).  At full size the oracle runs on one (batch, group)
 slice -- every channel of the group, so dB and dC of that slice are complete
 sums -- and on every batch of three channels for dA, dD and ddelta_bias.
@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as orc
-from state_space_model_scan_amd.inputs import (BF16, F32, WORKLOADS, bf16_bits_to_f32, make_dout,
+from state_space_model_scan_amd.inputs import (BF16, F16, F32, WORKLOADS, io_bits_to_f64, make_dout,
                                                make_inputs)
 from tests.harness import TOL, log, to_dev
 
@@ -24,9 +24,7 @@ BASE = WORKLOADS["tiny"].scaled(batch=2, dim=32, seqlen=100, dstate=16, A_mode="
 
 
 def _as_f64(a, io):
-    if a is None:
-        return None
-    return bf16_bits_to_f32(a).astype(np.float64) if io == BF16 else a.astype(np.float64)
+    return None if a is None else io_bits_to_f64(a, io)
 
 
 def _kinds(t):
@@ -94,7 +92,7 @@ def _run(w, what, init=None, t=None):
     return _compare(w, got, want, what)
 
 
-@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("io", [F32, BF16, F16])
 def test_bwd_base(io):
     _run(BASE.scaled(io_dtype=io, seed=500 + io), f"base io={io}")
 
@@ -107,7 +105,7 @@ def test_bwd_sizes(n, seqlen):
 
 
 @pytest.mark.parametrize("bc", ["varying", "fixed", "Bfixed", "Cfixed"])
-@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("io", [F32, BF16, F16])
 def test_bwd_bc_layouts(bc, io):
     w = BASE.scaled(io_dtype=io, bc_kind="fixed" if bc == "fixed" else "varying", seed=530 + len(bc) + io)
     t = make_inputs(w)
@@ -136,7 +134,7 @@ def test_bwd_optional_inputs(flags):
     _run(w, f"flags={flags}", t=t)
 
 
-@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("io", [F32, BF16, F16])
 def test_bwd_initial_state(io):
     w = BASE.scaled(io_dtype=io, seqlen=70, seed=560 + io)
     init = np.random.default_rng(561).standard_normal((w.batch, w.dim, w.dstate))

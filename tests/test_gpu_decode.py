@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as orc
-from state_space_model_scan_amd.inputs import (BF16, DECODE_WORKLOADS, F32, WORKLOADS,
+from state_space_model_scan_amd.inputs import (BF16, F16, DECODE_WORKLOADS, F32, WORKLOADS,
                                                make_decode_inputs, make_inputs)
 from tests.harness import TOL, log, max_err, to_dev
 
@@ -49,7 +49,7 @@ def _state_update_oracle(t, w):
 
 def _check_su(w, t, what, **kw):
     log(f"[state_update] {what}: b={w.batch} d={w.dim} n={w.dstate} g={w.ngroups} "
-        f"io={'bf16' if w.io_dtype == BF16 else 'fp32'}")
+        f"io={w.io_dtype}")
     out, st = _state_update_gpu(t, w, **kw)
     ref_out, ref_st = _state_update_oracle(t, w)
     tol = TOL[w.io_dtype]
@@ -64,7 +64,7 @@ def test_state_update_tiny(name):
     _check_su(w, make_decode_inputs(w), name)
 
 
-@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("io", [F32, BF16, F16])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 12, 16])
 def test_state_update_dstate(io, n):
     w = DECODE_WORKLOADS["decode_tiny"].scaled(batch=3, dim=40, dstate=n, io_dtype=io, ngroups=2,
@@ -143,14 +143,14 @@ def _conv_update_gpu(t, io, act, ring):
                                  to_dev(t["conv_bias"], param=True), "silu" if act else None, seq, out=out)
     torch.cuda.synchronize()
     new = cs.cpu()
-    if io == BF16:
+    if io != F32:
         new = new.view(torch.int16).numpy().view(np.uint16)
     else:
         new = new.numpy()
     return out.float().cpu().numpy().astype(np.float64), new
 
 
-@pytest.mark.parametrize("io", [F32, BF16])
+@pytest.mark.parametrize("io", [F32, BF16, F16])
 @pytest.mark.parametrize("width,state_len,tokens", [(4, 3, 1), (4, 4, 1), (4, 8, 5), (3, 2, 1),
                                                     (2, 1, 3), (4, 3, 7)])
 @pytest.mark.parametrize("ring", [False, True])
