@@ -135,6 +135,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     Dv8[i] = p.D ? (p.D_per_channel ? p.D[h * kP + pp] : p.D[h]) : 0.0f;
   }
   float *sY = reinterpret_cast<float *>(&sM[0][0]);   // Y [t][p] (fp32), 16-byte groups permuted by t
+  // B row-major [t][n] for the A operand of C B^T, in M's space until M is written
+  uint16_t *sBr = &sM[0][0];
+  static_assert(kQ * N <= 2 * kQ * kQ, "the row-major B tile fits in M's space");
 
   // state, transposed: wave w holds S[p = 16w + r][n = 16 nt + 4kq + i]
   f32x4 accs[NT];
@@ -190,6 +193,10 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     float dtraw = 0.0f;
     if (w == 0 && l < len) dtraw = bf2f(dtb[(t0 + l) * p.nheads]);
 
+    // the previous chunk's epilogue reads Y from M's space, which the
+    // row-major B copy below overwrites (the wait overlaps the loads above)
+    __syncthreads();
+
     // ---- X^T and B^T into LDS, two tokens per 32-bit store
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -207,6 +214,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
                            (static_cast<uint32_t>(raw_bits(br[j][1], i)) << 16);
         *reinterpret_cast<uint32_t *>(&sBT[swz<kQ>(n0 + i, t)]) = v;
       }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(&sBr[swz<N>(t + k, n0)]) = br[j][k];
     }
     // ---- the steps and their running sum inside the chunk (padding: dt' = 0)
     if (w == 0) {
@@ -230,21 +239,27 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     // the state-update weights w_t = exp(cs_last - cs_t) * dt'_t
     if (tid < kQ) sW[tid] = fast_exp2((csl - sCs[tid]) * kLog2e) * sDt[tid];
     // ---- M, from G^T = B C^T: lane holds G[t = 16w + r][tau = 16 tb + 4kq + i],
-    // masked to tau <= t, decayed, split, stored as 4 consecutive tau
+    // masked to tau <= t, decayed, split, stored as 4 consecutive tau.  The
+    // products read B from its row-major LDS copy; M overwrites that copy, so
+    // every wave's products are done before any M is stored.
     {
       const int t = 16 * w + r;
       const float cst = sCs[t];
+      f32x4 accg[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        accg[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         if (tb <= w) {
           const int tau_row = 16 * tb + r;   // the B row this lane feeds as A operand
 #pragma unroll
-          for (int kk = 0; kk < KN; ++kk) {
-            const bf16x8 bop = tau_row < len ? ld8(Bb + (t0 + tau_row) * bcrow + 32 * kk + 8 * kq) : zero8;
-            acc = mfma(bop, cop[kk], acc);
-          }
+          for (int kk = 0; kk < KN; ++kk)
+            accg[tb] = mfma(ld8(&sBr[swz<N>(tau_row, 32 * kk + 8 * kq)]), cop[kk], accg[tb]);
         }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 acc = accg[tb];
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
