@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * kQ];    // B^T   [n][t]
   __shared__ __attribute__((aligned(16))) uint16_t sM[2][kQ * kQ];    // M     [t][tau], hi / lo
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][kP * N];     // state [p][n], hi / lo
-  __shared__ float sCs[kQ], sDt[kQ], sW[kQ];
+  __shared__ __attribute__((aligned(16))) float sCs[kQ], sDt[kQ], sW[kQ];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, kq = l >> 4;
@@ -260,12 +260,16 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const f32x4 acc = accg[tb];
+        // the four taus' cumulative steps and steps, one vector read each
+        const float4 cs4 = *reinterpret_cast<const float4 *>(&sCs[16 * tb + 4 * kq]);
+        const float4 dt4 = *reinterpret_cast<const float4 *>(&sDt[16 * tb + 4 * kq]);
+        const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tau = 16 * tb + 4 * kq + i;
           float m = 0.0f;
-          if (tb <= w && tau <= t) m = acc[i] * fast_exp2((cst - sCs[tau]) * kLog2e) * sDt[tau];
+          if (tb <= w && tau <= t) m = acc[i] * fast_exp2((cst - csv[i]) * kLog2e) * dtv[i];
           split_bf(m, hi[i], lo[i]);
         }
         const int o = swz<kQ>(t, 16 * tb + 4 * kq);
@@ -276,16 +280,24 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     __syncthreads();
 
     // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T: lane holds Y[t = 16w + r][p = 16 pb + 4kq + i]
+    // (k-step outer, channel block inner: consecutive products feed four
+    // independent accumulators and a step's operand reads issue together)
     f32x4 accy[4];
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      accy[pb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int pb = 0; pb < 4; ++pb) accy[pb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < KN; ++kk) {
+    for (int kk = 0; kk < KN; ++kk) {
+      bf16x8 shi[4], slo[4];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
         const int o = swz<N>(16 * pb + r, 32 * kk + 8 * kq);
-        accy[pb] = mfma(ld8(&sS[0][o]), cop[kk], accy[pb]);
-        accy[pb] = mfma(ld8(&sS[1][o]), cop[kk], accy[pb]);
+        shi[pb] = ld8(&sS[0][o]);
+        slo[pb] = ld8(&sS[1][o]);
       }
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(shi[pb], cop[kk], accy[pb]);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(slo[pb], cop[kk], accy[pb]);
     }
     {
       const float e = fast_exp2(sCs[16 * w + r] * kLog2e);
