@@ -230,3 +230,37 @@ def test_bwd_full_size_slices():
                 "dD": g["dD"][d:d + 1].cpu().numpy().astype(np.float64),
                 "ddelta_bias": g["ddelta_bias"][d:d + 1].cpu().numpy().astype(np.float64)}
         _compare(w, got1, want1, f"full size channel {d}", names=("dA", "dD", "ddelta_bias"))
+
+
+def test_bwd_longseq_sampled_channels():
+    """longseq (b=1 d=2560 l=65536 n=16 fp32, no z): 2048 chunks per row.
+    The oracle on three single channels gives their complete du, ddelta, dA,
+    dD and d(delta_bias) (one batch row: no sum over the batch)."""
+    import torch
+    from state_space_model_scan_amd import binding
+    w = WORKLOADS["longseq"]
+    log(f"[bwd] long sequence {w.name}")
+    t = make_inputs(w)
+    dout = make_dout(w)
+    io = w.io_dtype
+    dev = lambda a: to_dev(a, io)
+    par = lambda a: to_dev(a, param=True)
+    ck = torch.empty((w.batch, w.dim, binding.checkpoint_count(w.seqlen), w.dstate), dtype=torch.float32,
+                     device="cuda")
+    u, delta, B, C = dev(t["u"]), dev(t["delta"]), dev(t["B"]), dev(t["C"])
+    A, D, bias = par(t["A"]), par(t["D"]), par(t["delta_bias"])
+    binding.ssm_scan_fwd(u, delta, A, B, C, D, None, bias, w.softplus, checkpoints=ck)
+    g = binding.ssm_scan_bwd(u, delta, A, B, C, dev(dout), ck, D=D, delta_bias=bias, delta_softplus=w.softplus)
+    torch.cuda.synchronize()
+    for d in (0, 1283, 2559):
+        one = w.scaled(dim=1)
+        t1 = dict(t)
+        for k in ("u", "delta"):
+            t1[k] = np.ascontiguousarray(t[k][:, d:d + 1])
+        for k in ("A", "D", "delta_bias"):
+            t1[k] = np.ascontiguousarray(t[k][d:d + 1])
+        want = _oracle(one, t1, np.ascontiguousarray(dout[:, d:d + 1]))
+        got = {k: g[k][:, d:d + 1].float().cpu().numpy().astype(np.float64) for k in ("du", "ddelta")}
+        for k in ("dA", "dD", "ddelta_bias"):
+            got[k] = g[k][d:d + 1].cpu().numpy().astype(np.float64)
+        _compare(w, got, want, f"longseq channel {d}", names=("du", "ddelta", "dA", "dD", "ddelta_bias"))
