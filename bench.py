@@ -650,7 +650,8 @@ def bwd_main(args):
             "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)",
             "frac": tops / ALU_PEAK_TOPS,
             "traffic": load_traffic(f"{w.name}_bwd", BWD_SRCS),
-            "kernel": "scan_bwd_kernel (+ the partial-sum kernels: the step's events bracket both)",
+            "kernel": "scan_bwd_kernel (+ the sequence split's carry pass and the partial-sum kernels: the "
+                      "step's events bracket all of them)",
             "kernel_avg_ms": k_s * 1e3,
             "kernel_median_ms": float(np.median(ms)),
             "hbm": {"achieved_GBs": gbs, "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,

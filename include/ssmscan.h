@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -156,6 +156,14 @@ typedef struct ssm_scan_bwd_args {
    * When NULL the library takes it from the stream-ordered allocator. */
   void *workspace;
   size_t workspace_bytes;
+  /* Sequence split: 0 lets the library choose how many segments of whole
+   * SSM_CKPT_INTERVAL chunks the sequence is cut into (it splits when the
+   * channels alone leave compute units idle); k >= 1 asks for at most k
+   * segments (equal whole-chunk lengths, so possibly fewer).  Segments after
+   * the first first get their adjoint carry from a pass of their own; the
+   * results differ from the unsplit ones only by rounding order.  Negative
+   * values return SSM_ERR_SHAPE. */
+  int32_t seq_segments;
 } ssm_scan_bwd_args_t;
 
 /* Selective-scan backward (the same page, section 4.1: the operator's
@@ -184,7 +192,8 @@ int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
 /* Host-only argument check of ssm_scan_bwd (no HIP call). */
 int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *args);
 
-/* Scratch bytes ssm_scan_bwd needs for these arguments (host-only). */
+/* Scratch bytes ssm_scan_bwd needs for these arguments.  Host-only, no HIP
+ * call except a cached query of the device's compute-unit count. */
 int ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *args, size_t *bytes);
 
 /* Causal depthwise conv forward (PaddleNLP Kernel operator-library guide,

@@ -76,6 +76,7 @@ class BwdArgs(ctypes.Structure):
         ("du", _vp), ("ddelta", _vp), ("dz", _vp), ("dA", _vp), ("dB", _vp), ("dC", _vp),
         ("dD", _vp), ("ddelta_bias", _vp), ("dinitial_state", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("seq_segments", ctypes.c_int32),
     ]
 
 

@@ -138,13 +138,14 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
                  D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                  delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
                  want_dinitial_state: bool = False, workspace: Optional[torch.Tensor] = None,
-                 stream=None) -> dict:
+                 seq_segments: int = 0, stream=None) -> dict:
     """Enqueue ssm_scan_bwd; returns the gradients in a dict.
 
     Inputs as for ``ssm_scan_fwd`` (B/C 2-D fixed or 4-D grouped), ``dout`` in
     the io dtype and the ``checkpoints`` that forward call wrote.  du, ddelta
     and dz come back in the io dtype; dA, dB, dC, dD, ddelta_bias and
-    dinitial_state in float32 (dB/dC in B's/C's layout).
+    dinitial_state in float32 (dB/dC in B's/C's layout).  ``seq_segments``
+    caps the sequence split (0: the library's choice).
     """
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
@@ -187,6 +188,7 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
     args.delta_softplus = int(bool(delta_softplus))
     args.checkpoints, args.dout = _ptr(checkpoints), _ptr(dout)
+    args.seq_segments = int(seq_segments)
     for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
         setattr(args, k, _ptr(g[k]))
     L = _lib.lib()

@@ -69,8 +69,12 @@ struct BwdParams {
   float *pA;            // (b, d, n)
   float *pD, *pbias;    // (b, d)
   float *dinit;         // (b, d, n) or null
-  int64_t dim, seqlen, cpg;
+  // sequence split: segment k >= 1's carry out of its first timestep with no
+  // carry coming in (nseg, b, d, n), and its sum of delta' (nseg, b, d)
+  float *loc, *ssum;
+  int64_t dim, seqlen, cpg, bd;   // bd = batch * dim
   int n, ngroups, nblk, nck, softplus;
+  int segc, nseg;                 // chunks per segment, segments
 };
 
 __device__ __forceinline__ float sigmoid_f(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
@@ -196,6 +200,9 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
   const int bg = blockIdx.x / p.nblk;          // b * ngroups + g
   const int g = bg % p.ngroups;
   const int64_t b = bg / p.ngroups;
+  const int seg = blockIdx.y;                  // this workgroup's chunks: [cbeg, cend)
+  const int cbeg = seg * p.segc;
+  const int cend = cbeg + p.segc < p.nck ? cbeg + p.segc : p.nck;
   const int64_t lc = static_cast<int64_t>(blk) * kCPB + w * kCPW + c;   // channel within the group
   const bool valid = lc < p.cpg;
   const int64_t dl = g * p.cpg + (valid ? lc : p.cpg - 1);
@@ -236,6 +243,14 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
 
   // ---- running state of this lane
   float gcar = 0.0f;                          // h carried into the next-earlier timestep
+  if (seg + 1 < p.nseg && sv) {
+    // carry into this segment: the later segments' own carries, each scaled
+    // by the decay of the segments between (exp2(A' * sum of delta'))
+    for (int k = p.nseg - 1; k > seg; --k) {
+      const int64_t r = static_cast<int64_t>(k) * p.bd + row;
+      gcar = fmaf(fast_exp2(Ap * p.ssum[r]), gcar, p.loc[r * n + s]);
+    }
+  }
   float dA_acc = 0.0f, dBf_acc = 0.0f, dCf_acc = 0.0f;
   float accD = 0.0f, accBias = 0.0f;          // owner sums over its timesteps
 
@@ -260,13 +275,13 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
     }
   };
 
-  fetch_own(p.nck - 1);
-  fetch_tile(p.nck - 1);
+  fetch_own(cend - 1);
+  fetch_tile(cend - 1);
   store_tile(0);
   __syncthreads();
 
-  for (int k = 0; k < p.nck; ++k) {
-    const int ci = p.nck - 1 - k;
+  for (int k = 0; k < cend - cbeg; ++k) {
+    const int ci = cend - 1 - k;
     const int kb = k & 1;
     const int64_t t0 = static_cast<int64_t>(ci) * kT;
     const int len = static_cast<int>((L - t0 < kT) ? L - t0 : kT);
@@ -282,7 +297,7 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
       c_go[h] = raw_float<IO>(r_go[h]);
       c_z[h] = raw_float<IO>(r_z[h]);
     }
-    if (ci > 0) {
+    if (ci > cbeg) {
       fetch_own(ci - 1);
       fetch_tile(ci - 1);
     }
@@ -382,8 +397,20 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
       gcar = h * a;
 
       float vb = 0.0f, vc = 0.0f;
-      if constexpr (BV) vb = h * bc<K>(o_dtu[H]); else dBf_acc = fmaf(h, bc<K>(o_dtu[H]), dBf_acc);
-      if constexpr (CV) vc = gg * xt; else dCf_acc = fmaf(gg, xt, dCf_acc);
+      // the empty asm keeps each fixed-B/C sum in step with the walk; left
+      // free, the scheduler holds the chunk's products live and spills
+      if constexpr (BV) {
+        vb = h * bc<K>(o_dtu[H]);
+      } else {
+        dBf_acc = fmaf(h, bc<K>(o_dtu[H]), dBf_acc);
+        asm volatile("" : "+v"(dBf_acc));
+      }
+      if constexpr (CV) {
+        vc = gg * xt;
+      } else {
+        dCf_acc = fmaf(gg, xt, dCf_acc);
+        asm volatile("" : "+v"(dCf_acc));
+      }
       if constexpr (ANYV) {
         if constexpr (t & 1) {
           pb_hi = vb;
@@ -421,7 +448,7 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
 
     // next tile into the other buffer; after the barrier the chunk's dB/dC
     // accumulator is complete
-    if (ci > 0) store_tile(kb ^ 1);
+    if (ci > cbeg) store_tile(kb ^ 1);
     __syncthreads();
     if (ANYV && t_thr) {
       // the workgroup's sum: its waves' slots added in wave order
@@ -440,12 +467,13 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
     }
   }
 
-  // ---- per-lane results over the whole sequence
+  // ---- per-lane results over the segment (partials indexed (seg, b, d))
+  const int64_t prow = seg * p.bd + row;
   if (valid && sv) {
-    if (p.dinit) p.dinit[row * n + s] = gcar;
-    p.pA[row * n + s] = dA_acc;
-    if constexpr (!BV) p.pB[row * n + s] = dBf_acc;
-    if constexpr (!CV) p.pC[row * n + s] = dCf_acc;
+    if (p.dinit && seg == 0) p.dinit[row * n + s] = gcar;
+    p.pA[prow * n + s] = dA_acc;
+    if constexpr (!BV) p.pB[prow * n + s] = dBf_acc;
+    if constexpr (!CV) p.pC[prow * n + s] = dCf_acc;
   }
   // owner sums over the row's 16 lanes
 #pragma unroll
@@ -454,9 +482,128 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
     accBias += __shfl_xor(accBias, m, 16);
   }
   if (valid && s == 0) {
-    if (p.pD) p.pD[row] = accD;
-    if (p.pbias) p.pbias[row] = accBias;
+    if (p.pD) p.pD[prow] = accD;
+    if (p.pbias) p.pbias[prow] = accBias;
   }
+}
+
+// Sequence split, first pass.  The adjoint carry is linear in what comes in
+// from later timesteps: over segment k it maps an incoming carry G to
+// loc_k + exp2(A' * sum_k) * G, where loc_k is the carry out of the segment's
+// first timestep when G = 0 (h_t = g_t C_t + a_{t+1} h_{t+1} walked over the
+// segment alone) and sum_k the segment's sum of delta'.  This kernel writes
+// loc_k and sum_k for every segment k >= 1; it needs only delta, dout, z and
+// C.  A 256-thread workgroup holds 16 channels of one (batch, group), one
+// 16-lane row (one lane per state) each, and walks its segment in tiles of
+// 64 timesteps: the tile's C (shared by the 16 channels) is loaded
+// coalesced and staged through LDS, one tile ahead; lane j of a row owns
+// timesteps j, j+16, j+32, j+48 of the tile, computes their delta' and
+// dout * silu(z), and the row reads them by DPP broadcast.
+constexpr int kCT = 64;   // timesteps per carry tile
+
+template <int IO, bool CV, bool HZ>
+__global__ void __launch_bounds__(256) seg_carry_kernel(const BwdParams p) {
+  __shared__ __align__(16) float s_c[CV ? 2 : 1][kNP][kCT + 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c = lane >> 4, s = lane & 15;
+  const int n = p.n;
+  const bool sv = s < n;
+  const int64_t L = p.seqlen;
+  const int nb16 = static_cast<int>((p.cpg + 15) / 16);
+  const int blk = blockIdx.x % nb16;
+  const int bg = blockIdx.x / nb16;
+  const int g = bg % p.ngroups;
+  const int64_t b = bg / p.ngroups;
+  const int64_t lc = static_cast<int64_t>(blk) * 16 + w * 4 + c;
+  const bool valid = lc < p.cpg;
+  const int64_t dl = g * p.cpg + (valid ? lc : p.cpg - 1);
+  const int64_t row = b * p.dim + dl;
+  const int64_t rbase = row * L;
+  const int seg = blockIdx.y + 1;
+  const int64_t tbeg = static_cast<int64_t>(seg) * p.segc * kT;
+  const int64_t tend = tbeg + static_cast<int64_t>(p.segc) * kT < L ? tbeg + static_cast<int64_t>(p.segc) * kT : L;
+
+  const float Ap = (sv ? p.A[dl * n + s] : 0.0f) * kLog2e;
+  const float Cf = (!CV && sv) ? load_io<IO>(p.C, dl * n + s) : 0.0f;
+  const float bias = p.dbias ? p.dbias[dl] : 0.0f;
+
+  // C tile: thread -> (state tid >> 4, timesteps 4 * (tid & 15) + 0..3);
+  // rows of states >= n are staged as zeros
+  const int cs = tid >> 4, ct = (tid & 15) * 4;
+  const bool c_on = CV && cs < n;
+  const int64_t csrc = (static_cast<int64_t>(bg) * n + (c_on ? cs : 0)) * L;
+  // raw bits of the next tile: the owned timesteps' delta, dout, z and the
+  // thread's four C elements
+  uint32_t r_d[4], r_go[4], r_z[4], r_c[4];
+  auto fetch = [&](int64_t tb) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int64_t t = tb + s + 16 * h;
+      r_d[h] = r_go[h] = r_z[h] = 0;
+      if (t < tend) {
+        r_d[h] = raw_load<IO>(p.delta, rbase + t);
+        r_go[h] = raw_load<IO>(p.dout, rbase + t);
+        if constexpr (HZ) r_z[h] = raw_load<IO>(p.z, rbase + t);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r_c[j] = 0;
+      if (c_on && tb + ct + j < tend) r_c[j] = raw_load<IO>(p.C, csrc + tb + ct + j);
+    }
+  };
+  auto stage = [&](int buf) {
+    if constexpr (CV)
+      *reinterpret_cast<float4 *>(&s_c[buf][cs][ct]) =
+          make_float4(raw_float<IO>(r_c[0]), raw_float<IO>(r_c[1]), raw_float<IO>(r_c[2]), raw_float<IO>(r_c[3]));
+  };
+
+  float gcar = 0.0f, dsum = 0.0f;
+  const int ntile = static_cast<int>((tend - tbeg + kCT - 1) / kCT);
+  fetch(tbeg + static_cast<int64_t>(ntile - 1) * kCT);
+  stage(0);
+  __syncthreads();
+  for (int i = ntile - 1, k = 0; i >= 0; --i, ++k) {
+    const int buf = CV ? (k & 1) : 0;
+    const int64_t tb = tbeg + static_cast<int64_t>(i) * kCT;
+    float o_dt[4], o_g[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float raw = raw_float<IO>(r_d[h]) + bias;
+      float dt = p.softplus ? softplus_f(raw) : raw;
+      const float go = raw_float<IO>(r_go[h]);
+      float gg = go;
+      if constexpr (HZ) {
+        const float zz = raw_float<IO>(r_z[h]);
+        gg = go * zz * sigmoid_f(zz);
+      }
+      if (tb + s + 16 * h >= tend) { dt = 0.0f; gg = 0.0f; }   // inert timestep
+      o_dt[h] = dt;
+      o_g[h] = gg;
+      dsum += dt;
+    }
+    if (i > 0) fetch(tb - kCT);
+
+    const float(*cr)[kCT + 4] = s_c[buf];
+    float4 C4 = make_float4(Cf, Cf, Cf, Cf);
+    static_for(std::make_integer_sequence<int, kCT>{}, [&](auto RR) {
+      constexpr int t = kCT - 1 - decltype(RR)::value;
+      constexpr int K = t & 15, H = t >> 4;
+      if constexpr (CV && (t & 3) == 3) C4 = *reinterpret_cast<const float4 *>(&cr[s][t - 3]);
+      const float h = fmaf(bc<K>(o_g[H]), f4get<t & 3>(C4), gcar);
+      gcar = h * fast_exp2(bc<K>(o_dt[H]) * Ap);
+    });
+    if constexpr (CV) {
+      if (i > 0) stage(buf ^ 1);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 16);
+  const int64_t prow = static_cast<int64_t>(seg) * p.bd + row;
+  if (valid && sv) p.loc[prow * n + s] = gcar;
+  if (valid && s == 0) p.ssum[prow] = dsum;
 }
 
 // out[i, j] = sum_k in[i, k, j] for an (I, K, J) array, k in increasing order.
@@ -485,27 +632,74 @@ BwdFn pick_bwd(bool bv, bool cv, bool hz) {
   return hz ? pick_bc<IO, true>(bv, cv) : pick_bc<IO, false>(bv, cv);
 }
 
+template <int IO>
+BwdFn pick_carry(bool cv, bool hz) {
+  if (cv) return hz ? seg_carry_kernel<IO, true, true> : seg_carry_kernel<IO, true, false>;
+  return hz ? seg_carry_kernel<IO, false, true> : seg_carry_kernel<IO, false, false>;
+}
+
+constexpr int kMaxSeg = 64;   // most segments the library picks by itself
+constexpr int kMinSegChunks = 4;   // and the fewest chunks it gives a segment
+
 struct BwdPlan {
   int64_t cpg, nblk, nck, blocks;
-  size_t nB, nC, nA, nD;   // partial element counts
+  int segc, nseg;
+  size_t nB, nC, nA, nD, nLoc, nSum;   // partial element counts
   size_t bytes;
 };
 
-BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a) {
+// Segments of the sequence split.  One 768-thread workgroup fills a compute
+// unit, so a grid of few workgroups leaves units idle, and one that is not a
+// whole number of rounds leaves its last round part-empty.  Cutting the
+// sequence into ns segments multiplies the workgroups by ns and divides each
+// one's length by ns, at the price of the carry pass over the segments after
+// the first, which costs about a quarter of the main pass per (channel,
+// timestep) when it fills the chip (measured).  Modelled time, in units of
+// one workgroup walking one chunk:
+//   ceil(blocks * ns / cus) * segc  +  kCarryCost * (ns - 1) / ns * blocks * nck / cus
+// and the plan takes the segment count that minimises it.
+constexpr double kCarryCost = 0.25;
+
+int pick_segments(int64_t blocks, int64_t nck, int cus) {
+  const int64_t most = nck / kMinSegChunks < kMaxSeg ? nck / kMinSegChunks : kMaxSeg;
+  const double work = static_cast<double>(blocks) * static_cast<double>(nck) / cus;
+  int best = 1;
+  double best_t = 1e300;
+  for (int64_t k = 1; k <= (most > 1 ? most : 1); ++k) {
+    const int64_t segc = (nck + k - 1) / k;
+    const int64_t ns = (nck + segc - 1) / segc;
+    const double rounds = static_cast<double>((blocks * ns + cus - 1) / cus);
+    const double t = rounds * static_cast<double>(segc) + kCarryCost * static_cast<double>(ns - 1) / ns * work;
+    if (t < best_t * 0.99) {   // a split has to win by more than the model's noise
+      best_t = t;
+      best = static_cast<int>(ns);
+    }
+  }
+  return best;
+}
+
+BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a, int cus) {
   BwdPlan pl{};
   pl.cpg = a->dim / a->ngroups;
   pl.nblk = (pl.cpg + kCPB - 1) / kCPB;
   pl.nck = (a->seqlen + kT - 1) / kT;
   pl.blocks = a->batch * a->ngroups * pl.nblk;
+  int64_t want = a->seq_segments > 0 ? a->seq_segments : pick_segments(pl.blocks, pl.nck, cus);
+  if (want > pl.nck) want = pl.nck;
+  pl.segc = static_cast<int>((pl.nck + want - 1) / want);
+  pl.nseg = static_cast<int>((pl.nck + pl.segc - 1) / pl.segc);   // every segment holds a chunk
+  const size_t ns = static_cast<size_t>(pl.nseg);
   const size_t bgn = static_cast<size_t>(a->batch * a->ngroups) * pl.nblk * a->dstate * a->seqlen;
   const size_t bdn = static_cast<size_t>(a->batch * a->dim * a->dstate);
-  pl.nB = a->B_kind == SSM_BC_VARYING ? bgn : bdn;
-  pl.nC = a->C_kind == SSM_BC_VARYING ? bgn : bdn;
-  pl.nA = bdn;
-  pl.nD = static_cast<size_t>(a->batch * a->dim);
+  pl.nB = a->B_kind == SSM_BC_VARYING ? bgn : ns * bdn;
+  pl.nC = a->C_kind == SSM_BC_VARYING ? bgn : ns * bdn;
+  pl.nA = ns * bdn;
+  pl.nD = ns * static_cast<size_t>(a->batch * a->dim);
+  pl.nLoc = pl.nseg > 1 ? ns * bdn : 0;
+  pl.nSum = pl.nseg > 1 ? pl.nD : 0;
   // every partial array starts on a 256-byte boundary
   auto up = [](size_t e) { return (e * sizeof(float) + 255) / 256 * 256; };
-  pl.bytes = up(pl.nB) + up(pl.nC) + up(pl.nA) + 2 * up(pl.nD);
+  pl.bytes = up(pl.nB) + up(pl.nC) + up(pl.nA) + 2 * up(pl.nD) + up(pl.nLoc) + up(pl.nSum);
   return pl;
 }
 
@@ -518,15 +712,17 @@ extern "C" int ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *a, size_t 
   const int st = ssm_scan_bwd_validate(a);
   if (st != SSM_OK) return st;
   if (!bytes) return SSM_ERR_NULL;
-  *bytes = plan_bwd(a).bytes;
+  *bytes = plan_bwd(a, cu_count_cached()).bytes;
   return SSM_OK;
 }
 
 extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   const int st = ssm_scan_bwd_validate(a);
   if (st != SSM_OK) return st;
-  const BwdPlan pl = plan_bwd(a);
-  if (pl.blocks > 0x7fffffffLL || static_cast<int64_t>(pl.nB / 256) > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  const BwdPlan pl = plan_bwd(a, cu_count_cached());
+  if (pl.blocks > 0x7fffffffLL || static_cast<int64_t>(pl.nB / 256) > 0x7fffffffLL ||
+      static_cast<int64_t>(pl.nA / 256) > 0x7fffffffLL || pl.nseg > 65535)
+    return SSM_ERR_SHAPE;
   if (a->workspace && a->workspace_bytes < pl.bytes) return SSM_ERR_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
@@ -554,18 +750,34 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   float *pd = take(pl.nD), *pbias = take(pl.nD);
   p.pD = a->D ? pd : nullptr;
   p.pbias = a->delta_bias ? pbias : nullptr;
+  p.loc = pl.nLoc ? take(pl.nLoc) : nullptr;
+  p.ssum = pl.nSum ? take(pl.nSum) : nullptr;
   p.dinit = a->dinitial_state;
-  p.dim = a->dim; p.seqlen = a->seqlen; p.cpg = pl.cpg;
+  p.dim = a->dim; p.seqlen = a->seqlen; p.cpg = pl.cpg; p.bd = a->batch * a->dim;
   p.n = static_cast<int>(a->dstate); p.ngroups = static_cast<int>(a->ngroups);
   p.nblk = static_cast<int>(pl.nblk); p.nck = static_cast<int>(pl.nck);
   p.softplus = a->delta_softplus;
+  p.segc = pl.segc; p.nseg = pl.nseg;
 
   const bool hz = a->z != nullptr;
+  hipError_t e = hipSuccess;
+  if (pl.nseg > 1) {
+    const BwdFn fc = a->io_dtype == SSM_BF16  ? pick_carry<1>(cv, hz)
+                    : a->io_dtype == SSM_F16 ? pick_carry<2>(cv, hz)
+                                             : pick_carry<0>(cv, hz);
+    const int64_t cblocks = a->batch * a->ngroups * ((pl.cpg + 15) / 16);
+    hipLaunchKernelGGL(fc, dim3(static_cast<unsigned>(cblocks), static_cast<unsigned>(pl.nseg - 1)), dim3(256), 0,
+                       stream, p);
+    e = hipGetLastError();
+  }
   const BwdFn f = a->io_dtype == SSM_BF16  ? pick_bwd<1>(bv, cv, hz)
                  : a->io_dtype == SSM_F16 ? pick_bwd<2>(bv, cv, hz)
                                           : pick_bwd<0>(bv, cv, hz);
-  hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(pl.blocks)), dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(pl.blocks), static_cast<unsigned>(pl.nseg)), dim3(kThreads), 0,
+                       stream, p);
+    e = hipGetLastError();
+  }
 
   auto reduce = [&](const float *in, float *out, int64_t I, int64_t K, int64_t J) {
     if (e != hipSuccess) return;
@@ -574,13 +786,14 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
     e = hipGetLastError();
   };
   const int64_t bsz = a->batch, n = a->dstate, L = a->seqlen, dim = a->dim;
+  const int64_t kpart = pl.nseg * bsz;   // per-(segment, batch) partials
   if (bv) reduce(p.pB, a->dB, bsz * a->ngroups, pl.nblk, n * L);
-  else reduce(p.pB, a->dB, 1, bsz, dim * n);
+  else reduce(p.pB, a->dB, 1, kpart, dim * n);
   if (cv) reduce(p.pC, a->dC, bsz * a->ngroups, pl.nblk, n * L);
-  else reduce(p.pC, a->dC, 1, bsz, dim * n);
-  reduce(p.pA, a->dA, 1, bsz, dim * n);
-  if (a->D) reduce(p.pD, a->dD, 1, bsz, dim);
-  if (a->delta_bias) reduce(p.pbias, a->ddelta_bias, 1, bsz, dim);
+  else reduce(p.pC, a->dC, 1, kpart, dim * n);
+  reduce(p.pA, a->dA, 1, kpart, dim * n);
+  if (a->D) reduce(p.pD, a->dD, 1, kpart, dim);
+  if (a->delta_bias) reduce(p.pbias, a->ddelta_bias, 1, kpart, dim);
 
   if (owned) {
     const hipError_t ef = hipFreeAsync(ws, stream);

@@ -10,6 +10,10 @@ namespace ssm {
 // Records a failed HIP call for ssm_last_hip_error() and returns SSM_ERR_HIP.
 int hip_fail(hipError_t e);
 
+// Compute units of the current device (queried once per device; 256 when the
+// query fails).
+int cu_count_cached();
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace ssm

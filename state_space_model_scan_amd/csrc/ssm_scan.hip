@@ -25,6 +25,20 @@ int hip_fail(hipError_t e) {
   return SSM_ERR_HIP;
 }
 
+int cu_count_cached() {
+  static std::mutex mu;
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (counts[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    counts[dev] = v;
+  }
+  return counts[dev];
+}
+
 }  // namespace ssm
 
 namespace {
@@ -106,19 +120,6 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
 // host side
 // ---------------------------------------------------------------------------
 
-int cu_count_cached() {
-  static std::mutex mu;
-  static int counts[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lk(mu);
-  if (counts[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    counts[dev] = v;
-  }
-  return counts[dev];
-}
 
 struct Plan {
   int n_pad, nsw, lpc, T;

@@ -77,6 +77,7 @@ extern "C" int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *a) {
       (a->C_kind != SSM_BC_FIXED && a->C_kind != SSM_BC_VARYING))
     return SSM_ERR_UNSUPPORTED;
   if (a->delta_softplus != 0 && a->delta_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->seq_segments < 0) return SSM_ERR_SHAPE;
   if (!a->u || !a->delta || !a->A || !a->B || !a->C || !a->checkpoints || !a->dout ||
       !a->du || !a->ddelta || !a->dA || !a->dB || !a->dC)
     return SSM_ERR_NULL;

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 6
+    assert L.ssm_abi_version() == 7
 
 
 def test_status_strings():
@@ -268,10 +268,18 @@ def test_bwd_validation():
     assert L.ssm_scan_bwd(ctypes.byref(_good_bwd(dout=None)), None) == _lib.SSM_ERR_NULL
     need = ctypes.c_size_t(0)
     assert L.ssm_scan_bwd_workspace_size(ctypes.byref(_good_bwd()), ctypes.byref(need)) == _lib.SSM_OK
-    # partial dB/dC per 32-channel workgroup, dA per batch, dD and ddelta_bias per batch
-    nblk = (64 // 2 + 31) // 32
+    # partial dB/dC per 48-channel workgroup, dA per batch, dD and ddelta_bias per batch
+    nblk = (64 // 2 + 47) // 48
     up = lambda e: (e * 4 + 255) // 256 * 256
     assert need.value == 2 * up(2 * 2 * nblk * 16 * 100) + up(2 * 64 * 16) + 2 * up(2 * 64)
+    # a sequence split (100 timesteps: 4 chunks) keeps dA, dD, ddelta_bias per
+    # (segment, batch) and adds each segment's carry and sum of delta'
+    for segs, ns in ((2, 2), (3, 2), (4, 4), (1000, 4)):
+        assert L.ssm_scan_bwd_workspace_size(ctypes.byref(_good_bwd(seq_segments=segs)),
+                                             ctypes.byref(need)) == _lib.SSM_OK
+        assert need.value == (2 * up(2 * 2 * nblk * 16 * 100) + up(ns * 2 * 64 * 16) + 2 * up(ns * 2 * 64)
+                              + up(ns * 2 * 64 * 16) + up(ns * 2 * 64)), segs
+    assert v(_good_bwd(seq_segments=-1)) == _lib.SSM_ERR_SHAPE
 
 
 def test_bwd_binding_errors():

@@ -33,7 +33,7 @@ def _kinds(t):
     return bk, ck
 
 
-def _gpu(w, t, dout, init=None, want_dinit=True, ret_ckpt=False):
+def _gpu(w, t, dout, init=None, want_dinit=True, ret_ckpt=False, seq_segments=0):
     import torch
     from state_space_model_scan_amd import binding
     io = w.io_dtype
@@ -46,7 +46,8 @@ def _gpu(w, t, dout, init=None, want_dinit=True, ret_ckpt=False):
     init_t = None if init is None else par(init.astype(np.float32))
     binding.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, w.softplus, initial_state=init_t, checkpoints=ck)
     g = binding.ssm_scan_bwd(u, delta, A, B, C, dev(dout), ck, D=D, z=z, delta_bias=bias,
-                             delta_softplus=w.softplus, want_dinitial_state=want_dinit)
+                             delta_softplus=w.softplus, want_dinitial_state=want_dinit,
+                             seq_segments=seq_segments)
     torch.cuda.synchronize()
     res = {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
     if ret_ckpt:
@@ -82,12 +83,12 @@ def _compare(w, got, want, what, names=None):
     return errs
 
 
-def _run(w, what, init=None, t=None):
+def _run(w, what, init=None, t=None, seq_segments=0):
     log(f"[bwd] {what}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} io={w.io_dtype} "
-        f"bc={w.bc_kind} z={w.has_z} D={w.has_D} bias={w.has_bias} sp={w.softplus}")
+        f"bc={w.bc_kind} z={w.has_z} D={w.has_D} bias={w.has_bias} sp={w.softplus} seg={seq_segments}")
     t = make_inputs(w) if t is None else t
     dout = make_dout(w)
-    got = _gpu(w, t, dout, init)
+    got = _gpu(w, t, dout, init, seq_segments=seq_segments)
     want = _oracle(w, t, dout, init)
     return _compare(w, got, want, what)
 
@@ -139,6 +140,41 @@ def test_bwd_initial_state(io):
     w = BASE.scaled(io_dtype=io, seqlen=70, seed=560 + io)
     init = np.random.default_rng(561).standard_normal((w.batch, w.dim, w.dstate))
     _run(w, f"initial state io={io}", init=init)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 8, 1000])
+@pytest.mark.parametrize("bc", ["varying", "fixed"])
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_bwd_sequence_split(segments, bc, io):
+    """The sequence cut into segments of whole chunks (229 timesteps: 8
+    chunks, the last ragged; 1000 is capped at one chunk per segment), every
+    gradient against the oracle, from an initial state so dinitial_state
+    carries the adjoint through every segment."""
+    w = BASE.scaled(seqlen=229, io_dtype=io, bc_kind=bc, seed=590 + segments + io)
+    init = np.random.default_rng(591).standard_normal((w.batch, w.dim, w.dstate))
+    _run(w, f"split {segments} bc={bc}", init=init, seq_segments=segments)
+
+
+@pytest.mark.parametrize("flags", [dict(has_z=False), dict(softplus=False, delta_mean=0.3, delta_std=0.1)])
+def test_bwd_sequence_split_flags(flags):
+    w = BASE.scaled(seqlen=200, io_dtype=F32, seed=595, **flags)
+    t = make_inputs(w)
+    if not w.softplus:
+        t["delta"] = (np.abs(t["delta"]) + 0.05).astype(np.float32)
+    _run(w, f"split 3 flags={flags}", t=t, seq_segments=3)
+
+
+def test_bwd_split_agrees_with_unsplit():
+    """Split and unsplit differ only by rounding order (fp32 io)."""
+    w = BASE.scaled(seqlen=300, io_dtype=F32, dim=64, ngroups=2, seed=597)
+    t = make_inputs(w)
+    dout = make_dout(w)
+    a = _gpu(w, t, dout, seq_segments=1)
+    b = _gpu(w, t, dout, seq_segments=5)
+    for k, v in a.items():
+        if v is not None:
+            e = _err(b[k], v)
+            assert e <= 2e-5, f"{k}: split vs unsplit {e:.3e}"
 
 
 def test_checkpoints_are_the_forward_states():
