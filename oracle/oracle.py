@@ -92,6 +92,11 @@ def _load():
         lib.oracle_round_f16.restype = ctypes.c_double
         lib.oracle_f16_bits_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_bits_to_double.restype = ctypes.c_double
+        lib.oracle_selective_scan_complex.argtypes = [
+            i64, i64, i64, i64, i64, i32,
+            p, p, p, p, i32, p, i32, p, p, p, i32, p,
+            p, i64, p, p, i32]
+        lib.oracle_selective_scan_complex.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -180,6 +185,46 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(rows_a), nrows, _ptr(out), _ptr(last), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_selective_scan failed with status {rc}")
+    return out, last
+
+
+def selective_scan_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=False, *, io_dtype=F32, ngroups=1,
+                           B_kind=BC_VARYING, C_kind=BC_VARYING, initial_state=None,
+                           rows=None, nthreads=0):
+    """Oracle selective scan with complex A (see ``ssm_oracle.c``).
+
+    u, delta, z: (batch, dim, seqlen) io bits; A: (dim, dstate, 2) float32
+    (real, imaginary) pairs; B/C: io bits with a trailing pair axis,
+    (dim, dstate, 2) fixed or (batch, ngroups, dstate, seqlen, 2) varying;
+    initial_state: (batch, dim, dstate, 2) float64 or None.
+    Returns (out (nrows, seqlen) float64, last_state (nrows, dstate, 2) float64).
+    """
+    lib = _load()
+    delta = _io(delta, io_dtype)
+    batch, dim, seqlen = delta.shape
+    A = _f32(A)
+    if A.ndim != 3 or A.shape[2] != 2:
+        raise ValueError("A must be (dim, dstate, 2) pairs")
+    dstate = A.shape[1]
+    u, z = _io(u, io_dtype), _io(z, io_dtype)
+    B, C = _io(B, io_dtype), _io(C, io_dtype)
+    for name, t in (("B", B), ("C", C)):
+        if t.shape[-1] != 2:
+            raise ValueError(f"{name} must end in a (real, imaginary) pair axis")
+    D, delta_bias = _f32(D), _f32(delta_bias)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = batch * dim if rows_a is None else rows_a.shape[0]
+    out = np.empty((nrows, seqlen), dtype=np.float64)
+    last = np.empty((nrows, dstate, 2), dtype=np.float64)
+    rc = lib.oracle_selective_scan_complex(
+        batch, dim, seqlen, dstate, ngroups, io_dtype,
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), B_kind, _ptr(C), C_kind,
+        _ptr(D), _ptr(delta_bias), _ptr(z), int(bool(delta_softplus)), _ptr(init),
+        _ptr(rows_a), nrows, _ptr(out), _ptr(last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan_complex failed with status {rc}")
     return out, last
 
 

@@ -46,6 +46,7 @@
  * are double.  Rows are independent, so the optional thread split over rows
  * gives bit-identical results for any thread count.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -327,6 +328,105 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t seqlen,
         }
         free(x);
         free(urow);
+    }
+    (void)nthreads;
+    return failed ? 5 : 0;
+}
+
+/* ---- selective scan with complex A -------------------------------------- */
+
+/* The guide's section 4.1 says A (dim, dstate) may be real or complex and
+ * prints nothing more about the complex case.  Reading: the same recurrence
+ * over the complex numbers, with B and C complex too (a real B or C is the
+ * case of zero imaginary parts), and the output the real part of the
+ * contraction:
+ *   x_t = exp(dt' A) x_{t-1} + dt' B_t u_t     (complex, per state),
+ *   y_t = Re(sum_s C_t[s] x_t[s]),  out = (y + D u) silu(z).
+ * dt', u, z, D and delta_bias are real as before.  Complex values are stored
+ * as (real, imaginary) pairs, the pair innermost: A (dim, dstate, 2) fp32;
+ * B/C (dim, dstate, 2) or (batch, groups, dstate, seqlen, 2) io;
+ * initial_state and last_state (batch, dim, dstate, 2) double. */
+static double complex bc_at_c(const void *p, int kind, int dtype, const oracle_scan_args *a,
+                              int64_t b, int64_t d, int64_t s, int64_t t) {
+    int64_t i;
+    if (kind == OR_BC_FIXED) {
+        i = d * a->dstate + s;
+    } else {
+        const int64_t g = d / (a->dim / a->ngroups);
+        i = ((b * a->ngroups + g) * a->dstate + s) * a->seqlen + t;
+    }
+    return load_io(p, dtype, 2 * i) + I * load_io(p, dtype, 2 * i + 1);
+}
+
+static void scan_row_complex(const oracle_scan_args *a, int64_t row, double *out, double *last,
+                             double complex *x) {
+    const int64_t l = a->seqlen, n = a->dstate;
+    const int64_t b = row / a->dim, d = row % a->dim;
+    const int64_t base = row * l;
+    for (int64_t s = 0; s < n; ++s)
+        x[s] = a->initial_state ? a->initial_state[2 * (row * n + s)] + I * a->initial_state[2 * (row * n + s) + 1]
+                                : 0.0;
+    for (int64_t t = 0; t < l; ++t) {
+        double dt = load_io(a->delta, a->io_dtype, base + t);
+        if (a->delta_bias) dt += (double)a->delta_bias[d];
+        if (a->delta_softplus) dt = oracle_softplus(dt);
+        const double ut = load_io(a->u, a->io_dtype, base + t);
+        double y = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            const double complex Av = (double)a->A[2 * (d * n + s)] + I * (double)a->A[2 * (d * n + s) + 1];
+            const double complex dA = cexp(dt * Av);
+            x[s] = dA * x[s] + dt * bc_at_c(a->B, a->B_kind, a->io_dtype, a, b, d, s, t) * ut;
+            y += creal(bc_at_c(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s]);
+        }
+        if (a->D) y += (double)a->D[d] * ut;
+        if (a->z) y *= oracle_silu(load_io(a->z, a->io_dtype, base + t));
+        out[t] = y;
+    }
+    if (last)
+        for (int64_t s = 0; s < n; ++s) {
+            last[2 * s] = creal(x[s]);
+            last[2 * s + 1] = cimag(x[s]);
+        }
+}
+
+/* Complex-A selective-scan forward over selected rows (NULL = all); the
+ * layouts are above.  out: (nrows, seqlen) double; last_state: (nrows,
+ * dstate, 2) double or NULL.  No conv prologue.  Returns 0, 1 (null required
+ * pointer), 2 (bad shape). */
+int oracle_selective_scan_complex(int64_t batch, int64_t dim, int64_t seqlen,
+                                  int64_t dstate, int64_t ngroups, int io_dtype,
+                                  const void *u, const void *delta, const float *A,
+                                  const void *B, int B_kind, const void *C, int C_kind,
+                                  const float *D, const float *delta_bias, const void *z,
+                                  int delta_softplus, const double *initial_state,
+                                  const int64_t *rows, int64_t nrows,
+                                  double *out, double *last_state, int nthreads) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!u || !delta || !A || !B || !C || !out) return 1;
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, D, delta_bias, z, delta_softplus,
+                          initial_state, NULL, NULL, NULL, 0, 0};
+    const int64_t total = rows ? nrows : batch * dim;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(|:failed)
+#endif
+    {
+        double complex *x = (double complex *)malloc(sizeof(double complex) * (size_t)dstate);
+        if (!x) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t r = 0; r < total; ++r) {
+                const int64_t row = rows ? rows[r] : r;
+                scan_row_complex(&a, row, out + r * seqlen, last_state ? last_state + r * 2 * dstate : NULL, x);
+            }
+        }
+        free(x);
     }
     (void)nthreads;
     return failed ? 5 : 0;
