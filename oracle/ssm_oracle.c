@@ -367,8 +367,7 @@ static void scan_row_complex(const oracle_scan_args *a, int64_t row, double *out
         x[s] = a->initial_state ? a->initial_state[2 * (row * n + s)] + I * a->initial_state[2 * (row * n + s) + 1]
                                 : 0.0;
     for (int64_t t = 0; t < l; ++t) {
-        double dt = load_io(a->delta, a->io_dtype, base + t);
-        if (a->delta_bias) dt += (double)a->delta_bias[d];
+        double dt = load_io(a->delta, a->io_dtype, base + t) + (a->delta_bias ? (double)a->delta_bias[d] : 0.0);
         if (a->delta_softplus) dt = oracle_softplus(dt);
         const double ut = load_io(a->u, a->io_dtype, base + t);
         double y = 0.0;
@@ -378,8 +377,8 @@ static void scan_row_complex(const oracle_scan_args *a, int64_t row, double *out
             x[s] = dA * x[s] + dt * bc_at_c(a->B, a->B_kind, a->io_dtype, a, b, d, s, t) * ut;
             y += creal(bc_at_c(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s]);
         }
-        if (a->D) y += (double)a->D[d] * ut;
-        if (a->z) y *= oracle_silu(load_io(a->z, a->io_dtype, base + t));
+        if (a->D) y += ut * (double)a->D[d];
+        if (a->z) y = y * oracle_silu(load_io(a->z, a->io_dtype, base + t));
         out[t] = y;
     }
     if (last)

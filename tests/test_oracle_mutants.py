@@ -353,33 +353,33 @@ def test_f16_pins_catch_mutant(mutant, tmp_path):
 # the complex-A scan against its own pins
 # --------------------------------------------------------------------------
 
-import tests.test_oracle_complex_pins as cpins  # noqa: E402
+import tests.test_oracle_complex_pins as xpins  # noqa: E402
 
 COMPLEX_MUTANTS = {
-    "cx_conj_rotation": ("const double complex dA = cexp(dt * Av);", "const double complex dA = cexp(dt * conj(Av));"),
-    "cx_conj_C": ("y += creal(bc_at_c(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s]);",
+    "cplx_conj_rotation": ("const double complex dA = cexp(dt * Av);", "const double complex dA = cexp(dt * conj(Av));"),
+    "cplx_conj_C": ("y += creal(bc_at_c(a->C, a->C_kind, a->io_dtype, a, b, d, s, t) * x[s]);",
                   "y += creal(conj(bc_at_c(a->C, a->C_kind, a->io_dtype, a, b, d, s, t)) * x[s]);"),
-    "cx_imag_output": ("y += creal(bc_at_c(", "y += cimag(bc_at_c("),
-    "cx_drop_imag_of_BC": ("return load_io(p, dtype, 2 * i) + I * load_io(p, dtype, 2 * i + 1);",
+    "cplx_imag_output": ("y += creal(bc_at_c(", "y += cimag(bc_at_c("),
+    "cplx_drop_imag_of_BC": ("return load_io(p, dtype, 2 * i) + I * load_io(p, dtype, 2 * i + 1);",
                            "return load_io(p, dtype, 2 * i) + 0.0 * load_io(p, dtype, 2 * i + 1);"),
-    "cx_pair_order": ("return load_io(p, dtype, 2 * i) + I * load_io(p, dtype, 2 * i + 1);",
+    "cplx_pair_order": ("return load_io(p, dtype, 2 * i) + I * load_io(p, dtype, 2 * i + 1);",
                       "return load_io(p, dtype, 2 * i + 1) + I * load_io(p, dtype, 2 * i);"),
-    "cx_init_imag_dropped": ("+ I * a->initial_state[2 * (row * n + s) + 1]", "+ 0.0 * a->initial_state[2 * (row * n + s) + 1]"),
-    "cx_last_imag": ("last[2 * s + 1] = cimag(x[s]);", "last[2 * s + 1] = -cimag(x[s]);"),
-    "cx_group_interleaved": ("const int64_t g = d / (a->dim / a->ngroups);", "const int64_t g = d % a->ngroups;"),
-    "cx_drop_dt_in_input": ("x[s] = dA * x[s] + dt * bc_at_c(", "x[s] = dA * x[s] + bc_at_c("),
+    "cplx_init_imag_dropped": ("+ I * a->initial_state[2 * (row * n + s) + 1]", "+ 0.0 * a->initial_state[2 * (row * n + s) + 1]"),
+    "cplx_last_imag": ("last[2 * s + 1] = cimag(x[s]);", "last[2 * s + 1] = -cimag(x[s]);"),
+    "cplx_group_interleaved": ("const int64_t g = d / (a->dim / a->ngroups);", "const int64_t g = d % a->ngroups;"),
+    "cplx_drop_dt_in_input": ("x[s] = dA * x[s] + dt * bc_at_c(", "x[s] = dA * x[s] + bc_at_c("),
 }
 
 
 def _complex_pin_calls():
     F32, BF16 = orc.F32, orc.BF16
     return [
-        ("real_case_f32_g2", lambda: cpins.test_complex_real_case_equals_real_scan(F32, False, 2)),
-        ("real_case_bf16_fixed", lambda: cpins.test_complex_real_case_equals_real_scan(BF16, True, 1)),
-        ("brute_varying", lambda: cpins.test_complex_brute_force_tiny(False, True)),
-        ("brute_fixed", lambda: cpins.test_complex_brute_force_tiny(True, False)),
-        ("rotation", cpins.test_complex_rotation_closed_form),
-        ("conjugate", cpins.test_complex_conjugate_symmetry),
+        ("real_case_f32_g2", lambda: xpins.test_complex_real_case_equals_real_scan(F32, False, 2)),
+        ("real_case_bf16_fixed", lambda: xpins.test_complex_real_case_equals_real_scan(BF16, True, 1)),
+        ("brute_varying", lambda: xpins.test_complex_brute_force_tiny(False, True)),
+        ("brute_fixed", lambda: xpins.test_complex_brute_force_tiny(True, False)),
+        ("rotation", xpins.test_complex_rotation_closed_form),
+        ("conjugate", xpins.test_complex_conjugate_symmetry),
     ]
 
 
