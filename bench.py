@@ -75,6 +75,7 @@ KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip"
 DECODE_SRCS = ("decode.hip", "device_util.h")
 SSD_SRCS = ("ssd.hip", "device_util.h")
 BWD_SRCS = ("bwd.hip", "device_util.h")
+COMPLEX_SRCS = ("scan_complex.hip", "scan_kernel.h", "device_util.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -190,6 +191,9 @@ def main():
         return ssd_main(args)
     if args.backward:
         return bwd_main(args)
+    from state_space_model_scan_amd.inputs import COMPLEX_WORKLOADS
+    if args.workload in COMPLEX_WORKLOADS:
+        return complex_main(args)
 
     def to_dev(a, io_dtype, param=False):
         x = torch.from_numpy(np.ascontiguousarray(a))
@@ -284,6 +288,140 @@ def main():
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
 
+
+
+def complex_algorithmic_bytes(w) -> int:
+    """Every input read once and every output written once: u, delta, z, out
+    (b, d, l) io; complex B, C (pairs) io; A (d, n, 2), D, delta_bias fp32;
+    last_state (b, d, n, 2) fp32."""
+    es = 2 if w.io_dtype in (1, 2) else 4
+    e = w.batch * w.dim * w.seqlen
+    vecs = (3 + (1 if w.has_z else 0)) * e * es
+    per_bc = (w.dim * w.dstate * 2 if w.bc_kind == "fixed"
+              else w.batch * w.ngroups * w.dstate * w.seqlen * 2) * es
+    params = w.dim * w.dstate * 8 + (w.dim * 4 if w.has_D else 0) + (w.dim * 4 if w.has_bias else 0)
+    return vecs + 2 * per_bc + params + w.batch * w.dim * w.dstate * 8
+
+
+def complex_algorithmic_alu_ops(w) -> float:
+    """Per (timestep, state): delta' times Re A and Im A, the fraction of the
+    phase, the decay's two products, B's two products with delta' u, four
+    FMAs of the complex state update and two of Re(C.x) (13 plain ops), plus
+    exp2, sine and cosine, each weighted 4 (quarter rate); per element the
+    26 of the real scan (softplus, gate, D)."""
+    return float(w.elements) * (25 * w.dstate + 26)
+
+
+def complex_main(args):
+    """One ssm_scan_fwd_complex launch per timed step."""
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, COMPLEX_WORKLOADS, F16, make_complex_inputs
+
+    _lib.lib()
+    w = COMPLEX_WORKLOADS[args.workload]
+    t = make_complex_inputs(w)
+    io = w.io_dtype
+
+    def dev(a, param=False):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and io in (BF16, F16) and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16 if io == BF16 else torch.float16)
+        return x.cuda()
+
+    u, delta, z, B, C = dev(t["u"]), dev(t["delta"]), dev(t["z"]), dev(t["B"]), dev(t["C"])
+    A, D, bias = dev(t["A"], True), dev(t["D"], True), dev(t["delta_bias"], True)
+    init = dev(t["initial_state"], True)
+    out = torch.empty_like(delta)
+    last = torch.empty((w.batch, w.dim, w.dstate, 2), dtype=torch.float32, device="cuda")
+
+    def step():
+        binding.ssm_scan_fwd_complex(u, delta, A, B, C, D, z, bias, w.softplus, out=out, last_state=last,
+                                     initial_state=init)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    abytes = complex_algorithmic_bytes(w)
+    alu_tops = complex_algorithmic_alu_ops(w) / avg_launch_s / 1e12
+    hbm_gbs = abytes / avg_launch_s / 1e9
+    iot = {0: "fp32", 1: "bf16", 2: "fp16"}[io]
+    rec = {
+        "metric": METRIC, "value": w.elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} "
+                               f"complex A/B/C, B/C {w.bc_kind}, {iot} io, fp32 complex state"
+                               f"{', z gate' if w.has_z else ''}",
+                   "io_dtype": iot, "elements_per_step": w.elements},
+        "roofline": {
+            "bound": "alu", "achieved": alu_tops, "peak": ALU_PEAK_TOPS,
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)", "frac": alu_tops / ALU_PEAK_TOPS,
+            "traffic": load_traffic(w.name, COMPLEX_SRCS),
+            "kernel_avg_ms": avg_launch_s * 1e3, "kernel_median_ms": float(np.median(launch_ms)),
+            "kernel_min_ms": float(np.min(launch_ms)),
+            "hbm": {"achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": abytes},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = complex_cpu_baseline(w, t, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+def complex_cpu_baseline(w, t, budget_s: float):
+    """The oracle's complex scan on a bounded sample of rows (all host threads)."""
+    from oracle import oracle as orc
+    threads = orc.max_threads()
+    total_rows = w.batch * w.dim
+    rng = np.random.default_rng(0)
+    kind = orc.BC_FIXED if w.bc_kind == "fixed" else orc.BC_VARYING
+    init = None if t["initial_state"] is None else t["initial_state"].astype(np.float64)
+
+    def run(rows):
+        orc.selective_scan_complex(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                   t["delta_bias"], w.softplus, io_dtype=w.io_dtype, ngroups=w.ngroups,
+                                   B_kind=kind, C_kind=kind, initial_state=init, rows=rows,
+                                   nthreads=threads)
+
+    n = min(total_rows, max(threads, 16))
+    while True:
+        probe = np.sort(rng.choice(total_rows, size=n, replace=False))
+        t0 = time.perf_counter()
+        run(probe)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 or n == total_rows:
+            break
+        n = min(total_rows, 4 * n)
+    nrows = int(min(total_rows, max(len(probe), budget_s / max(dt / len(probe), 1e-9))))
+    rows = np.sort(rng.choice(total_rows, size=nrows, replace=False))
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    return {"value": nrows * w.seqlen / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} of {total_rows} (b,d) rows x full seqlen {w.seqlen}, "
+                      f"{dt:.1f} s float64 complex scan on {threads} threads"}
 
 
 def decode_main(args):

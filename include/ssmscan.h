@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -124,6 +124,33 @@ int ssm_scan_validate(const ssm_scan_args_t *args);
  * the whole sequence in one pass).  Host-only, no HIP call except a cached
  * query of the device's compute-unit count. */
 int ssm_scan_workspace_size(const ssm_scan_args_t *args, size_t *bytes);
+
+/* Selective-scan forward with complex A (the same page, section 4.1: A
+ * (dim, dstate) may be real or complex; nothing more is printed about the
+ * complex case).  Read as the recurrence above over the complex numbers, with
+ * B and C complex too (a real B or C is the case of zero imaginary parts),
+ * and the output the real part of the contraction:
+ *
+ *     x_t[s] = exp(delta'_t A[d,s]) x_{t-1}[s] + delta'_t B_t[s] u_t   (complex)
+ *     y_t    = Re(sum_s C_t[s] x_t[s]),   out_t = (y_t + D[d] u_t) silu(z_t)
+ *
+ * delta', u, z, D, delta_bias and out are real as in ssm_scan_fwd.  The
+ * arguments are those of ssm_scan_fwd with these layouts, every complex value
+ * a (real, imaginary) pair with the pair innermost:
+ *   A: (dim, dstate, 2) fp32;
+ *   B, C: io, fixed (dim, dstate, 2) or varying (batch, ngroups, dstate,
+ *         seqlen, 2);
+ *   initial_state, last_state: (batch, dim, dstate, 2) fp32 or NULL.
+ * Not taken (SSM_ERR_UNSUPPORTED): the fused conv prologue (conv_weight must
+ * be NULL; run causal_conv1d_fwd first) and checkpoints (there is no complex
+ * backward).  u is required; workspace is ignored (the sequence is walked in
+ * one pass).  The decay's phase uses the hardware sine and cosine on the
+ * fractional part of delta' Im(A) / (2 pi).  Same conventions and status
+ * codes as ssm_scan_fwd. */
+int ssm_scan_fwd_complex(const ssm_scan_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssm_scan_fwd_complex (no HIP call). */
+int ssm_scan_complex_validate(const ssm_scan_args_t *args);
 
 /* Arguments of ssm_scan_bwd.  Every pointer is a device pointer.  The inputs
  * are those of the forward call (same shapes, dtypes and layout kinds);

@@ -12,4 +12,5 @@ from .binding import (  # noqa: F401
     conv1d_selective_scan_fn,
     selective_scan_fn,
     ssm_scan_fwd,
+    ssm_scan_fwd_complex,
 )

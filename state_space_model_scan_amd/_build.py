@@ -30,6 +30,7 @@ SOURCES = [
     ("scan_f32.hip", True),
     ("scan_f16.hip", True),
     ("ssm_scan.hip", True),
+    ("scan_complex.hip", True),
     ("decode.hip", True),
     ("ssd.hip", True),
     ("bwd.hip", True),

@@ -21,6 +21,7 @@ SSM_CKPT_INTERVAL = 32
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
     "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size",
+    "ssm_scan_fwd_complex", "ssm_scan_complex_validate",
     "causal_conv1d_fwd", "causal_conv1d_validate", "causal_conv1d_fwd_ex", "causal_conv1d_ex_validate",
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
@@ -133,6 +134,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_validate.restype = ctypes.c_int
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_workspace_size.restype = ctypes.c_int
+        L.ssm_scan_fwd_complex.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        L.ssm_scan_fwd_complex.restype = ctypes.c_int
+        L.ssm_scan_complex_validate.argtypes = [ctypes.POINTER(ScanArgs)]
+        L.ssm_scan_complex_validate.restype = ctypes.c_int
         L.causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, i64, i64, i64, i32, i32, i32, _vp]
         L.causal_conv1d_fwd.restype = ctypes.c_int
         L.causal_conv1d_validate.argtypes = [_vp, _vp, _vp, i64, i64, i64, i32, i32, i32]

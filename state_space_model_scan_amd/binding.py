@@ -128,6 +128,84 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     return out
 
 
+def _pairs(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """A complex tensor as its (real, imaginary) pairs; other tensors as given."""
+    if t is None:
+        return None
+    return torch.view_as_real(t) if t.is_complex() else t
+
+
+def _bc_kind_complex(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    """(kind, ngroups) of a complex B or C given as pairs (trailing axis 2)."""
+    if t.shape[-1] != 2:
+        raise ValueError(f"{name} must be complex or end in a (real, imaginary) pair axis")
+    kind, g = _bc_kind(t[..., 0], name)
+    return kind, g
+
+
+def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                         B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                         z: Optional[torch.Tensor] = None,
+                         delta_bias: Optional[torch.Tensor] = None,
+                         delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                         last_state: Optional[torch.Tensor] = None,
+                         initial_state: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """Enqueue ssm_scan_fwd_complex on the current stream; returns ``out``.
+
+    A is complex64 (dim, dstate) or float32 pairs (dim, dstate, 2).  B and C
+    are complex64 (fp32 io) or io-dtype pairs: fixed (dim, dstate, 2), varying
+    (batch, dstate, seqlen, 2) or (batch, groups, dstate, seqlen, 2).
+    ``last_state`` / ``initial_state`` are complex64 or float32 pairs
+    (batch, dim, dstate, 2).  u, delta, z and out are real, as in ssm_scan_fwd.
+    """
+    delta = _dense(delta)
+    io = _IO.get(delta.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
+    batch, dim, seqlen = delta.shape
+    A, B, C = _pairs(A), _pairs(B), _pairs(C)
+    initial_state = _pairs(initial_state)
+    if last_state is not None:
+        last_state = _pairs(last_state)
+        if not last_state.is_contiguous():
+            raise ValueError("last_state must be contiguous")
+    if A.dim() != 3 or A.shape[-1] != 2:
+        raise ValueError("A must be complex (dim, dstate) or float32 pairs (dim, dstate, 2)")
+    dstate = A.shape[1]
+    if B.dim() == 4:
+        B = B.unsqueeze(1)
+    if C.dim() == 4:
+        C = C.unsqueeze(1)
+    B, C = _dense(B), _dense(C)
+    bk, bg = _bc_kind_complex(B, "B")
+    ck, cg = _bc_kind_complex(C, "C")
+    if bk == _lib.SSM_BC_VARYING and ck == _lib.SSM_BC_VARYING and bg != cg:
+        raise ValueError("B and C must have the same number of groups")
+    ngroups = max(bg, cg, 1)
+    for name, t in (("u", u), ("z", z), ("B", B), ("C", C)):
+        if t is not None and t.dtype != delta.dtype:
+            raise ValueError(f"{name} must have the io dtype {delta.dtype} (as pairs), got {t.dtype}")
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("initial_state", initial_state),
+                    ("last_state", last_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 (complex64 for A and the states), got {t.dtype}")
+    if out is None:
+        out = torch.empty_like(delta)
+    args = ScanArgs()
+    args.batch, args.dim, args.seqlen, args.dstate, args.ngroups = batch, dim, seqlen, dstate, ngroups
+    args.io_dtype = io
+    u, A, D, z, delta_bias = _dense(u), _dense(A), _dense(D), _dense(z), _dense(delta_bias)
+    initial_state = _dense(initial_state)
+    args.u, args.delta, args.A = _ptr(u), _ptr(delta), _ptr(A)
+    args.B, args.B_kind, args.C, args.C_kind = _ptr(B), bk, _ptr(C), ck
+    args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
+    args.delta_softplus = int(bool(delta_softplus))
+    args.out, args.last_state, args.initial_state = _ptr(out), _ptr(last_state), _ptr(initial_state)
+    check(_lib.lib().ssm_scan_fwd_complex(ctypes.byref(args), _stream(delta.device, stream)))
+    return out
+
+
 def checkpoint_count(seqlen: int) -> int:
     """Saved states per channel: one every SSM_CKPT_INTERVAL timesteps."""
     return (seqlen + _lib.SSM_CKPT_INTERVAL - 1) // _lib.SSM_CKPT_INTERVAL
@@ -224,7 +302,18 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
 def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                       delta_softplus=False, return_last_state=False
                       ) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
-    """Forward of selective_scan_fn with the page's signature and returns."""
+    """Forward of selective_scan_fn with the page's signature and returns.
+    A complex A (section 4.1: real or complex) runs ssm_scan_fwd_complex;
+    its B and C are then complex too (complex64, or io-dtype pairs), and
+    last_state is complex64."""
+    if A.is_complex():
+        last = None
+        if return_last_state:
+            last = torch.empty((delta.shape[0], delta.shape[1], A.shape[1]), dtype=torch.complex64,
+                               device=delta.device)
+        out = ssm_scan_fwd_complex(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                   last_state=last)
+        return (out, last) if return_last_state else out
     if B.dim() == 3:
         B = B.unsqueeze(1)
     if C.dim() == 3:

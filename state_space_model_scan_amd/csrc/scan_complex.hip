@@ -1,0 +1,338 @@
+// scan_complex.hip -- the selective-scan forward with complex A for gfx950,
+// and its C-ABI entry point ssm_scan_fwd_complex.
+//
+// Operation: PaddleNLP Kernel operator-library guide, section 4.1
+// (selective_scan_fn): A (dim, dstate) may be real or complex.  The page
+// prints nothing more about the complex case; it is read as the same
+// recurrence over the complex numbers, with B and C complex as well and the
+// output the real part of the contraction (include/ssmscan.h):
+//
+//     x_t[s] = exp(delta'_t A[d,s]) x_{t-1}[s] + delta'_t B_t[s] u_t
+//     y_t    = Re(sum_s C_t[s] x_t[s]),   out_t = (y_t + D u_t) silu(z_t)
+//
+// Complex values are (real, imaginary) pairs of the element type, the pair
+// innermost.  Per (timestep, state) the decay is
+//   exp(delta' A) = 2^(delta' Re A log2 e) * (cos 2 pi r, sin 2 pi r),
+//   r = fract(delta' Im A / (2 pi)),
+// with the hardware exp2 and the hardware sine and cosine, which take their
+// argument in revolutions (the fraction keeps it in [0, 1)).
+//
+// Work decomposition (the real kernel's, in scan_kernel.h): four lanes per
+// channel, lane q holding complex states [q*NSW, (q+1)*NSW) in VGPRs; chunks
+// of 32 timesteps, lane q owning timesteps [8q, 8q+8) of each chunk for the
+// loads, delta' = softplus(delta + bias), delta'*u and the gated store;
+// delta' and delta'*u reach the quad by DPP broadcasts; time-varying B/C of a
+// chunk are staged in the wave's LDS slice (complex pairs interleaved, as in
+// memory) and read two timesteps ahead; each lane's partial Re(C.x) goes to
+// LDS and the owner sums the quad's partials.  The whole sequence is walked
+// in one pass (no sequence split).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "host_util.h"
+#include "scan_kernel.h"
+#include "ssmscan.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+constexpr int kLPC = 4;                 // lanes per channel
+constexpr int kT = 8 * kLPC;            // timesteps per chunk
+constexpr int kCPW = 64 / kLPC;         // channels per wave
+
+struct CplxParams {
+  const void *u, *delta, *B, *C, *z;
+  const float *A, *D, *dbias, *init;
+  void *out;
+  float *last;
+  int64_t batch, dim, seqlen, cpg;
+  int n, ngroups, groups_eff, nblk, nblocks;
+  int softplus, vec, xcd_swizzle;
+};
+
+// exp(dt * (ar + i ai)) with ar2 = ar * log2 e and airev = ai / (2 pi)
+__device__ __forceinline__ void cexp_step(float dt, float ar2, float airev, float &er, float &ei) {
+  const float mag = fast_exp2(dt * ar2);
+  const float r = __builtin_amdgcn_fractf(dt * airev);
+  er = mag * __builtin_amdgcn_cosf(r);
+  ei = mag * __builtin_amdgcn_sinf(r);
+}
+
+template <int IO, int NSW, bool BV, bool CV>
+__global__ void __launch_bounds__(64)
+scan_complex_kernel(const CplxParams p) {
+  constexpr bool ANYV = BV || CV;
+  constexpr int NP = NSW * kLPC;        // padded state count
+  constexpr int PIECES = NP * (kT / 8); // B/C staging pieces: 8 timesteps of one state
+  static_assert(PIECES <= 64, "one B/C piece per lane");
+
+  // [B or C][timestep][state][re, im]
+  __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kT : 1][ANYV ? NP : 1][2];
+  // partial Re(C.x) of every (timestep, channel, lane) of the chunk
+  __shared__ float s_yp[kT * kCPW * kLPC];
+
+  const int lane = threadIdx.x & 63;
+  const int q = lane % kLPC;
+  const int cw_idx = lane / kLPC;
+
+  int bid = blockIdx.x;
+  if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
+  const int blk = bid % p.nblk;
+  const int rest = bid / p.nblk;
+  const int g = rest % p.groups_eff;
+  const int64_t b = rest / p.groups_eff;
+  const int64_t d_end = (g + 1) * p.cpg;
+  const int64_t d = g * p.cpg + static_cast<int64_t>(blk) * kCPW + cw_idx;
+  const bool valid = d < d_end;
+  const int64_t dl = valid ? d : d_end - 1;
+  const int64_t row = b * p.dim + dl;
+  const int64_t rbase = row * p.seqlen;
+  const int64_t seqlen = p.seqlen;
+  const int s0 = q * NSW;
+  const int n = p.n;
+  const bool vec = p.vec != 0;
+
+  float Ar[NSW], Ai[NSW], Bfr[NSW], Bfi[NSW], Cfr[NSW], Cfi[NSW], xr[NSW], xi[NSW];
+#pragma unroll
+  for (int k = 0; k < NSW; ++k) {
+    const int s = s0 + k;
+    const bool sv = s < n;
+    const int64_t e = (dl * n + s) * 2;
+    Ar[k] = sv ? p.A[e] * kLog2e : 0.0f;
+    Ai[k] = sv ? p.A[e + 1] * kInv2Pi : 0.0f;
+    Bfr[k] = (!BV && sv) ? load_io<IO>(p.B, e) : 0.0f;
+    Bfi[k] = (!BV && sv) ? load_io<IO>(p.B, e + 1) : 0.0f;
+    Cfr[k] = (!CV && sv) ? load_io<IO>(p.C, e) : 0.0f;
+    Cfi[k] = (!CV && sv) ? load_io<IO>(p.C, e + 1) : 0.0f;
+    xr[k] = (p.init && sv) ? p.init[(row * n + s) * 2] : 0.0f;
+    xi[k] = (p.init && sv) ? p.init[(row * n + s) * 2 + 1] : 0.0f;
+  }
+  const float bias = p.dbias ? p.dbias[dl] : 0.0f;
+  const float Dd = p.D ? p.D[dl] : 0.0f;
+  // element index of (b, g, state 0, t 0, re) in a varying B/C
+  const int64_t bc_base = ((b * p.ngroups + g) * n) * seqlen * 2;
+
+  const int own = q * kKP;
+  auto count = [&](int64_t c) {
+    const int64_t tp0 = c + own;
+    return static_cast<int>((seqlen - tp0 < kKP) ? seqlen - tp0 : kKP);
+  };
+
+  RawV<IO, kKP> r_u, r_dl, r_z;
+  r_u.zero(); r_dl.zero(); r_z.zero();
+  auto fetch = [&](int64_t c) {
+    const int64_t tp0 = c + own;
+    const int cnt = count(c);
+    r_u.load(p.u, rbase + tp0, cnt, vec);
+    r_dl.load(p.delta, rbase + tp0, cnt, vec);
+    if (p.z) r_z.load(p.z, rbase + tp0, cnt, vec);
+  };
+
+  // B/C tile of a chunk: lane v < PIECES loads 8 timesteps (16 io elements)
+  // of one state of B and of C
+  const int bc_s = lane / (kT / 8);
+  const int bc_t0 = (lane % (kT / 8)) * 8;
+  const bool bc_lane = ANYV && lane < PIECES;
+  const bool bc_real = bc_lane && bc_s < n;
+  RawV<IO, 8> rB0, rB1, rC0, rC1;
+  rB0.zero(); rB1.zero(); rC0.zero(); rC1.zero();
+  auto fetch_bc = [&](int64_t c) {
+    if (bc_real) {
+      const int64_t e = bc_base + (static_cast<int64_t>(bc_s) * seqlen + c + bc_t0) * 2;
+      const int64_t left = seqlen - (c + bc_t0);
+      const int ec = 2 * static_cast<int>(left < 8 ? left : 8);   // io elements in range
+      if constexpr (BV) { rB0.load(p.B, e, ec, vec); rB1.load(p.B, e + 8, ec - 8, vec); }
+      if constexpr (CV) { rC0.load(p.C, e, ec, vec); rC1.load(p.C, e + 8, ec - 8, vec); }
+    }
+  };
+  auto stage_bc = [&]() {
+    if (bc_lane) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const RawV<IO, 8> &sb = i < 4 ? rB0 : rB1;
+        const RawV<IO, 8> &sc = i < 4 ? rC0 : rC1;
+        if constexpr (BV) {
+          s_bc[0][bc_t0 + i][bc_s][0] = sb.get(2 * (i & 3));
+          s_bc[0][bc_t0 + i][bc_s][1] = sb.get(2 * (i & 3) + 1);
+        }
+        if constexpr (CV) {
+          s_bc[ANYV ? 1 : 0][bc_t0 + i][bc_s][0] = sc.get(2 * (i & 3));
+          s_bc[ANYV ? 1 : 0][bc_t0 + i][bc_s][1] = sc.get(2 * (i & 3) + 1);
+        }
+      }
+    }
+  };
+
+  float dtv[kKP], dtuv[kKP], duv[kKP], yv[kKP];
+#pragma unroll
+  for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
+
+  auto prep = [&](int64_t c) {
+    const int cnt = count(c);
+#pragma unroll
+    for (int i = 0; i < kKP; ++i) {
+      const float uu = r_u.get(i);
+      float dt = r_dl.get(i) + bias;
+      if (p.softplus) dt = softplus_f(dt);
+      if (i >= cnt) dt = 0.0f;
+      dtv[i] = dt;
+      dtuv[i] = dt * uu;
+      duv[i] = Dd * uu;
+    }
+  };
+
+  struct StepIn {
+    float dt, dtu, Br[NSW], Bi[NSW], Cr[NSW], Ci[NSW];
+  };
+  auto load_in = [&](auto TT, StepIn &in) {
+    constexpr int t = decltype(TT)::value;
+    in.dt = dpp_bcast_reg<quad_bcast_ctrl<kLPC, t / kKP>()>(dtv[t % kKP]);
+    in.dtu = dpp_bcast_reg<quad_bcast_ctrl<kLPC, t / kKP>()>(dtuv[t % kKP]);
+#pragma unroll
+    for (int k = 0; k < NSW; ++k) {
+      if constexpr (BV) { in.Br[k] = s_bc[0][t][s0 + k][0]; in.Bi[k] = s_bc[0][t][s0 + k][1]; }
+      else { in.Br[k] = Bfr[k]; in.Bi[k] = Bfi[k]; }
+      if constexpr (CV) { in.Cr[k] = s_bc[ANYV ? 1 : 0][t][s0 + k][0]; in.Ci[k] = s_bc[ANYV ? 1 : 0][t][s0 + k][1]; }
+      else { in.Cr[k] = Cfr[k]; in.Ci[k] = Cfi[k]; }
+    }
+  };
+
+  // one timestep: complex state update, then this lane's part of Re(C.x)
+  auto step = [&](auto TT, const StepIn &in) {
+    constexpr int t = decltype(TT)::value;
+    float y = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NSW; ++k) {
+      float er, ei;
+      cexp_step(in.dt, Ar[k], Ai[k], er, ei);
+      const float br = in.Br[k] * in.dtu, bi = in.Bi[k] * in.dtu;
+      const float nr = fmaf(er, xr[k], fmaf(-ei, xi[k], br));
+      const float ni = fmaf(er, xi[k], fmaf(ei, xr[k], bi));
+      xr[k] = nr;
+      xi[k] = ni;
+      y = fmaf(in.Cr[k], nr, y);
+      y = fmaf(-in.Ci[k], ni, y);
+    }
+    s_yp[(t * kCPW + cw_idx) * kLPC + q] = y;
+  };
+
+  fetch(0);
+  if constexpr (ANYV) fetch_bc(0);
+
+  for (int64_t c = 0; c < seqlen; c += kT) {
+    const int len = static_cast<int>((seqlen - c < kT) ? seqlen - c : kT);
+    prep(c);
+    if constexpr (ANYV) {
+      wave_lds_sync();          // the previous chunk's reads of the slice are done
+      stage_bc();
+      wave_lds_sync();          // the slice is written before any lane reads it
+    }
+    const RawV<IO, kKP> z_cur = r_z;
+    if (c + kT < seqlen) {
+      fetch(c + kT);
+      if constexpr (ANYV) fetch_bc(c + kT);
+    }
+    if (len == kT) {
+      constexpr int AH = 2;
+      StepIn in[AH + 1];
+      load_in(std::integral_constant<int, 0>{}, in[0]);
+      load_in(std::integral_constant<int, 1>{}, in[1]);
+      static_for(std::make_integer_sequence<int, kT>{}, [&](auto TT) {
+        constexpr int t = decltype(TT)::value;
+        if constexpr (t + AH < kT) load_in(std::integral_constant<int, t + AH>{}, in[(t + AH) % (AH + 1)]);
+        step(TT, in[t % (AH + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+      static_for(std::make_integer_sequence<int, kT>{}, [&](auto TT) {
+        if (decltype(TT)::value < len) {
+          StepIn in1;
+          load_in(TT, in1);
+          step(TT, in1);
+        }
+      });
+    }
+    // the quad's partial Re(C.x) of this lane's timesteps
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < kKP; ++i) {
+      const float *yp = &s_yp[((own + i) * kCPW + cw_idx) * kLPC];
+      yv[i] = (yp[0] + yp[1]) + (yp[2] + yp[3]);
+    }
+    const int cnt = count(c);
+    if (cnt > 0 && valid) {
+      float o[kKP];
+#pragma unroll
+      for (int i = 0; i < kKP; ++i) {
+        float y = yv[i] + duv[i];
+        if (p.z) y *= silu_f(z_cur.get(i));
+        o[i] = y;
+      }
+      store_n<IO, kKP>(p.out, rbase + c + own, o, cnt, vec);
+    }
+  }
+
+  if (p.last && valid) {
+#pragma unroll
+    for (int k = 0; k < NSW; ++k)
+      if (s0 + k < n) {
+        p.last[(row * n + s0 + k) * 2] = xr[k];
+        p.last[(row * n + s0 + k) * 2 + 1] = xi[k];
+      }
+  }
+}
+
+using CplxFn = void (*)(const CplxParams);
+
+template <int IO, int NSW>
+CplxFn pick_bc(bool bv, bool cv) {
+  if (bv && cv) return scan_complex_kernel<IO, NSW, true, true>;
+  if (bv) return scan_complex_kernel<IO, NSW, true, false>;
+  if (cv) return scan_complex_kernel<IO, NSW, false, true>;
+  return scan_complex_kernel<IO, NSW, false, false>;
+}
+template <int IO>
+CplxFn pick_nsw(int nsw, bool bv, bool cv) {
+  if (nsw == 4) return pick_bc<IO, 4>(bv, cv);
+  if (nsw == 2) return pick_bc<IO, 2>(bv, cv);
+  return pick_bc<IO, 1>(bv, cv);
+}
+
+}  // namespace
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" int ssm_scan_fwd_complex(const ssm_scan_args_t *a, void *stream_ptr) {
+  const int st = ssm_scan_complex_validate(a);
+  if (st != SSM_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int n = static_cast<int>(a->dstate);
+  const int nsw = n > 8 ? 4 : n > 4 ? 2 : 1;   // four lanes per channel, 4*nsw >= n states
+  const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
+  CplxParams p{};
+  p.u = a->u; p.delta = a->delta; p.B = a->B; p.C = a->C; p.z = a->z;
+  p.A = a->A; p.D = a->D; p.dbias = a->delta_bias; p.init = a->initial_state;
+  p.out = a->out; p.last = a->last_state;
+  p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
+  p.n = n; p.ngroups = static_cast<int>(a->ngroups);
+  p.groups_eff = (bv || cv) ? p.ngroups : 1;
+  p.cpg = a->dim / p.groups_eff;
+  p.nblk = static_cast<int>((p.cpg + kCPW - 1) / kCPW);
+  const int64_t nblocks = a->batch * p.groups_eff * p.nblk;
+  if (nblocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  p.nblocks = static_cast<int>(nblocks);
+  p.softplus = a->delta_softplus;
+  p.vec = (a->seqlen % 8 == 0) && aligned16(a->u) && aligned16(a->delta) && aligned16(a->out) &&
+          (!a->z || aligned16(a->z)) && (!bv || aligned16(a->B)) && (!cv || aligned16(a->C));
+  p.xcd_swizzle = (p.nblocks % 8 == 0);
+  CplxFn f = a->io_dtype == SSM_BF16 ? pick_nsw<1>(nsw, bv, cv)
+           : a->io_dtype == SSM_F16  ? pick_nsw<2>(nsw, bv, cv)
+                                     : pick_nsw<0>(nsw, bv, cv);
+  hipLaunchKernelGGL(f, dim3(p.nblocks), dim3(64), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}

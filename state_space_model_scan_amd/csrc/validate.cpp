@@ -51,6 +51,19 @@ extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
   return SSM_OK;
 }
 
+// selective_scan_fn with complex A (guide section 4.1): the checks of the
+// real scan, with B/C holding (real, imaginary) pairs; no conv prologue and
+// no checkpoints.
+extern "C" int ssm_scan_complex_validate(const ssm_scan_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  if (!product_fits(a->batch, 2 * a->ngroups * a->dstate, a->seqlen)) return SSM_ERR_SHAPE;
+  if (a->conv_weight || a->checkpoints) return SSM_ERR_UNSUPPORTED;
+  if (!a->u) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
 extern "C" int causal_conv1d_ex_validate(const causal_conv1d_args_t *a) {
   if (!a) return SSM_ERR_NULL;
   const int st = causal_conv1d_validate(a->x, a->weight, a->out, a->batch, a->dim, a->seqlen, a->width,

@@ -250,6 +250,77 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray
     return t
 
 
+@dataclasses.dataclass(frozen=True)
+class ComplexWorkload:
+    """The selective scan with complex A (the page's section 4.1: A may be real
+    or complex): u, delta, z (batch, dim, seqlen) real; A (dim, dstate, 2)
+    float32 (real, imaginary) pairs; B, C complex io pairs, fixed
+    (dim, dstate, 2) or varying (batch, ngroups, dstate, seqlen, 2)."""
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    io_dtype: int
+    bc_kind: str = "varying"     # "varying" or "fixed" (both B and C)
+    ngroups: int = 1
+    has_z: bool = True
+    has_D: bool = True
+    has_bias: bool = True
+    softplus: bool = True
+    delta_mean: float = -2.0
+    delta_std: float = 0.5
+    A_imag: str = "lin"          # "lin": Im A[d, s] = pi * s;  "normal": Im A ~ N(0, 3)
+    init_state: bool = False
+    seed: int = 0
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+    def scaled(self, **kw) -> "ComplexWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# mamba2p8b_complex: the Mamba-2.8B-shaped layer of mamba2p8b (b=8, d=5120,
+# l=2048, n=16, g=4, bf16) with complex A, B and C.
+COMPLEX_WORKLOADS: Dict[str, ComplexWorkload] = {
+    "complex_tiny": ComplexWorkload("complex_tiny", 2, 24, 100, 16, F32, ngroups=2, init_state=True,
+                                    seed=30),
+    "mamba2p8b_complex": ComplexWorkload("mamba2p8b_complex", 8, 5120, 2048, 16, BF16, ngroups=4,
+                                         seed=32),
+}
+
+
+def make_complex_inputs(w: ComplexWorkload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw every tensor of complex-A workload ``w``, in this order: u,
+    delta (N(delta_mean, delta_std)), z, B, C (each component N(0, 1)), D,
+    delta_bias (U(-0.1, 0.1)), Re A = -exp(N(0, 0.5)), Im A (pi * s, or
+    N(0, 3) drawn here), initial state (batch, dim, dstate, 2) N(0, 1) when
+    the workload has one.  Same storage rules as ``make_inputs``."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    b, d, l, n, g = w.batch, w.dim, w.seqlen, w.dstate, w.ngroups
+    io = w.io_dtype
+    t: Dict[str, Optional[np.ndarray]] = {}
+    t["u"] = _store(_normal(rng, (b, d, l)), io)
+    t["delta"] = _store(_normal(rng, (b, d, l), w.delta_mean, w.delta_std), io)
+    t["z"] = _store(_normal(rng, (b, d, l)), io) if w.has_z else None
+    bc_shape = (d, n, 2) if w.bc_kind == "fixed" else (b, g, n, l, 2)
+    t["B"] = _store(_normal(rng, bc_shape), io)
+    t["C"] = _store(_normal(rng, bc_shape), io)
+    t["D"] = _normal(rng, (d,)) if w.has_D else None
+    t["delta_bias"] = _uniform(rng, (d,), -0.1, 0.1) if w.has_bias else None
+    A = np.empty((d, n, 2), dtype=np.float32)
+    A[..., 0] = (-np.exp(_normal(rng, (d, n), 0.0, 0.5).astype(np.float64))).astype(np.float32)
+    if w.A_imag == "normal":
+        A[..., 1] = _normal(rng, (d, n), 0.0, 3.0)
+    else:
+        A[..., 1] = (np.pi * np.arange(n, dtype=np.float64)).astype(np.float32)
+    t["A"] = A
+    t["initial_state"] = _normal(rng, (b, d, n, 2)) if w.init_state else None
+    return t
+
+
 def make_dout(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     """The output gradient of the backward: N(0, 1) of shape (batch, dim,
     seqlen) in the io dtype, from its own stream (seed + 1000)."""

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 7
+    assert L.ssm_abi_version() == 8
 
 
 def test_status_strings():
@@ -347,3 +347,35 @@ def test_fp16_io_is_taken_by_all_but_the_mamba2_scan():
     assert L.causal_conv1d_ex_validate(ctypes.byref(_good_conv(io_dtype=_lib.SSM_F16))) == _lib.SSM_OK
     assert L.ssm_scan_bwd_validate(ctypes.byref(_good_bwd(io_dtype=_lib.SSM_F16))) == _lib.SSM_OK
     assert L.ssd_scan_validate(ctypes.byref(_good_ssd(io_dtype=_lib.SSM_F16))) == _lib.SSM_ERR_UNSUPPORTED
+
+
+def test_complex_validation():
+    """ssm_scan_fwd_complex: the real scan's checks, plus no conv prologue,
+    no checkpoints and a required u; rejected before any HIP call."""
+    L = _lib.lib()
+    v = lambda a: L.ssm_scan_complex_validate(ctypes.byref(a))  # noqa: E731
+    assert v(_good_args()) == _lib.SSM_OK
+    assert v(_good_args(io_dtype=_lib.SSM_F16, dstate=3, B_kind=_lib.SSM_BC_FIXED)) == _lib.SSM_OK
+    assert v(_good_args(u=None)) == _lib.SSM_ERR_NULL
+    assert v(_good_args(A=None)) == _lib.SSM_ERR_NULL
+    assert v(_good_args(ngroups=3)) == _lib.SSM_ERR_SHAPE
+    assert v(_good_args(dstate=17)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_args(conv_weight=FAKE, conv_x=FAKE, conv_width=4)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_args(checkpoints=FAKE)) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssm_scan_complex_validate(None) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_fwd_complex(ctypes.byref(_good_args(delta=None)), None) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_fwd_complex(ctypes.byref(_good_args(checkpoints=FAKE)), None) == _lib.SSM_ERR_UNSUPPORTED
+
+
+def test_complex_binding_errors():
+    import torch
+    from state_space_model_scan_amd import binding
+    u = torch.zeros(1, 4, 8)
+    A = torch.zeros(4, 2, dtype=torch.complex64)
+    Bv = torch.zeros(1, 2, 8, dtype=torch.complex64)
+    with pytest.raises(ValueError, match="pair"):
+        binding.ssm_scan_fwd_complex(u, u, A, torch.zeros(1, 2, 8, 3), Bv)
+    with pytest.raises(ValueError, match="A must be"):
+        binding.ssm_scan_fwd_complex(u, u, torch.zeros(4, 2), Bv, Bv)
+    with pytest.raises(ValueError, match="io dtype"):
+        binding.ssm_scan_fwd_complex(u, u, A, torch.zeros(1, 2, 8, 2, dtype=torch.bfloat16), Bv)
