@@ -237,9 +237,12 @@ scan_kernel(const ScanParams p) {
 #pragma unroll
   for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
 
-  // CSc: silu after the conv (a compile-time constant, chosen once per chunk)
-  auto prep = [&](int64_t c, auto CSc) {
+  // CSc: silu after the conv; FCc: a whole chunk, so no lane owns timesteps
+  // past the end and none needs masking (compile-time constants, chosen once
+  // per chunk)
+  auto prep = [&](int64_t c, auto CSc, auto FCc) {
     constexpr bool CS = decltype(CSc)::value;
+    constexpr bool FC = decltype(FCc)::value;
     float uu[kKP];
     if constexpr (CONV) {
       float xv[kKP + 3];
@@ -265,7 +268,7 @@ scan_kernel(const ScanParams p) {
     for (int i = 0; i < kKP; ++i) {
       float dt = r_dl.get(i) + bias;
       if (p.softplus) dt = softplus_f(dt);
-      if (i >= cnt) dt = 0.0f;
+      if (!FC && i >= cnt) dt = 0.0f;
       dtv[i] = dt;
       dtuv[i] = dt * uu[i];
       duv[i] = Dd * uu[i];
@@ -351,6 +354,7 @@ scan_kernel(const ScanParams p) {
 
   for (int64_t c = t_begin; c < t_end; c += T) {
     const int len = static_cast<int>((t_end - c < T) ? t_end - c : T);
+    const bool csilu = CONV && p.conv_silu;
     if constexpr (FULL) {
       // the state before timestep c, every SSM_CKPT_INTERVAL timesteps
       if (p.ckpt && valid && (c % SSM_CKPT_INTERVAL) == 0) {
@@ -360,7 +364,11 @@ scan_kernel(const ScanParams p) {
           if (s0 + k < n) dst[s0 + k] = x[k];
       }
     }
-    if (CONV && p.conv_silu) prep(c, std::true_type{}); else prep(c, std::false_type{});
+    if (len == T) {
+      if (csilu) prep(c, std::true_type{}, std::true_type{}); else prep(c, std::false_type{}, std::true_type{});
+    } else {
+      if (csilu) prep(c, std::true_type{}, std::false_type{}); else prep(c, std::false_type{}, std::false_type{});
+    }
     if constexpr (ANYV) {
       wave_lds_sync();          // the previous chunk's reads of the slice are done
       stage_bc();
