@@ -16,10 +16,11 @@
 //     timesteps [8q, 8q+8) of each chunk: it loads them as one vector per
 //     input, computes delta' = softplus(delta + bias), delta'*u and D*u in
 //     registers, and after the chunk gates and stores its 8 outputs;
-//   * per timestep the owner's delta' and delta'*u reach the other lanes of
-//     the quad by one DPP quad broadcast each; every lane writes its partial
-//     C.x to the wave's LDS slice, and after the chunk the owner sums the LPC
-//     partials of its timesteps;
+//   * the owner writes delta' and delta'*u of its timesteps to the wave's LDS
+//     slice once per chunk, and every lane of the channel reads them four
+//     timesteps at a time (one 16-byte read each; cross-lane DPP moves per
+//     timestep cost more); every lane writes its partial C.x to the slice,
+//     and after the chunk the owner sums the LPC partials of its timesteps;
 //   * time-varying B/C are the same for every channel of a wave: the wave
 //     stages the chunk's B/C tile (all states) in its own LDS slice, and lane
 //     q reads its NSW states of timestep t with one LDS vector load each, two
@@ -103,8 +104,18 @@ scan_kernel(const ScanParams p) {
 
   __shared__ float s_bc[ANYV ? kWavesPerBlock : 1][ANYV ? 2 : 1][ANYV ? T : 1][ANYV ? NP : 1];
   constexpr bool XCH = LPC > 1;          // lanes of a channel exchange data
-  // partial C.x of every (timestep, channel, lane) of the chunk
-  __shared__ float s_yp[(XCH && FULL) ? T * CPW * LPC : 1];
+  // partial C.x of every (timestep, channel, lane) of the chunk; the row of
+  // timestep t starts at t*CPW*LPC + 8*(t/8), so the owner's reads of its
+  // timesteps (rows 8 apart) spread over the banks
+  constexpr int YROW_SKEW = 8;
+  __shared__ __attribute__((aligned(16))) float s_yp[(XCH && FULL) ? T * CPW * LPC + YROW_SKEW * (T / 8) : 4];
+  auto yrow = [](int t) { return t * CPW * LPC + YROW_SKEW * (t / 8); };
+  // delta' and delta'*u of timestep group g (timesteps 4g..4g+3) as
+  // [channel][4] each.  In the full pass they sit in the C.x rows of the
+  // group's first timesteps: every lane reads a group before the step that
+  // first overwrites those rows (LDS operations of a wave complete in order).
+  __shared__ __attribute__((aligned(16))) float s_dd[(XCH && !FULL) ? T * CPW * 2 : 4];
+  auto dd_at = [&](int g) -> float * { return FULL ? &s_yp[yrow(4 * g)] : &s_dd[g * 2 * CPW * 4]; };
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -279,7 +290,7 @@ scan_kernel(const ScanParams p) {
       wave_lds_sync();
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
-        const float *yp = &s_yp[((own + i) * CPW + cw_idx) * LPC];
+        const float *yp = &s_yp[yrow(own + i) + cw_idx * LPC];
         float y = yp[0];
 #pragma unroll
         for (int k = 1; k < LPC; ++k) y += yp[k];
@@ -308,11 +319,18 @@ scan_kernel(const ScanParams p) {
   struct StepIn {
     float dt, dtu, Bv[NSW], Cv[NSW];
   };
+  float4 dtq[2], dtuq[2];   // delta' and delta'*u of the current and next group of 4 timesteps
   auto load_in = [&](auto TT, StepIn &in) {
     constexpr int t = decltype(TT)::value;
     if constexpr (XCH) {
-      in.dt = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtv[t % kKP]);
-      in.dtu = dpp_bcast_reg<quad_bcast_ctrl<LPC, t / kKP>()>(dtuv[t % kKP]);
+      constexpr int gb = (t / 4) % 2;
+      if constexpr (t % 4 == 0) {
+        dtq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + cw_idx * 4);
+        dtuq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + CPW * 4 + cw_idx * 4);
+      }
+      constexpr int e = t % 4;
+      in.dt = e == 0 ? dtq[gb].x : e == 1 ? dtq[gb].y : e == 2 ? dtq[gb].z : dtq[gb].w;
+      in.dtu = e == 0 ? dtuq[gb].x : e == 1 ? dtuq[gb].y : e == 2 ? dtuq[gb].z : dtuq[gb].w;
     } else {
       in.dt = dtv[t % kKP];
       in.dtu = dtuv[t % kKP];
@@ -344,7 +362,7 @@ scan_kernel(const ScanParams p) {
       float y = in.Cv[0] * x[0];
 #pragma unroll
       for (int k = 1; k < NSW; ++k) y = fmaf(in.Cv[k], x[k], y);
-      if constexpr (XCH) s_yp[(t * CPW + cw_idx) * LPC + q] = y;
+      if constexpr (XCH) s_yp[yrow(t) + cw_idx * LPC + q] = y;
       else yv[t % kKP] = y;
     }
   };
@@ -368,6 +386,19 @@ scan_kernel(const ScanParams p) {
       if (csilu) prep(c, std::true_type{}, std::true_type{}); else prep(c, std::false_type{}, std::true_type{});
     } else {
       if (csilu) prep(c, std::true_type{}, std::false_type{}); else prep(c, std::false_type{}, std::false_type{});
+    }
+    if constexpr (XCH) {
+      // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
+      // reads of the slice are issued before these stores
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float *dp = dd_at((own >> 2) + j);
+        *reinterpret_cast<float4 *>(dp + cw_idx * 4) = make_float4(dtv[4 * j], dtv[4 * j + 1], dtv[4 * j + 2], dtv[4 * j + 3]);
+        *reinterpret_cast<float4 *>(dp + CPW * 4 + cw_idx * 4) =
+            make_float4(dtuv[4 * j], dtuv[4 * j + 1], dtuv[4 * j + 2], dtuv[4 * j + 3]);
+      }
+      if constexpr (!ANYV) wave_lds_sync();   // with B/C staging the sync below covers these
     }
     if constexpr (ANYV) {
       wave_lds_sync();          // the previous chunk's reads of the slice are done
