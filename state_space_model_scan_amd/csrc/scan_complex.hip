@@ -21,10 +21,11 @@
 // channel, lane q holding complex states [q*NSW, (q+1)*NSW) in VGPRs; chunks
 // of 32 timesteps, lane q owning timesteps [8q, 8q+8) of each chunk for the
 // loads, delta' = softplus(delta + bias), delta'*u and the gated store;
-// delta' and delta'*u reach the quad by DPP broadcasts; time-varying B/C of a
-// chunk are staged in the wave's LDS slice (complex pairs interleaved, as in
-// memory) and read two timesteps ahead; each lane's partial Re(C.x) goes to
-// LDS and the owner sums the quad's partials.  The whole sequence is walked
+// delta' and delta'*u reach the quad through LDS (stored by the owner once per
+// chunk in the partial-sum rows, read four timesteps at a time); time-varying
+// B/C of a chunk are staged in the wave's LDS slice (complex pairs
+// interleaved, as in memory) and read two timesteps ahead; each lane's
+// partial Re(C.x) goes to LDS and the owner sums the quad's partials.  The whole sequence is walked
 // in one pass (no sequence split).
 #include <hip/hip_runtime.h>
 
@@ -70,8 +71,12 @@ scan_complex_kernel(const CplxParams p) {
 
   // [B or C][timestep][state][re, im]
   __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kT : 1][ANYV ? NP : 1][2];
-  // partial Re(C.x) of every (timestep, channel, lane) of the chunk
-  __shared__ float s_yp[kT * kCPW * kLPC];
+  // partial Re(C.x) of every (timestep, channel, lane) of the chunk.  At the
+  // chunk's start the rows of timesteps 4g and 4g+1 hold delta' and delta'*u
+  // of timesteps 4g..4g+3 as [channel][4] each: every lane reads them before
+  // step 4g overwrites those rows (a wave's LDS operations complete in order).
+  __shared__ __attribute__((aligned(16))) float s_yp[kT * kCPW * kLPC];
+  auto dd_at = [&](int g) -> float * { return &s_yp[4 * g * kCPW * kLPC]; };
 
   const int lane = threadIdx.x & 63;
   const int q = lane % kLPC;
@@ -186,10 +191,17 @@ scan_complex_kernel(const CplxParams p) {
   struct StepIn {
     float dt, dtu, Br[NSW], Bi[NSW], Cr[NSW], Ci[NSW];
   };
+  float4 dtq[2], dtuq[2];   // delta' and delta'*u of the current and next group of 4 timesteps
   auto load_in = [&](auto TT, StepIn &in) {
     constexpr int t = decltype(TT)::value;
-    in.dt = dpp_bcast_reg<quad_bcast_ctrl<kLPC, t / kKP>()>(dtv[t % kKP]);
-    in.dtu = dpp_bcast_reg<quad_bcast_ctrl<kLPC, t / kKP>()>(dtuv[t % kKP]);
+    constexpr int gb = (t / 4) % 2;
+    if constexpr (t % 4 == 0) {
+      dtq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + cw_idx * 4);
+      dtuq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + kCPW * 4 + cw_idx * 4);
+    }
+    constexpr int e = t % 4;
+    in.dt = e == 0 ? dtq[gb].x : e == 1 ? dtq[gb].y : e == 2 ? dtq[gb].z : dtq[gb].w;
+    in.dtu = e == 0 ? dtuq[gb].x : e == 1 ? dtuq[gb].y : e == 2 ? dtuq[gb].z : dtuq[gb].w;
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
       if constexpr (BV) { in.Br[k] = s_bc[0][t][s0 + k][0]; in.Bi[k] = s_bc[0][t][s0 + k][1]; }
@@ -224,11 +236,18 @@ scan_complex_kernel(const CplxParams p) {
   for (int64_t c = 0; c < seqlen; c += kT) {
     const int len = static_cast<int>((seqlen - c < kT) ? seqlen - c : kT);
     prep(c);
-    if constexpr (ANYV) {
-      wave_lds_sync();          // the previous chunk's reads of the slice are done
-      stage_bc();
-      wave_lds_sync();          // the slice is written before any lane reads it
+    // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
+    // reads of the rows are issued before these stores
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float *dp = dd_at((own >> 2) + j);
+      *reinterpret_cast<float4 *>(dp + cw_idx * 4) = make_float4(dtv[4 * j], dtv[4 * j + 1], dtv[4 * j + 2], dtv[4 * j + 3]);
+      *reinterpret_cast<float4 *>(dp + kCPW * 4 + cw_idx * 4) =
+          make_float4(dtuv[4 * j], dtuv[4 * j + 1], dtuv[4 * j + 2], dtuv[4 * j + 3]);
     }
+    if constexpr (ANYV) stage_bc();
+    wave_lds_sync();            // the slice is written before any lane reads it
     const RawV<IO, kKP> z_cur = r_z;
     if (c + kT < seqlen) {
       fetch(c + kT);
