@@ -133,6 +133,17 @@ def decode_conv_update_bytes(w) -> int:
             + w.dim * w.conv_width * 4 + w.dim * 4)
 
 
+def inputs_digest(t) -> str:
+    """SHA-256 over every input tensor's bytes, in name order (absent ones
+    skipped): names the exact synthetic inputs the line was measured on."""
+    h = hashlib.sha256()
+    for k in sorted(t):
+        if t[k] is not None:
+            h.update(k.encode())
+            h.update(np.ascontiguousarray(t[k]).view(np.uint8))
+    return h.hexdigest()
+
+
 def cpu_baseline(w, t, budget_s: float):
     """Oracle throughput on a bounded sample of rows (all host threads)."""
     from oracle import oracle as orc
@@ -157,7 +168,13 @@ def cpu_baseline(w, t, budget_s: float):
     t0 = time.perf_counter()
     run_oracle(w, t, rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
+    # one thread on a slice of the same rows, as a per-core figure
+    one = rows[: max(1, min(len(rows), int(len(rows) * 2.0 / max(dt * threads, 1e-9))))]
+    t1 = time.perf_counter()
+    run_oracle(w, t, rows=one, nthreads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": nrows * w.seqlen / dt, "unit": "elements/s", "cores": threads,
+            "single_thread_value": len(one) * w.seqlen / dt1,
             "kind": "oracle",
             "sample": f"{nrows} of {total_rows} (b,d) rows x full seqlen {w.seqlen}, "
                       f"{dt:.1f} s float64 on {threads} threads"}
@@ -243,6 +260,20 @@ def main():
     elems = w.elements
     value = elems * args.steps / wall
 
+    # the same launches with the caches evicted before each (a 512 MiB write
+    # outside the timed pair): the launch time from cold L2 and last-level cache
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold_ms = []
+    for i in range(min(args.steps, 20)):
+        evict.fill_(i & 0xff)
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record(stream)
+        step()
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(s_ev.elapsed_time(e_ev))
+    del evict
+
     abytes = algorithmic_bytes(w)
     aops = algorithmic_alu_ops(w)
     alu_tops = aops / avg_launch_s / 1e12
@@ -267,6 +298,7 @@ def main():
                         f"{', conv prologue' if w.conv else ''}{', z gate' if w.has_z else ''}",
             "io_dtype": "bf16" if io == BF16 else "fp32",
             "elements_per_step": elems,
+            "inputs_sha256": inputs_digest(t),
         },
         "roofline": {
             "bound": "alu",
@@ -278,6 +310,7 @@ def main():
             "kernel_avg_ms": avg_launch_s * 1e3,
             "kernel_median_ms": float(np.median(launch_ms)),
             "kernel_min_ms": float(np.min(launch_ms)),
+            "kernel_avg_ms_cold_caches": float(np.mean(cold_ms)),
             "hbm": {"achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
                     "algorithmic_bytes": abytes},
         },
