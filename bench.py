@@ -28,7 +28,17 @@ profiles/traffic_<workload>.json when that file was taken from the current
 kernel source, else null.
 
 cpu_baseline: the float64 oracle (test infrastructure) timed on this host's
-cores over a bounded sample of the workload's rows, scaled to elements/s.
+cores over a bounded sample of the workload's rows, scaled to elements/s,
+with a single-thread figure on a slice of those rows beside it.  After the
+timed steps, 20 more launches each follow a 512 MiB write that evicts the
+caches (outside their timed pair): roofline.kernel_avg_ms_cold_caches.
+config.inputs_sha256 digests every input tensor.
+
+Complex-A workloads (--workload mamba2p8b_complex): a step is one
+ssm_scan_fwd_complex call (complex A, B and C; real u, delta, z, out).  The
+value is elements/s; the roofline is ALU with 25 weighted ops per (timestep,
+state) -- 13 plain ops and exp2, sine and cosine weighted 4 -- plus the 26 per
+element of the real scan, and the HBM rate beside it.
 
 Decode workloads (--workload decode2p8b): a step is one decode step of one
 layer, causal_conv1d_update (one new token against the conv cache) then
