@@ -80,6 +80,9 @@ EDGE = {
     "segmented_f32": _case(dstate=16, dim=64, seqlen=3000, delta_mean=-4.0),
     "segmented_bf16_ragged": _case(io_dtype=BF16, dstate=16, dim=72, seqlen=2999),
     "segmented_conv": _case(conv=True, io_dtype=BF16, dstate=16, dim=64, seqlen=1500),
+    # the segmented plan with two lanes per channel (dstate <= 8)
+    "segmented_n8_bf16": _case(io_dtype=BF16, dstate=8, dim=64, seqlen=2500),
+    "segmented_n5_fixed": _case(bc_kind="fixed", dstate=5, dim=40, seqlen=2100, delta_mean=-4.0),
 }
 
 
