@@ -306,17 +306,17 @@ scan_complex_kernel(const CplxParams p) {
 using CplxFn = void (*)(const CplxParams);
 
 template <int IO, int NSW>
-CplxFn pick_bc(bool bv, bool cv) {
+CplxFn pick_cplx_bc(bool bv, bool cv) {
   if (bv && cv) return scan_complex_kernel<IO, NSW, true, true>;
   if (bv) return scan_complex_kernel<IO, NSW, true, false>;
   if (cv) return scan_complex_kernel<IO, NSW, false, true>;
   return scan_complex_kernel<IO, NSW, false, false>;
 }
 template <int IO>
-CplxFn pick_nsw(int nsw, bool bv, bool cv) {
-  if (nsw == 4) return pick_bc<IO, 4>(bv, cv);
-  if (nsw == 2) return pick_bc<IO, 2>(bv, cv);
-  return pick_bc<IO, 1>(bv, cv);
+CplxFn pick_cplx(int nsw, bool bv, bool cv) {
+  if (nsw == 4) return pick_cplx_bc<IO, 4>(bv, cv);
+  if (nsw == 2) return pick_cplx_bc<IO, 2>(bv, cv);
+  return pick_cplx_bc<IO, 1>(bv, cv);
 }
 
 }  // namespace
@@ -347,9 +347,9 @@ extern "C" int ssm_scan_fwd_complex(const ssm_scan_args_t *a, void *stream_ptr) 
   p.vec = (a->seqlen % 8 == 0) && aligned16(a->u) && aligned16(a->delta) && aligned16(a->out) &&
           (!a->z || aligned16(a->z)) && (!bv || aligned16(a->B)) && (!cv || aligned16(a->C));
   p.xcd_swizzle = (p.nblocks % 8 == 0);
-  CplxFn f = a->io_dtype == SSM_BF16 ? pick_nsw<1>(nsw, bv, cv)
-           : a->io_dtype == SSM_F16  ? pick_nsw<2>(nsw, bv, cv)
-                                     : pick_nsw<0>(nsw, bv, cv);
+  CplxFn f = a->io_dtype == SSM_BF16 ? pick_cplx<1>(nsw, bv, cv)
+           : a->io_dtype == SSM_F16  ? pick_cplx<2>(nsw, bv, cv)
+                                     : pick_cplx<0>(nsw, bv, cv);
   hipLaunchKernelGGL(f, dim3(p.nblocks), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
