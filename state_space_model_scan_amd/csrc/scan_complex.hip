@@ -174,14 +174,16 @@ scan_complex_kernel(const CplxParams p) {
 #pragma unroll
   for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
 
-  auto prep = [&](int64_t c) {
+  // FCc: a whole chunk, so no lane owns timesteps past the end
+  auto prep = [&](int64_t c, auto FCc) {
+    constexpr bool FC = decltype(FCc)::value;
     const int cnt = count(c);
 #pragma unroll
     for (int i = 0; i < kKP; ++i) {
       const float uu = r_u.get(i);
       float dt = r_dl.get(i) + bias;
       if (p.softplus) dt = softplus_f(dt);
-      if (i >= cnt) dt = 0.0f;
+      if (!FC && i >= cnt) dt = 0.0f;
       dtv[i] = dt;
       dtuv[i] = dt * uu;
       duv[i] = Dd * uu;
@@ -235,7 +237,7 @@ scan_complex_kernel(const CplxParams p) {
 
   for (int64_t c = 0; c < seqlen; c += kT) {
     const int len = static_cast<int>((seqlen - c < kT) ? seqlen - c : kT);
-    prep(c);
+    if (len == kT) prep(c, std::true_type{}); else prep(c, std::false_type{});
     // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
     // reads of the rows are issued before these stores
     wave_lds_sync();

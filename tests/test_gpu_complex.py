@@ -70,6 +70,8 @@ CASES = [
     (2, 16, 256, 1, 1, BF16, "fixed", "lin", dict(has_bias=False, softplus=False, delta_mean=0.1,
                                                   delta_std=0.02)),
     (1, 64, 512, 16, 4, F32, "varying", "normal", dict(init_state=True, delta_mean=-4.0)),
+    (2, 256, 1024, 16, 2, F16, "varying", "lin", {}),
+    (4, 96, 777, 12, 1, BF16, "fixed", "normal", dict(init_state=True)),
 ]
 
 
