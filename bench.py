@@ -34,6 +34,10 @@ timed steps, 20 more launches each follow a 512 MiB write that evicts the
 caches (outside their timed pair): roofline.kernel_avg_ms_cold_caches.
 config.inputs_sha256 digests every input tensor.
 
+Standalone conv (--conv): a step is one causal_conv1d_fwd (width 4, silu) on
+the conv workload's input; the roofline is HBM (x read and out written once,
+plus the weights).
+
 Complex-A workloads (--workload mamba2p8b_complex): a step is one
 ssm_scan_fwd_complex call (complex A, B and C; real u, delta, z, out).  The
 value is elements/s; the roofline is ALU with 25 weighted ops per (timestep,
@@ -86,6 +90,7 @@ DECODE_SRCS = ("decode.hip", "device_util.h")
 SSD_SRCS = ("ssd.hip", "device_util.h")
 BWD_SRCS = ("bwd.hip", "device_util.h")
 COMPLEX_SRCS = ("scan_complex.hip", "scan_kernel.h", "device_util.h")
+CONV_SRCS = ("ssm_scan.hip", "device_util.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -200,6 +205,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 512 MiB device copy (for rocprofv3 counter scaling)")
+    ap.add_argument("--conv", action="store_true",
+                    help="time the standalone causal_conv1d_fwd on the conv workload's input")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (all gradients) on the selective-scan workload")
     args = ap.parse_args()
@@ -218,6 +225,8 @@ def main():
         return ssd_main(args)
     if args.backward:
         return bwd_main(args)
+    if args.conv:
+        return conv_main(args)
     from state_space_model_scan_amd.inputs import COMPLEX_WORKLOADS
     if args.workload in COMPLEX_WORKLOADS:
         return complex_main(args)
@@ -465,6 +474,73 @@ def complex_cpu_baseline(w, t, budget_s: float):
     return {"value": nrows * w.seqlen / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{nrows} of {total_rows} (b,d) rows x full seqlen {w.seqlen}, "
                       f"{dt:.1f} s float64 complex scan on {threads} threads"}
+
+
+def conv_main(args):
+    """One standalone causal_conv1d_fwd per timed step (width 4, silu) on the
+    conv input of the workload (convfixed by default: b=16 d=2048 l=4096
+    bf16).  HBM-bound: x read once and out written once, plus the weights."""
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, F16, WORKLOADS, make_inputs
+
+    _lib.lib()
+    name = args.workload if args.workload != "mamba2p8b" else "convfixed"
+    w = WORKLOADS[name]
+    if not w.conv:
+        raise SystemExit(f"--conv needs a workload with the conv prologue, not {name}")
+    t = make_inputs(w)
+    io = w.io_dtype
+    x = torch.from_numpy(t["conv_x"])
+    if io in (BF16, F16):
+        x = x.view(torch.bfloat16 if io == BF16 else torch.float16)
+    x = x.cuda()
+    wt = torch.from_numpy(t["conv_weight"]).cuda()
+    bias = torch.from_numpy(t["conv_bias"]).cuda()
+    out = torch.empty_like(x)
+
+    def step():
+        binding.causal_conv1d_fwd(x, wt, bias, out=out, act=_lib.SSM_ACT_SILU)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+    avg_s = float(np.mean(launch_ms)) / 1e3
+    es = 2 if io in (BF16, F16) else 4
+    abytes = 2 * w.elements * es + w.dim * 4 * 4 + w.dim * 4
+    gbs = abytes / avg_s / 1e9
+    rec = {
+        "metric": METRIC, "value": w.elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"causal_conv1d_fwd on {w.name}'s input: b={w.batch} d={w.dim} l={w.seqlen} "
+                               f"width 4, silu, {'bf16' if io == BF16 else 'fp16' if io == F16 else 'fp32'} io",
+                   "elements_per_step": w.elements},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(f"conv_{w.name}", CONV_SRCS),
+                     "kernel": "conv_kernel",
+                     "kernel_avg_ms": avg_s * 1e3, "kernel_median_ms": float(np.median(launch_ms)),
+                     "algorithmic_bytes": abytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def decode_main(args):
