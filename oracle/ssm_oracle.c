@@ -25,7 +25,8 @@
  *   - same page, section 4.2 (causal_conv1d): depthwise weight (dim,width),
  *     optional bias (dim,), activation None / silu / swish.
  *   - The recurrence itself is not printed on the pages.  The reading used is
- *     the standard zero-order-hold discretisation named by the benchmark spec:
+ *     the standard zero-order-hold discretisation (exp on A, an Euler step on
+ *     B):
  *       dA = exp(delta'*A),  x_t = dA*x_{t-1} + delta'*B_t*u_t,  x_{-1} = 0,
  *       y_t = C_t . x_t,  out = (y + D*u) * silu(z).
  *
