@@ -175,3 +175,25 @@ def test_complex_full_size_sampled_rows():
     ref = _oracle(w, t, rows=rows)
     e, el = _check(w, (o[rows], ls[rows]), ref, w.name)
     log(f"  max normalised error out {e:.2e} last_state {el:.2e}")
+
+
+def test_complex_misaligned_pointers():
+    """Every io tensor one element off 16-byte alignment at a sequence length
+    divisible by 8: the element-wise loads and stores."""
+    import torch
+    from state_space_model_scan_amd import binding
+    from tests.test_gpu_parity import _offset_view
+    w = BASE.scaled(batch=2, dim=24, seqlen=128, dstate=8, io_dtype=BF16, seed=355)
+    t = make_complex_inputs(w)
+    log("complex misaligned")
+    ov = lambda k: _offset_view(t[k], w.io_dtype)  # noqa: E731
+    out = _offset_view(np.zeros(t["delta"].shape, dtype=t["delta"].dtype), w.io_dtype)
+    last = torch.empty((w.batch, w.dim, w.dstate, 2), dtype=torch.float32, device="cuda")
+    binding.ssm_scan_fwd_complex(ov("u"), ov("delta"), to_dev(t["A"], param=True), ov("B"), ov("C"),
+                                 to_dev(t["D"], param=True), ov("z"), to_dev(t["delta_bias"], param=True), True,
+                                 out=out, last_state=last,
+                                 initial_state=to_dev(t["initial_state"], param=True))
+    torch.cuda.synchronize()
+    got = (out.float().cpu().numpy().astype(np.float64).reshape(-1, w.seqlen),
+           last.cpu().numpy().astype(np.float64).reshape(-1, w.dstate, 2))
+    _check(w, got, _oracle(w, t), "complex misaligned")

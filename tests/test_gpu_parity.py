@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 from state_space_model_scan_amd.inputs import BF16, F32, WORKLOADS, make_inputs, sample_rows
-from tests.harness import check, log, run_gpu, run_oracle
+from oracle import oracle as orc
+from tests.harness import TOL, check, log, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -233,3 +234,49 @@ def test_degenerate_cases(kind):
     out, last = run_gpu(w, t, init=init)
     ref, ref_last = run_oracle(w, t, init=init)
     check(w, out, ref, last, ref_last, what=kind)
+
+
+def _offset_view(a, io_dtype):
+    """The array on the device as a view one element into a larger buffer:
+    same values, a base address no longer 16-byte aligned."""
+    import torch
+    from tests.harness import to_dev
+    flat = to_dev(np.ascontiguousarray(a).reshape(-1), io_dtype)
+    buf = torch.empty(flat.numel() + 1, dtype=flat.dtype, device="cuda")
+    buf[1:].copy_(flat)
+    return buf[1:].view(a.shape)
+
+
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_misaligned_pointers(io):
+    """Every io tensor one element off 16-byte alignment at a sequence length
+    divisible by 8: the kernels take their element-wise loads and stores."""
+    import torch
+    from state_space_model_scan_amd import binding
+    from tests.harness import to_dev
+    w = _case(io_dtype=io, dstate=16, dim=48, ngroups=2, seqlen=256, seed=77)
+    t = make_inputs(w)
+    log(f"[parity] misaligned io={io}")
+    ov = lambda k: _offset_view(t[k], io)  # noqa: E731
+    out = _offset_view(np.zeros(t["delta"].shape, dtype=t["delta"].dtype), io)
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device="cuda")
+    binding.ssm_scan_fwd(ov("u"), ov("delta"), to_dev(t["A"], param=True), ov("B"), ov("C"),
+                         to_dev(t["D"], param=True), ov("z"), to_dev(t["delta_bias"], param=True), True,
+                         out=out, last_state=last)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64).reshape(w.batch * w.dim, w.seqlen)
+    gl = last.cpu().numpy().astype(np.float64).reshape(w.batch * w.dim, w.dstate)
+    ref, ref_last = run_oracle(w, t)
+    check(w, got, ref, gl, ref_last, what=f"misaligned io={io}")
+    # the standalone conv on the same misaligned input
+    wc = _case(io_dtype=io, conv=True, dstate=16, dim=48, seqlen=256, seed=78)
+    tc = make_inputs(wc)
+    x = _offset_view(tc["conv_x"], io)
+    y = _offset_view(np.zeros(tc["conv_x"].shape, dtype=tc["conv_x"].dtype), io)
+    binding.causal_conv1d_fwd(x, to_dev(tc["conv_weight"], param=True), to_dev(tc["conv_bias"], param=True),
+                              out=y, act=orc.ACT_SILU)
+    torch.cuda.synchronize()
+    ref_c = orc.causal_conv1d(tc["conv_x"], tc["conv_weight"], tc["conv_bias"], orc.ACT_SILU, io_dtype=io)
+    yc = y.float().cpu().numpy().astype(np.float64).reshape(ref_c.shape)
+    err = float(np.max(np.abs(yc - ref_c) / (1.0 + np.abs(ref_c))))
+    assert err <= TOL[io], f"misaligned conv: {err:.3e}"
