@@ -148,6 +148,19 @@ def decode_conv_update_bytes(w) -> int:
             + w.dim * w.conv_width * 4 + w.dim * 4)
 
 
+def cpu_model() -> str:
+    """The host CPU's model string (Linux), or the platform's processor name."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def inputs_digest(t) -> str:
     """SHA-256 over every input tensor's bytes, in name order (absent ones
     skipped): names the exact synthetic inputs the line was measured on."""
@@ -190,6 +203,7 @@ def cpu_baseline(w, t, budget_s: float):
     dt1 = time.perf_counter() - t1
     return {"value": nrows * w.seqlen / dt, "unit": "elements/s", "cores": threads,
             "single_thread_value": len(one) * w.seqlen / dt1,
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{nrows} of {total_rows} (b,d) rows x full seqlen {w.seqlen}, "
                       f"{dt:.1f} s float64 on {threads} threads"}
