@@ -223,12 +223,16 @@ def main():
                     help="time the standalone causal_conv1d_fwd on the conv workload's input")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (all gradients) on the selective-scan workload")
+    ap.add_argument("--microbench", action="store_true",
+                    help="measure the VALU, transcendental, LDS and copy rates the ALU ceilings use")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the operator shards with no communication along batch and channels", file=sys.stderr)
         sys.exit(2)
 
+    if args.microbench:
+        return microbench_main(args)
     import torch
     from state_space_model_scan_amd import _lib, binding
     from state_space_model_scan_amd.inputs import BF16, DECODE_WORKLOADS, WORKLOADS, make_inputs
@@ -962,6 +966,91 @@ def bwd_cpu_baseline(w, t, dout, budget_s: float):
     return {"value": nch * w.seqlen / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": f"{nch} channels of batch 0 x full seqlen {w.seqlen} (backward), {dt:.1f} s float64 "
                       f"on 1 thread"}
+
+
+
+# ---------------------------------------------------------------------------
+# --microbench: the chip rates behind the ALU ceilings (include/ssmmicro.h)
+# ---------------------------------------------------------------------------
+
+# probe -> (kind, VALU wave-instructions per loop iteration, transcendental
+# wave-instructions per iteration, LDS bytes per iteration per wave)
+MB_PROBES = {
+    "fma": (0, 128, 0, 0),
+    "exp": (1, 0, 128, 0),
+    "mix": (2, 136, 32, 0),
+    "dpp": (3, 128, 0, 0),
+    "lds_read_b128_broadcast": (4, 0, 0, 16 * 64 * 16),
+    "lds_read_b128_linear": (5, 0, 0, 16 * 64 * 16),
+    "lds_write_b32": (6, 0, 0, 16 * 64 * 4),
+}
+NOMINAL_CLK_HZ = 2.4e9
+NUM_CU = 256
+
+
+def microbench_main(args):
+    """Instruction rates per compute unit and clock at k waves per SIMD, and
+    the device copy bandwidth.  Rates use the nominal 2.4 GHz clock; the
+    shader clock measured inside the probe (s_memtime against the 100 MHz
+    s_memrealtime) is reported beside them."""
+    import ctypes
+
+    import torch
+    from state_space_model_scan_amd import _build
+    lib = ctypes.CDLL(_build.MICRO_LIB)
+    lib.ssm_microbench.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+
+    def run(kind, blocks, iters, buf, reps=5):
+        rc = lib.ssm_microbench(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()),
+                                ctypes.c_void_p(clk.data_ptr()), sp)
+        if rc != 0:
+            raise RuntimeError(f"ssm_microbench({kind}) returned {rc}")
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            lib.ssm_microbench(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()),
+                               ctypes.c_void_p(clk.data_ptr()), sp)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        c = clk.cpu().tolist()
+        real = (c[3] - c[1]) / 100e6
+        shader_hz = (c[2] - c[0]) / real if real > 0 else None
+        return best / 1e3, shader_hz
+
+    res = {"nominal_clock_GHz": NOMINAL_CLK_HZ / 1e9, "compute_units": NUM_CU, "probes": {}}
+    for name, (kind, valu, trans, lds) in MB_PROBES.items():
+        rows = {}
+        for k in (1, 2, 3, 4, 8):
+            blocks = NUM_CU * k
+            iters = max(64, 2048 // k)
+            buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            t, hz = run(kind, blocks, iters, buf)
+            waves = blocks * 4
+            cu_clk = t * NUM_CU * NOMINAL_CLK_HZ
+            row = {"ms": t * 1e3, "shader_clock_GHz": None if hz is None else hz / 1e9}
+            if valu:
+                row["valu_per_cu_clk"] = waves * iters * valu / cu_clk
+            if trans:
+                row["trans_per_cu_clk"] = waves * iters * trans / cu_clk
+            if lds:
+                row["lds_bytes_per_cu_clk"] = waves * iters * lds / cu_clk
+            rows[f"{k}_waves_per_simd"] = row
+        res["probes"][name] = rows
+    # device copy: 1 GiB read + 1 GiB written
+    blocks, iters = NUM_CU * 8, 128
+    nbytes = blocks * 256 * iters * 16
+    buf = torch.empty(2 * nbytes // 4, dtype=torch.float32, device="cuda")
+    t, _ = run(7, blocks, iters, buf)
+    res["copy"] = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": t * 1e3,
+                   "GBs": 2 * nbytes / t / 1e9, "frac_of_8TBs": 2 * nbytes / t / 1e9 / HBM_PEAK_GBS}
+    print(json.dumps({"microbench": res}), flush=True)
 
 
 if __name__ == "__main__":

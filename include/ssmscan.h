@@ -38,8 +38,10 @@
  *  - Errors: arguments are checked on the host before anything is enqueued.
  *    Status 1-3 and 5 leave all memory untouched.  Status 4 means a HIP call
  *    failed while enqueueing (ssm_last_hip_error() gives the hipError_t).
- *  - The library keeps no state between calls except a cached device
- *    property query; calls from several host threads are safe.
+ *  - The library allocates no memory and reads no environment variables: the
+ *    caller passes every buffer, scratch included (the *_workspace_size
+ *    queries give the size).  It keeps no state between calls except a
+ *    cached device property query; calls from several host threads are safe.
  */
 #ifndef SSMSCAN_H
 #define SSMSCAN_H
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -71,7 +73,7 @@ enum {
   SSM_ERR_SHAPE = 2,        /* a size <= 0, dim % ngroups != 0, or overflow */
   SSM_ERR_UNSUPPORTED = 3,  /* dtype, dstate > 16, conv width != 4, bad enum */
   SSM_ERR_HIP = 4,          /* a HIP runtime call failed */
-  SSM_ERR_WORKSPACE = 5     /* workspace given but smaller than required */
+  SSM_ERR_WORKSPACE = 5     /* scratch needed but workspace NULL or too small */
 };
 
 /* Arguments of ssm_scan_fwd.  Every pointer is a device pointer. */
@@ -99,9 +101,13 @@ typedef struct ssm_scan_args {
   const float *conv_bias;                       /* (d) fp32 or NULL */
   int32_t conv_width;                           /* must be 4 */
   int32_t conv_act;                             /* SSM_ACT_* */
-  /* Scratch for the sequence-split plan (see ssm_scan_workspace_size).  When
-   * NULL and scratch is needed, the library takes it from the stream-ordered
-   * allocator (hipMallocAsync/hipFreeAsync on hip_stream). */
+  /* Scratch for the sequence-split plan (see ssm_scan_workspace_size),
+   * caller-allocated device memory of workspace_bytes bytes.  The library
+   * allocates nothing: when the plan needs scratch and workspace is NULL or
+   * smaller than ssm_scan_workspace_size reports, the call returns
+   * SSM_ERR_WORKSPACE before anything is enqueued.  It is not read before it
+   * is written, so it needs no clearing, and it may be reused once the call's
+   * work on hip_stream has finished. */
   void *workspace;
   size_t workspace_bytes;
   /* Optional output for the backward (ssm_scan_bwd): the state before every
@@ -109,6 +115,12 @@ typedef struct ssm_scan_args {
    * nck = ceil(seqlen / SSM_CKPT_INTERVAL); entry k is x_{k*32-1}, so entry 0
    * is initial_state (zero when not given).  NULL: not written. */
   float *checkpoints;
+  /* Sequence split: 0 lets the library choose how many segments the sequence
+   * is cut into (it splits only when the channels alone leave the GPU short
+   * of waves); k >= 1 asks for k segments (equal lengths of whole chunks, so
+   * possibly fewer).  The split changes the results only by rounding order.
+   * Negative values return SSM_ERR_SHAPE. */
+  int32_t seq_segments;
 } ssm_scan_args_t;
 
 /* Selective-scan forward.  Enqueues the scan on hip_stream and returns a
@@ -179,8 +191,10 @@ typedef struct ssm_scan_bwd_args {
   float *dD;                                    /* (d) fp32, required iff D */
   float *ddelta_bias;                           /* (d) fp32, required iff delta_bias */
   float *dinitial_state;                        /* (b,d,n) fp32 or NULL */
-  /* Scratch for the per-workgroup partial sums (ssm_scan_bwd_workspace_size).
-   * When NULL the library takes it from the stream-ordered allocator. */
+  /* Scratch for the per-workgroup partial sums (ssm_scan_bwd_workspace_size),
+   * caller-allocated device memory; the library allocates nothing, and a NULL
+   * or too small workspace returns SSM_ERR_WORKSPACE before anything is
+   * enqueued.  Every partial is written before it is read. */
   void *workspace;
   size_t workspace_bytes;
   /* Sequence split: 0 lets the library choose how many segments of whole

@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssmscan.so")
+# instruction-rate and bandwidth probes (bench.py --microbench), a library of
+# their own so that the operator's ABI holds only the operator
+MICRO_LIB = os.path.join(PKG, "libssmmicro.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,6 +32,9 @@ SOURCES = [
     ("scan_bf16.hip", True),
     ("scan_f32.hip", True),
     ("scan_f16.hip", True),
+    ("scan_bf16_ew.hip", True),
+    ("scan_f32_ew.hip", True),
+    ("scan_f16_ew.hip", True),
     ("ssm_scan.hip", True),
     ("scan_complex.hip", True),
     ("decode.hip", True),
@@ -36,6 +42,7 @@ SOURCES = [
     ("bwd.hip", True),
     ("validate.cpp", False),
 ]
+MICRO_SOURCES = [("microbench.hip", True)]
 
 
 def _compile(src: str, is_hip: bool) -> str:
@@ -49,19 +56,26 @@ def _compile(src: str, is_hip: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libssmscan.so (always rebuilds)."""
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("linking libssmscan.so failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libssmscan.so and libssmmicro.so (always
+    rebuilds)."""
+    srcs = SOURCES + MICRO_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(*s), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], MICRO_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MICRO_LIB}")
     return LIB
 
 

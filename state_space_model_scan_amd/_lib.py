@@ -49,6 +49,7 @@ class ScanArgs(ctypes.Structure):
         ("conv_width", ctypes.c_int32), ("conv_act", ctypes.c_int32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("checkpoints", _vp),
+        ("seq_segments", ctypes.c_int32),
     ]
 
 

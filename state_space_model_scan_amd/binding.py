@@ -66,7 +66,7 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
                  conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
                  conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
                  workspace: Optional[torch.Tensor] = None, stream=None,
-                 checkpoints: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 checkpoints: Optional[torch.Tensor] = None, seq_segments: int = 0) -> torch.Tensor:
     """Enqueue ssm_scan_fwd on the current stream; returns ``out``.
 
     Shapes as in include/ssmscan.h.  ``out`` (same dtype as delta) and
@@ -74,7 +74,8 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     allocated when not given.  With ``conv_weight`` the conv prologue computes
     u from ``conv_x`` and ``u`` may be None.  ``checkpoints`` (float32,
     (batch, dim, ceil(seqlen / 32), dstate), optional) receives the states the
-    backward starts its chunks from.
+    backward starts its chunks from.  ``seq_segments`` (0: the library's
+    choice) asks for a sequence split into that many parallel segments.
     """
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
@@ -111,6 +112,7 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     args.conv_x, args.conv_weight, args.conv_bias = _ptr(conv_x), _ptr(conv_weight), _ptr(conv_bias)
     args.conv_width = 0 if conv_weight is None else conv_weight.shape[1]
     args.conv_act = conv_act
+    args.seq_segments = int(seq_segments)
     if checkpoints is not None:
         want = (batch, dim, checkpoint_count(seqlen), dstate)
         if tuple(checkpoints.shape) != want or checkpoints.dtype != torch.float32 or not checkpoints.is_contiguous():

@@ -723,18 +723,11 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   if (pl.blocks > 0x7fffffffLL || static_cast<int64_t>(pl.nB / 256) > 0x7fffffffLL ||
       static_cast<int64_t>(pl.nA / 256) > 0x7fffffffLL || pl.nseg > 65535)
     return SSM_ERR_SHAPE;
-  if (a->workspace && a->workspace_bytes < pl.bytes) return SSM_ERR_WORKSPACE;
+  if (!a->workspace || a->workspace_bytes < pl.bytes) return SSM_ERR_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
 
-  void *ws = a->workspace;
-  bool owned = false;
-  if (!ws) {
-    const hipError_t e = hipMallocAsync(&ws, pl.bytes, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    owned = true;
-  }
-  char *base = static_cast<char *>(ws);
+  char *base = static_cast<char *>(a->workspace);
   auto take = [&](size_t elems) {
     float *r = reinterpret_cast<float *>(base);
     base += (elems * sizeof(float) + 255) / 256 * 256;
@@ -795,10 +788,6 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   if (a->D) reduce(p.pD, a->dD, 1, kpart, dim);
   if (a->delta_bias) reduce(p.pbias, a->ddelta_bias, 1, kpart, dim);
 
-  if (owned) {
-    const hipError_t ef = hipFreeAsync(ws, stream);
-    if (e == hipSuccess) e = ef;
-  }
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }

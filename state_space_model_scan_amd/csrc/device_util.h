@@ -68,11 +68,19 @@ struct RawV {  // NV consecutive io elements as loaded from memory (NV = 4 or 8)
     }
   }
   // Element loads of [idx, idx+cnt), zero beyond cnt (cnt may be <= 0).
+  // Every element lands in a register of its own and the words are packed
+  // after the last load, so no load waits on the one before it.
   __device__ __forceinline__ void load_elems(const void *base, int64_t idx, int cnt) {
-    zero();
+    if constexpr (IO != 0) {
+      uint32_t h[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (i < cnt) load_one(base, idx + i, i);
+      for (int i = 0; i < NV; ++i) h[i] = i < cnt ? static_cast<const uint16_t *>(base)[idx + i] : 0u;
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) w[j] = h[2 * j] | (h[2 * j + 1] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) w[i] = i < cnt ? __float_as_uint(static_cast<const float *>(base)[idx + i]) : 0u;
+    }
   }
   __device__ __forceinline__ void load(const void *base, int64_t idx, int cnt, bool vec) {
     if (vec && cnt >= NV) load_vec(base, idx);

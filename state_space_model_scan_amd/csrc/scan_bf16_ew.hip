@@ -1,0 +1,9 @@
+// bf16-io instances of the selective-scan kernel (see scan_kernel.h) that
+// move io element by element: misaligned pointers or seqlen % 8 != 0.
+#include "scan_kernel.h"
+
+namespace ssm {
+ScanFn pick_scan_bf16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
+  return pick_scan<1, false>(nsw, lpc, bv, cv, conv, mode);
+}
+}  // namespace ssm

@@ -1,8 +1,9 @@
-// fp16-io instances of the selective-scan kernel (see scan_kernel.h).
+// fp16-io instances of the selective-scan kernel (see scan_kernel.h) with
+// vector io; the element-by-element instances are in scan_f16_ew.hip.
 #include "scan_kernel.h"
 
 namespace ssm {
-ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  return pick_scan<2>(nsw, lpc, bv, cv, conv, mode);
+ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec) {
+  return vec ? pick_scan<2, true>(nsw, lpc, bv, cv, conv, mode) : pick_scan_f16_ew(nsw, lpc, bv, cv, conv, mode);
 }
 }  // namespace ssm

@@ -33,7 +33,16 @@
 //     segment from the exact carried state
 //       x_in(k) = E_{k-1} + exp(A * S_{k-1}) * (E_{k-2} + exp(A * S_{k-2}) * ...)
 //     with E_j the end state of segment j from zero and S_j its summed step:
-//     the same recurrence, reassociated.
+//     the same recurrence, reassociated;
+//   * when the waves do not divide evenly over the SIMDs (the Mamba-2.8B
+//     layer gives 2560 waves for 1024 SIMDs), the last `hand_units` channel
+//     blocks are cut into `hand_parts` consecutive time ranges run by
+//     different waves: part p waits until part p-1 has published its end
+//     state, then continues the recurrence from it (exactly the sequential
+//     recurrence, handed over through memory).  Every SIMD then gets whole
+//     blocks plus one part instead of some getting a whole block more.
+//     Parts are ordered by workgroup id and workgroups are dispatched in id
+//     order, so a waiting part's predecessor is always resident or done.
 #pragma once
 
 #include "device_util.h"
@@ -46,12 +55,18 @@ struct ScanParams {
   const float *A, *D, *dbias, *init, *cw, *cb;
   void *out;
   float *last;
-  float *ws_state, *ws_sumdt;
-  float *ckpt;           // saved states for the backward, or null
+  float *ws_state, *ws_sumdt;   // segment plan: end states from zero, summed steps
+  float *carry;                 // hand-over plan: published end states [slot][k][lane]
+  int *flags;                   // hand-over plan: one flag per slot, zero before the launch
+  int *status;                  // set when a hand-over wait ran out (never under in-order dispatch)
+  float *ckpt;                  // saved states for the backward, or null
   int64_t batch, dim, seqlen, seg_len, cpg, nck;
   int n, n_pad, ngroups, groups_eff, nblk, nseg, nblocks;
-  int softplus, conv_silu, vec, xcd_swizzle;
+  int hand_units, hand_parts;   // hand-over plan (0, 1: none)
+  int softplus, conv_silu, xcd_swizzle;
 };
+
+constexpr int kHandSpinLimit = 1 << 22;   // bounded wait of a hand-over part
 
 enum { MODE_STATE = 0, MODE_FULL = 1 };
 
@@ -89,7 +104,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE>
+// VEC: every io pointer is 16-byte aligned and seqlen % 8 == 0, so every
+// owned 8-timestep range and every B/C piece is either whole or past the
+// end, and is moved as one vector; otherwise element by element.
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE, bool VEC>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 scan_kernel(const ScanParams p) {
   constexpr bool FULL = MODE == MODE_FULL;
@@ -122,11 +140,24 @@ scan_kernel(const ScanParams p) {
   const int q = lane % LPC;             // state group of this lane within its channel
   const int cw_idx = lane / LPC;        // channel within the wave
 
-  // Block -> (batch, channel group, channel block).  Consecutive logical
-  // blocks share B/C; the hardware deals blocks to the 8 XCDs round-robin, so
-  // the remap keeps the blocks of one group on one XCD's L2.
-  int bid = blockIdx.x;
-  if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
+  // Block -> (channel block, time range).  Consecutive logical blocks share
+  // B/C; the hardware deals blocks to the 8 XCDs round-robin, so the remap
+  // keeps the blocks of one group on one XCD's L2.  Blocks past the whole
+  // ones are the hand-over parts, ordered by part.
+  const int nwhole = p.nblocks - p.hand_units;
+  int bid = blockIdx.x, part = 0, hidx = 0;
+  if (bid < nwhole) {
+    if (p.xcd_swizzle) bid = (bid & 7) * (nwhole >> 3) + (bid >> 3);
+  } else {
+    part = (bid - nwhole) / p.hand_units;
+    hidx = (bid - nwhole) % p.hand_units;
+    bid = nwhole + hidx;
+    // A SIMD issues from its oldest waves first, and the parts are the
+    // youngest: without a higher priority part 0 would only finish near the
+    // end and part 1 would then run mostly alone.
+    __builtin_amdgcn_s_setprio(3);
+  }
+  const int nparts = bid < nwhole ? 1 : p.hand_parts;
   const int blk = bid % p.nblk;
   const int rest = bid / p.nblk;
   const int g = rest % p.groups_eff;
@@ -138,12 +169,12 @@ scan_kernel(const ScanParams p) {
   const int64_t row = b * p.dim + dl;
   const int64_t rbase = row * p.seqlen;
   const int64_t BD = p.batch * p.dim;
-  const int seg = blockIdx.y;
-  const int64_t t_begin = seg * p.seg_len;
-  const int64_t t_end = (t_begin + p.seg_len < p.seqlen) ? t_begin + p.seg_len : p.seqlen;
+  const int seg = p.nseg > 1 ? static_cast<int>(blockIdx.y) : part;
+  const int nsegs = p.nseg > 1 ? p.nseg : nparts;
+  const int64_t t_begin = nsegs > 1 ? seg * p.seg_len : 0;
+  const int64_t t_end = (nsegs > 1 && t_begin + p.seg_len < p.seqlen) ? t_begin + p.seg_len : p.seqlen;
   const int s0 = q * NSW;
   const int n = p.n;
-  const bool vec = p.vec != 0;
 
   // ---- per-lane parameters
   float Ap[NSW], Bf[NSW], Cf[NSW], x[NSW];
@@ -172,17 +203,38 @@ scan_kernel(const ScanParams p) {
       for (int k = 0; k < NSW; ++k)
         if (s0 + k < n) x[k] = p.init[row * n + s0 + k];
     }
-  } else if constexpr (FULL) {
+  } else if (p.nseg > 1) {
+    if constexpr (FULL) {
 #pragma unroll
-    for (int k = 0; k < NSW; ++k) x[k] = p.ws_state[static_cast<int64_t>(s0 + k) * BD + row];
-    for (int j = 1; j < seg; ++j) {
-      const float sdt = p.ws_sumdt[static_cast<int64_t>(j) * BD + row];
+      for (int k = 0; k < NSW; ++k) x[k] = p.ws_state[static_cast<int64_t>(s0 + k) * BD + row];
+      for (int j = 1; j < seg; ++j) {
+        const float sdt = p.ws_sumdt[static_cast<int64_t>(j) * BD + row];
 #pragma unroll
-      for (int k = 0; k < NSW; ++k) {
-        const float e = fast_exp2(sdt * Ap[k]);
-        x[k] = fmaf(e, x[k], p.ws_state[(static_cast<int64_t>(j) * p.n_pad + s0 + k) * BD + row]);
+        for (int k = 0; k < NSW; ++k) {
+          const float e = fast_exp2(sdt * Ap[k]);
+          x[k] = fmaf(e, x[k], p.ws_state[(static_cast<int64_t>(j) * p.n_pad + s0 + k) * BD + row]);
+        }
       }
     }
+  } else {
+    // hand-over: wait for part seg-1 of this block.  Lane 0 polls the flag
+    // with relaxed coherent loads; the acquire fence (a cache invalidation)
+    // is taken once, after the flag is seen -- an acquire load per poll would
+    // invalidate the caches under every other wave of the compute unit.
+    const int64_t slot = static_cast<int64_t>(hidx) * (nparts - 1) + (seg - 1);
+    if (lane == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(p.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        if (++spins > kHandSpinLimit) {
+          __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+    for (int k = 0; k < NSW; ++k) x[k] = p.carry[(slot * NSW + k) * 64 + lane];
   }
 
   // ---- this lane's timesteps of a chunk: [c + 8q, c + 8q + 8)
@@ -192,25 +244,41 @@ scan_kernel(const ScanParams p) {
     return static_cast<int>((t_end - tp0 < kKP) ? t_end - tp0 : kKP);
   };
 
-  // global inputs of the next chunk, loaded before the current recurrence
-  RawV<IO, kKP> r_a, r_dl, r_z, r_h;   // u (or conv x), delta, z, conv halo
-  r_a.zero(); r_dl.zero(); r_z.zero(); r_h.zero();
-  auto fetch = [&](int64_t c) {
+  // Raw global inputs of a chunk.  Two sets alternate (the chunk loop is
+  // unrolled by two), so no loop-carried copy waits on the loads in flight.
+  struct RawSet {
+    RawV<IO, kKP> a, dl, z, h;   // u (or conv x), delta, z, the 8 samples before (conv halo)
+    RawV<IO, 8> B, C;            // this lane's piece of the chunk's B / C tile
+    float du[kKP];               // D*u of the owned timesteps (prepared, for the epilogue)
+  };
+  // VEC: one unconditional vector load per input.  A range past the end of
+  // the time range reads the row's last vector instead (those values only
+  // ever meet delta' = 0, a zero input term or an output that is not
+  // stored), so no load sits behind a branch and the compiler's waits count
+  // exactly the loads in flight.  Otherwise element by element.
+  const int64_t last_v = (t_end - 1) & ~static_cast<int64_t>(kKP - 1);   // row offset of the last vector
+  const void *zsrc = p.z ? p.z : p.delta;   // without z: delta again, from cache, unused
+  auto fetch = [&](RawSet &r, int64_t c) {
     const int64_t tp0 = c + own;
-    const int cnt = count(c);
-    r_a.load(CONV ? p.cx : p.u, rbase + tp0, cnt, vec);
-    r_dl.load(p.delta, rbase + tp0, cnt, vec);
-    if (FULL && p.z) r_z.load(p.z, rbase + tp0, cnt, vec);
-    if constexpr (CONV) {
-      // the three samples before tp0 land in slots 5..7 (zero before t = 0)
-      if (vec && tp0 >= kKP) {
-        r_h.load_vec(p.cx, rbase + tp0 - kKP);
-      } else {
-        r_h.zero();
+    if constexpr (VEC) {
+      const int64_t tv = tp0 < last_v ? tp0 : last_v;
+      r.a.load_vec(CONV ? p.cx : p.u, rbase + tv);
+      r.dl.load_vec(p.delta, rbase + tv);
+      if constexpr (FULL) r.z.load_vec(zsrc, rbase + tv);
+      // the halo of the first range of a row is zeroed where it is used
+      if constexpr (CONV) r.h.load_vec(p.cx, rbase + (tv >= kKP ? tv - kKP : 0));
+    } else {
+      const int cnt = count(c);
+      r.a.load_elems(CONV ? p.cx : p.u, rbase + tp0, cnt);
+      r.dl.load_elems(p.delta, rbase + tp0, cnt);
+      if (FULL && p.z) r.z.load_elems(p.z, rbase + tp0, cnt);
+      if constexpr (CONV) {
+        // the three samples before tp0 land in slots 5..7 (zero before t = 0)
+        r.h.zero();
 #pragma unroll
         for (int i = kKP - 3; i < kKP; ++i) {
           const int64_t t = tp0 - kKP + i;
-          if (t >= 0 && t < p.seqlen) r_h.load_one(p.cx, rbase + t, i);
+          if (t >= 0 && t < p.seqlen) r.h.load_one(p.cx, rbase + t, i);
         }
       }
     }
@@ -218,48 +286,60 @@ scan_kernel(const ScanParams p) {
 
   // B/C tile of a chunk: lane v < PIECES loads 8 timesteps of one state of B
   // and of C (rows of the (b, g) group), and writes them transposed to LDS.
+  // With VEC every lane loads (lanes without a piece, or with a padded
+  // state, read state 0's row and stage nothing or zeros).
   const int bc_s = lane / (T / 8);
   const int bc_t0 = (lane % (T / 8)) * 8;
   const bool bc_lane = ANYV && lane < PIECES;
   const bool bc_real = bc_lane && bc_s < n;
-  RawV<IO, 8> r_B, r_C;
-  r_B.zero(); r_C.zero();
-  auto fetch_bc = [&](int64_t c) {
-    if (bc_real) {
-      const int64_t e = bc_base + static_cast<int64_t>(bc_s) * p.seqlen + c + bc_t0;
-      const int64_t left = t_end - (c + bc_t0);
-      const int cnt = static_cast<int>(left < 8 ? left : 8);
-      if constexpr (BV) r_B.load(p.B, e, cnt, vec);
-      if constexpr (CV && FULL) r_C.load(p.C, e, cnt, vec);
+  const int64_t bc_row = bc_base + static_cast<int64_t>(bc_real ? bc_s : 0) * p.seqlen;
+  auto fetch_bc = [&](RawSet &r, int64_t c) {
+    if constexpr (VEC) {
+      const int64_t t_last = (t_end - 1) & ~static_cast<int64_t>(7);
+      const int64_t t0 = c + bc_t0 < t_last ? c + bc_t0 : t_last;
+      if constexpr (BV) r.B.load_vec(p.B, bc_row + t0);
+      if constexpr (CV && FULL) r.C.load_vec(p.C, bc_row + t0);
+    } else {
+      r.B.zero();
+      r.C.zero();
+      if (bc_real) {
+        const int64_t left = t_end - (c + bc_t0);
+        const int cnt = static_cast<int>(left < 8 ? left : 8);
+        if constexpr (BV) r.B.load_elems(p.B, bc_row + c + bc_t0, cnt);
+        if constexpr (CV && FULL) r.C.load_elems(p.C, bc_row + c + bc_t0, cnt);
+      }
     }
   };
-  auto stage_bc = [&]() {
+  auto stage_bc = [&](const RawSet &r) {
     if (bc_lane) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (BV) s_bc[ANYV ? w : 0][0][bc_t0 + i][bc_s] = r_B.get(i);
-        if constexpr (CV && FULL) s_bc[ANYV ? w : 0][ANYV ? 1 : 0][bc_t0 + i][bc_s] = r_C.get(i);
+        if constexpr (BV) s_bc[ANYV ? w : 0][0][bc_t0 + i][bc_s] = bc_real ? r.B.get(i) : 0.0f;
+        if constexpr (CV && FULL) s_bc[ANYV ? w : 0][ANYV ? 1 : 0][bc_t0 + i][bc_s] = bc_real ? r.C.get(i) : 0.0f;
       }
     }
   };
 
   // per-lane chunk values for its own timesteps
-  float dtv[kKP], dtuv[kKP], duv[kKP], yv[kKP];
+  float dtv[kKP], dtuv[kKP], yv[kKP];
 #pragma unroll
-  for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
+  for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = yv[i] = 0.0f; }
 
   // CSc: silu after the conv; FCc: a whole chunk, so no lane owns timesteps
   // past the end and none needs masking (compile-time constants, chosen once
   // per chunk)
-  auto prep = [&](int64_t c, auto CSc, auto FCc) {
+  auto prep = [&](RawSet &r, int64_t c, auto CSc, auto FCc) {
     constexpr bool CS = decltype(CSc)::value;
     constexpr bool FC = decltype(FCc)::value;
     float uu[kKP];
     if constexpr (CONV) {
       float xv[kKP + 3];
-      xv[0] = r_h.get(kKP - 3); xv[1] = r_h.get(kKP - 2); xv[2] = r_h.get(kKP - 1);
+      const bool h_on = !VEC || c + own >= kKP;   // zero samples before t = 0
+      xv[0] = h_on ? r.h.get(kKP - 3) : 0.0f;
+      xv[1] = h_on ? r.h.get(kKP - 2) : 0.0f;
+      xv[2] = h_on ? r.h.get(kKP - 1) : 0.0f;
 #pragma unroll
-      for (int i = 0; i < kKP; ++i) xv[i + 3] = r_a.get(i);
+      for (int i = 0; i < kKP; ++i) xv[i + 3] = r.a.get(i);
 #pragma unroll
       for (int i = 0; i < kKP; ++i) {
         float acc = cbias;
@@ -272,17 +352,17 @@ scan_kernel(const ScanParams p) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kKP; ++i) uu[i] = r_a.get(i);
+      for (int i = 0; i < kKP; ++i) uu[i] = r.a.get(i);
     }
     const int cnt = count(c);
 #pragma unroll
     for (int i = 0; i < kKP; ++i) {
-      float dt = r_dl.get(i) + bias;
+      float dt = r.dl.get(i) + bias;
       if (p.softplus) dt = softplus_f(dt);
       if (!FC && i >= cnt) dt = 0.0f;
       dtv[i] = dt;
       dtuv[i] = dt * uu[i];
-      duv[i] = Dd * uu[i];
+      r.du[i] = Dd * uu[i];
     }
   };
   auto gather_y = [&]() {     // sum of the quad's partial C.x of this lane's timesteps
@@ -299,17 +379,17 @@ scan_kernel(const ScanParams p) {
     }
   };
 
-  auto epilogue = [&](int64_t c) {
+  auto epilogue = [&](int64_t c, const RawSet &r) {
     const int cnt = count(c);
     if (cnt <= 0 || !valid) return;
     float o[kKP];
 #pragma unroll
     for (int i = 0; i < kKP; ++i) {
-      float y = yv[i] + duv[i];
-      if (p.z) y *= silu_f(r_z.get(i));
+      float y = yv[i] + r.du[i];
+      if (p.z) y *= silu_f(r.z.get(i));
       o[i] = y;
     }
-    store_n<IO, kKP>(p.out, rbase + c + own, o, cnt, vec);
+    store_n<IO, kKP>(p.out, rbase + c + own, o, cnt, VEC);
   };
 
   float sumdt = 0.0f;   // summed delta' of the segment (MODE_STATE)
@@ -367,25 +447,20 @@ scan_kernel(const ScanParams p) {
     }
   };
 
-  fetch(t_begin);
-  if constexpr (ANYV) fetch_bc(t_begin);
-
-  for (int64_t c = t_begin; c < t_end; c += T) {
+  const int64_t nch = (t_end - t_begin + T - 1) / T;
+  const int64_t c_last = t_begin + (nch - 1) * T;   // VEC prefetches never start past it
+  // Chunk c's epilogue runs in the next chunk's body, before that body's
+  // prefetch and recurrence: the output store then completes during the
+  // recurrence, and no later wait for a load waits on it.  The other set
+  // (nxt) still holds chunk c - T's z and D*u when the epilogue reads them,
+  // and is refilled right after.
+  auto body = [&](int64_t c, RawSet &cur, RawSet &nxt) {
     const int len = static_cast<int>((t_end - c < T) ? t_end - c : T);
     const bool csilu = CONV && p.conv_silu;
-    if constexpr (FULL) {
-      // the state before timestep c, every SSM_CKPT_INTERVAL timesteps
-      if (p.ckpt && valid && (c % SSM_CKPT_INTERVAL) == 0) {
-        float *dst = p.ckpt + (row * p.nck + c / SSM_CKPT_INTERVAL) * n;
-#pragma unroll
-        for (int k = 0; k < NSW; ++k)
-          if (s0 + k < n) dst[s0 + k] = x[k];
-      }
-    }
     if (len == T) {
-      if (csilu) prep(c, std::true_type{}, std::true_type{}); else prep(c, std::false_type{}, std::true_type{});
+      if (csilu) prep(cur, c, std::true_type{}, std::true_type{}); else prep(cur, c, std::false_type{}, std::true_type{});
     } else {
-      if (csilu) prep(c, std::true_type{}, std::false_type{}); else prep(c, std::false_type{}, std::false_type{});
+      if (csilu) prep(cur, c, std::true_type{}, std::false_type{}); else prep(cur, c, std::false_type{}, std::false_type{});
     }
     if constexpr (XCH) {
       // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
@@ -402,13 +477,29 @@ scan_kernel(const ScanParams p) {
     }
     if constexpr (ANYV) {
       wave_lds_sync();          // the previous chunk's reads of the slice are done
-      stage_bc();
+      stage_bc(cur);
       wave_lds_sync();          // the slice is written before any lane reads it
     }
-    const RawV<IO, kKP> z_cur = r_z;
-    if (c + T < t_end) {
-      fetch(c + T);
-      if constexpr (ANYV) fetch_bc(c + T);
+    if constexpr (FULL) {
+      if (c > t_begin) epilogue(c - T, nxt);
+    }
+    if constexpr (VEC) {
+      const int64_t cn = c + T < c_last ? c + T : c_last;
+      fetch(nxt, cn);
+      if constexpr (ANYV) fetch_bc(nxt, cn);
+    } else if (c + T < t_end) {
+      fetch(nxt, c + T);
+      if constexpr (ANYV) fetch_bc(nxt, c + T);
+    }
+    if constexpr (FULL) {
+      // the state before timestep c, every SSM_CKPT_INTERVAL timesteps (a
+      // conditional store: issued after this body's waits for loaded data)
+      if (p.ckpt && valid && (c % SSM_CKPT_INTERVAL) == 0) {
+        float *dst = p.ckpt + (row * p.nck + c / SSM_CKPT_INTERVAL) * n;
+#pragma unroll
+        for (int k = 0; k < NSW; ++k)
+          if (s0 + k < n) dst[s0 + k] = x[k];
+      }
     }
     if (len == T) {
       // whole chunk, fully unrolled; operands read from LDS two timesteps
@@ -436,19 +527,34 @@ scan_kernel(const ScanParams p) {
       });
     }
     if constexpr (XCH && FULL) gather_y();   // sum of the quad's partial C.x
-    if constexpr (FULL) {
-      const RawV<IO, kKP> z_next = r_z;
-      r_z = z_cur;
-      epilogue(c);
-      r_z = z_next;
-    }
+  };
+
+  RawSet S0, S1;
+  fetch(S0, t_begin);
+  if constexpr (ANYV) fetch_bc(S0, t_begin);
+  for (int64_t i = 0; i < nch; i += 2) {
+    body(t_begin + i * T, S0, S1);
+    if (i + 1 < nch) body(t_begin + (i + 1) * T, S1, S0);
+  }
+  if constexpr (FULL) {
+    if ((nch - 1) & 1) epilogue(c_last, S1);
+    else epilogue(c_last, S0);
   }
 
   if constexpr (FULL) {
-    if (p.last && seg == p.nseg - 1 && valid) {
+    if (seg == nsegs - 1) {
+      if (p.last && valid) {
 #pragma unroll
-      for (int k = 0; k < NSW; ++k)
-        if (s0 + k < n) p.last[row * n + s0 + k] = x[k];
+        for (int k = 0; k < NSW; ++k)
+          if (s0 + k < n) p.last[row * n + s0 + k] = x[k];
+      }
+    } else if (p.nseg <= 1) {
+      // hand-over: publish this part's end state, then its flag
+      const int64_t slot = static_cast<int64_t>(hidx) * (nparts - 1) + seg;
+#pragma unroll
+      for (int k = 0; k < NSW; ++k) p.carry[(slot * NSW + k) * 64 + lane] = x[k];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane == 0) __hip_atomic_store(p.flags + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     if (valid) {
@@ -464,36 +570,39 @@ using ScanFn = void (*)(const ScanParams);
 
 // Kernel instance for a plan.  (nsw, lpc) is one of (4,4), (4,2), (4,1),
 // (2,1), (1,1): n_pad = nsw * lpc states.
-template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV>
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, bool VEC>
 ScanFn pick_mode(int mode) {
-  return mode == MODE_FULL ? scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_FULL>
-                           : scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_STATE>;
+  return mode == MODE_FULL ? scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_FULL, VEC>
+                           : scan_kernel<IO, NSW, LPC, BV, CV, CONV, MODE_STATE, VEC>;
 }
-template <int IO, int NSW, int LPC, bool BV, bool CV>
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool VEC>
 ScanFn pick_conv(bool conv, int mode) {
-  return conv ? pick_mode<IO, NSW, LPC, BV, CV, true>(mode) : pick_mode<IO, NSW, LPC, BV, CV, false>(mode);
+  return conv ? pick_mode<IO, NSW, LPC, BV, CV, true, VEC>(mode) : pick_mode<IO, NSW, LPC, BV, CV, false, VEC>(mode);
 }
-template <int IO, int NSW, int LPC>
+template <int IO, int NSW, int LPC, bool VEC>
 ScanFn pick_bc(bool bv, bool cv, bool conv, int mode) {
-  if (bv && cv) return pick_conv<IO, NSW, LPC, true, true>(conv, mode);
-  if (bv) return pick_conv<IO, NSW, LPC, true, false>(conv, mode);
-  if (cv) return pick_conv<IO, NSW, LPC, false, true>(conv, mode);
-  return pick_conv<IO, NSW, LPC, false, false>(conv, mode);
+  if (bv && cv) return pick_conv<IO, NSW, LPC, true, true, VEC>(conv, mode);
+  if (bv) return pick_conv<IO, NSW, LPC, true, false, VEC>(conv, mode);
+  if (cv) return pick_conv<IO, NSW, LPC, false, true, VEC>(conv, mode);
+  return pick_conv<IO, NSW, LPC, false, false, VEC>(conv, mode);
 }
-template <int IO>
+template <int IO, bool VEC>
 ScanFn pick_scan(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  if (nsw == 4 && lpc == 4) return pick_bc<IO, 4, 4>(bv, cv, conv, mode);
-  if (nsw == 4 && lpc == 2) return pick_bc<IO, 4, 2>(bv, cv, conv, mode);
-  if (nsw == 4 && lpc == 1) return pick_bc<IO, 4, 1>(bv, cv, conv, mode);
-  if (nsw == 2 && lpc == 1) return pick_bc<IO, 2, 1>(bv, cv, conv, mode);
-  if (nsw == 1 && lpc == 1) return pick_bc<IO, 1, 1>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 4) return pick_bc<IO, 4, 4, VEC>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 2) return pick_bc<IO, 4, 2, VEC>(bv, cv, conv, mode);
+  if (nsw == 4 && lpc == 1) return pick_bc<IO, 4, 1, VEC>(bv, cv, conv, mode);
+  if (nsw == 2 && lpc == 1) return pick_bc<IO, 2, 1, VEC>(bv, cv, conv, mode);
+  if (nsw == 1 && lpc == 1) return pick_bc<IO, 1, 1, VEC>(bv, cv, conv, mode);
   return nullptr;
 }
 
-// Defined in scan_f32.hip / scan_bf16.hip / scan_f16.hip (one translation
-// unit per io dtype).
-ScanFn pick_scan_f32(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
-ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
-ScanFn pick_scan_bf16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
+// Defined in scan_<dtype>.hip (vector io) and scan_<dtype>_ew.hip (element
+// by element): one translation unit per io dtype and load width.
+ScanFn pick_scan_f32(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec);
+ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec);
+ScanFn pick_scan_bf16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec);
+ScanFn pick_scan_f32_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
+ScanFn pick_scan_f16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
+ScanFn pick_scan_bf16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
 
 }  // namespace ssm

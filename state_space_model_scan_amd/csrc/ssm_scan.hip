@@ -7,7 +7,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 #include <mutex>
 
 #include "host_util.h"
@@ -121,12 +120,23 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
 // ---------------------------------------------------------------------------
 
 
+// Fills n ints with zero (the hand-over flags): a kernel, so that the call
+// records no memset node when a caller captures it in a graph.
+__global__ void __launch_bounds__(256) zero_ints_kernel(int *p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 struct Plan {
   int n_pad, nsw, lpc, T;
   int groups_eff, nblk, nblocks, nseg;
+  int hand_units, hand_parts;    // hand-over plan (0, 1: none)
   int64_t cpg, seg_len;
+  size_t off_carry, off_flags, nflags;
   size_t ws_bytes;
 };
+
+size_t up256(size_t bytes) { return (bytes + 255) / 256 * 256; }
 
 int pow2ceil(int v) {
   int r = 1;
@@ -169,10 +179,8 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
     nseg = static_cast<int>(want < cap ? want : cap);
     if (nseg < 1) nseg = 1;
   }
-  if (const char *env = std::getenv("SSMSCAN_NSEG")) {
-    const int v = std::atoi(env);
-    if (v >= 1) nseg = v;
-  }
+  if (a->seq_segments >= 1) nseg = a->seq_segments;
+  if (nseg > a->seqlen / pl.T) nseg = static_cast<int>(a->seqlen / pl.T > 0 ? a->seqlen / pl.T : 1);
   int64_t seg_len = (a->seqlen + nseg - 1) / nseg;
   // checkpoints sit at multiples of SSM_CKPT_INTERVAL, which every chunk
   // length divides: segments then start on a checkpoint too
@@ -180,16 +188,49 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   seg_len = (seg_len + align - 1) / align * align;
   pl.seg_len = seg_len;
   pl.nseg = static_cast<int>((a->seqlen + seg_len - 1) / seg_len);
-  pl.ws_bytes = pl.nseg > 1
-                    ? static_cast<size_t>(pl.nseg - 1) * (pl.n_pad + 1) * a->batch * a->dim * sizeof(float)
-                    : 0;
+  size_t off = pl.nseg > 1
+                   ? up256(static_cast<size_t>(pl.nseg - 1) * (pl.n_pad + 1) * a->batch * a->dim * sizeof(float))
+                   : 0;
+  // Hand-over: with q whole waves per SIMD and r waves over, some SIMDs
+  // would run a whole wave more than the others.  Cut those r blocks into
+  // S = min(4, SIMDs / r) consecutive time parts instead, so every SIMD gets
+  // q whole waves and at most one part -- provided q + 1 waves fit a SIMD
+  // at once (the LDS of a wave sets how many do).
+  pl.hand_units = 0;
+  pl.hand_parts = 1;
+  if (pl.nseg == 1 && a->seq_segments == 0) {
+    const int simds = 4 * cus;
+    const int q = pl.nblocks / simds, r = pl.nblocks % simds;
+    const int lds = static_cast<int>(2 * pl.T * pl.n_pad * sizeof(float) +
+                                     (pl.lpc > 1 ? (pl.T * 64 + 8 * (pl.T / 8)) * sizeof(float) : 16));
+    const int fit = 160 * 1024 / lds / 4;   // waves of this kernel one SIMD holds
+    int S = r > 0 ? simds / r : 0;
+    if (S > 4) S = 4;
+    if (q >= 1 && S >= 2 && q + 1 <= fit) {
+      int64_t len = (a->seqlen + S - 1) / S;
+      len = (len + align - 1) / align * align;
+      const int parts = static_cast<int>((a->seqlen + len - 1) / len);
+      if (parts >= 2) {
+        pl.hand_units = r;
+        pl.hand_parts = parts;
+        pl.seg_len = len;
+        const size_t slots = static_cast<size_t>(r) * (parts - 1);
+        pl.off_carry = off;
+        off += up256(slots * pl.nsw * 64 * sizeof(float));
+        pl.off_flags = off;
+        pl.nflags = slots + 1;   // one per slot, then the status word
+        off += up256(pl.nflags * sizeof(int));
+      }
+    }
+  }
+  pl.ws_bytes = off;
   return pl;
 }
 
-ScanFn pick(int io, int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
-  if (io == SSM_BF16) return pick_scan_bf16(nsw, lpc, bv, cv, conv, mode);
-  if (io == SSM_F16) return pick_scan_f16(nsw, lpc, bv, cv, conv, mode);
-  return pick_scan_f32(nsw, lpc, bv, cv, conv, mode);
+ScanFn pick(int io, int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec) {
+  if (io == SSM_BF16) return pick_scan_bf16(nsw, lpc, bv, cv, conv, mode, vec);
+  if (io == SSM_F16) return pick_scan_f16(nsw, lpc, bv, cv, conv, mode, vec);
+  return pick_scan_f32(nsw, lpc, bv, cv, conv, mode, vec);
 }
 
 }  // namespace
@@ -206,7 +247,7 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   const int st = ssm_scan_validate(a);
   if (st != SSM_OK) return st;
   const Plan pl = make_plan(a, cu_count_cached());
-  if (a->workspace && a->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
+  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
   const int io = a->io_dtype;
@@ -222,42 +263,49 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
   p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
   p.n = static_cast<int>(a->dstate); p.n_pad = pl.n_pad; p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = pl.groups_eff; p.nblk = pl.nblk; p.nseg = pl.nseg; p.nblocks = pl.nblocks;
+  p.hand_units = pl.hand_units; p.hand_parts = pl.hand_parts;
   p.softplus = a->delta_softplus; p.conv_silu = a->conv_act == SSM_ACT_SILU;
-  p.vec = (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
+  const bool vec = (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
           (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z)) &&
           (a->B_kind != SSM_BC_VARYING || aligned16(a->B)) && (a->C_kind != SSM_BC_VARYING || aligned16(a->C));
-  p.xcd_swizzle = (pl.nblocks % 8 == 0);
+  p.xcd_swizzle = ((pl.nblocks - pl.hand_units) % 8 == 0);
 
   void *ws = a->workspace;
-  bool owned = false;
-  if (pl.ws_bytes > 0 && !ws) {
-    const hipError_t e = hipMallocAsync(&ws, pl.ws_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    owned = true;
-  }
   if (pl.nseg > 1) {
     float *wsf = static_cast<float *>(ws);
     p.ws_state = wsf;
     p.ws_sumdt = wsf + static_cast<size_t>(pl.nseg - 1) * pl.n_pad * a->batch * a->dim;
   }
+  if (pl.hand_units > 0) {
+    char *wsc = static_cast<char *>(ws);
+    p.carry = reinterpret_cast<float *>(wsc + pl.off_carry);
+    p.flags = reinterpret_cast<int *>(wsc + pl.off_flags);
+    p.status = p.flags + (pl.nflags - 1);
+  }
+  const int64_t grid_x = static_cast<int64_t>(pl.nblocks - pl.hand_units) +
+                         static_cast<int64_t>(pl.hand_units) * pl.hand_parts;
+  if (grid_x > 0x7fffffffLL) return SSM_ERR_SHAPE;
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
   int rc = SSM_OK;
-  const ScanFn f_state = pl.nseg > 1 ? pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE) : nullptr;
-  const ScanFn f_full = pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL);
+  const ScanFn f_state = pl.nseg > 1 ? pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE, vec) : nullptr;
+  const ScanFn f_full = pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL, vec);
   if (!f_full || (pl.nseg > 1 && !f_state)) rc = SSM_ERR_UNSUPPORTED;
+  if (rc == SSM_OK && pl.hand_units > 0) {
+    const int64_t nf = static_cast<int64_t>(pl.nflags);
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(static_cast<unsigned>((nf + 255) / 256)), dim3(256), 0, stream,
+                       p.flags, nf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) rc = hip_fail(e);
+  }
   if (rc == SSM_OK && pl.nseg > 1) {
     hipLaunchKernelGGL(f_state, dim3(pl.nblocks, pl.nseg - 1), dim3(64 * kWavesPerBlock), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e);
   }
   if (rc == SSM_OK) {
-    hipLaunchKernelGGL(f_full, dim3(pl.nblocks, pl.nseg), dim3(64 * kWavesPerBlock), 0, stream, p);
+    hipLaunchKernelGGL(f_full, dim3(static_cast<unsigned>(grid_x), pl.nseg), dim3(64 * kWavesPerBlock), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e);
-  }
-  if (owned) {
-    const hipError_t e = hipFreeAsync(ws, stream);
-    if (e != hipSuccess && rc == SSM_OK) rc = hip_fail(e);
   }
   return rc;
 }

@@ -31,6 +31,7 @@ extern "C" int ssm_scan_validate(const ssm_scan_args_t *a) {
       !positive(a->dstate) || !positive(a->ngroups))
     return SSM_ERR_SHAPE;
   if (a->dim % a->ngroups != 0) return SSM_ERR_SHAPE;
+  if (a->seq_segments < 0) return SSM_ERR_SHAPE;
   if (!product_fits(a->batch, a->dim, a->seqlen) ||
       !product_fits(a->batch, a->ngroups * a->dstate, a->seqlen))
     return SSM_ERR_SHAPE;

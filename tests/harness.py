@@ -37,7 +37,7 @@ def to_dev(a: Optional[np.ndarray], io_dtype: int = F32, param: bool = False):
 
 
 def run_gpu(w: Workload, t: Dict[str, np.ndarray], *, last: bool = True,
-            init: Optional[np.ndarray] = None, poison: bool = True):
+            init: Optional[np.ndarray] = None, poison: bool = True, seq_segments: int = 0):
     """Run ssm_scan_fwd on the workload's inputs.  Returns (out (b*d, l) float64,
     last_state (b*d, n) float64 or None)."""
     import torch
@@ -60,7 +60,7 @@ def run_gpu(w: Workload, t: Dict[str, np.ndarray], *, last: bool = True,
                          to_dev(t["delta_bias"], param=True), w.softplus, out=out,
                          last_state=last_t,
                          initial_state=None if init is None else to_dev(init.astype(np.float32), param=True),
-                         **kw)
+                         seq_segments=seq_segments, **kw)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64).reshape(w.batch * w.dim, w.seqlen)
     ls = None if last_t is None else last_t.cpu().numpy().astype(np.float64).reshape(w.batch * w.dim, w.dstate)

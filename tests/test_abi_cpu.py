@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 8
+    assert L.ssm_abi_version() == 9
 
 
 def test_status_strings():
@@ -74,7 +74,7 @@ def test_null_conv_input():
 
 
 @pytest.mark.parametrize("field,val", [("batch", 0), ("dim", -1), ("seqlen", 0), ("dstate", 0),
-                                       ("ngroups", 0), ("ngroups", 3)])
+                                       ("ngroups", 0), ("ngroups", 3), ("seq_segments", -1)])
 def test_bad_shapes(field, val):
     assert _validate(_good_args(**{field: val})) == _lib.SSM_ERR_SHAPE
 
@@ -100,6 +100,24 @@ def test_fwd_rejects_before_any_hip_call():
     assert L.ssm_scan_fwd(None, None) == _lib.SSM_ERR_NULL
     size = ctypes.c_size_t(0)
     assert L.ssm_scan_workspace_size(ctypes.byref(_good_args(seqlen=0)), ctypes.byref(size)) == _lib.SSM_ERR_SHAPE
+
+
+def test_missing_workspace_is_rejected_before_any_launch():
+    """The library allocates nothing: when its plan needs scratch (a sequence
+    split, or the hand-over of a long-channel plan) and the caller passes no
+    workspace, or too little, ssm_scan_fwd returns SSM_ERR_WORKSPACE before it
+    enqueues anything.  The pointers here are not dereferenceable, so any
+    memory access would crash the test."""
+    L = _lib.lib()
+    for kw in (dict(batch=1, dim=64, seqlen=4096), dict(seq_segments=2),
+               dict(batch=8, dim=5120, ngroups=4, seqlen=2048)):
+        a = _good_args(**kw)
+        need = ctypes.c_size_t(0)
+        assert L.ssm_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.SSM_OK
+        assert need.value > 0, kw
+        assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+        a.workspace, a.workspace_bytes = FAKE, need.value - 1
+        assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
 
 
 def test_conv_validation():
@@ -280,6 +298,12 @@ def test_bwd_validation():
         assert need.value == (2 * up(2 * 2 * nblk * 16 * 100) + up(ns * 2 * 64 * 16) + 2 * up(ns * 2 * 64)
                               + up(ns * 2 * 64 * 16) + up(ns * 2 * 64)), segs
     assert v(_good_bwd(seq_segments=-1)) == _lib.SSM_ERR_SHAPE
+    # the backward always needs scratch, and allocates none itself
+    a = _good_bwd()
+    assert L.ssm_scan_bwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+    L.ssm_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(need))
+    a.workspace, a.workspace_bytes = FAKE, need.value - 1
+    assert L.ssm_scan_bwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
 
 
 def test_bwd_binding_errors():

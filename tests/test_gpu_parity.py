@@ -133,16 +133,49 @@ def test_initial_state_segmented():
     check(w, out, ref, last, ref_last, what="initial_state segmented")
 
 
-@pytest.mark.parametrize("nseg", ["1", "2", "7"])
-def test_forced_segment_counts(nseg, monkeypatch):
+@pytest.mark.parametrize("nseg", [1, 2, 7])
+def test_forced_segment_counts(nseg):
     """The segmented plan reassociates the recurrence; every split must match."""
-    monkeypatch.setenv("SSMSCAN_NSEG", nseg)
     w = _case(io_dtype=F32, dstate=16, dim=128, seqlen=1000, A_mode="lognormal", delta_mean=-4.5)
     t = make_inputs(w)
     log(f"[parity] nseg={nseg}")
-    out, last = run_gpu(w, t)
+    out, last = run_gpu(w, t, seq_segments=nseg)
     ref, ref_last = run_oracle(w, t)
     check(w, out, ref, last, ref_last, what=f"nseg {nseg}")
+
+
+# Channel counts whose waves do not divide evenly over the 1024 SIMDs of the
+# 256-CU device: the plan cuts the leftover channel blocks into 4, 3 or 2
+# consecutive time parts handed over from wave to wave (16 channels per wave).
+HANDOVER = {
+    "parts4": dict(batch=2, dim=10240, seqlen=200),            # 1280 waves: 256 left over
+    "parts3": dict(batch=1, dim=21840, seqlen=333),            # 1365 waves: 341 left over
+    "parts2": dict(batch=2, dim=12288, seqlen=130),            # 1536 waves: 512 left over
+    "parts2_grouped": dict(batch=2, dim=12288, ngroups=4, seqlen=256),
+    "parts4_bf16": dict(batch=2, dim=10240, seqlen=160, io_dtype=BF16),
+}
+
+
+@pytest.mark.parametrize("name", list(HANDOVER))
+def test_handover_plan(name):
+    """Channel blocks cut into time parts that continue from the state the
+    previous part published: exactly the sequential recurrence."""
+    w = _case(dstate=16, **HANDOVER[name])
+    t = make_inputs(w)
+    log(f"[parity] handover {name} {w}")
+    out, last = run_gpu(w, t)
+    ref, ref_last = run_oracle(w, t, nthreads=16)
+    check(w, out, ref, last, ref_last, what=f"handover {name}")
+
+
+def test_handover_plan_initial_state():
+    w = _case(dstate=16, batch=2, dim=10240, seqlen=100)
+    t = make_inputs(w)
+    init = np.random.default_rng(9).standard_normal((w.batch, w.dim, w.dstate))
+    log("[parity] handover with initial_state")
+    out, last = run_gpu(w, t, init=init)
+    ref, ref_last = run_oracle(w, t, init=init, nthreads=16)
+    check(w, out, ref, last, ref_last, what="handover initial_state")
 
 
 def _contraction_magnitude(w, t):
