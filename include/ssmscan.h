@@ -57,6 +57,7 @@ extern "C" {
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
+#define SSM_NOALLOC_SCRATCH_BYTES (8u << 20)   /* built-in scratch of ssm_scan_fwd_noalloc, per device */
 
 /* io dtype.  SSM_F16 (IEEE binary16) is taken by every entry point except
  * ssd_scan_fwd (bf16 only), which returns SSM_ERR_UNSUPPORTED for it. */
@@ -73,7 +74,8 @@ enum {
   SSM_ERR_SHAPE = 2,        /* a size <= 0, dim % ngroups != 0, or overflow */
   SSM_ERR_UNSUPPORTED = 3,  /* dtype, dstate > 16, conv width != 4, bad enum */
   SSM_ERR_HIP = 4,          /* a HIP runtime call failed */
-  SSM_ERR_WORKSPACE = 5     /* scratch needed but workspace NULL or too small */
+  SSM_ERR_WORKSPACE = 5,    /* scratch needed but workspace NULL or too small */
+  SSM_ERR_SCRATCH = 6       /* ssm_scan_fwd_noalloc: the plan needs more than its scratch */
 };
 
 /* Arguments of ssm_scan_fwd.  Every pointer is a device pointer. */
@@ -126,6 +128,23 @@ typedef struct ssm_scan_args {
 /* Selective-scan forward.  Enqueues the scan on hip_stream and returns a
  * status code (SSM_OK on success). */
 int ssm_scan_fwd(const ssm_scan_args_t *args, void *hip_stream);
+
+/* ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and status codes as ssm_scan_fwd, except that
+ * args->workspace and workspace_bytes are ignored: the scratch of the plan
+ * (sequence segments or hand-over parts) lives in a buffer built into the
+ * library, SSM_NOALLOC_SCRATCH_BYTES per device, held until the process
+ * ends.  A plan that needs more scratch than that returns SSM_ERR_SCRATCH
+ * before anything is enqueued (ssm_scan_workspace_size gives the need; the
+ * Mamba-shaped layers need at most 6.6 MiB).  The caller still allocates
+ * every input and output.  The call allocates nothing: the first call on a
+ * device looks the buffer's address up once (hipGetSymbolAddress).  Every
+ * call on one device shares that device's buffer and leaves its contents
+ * behind, so calls that overlap on one device -- different streams, or
+ * different threads -- race and give wrong results; calls ordered on one
+ * stream are safe. */
+int ssm_scan_fwd_noalloc(const ssm_scan_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssm_scan_fwd: the same status the call would
  * return before enqueueing anything.  Touches no device memory and makes no

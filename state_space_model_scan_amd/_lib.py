@@ -10,7 +10,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssmscan.
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_BC_FIXED, SSM_BC_VARYING = 0, 1
 SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
-SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_WORKSPACE = range(6)
+SSM_OK, SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_WORKSPACE, SSM_ERR_SCRATCH = range(7)
+SSM_NOALLOC_SCRATCH_BYTES = 8 << 20
 SSM_MAX_DSTATE = 16
 SSM_CONV_WIDTH = 4
 SSM_MAX_CONV_STATE = 256
@@ -20,7 +21,7 @@ SSM_CKPT_INTERVAL = 32
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
-    "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size",
+    "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size", "ssm_scan_fwd_noalloc",
     "ssm_scan_fwd_complex", "ssm_scan_complex_validate",
     "causal_conv1d_fwd", "causal_conv1d_validate", "causal_conv1d_fwd_ex", "causal_conv1d_ex_validate",
     "ssm_state_update", "ssm_state_update_validate",
@@ -131,6 +132,8 @@ def lib() -> ctypes.CDLL:
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
         L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_scan_validate.argtypes = [ctypes.POINTER(ScanArgs)]
         L.ssm_scan_validate.restype = ctypes.c_int
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ctypes.c_size_t)]

@@ -57,26 +57,10 @@ def _act_code(activation) -> int:
     raise NotImplementedError("activation must be None, silu, or swish")
 
 
-def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
-                 B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
-                 z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
-                 delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
-                 last_state: Optional[torch.Tensor] = None,
-                 initial_state: Optional[torch.Tensor] = None,
-                 conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
-                 conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
-                 workspace: Optional[torch.Tensor] = None, stream=None,
-                 checkpoints: Optional[torch.Tensor] = None, seq_segments: int = 0) -> torch.Tensor:
-    """Enqueue ssm_scan_fwd on the current stream; returns ``out``.
-
-    Shapes as in include/ssmscan.h.  ``out`` (same dtype as delta) and
-    ``last_state`` (float32, optional) are written in place; ``out`` is
-    allocated when not given.  With ``conv_weight`` the conv prologue computes
-    u from ``conv_x`` and ``u`` may be None.  ``checkpoints`` (float32,
-    (batch, dim, ceil(seqlen / 32), dstate), optional) receives the states the
-    backward starts its chunks from.  ``seq_segments`` (0: the library's
-    choice) asks for a sequence split into that many parallel segments.
-    """
+def _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_state, initial_state,
+               conv_x, conv_weight, conv_bias, conv_act, checkpoints, seq_segments):
+    """ssm_scan_args_t for the tensors (made contiguous where needed); returns
+    (args, out, tensors kept alive until the call is enqueued)."""
     delta = _dense(delta)
     io = _IO.get(delta.dtype)
     if io is None:
@@ -118,6 +102,35 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
         if tuple(checkpoints.shape) != want or checkpoints.dtype != torch.float32 or not checkpoints.is_contiguous():
             raise ValueError(f"checkpoints must be a contiguous float32 tensor of shape {want}")
         args.checkpoints = _ptr(checkpoints)
+    keep = (u, delta, A, B, C, D, z, delta_bias, initial_state, conv_x, conv_weight, conv_bias)
+    return args, out, keep
+
+
+def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
+                 B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                 delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                 last_state: Optional[torch.Tensor] = None,
+                 initial_state: Optional[torch.Tensor] = None,
+                 conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
+                 conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 checkpoints: Optional[torch.Tensor] = None, seq_segments: int = 0) -> torch.Tensor:
+    """Enqueue ssm_scan_fwd on the current stream; returns ``out``.
+
+    Shapes as in include/ssmscan.h.  ``out`` (same dtype as delta) and
+    ``last_state`` (float32, optional) are written in place; ``out`` is
+    allocated when not given.  With ``conv_weight`` the conv prologue computes
+    u from ``conv_x`` and ``u`` may be None.  ``checkpoints`` (float32,
+    (batch, dim, ceil(seqlen / 32), dstate), optional) receives the states the
+    backward starts its chunks from.  ``seq_segments`` (0: the library's
+    choice) asks for a sequence split into that many parallel segments.  The
+    scratch the plan needs is allocated here (torch) unless ``workspace`` is
+    given.
+    """
+    args, out, keep = _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_state,
+                                 initial_state, conv_x, conv_weight, conv_bias, conv_act, checkpoints,
+                                 seq_segments)
     L = _lib.lib()
     if workspace is None:
         need = ctypes.c_size_t(0)
@@ -127,6 +140,28 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
     if workspace is not None:
         args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     check(L.ssm_scan_fwd(ctypes.byref(args), _stream(delta.device, stream)))
+    return out
+
+
+def ssm_scan_fwd_noalloc(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
+                         B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                         z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                         delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                         last_state: Optional[torch.Tensor] = None,
+                         initial_state: Optional[torch.Tensor] = None,
+                         conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
+                         conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
+                         stream=None, checkpoints: Optional[torch.Tensor] = None,
+                         seq_segments: int = 0) -> torch.Tensor:
+    """Enqueue ssm_scan_fwd_noalloc: ssm_scan_fwd with the plan's scratch in
+    the library's built-in per-device buffer (nothing allocated for it).
+    ``out`` must be given: a missing output would be an allocation."""
+    if out is None:
+        raise ValueError("ssm_scan_fwd_noalloc needs a caller-allocated out")
+    args, out, keep = _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_state,
+                                 initial_state, conv_x, conv_weight, conv_bias, conv_act, checkpoints,
+                                 seq_segments)
+    check(_lib.lib().ssm_scan_fwd_noalloc(ctypes.byref(args), _stream(delta.device, stream)))
     return out
 
 

@@ -243,11 +243,11 @@ extern "C" int ssm_scan_workspace_size(const ssm_scan_args_t *a, size_t *bytes) 
   return SSM_OK;
 }
 
-extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
-  const int st = ssm_scan_validate(a);
-  if (st != SSM_OK) return st;
-  const Plan pl = make_plan(a, cu_count_cached());
-  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
+namespace {
+
+// The forward for a validated call and its plan, with `ws` as the scratch
+// (pl.ws_bytes of it, or none).
+int scan_fwd_run(const ssm_scan_args_t *a, const Plan &pl, void *ws, void *stream_ptr) {
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
   const int io = a->io_dtype;
@@ -270,7 +270,6 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
           (a->B_kind != SSM_BC_VARYING || aligned16(a->B)) && (a->C_kind != SSM_BC_VARYING || aligned16(a->C));
   p.xcd_swizzle = ((pl.nblocks - pl.hand_units) % 8 == 0);
 
-  void *ws = a->workspace;
   if (pl.nseg > 1) {
     float *wsf = static_cast<float *>(ws);
     p.ws_state = wsf;
@@ -308,6 +307,58 @@ extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
     if (e != hipSuccess) rc = hip_fail(e);
   }
   return rc;
+}
+
+}  // namespace
+
+// Scratch of ssm_scan_fwd_noalloc: one per device the library runs on, held
+// until the process ends.  Host code must never pass `scratch` itself to a
+// kernel (on the host it only names the symbol): its device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+int scratch_ptr(void **out) {
+  static std::mutex mu;
+  static void *ptrs[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return SSM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" int ssm_scan_fwd(const ssm_scan_args_t *a, void *stream_ptr) {
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  const Plan pl = make_plan(a, cu_count_cached());
+  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
+  return scan_fwd_run(a, pl, a->workspace, stream_ptr);
+}
+
+extern "C" int ssm_scan_fwd_noalloc(const ssm_scan_args_t *a, void *stream_ptr) {
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  const Plan pl = make_plan(a, cu_count_cached());
+  if (pl.ws_bytes > kNoAllocScratchBytes) return SSM_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    const int rc = scratch_ptr(&ws);
+    if (rc != SSM_OK) return rc;
+  }
+  return scan_fwd_run(a, pl, ws, stream_ptr);
 }
 
 extern "C" int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, void *out,

@@ -176,6 +176,7 @@ extern "C" const char *ssm_status_str(int status) {
     case SSM_ERR_UNSUPPORTED: return "unsupported argument (dtype, dstate > 16, conv width or cache length out of range, or enum value)";
     case SSM_ERR_HIP: return "HIP runtime error";
     case SSM_ERR_WORKSPACE: return "workspace smaller than required";
+    case SSM_ERR_SCRATCH: return "plan needs more scratch than the built-in no-allocation buffer holds";
     default: return "unknown status";
   }
 }

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_header_symbols():
 
 def test_status_strings():
     L = _lib.lib()
-    for code in range(6):
+    for code in range(7):
         assert L.ssm_status_str(code)
     assert L.ssm_status_str(99) == b"unknown status"
 
@@ -118,6 +118,22 @@ def test_missing_workspace_is_rejected_before_any_launch():
         assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
         a.workspace, a.workspace_bytes = FAKE, need.value - 1
         assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """ssm_scan_fwd_noalloc validates like ssm_scan_fwd and rejects a plan
+    whose scratch exceeds its built-in buffer with SSM_ERR_SCRATCH, before
+    any HIP call (this runs on a machine with no GPU)."""
+    L = _lib.lib()
+    assert L.ssm_scan_fwd_noalloc(None, None) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_fwd_noalloc(ctypes.byref(_good_args(delta=None)), None) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_fwd_noalloc(ctypes.byref(_good_args(dstate=33)), None) == _lib.SSM_ERR_UNSUPPORTED
+    big = _good_args(batch=1, dim=4096, seqlen=1 << 16, seq_segments=200)
+    need = ctypes.c_size_t(0)
+    assert L.ssm_scan_workspace_size(ctypes.byref(big), ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value > _lib.SSM_NOALLOC_SCRATCH_BYTES
+    assert L.ssm_scan_fwd_noalloc(ctypes.byref(big), None) == _lib.SSM_ERR_SCRATCH
+    assert b"no-allocation" in L.ssm_status_str(_lib.SSM_ERR_SCRATCH)
 
 
 def test_conv_validation():

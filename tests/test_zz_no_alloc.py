@@ -1,0 +1,53 @@
+"""ssm_scan_fwd_noalloc (the forward for callers that cannot allocate: its
+scratch is the library's built-in per-device buffer) against ssm_scan_fwd on
+the same inputs, through the C ABI: two calls in a row, the second on a
+smaller input, for each plan that uses scratch (parallel sequence segments,
+hand-over parts) and for one that uses none.  The two entry points run the
+same kernels with the same plan, so the outputs agree bit for bit, which is
+inside the parity bar (|a - b| <= tol (1 + |b|)) a fortiori."""
+import numpy as np
+import pytest
+
+from state_space_model_scan_amd.inputs import BF16, WORKLOADS, make_inputs
+from tests.harness import TOL, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _call(fn, w, t, **kw):
+    import torch
+    io = w.io_dtype
+    delta = to_dev(t["delta"], io)
+    out = torch.full_like(delta, float("nan"))
+    last = torch.full((w.batch, w.dim, w.dstate), float("nan"), dtype=torch.float32, device="cuda")
+    fn(to_dev(t["u"], io), delta, to_dev(t["A"], param=True), to_dev(t["B"], io), to_dev(t["C"], io),
+       to_dev(t["D"], param=True), to_dev(t["z"], io), to_dev(t["delta_bias"], param=True), w.softplus,
+       out=out, last_state=last, **kw)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy().astype(np.float64), last.cpu().numpy().astype(np.float64))
+
+
+# (larger, smaller) input pairs per plan, called back to back
+PAIRS = {
+    "segments": (dict(dim=256, seqlen=8192), dict(dim=64, seqlen=4096)),
+    "handover": (dict(batch=2, dim=10240, seqlen=200), dict(batch=2, dim=10240, seqlen=100)),
+    "whole": (dict(batch=2, dim=16384, seqlen=128), dict(batch=2, dim=16384, seqlen=64)),
+}
+
+
+@pytest.mark.parametrize("plan", list(PAIRS))
+def test_noalloc_matches_scan_fwd(plan):
+    from state_space_model_scan_amd import binding
+    for k, shape in enumerate(PAIRS[plan]):
+        w = WORKLOADS["longseq"].scaled(io_dtype=BF16 if plan == "whole" else WORKLOADS["longseq"].io_dtype,
+                                        has_z=True, **shape)
+        t = make_inputs(w, seed=40 + k)
+        log(f"[noalloc] {plan} call {k + 1}: {w}")
+        ref, ref_last = _call(binding.ssm_scan_fwd, w, t)
+        got, got_last = _call(binding.ssm_scan_fwd_noalloc, w, t)
+        assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_last))
+        tol = TOL[w.io_dtype]
+        assert np.max(np.abs(got - ref) / (1.0 + np.abs(ref))) <= tol
+        assert np.max(np.abs(got_last - ref_last) / (1.0 + np.abs(ref_last))) <= 1e-4
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(got_last, ref_last)
