@@ -64,6 +64,10 @@ def _load():
             p, p, p, i32, i32,
             p, i64, p, p, i32]
         lib.oracle_selective_scan.restype = i32
+        lib.oracle_selective_scan_f32_floor.argtypes = [
+            i64, i64, i64, i64, i64, i32,
+            p, p, p, p, i32, p, i32, p, p, p, i32, p, p, i32]
+        lib.oracle_selective_scan_f32_floor.restype = i32
         lib.oracle_causal_conv1d.argtypes = [
             i64, i64, i64, i32, i32, p, p, p, i32, p, i64, p, i32]
         lib.oracle_causal_conv1d.restype = i32
@@ -185,6 +189,31 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(rows_a), nrows, _ptr(out), _ptr(last), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_selective_scan failed with status {rc}")
+    return out, last
+
+
+def selective_scan_f32_floor(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                             delta_softplus=False, *, io_dtype=F32, ngroups=1,
+                             B_kind=BC_VARYING, C_kind=BC_VARYING, nthreads=0):
+    """The selective scan evaluated in binary32, in order (see ``ssm_oracle.c``):
+    not a reference, but the rounding floor of a plain fp32 evaluation, used
+    to set the bar of inputs no fp32 evaluation can meet at fp32 tolerance.
+    Returns (out (batch*dim, seqlen), last_state (batch*dim, dstate)) float64."""
+    lib = _load()
+    delta = _io(delta, io_dtype)
+    batch, dim, seqlen = delta.shape
+    A = _f32(A)
+    dstate = A.shape[1]
+    u, B, C, z = _io(u, io_dtype), _io(B, io_dtype), _io(C, io_dtype), _io(z, io_dtype)
+    D, delta_bias = _f32(D), _f32(delta_bias)
+    out = np.empty((batch * dim, seqlen), dtype=np.float64)
+    last = np.empty((batch * dim, dstate), dtype=np.float64)
+    rc = lib.oracle_selective_scan_f32_floor(
+        batch, dim, seqlen, dstate, ngroups, io_dtype, _ptr(u), _ptr(delta), _ptr(A),
+        _ptr(B), B_kind, _ptr(C), C_kind, _ptr(D), _ptr(delta_bias), _ptr(z),
+        int(bool(delta_softplus)), _ptr(out), _ptr(last), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan_f32_floor failed with status {rc}")
     return out, last
 
 

@@ -334,6 +334,76 @@ int oracle_selective_scan(int64_t batch, int64_t dim, int64_t seqlen,
     return failed ? 5 : 0;
 }
 
+/* ---- the same definition in binary32: the fp32 rounding floor ------------ */
+
+/* The scan of oracle_selective_scan (no conv prologue, no initial state)
+ * evaluated in IEEE binary32 arithmetic, step by step in the same order:
+ *   dt = softplus(delta + bias) as max(v,0) + log1p(exp(-|v|)) in float,
+ *   x[s] = expf(dt*A) * x[s] + dt*B*u,  y = sum_s C*x[s] (s ascending),
+ *   y += D*u,  y *= z / (1 + expf(-z)).
+ * It is NOT a reference: it measures how far a plain in-order fp32
+ * evaluation of this recurrence lands from the float64 result, which sets
+ * the bar of inputs whose conditioning no fp32 evaluation can meet at the
+ * fp32 tolerance (a decay within a few ulp of 1 for 65536 steps).
+ * out: (batch*dim, seqlen) double (the float results widened); last_state:
+ * (batch*dim, dstate) double.  Returns 0, 1 (null pointer), 2 (bad shape). */
+int oracle_selective_scan_f32_floor(int64_t batch, int64_t dim, int64_t seqlen,
+                                    int64_t dstate, int64_t ngroups, int io_dtype,
+                                    const void *u, const void *delta, const float *A,
+                                    const void *B, int B_kind, const void *C, int C_kind,
+                                    const float *D, const float *delta_bias, const void *z,
+                                    int delta_softplus, double *out, double *last_state,
+                                    int nthreads) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!u || !delta || !A || !B || !C || !out || !last_state) return 1;
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, D, delta_bias, z, delta_softplus,
+                          NULL, NULL, NULL, NULL, 0, 0};
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel reduction(|:failed)
+#endif
+    {
+        float *x = (float *)malloc(sizeof(float) * (size_t)dstate);
+        if (!x) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t row = 0; row < batch * dim; ++row) {
+                const int64_t b = row / dim, d = row % dim, base = row * seqlen;
+                for (int64_t s = 0; s < dstate; ++s) x[s] = 0.0f;
+                for (int64_t t = 0; t < seqlen; ++t) {
+                    float dt = (float)load_io(delta, io_dtype, base + t);
+                    if (delta_bias) dt += delta_bias[d];
+                    if (delta_softplus) dt = fmaxf(dt, 0.0f) + log1pf(expf(-fabsf(dt)));
+                    const float ut = (float)load_io(u, io_dtype, base + t);
+                    float y = 0.0f;
+                    for (int64_t s = 0; s < dstate; ++s) {
+                        const float dA = expf(dt * A[d * dstate + s]);
+                        const float Bv = (float)bc_at(B, B_kind, io_dtype, &a, b, d, s, t);
+                        x[s] = dA * x[s] + dt * Bv * ut;
+                        y += (float)bc_at(C, C_kind, io_dtype, &a, b, d, s, t) * x[s];
+                    }
+                    if (D) y += D[d] * ut;
+                    if (z) {
+                        const float zt = (float)load_io(z, io_dtype, base + t);
+                        y *= zt / (1.0f + expf(-zt));
+                    }
+                    out[base + t] = (double)y;
+                }
+                for (int64_t s = 0; s < dstate; ++s) last_state[row * dstate + s] = (double)x[s];
+            }
+        }
+        free(x);
+    }
+    (void)nthreads;
+    return failed ? 5 : 0;
+}
+
 /* ---- selective scan with complex A -------------------------------------- */
 
 /* The guide's section 4.1 says A (dim, dstate) may be real or complex and

@@ -1,9 +1,10 @@
 """Shared helpers of the GPU parity tests: move seeded inputs to the device,
 run the HIP path through the C ABI, run the oracle on the same bits, compare.
 
-Tolerance (per element, for out and last_state):
-    |gpu - ref| <= tol * (1 + |ref|),  tol = 1e-4 for fp32 io, 2e-2 for bf16 io,
-    5e-3 for fp16 io.
+Tolerance (per element): |gpu - ref| <= tol * (1 + |ref|), with
+  out:        tol = 1e-4 for fp32 io, 2e-2 for bf16 io, 5e-3 for fp16 io;
+  last_state: tol = 1e-4 in every io dtype -- the state is fp32 throughout
+              and is never rounded to the io dtype.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ from state_space_model_scan_amd.inputs import BF16, F16, F32, Workload
 # fp16: ten half-units in the last place of binary16 (2^-11), as 2e-2 is
 # about ten for bf16 (2^-9)
 TOL = {F32: 1e-4, BF16: 2e-2, F16: 5e-3}
+# the fp32 state, in every io dtype
+TOL_STATE = 1e-4
 
 
 def log(msg: str) -> None:
@@ -87,14 +90,87 @@ def max_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(gpu - ref) / (1.0 + np.abs(ref))))
 
 
-def check(w: Workload, gpu, ref, last_gpu=None, last_ref=None, what=""):
+def _io_values(a: np.ndarray, io_dtype: int) -> np.ndarray:
+    """Stored io bits as float64 values."""
+    if a.dtype == np.uint16:
+        if io_dtype == BF16:
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.view(np.float16).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def conv_flip_slack(w: Workload, t: Dict[str, np.ndarray]) -> Optional[np.ndarray]:
+    """Allowance on last_state for the fused conv prologue with a 16-bit io
+    dtype, (batch*dim, dstate) float64, or None when there is nothing to allow.
+
+    The prologue rounds u = silu(conv(x)) to the io dtype: a rounding
+    decision taken by floating point.  The kernel takes it from an fp32
+    evaluation, the oracle from float64; where the float64 value lies within
+    the fp32 evaluation's error bound of a rounding midpoint, either rounding
+    is a correct one, and they differ by one io ulp.  The bound used for the
+    fp32 evaluation is generous: 12 eps32 times the sum of the conv terms'
+    magnitudes (an FMA chain), scaled by silu's slope (at most 1.1), plus
+    12 eps32 of the output (exp2, reciprocal and product).  last_state is
+    linear in u, x_T = sum_t prod_{tau > t} dA_tau * delta'_t B_t u_t + ...,
+    so a flip at timestep t moves x_T[s] by at most
+        |delta'_t B_t[s]| * ulp(u_t) * exp(A[d,s] * sum_{tau > t} delta'_tau);
+    the allowance is that sum over the ambiguous timesteps of each row.
+    Everything here comes from the inputs and the oracle, none from the GPU."""
+    if not w.conv or w.io_dtype == F32:
+        return None
+    mant = 8 if w.io_dtype == BF16 else 11                 # significant bits of the io dtype
+    eps32 = 2.0 ** -24
+    rows_all, l, n = w.batch * w.dim, w.seqlen, w.dstate
+    slack = np.zeros((rows_all, n))
+    xbits = t["conv_x"].reshape(rows_all, l)
+    dbits = t["delta"].reshape(rows_all, l)
+    for r0 in range(0, rows_all, 2048):                      # blocks of rows bound the memory
+        rr = np.arange(r0, min(rows_all, r0 + 2048), dtype=np.int64)
+        d_of = rr % w.dim
+        v = orc.causal_conv1d(t["conv_x"], t["conv_weight"], t["conv_bias"], orc.ACT_SILU,
+                              io_dtype=w.io_dtype, rows=rr, nthreads=16)   # unrounded
+        x = _io_values(xbits[rr], w.io_dtype)
+        wt = np.abs(t["conv_weight"].astype(np.float64))[d_of]            # (k, 4)
+        mag = np.repeat(np.abs(t["conv_bias"].astype(np.float64))[d_of][:, None], l, axis=1)
+        for k in range(4):
+            sh = 3 - k
+            mag[:, sh:] += wt[:, k:k + 1] * np.abs(x[:, :l - sh])
+        err = 1.1 * 12 * eps32 * mag + 12 * eps32 * np.abs(v)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 1e-300))) - (mant - 1))
+        u = np.round(v / ulp) * ulp                          # round to nearest, ties to even
+        amb = (ulp / 2 - np.abs(v - u)) <= err
+        ri, ti = np.nonzero(amb)
+        if ri.size == 0:
+            continue
+        dvar = _io_values(dbits[rr], w.io_dtype) + t["delta_bias"].astype(np.float64)[d_of][:, None]
+        dt = np.logaddexp(0.0, dvar) if w.softplus else dvar
+        suffix = dt.sum(1, keepdims=True) - np.cumsum(dt, axis=1)     # sum over tau > t
+        rows = rr[ri]
+        d_idx, b_idx = rows % w.dim, rows // w.dim
+        if t["B"].ndim == 2:
+            Bv = _io_values(t["B"], w.io_dtype)[d_idx]                       # (k, n)
+        else:
+            g = d_idx // (w.dim // t["B"].shape[1])
+            Bv = _io_values(t["B"], w.io_dtype)[b_idx, g, :, ti]            # (k, n)
+        A = t["A"].astype(np.float64)[d_idx]                                  # (k, n)
+        contrib = (np.abs(dt[ri, ti] * ulp[ri, ti])[:, None] * np.abs(Bv)
+                   * np.exp(A * suffix[ri, ti][:, None]))
+        np.add.at(slack, rows, contrib)
+    return slack
+
+
+def check(w: Workload, gpu, ref, last_gpu=None, last_ref=None, what="", last_slack=None):
+    """Per-element bars; last_slack (same shape as last_state) adds an
+    allowance where a rounding decision is not determined (conv_flip_slack)."""
     tol = TOL[w.io_dtype]
     e = max_err(gpu, ref)
     assert e <= tol, f"{what} out: max normalised error {e:.3e} > {tol:.0e}"
     if last_gpu is not None:
-        # the state is fp32 in every workload: hold last_state to the tighter
-        # bound when the io is fp32, and to the io bound otherwise
-        el = max_err(last_gpu, last_ref)
-        assert el <= tol, f"{what} last_state: max normalised error {el:.3e} > {tol:.0e}"
+        if last_slack is None:
+            el = max_err(last_gpu, last_ref)
+        else:
+            assert np.all(np.isfinite(last_gpu)), f"{what} last_state not finite"
+            el = float(np.max(np.maximum(np.abs(last_gpu - last_ref) - last_slack, 0.0) / (1.0 + np.abs(last_ref))))
+        assert el <= TOL_STATE, f"{what} last_state: max normalised error {el:.3e} > {TOL_STATE:.0e}"
         return e, el
     return e, None

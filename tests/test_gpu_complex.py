@@ -2,8 +2,9 @@
 page's section 4.1: A may be real or complex) against the float64 oracle's
 complex scan, element by element, on the same seeded inputs.
 
-Tolerance per element, for out and last_state (both pair components):
-|gpu - ref| <= tol * (1 + |ref|), tol = 1e-4 fp32 io, 2e-2 bf16, 5e-3 fp16.
+Tolerance per element (both pair components): |gpu - ref| <= tol * (1 + |ref|),
+for out tol = 1e-4 fp32 io, 2e-2 bf16, 5e-3 fp16; for last_state (fp32 in
+every io dtype) 1e-4.
 """
 import numpy as np
 import pytest
@@ -11,7 +12,7 @@ import pytest
 from oracle import oracle as orc
 from state_space_model_scan_amd.inputs import (BF16, COMPLEX_WORKLOADS, F16, F32, make_complex_inputs,
                                                sample_rows)
-from tests.harness import TOL, log, max_err, to_dev
+from tests.harness import TOL, TOL_STATE, log, max_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +54,7 @@ def _check(w, gpu, ref, what):
     assert e <= tol, f"{what} out: max normalised error {e:.3e} > {tol:.0e}"
     if gpu[1] is not None:
         el = max_err(gpu[1], ref[1])
-        assert el <= tol, f"{what} last_state: max normalised error {el:.3e} > {tol:.0e}"
+        assert el <= TOL_STATE, f"{what} last_state: max normalised error {el:.3e} > {TOL_STATE:.0e}"
         return e, el
     return e, None
 

@@ -1,9 +1,10 @@
 """GPU parity of the single-step decode entry points (ssm_state_update and
 causal_conv1d_update) against the float64 oracle, through the C ABI.
 
-Bars: the updated fp32 state and the output within the io tolerance of the
-harness (|gpu - ref| <= tol * (1 + |ref|), tol 1e-4 fp32 io, 2e-2 bf16 io);
-the conv cache after an update bit-exact (it holds raw inputs).
+Bars (|gpu - ref| <= tol * (1 + |ref|)): the output within the io tolerance
+(tol 1e-4 fp32 io, 2e-2 bf16 io), the updated state -- fp32 in every io
+dtype -- within 1e-4; the conv cache after an update bit-exact (it holds raw
+inputs).
 """
 import numpy as np
 import pytest
@@ -11,7 +12,7 @@ import pytest
 from oracle import oracle as orc
 from state_space_model_scan_amd.inputs import (BF16, F16, DECODE_WORKLOADS, F32, WORKLOADS,
                                                make_decode_inputs, make_inputs)
-from tests.harness import TOL, log, max_err, to_dev
+from tests.harness import TOL, TOL_STATE, log, max_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +56,7 @@ def _check_su(w, t, what, **kw):
     tol = TOL[w.io_dtype]
     eo, es = max_err(out, ref_out), max_err(st, ref_st)
     assert eo <= tol, f"{what} out: {eo:.3e} > {tol:.0e}"
-    assert es <= tol, f"{what} state: {es:.3e} > {tol:.0e}"
+    assert es <= TOL_STATE, f"{what} state: {es:.3e} > {TOL_STATE:.0e}"
 
 
 @pytest.mark.parametrize("name", ["decode_tiny"])
@@ -125,7 +126,7 @@ def test_state_update_chain_matches_oracle_scan(wl):
     got = np.stack(outs, axis=-1)
     tol = TOL[io]
     assert max_err(got, ref_out) <= tol
-    assert max_err(state.cpu().numpy().astype(np.float64), ref_last.reshape(init.shape)) <= tol
+    assert max_err(state.cpu().numpy().astype(np.float64), ref_last.reshape(init.shape)) <= TOL_STATE
 
 
 # --------------------------------------------------------------------------
@@ -222,4 +223,4 @@ def test_decode_pipeline_matches_fused_scan(ring):
     torch.cuda.synchronize()
     got = np.stack(outs, axis=-1)
     assert max_err(got, ref_out) <= TOL[io]
-    assert max_err(state.cpu().numpy().astype(np.float64), ref_last.reshape(w.batch, w.dim, w.dstate)) <= TOL[io]
+    assert max_err(state.cpu().numpy().astype(np.float64), ref_last.reshape(w.batch, w.dim, w.dstate)) <= TOL_STATE

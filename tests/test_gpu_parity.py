@@ -1,20 +1,20 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle, element
 by element, on the same seeded input bits.
 
-Bar (per element, out and last_state): |gpu - ref| <= tol * (1 + |ref|) with
-tol = 1e-4 for fp32 io and 2e-2 for bf16 io, the state being fp32 throughout.
-Small shapes are compared on every row; the full workload sizes -- in the launch
-configuration the benchmark times -- on a fixed spread of sampled rows that
-the oracle computes one by one.
+Bar (per element): |gpu - ref| <= tol * (1 + |ref|) with, for out, tol = 1e-4
+for fp32 io and 2e-2 for bf16 io, and for last_state 1e-4 in every io dtype
+(the state is fp32 throughout).  Every element of out and last_state is
+compared, at reduced sizes and at the full workload sizes in the launch
+configuration the benchmark times (the oracle runs multi-threaded over rows).
 """
 import zlib
 
 import numpy as np
 import pytest
 
-from state_space_model_scan_amd.inputs import BF16, F32, WORKLOADS, make_inputs, sample_rows
+from state_space_model_scan_amd.inputs import BF16, F32, WORKLOADS, make_inputs
 from oracle import oracle as orc
-from tests.harness import TOL, check, log, run_gpu, run_oracle
+from tests.harness import TOL, check, conv_flip_slack, log, max_err, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -34,20 +34,18 @@ def test_workload_small_all_rows(name):
     t = make_inputs(w)
     out, last = run_gpu(w, t)
     ref, ref_last = run_oracle(w, t)
-    check(w, out, ref, last, ref_last, what=name)
+    check(w, out, ref, last, ref_last, what=name, last_slack=conv_flip_slack(w, t))
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_workload_full_size_sampled_rows(name):
+def test_workload_full_size_all_rows(name):
+    """Every element of out and last_state at the workload's full size."""
     w = WORKLOADS[name]
     log(f"[parity] full {name} {w}")
     t = make_inputs(w)
     out, last = run_gpu(w, t)
-    rows = sample_rows(w, 24)
-    ref, ref_last = run_oracle(w, t, rows=rows)
-    check(w, out[rows], ref, last[rows], ref_last, what=name)
-    # every element was written (outputs were NaN-poisoned) and is finite
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(last))
+    ref, ref_last = run_oracle(w, t, nthreads=16)
+    check(w, out, ref, last, ref_last, what=name, last_slack=conv_flip_slack(w, t))
 
 
 def _case(base="tiny", **kw):
@@ -94,7 +92,7 @@ def test_edge_cases(name):
     t = make_inputs(w, seed=zlib.crc32(name.encode()) % 1000)
     out, last = run_gpu(w, t)
     ref, ref_last = run_oracle(w, t)
-    check(w, out, ref, last, ref_last, what=name)
+    check(w, out, ref, last, ref_last, what=name, last_slack=conv_flip_slack(w, t))
 
 
 def test_mixed_bc_kinds():
@@ -178,46 +176,36 @@ def test_handover_plan_initial_state():
     check(w, out, ref, last, ref_last, what="handover initial_state")
 
 
-def _contraction_magnitude(w, t):
-    """sum_s |C_t[s] x_t[s]| per (row, t), from a float64 recurrence in numpy:
-    the scale of the terms whose sum is y_t, used to bound fp32 rounding."""
-    b, d, l, n = w.batch, w.dim, w.seqlen, w.dstate
-    mag = np.zeros((b * d, l))
-    A = t["A"].astype(np.float64)
-    for bi in range(b):
-        u = t["u"][bi].astype(np.float64)
-        v = t["delta"][bi].astype(np.float64) + t["delta_bias"].astype(np.float64)[:, None]
-        dt = np.logaddexp(0.0, v)
-        B = t["B"][bi, 0].astype(np.float64)
-        C = t["C"][bi, 0].astype(np.float64)
-        x = np.zeros((d, n))
-        for s in range(l):
-            x = np.exp(dt[:, s, None] * A) * x + (dt[:, s] * u[:, s])[:, None] * B[None, :, s]
-            mag[bi * d:(bi + 1) * d, s] = np.abs(x * C[None, :, s]).sum(1)
-    return mag
-
-
 def test_slow_decay_carry_stress():
-    """A near zero decays slowly, so a dropped or wrong segment carry would show
-    as an O(1) error: the long-sequence shape at reduced width, A = -1e-4 (s+1).
+    """A near zero decays slowly, so a dropped or wrong carry between
+    sequence segments would show as an O(1) error: the long-sequence workload
+    at its full width and length (its real segment plan), with
+    A = -1e-4 (s+1).
 
-    Here dA is within a few ulp of 1 for 65536 steps, so fp32 rounding grows
-    with the sequence and y = C.x cancels: a plain sequential fp32 recurrence on
-    these inputs reaches 1.3e-3 in |err| / (1 + |ref|).  The bar for this case
-    is therefore taken relative to the size of the summed terms:
-    |err| <= 1e-4 * (1 + sum_s |C_s x_s|) for out (the sequential fp32
-    recurrence reaches 4e-5) and 1e-3 * (1 + |x|) for last_state."""
-    w = WORKLOADS["longseq"].scaled(dim=64)
+    There dA is within a few ulp of 1 for 65536 steps and fp32 rounding of
+    the state accumulates, so no fp32 evaluation meets the fp32 bar (1e-4):
+    the plain in-order binary32 evaluation of the same definition
+    (oracle.selective_scan_f32_floor) lands about 2e-3 from the float64
+    result on out and 2e-4 on last_state.  The bar here is therefore twice
+    that floor, measured on the same inputs in the test (and never below
+    the fp32 bar): an error of that size is rounding, a broken carry is
+    orders of magnitude larger."""
+    w = WORKLOADS["longseq"]
     t = make_inputs(w)
     t["A"] = (-1e-4 * (np.arange(w.dstate, dtype=np.float32) + 1))[None, :].repeat(w.dim, 0).astype(np.float32)
-    log("[parity] slow-decay carry stress")
+    log("[parity] slow-decay carry stress, full longseq shape")
     out, last = run_gpu(w, t)
-    ref, ref_last = run_oracle(w, t)
-    mag = _contraction_magnitude(w, t)
-    e_out = np.max(np.abs(out - ref) / (1.0 + mag))
-    e_last = np.max(np.abs(last - ref_last) / (1.0 + np.abs(ref_last)))
-    assert e_out <= 1e-4, f"out error {e_out:.3e} relative to the summed terms"
-    assert e_last <= 1e-3, f"last_state error {e_last:.3e}"
+    ref, ref_last = run_oracle(w, t, nthreads=16)
+    f32, f32_last = orc.selective_scan_f32_floor(
+        t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], w.softplus,
+        io_dtype=w.io_dtype, nthreads=16)
+    floor_out = max_err(f32, ref)
+    floor_last = max_err(f32_last, ref_last)
+    e_out, e_last = max_err(out, ref), max_err(last, ref_last)
+    log(f"[parity] slow decay: gpu out {e_out:.3e} last {e_last:.3e}; "
+        f"fp32 in-order floor out {floor_out:.3e} last {floor_last:.3e}")
+    assert e_out <= max(1e-4, 2 * floor_out), f"out error {e_out:.3e}, fp32 floor {floor_out:.3e}"
+    assert e_last <= max(1e-4, 2 * floor_last), f"last_state error {e_last:.3e}, fp32 floor {floor_last:.3e}"
 
 
 def test_deterministic():

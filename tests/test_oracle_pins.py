@@ -492,3 +492,27 @@ def test_conv_prologue_composition():
         sep, sep_last = _run(dict(ii, u=u), io_dtype=io)
         np.testing.assert_array_equal(fused, sep)
         np.testing.assert_array_equal(fused_last, sep_last)
+
+
+def test_f32_floor_is_the_same_definition():
+    """oracle.selective_scan_f32_floor (the binary32 in-order evaluation that
+    sets the slow-decay bar) computes the oracle's definition: on well
+    conditioned inputs it agrees with the float64 oracle to fp32 rounding,
+    with and without softplus, z and D, for time-varying and fixed B/C."""
+    import numpy as np
+    from state_space_model_scan_amd.inputs import WORKLOADS, make_inputs
+    for kw in (dict(), dict(softplus=False, delta_mean=0.1, delta_std=0.05),
+               dict(has_z=False, has_D=False), dict(bc_kind="fixed", dstate=8)):
+        w = WORKLOADS["tiny"].scaled(dim=24, seqlen=200, **kw)
+        t = make_inputs(w)
+        bk = orc.BC_FIXED if t["B"].ndim == 2 else orc.BC_VARYING
+        ref, ref_last = orc.selective_scan(
+            t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], w.softplus,
+            io_dtype=w.io_dtype, B_kind=bk, C_kind=bk)
+        f, fl = orc.selective_scan_f32_floor(
+            t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], w.softplus,
+            io_dtype=w.io_dtype, B_kind=bk, C_kind=bk)
+        assert np.max(np.abs(f - ref) / (1 + np.abs(ref))) < 2e-5, kw
+        assert np.max(np.abs(fl - ref_last) / (1 + np.abs(ref_last))) < 2e-5, kw
+        # and it is a float32 evaluation: not the float64 result itself
+        assert not np.array_equal(f, ref)
