@@ -385,7 +385,7 @@ int oracle_selective_scan_f32_floor(int64_t batch, int64_t dim, int64_t seqlen,
                     for (int64_t s = 0; s < dstate; ++s) {
                         const float dA = expf(dt * A[d * dstate + s]);
                         const float Bv = (float)bc_at(B, B_kind, io_dtype, &a, b, d, s, t);
-                        x[s] = dA * x[s] + dt * Bv * ut;
+                        x[s] = dA * x[s] + (dt * Bv) * ut;     /* the oracle's order, in float */
                         y += (float)bc_at(C, C_kind, io_dtype, &a, b, d, s, t) * x[s];
                     }
                     if (D) y += D[d] * ut;
