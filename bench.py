@@ -11,16 +11,17 @@ one JSON line.
 Default workload: mamba2p8b (b=8, d=5120, l=2048, n=16, g=4, bf16 io, fp32
 state), the Mamba-2.8B-shaped layer the throughput target is quoted on.
 
-Roofline of the scan kernel (the only kernel of that workload):
-  * alu: algorithmic fp32 VALU operations per launch / measured launch time,
-    against 78.6 T lane-ops/s (256 CUs x 128 fp32 lanes x 2.4 GHz, i.e. the
-    157.3 TFLOP/s vector figure with an FMA counted once).  The method needs,
-    per (timestep, state), 4 plain ops (delta'*A, delta'u*B, state FMA, C.x FMA)
-    and one exp; per element 10 plain ops and 4 transcendentals (softplus:
-    exp, log; silu: exp, rcp).  A transcendental issues at a quarter of the
-    plain rate, so it is weighted 4: ops = E * (8 n + 26).
-  * hbm: algorithmic bytes (every input read once, every output written once)
-    / launch time, against 8 TB/s.
+Roofline of the scan kernel (the only kernel of that workload), the metric's
+own: bound "hbm", achieved = algorithmic bytes (every input read once, every
+output written once) / launch time, against 8 TB/s.  The ALU figures sit
+beside it as flat keys (alu_*), from the rates `--microbench` measures:
+  * one plain fp32 VALU wave-instruction per clock per compute unit (4 SIMDs
+    x 16 lanes; the build turns packed FP32 off), so the peak is 256 CUs x 64
+    lanes x 2.4 GHz = 39.3 T lane-ops/s;
+  * v_exp_f32 (and log, rcp) at half that rate, so a transcendental weighs 2.
+  The method needs, per (timestep, state), 4 plain ops (delta'*A, delta'u*B,
+  state FMA, C.x FMA) and one exp; per element 10 plain ops and 4
+  transcendentals (softplus: exp, log; silu: exp, rcp): ops = E * (6 n + 18).
 The launch time is measured live with HIP events on the stream the kernel runs
 on.  `traffic` (HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE,
 scaled by the same counters on a copy of known size) is read from
@@ -29,9 +30,9 @@ kernel source, else null.
 
 cpu_baseline: the float64 oracle (test infrastructure) timed on this host's
 cores over a bounded sample of the workload's rows, scaled to elements/s,
-with a single-thread figure on a slice of those rows beside it.  After the
-timed steps, 20 more launches each follow a 512 MiB write that evicts the
-caches (outside their timed pair): roofline.kernel_avg_ms_cold_caches.
+with a single-thread figure on a slice of those rows beside it.  Before the
+warm-up, 20 launches each follow a 512 MiB write that evicts the caches
+(outside their timed pair): roofline.kernel_avg_ms_cold_caches.
 config.inputs_sha256 digests every input tensor.
 
 Standalone conv (--conv): a step is one causal_conv1d_fwd (width 4, silu) on
@@ -40,8 +41,8 @@ plus the weights).
 
 Complex-A workloads (--workload mamba2p8b_complex): a step is one
 ssm_scan_fwd_complex call (complex A, B and C; real u, delta, z, out).  The
-value is elements/s; the roofline is ALU with 25 weighted ops per (timestep,
-state) -- 13 plain ops and exp2, sine and cosine weighted 4 -- plus the 26 per
+value is elements/s; the roofline is ALU with 19 weighted ops per (timestep,
+state) -- 13 plain ops and exp2, sine and cosine weighted 2 -- plus the 18 per
 element of the real scan, and the HBM rate beside it.
 
 Decode workloads (--workload decode2p8b): a step is one decode step of one
@@ -83,7 +84,20 @@ import numpy as np  # noqa: E402
 
 METRIC = "selective-scan fwd elements/s (b·d·l) and HBM GB/s as % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
-ALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12       # 78.64 T fp32 lane-ops/s
+# one plain fp32 VALU wave-instruction per clock per CU (measured 0.94 at 8
+# waves per SIMD by --microbench; packed FP32 is off): 39.32 T lane-ops/s
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+TRANS_WEIGHT = 2     # v_exp_f32 / v_log_f32 / v_rcp_f32 issue at half the plain rate (--microbench)
+
+
+def io_bytes(io_dtype: int) -> int:
+    """Bytes of one io element: fp32 4, bf16 and fp16 2."""
+    return 4 if io_dtype == 0 else 2
+
+
+def dtype_label(io_dtype: int) -> str:
+    """io dtype and arithmetic: the state and every operation are fp32."""
+    return {0: "fp32", 1: "bf16-io/fp32", 2: "fp16-io/fp32"}[io_dtype]
 CSRC = os.path.join(ROOT, "state_space_model_scan_amd", "csrc")
 KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip", "ssm_scan.hip")
 DECODE_SRCS = ("decode.hip", "device_util.h")
@@ -97,7 +111,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def algorithmic_bytes(w) -> int:
     """Every input read once, every output written once (the fused minimum for
     the conv workload: the conv input replaces u, u never touches memory)."""
-    es = 2 if w.io_dtype == 1 else 4
+    es = io_bytes(w.io_dtype)
     E = w.elements
     n = w.dstate
     io_tensors = 2 + (1 if w.has_z else 0) + 1          # u or conv x, delta, z, out
@@ -111,7 +125,9 @@ def algorithmic_bytes(w) -> int:
 
 
 def algorithmic_alu_ops(w) -> float:
-    return float(w.elements) * (8 * w.dstate + 26)
+    """Per (timestep, state) 4 plain + 1 exp, per element 10 plain + 4
+    transcendentals; a transcendental weighs TRANS_WEIGHT plain slots."""
+    return float(w.elements) * ((4 + TRANS_WEIGHT) * w.dstate + 10 + 4 * TRANS_WEIGHT)
 
 
 def kernel_sha(srcs=KERNEL_SRCS) -> str:
@@ -132,7 +148,7 @@ def load_traffic(name: str, srcs=KERNEL_SRCS):
 
 
 def decode_state_update_bytes(w) -> int:
-    es = 2 if w.io_dtype == 1 else 4
+    es = io_bytes(w.io_dtype)
     bd = w.batch * w.dim
     state = 2 * bd * w.dstate * 4
     vecs = (3 + (1 if w.has_z else 0)) * bd * es            # x, dt, out (+ z)
@@ -142,7 +158,7 @@ def decode_state_update_bytes(w) -> int:
 
 
 def decode_conv_update_bytes(w) -> int:
-    es = 2 if w.io_dtype == 1 else 4
+    es = io_bytes(w.io_dtype)
     bd = w.batch * w.dim
     return (2 * bd * w.conv_tokens * es + 2 * bd * w.conv_state_len * es
             + w.dim * w.conv_width * 4 + w.dim * 4)
@@ -277,10 +293,24 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    stream = torch.cuda.current_stream()
+    # launches from cold caches: each after a 512 MiB write (outside the timed
+    # pair) that evicts L2 and the last-level cache
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold_ms = []
+    for i in range(20):
+        evict.fill_(i & 0xff)
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record(stream)
+        step()
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(s_ev.elapsed_time(e_ev))
+    del evict
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -296,20 +326,6 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     elems = w.elements
     value = elems * args.steps / wall
-
-    # the same launches with the caches evicted before each (a 512 MiB write
-    # outside the timed pair): the launch time from cold L2 and last-level cache
-    evict = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold_ms = []
-    for i in range(min(args.steps, 20)):
-        evict.fill_(i & 0xff)
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record(stream)
-        step()
-        e_ev.record(stream)
-        torch.cuda.synchronize()
-        cold_ms.append(s_ev.elapsed_time(e_ev))
-    del evict
 
     abytes = algorithmic_bytes(w)
     aops = algorithmic_alu_ops(w)
@@ -327,29 +343,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype_label(io),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} "
-                        f"B/C {w.bc_kind}, {'bf16' if io == BF16 else 'fp32'} io, fp32 state"
-                        f"{', conv prologue' if w.conv else ''}{', z gate' if w.has_z else ''}",
-            "io_dtype": "bf16" if io == BF16 else "fp32",
+                        f"B/C {w.bc_kind}, {dtype_label(io)} (io/state), "
+                        f"{'conv prologue, ' if w.conv else ''}{'z gate' if w.has_z else 'no z'}",
+            "io_dtype": {0: "fp32", 1: "bf16", 2: "fp16"}[io],
+            "state_dtype": "fp32",
             "elements_per_step": elems,
             "inputs_sha256": inputs_digest(t),
         },
         "roofline": {
-            "bound": "alu",
-            "achieved": alu_tops,
-            "peak": ALU_PEAK_TOPS,
-            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)",
-            "frac": alu_tops / ALU_PEAK_TOPS,
+            "bound": "hbm",
+            "achieved": hbm_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": hbm_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
+            "algorithmic_bytes": abytes,
+            "kernel": "scan_kernel",
             "kernel_avg_ms": avg_launch_s * 1e3,
             "kernel_median_ms": float(np.median(launch_ms)),
             "kernel_min_ms": float(np.min(launch_ms)),
             "kernel_avg_ms_cold_caches": float(np.mean(cold_ms)),
-            "hbm": {"achieved_GBs": hbm_gbs, "peak_GBs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS,
-                    "algorithmic_bytes": abytes},
+            "alu_achieved_tops": alu_tops,
+            "alu_peak_tops": ALU_PEAK_TOPS,
+            "alu_frac": alu_tops / ALU_PEAK_TOPS,
+            "alu_ops_per_element": (4 + TRANS_WEIGHT) * w.dstate + 10 + 4 * TRANS_WEIGHT,
+            "alu_trans_weight": TRANS_WEIGHT,
         },
     }
     if not args.no_cpu_baseline:
@@ -377,9 +399,9 @@ def complex_algorithmic_alu_ops(w) -> float:
     """Per (timestep, state): delta' times Re A and Im A, the fraction of the
     phase, the decay's two products, B's two products with delta' u, four
     FMAs of the complex state update and two of Re(C.x) (13 plain ops), plus
-    exp2, sine and cosine, each weighted 4 (quarter rate); per element the
-    26 of the real scan (softplus, gate, D)."""
-    return float(w.elements) * (25 * w.dstate + 26)
+    exp2, sine and cosine, each weighted TRANS_WEIGHT; per element the 10
+    plain ops and 4 transcendentals of the real scan (softplus, gate, D)."""
+    return float(w.elements) * ((13 + 3 * TRANS_WEIGHT) * w.dstate + 10 + 4 * TRANS_WEIGHT)
 
 
 def complex_main(args):
@@ -446,7 +468,7 @@ def complex_main(args):
                    "io_dtype": iot, "elements_per_step": w.elements},
         "roofline": {
             "bound": "alu", "achieved": alu_tops, "peak": ALU_PEAK_TOPS,
-            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)", "frac": alu_tops / ALU_PEAK_TOPS,
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 2)", "frac": alu_tops / ALU_PEAK_TOPS,
             "traffic": load_traffic(w.name, COMPLEX_SRCS),
             "kernel_avg_ms": avg_launch_s * 1e3, "kernel_median_ms": float(np.median(launch_ms)),
             "kernel_min_ms": float(np.min(launch_ms)),
@@ -820,7 +842,7 @@ def ssd_cpu_baseline(w, t, budget_s: float):
 def bwd_bytes(w) -> int:
     """Backward minimum: u, delta, z, dout, B, C and the checkpoints read once;
     du, ddelta, dz (io) and dA, dB, dC, dD, d(delta_bias) (fp32) written once."""
-    es = 2 if w.io_dtype == 1 else 4
+    es = io_bytes(w.io_dtype)
     E = w.elements
     n = w.dstate
     zed = 1 if w.has_z else 0
@@ -833,13 +855,13 @@ def bwd_bytes(w) -> int:
 
 def bwd_alu_ops(w) -> float:
     """Per (timestep, state): the forward re-run (delta'*A, delta'u*B, the
-    state FMA, C.x for dz, one exp weighted 4) = 8, and the adjoint (h FMA,
-    carry multiply, a*x, h*a*x, dA FMA, h*B, A*hax FMA with u*hB, the two sums
-    over states, dB and dC products and their sums over channels) = 14, plus
-    the sum of C.x over states = 1: 23.  Per element: softplus (exp, log),
-    its derivative (exp, rcp), silu and its derivative (exp, rcp) -- six
-    transcendentals weighted 4 -- and about 16 plain ops: 40."""
-    return float(w.elements) * (23 * w.dstate + 40)
+    state FMA, C.x for dz: 4 plain, and one exp weighted TRANS_WEIGHT), the
+    adjoint (h FMA, carry multiply, a*x, h*a*x, dA FMA, h*B, A*hax FMA with
+    u*hB, the two sums over states, dB and dC products and their sums over
+    channels) = 14, plus the sum of C.x over states = 1.  Per element:
+    softplus (exp, log), its derivative (exp, rcp), silu and its derivative
+    (exp, rcp) -- six transcendentals -- and about 16 plain ops."""
+    return float(w.elements) * ((19 + TRANS_WEIGHT) * w.dstate + 16 + 6 * TRANS_WEIGHT)
 
 
 def bwd_main(args):
@@ -922,7 +944,7 @@ def bwd_main(args):
             "bound": "alu",
             "achieved": tops,
             "peak": ALU_PEAK_TOPS,
-            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 4)",
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 2)",
             "frac": tops / ALU_PEAK_TOPS,
             "traffic": load_traffic(f"{w.name}_bwd", BWD_SRCS),
             "kernel": "scan_bwd_kernel (+ the sequence split's carry pass and the partial-sum kernels: the "

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -117,11 +117,13 @@ typedef struct ssm_scan_args {
    * nck = ceil(seqlen / SSM_CKPT_INTERVAL); entry k is x_{k*32-1}, so entry 0
    * is initial_state (zero when not given).  NULL: not written. */
   float *checkpoints;
-  /* Sequence split: 0 lets the library choose how many segments the sequence
-   * is cut into (it splits only when the channels alone leave the GPU short
-   * of waves); k >= 1 asks for k segments (equal lengths of whole chunks, so
-   * possibly fewer).  The split changes the results only by rounding order.
-   * Negative values return SSM_ERR_SHAPE. */
+  /* Sequence split: 0 lets the library choose its plan (it splits the
+   * sequence only when the channels alone leave the GPU short of waves, and
+   * at dstate 13..16 may run leftover channels with eight lanes per channel
+   * to even out the load per SIMD); k >= 1 asks for k segments (equal
+   * lengths of whole chunks, so possibly fewer) of the four-lane kernel.
+   * The plan changes the results only by rounding order.  Negative values
+   * return SSM_ERR_SHAPE. */
   int32_t seq_segments;
 } ssm_scan_args_t;
 
@@ -133,7 +135,7 @@ int ssm_scan_fwd(const ssm_scan_args_t *args, void *hip_stream);
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, results and status codes as ssm_scan_fwd, except that
  * args->workspace and workspace_bytes are ignored: the scratch of the plan
- * (sequence segments or hand-over parts) lives in a buffer built into the
+ * (the sequence segments' end states) lives in a buffer built into the
  * library, SSM_NOALLOC_SCRATCH_BYTES per device, held until the process
  * ends.  A plan that needs more scratch than that returns SSM_ERR_SCRATCH
  * before anything is enqueued (ssm_scan_workspace_size gives the need; the
@@ -152,9 +154,26 @@ int ssm_scan_fwd_noalloc(const ssm_scan_args_t *args, void *hip_stream);
 int ssm_scan_validate(const ssm_scan_args_t *args);
 
 /* Scratch bytes ssm_scan_fwd needs for these arguments (0 when the plan keeps
- * the whole sequence in one pass).  Host-only, no HIP call except a cached
- * query of the device's compute-unit count. */
+ * the whole sequence in one pass).  Host-only: no HIP call except cached
+ * queries of the device's compute-unit count and of how many workgroups of
+ * a kernel one compute unit holds (on a machine without a GPU those fail and
+ * the plan assumes 256 compute units and no mixed plan). */
 int ssm_scan_workspace_size(const ssm_scan_args_t *args, size_t *bytes);
+
+/* The launch plan ssm_scan_fwd takes for these arguments (same queries as
+ * ssm_scan_workspace_size).  Every wave runs lanes_per_channel lanes per
+ * channel over 64 / lanes_per_channel channels; at dstate 13..16 the mixed
+ * plan runs the channel blocks left over after whole waves fill the SIMDs
+ * evenly as eight_lane_waves waves of eight lanes per channel (8 channels,
+ * about half the work each). */
+typedef struct {
+  int32_t segments;            /* sequence segments (1: one pass) */
+  int32_t waves;               /* waves of lanes_per_channel lanes, per segment */
+  int32_t lanes_per_channel;
+  int32_t eight_lane_waves;    /* mixed plan's extra waves (0: not mixed) */
+  size_t workspace_bytes;      /* as ssm_scan_workspace_size */
+} ssm_scan_plan_t;
+int ssm_scan_plan(const ssm_scan_args_t *args, ssm_scan_plan_t *plan);
 
 /* Selective-scan forward with complex A (the same page, section 4.1: A
  * (dim, dstate) may be real or complex; nothing more is printed about the

@@ -21,7 +21,7 @@ SSM_CKPT_INTERVAL = 32
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = (
-    "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size", "ssm_scan_fwd_noalloc",
+    "ssm_scan_fwd", "ssm_scan_validate", "ssm_scan_workspace_size", "ssm_scan_fwd_noalloc", "ssm_scan_plan",
     "ssm_scan_fwd_complex", "ssm_scan_complex_validate",
     "causal_conv1d_fwd", "causal_conv1d_validate", "causal_conv1d_fwd_ex", "causal_conv1d_ex_validate",
     "ssm_state_update", "ssm_state_update_validate",
@@ -32,6 +32,13 @@ EXPORTS = (
 )
 
 _vp = ctypes.c_void_p
+
+
+class ScanPlan(ctypes.Structure):
+    """ssm_scan_plan_t"""
+    _fields_ = [("segments", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("lanes_per_channel", ctypes.c_int32), ("eight_lane_waves", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class ScanArgs(ctypes.Structure):
@@ -138,6 +145,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_validate.restype = ctypes.c_int
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_workspace_size.restype = ctypes.c_int
+        L.ssm_scan_plan.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanPlan)]
+        L.ssm_scan_plan.restype = ctypes.c_int
         L.ssm_scan_fwd_complex.argtypes = [ctypes.POINTER(ScanArgs), _vp]
         L.ssm_scan_fwd_complex.restype = ctypes.c_int
         L.ssm_scan_complex_validate.argtypes = [ctypes.POINTER(ScanArgs)]

@@ -37,6 +37,69 @@ def _stream(device: torch.device, stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Every wrapper checks each tensor against the sizes that delta (or x) and A
+# fix before it hands a pointer to the library: the kernels index their
+# buffers with those sizes, so a wrong shape, dtype or device would be an
+# access outside a buffer, not an error.
+
+def _spec(t: Optional[torch.Tensor], name: str, shape, dtype, dev: torch.device) -> None:
+    """Raise ValueError unless t (when given) has this shape and dtype and
+    lives on dev."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev} with the other tensors, got {t.device}")
+
+
+def _out_spec(t: Optional[torch.Tensor], name: str, shape, dtype, dev: torch.device) -> None:
+    """_spec for a tensor the library writes in place: also contiguous (the
+    kernels write it as a dense row-major array)."""
+    _spec(t, name, shape, dtype, dev)
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} is written in place and must be contiguous")
+
+
+def _on_gpu(dev: torch.device) -> None:
+    if dev.type != "cuda":
+        raise ValueError(f"the operator runs on the GPU: tensors must be on a cuda device, got {dev}")
+
+
+def _io_of(t: torch.Tensor, name: str, ndim: int) -> int:
+    io = _IO.get(t.dtype)
+    if io is None:
+        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return io
+
+
+def _workspace_spec(ws: torch.Tensor, dev: torch.device) -> None:
+    if ws.device != dev or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+
+
+def _conv_params_spec(weight: torch.Tensor, bias: Optional[torch.Tensor], dim: int,
+                      dev: torch.device) -> None:
+    if weight.dim() != 2:
+        raise ValueError(f"conv weight must be (dim, width), got shape {tuple(weight.shape)}")
+    _spec(weight, "weight", (dim, weight.shape[1]), torch.float32, dev)
+    _spec(bias, "bias", (dim,), torch.float32, dev)
+
+
+def _bc_shape(t: torch.Tensor, kind: int, ngroups: int, batch: int, dim: int, dstate: int,
+              seqlen: int, tail=()) -> tuple:
+    """The shape a B or C of this kind must have (tail: the pair axis)."""
+    if kind == _lib.SSM_BC_FIXED:
+        return (dim, dstate) + tail
+    if t.dim() == 3 + len(tail):
+        return (batch, dstate, seqlen) + tail
+    return (batch, ngroups, dstate, seqlen) + tail
+
+
 def _bc_kind(t: torch.Tensor, name: str) -> Tuple[int, int]:
     """(kind, ngroups) of a B or C tensor from its rank."""
     if t.dim() == 2:
@@ -62,10 +125,10 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_st
     """ssm_scan_args_t for the tensors (made contiguous where needed); returns
     (args, out, tensors kept alive until the call is enqueued)."""
     delta = _dense(delta)
-    io = _IO.get(delta.dtype)
-    if io is None:
-        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
+    io = _io_of(delta, "delta", 3)
     batch, dim, seqlen = delta.shape
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError(f"A must be (dim, dstate) with dim {dim}, got shape {tuple(A.shape)}")
     dstate = A.shape[1]
     B, C = _dense(B), _dense(C)
     bk, bg = _bc_kind(B, "B")
@@ -80,6 +143,28 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_st
                     ("conv_weight", conv_weight), ("conv_bias", conv_bias)):
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32, got {t.dtype}")
+    dev, f32, bld, bdn = delta.device, torch.float32, (batch, dim, seqlen), (batch, dim, dstate)
+    for name, t in (("u", u), ("z", z), ("conv_x", conv_x)):
+        _spec(t, name, bld, delta.dtype, dev)
+    _spec(A, "A", (dim, dstate), f32, dev)
+    _spec(B, "B", _bc_shape(B, bk, ngroups, batch, dim, dstate, seqlen), delta.dtype, dev)
+    _spec(C, "C", _bc_shape(C, ck, ngroups, batch, dim, dstate, seqlen), delta.dtype, dev)
+    for name, t in (("D", D), ("delta_bias", delta_bias), ("conv_bias", conv_bias)):
+        _spec(t, name, (dim,), f32, dev)
+    _spec(initial_state, "initial_state", bdn, f32, dev)
+    if conv_weight is not None:
+        if conv_weight.dim() != 2:
+            raise ValueError(f"conv_weight must be (dim, width), got shape {tuple(conv_weight.shape)}")
+        _spec(conv_weight, "conv_weight", (dim, conv_weight.shape[1]), f32, dev)
+        if conv_x is None:
+            raise ValueError("the conv prologue needs conv_x")
+    elif u is None:
+        raise ValueError("u is required without the conv prologue")
+    _out_spec(out, "out", bld, delta.dtype, dev)
+    _out_spec(last_state, "last_state", bdn, f32, dev)
+    if checkpoints is not None:
+        _out_spec(checkpoints, "checkpoints", (batch, dim, checkpoint_count(seqlen), dstate), f32, dev)
+    _on_gpu(dev)
     if out is None:
         out = torch.empty_like(delta)
     args = ScanArgs()
@@ -98,9 +183,6 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_st
     args.conv_act = conv_act
     args.seq_segments = int(seq_segments)
     if checkpoints is not None:
-        want = (batch, dim, checkpoint_count(seqlen), dstate)
-        if tuple(checkpoints.shape) != want or checkpoints.dtype != torch.float32 or not checkpoints.is_contiguous():
-            raise ValueError(f"checkpoints must be a contiguous float32 tensor of shape {want}")
         args.checkpoints = _ptr(checkpoints)
     keep = (u, delta, A, B, C, D, z, delta_bias, initial_state, conv_x, conv_weight, conv_bias)
     return args, out, keep
@@ -138,9 +220,31 @@ def ssm_scan_fwd(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor
         if need.value:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=delta.device)
     if workspace is not None:
+        _workspace_spec(workspace, delta.device)
         args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     check(L.ssm_scan_fwd(ctypes.byref(args), _stream(delta.device, stream)))
     return out
+
+
+def ssm_scan_plan(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
+                  B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                  delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
+                  last_state: Optional[torch.Tensor] = None,
+                  initial_state: Optional[torch.Tensor] = None,
+                  conv_x: Optional[torch.Tensor] = None, conv_weight: Optional[torch.Tensor] = None,
+                  conv_bias: Optional[torch.Tensor] = None, conv_act: int = _lib.SSM_ACT_SILU,
+                  checkpoints: Optional[torch.Tensor] = None, seq_segments: int = 0) -> dict:
+    """The plan ssm_scan_fwd takes for these tensors (ssm_scan_plan): a dict
+    of segments, waves, lanes_per_channel, eight_lane_waves and
+    workspace_bytes.  ``out`` should be the tensor the call will write (its
+    alignment is part of the plan)."""
+    args, out, keep = _scan_args(u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, last_state,
+                                 initial_state, conv_x, conv_weight, conv_bias, conv_act, checkpoints,
+                                 seq_segments)
+    plan = _lib.ScanPlan()
+    check(_lib.lib().ssm_scan_plan(ctypes.byref(args), ctypes.byref(plan)))
+    return {k: getattr(plan, k) for k, _ in _lib.ScanPlan._fields_}
 
 
 def ssm_scan_fwd_noalloc(u: Optional[torch.Tensor], delta: torch.Tensor, A: torch.Tensor,
@@ -197,9 +301,7 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
     (batch, dim, dstate, 2).  u, delta, z and out are real, as in ssm_scan_fwd.
     """
     delta = _dense(delta)
-    io = _IO.get(delta.dtype)
-    if io is None:
-        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
+    io = _io_of(delta, "delta", 3)
     batch, dim, seqlen = delta.shape
     A, B, C = _pairs(A), _pairs(B), _pairs(C)
     initial_state = _pairs(initial_state)
@@ -207,8 +309,8 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
         last_state = _pairs(last_state)
         if not last_state.is_contiguous():
             raise ValueError("last_state must be contiguous")
-    if A.dim() != 3 or A.shape[-1] != 2:
-        raise ValueError("A must be complex (dim, dstate) or float32 pairs (dim, dstate, 2)")
+    if A.dim() != 3 or A.shape[-1] != 2 or A.shape[0] != dim:
+        raise ValueError(f"A must be complex (dim, dstate) or float32 pairs (dim, dstate, 2) with dim {dim}")
     dstate = A.shape[1]
     if B.dim() == 4:
         B = B.unsqueeze(1)
@@ -227,6 +329,20 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                     ("last_state", last_state)):
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32 (complex64 for A and the states), got {t.dtype}")
+    if u is None:
+        raise ValueError("u is required")
+    dev, f32, bld, bdn2 = delta.device, torch.float32, (batch, dim, seqlen), (batch, dim, dstate, 2)
+    _spec(u, "u", bld, delta.dtype, dev)
+    _spec(z, "z", bld, delta.dtype, dev)
+    _spec(A, "A", (dim, dstate, 2), f32, dev)
+    _spec(B, "B", _bc_shape(B, bk, ngroups, batch, dim, dstate, seqlen, (2,)), delta.dtype, dev)
+    _spec(C, "C", _bc_shape(C, ck, ngroups, batch, dim, dstate, seqlen, (2,)), delta.dtype, dev)
+    _spec(D, "D", (dim,), f32, dev)
+    _spec(delta_bias, "delta_bias", (dim,), f32, dev)
+    _spec(initial_state, "initial_state", bdn2, f32, dev)
+    _out_spec(out, "out", bld, delta.dtype, dev)
+    _out_spec(last_state, "last_state", bdn2, f32, dev)
+    _on_gpu(dev)
     if out is None:
         out = torch.empty_like(delta)
     args = ScanArgs()
@@ -263,10 +379,10 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     caps the sequence split (0: the library's choice).
     """
     delta = _dense(delta)
-    io = _IO.get(delta.dtype)
-    if io is None:
-        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {delta.dtype}")
+    io = _io_of(delta, "delta", 3)
     batch, dim, seqlen = delta.shape
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError(f"A must be (dim, dstate) with dim {dim}, got shape {tuple(A.shape)}")
     dstate = A.shape[1]
     u, B, C, z, dout = _dense(u), _dense(B), _dense(C), _dense(z), _dense(dout)
     bk, bg = _bc_kind(B, "B")
@@ -280,11 +396,19 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
     for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("checkpoints", checkpoints)):
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32, got {t.dtype}")
-    want = (batch, dim, checkpoint_count(seqlen), dstate)
-    if tuple(checkpoints.shape) != want:
-        raise ValueError(f"checkpoints must have shape {want}, got {tuple(checkpoints.shape)}")
+    dev, bld = delta.device, (batch, dim, seqlen)
+    for name, t in (("u", u), ("dout", dout), ("z", z)):
+        _spec(t, name, bld, delta.dtype, dev)
+    _spec(A, "A", (dim, dstate), torch.float32, dev)
+    _spec(B, "B", _bc_shape(B, bk, ngroups, batch, dim, dstate, seqlen), delta.dtype, dev)
+    _spec(C, "C", _bc_shape(C, ck, ngroups, batch, dim, dstate, seqlen), delta.dtype, dev)
+    _spec(D, "D", (dim,), torch.float32, dev)
+    _spec(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _spec(checkpoints, "checkpoints", (batch, dim, checkpoint_count(seqlen), dstate), torch.float32, dev)
+    if workspace is not None:
+        _workspace_spec(workspace, dev)
+    _on_gpu(dev)
     A, D, delta_bias, checkpoints = _dense(A), _dense(D), _dense(delta_bias), _dense(checkpoints)
-    dev = delta.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = {
         "du": torch.empty_like(delta), "ddelta": torch.empty_like(delta),
@@ -321,15 +445,16 @@ def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torc
                       stream=None) -> torch.Tensor:
     """Enqueue causal_conv1d_fwd on the current stream; returns ``out``."""
     x = _dense(x)
-    io = _IO.get(x.dtype)
-    if io is None:
-        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {x.dtype}")
+    io = _io_of(x, "x", 3)
     weight, bias = _dense(weight), _dense(bias)
     if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("conv weight and bias must be float32")
+    batch, dim, seqlen = x.shape
+    _conv_params_spec(weight, bias, dim, x.device)
+    _out_spec(out, "out", (batch, dim, seqlen), x.dtype, x.device)
+    _on_gpu(x.device)
     if out is None:
         out = torch.empty_like(x)
-    batch, dim, seqlen = x.shape
     check(_lib.lib().causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out),
                                        batch, dim, seqlen, weight.shape[1], io, act,
                                        _stream(x.device, stream)))
@@ -372,13 +497,12 @@ def causal_conv1d_fwd_ex(x: torch.Tensor, weight: torch.Tensor, bias: Optional[t
     """Enqueue causal_conv1d_fwd_ex; returns ``out``.  ``final_states``
     (batch, dim, width-1) in the io dtype is written when given."""
     x = _dense(x)
-    io = _IO.get(x.dtype)
-    if io is None:
-        raise ValueError(f"io dtype must be float32, bfloat16 or float16, got {x.dtype}")
+    io = _io_of(x, "x", 3)
     weight, bias = _dense(weight), _dense(bias)
     if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
         raise ValueError("conv weight and bias must be float32")
     batch, dim, seqlen = x.shape
+    _conv_params_spec(weight, bias, dim, x.device)
     width = weight.shape[1]
     if seq_idx is not None:
         seq_idx = _dense(seq_idx)
@@ -388,6 +512,11 @@ def causal_conv1d_fwd_ex(x: torch.Tensor, weight: torch.Tensor, bias: Optional[t
         if t is not None and (t.dtype != x.dtype or tuple(t.shape) != (batch, dim, width - 1)
                               or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous {x.dtype} tensor of shape {(batch, dim, width - 1)}")
+    for name, t in (("seq_idx", seq_idx), ("initial_states", initial_states), ("final_states", final_states)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} must be on {x.device} with the other tensors, got {t.device}")
+    _out_spec(out, "out", (batch, dim, seqlen), x.dtype, x.device)
+    _on_gpu(x.device)
     if out is None:
         out = torch.empty_like(x)
     a = ConvArgs()
@@ -472,6 +601,16 @@ def selective_state_update(state: torch.Tensor, x: torch.Tensor, dt: torch.Tenso
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32, got {t.dtype}")
     batch, dim, dstate = state.shape
+    dev, G = state.device, B.shape[1]
+    for name, t in (("x", x), ("dt", dt), ("z", z)):
+        _spec(t, name, (batch, dim), x.dtype, dev)
+    _spec(A, "A", (dim, dstate), torch.float32, dev)
+    _spec(B, "B", (batch, G, dstate), x.dtype, dev)
+    _spec(C, "C", (batch, G, dstate), x.dtype, dev)
+    _spec(D, "D", (dim,), torch.float32, dev)
+    _spec(dt_bias, "dt_bias", (dim,), torch.float32, dev)
+    _out_spec(out, "out", (batch, dim), x.dtype, dev)
+    _on_gpu(dev)
     if out is None:
         out = torch.empty_like(x)
     a = _lib.StateUpdateArgs()
@@ -495,8 +634,12 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
     Returns ``out`` shaped like x."""
     if not conv_state.is_contiguous() or conv_state.dim() != 3:
         raise ValueError("conv_state must be a contiguous (batch, dim, state_len) tensor")
+    act = _act_code(activation)
     squeeze = x.dim() == 2
+    x_shape = tuple(x.shape)
     x = _dense(x.unsqueeze(-1) if squeeze else x)
+    if x.dim() != 3:
+        raise ValueError(f"x must be (batch, dim) or (batch, dim, seqlen), got shape {x_shape}")
     io = _IO.get(x.dtype)
     if io is None or conv_state.dtype != x.dtype:
         raise ValueError("x and conv_state must share the io dtype (float32 or bfloat16)")
@@ -508,11 +651,19 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
             raise ValueError("cache_seqlens must be int32")
         cache_seqlens = _dense(cache_seqlens)
     batch, dim, seqlen = x.shape
+    dev = x.device
+    _spec(conv_state, "conv_state", (batch, dim, conv_state.shape[2]), x.dtype, dev)
+    _conv_params_spec(weight, bias, dim, dev)
+    _spec(cache_seqlens, "cache_seqlens", (batch,), torch.int32, dev)
+    _out_spec(out, "out", x_shape, x.dtype, dev)
+    _on_gpu(dev)
     if out is None:
         out = torch.empty_like(x)
+    elif squeeze:
+        out = out.unsqueeze(-1)
     check(_lib.lib().causal_conv1d_update(
         _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias), _ptr(cache_seqlens), _ptr(out),
-        batch, dim, seqlen, conv_state.shape[2], weight.shape[1], io, _act_code(activation),
+        batch, dim, seqlen, conv_state.shape[2], weight.shape[1], io, act,
         _stream(x.device, stream)))
     return out.squeeze(-1) if squeeze else out
 
@@ -542,7 +693,23 @@ def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Te
     for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias), ("initial_states", initial_states)):
         if t is not None and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, nheads, headdim) and B (batch, seqlen, ngroups, dstate)")
     batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    dev, f32 = x.device, torch.float32
+    _spec(z, "z", x.shape, x.dtype, dev)
+    _spec(dt, "dt", (batch, seqlen, nheads), x.dtype, dev)
+    _spec(B, "B", (batch, seqlen, ngroups, dstate), x.dtype, dev)
+    _spec(C, "C", (batch, seqlen, ngroups, dstate), x.dtype, dev)
+    _spec(A, "A", (nheads,), f32, dev)
+    _spec(dt_bias, "dt_bias", (nheads,), f32, dev)
+    if D is not None:
+        _spec(D, "D", (nheads,) if D.dim() == 1 else (nheads, headdim), f32, dev)
+    _spec(initial_states, "initial_states", (batch, nheads, headdim, dstate), f32, dev)
+    _out_spec(out, "out", x.shape, x.dtype, dev)
+    _out_spec(final_states, "final_states", (batch, nheads, headdim, dstate), f32, dev)
+    _on_gpu(dev)
     if out is None:
         out = torch.empty_like(x)
     a = _lib.SsdArgs()

@@ -6,4 +6,7 @@ namespace ssm {
 ScanFn pick_scan_bf16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
   return pick_scan<1, false>(nsw, lpc, bv, cv, conv, mode);
 }
+ScanFn pick_mix_bf16_ew(bool bv, bool cv, bool conv) {
+  return pick_mix<1, false>(bv, cv, conv);
+}
 }  // namespace ssm

@@ -6,4 +6,7 @@ namespace ssm {
 ScanFn pick_scan_f16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec) {
   return vec ? pick_scan<2, true>(nsw, lpc, bv, cv, conv, mode) : pick_scan_f16_ew(nsw, lpc, bv, cv, conv, mode);
 }
+ScanFn pick_mix_f16(bool bv, bool cv, bool conv, bool vec) {
+  return vec ? pick_mix<2, true>(bv, cv, conv) : pick_mix_f16_ew(bv, cv, conv);
+}
 }  // namespace ssm

@@ -6,4 +6,7 @@ namespace ssm {
 ScanFn pick_scan_f16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
   return pick_scan<2, false>(nsw, lpc, bv, cv, conv, mode);
 }
+ScanFn pick_mix_f16_ew(bool bv, bool cv, bool conv) {
+  return pick_mix<2, false>(bv, cv, conv);
+}
 }  // namespace ssm

@@ -35,14 +35,11 @@
 //     with E_j the end state of segment j from zero and S_j its summed step:
 //     the same recurrence, reassociated;
 //   * when the waves do not divide evenly over the SIMDs (the Mamba-2.8B
-//     layer gives 2560 waves for 1024 SIMDs), the last `hand_units` channel
-//     blocks are cut into `hand_parts` consecutive time ranges run by
-//     different waves: part p waits until part p-1 has published its end
-//     state, then continues the recurrence from it (exactly the sequential
-//     recurrence, handed over through memory).  Every SIMD then gets whole
-//     blocks plus one part instead of some getting a whole block more.
-//     Parts are ordered by workgroup id and workgroups are dispatched in id
-//     order, so a waiting part's predecessor is always resident or done.
+//     layer gives 2560 waves of 16 channels for 1024 SIMDs), the channel
+//     blocks left over are run by waves of eight lanes per channel (two
+//     states each, 8 channels, four timesteps per lane and chunk): two such
+//     waves per block, each with about half the work, so every SIMD gets its
+//     whole waves plus at most one half wave (scan_mix_kernel).
 #pragma once
 
 #include "device_util.h"
@@ -56,46 +53,41 @@ struct ScanParams {
   void *out;
   float *last;
   float *ws_state, *ws_sumdt;   // segment plan: end states from zero, summed steps
-  float *carry;                 // hand-over plan: published end states [slot][k][lane]
-  int *flags;                   // hand-over plan: one flag per slot, zero before the launch
-  int *status;                  // set when a hand-over wait ran out (never under in-order dispatch)
   float *ckpt;                  // saved states for the backward, or null
   int64_t batch, dim, seqlen, seg_len, cpg, nck;
   int n, n_pad, ngroups, groups_eff, nblk, nseg, nblocks;
-  int hand_units, hand_parts;   // hand-over plan (0, 1: none)
+  int mix_whole, mix_small;     // mixed plan: four-lane waves, then eight-lane waves
   int softplus, conv_silu, xcd_swizzle;
 };
 
-constexpr int kHandSpinLimit = 1 << 22;   // bounded wait of a hand-over part
-
 enum { MODE_STATE = 0, MODE_FULL = 1 };
 
-constexpr int kWavesPerBlock = 1;   // every wave is independent
-constexpr int kKP = 8;                                   // timesteps each lane owns per chunk
-constexpr int chunk_of(int lpc) { return kKP * lpc; }    // chunk length
-constexpr int channels_per_block(int lpc) { return kWavesPerBlock * 64 / lpc; }
+constexpr int kKP = 8;   // timesteps a lane owns per chunk (complex kernel; the real one uses kp_of)
+// Timesteps a lane owns per chunk, and the chunk length, for LPC lanes per
+// channel: 8 per lane up to four lanes per channel (chunks of 8, 16, 32), 4
+// per lane with eight lanes per channel (chunks of 32), so the LDS of a wave
+// stays the same.
+constexpr int kp_of(int lpc) { return lpc >= 8 ? 4 : 8; }
+constexpr int chunk_of(int lpc) { return kp_of(lpc) * lpc; }
+constexpr int channels_per_block(int lpc) { return 64 / lpc; }
 
-// DPP quad_perm control word broadcasting lane SRC of each group of LPC lanes.
-template <int LPC, int SRC>
-constexpr int quad_bcast_ctrl() {
-  if constexpr (LPC == 4) return SRC | (SRC << 2) | (SRC << 4) | (SRC << 6);
-  else return SRC | (SRC << 2) | ((2 + SRC) << 4) | ((2 + SRC) << 6);   // LPC == 2
+// LDS floats of one wave of the kernel: the B/C tile (both tensors), the
+// partial C.x rows (full pass) or the delta' / delta'*u hand-off (state pass).
+constexpr int round4(int v) { return (v + 3) / 4 * 4; }
+constexpr int lds_floats(int nsw, int lpc, bool anyv, bool full) {
+  return round4(anyv ? 2 * chunk_of(lpc) * nsw * lpc : 0) +
+         round4((lpc > 1 && full) ? chunk_of(lpc) * 64 + 8 * (chunk_of(lpc) / 8) : 0) +
+         ((lpc > 1 && !full) ? chunk_of(lpc) * (64 / lpc) * 2 : 0) + 4;
 }
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  // every lane reads a lane of its own quad, so bound_ctrl never applies and
-  // no "old" value has to be materialised
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-// A broadcast value used by several multiplies: one DPP move, then plain
-// operands (the empty asm keeps the compiler from folding the DPP into every
-// use, which would make each of them a slower DPP instruction).
-template <int CTRL>
-__device__ __forceinline__ float dpp_bcast_reg(float v) {
-  float r = dpp_mov<CTRL>(v);
-  asm volatile("" : "+v"(r));
-  return r;
-}
+
+// The work of one wave: batch, B/C group, its first channel and its
+// segment of the sequence.
+struct WaveWork {
+  int64_t b;
+  int g;
+  int64_t d0;
+  int seg;
+};
 
 // Keep the compiler from moving LDS accesses across this point and wait for
 // this wave's LDS operations: the lanes of a wave hand data to each other
@@ -108,10 +100,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // owned 8-timestep range and every B/C piece is either whole or past the
 // end, and is moved as one vector; otherwise element by element.
 template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE, bool VEC>
-__global__ void __launch_bounds__(64 * kWavesPerBlock)
-scan_kernel(const ScanParams p) {
+__device__ __forceinline__ void scan_body(const ScanParams &p, float *lds, const WaveWork wk) {
   constexpr bool FULL = MODE == MODE_FULL;
   constexpr bool ANYV = BV || CV;
+  constexpr int kKP = kp_of(LPC);       // timesteps each lane owns per chunk
   constexpr int T = chunk_of(LPC);      // timesteps per chunk
   constexpr int NP = NSW * LPC;         // padded state count
   constexpr int CPW = 64 / LPC;         // channels per wave
@@ -120,57 +112,38 @@ scan_kernel(const ScanParams p) {
   static_assert(PIECES <= 64, "one B/C piece per lane");
   static_assert(NSW == 1 || NSW == 2 || NSW == 4, "states per lane");
 
-  __shared__ float s_bc[ANYV ? kWavesPerBlock : 1][ANYV ? 2 : 1][ANYV ? T : 1][ANYV ? NP : 1];
+  // The wave's LDS (lds_floats of these parameters, 16-byte aligned):
+  //   s_bc[2][T][NP]: the chunk's B and C tile, fp32;
+  //   s_yp: partial C.x of every (timestep, channel, lane) of the chunk; the
+  //     row of timestep t starts at t*CPW*LPC + 8*(t/8), so the owner's reads
+  //     of its timesteps (rows 8 apart) spread over the banks;
+  //   s_dd: the state pass's delta' / delta'*u hand-off.
   constexpr bool XCH = LPC > 1;          // lanes of a channel exchange data
-  // partial C.x of every (timestep, channel, lane) of the chunk; the row of
-  // timestep t starts at t*CPW*LPC + 8*(t/8), so the owner's reads of its
-  // timesteps (rows 8 apart) spread over the banks
   constexpr int YROW_SKEW = 8;
-  __shared__ __attribute__((aligned(16))) float s_yp[(XCH && FULL) ? T * CPW * LPC + YROW_SKEW * (T / 8) : 4];
+  float *s_bc = lds;
+  float *s_yp = lds + round4(ANYV ? 2 * T * NP : 0);
+  float *s_dd = s_yp + round4((XCH && FULL) ? T * CPW * LPC + YROW_SKEW * (T / 8) : 0);
+  auto sbc = [&](int tensor, int t) -> float * { return s_bc + (tensor * T + t) * NP; };
   auto yrow = [](int t) { return t * CPW * LPC + YROW_SKEW * (t / 8); };
   // delta' and delta'*u of timestep group g (timesteps 4g..4g+3) as
   // [channel][4] each.  In the full pass they sit in the C.x rows of the
   // group's first timesteps: every lane reads a group before the step that
   // first overwrites those rows (LDS operations of a wave complete in order).
-  __shared__ __attribute__((aligned(16))) float s_dd[(XCH && !FULL) ? T * CPW * 2 : 4];
   auto dd_at = [&](int g) -> float * { return FULL ? &s_yp[yrow(4 * g)] : &s_dd[g * 2 * CPW * 4]; };
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
   const int q = lane % LPC;             // state group of this lane within its channel
   const int cw_idx = lane / LPC;        // channel within the wave
-
-  // Block -> (channel block, time range).  Consecutive logical blocks share
-  // B/C; the hardware deals blocks to the 8 XCDs round-robin, so the remap
-  // keeps the blocks of one group on one XCD's L2.  Blocks past the whole
-  // ones are the hand-over parts, ordered by part.
-  const int nwhole = p.nblocks - p.hand_units;
-  int bid = blockIdx.x, part = 0, hidx = 0;
-  if (bid < nwhole) {
-    if (p.xcd_swizzle) bid = (bid & 7) * (nwhole >> 3) + (bid >> 3);
-  } else {
-    part = (bid - nwhole) / p.hand_units;
-    hidx = (bid - nwhole) % p.hand_units;
-    bid = nwhole + hidx;
-    // A SIMD issues from its oldest waves first, and the parts are the
-    // youngest: without a higher priority part 0 would only finish near the
-    // end and part 1 would then run mostly alone.
-    __builtin_amdgcn_s_setprio(3);
-  }
-  const int nparts = bid < nwhole ? 1 : p.hand_parts;
-  const int blk = bid % p.nblk;
-  const int rest = bid / p.nblk;
-  const int g = rest % p.groups_eff;
-  const int64_t b = rest / p.groups_eff;
+  const int64_t b = wk.b;
+  const int g = wk.g;
+  const int seg = wk.seg, nsegs = p.nseg;
   const int64_t d_end = (g + 1) * p.cpg;
-  const int64_t d = g * p.cpg + static_cast<int64_t>(blk) * (kWavesPerBlock * CPW) + w * CPW + cw_idx;
+  const int64_t d = wk.d0 + cw_idx;
   const bool valid = d < d_end;
   const int64_t dl = valid ? d : d_end - 1;
   const int64_t row = b * p.dim + dl;
   const int64_t rbase = row * p.seqlen;
   const int64_t BD = p.batch * p.dim;
-  const int seg = p.nseg > 1 ? static_cast<int>(blockIdx.y) : part;
-  const int nsegs = p.nseg > 1 ? p.nseg : nparts;
   const int64_t t_begin = nsegs > 1 ? seg * p.seg_len : 0;
   const int64_t t_end = (nsegs > 1 && t_begin + p.seg_len < p.seqlen) ? t_begin + p.seg_len : p.seqlen;
   const int s0 = q * NSW;
@@ -203,7 +176,7 @@ scan_kernel(const ScanParams p) {
       for (int k = 0; k < NSW; ++k)
         if (s0 + k < n) x[k] = p.init[row * n + s0 + k];
     }
-  } else if (p.nseg > 1) {
+  } else {
     if constexpr (FULL) {
 #pragma unroll
       for (int k = 0; k < NSW; ++k) x[k] = p.ws_state[static_cast<int64_t>(s0 + k) * BD + row];
@@ -216,25 +189,6 @@ scan_kernel(const ScanParams p) {
         }
       }
     }
-  } else {
-    // hand-over: wait for part seg-1 of this block.  Lane 0 polls the flag
-    // with relaxed coherent loads; the acquire fence (a cache invalidation)
-    // is taken once, after the flag is seen -- an acquire load per poll would
-    // invalidate the caches under every other wave of the compute unit.
-    const int64_t slot = static_cast<int64_t>(hidx) * (nparts - 1) + (seg - 1);
-    if (lane == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(p.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-        if (++spins > kHandSpinLimit) {
-          __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-    for (int k = 0; k < NSW; ++k) x[k] = p.carry[(slot * NSW + k) * 64 + lane];
   }
 
   // ---- this lane's timesteps of a chunk: [c + 8q, c + 8q + 8)
@@ -314,8 +268,8 @@ scan_kernel(const ScanParams p) {
     if (bc_lane) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (BV) s_bc[ANYV ? w : 0][0][bc_t0 + i][bc_s] = bc_real ? r.B.get(i) : 0.0f;
-        if constexpr (CV && FULL) s_bc[ANYV ? w : 0][ANYV ? 1 : 0][bc_t0 + i][bc_s] = bc_real ? r.C.get(i) : 0.0f;
+        if constexpr (BV) sbc(0, bc_t0 + i)[bc_s] = bc_real ? r.B.get(i) : 0.0f;
+        if constexpr (CV && FULL) sbc(1, bc_t0 + i)[bc_s] = bc_real ? r.C.get(i) : 0.0f;
       }
     }
   };
@@ -416,8 +370,8 @@ scan_kernel(const ScanParams p) {
       in.dtu = dtuv[t % kKP];
     }
     if constexpr (ANYV) {
-      const float *rowB = &s_bc[ANYV ? w : 0][0][t][s0];
-      const float *rowC = &s_bc[ANYV ? w : 0][ANYV ? 1 : 0][t][s0];
+      const float *rowB = sbc(0, t) + s0;
+      const float *rowC = sbc(1, t) + s0;
 #pragma unroll
       for (int k = 0; k < NSW; ++k) {
         in.Bv[k] = BV ? rowB[k] : Bf[k];
@@ -463,11 +417,11 @@ scan_kernel(const ScanParams p) {
       if (csilu) prep(cur, c, std::true_type{}, std::false_type{}); else prep(cur, c, std::false_type{}, std::false_type{});
     }
     if constexpr (XCH) {
-      // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
-      // reads of the slice are issued before these stores
+      // this lane's timesteps are groups own/4 .. own/4 + kKP/4 - 1; the
+      // previous chunk's reads of the slice are issued before these stores
       wave_lds_sync();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kKP / 4; ++j) {
         float *dp = dd_at((own >> 2) + j);
         *reinterpret_cast<float4 *>(dp + cw_idx * 4) = make_float4(dtv[4 * j], dtv[4 * j + 1], dtv[4 * j + 2], dtv[4 * j + 3]);
         *reinterpret_cast<float4 *>(dp + CPW * 4 + cw_idx * 4) =
@@ -548,13 +502,6 @@ scan_kernel(const ScanParams p) {
         for (int k = 0; k < NSW; ++k)
           if (s0 + k < n) p.last[row * n + s0 + k] = x[k];
       }
-    } else if (p.nseg <= 1) {
-      // hand-over: publish this part's end state, then its flag
-      const int64_t slot = static_cast<int64_t>(hidx) * (nparts - 1) + seg;
-#pragma unroll
-      for (int k = 0; k < NSW; ++k) p.carry[(slot * NSW + k) * 64 + lane] = x[k];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      if (lane == 0) __hip_atomic_store(p.flags + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     if (valid) {
@@ -564,6 +511,57 @@ scan_kernel(const ScanParams p) {
       if (q == 0) p.ws_sumdt[static_cast<int64_t>(seg) * BD + row] = sumdt;
     }
   }
+}
+
+// One wave per workgroup.  Block -> (channel block, segment): consecutive
+// logical blocks share B/C; the hardware deals blocks to the 8 XCDs
+// round-robin, so the remap keeps the blocks of one group on one XCD's L2.
+template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE, bool VEC>
+__global__ void __launch_bounds__(64) scan_kernel(const ScanParams p) {
+  __shared__ __attribute__((aligned(16))) float lds[lds_floats(NSW, LPC, BV || CV, MODE == MODE_FULL)];
+  int bid = blockIdx.x;
+  if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
+  const int blk = bid % p.nblk;
+  const int rest = bid / p.nblk;
+  WaveWork wk;
+  wk.g = rest % p.groups_eff;
+  wk.b = rest / p.groups_eff;
+  wk.d0 = wk.g * p.cpg + static_cast<int64_t>(blk) * channels_per_block(LPC);
+  wk.seg = static_cast<int>(blockIdx.y);
+  scan_body<IO, NSW, LPC, BV, CV, CONV, MODE, VEC>(p, lds, wk);
+}
+
+// The mixed plan at dstate 16: workgroups below mix_whole are four-lane
+// waves over 16-channel blocks; each 16-channel block left over is covered
+// by two eight-lane waves of 8 channels (two states per lane), each with
+// about half the work of a four-lane wave.  With at most one such wave per
+// SIMD the load per SIMD evens out and no SIMD runs with fewer waves than
+// the others until its last wave ends.
+template <int IO, bool BV, bool CV, bool CONV, bool VEC>
+__global__ void __launch_bounds__(64) scan_mix_kernel(const ScanParams p) {
+  constexpr int L4 = lds_floats(4, 4, BV || CV, true), L8 = lds_floats(2, 8, BV || CV, true);
+  __shared__ __attribute__((aligned(16))) float lds[L4 > L8 ? L4 : L8];
+  const int nwhole = p.mix_whole;
+  int bid = blockIdx.x;
+  int unit, half = 0;
+  const bool big = bid < nwhole;
+  if (big) {
+    unit = p.xcd_swizzle ? (bid & 7) * (nwhole >> 3) + (bid >> 3) : bid;
+  } else {
+    int j = bid - nwhole;
+    if (p.xcd_swizzle && p.mix_small % 8 == 0) j = (j & 7) * (p.mix_small >> 3) + (j >> 3);
+    unit = nwhole + j / 2;
+    half = j % 2;
+  }
+  const int blk = unit % p.nblk;
+  const int rest = unit / p.nblk;
+  WaveWork wk;
+  wk.g = rest % p.groups_eff;
+  wk.b = rest / p.groups_eff;
+  wk.d0 = wk.g * p.cpg + static_cast<int64_t>(blk) * 16 + 8 * half;
+  wk.seg = 0;
+  if (big) scan_body<IO, 4, 4, BV, CV, CONV, MODE_FULL, VEC>(p, lds, wk);
+  else scan_body<IO, 2, 8, BV, CV, CONV, MODE_FULL, VEC>(p, lds, wk);
 }
 
 using ScanFn = void (*)(const ScanParams);
@@ -596,6 +594,14 @@ ScanFn pick_scan(int nsw, int lpc, bool bv, bool cv, bool conv, int mode) {
   return nullptr;
 }
 
+template <int IO, bool VEC>
+ScanFn pick_mix(bool bv, bool cv, bool conv) {
+  if (bv && cv) return conv ? scan_mix_kernel<IO, true, true, true, VEC> : scan_mix_kernel<IO, true, true, false, VEC>;
+  if (bv) return conv ? scan_mix_kernel<IO, true, false, true, VEC> : scan_mix_kernel<IO, true, false, false, VEC>;
+  if (cv) return conv ? scan_mix_kernel<IO, false, true, true, VEC> : scan_mix_kernel<IO, false, true, false, VEC>;
+  return conv ? scan_mix_kernel<IO, false, false, true, VEC> : scan_mix_kernel<IO, false, false, false, VEC>;
+}
+
 // Defined in scan_<dtype>.hip (vector io) and scan_<dtype>_ew.hip (element
 // by element): one translation unit per io dtype and load width.
 ScanFn pick_scan_f32(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec);
@@ -604,5 +610,11 @@ ScanFn pick_scan_bf16(int nsw, int lpc, bool bv, bool cv, bool conv, int mode, b
 ScanFn pick_scan_f32_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
 ScanFn pick_scan_f16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
 ScanFn pick_scan_bf16_ew(int nsw, int lpc, bool bv, bool cv, bool conv, int mode);
+ScanFn pick_mix_f32(bool bv, bool cv, bool conv, bool vec);
+ScanFn pick_mix_f16(bool bv, bool cv, bool conv, bool vec);
+ScanFn pick_mix_bf16(bool bv, bool cv, bool conv, bool vec);
+ScanFn pick_mix_f32_ew(bool bv, bool cv, bool conv);
+ScanFn pick_mix_f16_ew(bool bv, bool cv, bool conv);
+ScanFn pick_mix_bf16_ew(bool bv, bool cv, bool conv);
 
 }  // namespace ssm

@@ -8,6 +8,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <unordered_map>
 
 #include "host_util.h"
 #include "scan_kernel.h"
@@ -120,19 +121,12 @@ conv_kernel(const void *x, const float *wgt, const float *bias, void *out,
 // ---------------------------------------------------------------------------
 
 
-// Fills n ints with zero (the hand-over flags): a kernel, so that the call
-// records no memset node when a caller captures it in a graph.
-__global__ void __launch_bounds__(256) zero_ints_kernel(int *p, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
 struct Plan {
   int n_pad, nsw, lpc, T;
   int groups_eff, nblk, nblocks, nseg;
-  int hand_units, hand_parts;    // hand-over plan (0, 1: none)
+  int mix_whole, mix_small;      // mixed plan: four-lane waves, eight-lane waves (0, 0: none)
+  bool vec;                      // 16-byte vector io (see vector_io)
   int64_t cpg, seg_len;
-  size_t off_carry, off_flags, nflags;
   size_t ws_bytes;
 };
 
@@ -144,12 +138,53 @@ int pow2ceil(int v) {
   return r;
 }
 
+ScanFn pick(int io, int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec) {
+  if (io == SSM_BF16) return pick_scan_bf16(nsw, lpc, bv, cv, conv, mode, vec);
+  if (io == SSM_F16) return pick_scan_f16(nsw, lpc, bv, cv, conv, mode, vec);
+  return pick_scan_f32(nsw, lpc, bv, cv, conv, mode, vec);
+}
+
+ScanFn pick_mixed(int io, bool bv, bool cv, bool conv, bool vec) {
+  if (io == SSM_BF16) return pick_mix_bf16(bv, cv, conv, vec);
+  if (io == SSM_F16) return pick_mix_f16(bv, cv, conv, vec);
+  return pick_mix_f32(bv, cv, conv, vec);
+}
+
+// Workgroups of kernel f (64 lanes each) one compute unit holds at once, or
+// 0 when the runtime cannot say (no device): cached per kernel.
+int blocks_per_cu(ScanFn f) {
+  static std::mutex mu;
+  static std::unordered_map<const void *, int> cache;
+  if (!f) return 0;
+  const void *key = reinterpret_cast<const void *>(f);
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, 64, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache.emplace(key, nb);
+  return nb;
+}
+
+// Every io pointer 16-byte aligned and seqlen % 8 == 0: the kernels move
+// whole 8-timestep ranges as vectors.
+bool vector_io(const ssm_scan_args_t *a) {
+  const bool conv = a->conv_weight != nullptr;
+  return (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
+         (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z)) &&
+         (a->B_kind != SSM_BC_VARYING || aligned16(a->B)) && (a->C_kind != SSM_BC_VARYING || aligned16(a->C));
+}
+
 // A channel's states are spread over lpc lanes of nsw states each (four
 // lanes of four at dstate 16): enough waves to fill the GPU at the Mamba
 // shapes, and each lane still runs several independent state chains.
 Plan make_plan(const ssm_scan_args_t *a, int cus) {
   Plan pl{};
   pl.n_pad = pow2ceil(static_cast<int>(a->dstate));
+  pl.vec = vector_io(a);
   switch (pl.n_pad) {
     case 16: pl.nsw = 4; pl.lpc = 4; break;
     case 8: pl.nsw = 4; pl.lpc = 2; break;
@@ -164,7 +199,7 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   const int cpb = channels_per_block(pl.lpc);
   pl.nblk = static_cast<int>((pl.cpg + cpb - 1) / cpb);
   pl.nblocks = static_cast<int>(a->batch * pl.groups_eff * pl.nblk);
-  const int64_t waves = static_cast<int64_t>(pl.nblocks) * kWavesPerBlock;
+  const int64_t waves = pl.nblocks;   // one wave per block
   // Split when the waves would leave the SIMDs short of work: the state pass
   // of a split costs more than it gains once a pass has >= ~2 waves per SIMD,
   // and narrow workloads keep gaining up to ~4-6 waves per SIMD.  Segments
@@ -191,46 +226,28 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   size_t off = pl.nseg > 1
                    ? up256(static_cast<size_t>(pl.nseg - 1) * (pl.n_pad + 1) * a->batch * a->dim * sizeof(float))
                    : 0;
-  // Hand-over: with q whole waves per SIMD and r waves over, some SIMDs
-  // would run a whole wave more than the others.  Cut those r blocks into
-  // S = min(4, SIMDs / r) consecutive time parts instead, so every SIMD gets
-  // q whole waves and at most one part -- provided q + 1 waves fit a SIMD
-  // at once (the LDS of a wave sets how many do).
-  pl.hand_units = 0;
-  pl.hand_parts = 1;
-  if (pl.nseg == 1 && a->seq_segments == 0) {
+  // Mixed plan (dstate 13..16, no split): with q >= 2 whole waves per SIMD
+  // and r channel blocks over, r SIMDs would run a whole wave more than the
+  // rest.  The r blocks become 2r eight-lane waves of 8 channels instead,
+  // each about half the work of a whole wave: with 2r <= SIMDs every SIMD
+  // holds q whole waves and at most one half wave -- provided q + 1 waves of
+  // the kernel fit a SIMD at once (its registers and LDS decide).  At q = 1
+  // the SIMDs are bound by the recurrence's latency rather than by issue, a
+  // half wave takes as long as a whole one, and the plain plan is faster.
+  pl.mix_whole = pl.mix_small = 0;
+  if (pl.nseg == 1 && a->seq_segments == 0 && pl.nsw == 4 && pl.lpc == 4) {
     const int simds = 4 * cus;
     const int q = pl.nblocks / simds, r = pl.nblocks % simds;
-    const int lds = static_cast<int>(2 * pl.T * pl.n_pad * sizeof(float) +
-                                     (pl.lpc > 1 ? (pl.T * 64 + 8 * (pl.T / 8)) * sizeof(float) : 16));
-    const int fit = 160 * 1024 / lds / 4;   // waves of this kernel one SIMD holds
-    int S = r > 0 ? simds / r : 0;
-    if (S > 4) S = 4;
-    if (q >= 1 && S >= 2 && q + 1 <= fit) {
-      int64_t len = (a->seqlen + S - 1) / S;
-      len = (len + align - 1) / align * align;
-      const int parts = static_cast<int>((a->seqlen + len - 1) / len);
-      if (parts >= 2) {
-        pl.hand_units = r;
-        pl.hand_parts = parts;
-        pl.seg_len = len;
-        const size_t slots = static_cast<size_t>(r) * (parts - 1);
-        pl.off_carry = off;
-        off += up256(slots * pl.nsw * 64 * sizeof(float));
-        pl.off_flags = off;
-        pl.nflags = slots + 1;   // one per slot, then the status word
-        off += up256(pl.nflags * sizeof(int));
-      }
+    if (q >= 2 && r > 0 && 2 * r <= simds &&
+        4 * (q + 1) <= blocks_per_cu(pick_mixed(a->io_dtype, a->B_kind == SSM_BC_VARYING,
+                                                a->C_kind == SSM_BC_VARYING, a->conv_weight != nullptr,
+                                                pl.vec))) {
+      pl.mix_whole = pl.nblocks - r;
+      pl.mix_small = 2 * r;
     }
   }
   pl.ws_bytes = off;
   return pl;
-}
-
-ScanFn pick(int io, int nsw, int lpc, bool bv, bool cv, bool conv, int mode, bool vec) {
-  if (io == SSM_BF16) return pick_scan_bf16(nsw, lpc, bv, cv, conv, mode, vec);
-  if (io == SSM_F16) return pick_scan_f16(nsw, lpc, bv, cv, conv, mode, vec);
-  return pick_scan_f32(nsw, lpc, bv, cv, conv, mode, vec);
 }
 
 }  // namespace
@@ -240,6 +257,19 @@ extern "C" int ssm_scan_workspace_size(const ssm_scan_args_t *a, size_t *bytes) 
   if (st != SSM_OK) return st;
   if (!bytes) return SSM_ERR_NULL;
   *bytes = make_plan(a, cu_count_cached()).ws_bytes;
+  return SSM_OK;
+}
+
+extern "C" int ssm_scan_plan(const ssm_scan_args_t *a, ssm_scan_plan_t *out) {
+  const int st = ssm_scan_validate(a);
+  if (st != SSM_OK) return st;
+  if (!out) return SSM_ERR_NULL;
+  const Plan pl = make_plan(a, cu_count_cached());
+  out->segments = pl.nseg;
+  out->waves = pl.mix_small ? pl.mix_whole : pl.nblocks;
+  out->lanes_per_channel = pl.lpc;
+  out->eight_lane_waves = pl.mix_small;
+  out->workspace_bytes = pl.ws_bytes;
   return SSM_OK;
 }
 
@@ -263,46 +293,31 @@ int scan_fwd_run(const ssm_scan_args_t *a, const Plan &pl, void *ws, void *strea
   p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
   p.n = static_cast<int>(a->dstate); p.n_pad = pl.n_pad; p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = pl.groups_eff; p.nblk = pl.nblk; p.nseg = pl.nseg; p.nblocks = pl.nblocks;
-  p.hand_units = pl.hand_units; p.hand_parts = pl.hand_parts;
+  p.mix_whole = pl.mix_whole; p.mix_small = pl.mix_small;
   p.softplus = a->delta_softplus; p.conv_silu = a->conv_act == SSM_ACT_SILU;
-  const bool vec = (a->seqlen % 8 == 0) && aligned16(a->delta) && aligned16(a->out) &&
-          (conv ? aligned16(a->conv_x) : aligned16(a->u)) && (!a->z || aligned16(a->z)) &&
-          (a->B_kind != SSM_BC_VARYING || aligned16(a->B)) && (a->C_kind != SSM_BC_VARYING || aligned16(a->C));
-  p.xcd_swizzle = ((pl.nblocks - pl.hand_units) % 8 == 0);
+  const bool vec = pl.vec;
+  p.xcd_swizzle = pl.mix_small ? (pl.mix_whole % 8 == 0) : (pl.nblocks % 8 == 0);
 
   if (pl.nseg > 1) {
     float *wsf = static_cast<float *>(ws);
     p.ws_state = wsf;
     p.ws_sumdt = wsf + static_cast<size_t>(pl.nseg - 1) * pl.n_pad * a->batch * a->dim;
   }
-  if (pl.hand_units > 0) {
-    char *wsc = static_cast<char *>(ws);
-    p.carry = reinterpret_cast<float *>(wsc + pl.off_carry);
-    p.flags = reinterpret_cast<int *>(wsc + pl.off_flags);
-    p.status = p.flags + (pl.nflags - 1);
-  }
-  const int64_t grid_x = static_cast<int64_t>(pl.nblocks - pl.hand_units) +
-                         static_cast<int64_t>(pl.hand_units) * pl.hand_parts;
+  const int64_t grid_x = pl.mix_small ? static_cast<int64_t>(pl.mix_whole) + pl.mix_small : pl.nblocks;
   if (grid_x > 0x7fffffffLL) return SSM_ERR_SHAPE;
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
   int rc = SSM_OK;
   const ScanFn f_state = pl.nseg > 1 ? pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_STATE, vec) : nullptr;
-  const ScanFn f_full = pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL, vec);
+  const ScanFn f_full = pl.mix_small ? pick_mixed(io, bv, cv, conv, vec)
+                                     : pick(io, pl.nsw, pl.lpc, bv, cv, conv, MODE_FULL, vec);
   if (!f_full || (pl.nseg > 1 && !f_state)) rc = SSM_ERR_UNSUPPORTED;
-  if (rc == SSM_OK && pl.hand_units > 0) {
-    const int64_t nf = static_cast<int64_t>(pl.nflags);
-    hipLaunchKernelGGL(zero_ints_kernel, dim3(static_cast<unsigned>((nf + 255) / 256)), dim3(256), 0, stream,
-                       p.flags, nf);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) rc = hip_fail(e);
-  }
   if (rc == SSM_OK && pl.nseg > 1) {
-    hipLaunchKernelGGL(f_state, dim3(pl.nblocks, pl.nseg - 1), dim3(64 * kWavesPerBlock), 0, stream, p);
+    hipLaunchKernelGGL(f_state, dim3(pl.nblocks, pl.nseg - 1), dim3(64), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e);
   }
   if (rc == SSM_OK) {
-    hipLaunchKernelGGL(f_full, dim3(static_cast<unsigned>(grid_x), pl.nseg), dim3(64 * kWavesPerBlock), 0, stream, p);
+    hipLaunchKernelGGL(f_full, dim3(static_cast<unsigned>(grid_x), pl.nseg), dim3(64), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) rc = hip_fail(e);
   }

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 9
+    assert L.ssm_abi_version() == 10
 
 
 def test_status_strings():
@@ -104,13 +104,12 @@ def test_fwd_rejects_before_any_hip_call():
 
 def test_missing_workspace_is_rejected_before_any_launch():
     """The library allocates nothing: when its plan needs scratch (a sequence
-    split, or the hand-over of a long-channel plan) and the caller passes no
-    workspace, or too little, ssm_scan_fwd returns SSM_ERR_WORKSPACE before it
-    enqueues anything.  The pointers here are not dereferenceable, so any
-    memory access would crash the test."""
+    split) and the caller passes no workspace, or too little, ssm_scan_fwd
+    returns SSM_ERR_WORKSPACE before it enqueues anything.  The pointers here
+    are not dereferenceable, so any memory access would crash the test."""
     L = _lib.lib()
     for kw in (dict(batch=1, dim=64, seqlen=4096), dict(seq_segments=2),
-               dict(batch=8, dim=5120, ngroups=4, seqlen=2048)):
+               dict(batch=1, dim=2560, seqlen=65536, B_kind=_lib.SSM_BC_VARYING)):
         a = _good_args(**kw)
         need = ctypes.c_size_t(0)
         assert L.ssm_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.SSM_OK
@@ -118,6 +117,11 @@ def test_missing_workspace_is_rejected_before_any_launch():
         assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
         a.workspace, a.workspace_bytes = FAKE, need.value - 1
         assert L.ssm_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+    # a plan with no split needs no scratch at all (the Mamba-2.8B layer)
+    need = ctypes.c_size_t(1)
+    a = _good_args(batch=8, dim=5120, ngroups=4, seqlen=2048)
+    assert L.ssm_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value == 0
 
 
 def test_noalloc_rejects_before_any_hip_call():
@@ -334,7 +338,7 @@ def test_bwd_binding_errors():
         binding.ssm_scan_bwd(u, u, A, B, B, u, torch.zeros(b, d, 2, n))
     with pytest.raises(ValueError, match="io dtype"):
         binding.ssm_scan_bwd(u, u, A, B, B, u.to(torch.bfloat16), ck)
-    with pytest.raises(ValueError, match="checkpoints must be a contiguous float32"):
+    with pytest.raises(ValueError, match="checkpoints must have shape"):
         binding.ssm_scan_fwd(u, u, A, B, B, checkpoints=torch.zeros(b, d, 2, n))
 
 
@@ -419,3 +423,26 @@ def test_complex_binding_errors():
         binding.ssm_scan_fwd_complex(u, u, torch.zeros(4, 2), Bv, Bv)
     with pytest.raises(ValueError, match="io dtype"):
         binding.ssm_scan_fwd_complex(u, u, A, torch.zeros(1, 2, 8, 2, dtype=torch.bfloat16), Bv)
+
+
+def test_plan_query():
+    """ssm_scan_plan reports the plan ssm_scan_fwd takes.  Without a GPU the
+    occupancy query fails, so the mixed plan is never chosen here."""
+    L = _lib.lib()
+    def plan(**kw):
+        p = _lib.ScanPlan()
+        assert L.ssm_scan_plan(ctypes.byref(_good_args(**kw)), ctypes.byref(p)) == _lib.SSM_OK
+        return p
+    p = plan(batch=8, dim=5120, ngroups=4, seqlen=2048)
+    assert (p.segments, p.waves, p.lanes_per_channel, p.eight_lane_waves, p.workspace_bytes) == (1, 2560, 4, 0, 0)
+    p = plan(batch=1, dim=2560, seqlen=65536)
+    assert p.segments > 1 and p.waves == 160 and p.workspace_bytes > 0
+    need = ctypes.c_size_t(0)
+    assert L.ssm_scan_workspace_size(ctypes.byref(_good_args(batch=1, dim=2560, seqlen=65536)),
+                                     ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value == p.workspace_bytes
+    assert plan(seq_segments=3, seqlen=960).segments == 3
+    assert plan(seq_segments=3).segments == 2   # whole chunks of 32: 64 + 64
+    assert plan(dstate=8).lanes_per_channel == 2 and plan(dstate=8).waves == 2 * 2
+    assert L.ssm_scan_plan(ctypes.byref(_good_args(delta=None)), ctypes.byref(_lib.ScanPlan())) == _lib.SSM_ERR_NULL
+    assert L.ssm_scan_plan(ctypes.byref(_good_args()), None) == _lib.SSM_ERR_NULL

@@ -12,7 +12,7 @@ import zlib
 import numpy as np
 import pytest
 
-from state_space_model_scan_amd.inputs import BF16, F32, WORKLOADS, make_inputs
+from state_space_model_scan_amd.inputs import BF16, F16, F32, WORKLOADS, make_inputs
 from oracle import oracle as orc
 from tests.harness import TOL, check, conv_flip_slack, log, max_err, run_gpu, run_oracle
 
@@ -142,38 +142,57 @@ def test_forced_segment_counts(nseg):
     check(w, out, ref, last, ref_last, what=f"nseg {nseg}")
 
 
-# Channel counts whose waves do not divide evenly over the 1024 SIMDs of the
-# 256-CU device: the plan cuts the leftover channel blocks into 4, 3 or 2
-# consecutive time parts handed over from wave to wave (16 channels per wave).
-HANDOVER = {
-    "parts4": dict(batch=2, dim=10240, seqlen=200),            # 1280 waves: 256 left over
-    "parts3": dict(batch=1, dim=21840, seqlen=333),            # 1365 waves: 341 left over
-    "parts2": dict(batch=2, dim=12288, seqlen=130),            # 1536 waves: 512 left over
-    "parts2_grouped": dict(batch=2, dim=12288, ngroups=4, seqlen=256),
-    "parts4_bf16": dict(batch=2, dim=10240, seqlen=160, io_dtype=BF16),
+# Channel counts whose 16-channel waves do not divide evenly over the 1024
+# SIMDs of the 256-CU device: with q >= 2 whole waves per SIMD and at most
+# 512 blocks over, the leftover blocks run as two eight-lane waves each (the
+# mixed plan) when q + 1 waves of the kernel fit a SIMD; otherwise (q = 1,
+# or fp32 io, whose kernels hold two waves per SIMD) every block is a
+# whole wave.
+MIXED = {
+    "bf16": (dict(batch=2, dim=20480, seqlen=256, io_dtype=BF16), True),         # 2560 waves: 512 over
+    "bf16_ragged": (dict(batch=1, dim=39990, seqlen=130, io_dtype=BF16), True),  # 2500: 452 over, 6-ch tail
+    "f16_grouped": (dict(batch=2, dim=20480, ngroups=4, seqlen=200, io_dtype=F16), True),
+    "bf16_q1": (dict(batch=2, dim=10240, seqlen=160, io_dtype=BF16), False),     # 1280 waves: q = 1
+    "f32": (dict(batch=2, dim=20480, seqlen=96, io_dtype=F32), None),            # as the occupancy says
 }
 
 
-@pytest.mark.parametrize("name", list(HANDOVER))
-def test_handover_plan(name):
-    """Channel blocks cut into time parts that continue from the state the
-    previous part published: exactly the sequential recurrence."""
-    w = _case(dstate=16, **HANDOVER[name])
+def _plan(w, t, **kw):
+    import torch
+    from state_space_model_scan_amd import binding
+    dev = "cuda"
+    io = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[w.io_dtype]
+    g = lambda k: torch.from_numpy(np.ascontiguousarray(t[k])).to(dev)  # noqa: E731
+    u, delta = g("u").to(io), g("delta").to(io)
+    B, C = g("B").to(io), g("C").to(io)
+    return binding.ssm_scan_plan(u, delta, g("A"), B, C, out=torch.empty_like(delta), **kw)
+
+
+@pytest.mark.parametrize("name", list(MIXED))
+def test_mixed_lane_plan(name):
+    """Leftover channel blocks run with eight lanes per channel: the same
+    recurrence per channel, so the same results."""
+    import torch
+    shape, mixed = MIXED[name]
+    w = _case(dstate=16, **shape)
     t = make_inputs(w)
-    log(f"[parity] handover {name} {w}")
+    plan = _plan(w, t)
+    log(f"[parity] mixed {name} {w} plan {plan}")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256 and mixed is not None:
+        assert (plan["eight_lane_waves"] > 0) == mixed, plan
     out, last = run_gpu(w, t)
     ref, ref_last = run_oracle(w, t, nthreads=16)
-    check(w, out, ref, last, ref_last, what=f"handover {name}")
+    check(w, out, ref, last, ref_last, what=f"mixed {name}")
 
 
-def test_handover_plan_initial_state():
-    w = _case(dstate=16, batch=2, dim=10240, seqlen=100)
+def test_mixed_lane_plan_initial_state_and_conv():
+    w = _case(dstate=16, batch=2, dim=20480, seqlen=96, io_dtype=BF16, conv=True)
     t = make_inputs(w)
     init = np.random.default_rng(9).standard_normal((w.batch, w.dim, w.dstate))
-    log("[parity] handover with initial_state")
+    log("[parity] mixed with initial_state and the conv prologue")
     out, last = run_gpu(w, t, init=init)
     ref, ref_last = run_oracle(w, t, init=init, nthreads=16)
-    check(w, out, ref, last, ref_last, what="handover initial_state")
+    check(w, out, ref, last, ref_last, what="mixed initial_state conv", last_slack=conv_flip_slack(w, t))
 
 
 def test_slow_decay_carry_stress():

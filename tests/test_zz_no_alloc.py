@@ -1,8 +1,9 @@
 """ssm_scan_fwd_noalloc (the forward for callers that cannot allocate: its
 scratch is the library's built-in per-device buffer) against ssm_scan_fwd on
 the same inputs, through the C ABI: two calls in a row, the second on a
-smaller input, for each plan that uses scratch (parallel sequence segments,
-hand-over parts) and for one that uses none.  The two entry points run the
+smaller input, for the plans that use scratch (parallel sequence segments,
+chosen by the library or asked for) and for ones that use none (whole
+waves, the mixed-lane plan).  The two entry points run the
 same kernels with the same plan, so the outputs agree bit for bit, which is
 inside the parity bar (|a - b| <= tol (1 + |b|)) a fortiori."""
 import numpy as np
@@ -27,24 +28,28 @@ def _call(fn, w, t, **kw):
     return (out.float().cpu().numpy().astype(np.float64), last.cpu().numpy().astype(np.float64))
 
 
-# (larger, smaller) input pairs per plan, called back to back
+# (larger, smaller) input pairs per plan, called back to back, and the
+# seq_segments argument
 PAIRS = {
-    "segments": (dict(dim=256, seqlen=8192), dict(dim=64, seqlen=4096)),
-    "handover": (dict(batch=2, dim=10240, seqlen=200), dict(batch=2, dim=10240, seqlen=100)),
-    "whole": (dict(batch=2, dim=16384, seqlen=128), dict(batch=2, dim=16384, seqlen=64)),
+    "segments": ((dict(dim=256, seqlen=8192), dict(dim=64, seqlen=4096)), 0),
+    "segments_asked": ((dict(batch=2, dim=1024, seqlen=2048), dict(batch=1, dim=512, seqlen=1024)), 5),
+    "whole": ((dict(batch=2, dim=16384, seqlen=128), dict(batch=2, dim=16384, seqlen=64)), 0),
+    "mixed": ((dict(batch=2, dim=20480, seqlen=128), dict(batch=2, dim=20480, seqlen=64)), 0),
 }
 
 
 @pytest.mark.parametrize("plan", list(PAIRS))
 def test_noalloc_matches_scan_fwd(plan):
     from state_space_model_scan_amd import binding
-    for k, shape in enumerate(PAIRS[plan]):
-        w = WORKLOADS["longseq"].scaled(io_dtype=BF16 if plan == "whole" else WORKLOADS["longseq"].io_dtype,
+    shapes, nseg = PAIRS[plan]
+    for k, shape in enumerate(shapes):
+        bf = plan in ("whole", "mixed")
+        w = WORKLOADS["longseq"].scaled(io_dtype=BF16 if bf else WORKLOADS["longseq"].io_dtype,
                                         has_z=True, **shape)
         t = make_inputs(w, seed=40 + k)
         log(f"[noalloc] {plan} call {k + 1}: {w}")
-        ref, ref_last = _call(binding.ssm_scan_fwd, w, t)
-        got, got_last = _call(binding.ssm_scan_fwd_noalloc, w, t)
+        ref, ref_last = _call(binding.ssm_scan_fwd, w, t, seq_segments=nseg)
+        got, got_last = _call(binding.ssm_scan_fwd_noalloc, w, t, seq_segments=nseg)
         assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_last))
         tol = TOL[w.io_dtype]
         assert np.max(np.abs(got - ref) / (1.0 + np.abs(ref))) <= tol
