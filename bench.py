@@ -287,6 +287,15 @@ def main():
         binding.ssm_scan_fwd(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
                              dev["delta_bias"], w.softplus, out=out, last_state=last, **conv)
 
+    plan = binding.ssm_scan_plan(dev["u"], dev["delta"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                 dev["delta_bias"], w.softplus, out=out, last_state=last, **conv)
+    if plan["segments"] > 1:
+        kernel = "scan_kernel (state pass + full pass)"
+    elif plan["eight_lane_waves"]:
+        kernel = "scan_mix_kernel"
+    else:
+        kernel = "scan_kernel"
+
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -362,7 +371,8 @@ def main():
             "frac": hbm_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes": abytes,
-            "kernel": "scan_kernel",
+            "kernel": kernel,
+            "plan": plan,
             "kernel_avg_ms": avg_launch_s * 1e3,
             "kernel_median_ms": float(np.median(launch_ms)),
             "kernel_min_ms": float(np.min(launch_ms)),

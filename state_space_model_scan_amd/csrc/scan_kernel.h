@@ -200,10 +200,15 @@ __device__ __forceinline__ void scan_body(const ScanParams &p, float *lds, const
 
   // Raw global inputs of a chunk.  Two sets alternate (the chunk loop is
   // unrolled by two), so no loop-carried copy waits on the loads in flight.
+  // D*u of the owned timesteps is kept for the epilogue only where u is not
+  // in the set as loaded (conv prologue) or takes an unpacking op (16-bit
+  // io); with fp32 io the epilogue forms it from the raw u, which leaves the
+  // full pass enough registers for three waves per SIMD.
+  constexpr bool KEEP_DU = CONV || IO != 0;
   struct RawSet {
     RawV<IO, kKP> a, dl, z, h;   // u (or conv x), delta, z, the 8 samples before (conv halo)
     RawV<IO, 8> B, C;            // this lane's piece of the chunk's B / C tile
-    float du[kKP];               // D*u of the owned timesteps (prepared, for the epilogue)
+    float du[KEEP_DU ? kKP : 1]; // D*u of the owned timesteps (prepared, for the epilogue)
   };
   // VEC: one unconditional vector load per input.  A range past the end of
   // the time range reads the row's last vector instead (those values only
@@ -316,7 +321,7 @@ __device__ __forceinline__ void scan_body(const ScanParams &p, float *lds, const
       if (!FC && i >= cnt) dt = 0.0f;
       dtv[i] = dt;
       dtuv[i] = dt * uu[i];
-      r.du[i] = Dd * uu[i];
+      if constexpr (KEEP_DU) r.du[i] = Dd * uu[i];
     }
   };
   auto gather_y = [&]() {     // sum of the quad's partial C.x of this lane's timesteps
@@ -339,7 +344,16 @@ __device__ __forceinline__ void scan_body(const ScanParams &p, float *lds, const
     float o[kKP];
 #pragma unroll
     for (int i = 0; i < kKP; ++i) {
-      float y = yv[i] + r.du[i];
+      float y;
+      if constexpr (KEEP_DU) {
+        y = yv[i] + r.du[i];
+      } else {
+        // the product rounded on its own, as where it is kept: the same
+        // output with or without the conv prologue
+#pragma clang fp contract(off)
+        const float du = Dd * r.a.get(i);
+        y = yv[i] + du;
+      }
       if (p.z) y *= silu_f(r.z.get(i));
       o[i] = y;
     }
@@ -513,11 +527,19 @@ __device__ __forceinline__ void scan_body(const ScanParams &p, float *lds, const
   }
 }
 
+// The fp32-io full pass with vector io and no conv prologue needs a few
+// registers more than three waves per SIMD allow; capped to three, it spills
+// two values outside its loop (setup and exit).  Other instances keep the
+// compiler's choice.
+template <int IO, bool CONV, int MODE, bool VEC>
+constexpr bool kFullF32Vec = IO == 0 && !CONV && MODE == MODE_FULL && VEC;
+
 // One wave per workgroup.  Block -> (channel block, segment): consecutive
 // logical blocks share B/C; the hardware deals blocks to the 8 XCDs
 // round-robin, so the remap keeps the blocks of one group on one XCD's L2.
 template <int IO, int NSW, int LPC, bool BV, bool CV, bool CONV, int MODE, bool VEC>
-__global__ void __launch_bounds__(64) scan_kernel(const ScanParams p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kFullF32Vec<IO, CONV, MODE, VEC> ? 3 : 1)))
+scan_kernel(const ScanParams p) {
   __shared__ __attribute__((aligned(16))) float lds[lds_floats(NSW, LPC, BV || CV, MODE == MODE_FULL)];
   int bid = blockIdx.x;
   if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);

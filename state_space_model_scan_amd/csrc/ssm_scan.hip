@@ -202,14 +202,17 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
   const int64_t waves = pl.nblocks;   // one wave per block
   // Split when the waves would leave the SIMDs short of work: the state pass
   // of a split costs more than it gains once a pass has >= ~2 waves per SIMD,
-  // and narrow workloads keep gaining up to ~4-6 waves per SIMD.  Segments
-  // keep at least 8 chunks: shorter ones spend too much on their start (the
-  // carry fold, the first chunk's loads) -- at b=4 d=1536 l=2048, 8 segments
-  // ran 9% faster than 16.
+  // and narrow workloads keep gaining up to ~4-6 waves per SIMD.  The count
+  // is rounded down, so the full pass never exceeds 6 waves per SIMD: just
+  // above a multiple of what the SIMDs hold at once, the few waves over run
+  // as a round of their own (b=1 d=2560 l=65536 fp32: 39 segments 1194 us,
+  // 38 segments 1121 us).  Segments keep at least 8 chunks: shorter ones
+  // spend too much on their start (the carry fold, the first chunk's loads)
+  // -- at b=4 d=1536 l=2048, 8 segments ran 9% faster than 16.
   const int64_t target = 16LL * cus;
   int nseg = 1;
   if (waves < 8LL * cus) {
-    const int64_t want = (3 * target + 2 * waves - 1) / (2 * waves);
+    const int64_t want = 3 * target / (2 * waves);
     const int64_t cap = a->seqlen / (8 * pl.T);
     nseg = static_cast<int>(want < cap ? want : cap);
     if (nseg < 1) nseg = 1;
