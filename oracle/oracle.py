@@ -84,7 +84,8 @@ def _load():
             i64, i64, i64, i32, i64, i32, p, p, p, p, i32, p, p, p]
         lib.oracle_causal_conv1d_update.restype = i32
         lib.oracle_ssd_scan.argtypes = [
-            i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, i32, p, p, i32, p, p, p, i32]
+            i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, i32, p, p, i32, p, p, p,
+            i32, ctypes.c_double, ctypes.c_double, p, i32]
         lib.oracle_ssd_scan.restype = i32
         lib.oracle_selective_scan_bwd.argtypes = [
             i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
@@ -331,13 +332,15 @@ def causal_conv1d_update(x, conv_state, weight, bias=None, act=ACT_NONE, cache_s
 
 
 def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, *,
-             io_dtype=F32, initial_states=None, nthreads=0):
+             io_dtype=F32, initial_states=None, dt_limit=None, seq_idx=None, nthreads=0):
     """Oracle Mamba-2 scan (scalar decay per head), sequential in time.
 
     x, z: (batch, seqlen, nheads, headdim) io bits; dt: (batch, seqlen, nheads)
     io bits; A, dt_bias: (nheads,) float32; B, C: (batch, seqlen, ngroups,
     dstate) io bits; D: (nheads,) or (nheads, headdim) float32;
-    initial_states: (batch, nheads, headdim, dstate) float.
+    initial_states: (batch, nheads, headdim, dstate) float; dt_limit: None or
+    (dt_min, dt_max), the step's clamp after softplus; seq_idx: None or
+    (batch, seqlen) int32 sequence ids (the state restarts where they change).
     Returns (out (batch, seqlen, nheads, headdim) float64,
              final_states (batch, nheads, headdim, dstate) float64).
     """
@@ -348,12 +351,17 @@ def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, *,
     batch, seqlen, nheads, headdim = x.shape
     ngroups, dstate = B.shape[2], B.shape[3]
     init = None if initial_states is None else np.ascontiguousarray(initial_states, dtype=np.float64)
+    sid = None if seq_idx is None else np.ascontiguousarray(seq_idx, dtype=np.int32)
+    if sid is not None and sid.shape != (batch, seqlen):
+        raise ValueError("seq_idx must be (batch, seqlen)")
+    lim = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
     out = np.empty(x.shape, dtype=np.float64)
     fin = np.empty((batch, nheads, headdim, dstate), dtype=np.float64)
     rc = lib.oracle_ssd_scan(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype,
                              _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                              int(D is not None and D.ndim == 2), _ptr(z), _ptr(dt_bias),
-                             int(bool(dt_softplus)), _ptr(init), _ptr(out), _ptr(fin), int(nthreads))
+                             int(bool(dt_softplus)), _ptr(init), _ptr(out), _ptr(fin),
+                             int(dt_limit is not None), lim[0], lim[1], _ptr(sid), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_ssd_scan failed with status {rc}")
     return out, fin

@@ -773,13 +773,23 @@ int oracle_causal_conv1d_update(int64_t batch, int64_t dim, int64_t seqlen,
  * H starts at initial_states (zero when NULL); final_states gets the last H.
  * The chunked evaluation is a reassociation of this sum; the oracle runs the
  * recurrence in order.  out: (batch*seqlen*nheads*headdim) double;
- * final_states: (batch*nheads*headdim*dstate) double or NULL. */
+ * final_states: (batch*nheads*headdim*dstate) double or NULL.
+ *
+ * The same section lists the operators' options without defining them; two
+ * are read here as follows.  dt_limit (the step's range): with dt_limit set,
+ * dt' = min(max(dt', dt_min), dt_max) after softplus.  seq_idx (several
+ * sequences packed along the sequence axis): (batch*seqlen) int32 ids that
+ * stay equal within a sequence; where the id changes (t > 0 and
+ * seq_idx[t] != seq_idx[t-1]) H restarts from zero before the update, so no
+ * token sees a token of another sequence.  initial_states is the state
+ * before the first sequence; final_states is the state after the last one. */
 int oracle_ssd_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                     int64_t dstate, int64_t ngroups, int io_dtype, const void *x,
                     const void *dt, const float *A, const void *B, const void *C,
                     const float *D, int D_per_channel, const void *z,
                     const float *dt_bias, int dt_softplus, const double *initial_states,
-                    double *out, double *final_states, int nthreads) {
+                    double *out, double *final_states, int dt_limit, double dt_min,
+                    double dt_max, const int32_t *seq_idx, int nthreads) {
     if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
         return 2;
     if (nheads % ngroups != 0) return 2;
@@ -804,9 +814,12 @@ int oracle_ssd_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
                 for (int64_t i = 0; i < headdim * dstate; ++i)
                     H[i] = initial_states ? initial_states[sbase + i] : 0.0;
                 for (int64_t t = 0; t < seqlen; ++t) {
+                    if (seq_idx && t > 0 && seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1])
+                        for (int64_t i = 0; i < headdim * dstate; ++i) H[i] = 0.0;
                     double step = load_io(dt, io_dtype, (b * seqlen + t) * nheads + h);
                     if (dt_bias) step += (double)dt_bias[h];
                     if (dt_softplus) step = oracle_softplus(step);
+                    if (dt_limit) step = step < dt_min ? dt_min : (step > dt_max ? dt_max : step);
                     const double dA = exp(step * (double)A[h]);
                     const int64_t bcb = ((b * seqlen + t) * ngroups + g) * dstate;
                     const int64_t xb = ((b * seqlen + t) * nheads + h) * headdim;

@@ -165,6 +165,18 @@ SSD_MUTANTS = {
                              "*hs = dA * *hs + load_io(B, io_dtype, bcb + s) * xv;"),
     "ssd_D_channel_index": ("D[h * headdim + pp]", "D[pp % nheads * headdim + h % headdim]"),
     "ssd_ignore_initial": ("H[i] = initial_states ? initial_states[sbase + i] : 0.0;", "H[i] = 0.0;"),
+    "ssd_limit_swapped": ("step = step < dt_min ? dt_min : (step > dt_max ? dt_max : step);",
+                          "step = step < dt_max ? dt_max : (step > dt_min ? dt_min : step);"),
+    "ssd_limit_before_softplus": (
+        "if (dt_softplus) step = oracle_softplus(step);\n"
+        "                    if (dt_limit) step = step < dt_min ? dt_min : (step > dt_max ? dt_max : step);",
+        "if (dt_limit) step = step < dt_min ? dt_min : (step > dt_max ? dt_max : step);\n"
+        "                    if (dt_softplus) step = oracle_softplus(step);"),
+    "ssd_no_reset": ("if (seq_idx && t > 0 && seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1])",
+                     "if (0)"),
+    "ssd_reset_after_update": (
+        "if (seq_idx && t > 0 && seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1])",
+        "if (seq_idx && t > 1 && seq_idx[b * seqlen + t - 1] != seq_idx[b * seqlen + t - 2])"),
 }
 
 
@@ -176,6 +188,8 @@ def _ssd_pin_calls():
         ("dual", lambda: spins.test_ssd_dual_quadratic_form(True)),
         ("split", spins.test_ssd_split_continuation),
         ("D_forms", spins.test_ssd_D_per_head_equals_per_channel),
+        ("dual_limit_seq", lambda: spins.test_ssd_dual_form_with_dt_limit_and_seq_idx(True)),
+        ("separate_runs", spins.test_ssd_seq_idx_equals_separate_runs),
     ]
 
 

@@ -134,3 +134,97 @@ def test_ssd_D_per_head_equals_per_channel():
     o3, _ = orc.ssd_scan(x, dt, A, B, C, Dc, None, bias, True)
     o4, _ = orc.ssd_scan(x, dt, A, B, C, None, None, bias, True)
     _close(o3 - o4, Dc[None, None] * x.astype(np.float64))
+
+
+def _seq_ids(rng, b, l, pieces):
+    """Non-decreasing ids per batch row from a list of piece lengths per row
+    (ids start at an arbitrary value and skip some values)."""
+    sid = np.zeros((b, l), np.int32)
+    for bb in range(b):
+        cur, t = int(rng.integers(0, 5)), 0
+        for n_ in pieces[bb]:
+            sid[bb, t:t + n_] = cur
+            t += n_
+            cur += int(rng.integers(1, 3))
+        assert t == l
+    return sid
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_ssd_dual_form_with_dt_limit_and_seq_idx(softplus):
+    """The quadratic form again, with the step clamped to [lo, hi] (both ends
+    active) and packed sequences: a token sees only earlier tokens of its own
+    sequence, the initial state reaches only the first sequence, and the
+    final state holds only the last one."""
+    rng = np.random.default_rng(63 + softplus)
+    b, l, h, p, n, g = 2, 12, 4, 3, 4, 2
+    x, dt, z, B, C, A, D, bias, init = _inputs(rng, b, l, h, p, n, g)
+    sid = _seq_ids(rng, b, l, [[3, 1, 5, 3], [12]])
+    step = dt.astype(np.float64) + bias.astype(np.float64)[None, None, :]
+    if softplus:
+        step = np.logaddexp(0.0, step)
+    lo, hi = np.quantile(step, 0.25), np.quantile(step, 0.7)
+    out, fin = orc.ssd_scan(x, dt, A, B, C, D, None, bias, softplus, initial_states=init,
+                            dt_limit=(lo, hi), seq_idx=sid)
+    assert (step < lo).any() and (step > hi).any()
+    step = np.clip(step, lo, hi)
+    want = np.zeros((b, l, h, p))
+    want_fin = np.zeros((b, h, p, n))
+    for bb in range(b):
+        s = sid[bb]
+        for hh in range(h):
+            gg = hh // (h // g)
+            a = float(A[hh])
+            cs = np.concatenate([[0.0], np.cumsum(step[bb, :, hh])])
+            Bm = B[bb, :, gg, :].astype(np.float64)
+            Cm = C[bb, :, gg, :].astype(np.float64)
+            X = x[bb, :, hh, :].astype(np.float64)
+            for t in range(l):
+                acc = np.zeros(p)
+                for tau in range(t + 1):
+                    if s[tau] != s[t]:
+                        continue
+                    w = (Cm[t] @ Bm[tau]) * np.exp(a * (cs[t + 1] - cs[tau + 1])) * step[bb, tau, hh]
+                    acc += w * X[tau]
+                if s[t] == s[0]:
+                    acc += np.exp(a * cs[t + 1]) * (init[bb, hh] @ Cm[t])
+                want[bb, t, hh] = acc + D[hh] * X[t]
+            Hf = np.exp(a * cs[l]) * init[bb, hh] if s[l - 1] == s[0] else np.zeros((p, n))
+            for tau in range(l):
+                if s[tau] == s[l - 1]:
+                    Hf += np.exp(a * (cs[l] - cs[tau + 1])) * step[bb, tau, hh] * np.outer(X[tau], Bm[tau])
+            want_fin[bb, hh] = Hf
+    _close(out, want, 1e-11)
+    _close(fin, want_fin, 1e-11)
+
+
+def test_ssd_seq_idx_equals_separate_runs():
+    """Packed sequences give exactly what each sequence gives on its own (the
+    first one from the initial state, the others from zero); the final state
+    is the last sequence's."""
+    rng = np.random.default_rng(65)
+    b, l, h, p, n, g = 2, 20, 2, 3, 4, 1
+    x, dt, z, B, C, A, D, bias, init = _inputs(rng, b, l, h, p, n, g)
+    pieces = [[6, 1, 13], [2, 9, 4, 5]]
+    sid = _seq_ids(rng, b, l, pieces)
+    out, fin = orc.ssd_scan(x, dt, A, B, C, D, z, bias, True, initial_states=init, seq_idx=sid)
+    for bb in range(b):
+        t0 = 0
+        for k, n_ in enumerate(pieces[bb]):
+            sl = lambda a: np.ascontiguousarray(a[bb:bb + 1, t0:t0 + n_])  # noqa: E731
+            o, f = orc.ssd_scan(sl(x), sl(dt), A, sl(B), sl(C), D, sl(z), bias, True,
+                                initial_states=init[bb:bb + 1] if k == 0 else None)
+            np.testing.assert_array_equal(out[bb:bb + 1, t0:t0 + n_], o)
+            t0 += n_
+        np.testing.assert_array_equal(fin[bb:bb + 1], f)
+
+
+def test_ssd_one_sequence_id_and_wide_limits_change_nothing():
+    rng = np.random.default_rng(66)
+    b, l, h, p, n, g = 1, 9, 2, 3, 4, 2
+    x, dt, z, B, C, A, D, bias, init = _inputs(rng, b, l, h, p, n, g)
+    o1, f1 = orc.ssd_scan(x, dt, A, B, C, D, z, bias, True, initial_states=init)
+    o2, f2 = orc.ssd_scan(x, dt, A, B, C, D, z, bias, True, initial_states=init,
+                          seq_idx=np.full((b, l), 7, np.int32), dt_limit=(0.0, np.inf))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(f1, f2)
