@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 10
+#define SSM_ABI_VERSION 11
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -426,6 +426,28 @@ typedef struct ssd_scan_args {
   const float *initial_states;    /* (b,h,p,n) fp32 or NULL (zero) */
   void *out;                      /* (b,l,h,p) io, required */
   float *final_states;            /* (b,h,p,n) fp32 or NULL */
+  /* Step range (the operators' dt_limit): when dt_limit is 1 the step is
+   * clamped, dt' = min(max(dt', dt_min), dt_max), after softplus; 0: no
+   * clamp.  dt_min > dt_max returns SSM_ERR_SHAPE. */
+  int32_t dt_limit;
+  float dt_min, dt_max;
+  /* Packed sequences (the operators' seq_idx): (b,l) int32 sequence ids, or
+   * NULL.  Ids must not decrease along l (each sequence is one contiguous
+   * run); where the id changes the state restarts from zero, so no token
+   * sees a token of another sequence.  initial_states is the state before
+   * the first sequence of each row, final_states the state after the last.
+   * Ids that decrease give unspecified results (never a fault). */
+  const int32_t *seq_idx;
+  /* Scratch for the sequence split (see ssd_scan_workspace_size): caller-
+   * allocated device memory; the library allocates nothing and returns
+   * SSM_ERR_WORKSPACE when the plan needs more than workspace_bytes.  Not
+   * read before written; reusable once the call's work has finished. */
+  void *workspace;
+  size_t workspace_bytes;
+  /* Sequence split: 0 lets the library choose; k >= 1 asks for k segments
+   * of whole chunks (possibly fewer).  Negative values return SSM_ERR_SHAPE.
+   * The split changes the results only by rounding order. */
+  int32_t seq_segments;
 } ssd_scan_args_t;
 
 /* ssd_scan_fwd: the Mamba-2 chunked scan (the guide's section 4.4 lists
@@ -434,7 +456,9 @@ typedef struct ssd_scan_args {
  * recurrence with a scalar decay per head, evaluated chunk by chunk).  For
  * every (b, h), head h in group g = h / (nheads / ngroups), and token t:
  *
- *     dt'          = softplus(dt[b,t,h] + dt_bias[h])   (or without softplus)
+ *     dt'          = softplus(dt[b,t,h] + dt_bias[h])   (or without softplus;
+ *                    then clamped to [dt_min, dt_max] with dt_limit)
+ *     H[p][n]     <- 0 first where seq_idx[b,t] != seq_idx[b,t-1]
  *     H[p][n]     <- exp(dt' * A[h]) * H[p][n] + dt' * B[b,t,g,n] * x[b,t,h,p]
  *     out[b,t,h,p] = (sum_n C[b,t,g,n] * H[p][n] + D * x[b,t,h,p]) * silu(z[b,t,h,p])
  *
@@ -442,6 +466,11 @@ typedef struct ssd_scan_args {
  * final_states.  The kernel evaluates each chunk of SSD_CHUNK tokens in the
  * quadratic (dual) form on the matrix cores -- products of bf16 operands
  * accumulated in fp32 -- and carries the fp32 state from chunk to chunk.
+ * When batch * nheads alone leaves the GPU short of workgroups, the chunks
+ * are cut into segments: a first launch finds each segment's end state
+ * from zero and its total decay (chunk_state), the second starts every
+ * segment from the state carried over the ones before it (state_passing)
+ * and computes the outputs (chunk_scan).
  * Supported: io_dtype SSM_BF16, headdim SSD_HEADDIM, dstate 32, 64 or 128;
  * other values return SSM_ERR_UNSUPPORTED.  Same conventions and status
  * codes as ssm_scan_fwd. */
@@ -449,6 +478,11 @@ int ssd_scan_fwd(const ssd_scan_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssd_scan_fwd (no HIP call). */
 int ssd_scan_validate(const ssd_scan_args_t *args);
+
+/* Scratch bytes ssd_scan_fwd needs for these arguments (0 without a
+ * sequence split).  Host-only apart from cached queries of the device's
+ * compute-unit count and the kernels' occupancy. */
+int ssd_scan_workspace_size(const ssd_scan_args_t *args, size_t *bytes);
 
 /* Static text for a status code. */
 const char *ssm_status_str(int status);

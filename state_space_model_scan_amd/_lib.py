@@ -26,7 +26,7 @@ EXPORTS = (
     "causal_conv1d_fwd", "causal_conv1d_validate", "causal_conv1d_fwd_ex", "causal_conv1d_ex_validate",
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
-    "ssd_scan_fwd", "ssd_scan_validate",
+    "ssd_scan_fwd", "ssd_scan_validate", "ssd_scan_workspace_size",
     "ssm_scan_bwd", "ssm_scan_bwd_validate", "ssm_scan_bwd_workspace_size",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
 )
@@ -113,6 +113,9 @@ class SsdArgs(ctypes.Structure):
         ("D", _vp), ("D_per_channel", ctypes.c_int32),
         ("z", _vp), ("dt_bias", _vp), ("dt_softplus", ctypes.c_int32),
         ("initial_states", _vp), ("out", _vp), ("final_states", _vp),
+        ("dt_limit", ctypes.c_int32), ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+        ("seq_idx", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("seq_segments", ctypes.c_int32),
     ]
 
 
@@ -169,6 +172,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_fwd.restype = ctypes.c_int
         L.ssd_scan_validate.argtypes = [ctypes.POINTER(SsdArgs)]
         L.ssd_scan_validate.restype = ctypes.c_int
+        L.ssd_scan_workspace_size.argtypes = [ctypes.POINTER(SsdArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_workspace_size.restype = ctypes.c_int
         L.causal_conv1d_fwd_ex.argtypes = [ctypes.POINTER(ConvArgs), _vp]
         L.causal_conv1d_fwd_ex.restype = ctypes.c_int
         L.causal_conv1d_ex_validate.argtypes = [ctypes.POINTER(ConvArgs)]

@@ -672,17 +672,10 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
 # Mamba-2 chunked scan
 # ---------------------------------------------------------------------------
 
-def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
-                 C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
-                 initial_states: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 final_states: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Enqueue ssd_scan_fwd; returns ``out`` (batch, seqlen, nheads, headdim).
-
-    x, z: (batch, seqlen, nheads, headdim) bf16; dt: (batch, seqlen, nheads) bf16;
-    A, dt_bias: (nheads,) float32; B, C: (batch, seqlen, ngroups, dstate) bf16;
-    D: (nheads,) or (nheads, headdim) float32; initial_states / final_states:
-    (batch, nheads, headdim, dstate) float32."""
+def _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, initial_states, out, final_states, seq_idx,
+              dt_limit, workspace, seq_segments):
+    """ssd_scan_args_t for the tensors (checked; made contiguous where
+    needed); returns (args, out, tensors kept alive until the call)."""
     x, dt, B, C = _dense(x), _dense(dt), _dense(B), _dense(C)
     if x.dtype != torch.bfloat16:
         raise ValueError(f"ssd_scan_fwd takes bfloat16 io, got {x.dtype}")
@@ -707,14 +700,19 @@ def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Te
     if D is not None:
         _spec(D, "D", (nheads,) if D.dim() == 1 else (nheads, headdim), f32, dev)
     _spec(initial_states, "initial_states", (batch, nheads, headdim, dstate), f32, dev)
+    if seq_idx is not None:
+        seq_idx = _dense(seq_idx)
+        _spec(seq_idx, "seq_idx", (batch, seqlen), torch.int32, dev)
     _out_spec(out, "out", x.shape, x.dtype, dev)
     _out_spec(final_states, "final_states", (batch, nheads, headdim, dstate), f32, dev)
+    if workspace is not None:
+        _workspace_spec(workspace, dev)
     _on_gpu(dev)
     if out is None:
         out = torch.empty_like(x)
     a = _lib.SsdArgs()
     a.batch, a.seqlen, a.nheads, a.headdim = batch, seqlen, nheads, headdim
-    a.dstate, a.ngroups = B.shape[3], B.shape[2]
+    a.dstate, a.ngroups = dstate, ngroups
     a.io_dtype = _lib.SSM_BF16
     a.x, a.dt, a.A, a.B, a.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C)
     a.D = _ptr(D)
@@ -722,5 +720,52 @@ def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Te
     a.z, a.dt_bias = _ptr(z), _ptr(dt_bias)
     a.dt_softplus = int(bool(dt_softplus))
     a.initial_states, a.out, a.final_states = _ptr(initial_states), _ptr(out), _ptr(final_states)
-    check(_lib.lib().ssd_scan_fwd(ctypes.byref(a), _stream(x.device, stream)))
+    if dt_limit is not None:
+        a.dt_limit, a.dt_min, a.dt_max = 1, float(dt_limit[0]), float(dt_limit[1])
+    a.seq_idx = _ptr(seq_idx)
+    a.seq_segments = int(seq_segments)
+    return a, out, (x, dt, A, B, C, D, z, dt_bias, initial_states, seq_idx)
+
+
+def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                 dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                 initial_states: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 final_states: Optional[torch.Tensor] = None, seq_idx: Optional[torch.Tensor] = None,
+                 dt_limit: Optional[Tuple[float, float]] = None, workspace: Optional[torch.Tensor] = None,
+                 seq_segments: int = 0, stream=None) -> torch.Tensor:
+    """Enqueue ssd_scan_fwd; returns ``out`` (batch, seqlen, nheads, headdim).
+
+    x, z: (batch, seqlen, nheads, headdim) bf16; dt: (batch, seqlen, nheads) bf16;
+    A, dt_bias: (nheads,) float32; B, C: (batch, seqlen, ngroups, dstate) bf16;
+    D: (nheads,) or (nheads, headdim) float32; initial_states / final_states:
+    (batch, nheads, headdim, dstate) float32; seq_idx: (batch, seqlen) int32
+    sequence ids, non-decreasing along seqlen; dt_limit: (dt_min, dt_max), the
+    step's clamp after softplus.  The scratch of a sequence split is allocated
+    here (torch) unless ``workspace`` is given; ``seq_segments`` (0: the
+    library's choice) asks for that many segments."""
+    a, out, keep = _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, initial_states, out, final_states,
+                             seq_idx, dt_limit, workspace, seq_segments)
+    dev = out.device
+    L = _lib.lib()
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        check(L.ssd_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+        if need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    check(L.ssd_scan_fwd(ctypes.byref(a), _stream(dev, stream)))
     return out
+
+
+def ssd_scan_workspace_size(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
+                            initial_states=None, out=None, final_states=None, seq_idx=None,
+                            dt_limit=None, seq_segments=0) -> int:
+    """Scratch bytes ssd_scan_fwd needs for these tensors (0 without a
+    sequence split)."""
+    a, _, keep = _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, initial_states, out, final_states,
+                           seq_idx, dt_limit, None, seq_segments)
+    need = ctypes.c_size_t(0)
+    check(_lib.lib().ssd_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    return need.value

@@ -14,6 +14,11 @@ int hip_fail(hipError_t e);
 // query fails).
 int cu_count_cached();
 
+// Workgroups of `block` threads of kernel f one compute unit holds at once
+// (registers and LDS decide), or 0 when the runtime cannot say (no device);
+// cached per kernel.
+int blocks_per_cu(const void *f, int block);
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace ssm

@@ -54,11 +54,19 @@ constexpr int kP = SSD_HEADDIM;   // channels per head
 struct SsdParams {
   const uint16_t *x, *dt, *B, *C, *z;
   const float *A, *D, *dt_bias, *init;
+  const int32_t *seq_idx;
   uint16_t *out;
   float *fin;
-  int64_t seqlen, nheads, ngroups;
-  int D_per_channel, softplus;
+  float *ws_state, *ws_decay;   // sequence split: end states from zero, total decays
+  int64_t seqlen, nheads, ngroups, seg_chunks;
+  int D_per_channel, softplus, dt_limit, nseg;
+  float dt_min, dt_max;
 };
+
+// The two launches of a sequence split: SSD_STATE finds each segment's end
+// state from zero and its total decay; SSD_FULL starts every segment from the
+// carried state and computes the outputs (one launch of it without a split).
+enum { SSD_STATE = 0, SSD_FULL = 1 };
 
 // element offset of (row, col) in a row-major LDS matrix whose rows hold
 // ROW_LEN bf16 elements: the row's 16-byte groups are permuted by
@@ -95,19 +103,26 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int N>
+// SEQ: packed sequences (seq_idx given); a template value so that the
+// kernel without them keeps its registers.
+template <int N, int MODE, bool SEQ>
 __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
+  constexpr bool FULL = MODE == SSD_FULL;
   constexpr int KN = N / 32;   // K steps over dstate
   constexpr int NT = N / 16;   // state tiles along dstate
   __shared__ __attribute__((aligned(16))) uint16_t sXT[kP * kQ];   // X^T   [p][t]
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * kQ];    // B^T   [n][t]
-  __shared__ __attribute__((aligned(16))) uint16_t sM[2][kQ * kQ];    // M     [t][tau], hi / lo
-  __shared__ __attribute__((aligned(16))) uint16_t sS[2][kP * N];     // state [p][n], hi / lo
+  // M [t][tau] and the state [p][n] as hi / lo bf16 (full pass only)
+  __shared__ __attribute__((aligned(16))) uint16_t sM[FULL ? 2 : 1][FULL ? kQ * kQ : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[FULL ? 2 : 1][FULL ? kP * N : 8];
   __shared__ __attribute__((aligned(16))) float sCs[kQ], sDt[kQ], sW[kQ];
+  __shared__ __attribute__((aligned(16))) int32_t sSid[SEQ ? kQ : 4];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, kq = l >> 4;
   const int64_t bh = blockIdx.x;
+  const int64_t BH = gridDim.x;
+  const int seg = blockIdx.y;
   const int64_t b = bh / p.nheads;
   const int64_t h = bh - b * p.nheads;
   const int64_t g = h / (p.nheads / p.ngroups);
@@ -122,7 +137,12 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   const uint16_t *Bb = p.B + (b * L * p.ngroups + g) * N;
   const uint16_t *Cb = p.C + (b * L * p.ngroups + g) * N;
   const uint16_t *dtb = p.dt + b * L * p.nheads + h;
+  const int32_t *sidb = SEQ ? p.seq_idx + b * L : nullptr;
   const bf16x8 zero8 = {};
+
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  const int64_t c_begin = seg * p.seg_chunks;
+  const int64_t c_end = seg + 1 < p.nseg ? c_begin + p.seg_chunks : nchunks;
 
   // Token pairs and channel groups this thread stages and stores:
   // tokens 2 (tid / 8) + {0, 1}, channels 8 (tid % 8) + 0..7.
@@ -132,37 +152,65 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int pp = xp0 + i;
-    Dv8[i] = p.D ? (p.D_per_channel ? p.D[h * kP + pp] : p.D[h]) : 0.0f;
+    Dv8[i] = (FULL && p.D) ? (p.D_per_channel ? p.D[h * kP + pp] : p.D[h]) : 0.0f;
   }
   float *sY = reinterpret_cast<float *>(&sM[0][0]);   // Y [t][p] (fp32), 16-byte groups permuted by t
   // B row-major [t][n] for the A operand of C B^T, in M's space until M is written
   uint16_t *sBr = &sM[0][0];
-  static_assert(kQ * N <= 2 * kQ * kQ, "the row-major B tile fits in M's space");
+  static_assert(!FULL || kQ * N <= 2 * kQ * kQ, "the row-major B tile fits in M's space");
 
-  // state, transposed: wave w holds S[p = 16w + r][n = 16 nt + 4kq + i]
+  // state, transposed: wave w holds S[p = 16w + r][n = 16 nt + 4kq + i].
+  // The state pass starts every segment from zero; the full pass starts
+  // segment k from the initial state carried over segments 0..k-1:
+  //   S_in(k) = E_{k-1} + P_{k-1} (E_{k-2} + P_{k-2} (... + P_0 S_init))
+  // with E_j segment j's end state from zero and P_j its total decay (zero
+  // where a sequence starts inside it).
   f32x4 accs[NT];
+  const int srow = (16 * w + r) * N + 4 * kq;   // this lane's first state element in a (p, n) block
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      accs[nt][i] = (FULL && p.init) ? p.init[bh * kP * N + srow + 16 * nt + i] : 0.0f;
+  }
+  if constexpr (FULL) {
+    for (int j = 0; j < seg; ++j) {
+      const float P = p.ws_decay[j * BH + bh];
+      const float *E = p.ws_state + (j * BH + bh) * kP * N + srow;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 e4 = *reinterpret_cast<const float4 *>(E + 16 * nt);
+        accs[nt][0] = fmaf(P, accs[nt][0], e4.x);
+        accs[nt][1] = fmaf(P, accs[nt][1], e4.y);
+        accs[nt][2] = fmaf(P, accs[nt][2], e4.z);
+        accs[nt][3] = fmaf(P, accs[nt][3], e4.w);
+      }
+    }
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int pp = 16 * w + r;
-    uint16_t hi[4], lo[4];
+    if constexpr (FULL) {
+      uint16_t hi[4], lo[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = 16 * nt + 4 * kq + i;
-      const float v = p.init ? p.init[(bh * kP + pp) * N + n] : 0.0f;
-      accs[nt][i] = v;
-      split_bf(v, hi[i], lo[i]);
+      for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
+      const int o = swz<N>(pp, 16 * nt + 4 * kq);
+      *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
-    const int o = swz<N>(pp, 16 * nt + 4 * kq);
-    *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   }
   __syncthreads();
 
-  const int64_t nchunks = (L + kQ - 1) / kQ;
+  // sequence id the incoming state belongs to: the token before the segment
+  // (the first token for the initial state)
+  int32_t sid_prev = 0;
+  if constexpr (SEQ) sid_prev = sidb[c_begin > 0 ? c_begin * kQ - 1 : 0];
+  float seg_decay = 1.0f;   // product of the chunks' decays (state pass)
+
   constexpr int G8 = N / 8;                      // 16-byte groups per B row
   constexpr int BPIECES = (kQ / 2) * G8;        // (token pair, 16-byte group) pieces of a B tile
   constexpr int BPAIRS = (BPIECES + 255) / 256;  // pieces per thread
-  for (int64_t c = 0; c < nchunks; ++c) {
+  for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t t0 = c * kQ;
     const int len = static_cast<int>((L - t0 < kQ) ? L - t0 : kQ);
 
@@ -173,7 +221,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       const int t = xt0 + k;
       const int64_t e = (t0 + t) * xrow + xp0;
       xr[k] = t < len ? ld8_raw(xb + e) : make_uint4(0, 0, 0, 0);
-      zr[k] = (zb && t < len) ? ld8_raw(zb + e) : make_uint4(0, 0, 0, 0);
+      zr[k] = (FULL && zb && t < len) ? ld8_raw(zb + e) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < BPAIRS; ++j) {
@@ -184,17 +232,22 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
         br[j][k] = (piece < BPIECES && t + k < len) ? ld8_raw(Bb + (t0 + t + k) * bcrow + n0)
                                                      : make_uint4(0, 0, 0, 0);
     }
-    bf16x8 cop[KN];   // this wave's C rows (tokens 16w + r)
-    {
+    bf16x8 cop[FULL ? KN : 1];   // this wave's C rows (tokens 16w + r)
+    if constexpr (FULL) {
       const int t = 16 * w + r;
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) cop[kk] = t < len ? ld8(Cb + (t0 + t) * bcrow + 32 * kk + 8 * kq) : zero8;
     }
     float dtraw = 0.0f;
-    if (w == 0 && l < len) dtraw = bf2f(dtb[(t0 + l) * p.nheads]);
+    int32_t sid = 0;
+    if (w == 0) {
+      if (l < len) dtraw = bf2f(dtb[(t0 + l) * p.nheads]);
+      if constexpr (SEQ) sid = sidb[t0 + (l < len ? l : len - 1)];
+    }
 
-    // the previous chunk's epilogue reads Y from M's space, which the
-    // row-major B copy below overwrites (the wait overlaps the loads above)
+    // the previous chunk's reads of the staged tiles (and, in the full pass,
+    // its epilogue's reads of Y from M's space, which the row-major B copy
+    // below overwrites) are done; the wait overlaps the loads above
     __syncthreads();
 
     // ---- X^T and B^T into LDS, two tokens per 32-bit store
@@ -214,8 +267,10 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
                            (static_cast<uint32_t>(raw_bits(br[j][1], i)) << 16);
         *reinterpret_cast<uint32_t *>(&sBT[swz<kQ>(n0 + i, t)]) = v;
       }
+      if constexpr (FULL) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(&sBr[swz<N>(t + k, n0)]) = br[j][k];
+        for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(&sBr[swz<N>(t + k, n0)]) = br[j][k];
+      }
     }
     // ---- the steps and their running sum inside the chunk (padding: dt' = 0)
     if (w == 0) {
@@ -223,6 +278,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       if (l < len) {
         const float v = dtraw + bias;
         dtp = p.softplus ? softplus_f(v) : v;
+        if (p.dt_limit) dtp = fminf(fmaxf(dtp, p.dt_min), p.dt_max);
       }
       float cs = dtp * Ah;
 #pragma unroll
@@ -232,19 +288,32 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       }
       sCs[l] = cs;
       sDt[l] = dtp;
+      if constexpr (SEQ) sSid[l] = sid;
     }
     __syncthreads();
 
     const float csl = sCs[kQ - 1];
-    // the state-update weights w_t = exp(cs_last - cs_t) * dt'_t
-    if (tid < kQ) sW[tid] = fast_exp2((csl - sCs[tid]) * kLog2e) * sDt[tid];
-    // ---- M, from G^T = B C^T: lane holds G[t = 16w + r][tau = 16 tb + 4kq + i],
-    // masked to tau <= t, decayed, split, stored as 4 consecutive tau.  The
-    // products read B from its row-major LDS copy; M overwrites that copy, so
-    // every wave's products are done before any M is stored.
-    {
+    // sequences: the chunk's last token's id, and whether the incoming state
+    // reaches the end of the chunk (no sequence starts inside it)
+    const int32_t sid_last = SEQ ? sSid[len - 1] : 0;
+    const bool carry = !SEQ || sid_last == sid_prev;
+    // the state-update weights w_t = exp(cs_last - cs_t) * dt'_t, for the
+    // tokens of the chunk's last sequence
+    if (tid < kQ) {
+      const bool mine = !SEQ || sSid[tid] == sid_last;
+      sW[tid] = mine ? fast_exp2((csl - sCs[tid]) * kLog2e) * sDt[tid] : 0.0f;
+    }
+    if constexpr (!FULL) __syncthreads();
+
+    if constexpr (FULL) {
+      // ---- M, from G^T = B C^T: lane holds G[t = 16w + r][tau = 16 tb + 4kq + i],
+      // masked to tau <= t (and the same sequence), decayed, split, stored as
+      // 4 consecutive tau.  The products read B from its row-major LDS copy; M
+      // overwrites that copy, so every wave's products are done before any M
+      // is stored.
       const int t = 16 * w + r;
       const float cst = sCs[t];
+      const int32_t sidt = SEQ ? sSid[t] : 0;
       f32x4 accg[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
@@ -260,66 +329,70 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const f32x4 acc = accg[tb];
-        // the four taus' cumulative steps and steps, one vector read each
+        // the four taus' cumulative steps, steps and ids, one vector read each
         const float4 cs4 = *reinterpret_cast<const float4 *>(&sCs[16 * tb + 4 * kq]);
         const float4 dt4 = *reinterpret_cast<const float4 *>(&sDt[16 * tb + 4 * kq]);
         const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+        int32_t sdv[4] = {0, 0, 0, 0};
+        if constexpr (SEQ) {
+          const int4 sd4 = *reinterpret_cast<const int4 *>(&sSid[16 * tb + 4 * kq]);
+          sdv[0] = sd4.x; sdv[1] = sd4.y; sdv[2] = sd4.z; sdv[3] = sd4.w;
+        }
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tau = 16 * tb + 4 * kq + i;
           float m = 0.0f;
-          if (tb <= w && tau <= t) m = acc[i] * fast_exp2((cst - csv[i]) * kLog2e) * dtv[i];
+          if (tb <= w && tau <= t && (!SEQ || sdv[i] == sidt))
+            m = acc[i] * fast_exp2((cst - csv[i]) * kLog2e) * dtv[i];
           split_bf(m, hi[i], lo[i]);
         }
         const int o = swz<kQ>(t, 16 * tb + 4 * kq);
         *reinterpret_cast<uint2 *>(&sM[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
         *reinterpret_cast<uint2 *>(&sM[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
       }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T: lane holds Y[t = 16w + r][p = 16 pb + 4kq + i]
-    // (k-step outer, channel block inner: consecutive products feed four
-    // independent accumulators and a step's operand reads issue together)
-    f32x4 accy[4];
+      // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T: lane holds Y[t = 16w + r][p = 16 pb + 4kq + i]
+      // (k-step outer, channel block inner: consecutive products feed four
+      // independent accumulators and a step's operand reads issue together)
+      f32x4 accy[4];
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) accy[pb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int pb = 0; pb < 4; ++pb) accy[pb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk) {
-      bf16x8 shi[4], slo[4];
+      for (int kk = 0; kk < KN; ++kk) {
+        bf16x8 shi[4], slo[4];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const int o = swz<N>(16 * pb + r, 32 * kk + 8 * kq);
-        shi[pb] = ld8(&sS[0][o]);
-        slo[pb] = ld8(&sS[1][o]);
+        for (int pb = 0; pb < 4; ++pb) {
+          const int o = swz<N>(16 * pb + r, 32 * kk + 8 * kq);
+          shi[pb] = ld8(&sS[0][o]);
+          slo[pb] = ld8(&sS[1][o]);
+        }
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(shi[pb], cop[kk], accy[pb]);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(slo[pb], cop[kk], accy[pb]);
       }
+      {
+        // the incoming state reaches token t only inside its own sequence
+        const float e = (!SEQ || sidt == sid_prev) ? fast_exp2(cst * kLog2e) : 0.0f;
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(shi[pb], cop[kk], accy[pb]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(slo[pb], cop[kk], accy[pb]);
-    }
-    {
-      const float e = fast_exp2(sCs[16 * w + r] * kLog2e);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) accy[pb] *= e;
-    }
-    const int kkmax = (16 * (w + 1) + 31) / 32;   // tau blocks at or before this wave's tokens
-    for (int kk = 0; kk < kkmax; ++kk) {
-      const int o = swz<kQ>(16 * w + r, 32 * kk + 8 * kq);
-      const bf16x8 mhi = ld8(&sM[0][o]), mlo = ld8(&sM[1][o]);
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const bf16x8 xop = ld8(&sXT[swz<kQ>(16 * pb + r, 32 * kk + 8 * kq)]);
-        accy[pb] = mfma(xop, mhi, accy[pb]);
-        accy[pb] = mfma(xop, mlo, accy[pb]);
+        for (int pb = 0; pb < 4; ++pb) accy[pb] *= e;
       }
-    }
-    __syncthreads();   // every read of M and of the old state is done
+      const int kkmax = (16 * (w + 1) + 31) / 32;   // tau blocks at or before this wave's tokens
+      for (int kk = 0; kk < kkmax; ++kk) {
+        const int o = swz<kQ>(16 * w + r, 32 * kk + 8 * kq);
+        const bf16x8 mhi = ld8(&sM[0][o]), mlo = ld8(&sM[1][o]);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          const bf16x8 xop = ld8(&sXT[swz<kQ>(16 * pb + r, 32 * kk + 8 * kq)]);
+          accy[pb] = mfma(xop, mhi, accy[pb]);
+          accy[pb] = mfma(xop, mlo, accy[pb]);
+        }
+      }
+      __syncthreads();   // every read of M and of the old state is done
 
-    // ---- Y into LDS (over M), four consecutive channels per store
-    {
-      const int t = 16 * w + r;
+      // ---- Y into LDS (over M), four consecutive channels per store
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
         const int grp = (4 * pb + kq) ^ (t & 15);   // 16-byte group of channels 16pb + 4kq, permuted by t
@@ -327,8 +400,10 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
             make_float4(accy[pb][0], accy[pb][1], accy[pb][2], accy[pb][3]);
       }
     }
-    // ---- S^T <- exp(cs_last) S^T + B^T (X w)
-    const float dec = fast_exp2(csl * kLog2e);
+    // ---- S^T <- exp(cs_last) S^T + B^T (X w); the old state only if no
+    // sequence starts inside the chunk
+    const float dec = carry ? fast_exp2(csl * kLog2e) : 0.0f;
+    if constexpr (!FULL) seg_decay *= dec;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) accs[nt] *= dec;
 #pragma unroll
@@ -350,52 +425,125 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
         accs[nt] = mfma(bop, xlo, accs[nt]);
       }
     }
+    sid_prev = sid_last;
+    if constexpr (FULL) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint16_t hi[4], lo[4];
+      for (int nt = 0; nt < NT; ++nt) {
+        uint16_t hi[4], lo[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
-      const int o = swz<N>(16 * w + r, 16 * nt + 4 * kq);
-      *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-    }
-    __syncthreads();
+        for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
+        const int o = swz<N>(16 * w + r, 16 * nt + 4 * kq);
+        *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+        *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      }
+      __syncthreads();
 
-    // ---- out = (Y + D x) * silu(z): this thread's x / z pieces, 16-byte stores
+      // ---- out = (Y + D x) * silu(z): this thread's x / z pieces, 16-byte stores
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int t = xt0 + k;
-      if (t < len) {
-        const int g0 = (xp0 >> 2) ^ (t & 15), g1 = ((xp0 >> 2) + 1) ^ (t & 15);
-        const float4 y0 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g0]);
-        const float4 y1 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g1]);
-        const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-        uint32_t pk[4];
+      for (int k = 0; k < 2; ++k) {
+        const int t = xt0 + k;
+        if (t < len) {
+          const int g0 = (xp0 >> 2) ^ (t & 15), g1 = ((xp0 >> 2) + 1) ^ (t & 15);
+          const float4 y0 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g0]);
+          const float4 y1 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g1]);
+          const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          uint32_t pk[4];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          float o2[2];
+          for (int i = 0; i < 8; i += 2) {
+            float o2[2];
 #pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            float y = yv[i + q2];
-            if (p.D) y = fmaf(Dv8[i + q2], bf2f(raw_bits(xr[k], i + q2)), y);
-            if (zb) y *= silu_f(bf2f(raw_bits(zr[k], i + q2)));
-            o2[q2] = y;
+            for (int q2 = 0; q2 < 2; ++q2) {
+              float y = yv[i + q2];
+              if (p.D) y = fmaf(Dv8[i + q2], bf2f(raw_bits(xr[k], i + q2)), y);
+              if (zb) y *= silu_f(bf2f(raw_bits(zr[k], i + q2)));
+              o2[q2] = y;
+            }
+            pk[i / 2] = static_cast<uint32_t>(f2bf(o2[0])) | (static_cast<uint32_t>(f2bf(o2[1])) << 16);
           }
-          pk[i / 2] = static_cast<uint32_t>(f2bf(o2[0])) | (static_cast<uint32_t>(f2bf(o2[1])) << 16);
+          *reinterpret_cast<uint4 *>(ob + (t0 + t) * xrow + xp0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
-        *reinterpret_cast<uint4 *>(ob + (t0 + t) * xrow + xp0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
   }
 
-  if (p.fin) {
+  if constexpr (FULL) {
+    if (p.fin && seg + 1 == p.nseg) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p.fin[(bh * kP + 16 * w + r) * N + 16 * nt + 4 * kq + i] = accs[nt][i];
+        for (int i = 0; i < 4; ++i)
+          p.fin[(bh * kP + 16 * w + r) * N + 16 * nt + 4 * kq + i] = accs[nt][i];
+      }
+    }
+  } else {
+    float *E = p.ws_state + (seg * BH + bh) * kP * N + srow;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<float4 *>(E + 16 * nt) = make_float4(accs[nt][0], accs[nt][1], accs[nt][2], accs[nt][3]);
+    if (tid == 0) p.ws_decay[seg * BH + bh] = seg_decay;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct SsdPlan {
+  int nseg;
+  int64_t seg_chunks;
+  size_t off_decay, ws_bytes;
+};
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+using SsdFn = void (*)(const SsdParams);
+
+template <int N>
+SsdFn ssd_fn_n(int mode, bool seq) {
+  if (mode == SSD_FULL) return seq ? ssd_kernel<N, SSD_FULL, true> : ssd_kernel<N, SSD_FULL, false>;
+  return seq ? ssd_kernel<N, SSD_STATE, true> : ssd_kernel<N, SSD_STATE, false>;
+}
+
+SsdFn ssd_fn(int64_t dstate, int mode, bool seq) {
+  switch (dstate) {
+    case 32: return ssd_fn_n<32>(mode, seq);
+    case 64: return ssd_fn_n<64>(mode, seq);
+    default: return ssd_fn_n<128>(mode, seq);
+  }
+}
+
+// Segments: a workgroup walks its (batch, head)'s chunks in order, so with
+// few (batch, head) pairs the chunks are cut into G segments of whole
+// chunks: enough workgroups for 1.5 times what the GPU holds at once, each
+// segment at least two chunks.  More segments only add state-pass work:
+// at b=8 l=2048 h=80 n=128 (640 pairs, 512 resident) one pass took 419 us,
+// 2 segments 381, 3 392, 4 399, 8 464.
+SsdPlan ssd_plan(const ssd_scan_args_t *a, int cus) {
+  SsdPlan pl{};
+  const int64_t nchunks = (a->seqlen + kQ - 1) / kQ;
+  const int64_t BH = a->batch * a->nheads;
+  int G = 1;
+  if (a->seq_segments >= 1) {
+    G = a->seq_segments;
+  } else {
+    int bf = blocks_per_cu(reinterpret_cast<const void *>(ssd_fn(a->dstate, SSD_FULL, a->seq_idx != nullptr)), 256);
+    if (bf <= 0) bf = 2;
+    const int64_t want = static_cast<int64_t>(bf) * cus * 3 / 2;
+    if (BH < want) {
+      int64_t g = (want + BH - 1) / BH;
+      if (g > nchunks / 2) g = nchunks / 2;
+      G = g > 1 ? static_cast<int>(g) : 1;
     }
   }
+  if (G > nchunks) G = static_cast<int>(nchunks);
+  pl.seg_chunks = (nchunks + G - 1) / G;
+  pl.nseg = static_cast<int>((nchunks + pl.seg_chunks - 1) / pl.seg_chunks);
+  if (pl.nseg > 1) {
+    const size_t ns = static_cast<size_t>(pl.nseg - 1) * BH;
+    pl.off_decay = up256(ns * kP * a->dstate * sizeof(float));
+    pl.ws_bytes = pl.off_decay + up256(ns * sizeof(float));
+  }
+  return pl;
 }
 
 }  // namespace
@@ -403,9 +551,19 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
 
 using namespace ssm;
 
+extern "C" int ssd_scan_workspace_size(const ssd_scan_args_t *a, size_t *bytes) {
+  const int st = ssd_scan_validate(a);
+  if (st != SSM_OK) return st;
+  if (!bytes) return SSM_ERR_NULL;
+  *bytes = ssd_plan(a, cu_count_cached()).ws_bytes;
+  return SSM_OK;
+}
+
 extern "C" int ssd_scan_fwd(const ssd_scan_args_t *a, void *stream_ptr) {
   const int st = ssd_scan_validate(a);
   if (st != SSM_OK) return st;
+  const SsdPlan pl = ssd_plan(a, cu_count_cached());
+  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
   SsdParams p{};
   p.x = static_cast<const uint16_t *>(a->x);
   p.dt = static_cast<const uint16_t *>(a->dt);
@@ -413,20 +571,30 @@ extern "C" int ssd_scan_fwd(const ssd_scan_args_t *a, void *stream_ptr) {
   p.C = static_cast<const uint16_t *>(a->C);
   p.z = static_cast<const uint16_t *>(a->z);
   p.A = a->A; p.D = a->D; p.dt_bias = a->dt_bias; p.init = a->initial_states;
+  p.seq_idx = a->seq_idx;
   p.out = static_cast<uint16_t *>(a->out);
   p.fin = a->final_states;
   p.seqlen = a->seqlen; p.nheads = a->nheads; p.ngroups = a->ngroups;
   p.D_per_channel = a->D_per_channel;
   p.softplus = a->dt_softplus;
+  p.dt_limit = a->dt_limit; p.dt_min = a->dt_min; p.dt_max = a->dt_max;
+  p.nseg = pl.nseg; p.seg_chunks = pl.seg_chunks;
+  if (pl.nseg > 1) {
+    char *ws = static_cast<char *>(a->workspace);
+    p.ws_state = reinterpret_cast<float *>(ws);
+    p.ws_decay = reinterpret_cast<float *>(ws + pl.off_decay);
+  }
   const int64_t blocks = a->batch * a->nheads;
   if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const dim3 grid(static_cast<unsigned>(blocks));
-  switch (a->dstate) {
-    case 32: hipLaunchKernelGGL(ssd_kernel<32>, grid, dim3(256), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(ssd_kernel<64>, grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL(ssd_kernel<128>, grid, dim3(256), 0, stream, p); break;
+  const unsigned gx = static_cast<unsigned>(blocks);
+  const bool seq = a->seq_idx != nullptr;
+  if (pl.nseg > 1) {
+    hipLaunchKernelGGL(ssd_fn(a->dstate, SSD_STATE, seq), dim3(gx, pl.nseg - 1), dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
   }
+  hipLaunchKernelGGL(ssd_fn(a->dstate, SSD_FULL, seq), dim3(gx, pl.nseg), dim3(256), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;

@@ -39,6 +39,22 @@ int cu_count_cached() {
   return counts[dev];
 }
 
+int blocks_per_cu(const void *f, int block) {
+  static std::mutex mu;
+  static std::unordered_map<const void *, int> cache;
+  if (!f) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(f);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, block, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache.emplace(f, nb);
+  return nb;
+}
+
 }  // namespace ssm
 
 namespace {
@@ -150,25 +166,6 @@ ScanFn pick_mixed(int io, bool bv, bool cv, bool conv, bool vec) {
   return pick_mix_f32(bv, cv, conv, vec);
 }
 
-// Workgroups of kernel f (64 lanes each) one compute unit holds at once, or
-// 0 when the runtime cannot say (no device): cached per kernel.
-int blocks_per_cu(ScanFn f) {
-  static std::mutex mu;
-  static std::unordered_map<const void *, int> cache;
-  if (!f) return 0;
-  const void *key = reinterpret_cast<const void *>(f);
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, 64, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  cache.emplace(key, nb);
-  return nb;
-}
-
 // Every io pointer 16-byte aligned and seqlen % 8 == 0: the kernels move
 // whole 8-timestep ranges as vectors.
 bool vector_io(const ssm_scan_args_t *a) {
@@ -242,9 +239,10 @@ Plan make_plan(const ssm_scan_args_t *a, int cus) {
     const int simds = 4 * cus;
     const int q = pl.nblocks / simds, r = pl.nblocks % simds;
     if (q >= 2 && r > 0 && 2 * r <= simds &&
-        4 * (q + 1) <= blocks_per_cu(pick_mixed(a->io_dtype, a->B_kind == SSM_BC_VARYING,
-                                                a->C_kind == SSM_BC_VARYING, a->conv_weight != nullptr,
-                                                pl.vec))) {
+        4 * (q + 1) <= blocks_per_cu(reinterpret_cast<const void *>(
+                                         pick_mixed(a->io_dtype, a->B_kind == SSM_BC_VARYING,
+                                                    a->C_kind == SSM_BC_VARYING, a->conv_weight != nullptr,
+                                                    pl.vec)), 64)) {
       pl.mix_whole = pl.nblocks - r;
       pl.mix_small = 2 * r;
     }

@@ -160,6 +160,9 @@ extern "C" int ssd_scan_validate(const ssd_scan_args_t *a) {
   if (a->dstate != 32 && a->dstate != 64 && a->dstate != 128) return SSM_ERR_UNSUPPORTED;
   if (a->dt_softplus != 0 && a->dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
   if (a->D_per_channel != 0 && a->D_per_channel != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_limit != 0 && a->dt_limit != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_limit && !(a->dt_min <= a->dt_max)) return SSM_ERR_SHAPE;
+  if (a->seq_segments < 0) return SSM_ERR_SHAPE;
   if (!a->x || !a->dt || !a->A || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
   const uintptr_t mis = (reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->B) |
                          reinterpret_cast<uintptr_t>(a->C) | reinterpret_cast<uintptr_t>(a->out) |

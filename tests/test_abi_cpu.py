@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 10
+    assert L.ssm_abi_version() == 11
 
 
 def test_status_strings():
@@ -270,6 +270,37 @@ def test_ssd_validation():
         assert v(_good_ssd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
     assert L.ssd_scan_fwd(ctypes.byref(_good_ssd(B=None)), None) == _lib.SSM_ERR_NULL
     assert L.ssd_scan_validate(None) == _lib.SSM_ERR_NULL
+    # the step range and the split
+    assert v(_good_ssd(dt_limit=1, dt_min=0.001, dt_max=0.1)) == _lib.SSM_OK
+    assert v(_good_ssd(dt_limit=1, dt_min=0.5, dt_max=0.5)) == _lib.SSM_OK
+    assert v(_good_ssd(dt_limit=1, dt_min=0.2, dt_max=0.1)) == _lib.SSM_ERR_SHAPE
+    assert v(_good_ssd(dt_limit=1, dt_min=float("nan"), dt_max=0.1)) == _lib.SSM_ERR_SHAPE
+    assert v(_good_ssd(dt_limit=0, dt_min=0.2, dt_max=0.1)) == _lib.SSM_OK   # range unused
+    assert v(_good_ssd(dt_limit=2)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_ssd(seq_segments=-1)) == _lib.SSM_ERR_SHAPE
+    assert v(_good_ssd(seq_idx=0x4000)) == _lib.SSM_OK
+
+
+def test_ssd_split_needs_workspace_before_any_launch():
+    """A forced split needs scratch: without it, or with too little, the call
+    returns SSM_ERR_WORKSPACE before anything is enqueued (the pointers are
+    not dereferenceable)."""
+    L = _lib.lib()
+    a = _good_ssd(seqlen=1024, seq_segments=4)
+    need = ctypes.c_size_t(0)
+    assert L.ssd_scan_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.SSM_OK
+    # three carried (headdim x dstate) fp32 states and decays per (batch, head)
+    assert need.value >= 3 * 2 * 8 * 64 * 128 * 4 + 3 * 2 * 8 * 4
+    assert L.ssd_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = 0x5000, need.value - 1
+    assert L.ssd_scan_fwd(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+    one = _good_ssd(seqlen=1024, seq_segments=1)
+    assert L.ssd_scan_workspace_size(ctypes.byref(one), ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value == 0
+    # more segments than chunks: one per chunk
+    few = _good_ssd(seqlen=100, seq_segments=9)
+    assert L.ssd_scan_workspace_size(ctypes.byref(few), ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value >= 1 * 2 * 8 * 64 * 128 * 4
 
 
 def _good_bwd(**kw):

@@ -17,7 +17,7 @@ from tests.harness import TOL, log, max_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(w, t, final=True):
+def _gpu(w, t, final=True, seq_idx=None, dt_limit=None, seq_segments=0):
     import torch
     from state_space_model_scan_amd import binding
     x = to_dev(t["x"], BF16)
@@ -30,19 +30,22 @@ def _gpu(w, t, final=True):
                          to_dev(t["C"], BF16), to_dev(t["D"], param=True), to_dev(t["z"], BF16),
                          to_dev(t["dt_bias"], param=True), w.softplus,
                          initial_states=to_dev(t["initial_states"], param=True), out=out,
-                         final_states=fin)
+                         final_states=fin,
+                         seq_idx=None if seq_idx is None else torch.from_numpy(seq_idx).to("cuda"),
+                         dt_limit=dt_limit, seq_segments=seq_segments)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     f = None if fin is None else fin.cpu().numpy().astype(np.float64)
     return o, f
 
 
-def _oracle(w, t, heads=None):
+def _oracle(w, t, heads=None, seq_idx=None, dt_limit=None):
     """Oracle on all heads, or on the listed heads only (returned in that order
     along the head axis)."""
     if heads is None:
         return orc.ssd_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"],
-                            w.softplus, io_dtype=BF16, initial_states=t["initial_states"])
+                            w.softplus, io_dtype=BF16, initial_states=t["initial_states"],
+                            seq_idx=seq_idx, dt_limit=dt_limit, nthreads=16)
     hpg = w.nheads // w.ngroups
     outs, fins = [], []
     for h in heads:
@@ -55,16 +58,17 @@ def _oracle(w, t, heads=None):
                             Dh, sl(t["z"], 2), None if t["dt_bias"] is None else t["dt_bias"][[h]],
                             w.softplus, io_dtype=BF16,
                             initial_states=None if t["initial_states"] is None else sl(t["initial_states"], 1),
-                            nthreads=0)
+                            seq_idx=seq_idx, dt_limit=dt_limit, nthreads=0)
         outs.append(o)
         fins.append(f)
     return np.concatenate(outs, axis=2), np.concatenate(fins, axis=1)
 
 
-def _check(w, t, what, heads=None):
-    log(f"[ssd] {what}: b={w.batch} l={w.seqlen} h={w.nheads} p={w.headdim} n={w.dstate} g={w.ngroups}")
-    out, fin = _gpu(w, t)
-    ref, ref_fin = _oracle(w, t, heads)
+def _check(w, t, what, heads=None, seq_idx=None, dt_limit=None, seq_segments=0):
+    log(f"[ssd] {what}: b={w.batch} l={w.seqlen} h={w.nheads} p={w.headdim} n={w.dstate} g={w.ngroups} "
+        f"segments={seq_segments}")
+    out, fin = _gpu(w, t, seq_idx=seq_idx, dt_limit=dt_limit, seq_segments=seq_segments)
+    ref, ref_fin = _oracle(w, t, heads, seq_idx=seq_idx, dt_limit=dt_limit)
     if heads is not None:
         out, fin = out[:, :, heads], fin[:, heads]
     tol = TOL[BF16]
@@ -120,3 +124,82 @@ def test_ssd_full_size_sampled_heads():
     w = SSD_WORKLOADS["ssd2p7b"]
     t = make_ssd_inputs(w)
     _check(w, t, "ssd2p7b", heads=[0, 37, 79])
+
+
+@pytest.mark.parametrize("n", [64, 128])
+@pytest.mark.parametrize("segments", [2, 3, 7])
+def test_ssd_forced_segments(n, segments):
+    """The split (end states from zero, then the carried state) is the same
+    recurrence reassociated; with the initial and final states."""
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=2, seqlen=1000, nheads=4, dstate=n, ngroups=2,
+                                         init_state=True, seed=300 + n + segments)
+    _check(w, make_ssd_inputs(w), f"segments={segments} n={n}", seq_segments=segments)
+
+
+def _packed_ids(rows, seqlen):
+    """Non-decreasing ids per row from cut positions (where a new sequence
+    starts)."""
+    sid = np.zeros((len(rows), seqlen), np.int32)
+    for b, cuts in enumerate(rows):
+        cur = 3 + b
+        prev = 0
+        for c in list(cuts) + [seqlen]:
+            sid[b, prev:c] = cur
+            cur += 1 + (c % 3)
+            prev = c
+    return sid
+
+
+# sequence starts: inside a chunk, on a chunk edge (64, 128, 192, 256),
+# one-token sequences, and (with 3 segments of 2 chunks) on and next to a
+# segment boundary (128)
+SEQ_CUTS = [[5, 64, 70, 71, 128, 200, 255], [1, 2, 127, 129, 192, 256, 299]]
+
+
+@pytest.mark.parametrize("segments", [1, 3])
+@pytest.mark.parametrize("n", [32, 128])
+def test_ssd_packed_sequences(segments, n):
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=2, seqlen=300, nheads=4, dstate=n, ngroups=2,
+                                         init_state=True, seed=400 + n + segments)
+    sid = _packed_ids(SEQ_CUTS, w.seqlen)
+    _check(w, make_ssd_inputs(w), f"packed sequences segments={segments}", seq_idx=sid,
+           seq_segments=segments)
+
+
+def test_ssd_packed_one_sequence_per_token_edge():
+    # every token its own sequence in the first chunk, then one long sequence
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=1, seqlen=200, nheads=2, dstate=64, ngroups=1,
+                                         init_state=True, seed=410)
+    sid = _packed_ids([list(range(1, 64))], w.seqlen)
+    _check(w, make_ssd_inputs(w), "one-token sequences", seq_idx=sid, seq_segments=2)
+
+
+@pytest.mark.parametrize("segments", [1, 4])
+def test_ssd_dt_limit(segments):
+    w = SSD_WORKLOADS["ssd_tiny"].scaled(batch=2, seqlen=500, nheads=4, dstate=64, ngroups=1,
+                                         init_state=True, seed=420 + segments)
+    t = make_ssd_inputs(w)
+    _check(w, t, f"dt_limit segments={segments}", dt_limit=(0.05, 0.2), seq_segments=segments)
+
+
+def test_ssd_dt_limit_and_packed_sequences_full_size_heads():
+    """The Mamba-2.7B-shaped call with both options, in the library's own plan
+    (a sequence split at this size), checked on sampled heads."""
+    w = SSD_WORKLOADS["ssd2p7b"]
+    t = make_ssd_inputs(w)
+    rng = np.random.default_rng(430)
+    rows = [sorted(rng.choice(np.arange(1, w.seqlen), size=6, replace=False).tolist()) for _ in range(w.batch)]
+    sid = _packed_ids(rows, w.seqlen)
+    _check(w, t, "ssd2p7b packed + dt_limit", heads=[3, 41], seq_idx=sid, dt_limit=(0.01, 0.3))
+
+
+def test_ssd_full_size_split_matches_one_pass():
+    """At full size the library's split and a single pass agree to rounding
+    (every element, GPU against GPU; each is checked against the oracle on
+    sampled heads elsewhere)."""
+    w = SSD_WORKLOADS["ssd2p7b"]
+    t = make_ssd_inputs(w)
+    o1, f1 = _gpu(w, t, seq_segments=1)
+    o2, f2 = _gpu(w, t)
+    tol = TOL[BF16]
+    assert max_err(o2, o1) <= tol and max_err(f2, f1) <= tol
