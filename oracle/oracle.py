@@ -91,6 +91,10 @@ def _load():
             i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
             p, p, p, p, p, p, p, p, p]
         lib.oracle_selective_scan_bwd.restype = i32
+        lib.oracle_selective_scan_complex_bwd.argtypes = [
+            i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
+            p, p, p, p, p, p, p, p, p]
+        lib.oracle_selective_scan_complex_bwd.restype = i32
         lib.oracle_causal_conv1d_ex.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, p, p, p, p]
         lib.oracle_causal_conv1d_ex.restype = i32
         lib.oracle_round_f16.argtypes = [ctypes.c_double]
@@ -401,6 +405,47 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dinitial_state"]))
     if rc != 0:
         raise ValueError(f"oracle_selective_scan_bwd failed with status {rc}")
+    return out
+
+
+def selective_scan_complex_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                               delta_softplus=False, *, io_dtype=F32, ngroups=1, B_kind=BC_VARYING,
+                               C_kind=BC_VARYING, initial_state=None):
+    """Oracle gradients of the complex-A forward (``selective_scan_complex``).
+
+    Inputs as there; dout: (batch, dim, seqlen) float.  Returns a dict of
+    float64 arrays: du, ddelta, dz, dD, ddelta_bias as in the real backward;
+    dA (dim, dstate, 2), dB / dC in B's / C's layout and dinitial_state
+    (batch, dim, dstate, 2), each the gradient of the real and the
+    imaginary part.
+    """
+    lib = _load()
+    delta = _io(delta, io_dtype)
+    batch, dim, seqlen = delta.shape
+    A = _f32(A)
+    if A.ndim != 3 or A.shape[2] != 2:
+        raise ValueError("A must be (dim, dstate, 2) pairs")
+    dstate = A.shape[1]
+    u, B, C, z = _io(u, io_dtype), _io(B, io_dtype), _io(C, io_dtype), _io(z, io_dtype)
+    D, delta_bias = _f32(D), _f32(delta_bias)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    out = {
+        "du": np.empty((batch, dim, seqlen)), "ddelta": np.empty((batch, dim, seqlen)),
+        "dA": np.empty((dim, dstate, 2)), "dB": np.empty(B.shape), "dC": np.empty(C.shape),
+        "dD": None if D is None else np.empty((dim,)),
+        "dz": None if z is None else np.empty((batch, dim, seqlen)),
+        "ddelta_bias": None if delta_bias is None else np.empty((dim,)),
+        "dinitial_state": np.empty((batch, dim, dstate, 2)),
+    }
+    rc = lib.oracle_selective_scan_complex_bwd(
+        batch, dim, seqlen, dstate, ngroups, io_dtype, _ptr(u), _ptr(delta), _ptr(A),
+        _ptr(B), B_kind, _ptr(C), C_kind, _ptr(D), _ptr(delta_bias), _ptr(z),
+        int(bool(delta_softplus)), _ptr(init), _ptr(dout),
+        _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+        _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dinitial_state"]))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan_complex_bwd failed with status {rc}")
     return out
 
 

@@ -616,6 +616,130 @@ int oracle_selective_scan_bwd(int64_t batch, int64_t dim, int64_t seqlen,
     return 0;
 }
 
+/* Gradients of the complex-A selective-scan forward above (the guide's
+ * section 4.1: A may be complex, and the operator has a backward).  For a
+ * complex quantity v the gradient is G_v = dL/dRe v + i dL/dIm v.  With
+ * w = c v (c fixed) G_v = conj(c) G_w, and with y = Re(c v) G_v = dy conj(c).
+ * Applied to x_t = a_t x_{t-1} + dt'_t B_t u_t, a_t = exp(dt'_t A), and
+ * y_t = Re(sum_s C_t[s] x_t[s]), the adjoint runs in reverse time:
+ *   h_t   = dy_t conj(C_t) + conj(a_{t+1}) h_{t+1},   h_l = 0
+ *   G_C_t = dy_t conj(x_t);   G_a_t = h_t conj(x_{t-1})
+ *   dA   += conj(dt'_t a_t) G_a_t;   dB_t += dt'_t u_t h_t
+ *   du_t  = D dy_t + dt'_t sum_s Re(h_t conj(B_t))
+ *   ddt'_t = sum_s Re(G_a_t conj(A a_t)) + u_t Re(h_t conj(B_t))
+ * and the real part of the chain through softplus, silu and D as in the
+ * real backward.  Layouts as the complex forward, gradients in double:
+ *   du, ddelta, dz: (batch, dim, seqlen); dA: (dim, dstate, 2); dB, dC: the
+ *   layout of B, C (pairs innermost); dD, ddelta_bias: (dim);
+ *   dinit: (batch, dim, dstate, 2). */
+int oracle_selective_scan_complex_bwd(int64_t batch, int64_t dim, int64_t seqlen,
+                                      int64_t dstate, int64_t ngroups, int io_dtype,
+                                      const void *u, const void *delta, const float *A,
+                                      const void *B, int B_kind, const void *C, int C_kind,
+                                      const float *D, const float *delta_bias, const void *z,
+                                      int delta_softplus, const double *initial_state,
+                                      const double *dout,
+                                      double *du, double *ddelta, double *dA, double *dB,
+                                      double *dC, double *dD, double *dz, double *ddelta_bias,
+                                      double *dinit) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC) return 1;
+    const int64_t l = seqlen, n = dstate;
+    const int64_t bsz = 2 * (B_kind == OR_BC_FIXED ? dim * n : batch * ngroups * n * l);
+    const int64_t csz = 2 * (C_kind == OR_BC_FIXED ? dim * n : batch * ngroups * n * l);
+    memset(du, 0, sizeof(double) * (size_t)(batch * dim * l));
+    memset(ddelta, 0, sizeof(double) * (size_t)(batch * dim * l));
+    memset(dA, 0, sizeof(double) * (size_t)(2 * dim * n));
+    memset(dB, 0, sizeof(double) * (size_t)bsz);
+    memset(dC, 0, sizeof(double) * (size_t)csz);
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)dim);
+    if (dz) memset(dz, 0, sizeof(double) * (size_t)(batch * dim * l));
+    if (ddelta_bias) memset(ddelta_bias, 0, sizeof(double) * (size_t)dim);
+    if (dinit) memset(dinit, 0, sizeof(double) * (size_t)(2 * batch * dim * n));
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, D, delta_bias, z, delta_softplus,
+                          NULL, NULL, NULL, NULL, 0, 0};
+    double complex *xs = (double complex *)malloc(sizeof(double complex) * (size_t)((l + 1) * n));
+    double complex *h = (double complex *)malloc(sizeof(double complex) * (size_t)n);
+    if (!xs || !h) { free(xs); free(h); return 5; }
+    const int64_t per_group = dim / ngroups;
+    for (int64_t row = 0; row < batch * dim; ++row) {
+        const int64_t b = row / dim, d = row % dim, g = d / per_group;
+        const int64_t base = row * l;
+        /* forward: xs[(t+1)*n + s] = x_t[s], xs[s] = x_{-1}[s] */
+        for (int64_t s = 0; s < n; ++s)
+            xs[s] = initial_state ? initial_state[2 * (row * n + s)] + I * initial_state[2 * (row * n + s) + 1]
+                                  : 0.0;
+        for (int64_t t = 0; t < l; ++t) {
+            double dt = load_io(delta, io_dtype, base + t);
+            if (delta_bias) dt += (double)delta_bias[d];
+            if (delta_softplus) dt = oracle_softplus(dt);
+            const double ut = load_io(u, io_dtype, base + t);
+            for (int64_t s = 0; s < n; ++s) {
+                const double complex Av = (double)A[2 * (d * n + s)] + I * (double)A[2 * (d * n + s) + 1];
+                xs[(t + 1) * n + s] = cexp(dt * Av) * xs[t * n + s]
+                                      + dt * bc_at_c(B, B_kind, io_dtype, &a, b, d, s, t) * ut;
+            }
+        }
+        /* reverse */
+        for (int64_t s = 0; s < n; ++s) h[s] = 0.0;
+        for (int64_t t = l - 1; t >= 0; --t) {
+            const double raw = load_io(delta, io_dtype, base + t) + (delta_bias ? (double)delta_bias[d] : 0.0);
+            const double dt = delta_softplus ? oracle_softplus(raw) : raw;
+            const double dsp_c = delta_softplus ? 1.0 / (1.0 + exp(-raw)) : 1.0;   /* softplus' */
+            const double ut = load_io(u, io_dtype, base + t);
+            double y = 0.0;
+            for (int64_t s = 0; s < n; ++s)
+                y += creal(xs[(t + 1) * n + s] * bc_at_c(C, C_kind, io_dtype, &a, b, d, s, t));
+            const double pre = y + (D ? (double)D[d] * ut : 0.0);
+            double dy = dout[base + t];
+            if (z) {
+                const double zt = load_io(z, io_dtype, base + t);
+                const double sg = 1.0 / (1.0 + exp(-zt));
+                dz[base + t] = pre * dy * sg * (1.0 + zt * (1.0 - sg));
+                dy *= zt * sg;
+            }
+            if (D) dD[d] += ut * dy;
+            double dut = D ? dy * (double)D[d] : 0.0;
+            double ddt = 0.0;
+            for (int64_t s = 0; s < n; ++s) {
+                const double complex Cv = bc_at_c(C, C_kind, io_dtype, &a, b, d, s, t);
+                const double complex Bv = bc_at_c(B, B_kind, io_dtype, &a, b, d, s, t);
+                const double complex Av = (double)A[2 * (d * n + s)] + I * (double)A[2 * (d * n + s) + 1];
+                const double complex aa = cexp(dt * Av);
+                h[s] += dy * conj(Cv);                              /* h_t */
+                const double complex gC = dy * conj(xs[(t + 1) * n + s]);
+                const double complex ga = h[s] * conj(xs[t * n + s]);   /* G of a_t */
+                ddt += creal(ga * conj(Av * aa)) + creal(h[s] * conj(Bv)) * ut;
+                const double complex gA = conj(dt * aa) * ga;
+                dA[2 * (d * n + s)] += creal(gA);
+                dA[2 * (d * n + s) + 1] += cimag(gA);
+                const double complex gB = dt * ut * h[s];
+                dut += dt * creal(h[s] * conj(Bv));
+                const int64_t ib = B_kind == OR_BC_FIXED ? d * n + s : ((b * ngroups + g) * n + s) * l + t;
+                const int64_t ic = C_kind == OR_BC_FIXED ? d * n + s : ((b * ngroups + g) * n + s) * l + t;
+                dB[2 * ib] += creal(gB);
+                dB[2 * ib + 1] += cimag(gB);
+                dC[2 * ic] += creal(gC);
+                dC[2 * ic + 1] += cimag(gC);
+                h[s] = conj(aa) * h[s];                              /* carried to t-1 */
+            }
+            du[base + t] = dut;
+            ddelta[base + t] = dsp_c * ddt;
+            if (ddelta_bias) ddelta_bias[d] += dsp_c * ddt;
+        }
+        if (dinit)
+            for (int64_t s = 0; s < n; ++s) {
+                dinit[2 * (row * n + s)] = creal(h[s]);
+                dinit[2 * (row * n + s) + 1] = cimag(h[s]);
+            }
+    }
+    free(xs);
+    free(h);
+    return 0;
+}
+
 /* ---- single-step decode -------------------------------------------------- */
 
 /* selective_state_update: one timestep of the recurrence above applied to a

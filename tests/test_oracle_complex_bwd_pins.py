@@ -1,0 +1,155 @@
+"""Pins for the oracle's complex-A backward (oracle_selective_scan_complex_bwd).
+
+The backward is the gradient of the complex forward oracle, which is pinned
+on its own (test_oracle_complex_pins.py).  Each pin checks it against the
+forward or the separately pinned real backward, never against its own code:
+
+  * central finite differences of L = sum(dout * out) through the complex
+    forward, element by element, for every input: u, delta, D, z, delta_bias
+    and the real and the imaginary part of A, B, C and the initial state
+    (time-varying, fixed and grouped B/C, softplus on and off);
+  * zero imaginary parts: the real parts of the gradients are the real
+    backward's, and the imaginary parts of dA, dB, dC and d(initial state)
+    vanish exactly;
+  * conjugation: conjugating A, B, C and the initial state leaves out
+    unchanged, so the real inputs' gradients stay and the complex ones are
+    conjugated;
+  * Euler's identity: out is real-linear in (u, initial state) jointly, so
+    <du, u> + <Re dinit, Re init> + <Im dinit, Im init> = L.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+
+
+def _rand(rng, shape, mean=0.0, std=1.0):
+    return (rng.standard_normal(shape) * std + mean).astype(np.float32)
+
+
+def _problem(rng, b=2, d=4, l=6, n=3, g=1, fixed_B=False, fixed_C=False, has_z=True, has_D=True,
+             has_bias=True, init=True):
+    A = np.stack([-rng.uniform(0.3, 2.0, (d, n)), rng.normal(0.0, 2.0, (d, n))], axis=-1).astype(np.float32)
+    p = {
+        "u": _rand(rng, (b, d, l)),
+        "delta": _rand(rng, (b, d, l), -0.5, 0.7),
+        "A": A,
+        "B": _rand(rng, (d, n, 2)) if fixed_B else _rand(rng, (b, g, n, l, 2)),
+        "C": _rand(rng, (d, n, 2)) if fixed_C else _rand(rng, (b, g, n, l, 2)),
+        "D": _rand(rng, (d,)) if has_D else None,
+        "z": _rand(rng, (b, d, l)) if has_z else None,
+        "delta_bias": rng.uniform(-0.3, 0.3, d).astype(np.float32) if has_bias else None,
+        "initial_state": rng.standard_normal((b, d, n, 2)) if init else None,
+    }
+    kinds = dict(ngroups=g, B_kind=orc.BC_FIXED if fixed_B else orc.BC_VARYING,
+                 C_kind=orc.BC_FIXED if fixed_C else orc.BC_VARYING)
+    return p, kinds
+
+
+def _forward(p, softplus, kinds):
+    out, _ = orc.selective_scan_complex(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                        p["delta_bias"], softplus, initial_state=p["initial_state"],
+                                        **kinds)
+    return out.reshape(p["delta"].shape)
+
+
+def _backward(p, dout, softplus, kinds):
+    return orc.selective_scan_complex_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], dout, p["D"],
+                                          p["z"], p["delta_bias"], softplus,
+                                          initial_state=p["initial_state"], **kinds)
+
+
+GRAD_OF = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+           "delta_bias": "ddelta_bias", "initial_state": "dinitial_state"}
+
+
+def _finite_difference(p, dout, softplus, kinds, name, h=1e-4):
+    """dL/d(p[name]) by central differences, real and imaginary parts as
+    separate entries; a float32 input moves by its float32-rounded step, and
+    the exact step taken is the divisor."""
+    base = p[name]
+    fd = np.zeros(base.shape)
+    for idx in np.ndindex(base.shape):
+        vals, steps = [], []
+        for sgn in (1.0, -1.0):
+            q = dict(p)
+            arr = base.copy()
+            arr[idx] = arr[idx] + sgn * h
+            steps.append(float(arr[idx]) - float(base[idx]))
+            q[name] = arr
+            vals.append(float(np.sum(_forward(q, softplus, kinds) * dout)))
+        fd[idx] = (vals[0] - vals[1]) / (steps[0] - steps[1])
+    return fd
+
+
+CASES = {
+    "varying": dict(),
+    "fixed_B": dict(fixed_B=True),
+    "fixed_BC": dict(fixed_B=True, fixed_C=True),
+    "groups2": dict(d=4, g=2),
+    "bare": dict(has_z=False, has_D=False, has_bias=False, init=False),
+}
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_complex_backward_matches_finite_differences(case, softplus):
+    rng = np.random.default_rng(700 + len(case) + 7 * softplus)
+    p, kinds = _problem(rng, **CASES[case])
+    if not softplus:   # keep the step positive without softplus
+        p["delta"] = (0.2 + 0.3 * np.abs(p["delta"])).astype(np.float32)
+    dout = rng.standard_normal(p["delta"].shape)
+    g = _backward(p, dout, softplus, kinds)
+    for name, gname in GRAD_OF.items():
+        if p[name] is None:
+            continue
+        fd = _finite_difference(p, dout, softplus, kinds, name)
+        err = np.max(np.abs(g[gname] - fd)) / (1.0 + np.max(np.abs(fd)))
+        assert err <= 1e-6, f"{case} softplus={softplus}: {gname} differs from finite differences by {err:.2e}"
+
+
+@pytest.mark.parametrize("case", ["varying", "fixed_BC", "groups2"])
+def test_zero_imaginary_parts_give_the_real_backward(case):
+    rng = np.random.default_rng(720 + len(case))
+    p, kinds = _problem(rng, **dict(dict(b=2, d=4, l=9, n=3), **CASES[case]))
+    for k in ("A", "B", "C", "initial_state"):
+        p[k] = p[k].copy()
+        p[k][..., 1] = 0.0
+    dout = rng.standard_normal(p["delta"].shape)
+    g = _backward(p, dout, True, kinds)
+    r = orc.selective_scan_bwd(p["u"], p["delta"], np.ascontiguousarray(p["A"][..., 0]),
+                               np.ascontiguousarray(p["B"][..., 0]), np.ascontiguousarray(p["C"][..., 0]),
+                               dout, p["D"], p["z"], p["delta_bias"], True,
+                               initial_state=np.ascontiguousarray(p["initial_state"][..., 0]), **kinds)
+    for name in ("du", "ddelta", "dD", "dz", "ddelta_bias"):
+        np.testing.assert_allclose(g[name], r[name], rtol=1e-12, atol=1e-12)
+    for name in ("dA", "dB", "dC", "dinitial_state"):
+        np.testing.assert_allclose(g[name][..., 0], r[name], rtol=1e-12, atol=1e-12)
+        assert np.all(g[name][..., 1] == 0.0), name
+
+
+def test_conjugation_conjugates_the_complex_gradients():
+    rng = np.random.default_rng(730)
+    p, kinds = _problem(rng, b=2, d=4, l=8, n=3, g=2)
+    dout = rng.standard_normal(p["delta"].shape)
+    g = _backward(p, dout, True, kinds)
+    q = dict(p)
+    for k in ("A", "B", "C", "initial_state"):
+        q[k] = p[k].copy()
+        q[k][..., 1] = -q[k][..., 1]
+    gq = _backward(q, dout, True, kinds)
+    for name in ("du", "ddelta", "dD", "dz", "ddelta_bias"):
+        np.testing.assert_allclose(gq[name], g[name], rtol=1e-10, atol=1e-12)
+    for name in ("dA", "dB", "dC", "dinitial_state"):
+        np.testing.assert_allclose(gq[name][..., 0], g[name][..., 0], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(gq[name][..., 1], -g[name][..., 1], rtol=1e-10, atol=1e-12)
+
+
+def test_euler_identity_in_u_and_the_initial_state():
+    rng = np.random.default_rng(740)
+    p, kinds = _problem(rng, b=2, d=5, l=10, n=4, g=1)
+    dout = rng.standard_normal(p["delta"].shape)
+    L = float(np.sum(_forward(p, True, kinds) * dout))
+    g = _backward(p, dout, True, kinds)
+    lin = np.sum(g["du"] * p["u"]) + np.sum(g["dinitial_state"] * p["initial_state"])
+    assert abs(lin - L) <= 1e-11 * (1 + abs(L))

@@ -418,3 +418,57 @@ def test_complex_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the complex-A backward against its own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_complex_bwd_pins as xbpins  # noqa: E402
+
+COMPLEX_BWD_MUTANTS = {
+    "cbwd_h_from_C_unconjugated": ("h[s] += dy * conj(Cv);                              /* h_t */",
+                                   "h[s] += dy * Cv;"),
+    "cbwd_carry_unconjugated": ("h[s] = conj(aa) * h[s];", "h[s] = aa * h[s];"),
+    "cbwd_dC_unconjugated": ("const double complex gC = dy * conj(xs[(t + 1) * n + s]);",
+                             "const double complex gC = dy * xs[(t + 1) * n + s];"),
+    "cbwd_dA_unconjugated": ("const double complex gA = conj(dt * aa) * ga;",
+                             "const double complex gA = dt * aa * ga;"),
+    "cbwd_ga_old_state_unconjugated": ("const double complex ga = h[s] * conj(xs[t * n + s]);",
+                                       "const double complex ga = h[s] * xs[t * n + s];"),
+    "cbwd_dB_imag_sign": ("dB[2 * ib + 1] += cimag(gB);", "dB[2 * ib + 1] -= cimag(gB);"),
+    "cbwd_dt_term_drops_rotation": ("ddt += creal(ga * conj(Av * aa))", "ddt += creal(ga * creal(Av) * conj(aa))"),
+    "cbwd_dinit_imag": ("dinit[2 * (row * n + s) + 1] = cimag(h[s]);", "dinit[2 * (row * n + s) + 1] = 0.0;"),
+}
+
+
+def _complex_bwd_pin_calls():
+    return [
+        ("fd_varying", lambda: xbpins.test_complex_backward_matches_finite_differences("varying", True)),
+        ("fd_fixed_BC", lambda: xbpins.test_complex_backward_matches_finite_differences("fixed_BC", False)),
+        ("conjugation", xbpins.test_conjugation_conjugates_the_complex_gradients),
+        ("euler", xbpins.test_euler_identity_in_u_and_the_initial_state),
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(COMPLEX_BWD_MUTANTS))
+def test_complex_bwd_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = COMPLEX_BWD_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _complex_bwd_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
