@@ -95,6 +95,9 @@ def _load():
             i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
             p, p, p, p, p, p, p, p, p]
         lib.oracle_selective_scan_complex_bwd.restype = i32
+        lib.oracle_selective_scan_complex_bwd_f32_floor.argtypes = [
+            i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, i32, p, p, p, p, p]
+        lib.oracle_selective_scan_complex_bwd_f32_floor.restype = i32
         lib.oracle_causal_conv1d_ex.argtypes = [i64, i64, i64, i32, i32, p, p, p, i32, p, p, p, p]
         lib.oracle_causal_conv1d_ex.restype = i32
         lib.oracle_round_f16.argtypes = [ctypes.c_double]
@@ -446,6 +449,34 @@ def selective_scan_complex_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bi
         _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dinitial_state"]))
     if rc != 0:
         raise ValueError(f"oracle_selective_scan_complex_bwd failed with status {rc}")
+    return out
+
+
+def selective_scan_complex_bwd_f32_floor(u, delta, A, B, C, dout, z=None, delta_bias=None,
+                                         delta_softplus=False, *, io_dtype=F32, ngroups=1,
+                                         B_kind=BC_VARYING, C_kind=BC_VARYING, initial_state=None):
+    """The complex backward's step gradient evaluated in binary32 in time
+    order (see ``ssm_oracle.c``): a dict of ddelta (batch, dim, seqlen),
+    ddelta_bias (dim) and dA (dim, dstate, 2) as float64 arrays.  Test
+    infrastructure: it sets the bar where fp32 cannot meet the fp32
+    tolerance."""
+    lib = _load()
+    delta = _io(delta, io_dtype)
+    batch, dim, seqlen = delta.shape
+    A = _f32(A)
+    dstate = A.shape[1]
+    u, B, C, z = _io(u, io_dtype), _io(B, io_dtype), _io(C, io_dtype), _io(z, io_dtype)
+    delta_bias = _f32(delta_bias)
+    init = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    out = {"ddelta": np.empty((batch, dim, seqlen)), "ddelta_bias": np.empty((dim,)),
+           "dA": np.empty((dim, dstate, 2))}
+    rc = lib.oracle_selective_scan_complex_bwd_f32_floor(
+        batch, dim, seqlen, dstate, ngroups, io_dtype, _ptr(u), _ptr(delta), _ptr(A),
+        _ptr(B), B_kind, _ptr(C), C_kind, _ptr(delta_bias), _ptr(z), int(bool(delta_softplus)),
+        _ptr(init), _ptr(dout), _ptr(out["ddelta"]), _ptr(out["ddelta_bias"]), _ptr(out["dA"]))
+    if rc != 0:
+        raise ValueError(f"oracle_selective_scan_complex_bwd_f32_floor failed with status {rc}")
     return out
 
 

@@ -740,6 +740,88 @@ int oracle_selective_scan_complex_bwd(int64_t batch, int64_t dim, int64_t seqlen
     return 0;
 }
 
+/* The complex backward's step gradient in binary32, in time order: the same
+ * definition as oracle_selective_scan_complex_bwd (float complex arithmetic,
+ * libm's expf/cexpf, sums over the states in state order).  It measures how
+ * far a plain fp32 evaluation lands from the float64 result where the
+ * decay's phase is large: the term Re(G_a conj(A a)) grows with |A|, so the
+ * step gradient's fp32 error does too.  Outputs ddelta (batch, dim, seqlen)
+ * and, when given, ddelta_bias (dim) and dA (dim, dstate, 2), as doubles
+ * widened from the float results. */
+int oracle_selective_scan_complex_bwd_f32_floor(int64_t batch, int64_t dim, int64_t seqlen,
+                                                int64_t dstate, int64_t ngroups, int io_dtype,
+                                                const void *u, const void *delta, const float *A,
+                                                const void *B, int B_kind, const void *C, int C_kind,
+                                                const float *delta_bias, const void *z,
+                                                int delta_softplus, const double *initial_state,
+                                                const double *dout, double *ddelta,
+                                                double *ddelta_bias, double *dA) {
+    if (batch <= 0 || dim <= 0 || seqlen <= 0 || dstate <= 0 || ngroups <= 0) return 2;
+    if (dim % ngroups != 0) return 2;
+    if (!u || !delta || !A || !B || !C || !dout || !ddelta) return 1;
+    const int64_t l = seqlen, n = dstate;
+    oracle_scan_args a = {batch, dim, seqlen, dstate, ngroups, io_dtype, u, delta, A,
+                          B, B_kind, C, C_kind, NULL, delta_bias, z, delta_softplus,
+                          NULL, NULL, NULL, NULL, 0, 0};
+    float complex *xf = (float complex *)malloc(sizeof(float complex) * (size_t)((l + 1) * n));
+    float complex *hf = (float complex *)malloc(sizeof(float complex) * (size_t)n);
+    float *bias_acc = (float *)calloc((size_t)dim, sizeof(float));
+    float complex *dA_acc = (float complex *)calloc((size_t)(dim * n), sizeof(float complex));
+    if (!xf || !hf || !bias_acc || !dA_acc) { free(xf); free(hf); free(bias_acc); free(dA_acc); return 5; }
+    for (int64_t row = 0; row < batch * dim; ++row) {
+        const int64_t b = row / dim, d = row % dim;
+        const int64_t base = row * l;
+        for (int64_t s = 0; s < n; ++s)
+            xf[s] = initial_state ? (float)initial_state[2 * (row * n + s)] + I * (float)initial_state[2 * (row * n + s) + 1]
+                                  : 0.0f;
+        for (int64_t t = 0; t < l; ++t) {
+            float st = (float)load_io(delta, io_dtype, base + t) + (delta_bias ? delta_bias[d] : 0.0f);
+            if (delta_softplus) st = fmaxf(st, 0.0f) + log1pf(expf(-fabsf(st)));
+            const float ut = (float)load_io(u, io_dtype, base + t);
+            for (int64_t s = 0; s < n; ++s) {
+                const float complex As = A[2 * (d * n + s)] + I * A[2 * (d * n + s) + 1];
+                const float complex Bs = (float complex)bc_at_c(B, B_kind, io_dtype, &a, b, d, s, t);
+                xf[(t + 1) * n + s] = cexpf(st * As) * xf[t * n + s] + (st * ut) * Bs;
+            }
+        }
+        for (int64_t s = 0; s < n; ++s) hf[s] = 0.0f;
+        for (int64_t t = l - 1; t >= 0; --t) {
+            const float rw = (float)load_io(delta, io_dtype, base + t) + (delta_bias ? delta_bias[d] : 0.0f);
+            const float st = delta_softplus ? fmaxf(rw, 0.0f) + log1pf(expf(-fabsf(rw))) : rw;
+            const float sp1 = delta_softplus ? 1.0f / (1.0f + expf(-rw)) : 1.0f;
+            const float ut = (float)load_io(u, io_dtype, base + t);
+            float gy = (float)dout[base + t];
+            if (z) {
+                const float zt = (float)load_io(z, io_dtype, base + t);
+                gy *= zt / (1.0f + expf(-zt));
+            }
+            float acc = 0.0f;
+            for (int64_t s = 0; s < n; ++s) {
+                const float complex As = A[2 * (d * n + s)] + I * A[2 * (d * n + s) + 1];
+                const float complex Bs = (float complex)bc_at_c(B, B_kind, io_dtype, &a, b, d, s, t);
+                const float complex Cs = (float complex)bc_at_c(C, C_kind, io_dtype, &a, b, d, s, t);
+                const float complex es = cexpf(st * As);
+                hf[s] = hf[s] + gy * conjf(Cs);
+                const float complex gas = hf[s] * conjf(xf[t * n + s]);
+                acc += crealf(gas * conjf(As * es)) + ut * crealf(hf[s] * conjf(Bs));
+                dA_acc[d * n + s] += conjf(st * es) * gas;
+                hf[s] = conjf(es) * hf[s];
+            }
+            ddelta[base + t] = (double)(acc * sp1);
+            bias_acc[d] += acc * sp1;
+        }
+    }
+    if (ddelta_bias)
+        for (int64_t d = 0; d < dim; ++d) ddelta_bias[d] = (double)bias_acc[d];
+    if (dA)
+        for (int64_t i = 0; i < dim * n; ++i) {
+            dA[2 * i] = (double)crealf(dA_acc[i]);
+            dA[2 * i + 1] = (double)cimagf(dA_acc[i]);
+        }
+    free(xf); free(hf); free(bias_acc); free(dA_acc);
+    return 0;
+}
+
 /* ---- single-step decode -------------------------------------------------- */
 
 /* selective_state_update: one timestep of the recurrence above applied to a

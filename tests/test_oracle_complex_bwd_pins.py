@@ -153,3 +153,43 @@ def test_euler_identity_in_u_and_the_initial_state():
     g = _backward(p, dout, True, kinds)
     lin = np.sum(g["du"] * p["u"]) + np.sum(g["dinitial_state"] * p["initial_state"])
     assert abs(lin - L) <= 1e-11 * (1 + abs(L))
+
+
+def test_f32_floor_is_the_same_definition():
+    """oracle.selective_scan_complex_bwd_f32_floor (the binary32 evaluation
+    that sets the bar of the large-phase GPU test) computes the same
+    gradients: on well-conditioned inputs it agrees with the float64
+    backward to fp32 rounding, and it is a float32 evaluation."""
+    rng = np.random.default_rng(750)
+    for case in ("varying", "fixed_BC", "groups2"):
+        p, kinds = _problem(rng, **dict(dict(b=2, d=4, l=12, n=3), **CASES[case]))
+        dout = rng.standard_normal(p["delta"].shape)
+        g = _backward(p, dout, True, kinds)
+        f = orc.selective_scan_complex_bwd_f32_floor(
+            p["u"], p["delta"], p["A"], p["B"], p["C"], dout, p["z"], p["delta_bias"], True,
+            initial_state=p["initial_state"], **kinds)
+        for name in ("ddelta", "ddelta_bias", "dA"):
+            err = np.max(np.abs(f[name] - g[name]) / (1.0 + np.abs(g[name])))
+            assert err < 2e-5, (case, name, err)
+        assert not np.array_equal(f["ddelta"], g["ddelta"])
+
+
+def test_f32_floor_on_the_ladder_is_near_the_fp32_tolerance():
+    """On the complex workloads' default ladder Im A[d, s] = pi s the binary32
+    evaluation's error in ddelta, ddelta_bias and dA is of the size of the
+    fp32 tolerance (1e-4): enough to need a bar of its own there, small
+    enough that three times it stays a tight bar."""
+    from state_space_model_scan_amd.inputs import (COMPLEX_WORKLOADS, F32, io_bits_to_f64,
+                                                   make_complex_inputs, make_dout)
+    w = COMPLEX_WORKLOADS["complex_tiny"].scaled(io_dtype=F32, init_state=True, seed=800)
+    t = make_complex_inputs(w)
+    dout = io_bits_to_f64(make_dout(w), F32)
+    init = t["initial_state"].astype(np.float32).astype(np.float64)
+    kw = dict(io_dtype=F32, ngroups=w.ngroups, initial_state=init)
+    ref = orc.selective_scan_complex_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dout, t["D"], t["z"],
+                                         t["delta_bias"], True, **kw)
+    f = orc.selective_scan_complex_bwd_f32_floor(t["u"], t["delta"], t["A"], t["B"], t["C"], dout, t["z"],
+                                                 t["delta_bias"], True, **kw)
+    errs = {k: float(np.max(np.abs(f[k] - ref[k]) / (1 + np.abs(ref[k])))) for k in f}
+    assert 2e-5 < errs["ddelta"] < 2.5e-4, errs
+    assert max(errs.values()) < 2.5e-4, errs
