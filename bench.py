@@ -103,7 +103,7 @@ KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip"
 DECODE_SRCS = ("decode.hip", "device_util.h")
 SSD_SRCS = ("ssd.hip", "device_util.h")
 BWD_SRCS = ("bwd.hip", "device_util.h")
-COMPLEX_SRCS = ("scan_complex.hip", "scan_kernel.h", "device_util.h")
+COMPLEX_SRCS = ("scan_complex.hip", "complex_util.h", "scan_kernel.h", "device_util.h")
 CONV_SRCS = ("ssm_scan.hip", "device_util.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 11
+#define SSM_ABI_VERSION 12
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -190,13 +190,18 @@ int ssm_scan_plan(const ssm_scan_args_t *args, ssm_scan_plan_t *plan);
  *   A: (dim, dstate, 2) fp32;
  *   B, C: io, fixed (dim, dstate, 2) or varying (batch, ngroups, dstate,
  *         seqlen, 2);
- *   initial_state, last_state: (batch, dim, dstate, 2) fp32 or NULL.
+ *   initial_state, last_state: (batch, dim, dstate, 2) fp32 or NULL;
+ *   checkpoints: (batch, dim, nck, dstate, 2) fp32 or NULL, the state before
+ *         every SSM_CKPT_INTERVAL-th timestep, for ssm_scan_bwd_complex.
  * Not taken (SSM_ERR_UNSUPPORTED): the fused conv prologue (conv_weight must
- * be NULL; run causal_conv1d_fwd first) and checkpoints (there is no complex
- * backward).  u is required; workspace is ignored (the sequence is walked in
- * one pass).  The decay's phase uses the hardware sine and cosine on the
- * fractional part of delta' Im(A) / (2 pi).  Same conventions and status
- * codes as ssm_scan_fwd. */
+ * be NULL; run causal_conv1d_fwd first).  u is required; workspace is ignored
+ * (the sequence is walked in one pass).  The decay's phase uses the
+ * hardware sine and cosine on the fractional part of delta' Im(A) / (2 pi),
+ * that product carried to about one rounding (Im(A) / (2 pi) held as two
+ * floats, the product's rounding error recovered with an fma), and delta'
+ * is the softplus without the cancellation of 1 + e^v: a large |Im A|
+ * magnifies an error in either.  Same conventions and status codes as
+ * ssm_scan_fwd. */
 int ssm_scan_fwd_complex(const ssm_scan_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssm_scan_fwd_complex (no HIP call). */
@@ -267,6 +272,34 @@ typedef struct ssm_scan_bwd_args {
  * so results are bit-for-bit repeatable.  Same conventions and status codes
  * as ssm_scan_fwd. */
 int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
+
+/* Gradients of the complex-A forward (ssm_scan_fwd_complex; the same page,
+ * section 4.1: A may be complex, and the operator has a backward).  The
+ * arguments are those of ssm_scan_bwd read with the complex forward's
+ * layouts: A (d,n,2) fp32; B/C io pairs, (d,n,2) fixed or (b,g,n,l,2)
+ * varying; checkpoints (b,d,nck,n,2) fp32 written by ssm_scan_fwd_complex;
+ * dA (d,n,2), dB/dC in B's/C's pair layout and dinitial_state (b,d,n,2),
+ * all fp32, each the gradient of the real and of the imaginary part
+ * (G_v = dL/dRe v + i dL/dIm v).  With a_t = exp(delta'_t A):
+ *
+ *     h_t     = dy_t conj(C_t) + conj(a_{t+1}) h_{t+1},  h_l = 0
+ *     dC_t    = dy_t conj(x_t),   G_a = h_t conj(x_{t-1})
+ *     dA     += conj(delta'_t a_t) G_a,   dB_t = delta'_t u_t h_t
+ *     du_t    = D dy_t + delta'_t sum_s Re(h_t conj(B_t))
+ *     ddelta_t = softplus'(.) (sum_s Re(G_a conj(A a_t)) + u_t sum_s Re(h_t conj(B_t)))
+ *
+ * with dy, dz, dD and d(delta_bias) as in ssm_scan_bwd; a_t and delta'_t
+ * are formed as in ssm_scan_fwd_complex.  seq_segments must
+ * be 0 or 1 (no sequence split; others return SSM_ERR_UNSUPPORTED); the
+ * workspace (ssm_scan_bwd_complex_workspace_size) holds the partial sums and
+ * is required.  Asynchronous on hip_stream; returns a status code. */
+int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *args, void *hip_stream);
+
+/* Host-only argument check of ssm_scan_bwd_complex (no HIP call). */
+int ssm_scan_bwd_complex_validate(const ssm_scan_bwd_args_t *args);
+
+/* Scratch bytes ssm_scan_bwd_complex needs (no HIP call). */
+int ssm_scan_bwd_complex_workspace_size(const ssm_scan_bwd_args_t *args, size_t *bytes);
 
 /* Host-only argument check of ssm_scan_bwd (no HIP call). */
 int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *args);

@@ -40,6 +40,7 @@ SOURCES = [
     ("decode.hip", True),
     ("ssd.hip", True),
     ("bwd.hip", True),
+    ("bwd_complex.hip", True),
     ("validate.cpp", False),
 ]
 MICRO_SOURCES = [("microbench.hip", True)]

@@ -28,6 +28,7 @@ EXPORTS = (
     "causal_conv1d_update", "causal_conv1d_update_validate",
     "ssd_scan_fwd", "ssd_scan_validate", "ssd_scan_workspace_size",
     "ssm_scan_bwd", "ssm_scan_bwd_validate", "ssm_scan_bwd_workspace_size",
+    "ssm_scan_bwd_complex", "ssm_scan_bwd_complex_validate", "ssm_scan_bwd_complex_workspace_size",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
 )
 
@@ -184,6 +185,12 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd_validate.restype = ctypes.c_int
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_int
+        L.ssm_scan_bwd_complex.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+        L.ssm_scan_bwd_complex.restype = ctypes.c_int
+        L.ssm_scan_bwd_complex_validate.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.ssm_scan_bwd_complex_validate.restype = ctypes.c_int
+        L.ssm_scan_bwd_complex_workspace_size.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_scan_bwd_complex_workspace_size.restype = ctypes.c_int
         L.ssm_status_str.argtypes = [ctypes.c_int]
         L.ssm_status_str.restype = ctypes.c_char_p
         L.ssm_last_hip_error.argtypes = []

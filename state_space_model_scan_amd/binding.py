@@ -291,7 +291,7 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                          delta_softplus: bool = False, out: Optional[torch.Tensor] = None,
                          last_state: Optional[torch.Tensor] = None,
                          initial_state: Optional[torch.Tensor] = None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, checkpoints: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Enqueue ssm_scan_fwd_complex on the current stream; returns ``out``.
 
     A is complex64 (dim, dstate) or float32 pairs (dim, dstate, 2).  B and C
@@ -342,6 +342,8 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
     _spec(initial_state, "initial_state", bdn2, f32, dev)
     _out_spec(out, "out", bld, delta.dtype, dev)
     _out_spec(last_state, "last_state", bdn2, f32, dev)
+    if checkpoints is not None:
+        _out_spec(checkpoints, "checkpoints", (batch, dim, checkpoint_count(seqlen), dstate, 2), f32, dev)
     _on_gpu(dev)
     if out is None:
         out = torch.empty_like(delta)
@@ -355,6 +357,7 @@ def ssm_scan_fwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
     args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
     args.delta_softplus = int(bool(delta_softplus))
     args.out, args.last_state, args.initial_state = _ptr(out), _ptr(last_state), _ptr(initial_state)
+    args.checkpoints = _ptr(checkpoints)
     check(_lib.lib().ssm_scan_fwd_complex(ctypes.byref(args), _stream(delta.device, stream)))
     return out
 
@@ -437,6 +440,85 @@ def ssm_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     check(L.ssm_scan_bwd(ctypes.byref(args), _stream(dev, stream)))
+    return g
+
+
+def ssm_scan_bwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                         C: torch.Tensor, dout: torch.Tensor, checkpoints: torch.Tensor,
+                         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                         delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                         want_dinitial_state: bool = False, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> dict:
+    """Enqueue ssm_scan_bwd_complex; returns the gradients in a dict.
+
+    Inputs as for ``ssm_scan_fwd_complex`` (A complex64 or float32 pairs
+    (dim, dstate, 2); B/C complex64 or io-dtype pairs, fixed (dim, dstate, 2)
+    or grouped (batch, groups, dstate, seqlen, 2)), ``dout`` in the io dtype
+    and the ``checkpoints`` (batch, dim, nck, dstate, 2) float32 that forward
+    call wrote.  du, ddelta, dz come back in the io dtype; dD, ddelta_bias in
+    float32; dA, dB, dC and dinitial_state as float32 (real, imaginary)
+    pairs in A's, B's, C's and the state's layouts (``torch.view_as_complex``
+    turns them into complex64)."""
+    delta = _dense(delta)
+    io = _io_of(delta, "delta", 3)
+    batch, dim, seqlen = delta.shape
+    A, B, C = _pairs(A), _pairs(B), _pairs(C)
+    if A.dim() != 3 or A.shape[-1] != 2 or A.shape[0] != dim:
+        raise ValueError(f"A must be complex (dim, dstate) or float32 pairs (dim, dstate, 2) with dim {dim}")
+    dstate = A.shape[1]
+    if B.dim() == 4:
+        B = B.unsqueeze(1)
+    if C.dim() == 4:
+        C = C.unsqueeze(1)
+    u, B, C, z, dout, A = _dense(u), _dense(B), _dense(C), _dense(z), _dense(dout), _dense(A)
+    bk, bg = _bc_kind_complex(B, "B")
+    ck, cg = _bc_kind_complex(C, "C")
+    if bk == _lib.SSM_BC_VARYING and ck == _lib.SSM_BC_VARYING and bg != cg:
+        raise ValueError("B and C must have the same number of groups")
+    ngroups = max(bg, cg, 1)
+    for name, t in (("u", u), ("z", z), ("B", B), ("C", C), ("dout", dout)):
+        if t is not None and t.dtype != delta.dtype:
+            raise ValueError(f"{name} must have the io dtype {delta.dtype} (as pairs), got {t.dtype}")
+    dev, f32, bld = delta.device, torch.float32, (batch, dim, seqlen)
+    for name, t in (("u", u), ("dout", dout), ("z", z)):
+        _spec(t, name, bld, delta.dtype, dev)
+    _spec(A, "A", (dim, dstate, 2), f32, dev)
+    _spec(B, "B", _bc_shape(B, bk, ngroups, batch, dim, dstate, seqlen, (2,)), delta.dtype, dev)
+    _spec(C, "C", _bc_shape(C, ck, ngroups, batch, dim, dstate, seqlen, (2,)), delta.dtype, dev)
+    _spec(D, "D", (dim,), f32, dev)
+    _spec(delta_bias, "delta_bias", (dim,), f32, dev)
+    _spec(checkpoints, "checkpoints", (batch, dim, checkpoint_count(seqlen), dstate, 2), f32, dev)
+    if workspace is not None:
+        _workspace_spec(workspace, dev)
+    _on_gpu(dev)
+    D, delta_bias, checkpoints = _dense(D), _dense(delta_bias), _dense(checkpoints)
+    g = {
+        "du": torch.empty_like(delta), "ddelta": torch.empty_like(delta),
+        "dz": None if z is None else torch.empty_like(delta),
+        "dA": torch.empty((dim, dstate, 2), dtype=f32, device=dev),
+        "dB": torch.empty(B.shape, dtype=f32, device=dev), "dC": torch.empty(C.shape, dtype=f32, device=dev),
+        "dD": None if D is None else torch.empty((dim,), dtype=f32, device=dev),
+        "ddelta_bias": None if delta_bias is None else torch.empty((dim,), dtype=f32, device=dev),
+        "dinitial_state": (torch.empty((batch, dim, dstate, 2), dtype=f32, device=dev)
+                           if want_dinitial_state else None),
+    }
+    args = BwdArgs()
+    args.batch, args.dim, args.seqlen, args.dstate, args.ngroups = batch, dim, seqlen, dstate, ngroups
+    args.io_dtype = io
+    args.u, args.delta, args.A = _ptr(u), _ptr(delta), _ptr(A)
+    args.B, args.B_kind, args.C, args.C_kind = _ptr(B), bk, _ptr(C), ck
+    args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
+    args.delta_softplus = int(bool(delta_softplus))
+    args.checkpoints, args.dout = _ptr(checkpoints), _ptr(dout)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
+        setattr(args, k, _ptr(g[k]))
+    L = _lib.lib()
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        check(L.ssm_scan_bwd_complex_workspace_size(ctypes.byref(args), ctypes.byref(need)))
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    check(L.ssm_scan_bwd_complex(ctypes.byref(args), _stream(dev, stream)))
     return g
 
 

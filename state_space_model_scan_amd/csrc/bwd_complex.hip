@@ -1,0 +1,434 @@
+// bwd_complex.hip -- the gradients of the complex-A forward
+// (ssm_scan_bwd_complex) for gfx950.
+//
+// Operation: PaddleNLP Kernel operator-library guide, section 4.1: A may be
+// real or complex, and the operator's backward is the extension's bwd entry.
+// With G_v = dL/dRe v + i dL/dIm v for a complex v, the adjoint of
+//   x_t = a_t x_{t-1} + delta'_t B_t u_t,  a_t = exp(delta'_t A),
+//   y_t = Re(sum_s C_t[s] x_t[s])
+// runs in reverse time, h_t = dy_t conj(C_t) + conj(a_{t+1}) h_{t+1}, and
+//   G_C_t = dy_t conj(x_t),  G_a_t = h_t conj(x_{t-1}),
+//   dA += conj(delta' a) G_a,  dB_t = delta' u h_t,
+//   du_t = D dy_t + delta' sum_s Re(h_t conj(B_t)),
+//   d delta'_t = sum_s Re(G_a conj(A a)) + u sum_s Re(h_t conj(B_t));
+// include/ssmscan.h writes out every gradient.
+//
+// Work decomposition: a channel is one 16-lane row of a wave, lane s owning
+// complex state s (padded states are inert: A = B = C = 0 keeps them zero);
+// a 512-thread workgroup holds 32 channels of one (batch, group).  The
+// sequence is walked in chunks of SSM_CKPT_INTERVAL timesteps from the last
+// to the first.  Per chunk every row re-runs the forward recurrence from the
+// state the forward saved at the chunk's start, keeping x_{t-1} of each
+// timestep in registers, then walks the chunk backwards recomputing a_t.
+// The per-(channel, timestep) scalars (delta', delta' u, u, dy) are formed
+// by the lane that owns the timestep (lane j owns timesteps j and j + 16)
+// and read by the row through DPP row broadcasts; sums over the states
+// (y for dz, the du and delta' terms) are DPP rotations within the row.
+// Time-varying dB/dC sum over every channel of the group: each wave adds its
+// four rows, the workgroup adds its waves in order through LDS and writes
+// its partial sums; a second kernel adds the workgroups' partials in a fixed
+// order, as it adds the per-batch partials of dA, fixed dB/dC, dD and
+// d(delta_bias).  No atomics: every output is bit-for-bit repeatable.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "complex_util.h"
+#include "device_util.h"
+#include "host_util.h"
+#include "ssmscan.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kCk = SSM_CKPT_INTERVAL;   // timesteps per chunk
+constexpr int kRowsPerWave = 4;          // channels per wave
+constexpr int kWavesPerWG = 8;
+constexpr int kChPerWG = kRowsPerWave * kWavesPerWG;
+static_assert(kCk == 32, "two owned timesteps per lane of a 16-lane row");
+
+struct CbwdParams {
+  const void *u, *delta, *B, *C, *z, *dout;
+  const float *A, *D, *dbias, *ckpt;
+  void *du, *ddelta, *dz;
+  float *dA, *dB, *dC, *dD, *ddbias, *dinit;
+  float *ws_bc;               // time-varying dB/dC partials [b*g][blk][t][s][4]
+  float *ws_dA, *ws_fB, *ws_fC, *ws_dD, *ws_db;   // per-batch partials
+  int64_t batch, dim, seqlen, nck, cpg;
+  int n, ngroups, groups_eff, nblk;
+  int softplus;
+};
+
+// sum over the 16 lanes of a row, in every lane (rotations within the row)
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return v;
+}
+
+// sum over the four rows of a wave, in every lane
+__device__ __forceinline__ float wave_rows_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int IO, bool BV, bool CV>
+__global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
+  constexpr bool ANYV = BV || CV;
+  __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kCk : 1][16][2];       // [B, C][t][s][re, im]
+  __shared__ float s_part[ANYV ? kWavesPerWG : 1][ANYV ? kCk : 1][16][4];   // per-wave (dB, dC) sums
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int rw = lane >> 4, s = lane & 15;
+  const int blk = blockIdx.x % p.nblk;
+  const int rest = blockIdx.x / p.nblk;
+  const int g = rest % p.groups_eff;
+  const int64_t b = rest / p.groups_eff;
+  const int64_t d_end = (g + 1) * p.cpg;
+  const int64_t d = g * p.cpg + static_cast<int64_t>(blk) * kChPerWG + wave * kRowsPerWave + rw;
+  const bool valid = d < d_end;
+  const int64_t dl = valid ? d : d_end - 1;
+  const int64_t row = b * p.dim + dl;
+  const int64_t rbase = row * p.seqlen;
+  const int64_t L = p.seqlen;
+  const int n = p.n;
+  const bool sv = s < n;
+
+  const int64_t ea = (dl * n + (sv ? s : 0)) * 2;
+  const float Ar = sv ? p.A[ea] : 0.0f, Ai = sv ? p.A[ea + 1] : 0.0f;
+  const float Ar2 = Ar * kLog2e;
+  const Turns Atr = turns_of(Ai);
+  float Bfr = 0.0f, Bfi = 0.0f, Cfr = 0.0f, Cfi = 0.0f;
+  if (!BV && sv) { Bfr = load_io<IO>(p.B, ea); Bfi = load_io<IO>(p.B, ea + 1); }
+  if (!CV && sv) { Cfr = load_io<IO>(p.C, ea); Cfi = load_io<IO>(p.C, ea + 1); }
+  const float bias = p.dbias ? p.dbias[dl] : 0.0f;
+  const float Dd = p.D ? p.D[dl] : 0.0f;
+  const int64_t bg = b * p.ngroups + g;
+  const int64_t bc_base = bg * n * L * 2;   // element of (b, g, state 0, t 0, re) in a varying B/C
+
+  float hr = 0.0f, hi = 0.0f;                                 // adjoint carry
+  float dAr = 0.0f, dAi = 0.0f, fBr = 0.0f, fBi = 0.0f, fCr = 0.0f, fCi = 0.0f;
+  float accD = 0.0f, accBias = 0.0f;                           // owner lanes' sums over their timesteps
+
+  for (int64_t ci = p.nck - 1; ci >= 0; --ci) {
+    const int64_t c0 = ci * kCk;
+    const int len = static_cast<int>((L - c0 < kCk) ? L - c0 : kCk);
+
+    // ---- the owned timesteps' scalars (lane s owns t = s and s + 16)
+    float o_dt[2], o_dtu[2], o_u[2], o_dy[2], o_dsp[2], o_dout[2], o_sg[2], o_z[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = s + 16 * k;
+      o_dt[k] = o_dtu[k] = o_u[k] = o_dy[k] = o_dsp[k] = o_dout[k] = o_sg[k] = o_z[k] = 0.0f;
+      if (t < len) {
+        const int64_t e = rbase + c0 + t;
+        const float raw = load_io<IO>(p.delta, e) + bias;
+        const float uu = load_io<IO>(p.u, e);
+        const float dt = p.softplus ? softplus_acc(raw) : raw;
+        const float dsp = p.softplus ? fast_rcp(1.0f + fast_exp2(-raw * kLog2e)) : 1.0f;
+        float dout = valid ? load_io<IO>(p.dout, e) : 0.0f;
+        float dy = dout;
+        if (p.z) {
+          const float zz = load_io<IO>(p.z, e);
+          const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+          o_sg[k] = sg;
+          o_z[k] = zz;
+          dy = dout * zz * sg;
+        }
+        o_dt[k] = dt; o_dtu[k] = dt * uu; o_u[k] = uu; o_dy[k] = dy; o_dsp[k] = dsp; o_dout[k] = dout;
+      }
+    }
+
+    // ---- the chunk's B/C tile (time-varying), and the chunk start's state
+    if constexpr (ANYV) {
+      __syncthreads();   // the previous chunk's reads of s_bc and s_part are done
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 512 * j;           // [tensor][state][t][re, im]
+        const int tensor = idx >> 10, r = idx & 1023;
+        const int st = r >> 6, tc = r & 63, t = tc >> 1, comp = tc & 1;
+        float v = 0.0f;
+        const bool want = tensor == 0 ? BV : CV;
+        if (want && st < n && t < len)
+          v = load_io<IO>(tensor == 0 ? p.B : p.C, bc_base + (static_cast<int64_t>(st) * L + c0 + t) * 2 + comp);
+        s_bc[tensor][t][st][comp] = v;
+      }
+      __syncthreads();
+    }
+    float xr = 0.0f, xi = 0.0f;
+    if (sv) {
+      const int64_t e = ((row * p.nck + ci) * n + s) * 2;
+      xr = p.ckpt[e];
+      xi = p.ckpt[e + 1];
+    }
+
+    auto bcoef = [&](int t, float &br, float &bi) {
+      if constexpr (BV) { br = s_bc[0][t][s][0]; bi = s_bc[0][t][s][1]; }
+      else { br = Bfr; bi = Bfi; }
+    };
+    auto ccoef = [&](int t, float &cr, float &cim) {
+      if constexpr (CV) { cr = s_bc[ANYV ? 1 : 0][t][s][0]; cim = s_bc[ANYV ? 1 : 0][t][s][1]; }
+      else { cr = Cfr; cim = Cfi; }
+    };
+
+    // ---- forward re-run: x_{t-1} of every timestep of the chunk
+    float pr[kCk], pim[kCk];
+    static_for(std::make_integer_sequence<int, kCk>{}, [&](auto TT) {
+      constexpr int t = decltype(TT)::value;
+      pr[t] = xr;
+      pim[t] = xi;
+      if (t < len) {
+        const float dt = row_bcast<t % 16>(o_dt[t / 16]);
+        const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
+        float er, ei, br, bi;
+        cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
+        bcoef(t, br, bi);
+        const float nr = fmaf(er, xr, fmaf(-ei, xi, br * dtu));
+        const float ni = fmaf(er, xi, fmaf(ei, xr, bi * dtu));
+        xr = nr;
+        xi = ni;
+      }
+    });
+
+    // ---- backward walk; the owners keep y_t, the delta' term and the u term
+    float r_y[2] = {0.0f, 0.0f}, r_ddt[2] = {0.0f, 0.0f}, r_du[2] = {0.0f, 0.0f};
+    static_for(std::make_integer_sequence<int, kCk>{}, [&](auto TR) {
+      constexpr int t = kCk - 1 - decltype(TR)::value;
+      if (t < len) {
+        const float dt = row_bcast<t % 16>(o_dt[t / 16]);
+        const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
+        const float uu = row_bcast<t % 16>(o_u[t / 16]);
+        const float dy = row_bcast<t % 16>(o_dy[t / 16]);
+        float er, ei, br, bi, cr, cim;
+        cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
+        bcoef(t, br, bi);
+        ccoef(t, cr, cim);
+        const float xpr = pr[t], xpi = pim[t];                 // x_{t-1}
+        const float xtr = fmaf(er, xpr, fmaf(-ei, xpi, br * dtu));
+        const float xti = fmaf(er, xpi, fmaf(ei, xpr, bi * dtu));
+        const float yp = fmaf(cr, xtr, -cim * xti);            // Re(C x_t)
+        hr = fmaf(dy, cr, hr);                                 // h_t = dy conj(C) + carry
+        hi = fmaf(-dy, cim, hi);
+        const float gCr = dy * xtr, gCi = -dy * xti;           // dy conj(x_t)
+        const float gar = fmaf(hr, xpr, hi * xpi);             // h conj(x_{t-1})
+        const float gai = fmaf(hi, xpr, -hr * xpi);
+        const float war = fmaf(Ar, er, -Ai * ei), wai = fmaf(Ar, ei, Ai * er);   // A a
+        const float term2 = fmaf(hr, br, hi * bi);             // Re(h conj(B))
+        const float ddtp = fmaf(gar, war, fmaf(gai, wai, uu * term2));
+        const float dup = dt * term2;
+        dAr = fmaf(dt, fmaf(er, gar, ei * gai), dAr);          // conj(dt a) G_a
+        dAi = fmaf(dt, fmaf(er, gai, -ei * gar), dAi);
+        const float gBr = dtu * hr, gBi = dtu * hi;
+        if constexpr (!BV) { fBr += gBr; fBi += gBi; }
+        if constexpr (!CV) { fCr += gCr; fCi += gCi; }
+        if constexpr (ANYV) {
+          const float v0 = BV ? wave_rows_sum(gBr) : 0.0f, v1 = BV ? wave_rows_sum(gBi) : 0.0f;
+          const float v2 = CV ? wave_rows_sum(gCr) : 0.0f, v3 = CV ? wave_rows_sum(gCi) : 0.0f;
+          if (rw == 0) *reinterpret_cast<float4 *>(&s_part[wave][t][s][0]) = make_float4(v0, v1, v2, v3);
+        }
+        const float nhr = fmaf(er, hr, ei * hi);               // carried: conj(a) h
+        const float nhi = fmaf(er, hi, -ei * hr);
+        hr = nhr;
+        hi = nhi;
+        const float ys = row_sum16(yp), ds = row_sum16(ddtp), us = row_sum16(dup);
+        if (s == t % 16) { r_y[t / 16] = ys; r_ddt[t / 16] = ds; r_du[t / 16] = us; }
+      }
+    });
+
+    // ---- the owners' gradients of their timesteps
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = s + 16 * k;
+      if (t < len && valid) {
+        const int64_t e = rbase + c0 + t;
+        const float ddt = r_ddt[k] * o_dsp[k];
+        store_one<IO>(p.du, e, fmaf(Dd, o_dy[k], r_du[k]));
+        store_one<IO>(p.ddelta, e, ddt);
+        if (p.z) {
+          const float pre = fmaf(Dd, o_u[k], r_y[k]);
+          const float sg = o_sg[k], zz = o_z[k];
+          store_one<IO>(p.dz, e, o_dout[k] * pre * sg * fmaf(zz, 1.0f - sg, 1.0f));
+        }
+        accD = fmaf(o_dy[k], o_u[k], accD);
+        accBias += ddt;
+      }
+    }
+
+    // ---- the workgroup's partial sums of time-varying dB/dC for the chunk
+    if constexpr (ANYV) {
+      __syncthreads();
+      static_assert(kCk * 16 == 512, "one (timestep, state) of the chunk per thread");
+      const int t = tid >> 4, st = tid & 15;
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int w = 0; w < kWavesPerWG; ++w) {
+        const float4 v = *reinterpret_cast<const float4 *>(&s_part[w][t][st][0]);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      if (t < len && st < n)
+        *reinterpret_cast<float4 *>(p.ws_bc + (((bg * p.nblk + blk) * L + c0 + t) * n + st) * 4) = acc;
+    }
+  }
+
+  // ---- per-channel results
+  if (valid && sv) {
+    const int64_t e = (row * n + s) * 2;
+    if (p.dinit) { p.dinit[e] = hr; p.dinit[e + 1] = hi; }
+    p.ws_dA[e] = dAr;
+    p.ws_dA[e + 1] = dAi;
+    if constexpr (!BV) { p.ws_fB[e] = fBr; p.ws_fB[e + 1] = fBi; }
+    if constexpr (!CV) { p.ws_fC[e] = fCr; p.ws_fC[e + 1] = fCi; }
+  }
+  const float sD = row_sum16(accD), sB = row_sum16(accBias);
+  if (valid && s == 0) {
+    p.ws_dD[row] = sD;
+    p.ws_db[row] = sB;
+  }
+}
+
+// Adds the partial sums in a fixed order: per (d, s) over the batch for dA
+// and fixed dB/dC; per d over the batch for dD and d(delta_bias); per
+// (b*g, s, t) over the group's workgroups for time-varying dB/dC.
+__global__ void __launch_bounds__(256) cbwd_sum_kernel(const CbwdParams p, int bv, int cv) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = p.n, L = p.seqlen;
+  const int64_t nds = p.dim * n;
+  if (i < nds) {
+    float ar = 0.0f, ai = 0.0f, br = 0.0f, bi = 0.0f, cr = 0.0f, cim = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b) {
+      const int64_t e = (b * nds + i) * 2;
+      ar += p.ws_dA[e]; ai += p.ws_dA[e + 1];
+      if (!bv) { br += p.ws_fB[e]; bi += p.ws_fB[e + 1]; }
+      if (!cv) { cr += p.ws_fC[e]; cim += p.ws_fC[e + 1]; }
+    }
+    p.dA[2 * i] = ar; p.dA[2 * i + 1] = ai;
+    if (!bv) { p.dB[2 * i] = br; p.dB[2 * i + 1] = bi; }
+    if (!cv) { p.dC[2 * i] = cr; p.dC[2 * i + 1] = cim; }
+  }
+  if (i < p.dim) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < p.batch; ++b) {
+      sd += p.ws_dD[b * p.dim + i];
+      sb += p.ws_db[b * p.dim + i];
+    }
+    if (p.dD) p.dD[i] = sd;
+    if (p.ddbias) p.ddbias[i] = sb;
+  }
+  if (bv || cv) {
+    const int64_t nbg = p.batch * p.ngroups;
+    if (i < nbg * L * n) {
+      const int64_t st = i % n, t = (i / n) % L, bgi = i / (n * L);
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int blk = 0; blk < p.nblk; ++blk) {
+        const float4 v = *reinterpret_cast<const float4 *>(p.ws_bc + (((bgi * p.nblk + blk) * L + t) * n + st) * 4);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      const int64_t o = ((bgi * n + st) * L + t) * 2;
+      if (bv) { p.dB[o] = acc.x; p.dB[o + 1] = acc.y; }
+      if (cv) { p.dC[o] = acc.z; p.dC[o + 1] = acc.w; }
+    }
+  }
+}
+
+using CbwdFn = void (*)(const CbwdParams);
+
+template <int IO>
+CbwdFn pick_cbwd(bool bv, bool cv) {
+  if (bv && cv) return cbwd_kernel<IO, true, true>;
+  if (bv) return cbwd_kernel<IO, true, false>;
+  if (cv) return cbwd_kernel<IO, false, true>;
+  return cbwd_kernel<IO, false, false>;
+}
+
+struct CbwdPlan {
+  int groups_eff, nblk;
+  int64_t cpg;
+  size_t off_bc, off_dA, off_fB, off_fC, off_dD, off_db, ws_bytes;
+};
+
+size_t up256c(size_t v) { return (v + 255) / 256 * 256; }
+
+CbwdPlan cbwd_plan(const ssm_scan_bwd_args_t *a) {
+  CbwdPlan pl{};
+  const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
+  pl.groups_eff = (bv || cv) ? static_cast<int>(a->ngroups) : 1;
+  pl.cpg = a->dim / pl.groups_eff;
+  pl.nblk = static_cast<int>((pl.cpg + kChPerWG - 1) / kChPerWG);
+  const size_t f = sizeof(float);
+  const size_t per_batch = static_cast<size_t>(a->batch) * a->dim * a->dstate * 2 * f;
+  size_t off = 0;
+  pl.off_bc = off;
+  if (bv || cv) off += up256c(static_cast<size_t>(a->batch) * a->ngroups * pl.nblk * a->seqlen * a->dstate * 4 * f);
+  pl.off_dA = off; off += up256c(per_batch);
+  pl.off_fB = off; if (!bv) off += up256c(per_batch);
+  pl.off_fC = off; if (!cv) off += up256c(per_batch);
+  pl.off_dD = off; off += up256c(static_cast<size_t>(a->batch) * a->dim * f);
+  pl.off_db = off; off += up256c(static_cast<size_t>(a->batch) * a->dim * f);
+  pl.ws_bytes = off;
+  return pl;
+}
+
+}  // namespace
+}  // namespace ssm
+
+using namespace ssm;
+
+extern "C" int ssm_scan_bwd_complex_workspace_size(const ssm_scan_bwd_args_t *a, size_t *bytes) {
+  const int st = ssm_scan_bwd_complex_validate(a);
+  if (st != SSM_OK) return st;
+  if (!bytes) return SSM_ERR_NULL;
+  *bytes = cbwd_plan(a).ws_bytes;
+  return SSM_OK;
+}
+
+extern "C" int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
+  const int st = ssm_scan_bwd_complex_validate(a);
+  if (st != SSM_OK) return st;
+  const CbwdPlan pl = cbwd_plan(a);
+  if (!a->workspace || a->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
+  const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
+  CbwdParams p{};
+  p.u = a->u; p.delta = a->delta; p.B = a->B; p.C = a->C; p.z = a->z; p.dout = a->dout;
+  p.A = a->A; p.D = a->D; p.dbias = a->delta_bias; p.ckpt = a->checkpoints;
+  p.du = a->du; p.ddelta = a->ddelta; p.dz = a->dz;
+  p.dA = a->dA; p.dB = a->dB; p.dC = a->dC; p.dD = a->dD; p.ddbias = a->ddelta_bias;
+  p.dinit = a->dinitial_state;
+  char *ws = static_cast<char *>(a->workspace);
+  p.ws_bc = reinterpret_cast<float *>(ws + pl.off_bc);
+  p.ws_dA = reinterpret_cast<float *>(ws + pl.off_dA);
+  p.ws_fB = reinterpret_cast<float *>(ws + pl.off_fB);
+  p.ws_fC = reinterpret_cast<float *>(ws + pl.off_fC);
+  p.ws_dD = reinterpret_cast<float *>(ws + pl.off_dD);
+  p.ws_db = reinterpret_cast<float *>(ws + pl.off_db);
+  p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
+  p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
+  p.cpg = pl.cpg;
+  p.n = static_cast<int>(a->dstate); p.ngroups = static_cast<int>(a->ngroups);
+  p.groups_eff = pl.groups_eff; p.nblk = pl.nblk;
+  p.softplus = a->delta_softplus;
+  const int64_t nwg = a->batch * pl.groups_eff * pl.nblk;
+  int64_t nsum = a->dim * a->dstate;
+  if (bv || cv) {
+    const int64_t v = a->batch * a->ngroups * a->seqlen * a->dstate;
+    if (v > nsum) nsum = v;
+  }
+  if (a->dim > nsum) nsum = a->dim;
+  const int64_t sum_blocks = (nsum + 255) / 256;
+  if (nwg > 0x7fffffffLL || sum_blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  CbwdFn f = a->io_dtype == SSM_BF16 ? pick_cbwd<1>(bv, cv)
+           : a->io_dtype == SSM_F16  ? pick_cbwd<2>(bv, cv)
+                                     : pick_cbwd<0>(bv, cv);
+  hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(nwg)), dim3(512), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  hipLaunchKernelGGL(cbwd_sum_kernel, dim3(static_cast<unsigned>(sum_blocks)), dim3(256), 0, stream, p,
+                     static_cast<int>(bv), static_cast<int>(cv));
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}

@@ -11,11 +11,10 @@
 //     y_t    = Re(sum_s C_t[s] x_t[s]),   out_t = (y_t + D u_t) silu(z_t)
 //
 // Complex values are (real, imaginary) pairs of the element type, the pair
-// innermost.  Per (timestep, state) the decay is
-//   exp(delta' A) = 2^(delta' Re A log2 e) * (cos 2 pi r, sin 2 pi r),
-//   r = fract(delta' Im A / (2 pi)),
-// with the hardware exp2 and the hardware sine and cosine, which take their
-// argument in revolutions (the fraction keeps it in [0, 1)).
+// innermost.  The decay exp(delta' A) and delta' = softplus(delta + bias)
+// are formed as complex_util.h describes: the hardware exp2, sine and cosine
+// (in revolutions), with the phase and the softplus carried to about one
+// rounding, since large |Im A| magnifies their errors.
 //
 // Work decomposition (the real kernel's, in scan_kernel.h): four lanes per
 // channel, lane q holding complex states [q*NSW, (q+1)*NSW) in VGPRs; chunks
@@ -31,6 +30,7 @@
 
 #include <cstdint>
 
+#include "complex_util.h"
 #include "host_util.h"
 #include "scan_kernel.h"
 #include "ssmscan.h"
@@ -38,28 +38,21 @@
 namespace ssm {
 namespace {
 
-constexpr float kInv2Pi = 0.15915494309189535f;
 constexpr int kLPC = 4;                 // lanes per channel
 constexpr int kT = 8 * kLPC;            // timesteps per chunk
 constexpr int kCPW = 64 / kLPC;         // channels per wave
+static_assert(kT == SSM_CKPT_INTERVAL, "a checkpoint at every chunk start");
 
 struct CplxParams {
   const void *u, *delta, *B, *C, *z;
   const float *A, *D, *dbias, *init;
   void *out;
   float *last;
-  int64_t batch, dim, seqlen, cpg;
+  float *ckpt;   // the state before every SSM_CKPT_INTERVAL-th timestep, or null
+  int64_t batch, dim, seqlen, cpg, nck;
   int n, ngroups, groups_eff, nblk, nblocks;
   int softplus, vec, xcd_swizzle;
 };
-
-// exp(dt * (ar + i ai)) with ar2 = ar * log2 e and airev = ai / (2 pi)
-__device__ __forceinline__ void cexp_step(float dt, float ar2, float airev, float &er, float &ei) {
-  const float mag = fast_exp2(dt * ar2);
-  const float r = __builtin_amdgcn_fractf(dt * airev);
-  er = mag * __builtin_amdgcn_cosf(r);
-  ei = mag * __builtin_amdgcn_sinf(r);
-}
 
 template <int IO, int NSW, bool BV, bool CV>
 __global__ void __launch_bounds__(64)
@@ -99,14 +92,16 @@ scan_complex_kernel(const CplxParams p) {
   const int n = p.n;
   const bool vec = p.vec != 0;
 
-  float Ar[NSW], Ai[NSW], Bfr[NSW], Bfi[NSW], Cfr[NSW], Cfi[NSW], xr[NSW], xi[NSW];
+  float Ar[NSW], Ai[NSW], Al[NSW], Bfr[NSW], Bfi[NSW], Cfr[NSW], Cfi[NSW], xr[NSW], xi[NSW];
 #pragma unroll
   for (int k = 0; k < NSW; ++k) {
     const int s = s0 + k;
     const bool sv = s < n;
     const int64_t e = (dl * n + s) * 2;
     Ar[k] = sv ? p.A[e] * kLog2e : 0.0f;
-    Ai[k] = sv ? p.A[e + 1] * kInv2Pi : 0.0f;
+    const Turns tr = turns_of(sv ? p.A[e + 1] : 0.0f);
+    Ai[k] = tr.hi;
+    Al[k] = tr.lo;
     Bfr[k] = (!BV && sv) ? load_io<IO>(p.B, e) : 0.0f;
     Bfi[k] = (!BV && sv) ? load_io<IO>(p.B, e + 1) : 0.0f;
     Cfr[k] = (!CV && sv) ? load_io<IO>(p.C, e) : 0.0f;
@@ -182,7 +177,7 @@ scan_complex_kernel(const CplxParams p) {
     for (int i = 0; i < kKP; ++i) {
       const float uu = r_u.get(i);
       float dt = r_dl.get(i) + bias;
-      if (p.softplus) dt = softplus_f(dt);
+      if (p.softplus) dt = softplus_acc(dt);
       if (!FC && i >= cnt) dt = 0.0f;
       dtv[i] = dt;
       dtuv[i] = dt * uu;
@@ -220,7 +215,7 @@ scan_complex_kernel(const CplxParams p) {
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
       float er, ei;
-      cexp_step(in.dt, Ar[k], Ai[k], er, ei);
+      cexp_turns(in.dt, Ar[k], Ai[k], Al[k], er, ei);
       const float br = in.Br[k] * in.dtu, bi = in.Bi[k] * in.dtu;
       const float nr = fmaf(er, xr[k], fmaf(-ei, xi[k], br));
       const float ni = fmaf(er, xi[k], fmaf(ei, xr[k], bi));
@@ -251,6 +246,15 @@ scan_complex_kernel(const CplxParams p) {
     if constexpr (ANYV) stage_bc();
     wave_lds_sync();            // the slice is written before any lane reads it
     const RawV<IO, kKP> z_cur = r_z;
+    if (p.ckpt && valid) {   // the state before timestep c (the backward starts its chunks there)
+      float *dst = p.ckpt + ((row * p.nck + c / kT) * n) * 2;
+#pragma unroll
+      for (int k = 0; k < NSW; ++k)
+        if (s0 + k < n) {
+          dst[(s0 + k) * 2] = xr[k];
+          dst[(s0 + k) * 2 + 1] = xi[k];
+        }
+    }
     if (c + kT < seqlen) {
       fetch(c + kT);
       if constexpr (ANYV) fetch_bc(c + kT);
@@ -337,6 +341,8 @@ extern "C" int ssm_scan_fwd_complex(const ssm_scan_args_t *a, void *stream_ptr) 
   p.u = a->u; p.delta = a->delta; p.B = a->B; p.C = a->C; p.z = a->z;
   p.A = a->A; p.D = a->D; p.dbias = a->delta_bias; p.init = a->initial_state;
   p.out = a->out; p.last = a->last_state;
+  p.ckpt = a->checkpoints;
+  p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
   p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
   p.n = n; p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = (bv || cv) ? p.ngroups : 1;

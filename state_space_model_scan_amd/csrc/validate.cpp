@@ -60,7 +60,7 @@ extern "C" int ssm_scan_complex_validate(const ssm_scan_args_t *a) {
   const int st = ssm_scan_validate(a);
   if (st != SSM_OK) return st;
   if (!product_fits(a->batch, 2 * a->ngroups * a->dstate, a->seqlen)) return SSM_ERR_SHAPE;
-  if (a->conv_weight || a->checkpoints) return SSM_ERR_UNSUPPORTED;
+  if (a->conv_weight) return SSM_ERR_UNSUPPORTED;
   if (!a->u) return SSM_ERR_NULL;
   return SSM_OK;
 }
@@ -96,6 +96,18 @@ extern "C" int ssm_scan_bwd_validate(const ssm_scan_bwd_args_t *a) {
       !a->du || !a->ddelta || !a->dA || !a->dB || !a->dC)
     return SSM_ERR_NULL;
   if ((a->z && !a->dz) || (a->D && !a->dD) || (a->delta_bias && !a->ddelta_bias)) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
+extern "C" int ssm_scan_bwd_complex_validate(const ssm_scan_bwd_args_t *a) {
+  if (!a) return SSM_ERR_NULL;
+  const int st = ssm_scan_bwd_validate(a);
+  if (st != SSM_OK) return st;
+  // complex B/C are pairs: twice the elements of the real layout
+  if (!product_fits(a->batch, 2 * a->ngroups * a->dstate, a->seqlen) ||
+      !product_fits(a->batch * a->dim, 2 * a->dstate, a->seqlen))
+    return SSM_ERR_SHAPE;
+  if (a->seq_segments > 1) return SSM_ERR_UNSUPPORTED;   // no sequence split
   return SSM_OK;
 }
 

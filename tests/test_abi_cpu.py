@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 11
+    assert L.ssm_abi_version() == 12
 
 
 def test_status_strings():
@@ -436,10 +436,11 @@ def test_complex_validation():
     assert v(_good_args(ngroups=3)) == _lib.SSM_ERR_SHAPE
     assert v(_good_args(dstate=17)) == _lib.SSM_ERR_UNSUPPORTED
     assert v(_good_args(conv_weight=FAKE, conv_x=FAKE, conv_width=4)) == _lib.SSM_ERR_UNSUPPORTED
-    assert v(_good_args(checkpoints=FAKE)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_args(checkpoints=FAKE)) == _lib.SSM_OK   # the backward's saved states
     assert L.ssm_scan_complex_validate(None) == _lib.SSM_ERR_NULL
     assert L.ssm_scan_fwd_complex(ctypes.byref(_good_args(delta=None)), None) == _lib.SSM_ERR_NULL
-    assert L.ssm_scan_fwd_complex(ctypes.byref(_good_args(checkpoints=FAKE)), None) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssm_scan_fwd_complex(ctypes.byref(_good_args(conv_weight=FAKE, conv_x=FAKE, conv_width=4)),
+                                  None) == _lib.SSM_ERR_UNSUPPORTED
 
 
 def test_complex_binding_errors():
@@ -477,3 +478,23 @@ def test_plan_query():
     assert plan(dstate=8).lanes_per_channel == 2 and plan(dstate=8).waves == 2 * 2
     assert L.ssm_scan_plan(ctypes.byref(_good_args(delta=None)), ctypes.byref(_lib.ScanPlan())) == _lib.SSM_ERR_NULL
     assert L.ssm_scan_plan(ctypes.byref(_good_args()), None) == _lib.SSM_ERR_NULL
+
+
+def test_complex_bwd_validation():
+    """ssm_scan_bwd_complex: the real backward's checks, no sequence split,
+    and the workspace required before anything is enqueued."""
+    L = _lib.lib()
+    v = lambda a: L.ssm_scan_bwd_complex_validate(ctypes.byref(a))  # noqa: E731
+    assert v(_good_bwd()) == _lib.SSM_OK
+    assert v(_good_bwd(seq_segments=1)) == _lib.SSM_OK
+    assert v(_good_bwd(seq_segments=2)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_bwd(checkpoints=None)) == _lib.SSM_ERR_NULL
+    assert v(_good_bwd(dstate=17)) == _lib.SSM_ERR_UNSUPPORTED
+    assert L.ssm_scan_bwd_complex_validate(None) == _lib.SSM_ERR_NULL
+    a = _good_bwd()
+    need = ctypes.c_size_t(0)
+    assert L.ssm_scan_bwd_complex_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.SSM_OK
+    assert need.value > 0
+    assert L.ssm_scan_bwd_complex(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE, need.value - 1
+    assert L.ssm_scan_bwd_complex(ctypes.byref(a), None) == _lib.SSM_ERR_WORKSPACE
