@@ -103,6 +103,7 @@ KERNEL_SRCS = ("scan_kernel.h", "device_util.h", "scan_bf16.hip", "scan_f32.hip"
 DECODE_SRCS = ("decode.hip", "device_util.h")
 SSD_SRCS = ("ssd.hip", "device_util.h")
 BWD_SRCS = ("bwd.hip", "device_util.h")
+CBWD_SRCS = ("bwd_complex.hip", "complex_util.h", "device_util.h")
 COMPLEX_SRCS = ("scan_complex.hip", "complex_util.h", "scan_kernel.h", "device_util.h")
 CONV_SRCS = ("ssm_scan.hip", "device_util.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -269,11 +270,11 @@ def main():
     from state_space_model_scan_amd.inputs import SSD_WORKLOADS
     if args.workload in SSD_WORKLOADS:
         return ssd_main(args)
+    from state_space_model_scan_amd.inputs import COMPLEX_WORKLOADS
     if args.backward:
-        return bwd_main(args)
+        return complex_bwd_main(args) if args.workload in COMPLEX_WORKLOADS else bwd_main(args)
     if args.conv:
         return conv_main(args)
-    from state_space_model_scan_amd.inputs import COMPLEX_WORKLOADS
     if args.workload in COMPLEX_WORKLOADS:
         return complex_main(args)
 
@@ -1025,6 +1026,151 @@ def bwd_cpu_baseline(w, t, dout, budget_s: float):
             "sample": f"{nch} channels of batch 0 x full seqlen {w.seqlen} (backward), {dt:.1f} s float64 "
                       f"on 1 thread"}
 
+
+
+def complex_bwd_bytes(w) -> int:
+    """Complex backward minimum: u, delta, z, dout (io), complex B, C (io
+    pairs) and the complex checkpoints (fp32 pairs) read once; du, ddelta, dz
+    (io) and dA, dB, dC (fp32 pairs), dD, d(delta_bias) (fp32) written once."""
+    es = io_bytes(w.io_dtype)
+    E = w.elements
+    n = w.dstate
+    zed = 1 if w.has_z else 0
+    bcn = 2 * (w.dim * n if w.bc_kind == "fixed" else w.batch * w.ngroups * n * w.seqlen)
+    nck = -(-w.seqlen // 32)
+    reads = ((3 + zed) * E * es + 2 * bcn * es + w.batch * w.dim * nck * n * 8 + w.dim * n * 8
+             + 2 * w.dim * 4)
+    writes = (2 + zed) * E * es + 2 * bcn * 4 + w.dim * n * 8 + 2 * w.dim * 4
+    return reads + writes
+
+
+def complex_bwd_alu_ops(w) -> float:
+    """Per (timestep, state): the forward re-run (delta' times Re A and Im A,
+    the phase's fraction, the decay's two products, delta'u B (2), the
+    complex state update (4): 11 plain ops and exp2, sine, cosine); the
+    adjoint (Re(C x) 2, h += dy conj C 2, dy conj x 2, h conj x 4, A a 4,
+    Re(h conj B) 2, the delta' term 3, the du term 1, dA 6, dB 2, the carry
+    conj(a) h 4, the three sums over states 3 and the four sums of dB/dC over
+    channels 4: 39).  Per element: softplus, its derivative, silu and its
+    derivative (seven transcendentals) and about 20 plain ops.  The kernel
+    also recomputes a_t and x_t in its backward walk; those are not counted."""
+    return float(w.elements) * ((50 + 3 * TRANS_WEIGHT) * w.dstate + 20 + 7 * TRANS_WEIGHT)
+
+
+def complex_bwd_main(args):
+    """One ssm_scan_bwd_complex call (every gradient) per timed step, from
+    the checkpoints of one ssm_scan_fwd_complex run before the timed region."""
+    import torch
+    from state_space_model_scan_amd import _lib, binding
+    from state_space_model_scan_amd.inputs import BF16, COMPLEX_WORKLOADS, F16, make_complex_inputs, make_dout
+
+    _lib.lib()
+    w = COMPLEX_WORKLOADS[args.workload]
+    t = make_complex_inputs(w)
+    dout_np = make_dout(w)
+    io = w.io_dtype
+
+    def dev(a, param=False):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if not param and io in (BF16, F16) and a.dtype == np.uint16:
+            x = x.view(torch.bfloat16 if io == BF16 else torch.float16)
+        return x.cuda()
+
+    u, delta, z, B, C = dev(t["u"]), dev(t["delta"]), dev(t["z"]), dev(t["B"]), dev(t["C"])
+    A, D, bias = dev(t["A"], True), dev(t["D"], True), dev(t["delta_bias"], True)
+    init = dev(t["initial_state"], True)
+    dout = dev(dout_np)
+    ck = torch.empty((w.batch, w.dim, binding.checkpoint_count(w.seqlen), w.dstate, 2), dtype=torch.float32,
+                     device="cuda")
+    binding.ssm_scan_fwd_complex(u, delta, A, B, C, D, z, bias, w.softplus, initial_state=init, checkpoints=ck)
+
+    def step():
+        binding.ssm_scan_bwd_complex(u, delta, A, B, C, dout, ck, D=D, z=z, delta_bias=bias,
+                                     delta_softplus=w.softplus)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    settle(step)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    k_s = float(np.mean(ms)) / 1e3
+    tops = complex_bwd_alu_ops(w) / k_s / 1e12
+    nbytes = complex_bwd_bytes(w)
+    gbs = nbytes / k_s / 1e9
+    iot = {0: "fp32", 1: "bf16", 2: "fp16"}[io]
+    rec = {
+        "metric": "complex-A selective-scan bwd elements/s (b·d·l), all input gradients",
+        "value": w.elements * args.steps / wall, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} backward: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} "
+                               f"g={w.ngroups} complex A/B/C, B/C {w.bc_kind}, {iot} io, fp32 complex state, "
+                               f"checkpoints every 32 timesteps from the forward",
+                   "io_dtype": iot, "elements_per_step": w.elements},
+        "roofline": {
+            "bound": "alu", "achieved": tops, "peak": ALU_PEAK_TOPS,
+            "unit": "T fp32 VALU lane-ops/s (transcendental weighted 2)", "frac": tops / ALU_PEAK_TOPS,
+            "traffic": load_traffic(f"{w.name}_bwd", CBWD_SRCS),
+            "kernel": "cbwd_kernel (+ cbwd_sum_kernel, the partial sums: the step's events bracket both)",
+            "kernel_avg_ms": k_s * 1e3, "kernel_median_ms": float(np.median(ms)),
+            "hbm": {"achieved_GBs": gbs, "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes": nbytes},
+        },
+        "cpu_baseline": (None if args.no_cpu_baseline
+                         else complex_bwd_cpu_baseline(w, t, dout_np, args.cpu_budget)),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def complex_bwd_cpu_baseline(w, t, dout, budget_s: float):
+    """The oracle's complex backward (one thread) on the first channels of
+    batch 0's first group, grown until it takes about budget_s / 4."""
+    from oracle import oracle as orc
+    from state_space_model_scan_amd.inputs import io_bits_to_f64
+    cpg = w.dim // w.ngroups
+    nch = 8
+    fixed = w.bc_kind == "fixed"
+    while True:
+        ch = slice(0, nch)
+        sub = {}
+        for k in ("u", "delta", "z"):
+            sub[k] = None if t[k] is None else np.ascontiguousarray(t[k][0:1, ch])
+        for k in ("B", "C"):
+            sub[k] = np.ascontiguousarray(t[k][ch] if fixed else t[k][0:1, 0:1])
+        for k in ("A", "D", "delta_bias"):
+            sub[k] = None if t[k] is None else np.ascontiguousarray(t[k][ch])
+        init = None if t["initial_state"] is None else t["initial_state"][0:1, ch].astype(np.float64)
+        d64 = io_bits_to_f64(np.ascontiguousarray(dout[0:1, ch]), w.io_dtype)
+        t0 = time.perf_counter()
+        orc.selective_scan_complex_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], d64, sub["D"],
+                                       sub["z"], sub["delta_bias"], w.softplus, io_dtype=w.io_dtype, ngroups=1,
+                                       B_kind=orc.BC_FIXED if fixed else orc.BC_VARYING,
+                                       C_kind=orc.BC_FIXED if fixed else orc.BC_VARYING, initial_state=init)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or nch >= cpg:
+            break
+        nch = min(cpg, nch * 4)
+    return {"value": nch * w.seqlen / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nch} channels of batch 0 x full seqlen {w.seqlen} (complex backward), {dt:.1f} s "
+                      f"float64 on 1 thread"}
 
 
 # ---------------------------------------------------------------------------

@@ -197,11 +197,9 @@ int ssm_scan_plan(const ssm_scan_args_t *args, ssm_scan_plan_t *plan);
  * be NULL; run causal_conv1d_fwd first).  u is required; workspace is ignored
  * (the sequence is walked in one pass).  The decay's phase uses the
  * hardware sine and cosine on the fractional part of delta' Im(A) / (2 pi),
- * that product carried to about one rounding (Im(A) / (2 pi) held as two
- * floats, the product's rounding error recovered with an fma), and delta'
- * is the softplus without the cancellation of 1 + e^v: a large |Im A|
- * magnifies an error in either.  Same conventions and status codes as
- * ssm_scan_fwd. */
+ * and delta' is the softplus without the cancellation of 1 + e^v (a large
+ * |Im A| magnifies an error in delta').  Same conventions and status codes
+ * as ssm_scan_fwd. */
 int ssm_scan_fwd_complex(const ssm_scan_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssm_scan_fwd_complex (no HIP call). */
@@ -288,8 +286,11 @@ int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
  *     du_t    = D dy_t + delta'_t sum_s Re(h_t conj(B_t))
  *     ddelta_t = softplus'(.) (sum_s Re(G_a conj(A a_t)) + u_t sum_s Re(h_t conj(B_t)))
  *
- * with dy, dz, dD and d(delta_bias) as in ssm_scan_bwd; a_t and delta'_t
- * are formed as in ssm_scan_fwd_complex.  seq_segments must
+ * with dy, dz, dD and d(delta_bias) as in ssm_scan_bwd.  delta'_t is formed
+ * as in ssm_scan_fwd_complex, and the phase of a_t to about one rounding
+ * (Im(A) / (2 pi) held as two floats, the product's rounding error
+ * recovered with an fma): ddelta weighs a phase error by |A|^2 delta'.
+ * seq_segments must
  * be 0 or 1 (no sequence split; others return SSM_ERR_UNSUPPORTED); the
  * workspace (ssm_scan_bwd_complex_workspace_size) holds the partial sums and
  * is required.  Asynchronous on hip_stream; returns a status code. */

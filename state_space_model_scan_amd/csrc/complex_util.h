@@ -8,13 +8,19 @@
 // Where |Im A| is large the phase carries most of the rounding: a relative
 // error e in delta' or in Im A / (2 pi) turns into a phase error of
 // e * delta' |Im A| radians, and the gradient of delta' (which holds A a_t)
-// weighs it once more by |A|.  So both are formed to about one rounding:
-//   * Im A / (2 pi) is held as hi + lo (hi the fp32 quotient, lo its
-//     residual), and r = fract(delta' hi) + (delta' lo + the exact rounding
-//     error of delta' hi, from an fma);
-//   * softplus(v) = max(v, 0) + log1p(e^-|v|), where log1p(w) is
+// weighs it once more by |A|.  Hence:
+//   * softplus(v) = max(v, 0) + log1p(e^-|v|) everywhere, log1p(w) being
 //     log(1 + w) corrected by the rounding of 1 + w: with u = fl(1 + w) and
-//     c = (u - 1) - w (exact), log1p(w) = log(u) - c / u to first order.
+//     c = (u - 1) - w (exact), log1p(w) = log(u) - c / u to first order (the
+//     plain log2(1 + 2^x) loses up to ~30 ulp of delta' to that rounding);
+//   * the backward's phase to about one rounding (cexp_turns): Im A / (2 pi)
+//     held as hi + lo (the fp32 quotient and its residual), and
+//     r = fract(delta' hi) + (delta' lo + the exact rounding error of
+//     delta' hi, from an fma);
+//   * the forward's phase as fract(delta' hi) (cexp_plain): its outputs and
+//     the checkpoints the backward restarts from weigh a phase error once by
+//     |A|, not twice, and the three extra operations would be a sixth of the
+//     forward's issue per (timestep, state).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,7 +44,16 @@ __device__ __forceinline__ Turns turns_of(float ai) {
   return {hi, lo};
 }
 
-// exp(dt (ar + i ai)) from ar2 = ar log2 e and (hi, lo) = turns_of(ai)
+// exp(dt (ar + i ai)) from ar2 = ar log2 e and hi = ai / (2 pi)
+__device__ __forceinline__ void cexp_plain(float dt, float ar2, float hi, float &er, float &ei) {
+  const float mag = fast_exp2(dt * ar2);
+  const float r = __builtin_amdgcn_fractf(dt * hi);
+  er = mag * __builtin_amdgcn_cosf(r);
+  ei = mag * __builtin_amdgcn_sinf(r);
+}
+
+// exp(dt (ar + i ai)) from ar2 = ar log2 e and (hi, lo) = turns_of(ai),
+// the phase to about one rounding
 __device__ __forceinline__ void cexp_turns(float dt, float ar2, float hi, float lo, float &er,
                                            float &ei) {
   const float mag = fast_exp2(dt * ar2);

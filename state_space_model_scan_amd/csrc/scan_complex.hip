@@ -13,8 +13,8 @@
 // Complex values are (real, imaginary) pairs of the element type, the pair
 // innermost.  The decay exp(delta' A) and delta' = softplus(delta + bias)
 // are formed as complex_util.h describes: the hardware exp2, sine and cosine
-// (in revolutions), with the phase and the softplus carried to about one
-// rounding, since large |Im A| magnifies their errors.
+// (in revolutions) on the fraction of delta' Im A / (2 pi), and the softplus
+// without the cancellation of 1 + e^v.
 //
 // Work decomposition (the real kernel's, in scan_kernel.h): four lanes per
 // channel, lane q holding complex states [q*NSW, (q+1)*NSW) in VGPRs; chunks
@@ -92,16 +92,14 @@ scan_complex_kernel(const CplxParams p) {
   const int n = p.n;
   const bool vec = p.vec != 0;
 
-  float Ar[NSW], Ai[NSW], Al[NSW], Bfr[NSW], Bfi[NSW], Cfr[NSW], Cfi[NSW], xr[NSW], xi[NSW];
+  float Ar[NSW], Ai[NSW], Bfr[NSW], Bfi[NSW], Cfr[NSW], Cfi[NSW], xr[NSW], xi[NSW];
 #pragma unroll
   for (int k = 0; k < NSW; ++k) {
     const int s = s0 + k;
     const bool sv = s < n;
     const int64_t e = (dl * n + s) * 2;
     Ar[k] = sv ? p.A[e] * kLog2e : 0.0f;
-    const Turns tr = turns_of(sv ? p.A[e + 1] : 0.0f);
-    Ai[k] = tr.hi;
-    Al[k] = tr.lo;
+    Ai[k] = sv ? p.A[e + 1] * kInv2PiF : 0.0f;
     Bfr[k] = (!BV && sv) ? load_io<IO>(p.B, e) : 0.0f;
     Bfi[k] = (!BV && sv) ? load_io<IO>(p.B, e + 1) : 0.0f;
     Cfr[k] = (!CV && sv) ? load_io<IO>(p.C, e) : 0.0f;
@@ -215,7 +213,7 @@ scan_complex_kernel(const CplxParams p) {
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
       float er, ei;
-      cexp_turns(in.dt, Ar[k], Ai[k], Al[k], er, ei);
+      cexp_plain(in.dt, Ar[k], Ai[k], er, ei);
       const float br = in.Br[k] * in.dtu, bi = in.Bi[k] * in.dtu;
       const float nr = fmaf(er, xr[k], fmaf(-ei, xi[k], br));
       const float ni = fmaf(er, xi[k], fmaf(ei, xr[k], bi));
