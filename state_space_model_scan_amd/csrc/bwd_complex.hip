@@ -175,12 +175,15 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
       else { cr = Cfr; cim = Cfi; }
     };
 
-    // ---- forward re-run: x_{t-1} of every timestep of the chunk
-    float pr[kCk], pim[kCk];
-    static_for(std::make_integer_sequence<int, kCk>{}, [&](auto TT) {
+    // ---- forward re-run and backward walk, in two halves of kH timesteps.
+    // x_{t-1} of the half being walked is kept in registers.  The first half
+    // is re-run twice, once to reach the second half's start and once to keep
+    // its states: a sixth more work for half the registers the saved states
+    // take, which lets two workgroups share a compute unit.
+    constexpr int kH = kCk / 2;
+    const float x0r = xr, x0i = xi;
+    auto fstep = [&](auto TT) {   // x <- a_t x + delta'_t u_t B_t
       constexpr int t = decltype(TT)::value;
-      pr[t] = xr;
-      pim[t] = xi;
       if (t < len) {
         const float dt = row_bcast<t % 16>(o_dt[t / 16]);
         const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
@@ -192,12 +195,11 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         xr = nr;
         xi = ni;
       }
-    });
-
-    // ---- backward walk; the owners keep y_t, the delta' term and the u term
+    };
+    // the owners keep y_t, the delta' term and the u term
     float r_y[2] = {0.0f, 0.0f}, r_ddt[2] = {0.0f, 0.0f}, r_du[2] = {0.0f, 0.0f};
-    static_for(std::make_integer_sequence<int, kCk>{}, [&](auto TR) {
-      constexpr int t = kCk - 1 - decltype(TR)::value;
+    auto bstep = [&](auto TT, const float xpv_r, const float xpv_i) {
+      constexpr int t = decltype(TT)::value;
       if (t < len) {
         const float dt = row_bcast<t % 16>(o_dt[t / 16]);
         const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
@@ -207,7 +209,7 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
         bcoef(t, br, bi);
         ccoef(t, cr, cim);
-        const float xpr = pr[t], xpi = pim[t];                 // x_{t-1}
+        const float xpr = xpv_r, xpi = xpv_i;                  // x_{t-1}
         const float xtr = fmaf(er, xpr, fmaf(-ei, xpi, br * dtu));
         const float xti = fmaf(er, xpi, fmaf(ei, xpr, bi * dtu));
         const float yp = fmaf(cr, xtr, -cim * xti);            // Re(C x_t)
@@ -237,6 +239,30 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         const float ys = row_sum16(yp), ds = row_sum16(ddtp), us = row_sum16(dup);
         if (s == t % 16) { r_y[t / 16] = ys; r_ddt[t / 16] = ds; r_du[t / 16] = us; }
       }
+    };
+    float pr[kH], pim[kH];
+    static_for(std::make_integer_sequence<int, kH>{}, [&](auto J) { fstep(J); });
+    static_for(std::make_integer_sequence<int, kH>{}, [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      pr[j] = xr;
+      pim[j] = xi;
+      fstep(std::integral_constant<int, kH + j>{});
+    });
+    static_for(std::make_integer_sequence<int, kH>{}, [&](auto J) {
+      constexpr int j = kH - 1 - decltype(J)::value;
+      bstep(std::integral_constant<int, kH + j>{}, pr[j], pim[j]);
+    });
+    xr = x0r;
+    xi = x0i;
+    static_for(std::make_integer_sequence<int, kH>{}, [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      pr[j] = xr;
+      pim[j] = xi;
+      fstep(J);
+    });
+    static_for(std::make_integer_sequence<int, kH>{}, [&](auto J) {
+      constexpr int j = kH - 1 - decltype(J)::value;
+      bstep(std::integral_constant<int, j>{}, pr[j], pim[j]);
     });
 
     // ---- the owners' gradients of their timesteps
