@@ -213,3 +213,51 @@ def test_complex_bwd_mid_size():
     w = BASE.scaled(batch=2, dim=256, seqlen=1000, dstate=16, ngroups=4, io_dtype=BF16, A_imag="normal",
                     init_state=True, seed=895)
     _run(w, "mid size")
+
+
+def test_complex_bwd_full_size_slices():
+    """mamba2p8b_complex (b=8 d=5120 l=2048 n=16 g=4, bf16, complex A/B/C)
+    through the GPU in the launch configuration bench.py times; the oracle on
+    batch 5 / group 1 (all 1280 channels of the group: complete dB and dC
+    sums) and on every batch of channels 0, 3001 and 5119 (dA, dD,
+    ddelta_bias)."""
+    import torch
+    from state_space_model_scan_amd import binding
+    w = COMPLEX_WORKLOADS["mamba2p8b_complex"]
+    log(f"[cbwd] full size {w.name}")
+    t = make_complex_inputs(w)
+    dout = make_dout(w)
+    g = _gpu(w, t, dout, want_dinit=False)
+
+    bb, gg = 5, 1
+    cpg = w.dim // w.ngroups
+    ch = slice(gg * cpg, (gg + 1) * cpg)
+    sub = w.scaled(batch=1, dim=cpg, ngroups=1)
+    ts = dict(t)
+    for k in ("u", "delta", "z"):
+        ts[k] = np.ascontiguousarray(t[k][bb:bb + 1, ch])
+    for k in ("B", "C"):
+        ts[k] = np.ascontiguousarray(t[k][bb:bb + 1, gg:gg + 1])
+    for k in ("A", "D", "delta_bias"):
+        ts[k] = np.ascontiguousarray(t[k][ch])
+    want = _oracle(sub, ts, np.ascontiguousarray(dout[bb:bb + 1, ch]))
+    got = {k: g[k][bb:bb + 1, ch] for k in ("du", "ddelta", "dz")}
+    got["dB"] = g["dB"][bb:bb + 1, gg:gg + 1]
+    got["dC"] = g["dC"][bb:bb + 1, gg:gg + 1]
+    errs = _compare(w, got, want, f"full size (b={bb}, g={gg})", names=("du", "ddelta", "dz", "dB", "dC"))
+    log(f"[cbwd]   slice errors {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
+
+    for d in (0, 3001, 5119):
+        gi = d // cpg
+        one = w.scaled(dim=1, ngroups=1)
+        t1 = dict(t)
+        for k in ("u", "delta", "z"):
+            t1[k] = np.ascontiguousarray(t[k][:, d:d + 1])
+        for k in ("B", "C"):
+            t1[k] = np.ascontiguousarray(t[k][:, gi:gi + 1])
+        for k in ("A", "D", "delta_bias"):
+            t1[k] = np.ascontiguousarray(t[k][d:d + 1])
+        want1 = _oracle(one, t1, np.ascontiguousarray(dout[:, d:d + 1]))
+        got1 = {k: g[k][d:d + 1] for k in ("dA", "dD", "ddelta_bias")}
+        errs = _compare(w, got1, want1, f"full size channel {d}", names=("dA", "dD", "ddelta_bias"))
+        log(f"[cbwd]   channel {d} errors {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
