@@ -87,6 +87,15 @@ def _load():
             i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, i32, p, p, i32, p, p, p,
             i32, ctypes.c_double, ctypes.c_double, p, i32]
         lib.oracle_ssd_scan.restype = i32
+        d = ctypes.c_double
+        lib.oracle_ssd_chunk_state.argtypes = [i64, i64, i64, i64, i64, i64, i32, i64, p, p, p, p, p, i32,
+                                               i32, d, d, p, p, p]
+        lib.oracle_ssd_chunk_state.restype = i32
+        lib.oracle_ssd_state_passing.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p]
+        lib.oracle_ssd_state_passing.restype = i32
+        lib.oracle_ssd_chunk_scan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i64, p, p, p, p, p, p, i32,
+                                              p, p, i32, i32, d, d, p, p, p, p]
+        lib.oracle_ssd_chunk_scan.restype = i32
         lib.oracle_selective_scan_bwd.argtypes = [
             i64, i64, i64, i64, i64, i32, p, p, p, p, i32, p, i32, p, p, p, i32, p, p,
             p, p, p, p, p, p, p, p, p]
@@ -371,6 +380,83 @@ def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False, *,
                              int(dt_limit is not None), lim[0], lim[1], _ptr(sid), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_ssd_scan failed with status {rc}")
+    return out, fin
+
+
+def _ssd_common(x, dt, B, dt_limit, seq_idx, io_dtype):
+    x, dt, B = _io(x, io_dtype), _io(dt, io_dtype), _io(B, io_dtype)
+    batch, seqlen, nheads, headdim = x.shape
+    sid = None if seq_idx is None else np.ascontiguousarray(seq_idx, dtype=np.int32)
+    if sid is not None and sid.shape != (batch, seqlen):
+        raise ValueError("seq_idx must be (batch, seqlen)")
+    lim = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    return x, dt, B, sid, lim
+
+
+def ssd_chunk_state(x, dt, A, B, chunk_size, dt_bias=None, dt_softplus=False, *, io_dtype=F32,
+                    dt_limit=None, seq_idx=None):
+    """Oracle chunk_state: per chunk of chunk_size tokens its end state from
+    a zero state and the factor P of the state entering it (0 where the
+    state restarts inside it).  Inputs as ``ssd_scan``.  Returns
+    (states (nchunks, batch, nheads, headdim, dstate), decays (nchunks,
+    batch, nheads)), float64."""
+    lib = _load()
+    x, dt, B, sid, lim = _ssd_common(x, dt, B, dt_limit, seq_idx, io_dtype)
+    A, dt_bias = _f32(A), _f32(dt_bias)
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    nc = -(-seqlen // chunk_size)
+    states = np.empty((nc, batch, nheads, headdim, dstate))
+    decays = np.empty((nc, batch, nheads))
+    rc = lib.oracle_ssd_chunk_state(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_size,
+                                    _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(dt_bias), int(bool(dt_softplus)),
+                                    int(dt_limit is not None), lim[0], lim[1], _ptr(sid), _ptr(states),
+                                    _ptr(decays))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_chunk_state failed with status {rc}")
+    return states, decays
+
+
+def ssd_state_passing(states, decays, initial_states=None):
+    """Oracle state_passing: carried[c] = the state entering chunk c
+    (S_0 = initial_states or zero, S_{c+1} = decays[c] S_c + states[c]) and
+    the final state.  Returns (carried (nchunks, batch, nheads, headdim,
+    dstate), final (batch, nheads, headdim, dstate)), float64."""
+    lib = _load()
+    states = np.ascontiguousarray(states, dtype=np.float64)
+    decays = np.ascontiguousarray(decays, dtype=np.float64)
+    nc, batch, nheads, headdim, dstate = states.shape
+    init = None if initial_states is None else np.ascontiguousarray(initial_states, dtype=np.float64)
+    carried = np.empty(states.shape)
+    fin = np.empty(states.shape[1:])
+    rc = lib.oracle_ssd_state_passing(nc, batch, nheads, headdim, dstate, _ptr(states), _ptr(decays),
+                                      _ptr(init), _ptr(carried), _ptr(fin))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_state_passing failed with status {rc}")
+    return carried, fin
+
+
+def ssd_chunk_scan(x, dt, A, B, C, carried, chunk_size, D=None, z=None, dt_bias=None, dt_softplus=False, *,
+                   io_dtype=F32, dt_limit=None, seq_idx=None):
+    """Oracle chunk scan: every chunk's outputs from the recurrence started
+    at carried[c].  Returns (out (batch, seqlen, nheads, headdim), the state
+    after the last chunk (batch, nheads, headdim, dstate)), float64."""
+    lib = _load()
+    x, dt, B, sid, lim = _ssd_common(x, dt, B, dt_limit, seq_idx, io_dtype)
+    C, z = _io(C, io_dtype), _io(z, io_dtype)
+    A, D, dt_bias = _f32(A), _f32(D), _f32(dt_bias)
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    carried = np.ascontiguousarray(carried, dtype=np.float64)
+    out = np.empty(x.shape)
+    fin = np.empty((batch, nheads, headdim, dstate))
+    rc = lib.oracle_ssd_chunk_scan(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_size,
+                                   _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   int(D is not None and D.ndim == 2), _ptr(z), _ptr(dt_bias),
+                                   int(bool(dt_softplus)), int(dt_limit is not None), lim[0], lim[1], _ptr(sid),
+                                   _ptr(carried), _ptr(out), _ptr(fin))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_chunk_scan failed with status {rc}")
     return out, fin
 
 

@@ -1052,6 +1052,148 @@ int oracle_ssd_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headd
     return failed ? 5 : 0;
 }
 
+/* ---- the chunk-scan operators split into their three parts ---------------- */
+
+/* Section 4.4 of the guide names chunk_state, state_passing and the chunk
+ * scan as the parts of mamba_chunk_scan_combined.  Read with the definitions
+ * of oracle_ssd_scan, over chunks of chunk_size tokens (the last one
+ * shorter); per (b, h) the scan over chunk c is an affine map of the state
+ * entering it, H_end = P_c H_start + E_c:
+ *   chunk_state:   E_c (the chunk run from a zero state) and P_c, which is
+ *                  exp(A[h] * sum of the chunk's steps), or 0 when the state
+ *                  restarts inside the chunk (seq_idx changes at one of its
+ *                  tokens, the first included, t > 0);
+ *   state_passing: S_0 = initial_states (zero when NULL),
+ *                  S_{c+1} = P_c S_c + E_c; carried[c] = S_c, final = S_nc;
+ *   chunk_scan:    out of every chunk from the recurrence started at
+ *                  carried[c], and the state after the last chunk.
+ * The three composed give oracle_ssd_scan.  Layouts: states and carried
+ * (nchunks, batch, nheads, headdim, dstate), decays (nchunks, batch,
+ * nheads), all double. */
+
+/* the step of token t of head h, and whether the state restarts before t */
+static double ssd_part_step(const void *dt, int io_dtype, int64_t b, int64_t t, int64_t seqlen,
+                            int64_t nheads, int64_t h, const float *dt_bias, int dt_softplus,
+                            int dt_limit, double dt_min, double dt_max) {
+    double v = load_io(dt, io_dtype, (b * seqlen + t) * nheads + h) + (dt_bias ? (double)dt_bias[h] : 0.0);
+    if (dt_softplus) v = oracle_softplus(v);
+    if (dt_limit) v = v < dt_min ? dt_min : (v > dt_max ? dt_max : v);
+    return v;
+}
+
+static int ssd_part_restarts(const int32_t *seq_idx, int64_t b, int64_t t, int64_t seqlen) {
+    return seq_idx && t > 0 && seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1];
+}
+
+/* Runs tokens [t0, t1) of (b, h) on the state St (headdim x dstate, in
+ * place), writing their outputs when out is given; returns the product of
+ * the decays seen since the last restart, or 0 after a restart. */
+static double ssd_part_run(int64_t b, int64_t h, int64_t t0, int64_t t1, int64_t seqlen,
+                           int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                           int io_dtype, const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D, int D_per_channel,
+                           const void *z, const float *dt_bias, int dt_softplus, int dt_limit,
+                           double dt_min, double dt_max, const int32_t *seq_idx, double *St,
+                           double *out) {
+    const int64_t g = h / (nheads / ngroups);
+    double reach = 1.0;
+    for (int64_t t = t0; t < t1; ++t) {
+        if (ssd_part_restarts(seq_idx, b, t, seqlen)) {
+            memset(St, 0, sizeof(double) * (size_t)(headdim * dstate));
+            reach = 0.0;
+        }
+        const double st = ssd_part_step(dt, io_dtype, b, t, seqlen, nheads, h, dt_bias, dt_softplus,
+                                        dt_limit, dt_min, dt_max);
+        const double decay = exp(st * (double)A[h]);
+        reach *= decay;
+        const int64_t brow = ((b * seqlen + t) * ngroups + g) * dstate;
+        const int64_t xrow = ((b * seqlen + t) * nheads + h) * headdim;
+        for (int64_t pp = 0; pp < headdim; ++pp) {
+            const double xv = load_io(x, io_dtype, xrow + pp);
+            double acc = 0.0;
+            for (int64_t s = 0; s < dstate; ++s) {
+                const double v = decay * St[pp * dstate + s] + st * xv * load_io(B, io_dtype, brow + s);
+                St[pp * dstate + s] = v;
+                if (out) acc += v * load_io(C, io_dtype, brow + s);
+            }
+            if (out) {
+                if (D) acc += xv * (double)(D_per_channel ? D[h * headdim + pp] : D[h]);
+                if (z) acc *= oracle_silu(load_io(z, io_dtype, xrow + pp));
+                out[xrow + pp] = acc;
+            }
+        }
+    }
+    return reach;
+}
+
+int oracle_ssd_chunk_state(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                           int64_t dstate, int64_t ngroups, int io_dtype, int64_t chunk_size,
+                           const void *x, const void *dt, const float *A, const void *B,
+                           const float *dt_bias, int dt_softplus, int dt_limit, double dt_min,
+                           double dt_max, const int32_t *seq_idx, double *states, double *decays) {
+    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        chunk_size <= 0 || nheads % ngroups != 0)
+        return 2;
+    if (!x || !dt || !A || !B || !states || !decays) return 1;
+    const int64_t nc = (seqlen + chunk_size - 1) / chunk_size, ps = headdim * dstate;
+    for (int64_t c = 0; c < nc; ++c)
+        for (int64_t bh = 0; bh < batch * nheads; ++bh) {
+            double *St = states + (c * batch * nheads + bh) * ps;
+            memset(St, 0, sizeof(double) * (size_t)ps);
+            const int64_t t0 = c * chunk_size, t1 = t0 + chunk_size < seqlen ? t0 + chunk_size : seqlen;
+            decays[c * batch * nheads + bh] =
+                ssd_part_run(bh / nheads, bh % nheads, t0, t1, seqlen, nheads, headdim, dstate, ngroups,
+                             io_dtype, x, dt, A, B, NULL, NULL, 0, NULL, dt_bias, dt_softplus, dt_limit,
+                             dt_min, dt_max, seq_idx, St, NULL);
+        }
+    return 0;
+}
+
+int oracle_ssd_state_passing(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim,
+                             int64_t dstate, const double *states, const double *decays,
+                             const double *initial_states, double *carried, double *final_states) {
+    if (nchunks <= 0 || batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0) return 2;
+    if (!states || !decays || !carried) return 1;
+    const int64_t ps = headdim * dstate, nbh = batch * nheads;
+    for (int64_t bh = 0; bh < nbh; ++bh)
+        for (int64_t i = 0; i < ps; ++i) {
+            double S = initial_states ? initial_states[bh * ps + i] : 0.0;
+            for (int64_t c = 0; c < nchunks; ++c) {
+                carried[(c * nbh + bh) * ps + i] = S;
+                S = decays[c * nbh + bh] * S + states[(c * nbh + bh) * ps + i];
+            }
+            if (final_states) final_states[bh * ps + i] = S;
+        }
+    return 0;
+}
+
+int oracle_ssd_chunk_scan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                          int64_t dstate, int64_t ngroups, int io_dtype, int64_t chunk_size,
+                          const void *x, const void *dt, const float *A, const void *B, const void *C,
+                          const float *D, int D_per_channel, const void *z, const float *dt_bias,
+                          int dt_softplus, int dt_limit, double dt_min, double dt_max,
+                          const int32_t *seq_idx, const double *carried, double *out,
+                          double *final_states) {
+    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        chunk_size <= 0 || nheads % ngroups != 0)
+        return 2;
+    if (!x || !dt || !A || !B || !C || !carried || !out) return 1;
+    const int64_t nc = (seqlen + chunk_size - 1) / chunk_size, ps = headdim * dstate;
+    double *St = (double *)malloc(sizeof(double) * (size_t)ps);
+    if (!St) return 5;
+    for (int64_t bh = 0; bh < batch * nheads; ++bh)
+        for (int64_t c = 0; c < nc; ++c) {
+            memcpy(St, carried + (c * batch * nheads + bh) * ps, sizeof(double) * (size_t)ps);
+            const int64_t t0 = c * chunk_size, t1 = t0 + chunk_size < seqlen ? t0 + chunk_size : seqlen;
+            ssd_part_run(bh / nheads, bh % nheads, t0, t1, seqlen, nheads, headdim, dstate, ngroups, io_dtype,
+                         x, dt, A, B, C, D, D_per_channel, z, dt_bias, dt_softplus, dt_limit, dt_min, dt_max,
+                         seq_idx, St, out);
+            if (final_states && c == nc - 1) memcpy(final_states + bh * ps, St, sizeof(double) * (size_t)ps);
+        }
+    free(St);
+    return 0;
+}
+
 /* Number of threads an OpenMP region would use (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -472,3 +472,66 @@ def test_complex_bwd_pins_catch_mutant(mutant, tmp_path):
     finally:
         orc.use_library(None)
     assert caught, f"no pin caught mutant {mutant}"
+
+
+# --------------------------------------------------------------------------
+# the split chunk-scan operators against their own pins
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_ssd_split_pins as sspins  # noqa: E402
+
+SSD_SPLIT_MUTANTS = {
+    "split_restart_not_zeroing_factor": ("            reach = 0.0;\n", ""),
+    "split_factor_skips_last_token": ("        reach *= decay;\n",
+                                      "        if (t + 1 < t1) reach *= decay;\n"),
+    "split_restart_ignores_first_token": ("if (ssd_part_restarts(seq_idx, b, t, seqlen)) {",
+                                          "if (t > t0 && ssd_part_restarts(seq_idx, b, t, seqlen)) {"),
+    "split_passing_state_after_update": (
+        "                carried[(c * nbh + bh) * ps + i] = S;\n"
+        "                S = decays[c * nbh + bh] * S + states[(c * nbh + bh) * ps + i];",
+        "                S = decays[c * nbh + bh] * S + states[(c * nbh + bh) * ps + i];\n"
+        "                carried[(c * nbh + bh) * ps + i] = S;"),
+    "split_passing_ignores_initial": ("double S = initial_states ? initial_states[bh * ps + i] : 0.0;",
+                                      "double S = 0.0;"),
+    "split_scan_from_wrong_chunk": ("memcpy(St, carried + (c * batch * nheads + bh) * ps",
+                                    "memcpy(St, carried + ((c > 0 ? c - 1 : 0) * batch * nheads + bh) * ps"),
+    "split_scan_last_chunk_short": ("t1 = t0 + chunk_size < seqlen ? t0 + chunk_size : seqlen;\n"
+                                    "            ssd_part_run(",
+                                    "t1 = t0 + chunk_size < seqlen ? t0 + chunk_size : seqlen - 1;\n"
+                                    "            ssd_part_run("),
+}
+
+
+def _ssd_split_pin_calls():
+    return [
+        ("compose_seq", lambda: sspins.test_composition_is_the_scan(4, "seq")),
+        ("compose_init", lambda: sspins.test_composition_is_the_scan(5, "init")),
+        ("compose_bf16", lambda: sspins.test_composition_is_the_scan(4, "bf16_all")),
+        ("chunk_alone", sspins.test_chunk_state_is_the_chunk_alone_from_zero),
+        ("factor_zero", sspins.test_chunk_state_factor_is_zero_where_a_sequence_starts),
+        ("affine", sspins.test_state_passing_is_affine),
+        ("true_boundaries", sspins.test_chunk_scan_from_the_true_boundary_states),
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(SSD_SPLIT_MUTANTS))
+def test_ssd_split_pins_catch_mutant(mutant, tmp_path):
+    src = open(orc.SRC).read()
+    old, new = SSD_SPLIT_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", lib,
+                    str(path), "-lm"], check=True, capture_output=True)
+    orc.use_library(lib)
+    caught = []
+    try:
+        for name, call in _ssd_split_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                caught.append(name)
+    finally:
+        orc.use_library(None)
+    assert caught, f"no pin caught mutant {mutant}"
