@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 12
+#define SSM_ABI_VERSION 13
 #define SSM_CKPT_INTERVAL 32  /* timesteps between saved states (checkpoints) */
 #define SSM_MAX_DSTATE 16   /* largest dstate the kernels are built for */
 #define SSM_CONV_WIDTH 4    /* the one conv width the kernels are built for */
@@ -517,6 +517,49 @@ int ssd_scan_validate(const ssd_scan_args_t *args);
  * sequence split).  Host-only apart from cached queries of the device's
  * compute-unit count and the kernels' occupancy. */
 int ssd_scan_workspace_size(const ssd_scan_args_t *args, size_t *bytes);
+
+/* The three parts of mamba_chunk_scan_combined as section 4.4 of the guide
+ * names them (chunk_state, state_passing, the chunk scan), over chunks of
+ * chunk_size tokens (a positive multiple of SSD_CHUNK; the last chunk may be
+ * shorter); nchunks = ceil(seqlen / chunk_size).  Per (b, h) the scan of
+ * chunk c maps the state entering it affinely, H_end = P_c H_start + E_c,
+ * and the three calls composed give ssd_scan_fwd's out and final_states:
+ *
+ *   ssd_chunk_state:   E_c, the chunk's end state from a zero state, into
+ *                      states (nchunks,b,h,p,n) fp32, and P_c into decays
+ *                      (nchunks,b,h) fp32: exp(A[h] * the chunk's summed
+ *                      steps), or 0 where seq_idx changes at one of the
+ *                      chunk's tokens (t > 0), the first included.  Reads
+ *                      x, dt, A, B, dt_bias, dt_softplus, dt_limit and
+ *                      seq_idx of args (C, D, z, out, the states, workspace
+ *                      and seq_segments are ignored and may be NULL).
+ *   ssd_state_passing: carried[c] = S_c with S_0 = initial_states (zero
+ *                      when NULL) and S_{c+1} = decays[c] S_c + states[c],
+ *                      each step one fp32 fma; final_states (b,h,p,n), if
+ *                      not NULL, gets S_nchunks.  Plain device arrays of
+ *                      the layouts above; carried (nchunks,b,h,p,n) fp32.
+ *   ssd_chunk_scan:    out of every chunk from the state carried[c] (the
+ *                      whole of args but initial_states, which carried[0]
+ *                      replaces, and workspace / seq_segments, which are
+ *                      ignored), and the state after the last chunk into
+ *                      final_states when given.
+ *
+ * Same supported sizes, alignment, conventions and status codes as
+ * ssd_scan_fwd; a chunk_size that is not a positive multiple of SSD_CHUNK
+ * returns SSM_ERR_UNSUPPORTED.  None of them needs scratch.  The *_validate
+ * calls are the host-only checks (no HIP call). */
+int ssd_chunk_state(const ssd_scan_args_t *args, int64_t chunk_size, float *states, float *decays,
+                    void *hip_stream);
+int ssd_chunk_state_validate(const ssd_scan_args_t *args, int64_t chunk_size, const float *states,
+                             const float *decays);
+int ssd_state_passing(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                      const float *states, const float *decays, const float *initial_states,
+                      float *carried, float *final_states, void *hip_stream);
+int ssd_state_passing_validate(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim,
+                               int64_t dstate, const float *states, const float *decays,
+                               const float *carried);
+int ssd_chunk_scan(const ssd_scan_args_t *args, int64_t chunk_size, const float *carried, void *hip_stream);
+int ssd_chunk_scan_validate(const ssd_scan_args_t *args, int64_t chunk_size, const float *carried);
 
 /* Static text for a status code. */
 const char *ssm_status_str(int status);

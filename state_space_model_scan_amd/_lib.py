@@ -27,6 +27,8 @@ EXPORTS = (
     "ssm_state_update", "ssm_state_update_validate",
     "causal_conv1d_update", "causal_conv1d_update_validate",
     "ssd_scan_fwd", "ssd_scan_validate", "ssd_scan_workspace_size",
+    "ssd_chunk_state", "ssd_chunk_state_validate", "ssd_state_passing", "ssd_state_passing_validate",
+    "ssd_chunk_scan", "ssd_chunk_scan_validate",
     "ssm_scan_bwd", "ssm_scan_bwd_validate", "ssm_scan_bwd_workspace_size",
     "ssm_scan_bwd_complex", "ssm_scan_bwd_complex_validate", "ssm_scan_bwd_complex_workspace_size",
     "ssm_status_str", "ssm_last_hip_error", "ssm_abi_version",
@@ -175,6 +177,19 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_validate.restype = ctypes.c_int
         L.ssd_scan_workspace_size.argtypes = [ctypes.POINTER(SsdArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_workspace_size.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.ssd_chunk_state.argtypes = [ctypes.POINTER(SsdArgs), i64, _vp, _vp, _vp]
+        L.ssd_chunk_state.restype = ctypes.c_int
+        L.ssd_chunk_state_validate.argtypes = [ctypes.POINTER(SsdArgs), i64, _vp, _vp]
+        L.ssd_chunk_state_validate.restype = ctypes.c_int
+        L.ssd_state_passing.argtypes = [i64, i64, i64, i64, i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.ssd_state_passing.restype = ctypes.c_int
+        L.ssd_state_passing_validate.argtypes = [i64, i64, i64, i64, i64, _vp, _vp, _vp]
+        L.ssd_state_passing_validate.restype = ctypes.c_int
+        L.ssd_chunk_scan.argtypes = [ctypes.POINTER(SsdArgs), i64, _vp, _vp]
+        L.ssd_chunk_scan.restype = ctypes.c_int
+        L.ssd_chunk_scan_validate.argtypes = [ctypes.POINTER(SsdArgs), i64, _vp]
+        L.ssd_chunk_scan_validate.restype = ctypes.c_int
         L.causal_conv1d_fwd_ex.argtypes = [ctypes.POINTER(ConvArgs), _vp]
         L.causal_conv1d_fwd_ex.restype = ctypes.c_int
         L.causal_conv1d_ex_validate.argtypes = [ctypes.POINTER(ConvArgs)]

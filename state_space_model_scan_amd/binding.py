@@ -755,7 +755,7 @@ def causal_conv1d_update(x: torch.Tensor, conv_state: torch.Tensor, weight: torc
 # ---------------------------------------------------------------------------
 
 def _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, initial_states, out, final_states, seq_idx,
-              dt_limit, workspace, seq_segments):
+              dt_limit, workspace, seq_segments, need_out=True):
     """ssd_scan_args_t for the tensors (checked; made contiguous where
     needed); returns (args, out, tensors kept alive until the call)."""
     x, dt, B, C = _dense(x), _dense(dt), _dense(B), _dense(C)
@@ -790,7 +790,7 @@ def _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, initial_states, out, f
     if workspace is not None:
         _workspace_spec(workspace, dev)
     _on_gpu(dev)
-    if out is None:
+    if out is None and need_out:
         out = torch.empty_like(x)
     a = _lib.SsdArgs()
     a.batch, a.seqlen, a.nheads, a.headdim = batch, seqlen, nheads, headdim
@@ -838,6 +838,85 @@ def ssd_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Te
     if workspace is not None:
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     check(L.ssd_scan_fwd(ctypes.byref(a), _stream(dev, stream)))
+    return out
+
+
+def _nchunks(seqlen: int, chunk_size: int) -> int:
+    if chunk_size <= 0 or chunk_size % _lib.SSD_CHUNK != 0:
+        raise ValueError(f"chunk_size must be a positive multiple of {_lib.SSD_CHUNK}, got {chunk_size}")
+    return -(-seqlen // chunk_size)
+
+
+def ssd_chunk_state(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, chunk_size: int,
+                    dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = False,
+                    seq_idx: Optional[torch.Tensor] = None, dt_limit: Optional[Tuple[float, float]] = None,
+                    states: Optional[torch.Tensor] = None, decays: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue ssd_chunk_state: per chunk of ``chunk_size`` tokens its end
+    state from zero, ``states`` (nchunks, batch, nheads, headdim, dstate)
+    float32, and the factor of the state entering it, ``decays`` (nchunks,
+    batch, nheads) float32.  Inputs as ``ssd_scan_fwd``."""
+    a, _, keep = _ssd_args(x, dt, A, B, None, None, None, dt_bias, dt_softplus, None, None, None, seq_idx,
+                           dt_limit, None, 0, need_out=False)
+    batch, seqlen, nheads, headdim = x.shape
+    dstate = B.shape[3]
+    nc = _nchunks(seqlen, chunk_size)
+    dev, f32 = x.device, torch.float32
+    _out_spec(states, "states", (nc, batch, nheads, headdim, dstate), f32, dev)
+    _out_spec(decays, "decays", (nc, batch, nheads), f32, dev)
+    if states is None:
+        states = torch.empty((nc, batch, nheads, headdim, dstate), dtype=f32, device=dev)
+    if decays is None:
+        decays = torch.empty((nc, batch, nheads), dtype=f32, device=dev)
+    check(_lib.lib().ssd_chunk_state(ctypes.byref(a), chunk_size, _ptr(states), _ptr(decays),
+                                     _stream(dev, stream)))
+    return states, decays
+
+
+def ssd_state_passing(states: torch.Tensor, decays: torch.Tensor, initial_states: Optional[torch.Tensor] = None,
+                      carried: Optional[torch.Tensor] = None, final_states: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Enqueue ssd_state_passing: ``carried`` (the state entering every
+    chunk, the shape of ``states``) and ``final_states`` (batch, nheads,
+    headdim, dstate), both float32."""
+    states, decays, initial_states = _dense(states), _dense(decays), _dense(initial_states)
+    if states.dim() != 5:
+        raise ValueError("states must be (nchunks, batch, nheads, headdim, dstate)")
+    nc, batch, nheads, headdim, dstate = states.shape
+    dev, f32 = states.device, torch.float32
+    _spec(states, "states", states.shape, f32, dev)
+    _spec(decays, "decays", (nc, batch, nheads), f32, dev)
+    _spec(initial_states, "initial_states", (batch, nheads, headdim, dstate), f32, dev)
+    _out_spec(carried, "carried", states.shape, f32, dev)
+    _out_spec(final_states, "final_states", (batch, nheads, headdim, dstate), f32, dev)
+    _on_gpu(dev)
+    if carried is None:
+        carried = torch.empty_like(states)
+    if final_states is None:
+        final_states = torch.empty((batch, nheads, headdim, dstate), dtype=f32, device=dev)
+    check(_lib.lib().ssd_state_passing(nc, batch, nheads, headdim, dstate, _ptr(states), _ptr(decays),
+                                       _ptr(initial_states), _ptr(carried), _ptr(final_states),
+                                       _stream(dev, stream)))
+    return carried, final_states
+
+
+def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                   carried: torch.Tensor, chunk_size: int, D: Optional[torch.Tensor] = None,
+                   z: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                   dt_softplus: bool = False, seq_idx: Optional[torch.Tensor] = None,
+                   dt_limit: Optional[Tuple[float, float]] = None, out: Optional[torch.Tensor] = None,
+                   final_states: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Enqueue ssd_chunk_scan: every chunk's outputs from ``carried``
+    (nchunks, batch, nheads, headdim, dstate) float32; returns ``out``.  The
+    state after the last chunk goes to ``final_states`` when given."""
+    a, out, keep = _ssd_args(x, dt, A, B, C, D, z, dt_bias, dt_softplus, None, out, final_states, seq_idx,
+                             dt_limit, None, 0)
+    batch, seqlen, nheads, headdim = x.shape
+    dstate = B.shape[3]
+    nc = _nchunks(seqlen, chunk_size)
+    carried = _dense(carried)
+    _spec(carried, "carried", (nc, batch, nheads, headdim, dstate), torch.float32, x.device)
+    check(_lib.lib().ssd_chunk_scan(ctypes.byref(a), chunk_size, _ptr(carried), _stream(x.device, stream)))
     return out
 
 

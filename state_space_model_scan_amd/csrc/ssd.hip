@@ -58,6 +58,7 @@ struct SsdParams {
   uint16_t *out;
   float *fin;
   float *ws_state, *ws_decay;   // sequence split: end states from zero, total decays
+  const float *carried;         // chunk scan: the state entering every segment (no fold)
   int64_t seqlen, nheads, ngroups, seg_chunks;
   int D_per_channel, softplus, dt_limit, nseg;
   float dt_min, dt_max;
@@ -165,16 +166,20 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   //   S_in(k) = E_{k-1} + P_{k-1} (E_{k-2} + P_{k-2} (... + P_0 S_init))
   // with E_j segment j's end state from zero and P_j its total decay (zero
   // where a sequence starts inside it).
+  // With carried states given (the chunk scan on its own) segment k starts
+  // from carried[k] as it is.
   f32x4 accs[NT];
   const int srow = (16 * w + r) * N + 4 * kq;   // this lane's first state element in a (p, n) block
+  const float *start = p.carried ? p.carried + seg * BH * kP * N : p.init;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      accs[nt][i] = (FULL && p.init) ? p.init[bh * kP * N + srow + 16 * nt + i] : 0.0f;
+      accs[nt][i] = (FULL && start) ? start[bh * kP * N + srow + 16 * nt + i] : 0.0f;
   }
   if constexpr (FULL) {
-    for (int j = 0; j < seg; ++j) {
+    const int nfold = p.carried ? 0 : seg;
+    for (int j = 0; j < nfold; ++j) {
       const float P = p.ws_decay[j * BH + bh];
       const float *E = p.ws_state + (j * BH + bh) * kP * N + srow;
 #pragma unroll
@@ -484,6 +489,23 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   }
 }
 
+// state_passing: one thread per state element of a (batch, head), the chunks
+// in order; S <- P S + E is one fp32 fma, as the fold in the full pass.
+__global__ void __launch_bounds__(256) ssd_state_passing_kernel(const float *states, const float *decays,
+                                                                const float *init, float *carried,
+                                                                float *fin, int64_t nchunks, int64_t nbh,
+                                                                int64_t ps) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nbh * ps) return;
+  const int64_t bh = i / ps;
+  float S = init ? init[i] : 0.0f;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    carried[c * nbh * ps + i] = S;
+    S = fmaf(decays[c * nbh + bh], S, states[c * nbh * ps + i]);
+  }
+  if (fin) fin[i] = S;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -559,11 +581,10 @@ extern "C" int ssd_scan_workspace_size(const ssd_scan_args_t *a, size_t *bytes) 
   return SSM_OK;
 }
 
-extern "C" int ssd_scan_fwd(const ssd_scan_args_t *a, void *stream_ptr) {
-  const int st = ssd_scan_validate(a);
-  if (st != SSM_OK) return st;
-  const SsdPlan pl = ssd_plan(a, cu_count_cached());
-  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
+namespace {
+
+// the kernel parameters every launch shares
+SsdParams ssd_params(const ssd_scan_args_t *a) {
   SsdParams p{};
   p.x = static_cast<const uint16_t *>(a->x);
   p.dt = static_cast<const uint16_t *>(a->dt);
@@ -578,6 +599,72 @@ extern "C" int ssd_scan_fwd(const ssd_scan_args_t *a, void *stream_ptr) {
   p.D_per_channel = a->D_per_channel;
   p.softplus = a->dt_softplus;
   p.dt_limit = a->dt_limit; p.dt_min = a->dt_min; p.dt_max = a->dt_max;
+  return p;
+}
+
+}  // namespace
+
+extern "C" int ssd_chunk_state(const ssd_scan_args_t *a, int64_t chunk_size, float *states, float *decays,
+                               void *stream_ptr) {
+  const int st = ssd_chunk_state_validate(a, chunk_size, states, decays);
+  if (st != SSM_OK) return st;
+  const int64_t nchunks = (a->seqlen + chunk_size - 1) / chunk_size;
+  const int64_t blocks = a->batch * a->nheads;
+  if (blocks > 0x7fffffffLL || nchunks > 65535) return SSM_ERR_SHAPE;
+  SsdParams p = ssd_params(a);
+  p.C = nullptr; p.z = nullptr; p.D = nullptr; p.init = nullptr; p.out = nullptr; p.fin = nullptr;
+  p.nseg = static_cast<int>(nchunks);
+  p.seg_chunks = chunk_size / kQ;
+  p.ws_state = states;
+  p.ws_decay = decays;
+  hipLaunchKernelGGL(ssd_fn(a->dstate, SSD_STATE, a->seq_idx != nullptr),
+                     dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(nchunks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream_ptr), p);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SSM_OK : hip_fail(e);
+}
+
+extern "C" int ssd_state_passing(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim,
+                                 int64_t dstate, const float *states, const float *decays,
+                                 const float *initial_states, float *carried, float *final_states,
+                                 void *stream_ptr) {
+  const int st = ssd_state_passing_validate(nchunks, batch, nheads, headdim, dstate, states, decays, carried);
+  if (st != SSM_OK) return st;
+  const int64_t nbh = batch * nheads, ps = headdim * dstate;
+  const int64_t blocks = (nbh * ps + 255) / 256;
+  if (blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  hipLaunchKernelGGL(ssd_state_passing_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream_ptr), states, decays, initial_states, carried,
+                     final_states, nchunks, nbh, ps);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SSM_OK : hip_fail(e);
+}
+
+extern "C" int ssd_chunk_scan(const ssd_scan_args_t *a, int64_t chunk_size, const float *carried,
+                              void *stream_ptr) {
+  const int st = ssd_chunk_scan_validate(a, chunk_size, carried);
+  if (st != SSM_OK) return st;
+  const int64_t nchunks = (a->seqlen + chunk_size - 1) / chunk_size;
+  const int64_t blocks = a->batch * a->nheads;
+  if (blocks > 0x7fffffffLL || nchunks > 65535) return SSM_ERR_SHAPE;
+  SsdParams p = ssd_params(a);
+  p.init = nullptr;
+  p.carried = carried;
+  p.nseg = static_cast<int>(nchunks);
+  p.seg_chunks = chunk_size / kQ;
+  hipLaunchKernelGGL(ssd_fn(a->dstate, SSD_FULL, a->seq_idx != nullptr),
+                     dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(nchunks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream_ptr), p);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SSM_OK : hip_fail(e);
+}
+
+extern "C" int ssd_scan_fwd(const ssd_scan_args_t *a, void *stream_ptr) {
+  const int st = ssd_scan_validate(a);
+  if (st != SSM_OK) return st;
+  const SsdPlan pl = ssd_plan(a, cu_count_cached());
+  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes)) return SSM_ERR_WORKSPACE;
+  SsdParams p = ssd_params(a);
   p.nseg = pl.nseg; p.seg_chunks = pl.seg_chunks;
   if (pl.nseg > 1) {
     char *ws = static_cast<char *>(a->workspace);

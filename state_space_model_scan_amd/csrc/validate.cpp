@@ -183,6 +183,62 @@ extern "C" int ssd_scan_validate(const ssd_scan_args_t *a) {
   return SSM_OK;
 }
 
+// the checks of ssd_scan_validate that the split operators share: sizes,
+// dtypes, enum values, and x / dt / A / B present and aligned
+static int ssd_common_validate(const ssd_scan_args_t *a, int64_t chunk_size) {
+  if (!a) return SSM_ERR_NULL;
+  if (!positive(a->batch) || !positive(a->seqlen) || !positive(a->nheads) ||
+      !positive(a->headdim) || !positive(a->dstate) || !positive(a->ngroups))
+    return SSM_ERR_SHAPE;
+  if (a->nheads % a->ngroups != 0) return SSM_ERR_SHAPE;
+  if (!product_fits(a->batch * a->seqlen, a->nheads, a->headdim) ||
+      !product_fits(a->batch * a->seqlen, a->ngroups, a->dstate) ||
+      !product_fits(a->batch, a->nheads, a->headdim * a->dstate))
+    return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (a->headdim != SSD_HEADDIM) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate != 32 && a->dstate != 64 && a->dstate != 128) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_softplus != 0 && a->dt_softplus != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_limit != 0 && a->dt_limit != 1) return SSM_ERR_UNSUPPORTED;
+  if (a->dt_limit && !(a->dt_min <= a->dt_max)) return SSM_ERR_SHAPE;
+  if (chunk_size <= 0 || chunk_size % SSD_CHUNK != 0) return SSM_ERR_UNSUPPORTED;
+  if (!a->x || !a->dt || !a->A || !a->B) return SSM_ERR_NULL;
+  const int64_t nchunks = (a->seqlen + chunk_size - 1) / chunk_size;
+  if (!product_fits(nchunks, a->batch * a->nheads, a->headdim * a->dstate)) return SSM_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->B)) & 15u) return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
+extern "C" int ssd_chunk_state_validate(const ssd_scan_args_t *a, int64_t chunk_size, const float *states,
+                                        const float *decays) {
+  const int st = ssd_common_validate(a, chunk_size);
+  if (st != SSM_OK) return st;
+  if (!states || !decays) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
+extern "C" int ssd_chunk_scan_validate(const ssd_scan_args_t *a, int64_t chunk_size, const float *carried) {
+  const int st = ssd_common_validate(a, chunk_size);
+  if (st != SSM_OK) return st;
+  if (a->D_per_channel != 0 && a->D_per_channel != 1) return SSM_ERR_UNSUPPORTED;
+  if (!a->C || !a->out || !carried) return SSM_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(a->C) | reinterpret_cast<uintptr_t>(a->out) |
+       reinterpret_cast<uintptr_t>(a->z)) & 15u)
+    return SSM_ERR_UNSUPPORTED;
+  return SSM_OK;
+}
+
+extern "C" int ssd_state_passing_validate(int64_t nchunks, int64_t batch, int64_t nheads, int64_t headdim,
+                                          int64_t dstate, const float *states, const float *decays,
+                                          const float *carried) {
+  if (!positive(nchunks) || !positive(batch) || !positive(nheads) || !positive(headdim) || !positive(dstate))
+    return SSM_ERR_SHAPE;
+  if (!product_fits(nchunks, batch * nheads, headdim * dstate) || !product_fits(batch, nheads, headdim * dstate))
+    return SSM_ERR_SHAPE;
+  if (!states || !decays || !carried) return SSM_ERR_NULL;
+  return SSM_OK;
+}
+
 extern "C" const char *ssm_status_str(int status) {
   switch (status) {
     case SSM_OK: return "ok";

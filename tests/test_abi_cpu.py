@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     assert set(funcs) == set(_lib.EXPORTS), funcs
     for name in funcs:
         assert hasattr(L, name), f"{name} not exported"
-    assert L.ssm_abi_version() == 12
+    assert L.ssm_abi_version() == 13
 
 
 def test_status_strings():
@@ -301,6 +301,42 @@ def test_ssd_split_needs_workspace_before_any_launch():
     few = _good_ssd(seqlen=100, seq_segments=9)
     assert L.ssd_scan_workspace_size(ctypes.byref(few), ctypes.byref(need)) == _lib.SSM_OK
     assert need.value >= 1 * 2 * 8 * 64 * 128 * 4
+
+
+def test_ssd_split_operator_validation():
+    """ssd_chunk_state / ssd_state_passing / ssd_chunk_scan reject bad
+    arguments before any launch (the device pointers are never touched)."""
+    L = _lib.lib()
+    st, dc, car = 0x6000, 0x7000, 0x8000
+    cs = lambda a, k=128, s=st, d=dc: L.ssd_chunk_state_validate(ctypes.byref(a), k, s, d)  # noqa: E731
+    sc = lambda a, k=128, c=car: L.ssd_chunk_scan_validate(ctypes.byref(a), k, c)             # noqa: E731
+    assert cs(_good_ssd()) == _lib.SSM_OK
+    assert sc(_good_ssd()) == _lib.SSM_OK
+    # chunk_state reads neither C nor out
+    assert cs(_good_ssd(C=None, out=None)) == _lib.SSM_OK
+    assert sc(_good_ssd(C=None)) == _lib.SSM_ERR_NULL
+    assert sc(_good_ssd(out=None)) == _lib.SSM_ERR_NULL
+    for k in (0, -64, 32, 100):
+        assert cs(_good_ssd(), k) == _lib.SSM_ERR_UNSUPPORTED, k
+        assert sc(_good_ssd(), k) == _lib.SSM_ERR_UNSUPPORTED, k
+    assert cs(_good_ssd(), 64, s=None) == _lib.SSM_ERR_NULL
+    assert cs(_good_ssd(), 64, d=None) == _lib.SSM_ERR_NULL
+    assert sc(_good_ssd(), 64, c=None) == _lib.SSM_ERR_NULL
+    for kw in (dict(io_dtype=_lib.SSM_F32), dict(headdim=32), dict(dstate=96), dict(x=0x1002)):
+        assert cs(_good_ssd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
+        assert sc(_good_ssd(**kw)) == _lib.SSM_ERR_UNSUPPORTED, kw
+    assert sc(_good_ssd(z=0x1008)) == _lib.SSM_ERR_UNSUPPORTED
+    assert cs(_good_ssd(ngroups=3)) == _lib.SSM_ERR_SHAPE
+    assert cs(_good_ssd(dt_limit=1, dt_min=0.2, dt_max=0.1)) == _lib.SSM_ERR_SHAPE
+    assert L.ssd_chunk_state(ctypes.byref(_good_ssd(B=None)), 64, st, dc, None) == _lib.SSM_ERR_NULL
+    assert L.ssd_chunk_scan(ctypes.byref(_good_ssd()), 96, car, None) == _lib.SSM_ERR_UNSUPPORTED
+    sp = L.ssd_state_passing_validate
+    assert sp(4, 2, 8, 64, 128, st, dc, car) == _lib.SSM_OK
+    assert sp(0, 2, 8, 64, 128, st, dc, car) == _lib.SSM_ERR_SHAPE
+    assert sp(4, 2, -8, 64, 128, st, dc, car) == _lib.SSM_ERR_SHAPE
+    for args in ((None, dc, car), (st, None, car), (st, dc, None)):
+        assert sp(4, 2, 8, 64, 128, *args) == _lib.SSM_ERR_NULL
+    assert L.ssd_state_passing(4, 2, 8, 64, 128, st, dc, None, None, None, None) == _lib.SSM_ERR_NULL
 
 
 def _good_bwd(**kw):

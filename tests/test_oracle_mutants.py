@@ -163,7 +163,8 @@ SSD_MUTANTS = {
         "                            *hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;"),
     "ssd_drop_dt_in_input": ("*hs = dA * *hs + step * load_io(B, io_dtype, bcb + s) * xv;",
                              "*hs = dA * *hs + load_io(B, io_dtype, bcb + s) * xv;"),
-    "ssd_D_channel_index": ("D[h * headdim + pp]", "D[pp % nheads * headdim + h % headdim]"),
+    "ssd_D_channel_index": ("y += (double)(D_per_channel ? D[h * headdim + pp]",
+                            "y += (double)(D_per_channel ? D[pp % nheads * headdim + h % headdim]"),
     "ssd_ignore_initial": ("H[i] = initial_states ? initial_states[sbase + i] : 0.0;", "H[i] = 0.0;"),
     "ssd_limit_swapped": ("step = step < dt_min ? dt_min : (step > dt_max ? dt_max : step);",
                           "step = step < dt_max ? dt_max : (step > dt_min ? dt_min : step);"),
