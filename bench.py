@@ -252,6 +252,10 @@ def main():
                     help="time the standalone causal_conv1d_fwd on the conv workload's input")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (all gradients) on the selective-scan workload")
+    ap.add_argument("--split", action="store_true",
+                    help="Mamba-2 workload: time ssd_chunk_state, ssd_state_passing and ssd_chunk_scan in turn")
+    ap.add_argument("--chunk-size", type=int, default=256,
+                    help="chunk size of --split (a multiple of 64; 256 is the usual Mamba-2 value)")
     ap.add_argument("--microbench", action="store_true",
                     help="measure the VALU, transcendental, LDS and copy rates the ALU ceilings use")
     args = ap.parse_args()
@@ -791,6 +795,24 @@ def ssd_main(args):
         binding.ssd_scan_fwd(x, dt, A, B, C, D, z, bias, w.softplus, initial_states=init, out=out,
                              final_states=fin, workspace=ws)
 
+    split_bytes = 0
+    if args.split:
+        # the three operators in turn, into preallocated states / carried
+        # states; their extra traffic is the fp32 chunk states written by
+        # chunk_state, read and carried by state_passing, read by chunk_scan
+        nc = -(-w.seqlen // args.chunk_size)
+        states = torch.empty((nc, w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+        decays = torch.empty((nc, w.batch, w.nheads), dtype=torch.float32, device="cuda")
+        carried = torch.empty_like(states)
+        fin_pass = torch.empty_like(fin)
+        split_bytes = 4 * states.numel() * 4 + 2 * decays.numel() * 4
+
+        def step():   # noqa: F811
+            binding.ssd_chunk_state(x, dt, A, B, args.chunk_size, bias, w.softplus, states=states, decays=decays)
+            binding.ssd_state_passing(states, decays, init, carried=carried, final_states=fin_pass)
+            binding.ssd_chunk_scan(x, dt, A, B, C, carried, args.chunk_size, D, z, bias, w.softplus, out=out,
+                                   final_states=fin)
+
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -816,6 +838,12 @@ def ssd_main(args):
     nbytes = ssd_bytes(w) + w.batch * w.nheads * w.headdim * w.dstate * 4   # + final states
     gbs = nbytes / k_s / 1e9
     tflops = ssd_flops(w) / k_s / 1e12
+    if args.split:
+        kernel = (f"ssd_chunk_state + ssd_state_passing + ssd_chunk_scan at chunk {args.chunk_size} (the step's "
+                  f"events bracket the three; the chunk states add {split_bytes / 1e6:.0f} MB of traffic beyond "
+                  f"the algorithmic bytes)")
+    else:
+        kernel = "ssd_kernel (state pass + full pass)" if need else "ssd_kernel"
     rec = {
         "metric": "Mamba-2 chunked scan elements/s (b·l·h·p)",
         "value": w.elements * args.steps / wall,
@@ -831,7 +859,8 @@ def ssd_main(args):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: b={w.batch} l={w.seqlen} h={w.nheads} p={w.headdim} n={w.dstate} "
-                        f"g={w.ngroups}, bf16 io, fp32 state, chunk 64",
+                        f"g={w.ngroups}, bf16 io, fp32 state, chunk 64"
+                        + (f", split operators at chunk_size {args.chunk_size}" if args.split else ""),
             "elements_per_step": w.elements,
         },
         "roofline": {
@@ -840,9 +869,9 @@ def ssd_main(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
-            "traffic": load_traffic(w.name, SSD_SRCS),
-            "kernel": "ssd_kernel (state pass + full pass)" if need else "ssd_kernel",
-            "workspace_bytes": need,
+            "traffic": None if args.split else load_traffic(w.name, SSD_SRCS),
+            "kernel": kernel,
+            "workspace_bytes": 0 if args.split else need,
             "kernel_avg_ms": k_s * 1e3,
             "kernel_median_ms": float(np.median(ms)),
             "algorithmic_bytes": nbytes,
