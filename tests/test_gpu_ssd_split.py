@@ -200,3 +200,31 @@ def test_full_size_composition():
     ef = max_err(_np(fin)[:, heads], rf)
     log(f"[ssd-split]   chunk 256: out {eo:.2e} final {ef:.2e}")
     assert eo <= TOL[BF16] and ef <= STATE_TOL, (eo, ef)
+
+
+@pytest.mark.parametrize("seqlen,chunk", [(1, 64), (64, 64), (65, 64), (129, 256), (256, 128)])
+def test_split_edges(seqlen, chunk):
+    """One token, whole and ragged last chunks, a single chunk longer than
+    the sequence, no initial state: each operator against the oracle and the
+    composition against ssd_scan_fwd with the matching segments."""
+    import torch
+    from state_space_model_scan_amd import binding
+    w, t = _case(n=32, seqlen=seqlen, init=False, seed=720 + seqlen + chunk)
+    log(f"[ssd-split] edge l={seqlen} chunk={chunk}")
+    d = _dev(t, None)
+    st, dc = binding.ssd_chunk_state(d["x"], d["dt"], d["A"], d["B"], chunk, d["dt_bias"], w.softplus)
+    torch.cuda.synchronize()
+    rs, rd = orc.ssd_chunk_state(t["x"], t["dt"], t["A"], t["B"], chunk, t["dt_bias"], w.softplus, io_dtype=BF16)
+    assert st.shape[0] == rs.shape[0] == -(-seqlen // chunk)
+    assert max_err(_np(st), rs) <= STATE_TOL and max_err(_np(dc), rd) <= EXACT_TOL
+    out, fin, fin2 = _composed(w, d, chunk, None, None)
+    ref_fin = torch.empty_like(fin)
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
+    nseg = -(-seqlen // chunk)
+    ref = binding.ssd_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], d["dt_bias"], w.softplus,
+                               final_states=ref_fin, workspace=ws, seq_segments=nseg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(fin2, ref_fin)
+    ro, rf = orc.ssd_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["z"], t["dt_bias"], w.softplus,
+                          io_dtype=BF16)
+    assert max_err(_np(out), ro) <= TOL[BF16] and max_err(_np(fin), rf) <= STATE_TOL
