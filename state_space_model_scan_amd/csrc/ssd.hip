@@ -81,6 +81,18 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * ROW_LEN + (col ^ (gsw << 3));
 }
 
+// element offset of (row, col) in a row-major LDS matrix of ROW_LEN bf16
+// whose rows are read in 8-byte pieces: the row's 8-byte pieces are permuted
+// by the row (mod 16), so 16 consecutive rows read at one column land on
+// different banks (measured: permuting 16-byte groups instead left these
+// reads with as many bank conflicts as no permutation)
+template <int ROW_LEN>
+__device__ __forceinline__ int swz8(int row, int col) {
+  constexpr int PIECES = ROW_LEN / 4;
+  constexpr int MASK = PIECES > 16 ? 15 : PIECES - 1;
+  return row * ROW_LEN + (col ^ ((row & MASK) << 2));
+}
+
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float v) {
   const __bf16 h = static_cast<__bf16>(v);
@@ -113,9 +125,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   constexpr int NT = N / 16;   // state tiles along dstate
   __shared__ __attribute__((aligned(16))) uint16_t sXT[kP * kQ];   // X^T   [p][t]
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * kQ];    // B^T   [n][t]
-  // M [t][tau] and the state [p][n] as hi / lo bf16 (full pass only)
+  // M [t][tau] as hi / lo bf16, and the chunk's C [t][n] (full pass only)
   __shared__ __attribute__((aligned(16))) uint16_t sM[FULL ? 2 : 1][FULL ? kQ * kQ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sS[FULL ? 2 : 1][FULL ? kP * N : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sC[FULL ? kQ * N : 8];
   __shared__ __attribute__((aligned(16))) float sCs[kQ], sDt[kQ], sW[kQ];
   __shared__ __attribute__((aligned(16))) int32_t sSid[SEQ ? kQ : 4];
 
@@ -192,18 +204,6 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       }
     }
   }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int pp = 16 * w + r;
-    if constexpr (FULL) {
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
-      const int o = swz<N>(pp, 16 * nt + 4 * kq);
-      *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-    }
-  }
   __syncthreads();
 
   // sequence id the incoming state belongs to: the token before the segment
@@ -275,6 +275,16 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       if constexpr (FULL) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) *reinterpret_cast<uint4 *>(&sBr[swz<N>(t + k, n0)]) = br[j][k];
+      }
+    }
+    if constexpr (FULL) {
+      // this wave's C rows (tokens 16w + r) for every wave's C S^T products
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) {
+        const uint4 cw = __builtin_bit_cast(uint4, cop[kk]);
+        const int rr = 16 * w + r;
+        *reinterpret_cast<uint2 *>(&sC[swz8<N>(rr, 32 * kk + 8 * kq)]) = make_uint2(cw.x, cw.y);
+        *reinterpret_cast<uint2 *>(&sC[swz8<N>(rr, 32 * kk + 8 * kq + 4)]) = make_uint2(cw.z, cw.w);
       }
     }
     // ---- the steps and their running sum inside the chunk (padding: dt' = 0)
@@ -358,51 +368,64 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       }
       __syncthreads();
 
-      // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T: lane holds Y[t = 16w + r][p = 16 pb + 4kq + i]
-      // (k-step outer, channel block inner: consecutive products feed four
-      // independent accumulators and a step's operand reads issue together)
+      // ---- Y^T = S C^T diag(exp(cs)) + X^T M^T for this wave's channels and
+      // every token: lane holds Y[t = 16 tb + r][p = 16w + 4kq + i].
+      // The state operand comes from this lane's own accumulators,
+      // S[p = 16w + r][n = 16 nt + 4kq + i]: the k index of each product runs
+      // over the 32 states 32kk + 16a + 4kq + j (a < 2, j < 4) in that order
+      // for both operands, a permutation of the states that leaves the sum
+      // unchanged; C's are the matching 8-byte pieces of its LDS rows.
       f32x4 accy[4];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) accy[pb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tb = 0; tb < 4; ++tb) accy[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
-        bf16x8 shi[4], slo[4];
+        bf16x8 shi, slo;
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const int o = swz<N>(16 * pb + r, 32 * kk + 8 * kq);
-          shi[pb] = ld8(&sS[0][o]);
-          slo[pb] = ld8(&sS[1][o]);
+        for (int i = 0; i < 8; ++i) {
+          const float v = accs[2 * kk + i / 4][i % 4];
+          const __bf16 hb = static_cast<__bf16>(v);
+          shi[i] = hb;
+          slo[i] = static_cast<__bf16>(v - static_cast<float>(hb));
         }
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(shi[pb], cop[kk], accy[pb]);
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) accy[pb] = mfma(slo[pb], cop[kk], accy[pb]);
+        for (int tb = 0; tb < 4; ++tb) {
+          const int row = 16 * tb + r;
+          const uint2 c0 = *reinterpret_cast<const uint2 *>(&sC[swz8<N>(row, 32 * kk + 4 * kq)]);
+          const uint2 c1 = *reinterpret_cast<const uint2 *>(&sC[swz8<N>(row, 32 * kk + 16 + 4 * kq)]);
+          const bf16x8 cop8 = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
+          accy[tb] = mfma(shi, cop8, accy[tb]);
+          accy[tb] = mfma(slo, cop8, accy[tb]);
+        }
       }
-      {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
         // the incoming state reaches token t only inside its own sequence
-        const float e = (!SEQ || sidt == sid_prev) ? fast_exp2(cst * kLog2e) : 0.0f;
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) accy[pb] *= e;
+        const int tt = 16 * tb + r;
+        const float e = (!SEQ || sSid[SEQ ? tt : 0] == sid_prev) ? fast_exp2(sCs[tt] * kLog2e) : 0.0f;
+        accy[tb] *= e;
       }
-      const int kkmax = (16 * (w + 1) + 31) / 32;   // tau blocks at or before this wave's tokens
-      for (int kk = 0; kk < kkmax; ++kk) {
-        const int o = swz<kQ>(16 * w + r, 32 * kk + 8 * kq);
-        const bf16x8 mhi = ld8(&sM[0][o]), mlo = ld8(&sM[1][o]);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const bf16x8 xop = ld8(&sXT[swz<kQ>(16 * pb + r, 32 * kk + 8 * kq)]);
-          accy[pb] = mfma(xop, mhi, accy[pb]);
-          accy[pb] = mfma(xop, mlo, accy[pb]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 xop = ld8(&sXT[swz<kQ>(16 * w + r, 32 * kk + 8 * kq)]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          if (32 * kk < 16 * (tb + 1)) {   // tau blocks at or before the token block
+            const int o = swz<kQ>(16 * tb + r, 32 * kk + 8 * kq);
+            accy[tb] = mfma(xop, ld8(&sM[0][o]), accy[tb]);
+            accy[tb] = mfma(xop, ld8(&sM[1][o]), accy[tb]);
+          }
         }
       }
       __syncthreads();   // every read of M and of the old state is done
 
       // ---- Y into LDS (over M), four consecutive channels per store
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const int grp = (4 * pb + kq) ^ (t & 15);   // 16-byte group of channels 16pb + 4kq, permuted by t
-        *reinterpret_cast<float4 *>(&sY[t * kP + 4 * grp]) =
-            make_float4(accy[pb][0], accy[pb][1], accy[pb][2], accy[pb][3]);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int ty = 16 * tb + r;
+        const int grp = (4 * w + kq) ^ (ty & 15);   // 16-byte group of channels 16w + 4kq, permuted by t
+        *reinterpret_cast<float4 *>(&sY[ty * kP + 4 * grp]) =
+            make_float4(accy[tb][0], accy[tb][1], accy[tb][2], accy[tb][3]);
       }
     }
     // ---- S^T <- exp(cs_last) S^T + B^T (X w); the old state only if no
@@ -432,16 +455,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     }
     sid_prev = sid_last;
     if constexpr (FULL) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        uint16_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split_bf(accs[nt][i], hi[i], lo[i]);
-        const int o = swz<N>(16 * w + r, 16 * nt + 4 * kq);
-        *reinterpret_cast<uint2 *>(&sS[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-        *reinterpret_cast<uint2 *>(&sS[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-      }
-      __syncthreads();
+      __syncthreads();   // Y is in LDS
 
       // ---- out = (Y + D x) * silu(z): this thread's x / z pieces, 16-byte stores
 #pragma unroll
