@@ -20,20 +20,23 @@
 // enter as two products each.  Rounding them to one bf16 instead costs 3-10%
 // of the output (C S^T sums 128 terms with heavy cancellation); the split
 // brings the error to about 1e-4.  The state stays in fp32 accumulators
-// across chunks, with its hi/lo copy in LDS as the operand of C S^T.
+// across chunks; C S^T takes its hi/lo split straight from them.
 //
 // Work decomposition: one 256-thread workgroup (four waves) per (batch,
 // head), walking the chunks in order.  Wave w owns the chunk's tokens
-// [16w, 16w+16) for M and Y, and the head's channels [16w, 16w+16) for the
-// state.  Operand layout of the 16x16x32 instruction (checked on the
-// device): lane l holds A[l%16][8(l/16)+i] and B[8(l/16)+i][l%16] for
-// i < 8, and accumulator i is D[4(l/16)+i][l%16].  The products are taken
-// transposed (G^T = B C^T, Y^T, S^T) so that each lane's four accumulators
-// are consecutive elements of one LDS row and go out in one store.  LDS
-// matrices are row-major with each row's 16-byte groups permuted by the row
-// index, so the operand reads and the transposed staging stores of X and B
-// spread over the banks without padding (measured: bank conflicts were the
-// largest stall before this layout).
+// [16w, 16w+16) for M, and the head's channels [16w, 16w+16) for Y (all 64
+// tokens) and for the state.  Operand layout of the 16x16x32 instruction
+// (checked on the device): lane l holds A[l%16][8(l/16)+i] and
+// B[8(l/16)+i][l%16] for i < 8, and accumulator i is D[4(l/16)+i][l%16].
+// The products are taken transposed (G^T = B C^T, Y^T, S^T) so that each
+// lane's four accumulators are consecutive elements of one LDS row and go
+// out in one store; in C S^T the state operand is this lane's own
+// accumulators, with the k index running over the states in their order
+// and C read in the same order.  LDS matrices are row-major with each row's
+// 16-byte groups (8-byte pieces for the C tile) permuted by the row index,
+// so the operand reads and the transposed staging stores of X and B spread
+// over the banks without padding (measured: bank conflicts were the largest
+// stall before this layout).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
