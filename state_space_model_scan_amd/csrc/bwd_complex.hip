@@ -24,9 +24,9 @@
 // by the lane that owns the timestep (lane j owns timesteps j and j + 16)
 // and read by the row through DPP row broadcasts; sums over the states
 // (y for dz, the du and delta' terms) are DPP rotations within the row.
-// Time-varying dB/dC sum over every channel of the group: each wave adds its
-// four rows, the workgroup adds its waves in order through LDS and writes
-// its partial sums; a second kernel adds the workgroups' partials in a fixed
+// Time-varying dB/dC sum over every channel of the group: each wave folds
+// its four rows with the row-swap instructions, the workgroup adds its waves
+// in order through LDS and writes its partial sums; a second kernel adds the workgroups' partials in a fixed
 // order, as it adds the per-batch partials of dA, fixed dB/dC, dD and
 // d(delta_bias).  No atomics: every output is bit-for-bit repeatable.
 #include <hip/hip_runtime.h>
@@ -61,18 +61,35 @@ struct CbwdParams {
 
 // sum over the 16 lanes of a row, in every lane (rotations within the row)
 __device__ __forceinline__ float row_sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));  // row_ror:2
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));  // row_ror:1
+  // row rotations write every lane: no old value (see row_bc)
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, true));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, true));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, true));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, true));  // row_ror:1
   return v;
 }
 
-// sum over the four rows of a wave, in every lane
-__device__ __forceinline__ float wave_rows_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// lane K of each 16-lane row, in every lane of the row (DPP row_newbcast).
+// It writes every lane, so no old value is needed: update_dpp with an old
+// value of 0 costs a register zeroed before every broadcast.
+template <int K>
+__device__ __forceinline__ float row_bc(float v) {
+  static_assert(K >= 0 && K < 16, "row lane");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + K, 0xf, 0xf, true));
+}
+
+// The wave's four rows (channels) summed with the gfx950 row-swap
+// instructions: v_permlane32_swap trades lanes 32..63 of x with lanes 0..31
+// of y, v_permlane16_swap rows 1 and 3 of x with rows 0 and 2 of y.  Of
+// (v0, v1, v2, v3), row 0 of the result holds the sum of v0 over the rows,
+// row 1 that of v2, row 2 that of v1, row 3 that of v3.
+__device__ __forceinline__ float fold_rows4(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+  const float r1 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float r2 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1), __float_as_uint(r2), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 template <int IO, bool BV, bool CV>
@@ -185,8 +202,8 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
     auto fstep = [&](auto TT) {   // x <- a_t x + delta'_t u_t B_t
       constexpr int t = decltype(TT)::value;
       if (t < len) {
-        const float dt = row_bcast<t % 16>(o_dt[t / 16]);
-        const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
+        const float dt = row_bc<t % 16>(o_dt[t / 16]);
+        const float dtu = row_bc<t % 16>(o_dtu[t / 16]);
         float er, ei, br, bi;
         cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
         bcoef(t, br, bi);
@@ -201,10 +218,10 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
     auto bstep = [&](auto TT, const float xpv_r, const float xpv_i) {
       constexpr int t = decltype(TT)::value;
       if (t < len) {
-        const float dt = row_bcast<t % 16>(o_dt[t / 16]);
-        const float dtu = row_bcast<t % 16>(o_dtu[t / 16]);
-        const float uu = row_bcast<t % 16>(o_u[t / 16]);
-        const float dy = row_bcast<t % 16>(o_dy[t / 16]);
+        const float dt = row_bc<t % 16>(o_dt[t / 16]);
+        const float dtu = row_bc<t % 16>(o_dtu[t / 16]);
+        const float uu = row_bc<t % 16>(o_u[t / 16]);
+        const float dy = row_bc<t % 16>(o_dy[t / 16]);
         float er, ei, br, bi, cr, cim;
         cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
         bcoef(t, br, bi);
@@ -228,9 +245,10 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         if constexpr (!BV) { fBr += gBr; fBi += gBi; }
         if constexpr (!CV) { fCr += gCr; fCi += gCi; }
         if constexpr (ANYV) {
-          const float v0 = BV ? wave_rows_sum(gBr) : 0.0f, v1 = BV ? wave_rows_sum(gBi) : 0.0f;
-          const float v2 = CV ? wave_rows_sum(gCr) : 0.0f, v3 = CV ? wave_rows_sum(gCi) : 0.0f;
-          if (rw == 0) *reinterpret_cast<float4 *>(&s_part[wave][t][s][0]) = make_float4(v0, v1, v2, v3);
+          // row rw holds the wave's sum of component ((rw & 1) << 1) | (rw >> 1)
+          // of (dB re, dB im, dC re, dC im)
+          const float v = fold_rows4(BV ? gBr : 0.0f, BV ? gBi : 0.0f, CV ? gCr : 0.0f, CV ? gCi : 0.0f);
+          s_part[wave][t][s][((rw & 1) << 1) | (rw >> 1)] = v;
         }
         const float nhr = fmaf(er, hr, ei * hi);               // carried: conj(a) h
         const float nhi = fmaf(er, hi, -ei * hr);
