@@ -1211,6 +1211,7 @@ def complex_bwd_cpu_baseline(w, t, dout, budget_s: float):
 MB_PROBES = {
     "fma": (0, 128, 0, 0),
     "exp": (1, 0, 128, 0),
+    "sin": (8, 0, 128, 0),
     "mix": (2, 136, 32, 0),
     "dpp": (3, 128, 0, 0),
     "lds_read_b128_broadcast": (4, 0, 0, 16 * 64 * 16),

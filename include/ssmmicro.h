@@ -23,6 +23,9 @@
  *   SSM_MB_LDS_BC   16 ds_read_b128 per iteration, every lane the same address
  *   SSM_MB_LDS_LIN  16 ds_read_b128 per iteration, lane i at 16*i bytes
  *   SSM_MB_LDS_W32  16 ds_write_b32 per iteration, lane i at 4*i bytes
+ *   SSM_MB_SIN      8 independent v_sin_f32 chains, 128 per iteration (the
+ *                   complex scan's decay takes a sine and a cosine per
+ *                   (timestep, state) besides its exp)
  *   SSM_MB_COPY     device copy of `iters` 16-byte vectors per thread (grid
  *                   stride, four loads in flight; iters a multiple of 4),
  *                   src = buf, dst = buf + half: bandwidth probe
@@ -51,7 +54,8 @@ enum {
   SSM_MB_LDS_BC = 4,
   SSM_MB_LDS_LIN = 5,
   SSM_MB_LDS_W32 = 6,
-  SSM_MB_COPY = 7
+  SSM_MB_COPY = 7,
+  SSM_MB_SIN = 8
 };
 
 int ssm_microbench(int32_t kind, int32_t blocks, int32_t iters, float *out, uint64_t *clk,

@@ -66,6 +66,26 @@ __global__ void __launch_bounds__(256) k_exp(float *out, uint64_t *clk, int iter
   stamp(clk, 1);
 }
 
+__global__ void __launch_bounds__(256) k_sin(float *out, uint64_t *clk, int iters) {
+  stamp(clk, 0);
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = gid * 1e-7f + 0.1f * k;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_sinf(x[k]);   // argument in revolutions
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += x[k];
+  out[gid] = s;
+  stamp(clk, 1);
+}
+
 // The scan step on 4 states over 8 timesteps per iteration; the step
 // operands are made opaque each iteration so no exp is hoisted.
 __global__ void __launch_bounds__(256) k_mix(float *out, uint64_t *clk, int iters) {
@@ -194,6 +214,7 @@ extern "C" int ssm_microbench(int32_t kind, int32_t blocks, int32_t iters, float
   switch (kind) {
     case SSM_MB_FMA: hipLaunchKernelGGL(k_fma, g, b, 0, st, out, clk, iters, 0.999999f, 1e-7f); break;
     case SSM_MB_EXP: hipLaunchKernelGGL(k_exp, g, b, 0, st, out, clk, iters); break;
+    case SSM_MB_SIN: hipLaunchKernelGGL(k_sin, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_MIX: hipLaunchKernelGGL(k_mix, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_DPP: hipLaunchKernelGGL(k_dpp, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_LDS_BC: hipLaunchKernelGGL(k_lds<0>, g, b, 0, st, out, clk, iters); break;
