@@ -21,11 +21,13 @@
 // of 32 timesteps, lane q owning timesteps [8q, 8q+8) of each chunk for the
 // loads, delta' = softplus(delta + bias), delta'*u and the gated store;
 // delta' and delta'*u reach the quad through LDS (stored by the owner once per
-// chunk in the partial-sum rows, read four timesteps at a time); time-varying
-// B/C of a chunk are staged in the wave's LDS slice (complex pairs
-// interleaved, as in memory) and read two timesteps ahead; each lane's
-// partial Re(C.x) goes to LDS and the owner sums the quad's partials.  The whole sequence is walked
-// in one pass (no sequence split).
+// chunk, read four timesteps at a time); time-varying B/C of a chunk are
+// staged in the wave's LDS slice (complex pairs interleaved, as in memory)
+// and read two timesteps ahead; the quad's partial Re(C.x) are summed with
+// two DPP quad permutes per step and the owner of the timestep keeps the
+// sum (unlike the real kernel, which sums them through LDS: here the LDS
+// that would take, 8 KB a wave, is what limits the waves per compute
+// unit).  The whole sequence is walked in one pass (no sequence split).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -64,12 +66,10 @@ scan_complex_kernel(const CplxParams p) {
 
   // [B or C][timestep][state][re, im]
   __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kT : 1][ANYV ? NP : 1][2];
-  // partial Re(C.x) of every (timestep, channel, lane) of the chunk.  At the
-  // chunk's start the rows of timesteps 4g and 4g+1 hold delta' and delta'*u
-  // of timesteps 4g..4g+3 as [channel][4] each: every lane reads them before
-  // step 4g overwrites those rows (a wave's LDS operations complete in order).
-  __shared__ __attribute__((aligned(16))) float s_yp[kT * kCPW * kLPC];
-  auto dd_at = [&](int g) -> float * { return &s_yp[4 * g * kCPW * kLPC]; };
+  // delta' and delta'*u of timesteps 4g..4g+3 as [channel][4] each, for
+  // every group g of the chunk (written by the owner, read by the quad)
+  __shared__ __attribute__((aligned(16))) float s_dd[(kT / 4) * 2 * kCPW * 4];
+  auto dd_at = [&](int g) -> float * { return &s_dd[g * 2 * kCPW * 4]; };
 
   const int lane = threadIdx.x & 63;
   const int q = lane % kLPC;
@@ -222,7 +222,11 @@ scan_complex_kernel(const CplxParams p) {
       y = fmaf(in.Cr[k], nr, y);
       y = fmaf(-in.Ci[k], ni, y);
     }
-    s_yp[(t * kCPW + cw_idx) * kLPC + q] = y;
+    // Re(C.x) over the quad's states: lanes (0,1) and (2,3) first, then the
+    // pairs (DPP quad permutes); the owner of timestep t keeps it
+    y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, true));  // [1,0,3,2]
+    y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, true));  // [2,3,0,1]
+    if (q == t / kKP) yv[t % kKP] = y;
   };
 
   fetch(0);
@@ -276,13 +280,6 @@ scan_complex_kernel(const CplxParams p) {
           step(TT, in1);
         }
       });
-    }
-    // the quad's partial Re(C.x) of this lane's timesteps
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < kKP; ++i) {
-      const float *yp = &s_yp[((own + i) * kCPW + cw_idx) * kLPC];
-      yv[i] = (yp[0] + yp[1]) + (yp[2] + yp[3]);
     }
     const int cnt = count(c);
     if (cnt > 0 && valid) {
