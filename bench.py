@@ -1213,6 +1213,7 @@ MB_PROBES = {
     "exp": (1, 0, 128, 0),
     "sin": (8, 0, 128, 0),
     "mix": (2, 136, 32, 0),
+    "mix_mfma": (9, 104, 32, 0),
     "dpp": (3, 128, 0, 0),
     "lds_read_b128_broadcast": (4, 0, 0, 16 * 64 * 16),
     "lds_read_b128_linear": (5, 0, 0, 16 * 64 * 16),

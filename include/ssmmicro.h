@@ -26,6 +26,11 @@
  *   SSM_MB_SIN      8 independent v_sin_f32 chains, 128 per iteration (the
  *                   complex scan's decay takes a sine and a cosine per
  *                   (timestep, state) besides its exp)
+ *   SSM_MB_MIXMM    SSM_MB_MIX with each timestep's products B * (delta' u)
+ *                   taken by one v_mfma_f32_16x16x4_f32 (an outer product of
+ *                   16 states and 16 channels): 104 plain, 32 exps and 8
+ *                   MFMAs per iteration; whether the matrix core's work
+ *                   overlaps the VALU stream
  *   SSM_MB_COPY     device copy of `iters` 16-byte vectors per thread (grid
  *                   stride, four loads in flight; iters a multiple of 4),
  *                   src = buf, dst = buf + half: bandwidth probe
@@ -55,7 +60,8 @@ enum {
   SSM_MB_LDS_LIN = 5,
   SSM_MB_LDS_W32 = 6,
   SSM_MB_COPY = 7,
-  SSM_MB_SIN = 8
+  SSM_MB_SIN = 8,
+  SSM_MB_MIXMM = 9
 };
 
 int ssm_microbench(int32_t kind, int32_t blocks, int32_t iters, float *out, uint64_t *clk,

@@ -3,7 +3,9 @@
 Every HIP source is compiled with the packed-FP32 feature switched off
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``): hipcc then emits only
 scalar fp32 VALU instructions.  hipcc's host pass warns that it does not know
-the feature; that warning is harmless.
+the feature; that warning is harmless.  ``-mllvm -amdgpu-mfma-vgpr-form``
+keeps matrix-core results in ordinary VGPRs, so the VALU reads them without
+an accumulator-register copy.
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", "-Wall"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-fno-gpu-rdc"]
+             "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-gpu-rdc"]
 
 SOURCES = [
     ("scan_bf16.hip", True),

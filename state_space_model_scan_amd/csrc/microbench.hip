@@ -125,6 +125,56 @@ __global__ void __launch_bounds__(256) k_mix(float *out, uint64_t *clk, int iter
   stamp(clk, 1);
 }
 
+// The scan step of k_mix with the products B * (delta' u) of a timestep
+// taken by one v_mfma_f32_16x16x4_f32 as an outer product (states x
+// channels, one nonzero k), so each lane's state update reads its four
+// products from the accumulators: 104 plain, 32 exps and 8 MFMAs per
+// iteration.
+typedef float mb_f32x4 __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) k_mixmm(float *out, uint64_t *clk, int iters) {
+  stamp(clk, 0);
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  float A[4], Cv[4], x[4], dt[8], bsel[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    A[k] = -1.0f - 0.25f * k;
+    Cv[k] = 0.3f - 0.05f * k;
+    x[k] = 0.0f;
+  }
+  float Bl = 0.5f + 0.01f * (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    dt[j] = 0.01f * (j + 1) + gid * 1e-9f;
+    bsel[j] = lane < 16 ? 0.02f * (j + 1) : 0.0f;
+  }
+  float acc = 0.0f;
+  const mb_f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < iters; ++i) {
+    mb_f32x4 bx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      touch(bsel[j]);
+      bx[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Bl, bsel[j], zero4, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      touch(dt[j]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = __builtin_amdgcn_exp2f(dt[j] * A[k]);
+        x[k] = fmaf(e, x[k], bx[j][k]);
+      }
+      float y = Cv[0] * x[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) y = fmaf(Cv[k], x[k], y);
+      acc += y;
+    }
+  }
+  out[gid] = acc;
+  stamp(clk, 1);
+}
+
 template <int K>
 __device__ __forceinline__ float bcast(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
@@ -216,6 +266,7 @@ extern "C" int ssm_microbench(int32_t kind, int32_t blocks, int32_t iters, float
     case SSM_MB_EXP: hipLaunchKernelGGL(k_exp, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_SIN: hipLaunchKernelGGL(k_sin, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_MIX: hipLaunchKernelGGL(k_mix, g, b, 0, st, out, clk, iters); break;
+    case SSM_MB_MIXMM: hipLaunchKernelGGL(k_mixmm, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_DPP: hipLaunchKernelGGL(k_dpp, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_LDS_BC: hipLaunchKernelGGL(k_lds<0>, g, b, 0, st, out, clk, iters); break;
     case SSM_MB_LDS_LIN: hipLaunchKernelGGL(k_lds<1>, g, b, 0, st, out, clk, iters); break;
