@@ -97,22 +97,36 @@ __device__ __forceinline__ int swz8(int row, int col) {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float v) {
-  const __bf16 h = static_cast<__bf16>(v);
-  return __builtin_bit_cast(uint16_t, h);
-}
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 // 8 consecutive bf16 as raw words (element i in the low / high half of word i/2)
 __device__ __forceinline__ uint4 ld8_raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint32_t raw_word(const uint4 &q, int j) {
+  return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+}
 __device__ __forceinline__ uint16_t raw_bits(const uint4 &q, int i) {
-  const uint32_t wd = (i >> 1) == 0 ? q.x : (i >> 1) == 1 ? q.y : (i >> 1) == 2 ? q.z : q.w;
+  const uint32_t wd = raw_word(q, i >> 1);
   return static_cast<uint16_t>((i & 1) ? (wd >> 16) : (wd & 0xffffu));
 }
 
-// v ~ hi + lo with both halves bf16 (hi rounded to nearest, lo the rounded rest)
-__device__ __forceinline__ void split_bf(float v, uint16_t &hi, uint16_t &lo) {
-  hi = f2bf(v);
-  lo = f2bf(v - bf2f(hi));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two floats rounded to bf16 (to nearest, ties to even) by one paired
+// conversion; a in the low half
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// a ~ hi + lo and b ~ hi + lo with all four halves bf16 (hi rounded to
+// nearest, lo the rounded rest), as two packed pairs: the same values as
+// rounding each element on its own, in three operations per element
+__device__ __forceinline__ void split_bf2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf2(a, b);
+  lo = pack_bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// the 16-bit halves of two words side by side (one byte permute): the low
+// halves (HIGH = false) or the high halves of a and b, a's in the low half
+template <bool HIGH>
+__device__ __forceinline__ uint32_t pair_halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, HIGH ? 0x07060302u : 0x05040100u);
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -261,7 +275,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     // ---- X^T and B^T into LDS, two tokens per 32-bit store
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t v = static_cast<uint32_t>(raw_bits(xr[0], i)) | (static_cast<uint32_t>(raw_bits(xr[1], i)) << 16);
+      const uint32_t v = (i & 1) ? pair_halves<true>(raw_word(xr[0], i >> 1), raw_word(xr[1], i >> 1))
+                                 : pair_halves<false>(raw_word(xr[0], i >> 1), raw_word(xr[1], i >> 1));
       *reinterpret_cast<uint32_t *>(&sXT[swz<kQ>(xp0 + i, xt0)]) = v;
     }
 #pragma unroll
@@ -271,8 +286,8 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       const int t = 2 * (piece / G8), n0 = (piece % G8) * 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t v = static_cast<uint32_t>(raw_bits(br[j][0], i)) |
-                           (static_cast<uint32_t>(raw_bits(br[j][1], i)) << 16);
+        const uint32_t v = (i & 1) ? pair_halves<true>(raw_word(br[j][0], i >> 1), raw_word(br[j][1], i >> 1))
+                                   : pair_halves<false>(raw_word(br[j][0], i >> 1), raw_word(br[j][1], i >> 1));
         *reinterpret_cast<uint32_t *>(&sBT[swz<kQ>(n0 + i, t)]) = v;
       }
       if constexpr (FULL) {
@@ -356,18 +371,24 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
           const int4 sd4 = *reinterpret_cast<const int4 *>(&sSid[16 * tb + 4 * kq]);
           sdv[0] = sd4.x; sdv[1] = sd4.y; sdv[2] = sd4.z; sdv[3] = sd4.w;
         }
-        uint16_t hi[4], lo[4];
+        // computed for every lane of a block at or before the wave's
+        // tokens and selected by the mask (no per-lane branch); the blocks
+        // after them are zero
+        float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (tb <= w) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tau = 16 * tb + 4 * kq + i;
-          float m = 0.0f;
-          if (tb <= w && tau <= t && (!SEQ || sdv[i] == sidt))
-            m = acc[i] * fast_exp2((cst - csv[i]) * kLog2e) * dtv[i];
-          split_bf(m, hi[i], lo[i]);
+          for (int i = 0; i < 4; ++i) {
+            const int tau = 16 * tb + 4 * kq + i;
+            const float v = acc[i] * fast_exp2((cst - csv[i]) * kLog2e) * dtv[i];
+            m[i] = (tau <= t && (!SEQ || sdv[i] == sidt)) ? v : 0.0f;
+          }
         }
+        uint2 hi, lo;
+        split_bf2(m[0], m[1], hi.x, lo.x);
+        split_bf2(m[2], m[3], hi.y, lo.y);
         const int o = swz<kQ>(t, 16 * tb + 4 * kq);
-        *reinterpret_cast<uint2 *>(&sM[0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-        *reinterpret_cast<uint2 *>(&sM[1][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        *reinterpret_cast<uint2 *>(&sM[0][o]) = hi;
+        *reinterpret_cast<uint2 *>(&sM[1][o]) = lo;
       }
       __syncthreads();
 
@@ -383,14 +404,12 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
       for (int tb = 0; tb < 4; ++tb) accy[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
-        bf16x8 shi, slo;
+        uint32_t sh[4], sl[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float v = accs[2 * kk + i / 4][i % 4];
-          const __bf16 hb = static_cast<__bf16>(v);
-          shi[i] = hb;
-          slo[i] = static_cast<__bf16>(v - static_cast<float>(hb));
-        }
+        for (int i = 0; i < 8; i += 2)
+          split_bf2(accs[2 * kk + i / 4][i % 4], accs[2 * kk + i / 4][i % 4 + 1], sh[i / 2], sl[i / 2]);
+        const bf16x8 shi = __builtin_bit_cast(bf16x8, make_uint4(sh[0], sh[1], sh[2], sh[3]));
+        const bf16x8 slo = __builtin_bit_cast(bf16x8, make_uint4(sl[0], sl[1], sl[2], sl[3]));
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const int row = 16 * tb + r;
@@ -441,14 +460,13 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     for (int kk = 0; kk < kQ / 32; ++kk) {
       // B operand: (X w) at tokens 32kk + 8kq + i, channel 16w + r, split hi / lo
       const uint4 xt = ld8_raw(&sXT[swz<kQ>(16 * w + r, 32 * kk + 8 * kq)]);
-      bf16x8 xhi, xlo;
+      uint32_t xh[4], xl[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = bf2f(raw_bits(xt, i)) * sW[32 * kk + 8 * kq + i];
-        const __bf16 hb = static_cast<__bf16>(v);
-        xhi[i] = hb;
-        xlo[i] = static_cast<__bf16>(v - static_cast<float>(hb));
-      }
+      for (int i = 0; i < 8; i += 2)
+        split_bf2(bf2f(raw_bits(xt, i)) * sW[32 * kk + 8 * kq + i],
+                  bf2f(raw_bits(xt, i + 1)) * sW[32 * kk + 8 * kq + i + 1], xh[i / 2], xl[i / 2]);
+      const bf16x8 xhi = __builtin_bit_cast(bf16x8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+      const bf16x8 xlo = __builtin_bit_cast(bf16x8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8 bop = ld8(&sBT[swz<kQ>(16 * nt + r, 32 * kk + 8 * kq)]);
@@ -468,20 +486,20 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
           const int g0 = (xp0 >> 2) ^ (t & 15), g1 = ((xp0 >> 2) + 1) ^ (t & 15);
           const float4 y0 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g0]);
           const float4 y1 = *reinterpret_cast<const float4 *>(&sY[t * kP + 4 * g1]);
-          const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          // the uniform conditions outside the element loops, so the eight
+          // gates' exp / rcp chains interleave
+          if (p.D) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] = fmaf(Dv8[i], bf2f(raw_bits(xr[k], i)), yv[i]);
+          }
+          if (zb) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yv[i] *= silu_f(bf2f(raw_bits(zr[k], i)));
+          }
           uint32_t pk[4];
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            float o2[2];
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              float y = yv[i + q2];
-              if (p.D) y = fmaf(Dv8[i + q2], bf2f(raw_bits(xr[k], i + q2)), y);
-              if (zb) y *= silu_f(bf2f(raw_bits(zr[k], i + q2)));
-              o2[q2] = y;
-            }
-            pk[i / 2] = static_cast<uint32_t>(f2bf(o2[0])) | (static_cast<uint32_t>(f2bf(o2[1])) << 16);
-          }
+          for (int i = 0; i < 8; i += 2) pk[i / 2] = pack_bf2(yv[i], yv[i + 1]);
           *reinterpret_cast<uint4 *>(ob + (t0 + t) * xrow + xp0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
       }
