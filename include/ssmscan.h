@@ -478,9 +478,11 @@ typedef struct ssd_scan_args {
    * read before written; reusable once the call's work has finished. */
   void *workspace;
   size_t workspace_bytes;
-  /* Sequence split: 0 lets the library choose; k >= 1 asks for k segments
-   * of whole chunks (possibly fewer).  Negative values return SSM_ERR_SHAPE.
-   * The split changes the results only by rounding order. */
+  /* Sequence split: 0 lets the library choose (its segments may differ in
+   * length); k >= 1 asks for k segments of ceil(chunks / k) whole chunks,
+   * the last one taking the rest (possibly fewer segments).  Negative values
+   * return SSM_ERR_SHAPE.  The split changes the results only by rounding
+   * order. */
   int32_t seq_segments;
 } ssd_scan_args_t;
 
