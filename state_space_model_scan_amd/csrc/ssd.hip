@@ -145,6 +145,7 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
   // M [t][tau] as hi / lo bf16, and the chunk's C [t][n] (full pass only)
   __shared__ __attribute__((aligned(16))) uint16_t sM[FULL ? 2 : 1][FULL ? kQ * kQ : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sC[FULL ? kQ * N : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sBrow[FULL ? kQ * N : 8];   // B [t][n] (full pass)
   __shared__ __attribute__((aligned(16))) float sCs[kQ], sDt[kQ], sW[kQ];
   __shared__ __attribute__((aligned(16))) int32_t sSid[SEQ ? kQ : 4];
 
@@ -187,10 +188,13 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     const int pp = xp0 + i;
     Dv8[i] = (FULL && p.D) ? (p.D_per_channel ? p.D[h * kP + pp] : p.D[h]) : 0.0f;
   }
-  float *sY = reinterpret_cast<float *>(&sM[0][0]);   // Y [t][p] (fp32), 16-byte groups permuted by t
-  // B row-major [t][n] for the A operand of C B^T, in M's space until M is written
-  uint16_t *sBr = &sM[0][0];
-  static_assert(!FULL || kQ * N <= 2 * kQ * kQ, "the row-major B tile fits in M's space");
+  // Y [t][p] (fp32, 16-byte groups permuted by t): in the row-major B copy's
+  // space where it fits (dstate 128), which its last reader left before M was
+  // stored, so the Y stores need no barrier after the products that read M;
+  // otherwise over M
+  constexpr bool Y_IN_BR = FULL && kQ * N * 2 >= kQ * kP * 4;
+  float *sY = Y_IN_BR ? reinterpret_cast<float *>(sBrow) : reinterpret_cast<float *>(&sM[0][0]);
+  uint16_t *sBr = sBrow;   // B row-major [t][n] for the A operand of C B^T
 
   // state, transposed: wave w holds S[p = 16w + r][n = 16 nt + 4kq + i].
   // The state pass starts every segment from zero; the full pass starts
@@ -271,8 +275,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     }
 
     // the previous chunk's reads of the staged tiles (and, in the full pass,
-    // its epilogue's reads of Y from M's space, which the row-major B copy
-    // below overwrites) are done; the wait overlaps the loads above
+    // its epilogue's reads of Y, which shares its space with the row-major B
+    // copy at dstate 128 and with M otherwise) are done; the wait overlaps
+    // the loads above
     __syncthreads();
 
     // ---- X^T and B^T into LDS, two tokens per 32-bit store
@@ -344,9 +349,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
     if constexpr (FULL) {
       // ---- M, from G^T = B C^T: lane holds G[t = 16w + r][tau = 16 tb + 4kq + i],
       // masked to tau <= t (and the same sequence), decayed, split, stored as
-      // 4 consecutive tau.  The products read B from its row-major LDS copy; M
-      // overwrites that copy, so every wave's products are done before any M
-      // is stored.
+      // 4 consecutive tau.  The products read B from its row-major LDS copy,
+      // an array of its own, so a wave stores its M as soon as its products
+      // are done.
       const int t = 16 * w + r;
       const float cst = sCs[t];
       const int32_t sidt = SEQ ? sSid[t] : 0;
@@ -361,7 +366,6 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
             accg[tb] = mfma(ld8(&sBr[swz<N>(tau_row, 32 * kk + 8 * kq)]), cop[kk], accg[tb]);
         }
       }
-      __syncthreads();
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const f32x4 acc = accg[tb];
@@ -442,9 +446,9 @@ __global__ void __launch_bounds__(256, 2) ssd_kernel(const SsdParams p) {
           }
         }
       }
-      __syncthreads();   // every read of M and of the old state is done
+      if constexpr (!Y_IN_BR) __syncthreads();   // every read of M is done
 
-      // ---- Y into LDS (over M), four consecutive channels per store
+      // ---- Y into LDS (the B copy's space or over M), four consecutive channels per store
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int ty = 16 * tb + r;
