@@ -74,7 +74,8 @@ struct BwdParams {
   float *loc, *ssum;
   int64_t dim, seqlen, cpg, bd;   // bd = batch * dim
   int n, ngroups, nblk, nck, softplus;
-  int segc, nseg;                 // chunks per segment, segments
+  int segc, nseg;                 // chunks per segment (after the first), segments
+  int seg0;                       // chunks of segment 0
 };
 
 __device__ __forceinline__ float sigmoid_f(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
@@ -201,8 +202,9 @@ __global__ void __launch_bounds__(kThreads, 3) scan_bwd_kernel(const BwdParams p
   const int g = bg % p.ngroups;
   const int64_t b = bg / p.ngroups;
   const int seg = blockIdx.y;                  // this workgroup's chunks: [cbeg, cend)
-  const int cbeg = seg * p.segc;
-  const int cend = cbeg + p.segc < p.nck ? cbeg + p.segc : p.nck;
+  const int cbeg = seg == 0 ? 0 : p.seg0 + (seg - 1) * p.segc;
+  const int clen = seg == 0 ? p.seg0 : p.segc;
+  const int cend = cbeg + clen < p.nck ? cbeg + clen : p.nck;
   const int64_t lc = static_cast<int64_t>(blk) * kCPB + w * kCPW + c;   // channel within the group
   const bool valid = lc < p.cpg;
   const int64_t dl = g * p.cpg + (valid ? lc : p.cpg - 1);
@@ -521,7 +523,7 @@ __global__ void __launch_bounds__(256) seg_carry_kernel(const BwdParams p) {
   const int64_t row = b * p.dim + dl;
   const int64_t rbase = row * L;
   const int seg = blockIdx.y + 1;
-  const int64_t tbeg = static_cast<int64_t>(seg) * p.segc * kT;
+  const int64_t tbeg = (static_cast<int64_t>(p.seg0) + static_cast<int64_t>(seg - 1) * p.segc) * kT;
   const int64_t tend = tbeg + static_cast<int64_t>(p.segc) * kT < L ? tbeg + static_cast<int64_t>(p.segc) * kT : L;
 
   const float Ap = (sv ? p.A[dl * n + s] : 0.0f) * kLog2e;
@@ -643,7 +645,7 @@ constexpr int kMinSegChunks = 4;   // and the fewest chunks it gives a segment
 
 struct BwdPlan {
   int64_t cpg, nblk, nck, blocks;
-  int segc, nseg;
+  int segc, nseg, seg0;
   size_t nB, nC, nA, nD, nLoc, nSum;   // partial element counts
   size_t bytes;
 };
@@ -678,6 +680,66 @@ int pick_segments(int64_t blocks, int64_t nck, int cus) {
   return best;
 }
 
+// The time (in chunk walks) at which the last of n workgroups of la chunks
+// and then n of lb chunks ends when each goes to the first compute unit free,
+// in that order: the dispatch of a two-segment grid, segment 0 first.
+int64_t two_class_makespan(int64_t n, int64_t la, int64_t lb, int64_t units) {
+  struct Group { int64_t t, k; };   // k units free from time t
+  Group g[8];
+  int ng = 1;
+  g[0] = {0, units};
+  int64_t end = 0;
+  auto place = [&](int64_t cnt, int64_t len) -> bool {
+    while (cnt > 0) {
+      int i = 0;
+      for (int j = 1; j < ng; ++j)
+        if (g[j].t < g[i].t) i = j;
+      const int64_t k = cnt < g[i].k ? cnt : g[i].k;
+      const int64_t t = g[i].t + len;
+      cnt -= k;
+      g[i].k -= k;
+      if (g[i].k == 0) g[i] = g[--ng];
+      int m = -1;
+      for (int j = 0; j < ng; ++j)
+        if (g[j].t == t) m = j;
+      if (m >= 0) {
+        g[m].k += k;
+      } else {
+        if (ng == 8) return false;   // never reached: at most three free times coexist
+        g[ng++] = {t, k};
+      }
+      if (t > end) end = t;
+    }
+    return true;
+  };
+  if (!place(n, la) || !place(n, lb)) return INT64_MAX;
+  return end;
+}
+
+// When the library splits the sequence in two, segment 0 (dispatched first)
+// may be the longer one: the carry pass then covers only the short second
+// segment, and the second segment's workgroups fill the units the first
+// segment's last round leaves free.  The length of segment 0 minimises the
+// modelled time of the two passes, two_class_makespan + kCarryCost * (chunks
+// of segment 1) * blocks / cus, equal halves where a longer first segment
+// does not pay (a grid of one round).  Measured at mamba2p8b (864 workgroups,
+// 64 chunks; the model picks 55): first segment of 32 chunks 1.711 ms, 48:
+// 1.641, 52: 1.587, 54: 1.606, 56: 1.593, 58: 1.634, 60: 1.675.
+int pick_first_segment(int64_t blocks, int64_t nck, int cus) {
+  const int64_t half = (nck + 1) / 2;
+  int64_t best = half;
+  double best_t = 1e300;
+  for (int64_t l0 = half; l0 < nck; ++l0) {
+    const double t = static_cast<double>(two_class_makespan(blocks, l0, nck - l0, cus)) +
+                     kCarryCost * static_cast<double>(nck - l0) * static_cast<double>(blocks) / cus;
+    if (t < best_t * 0.99) {
+      best_t = t;
+      best = l0;
+    }
+  }
+  return static_cast<int>(best);
+}
+
 BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a, int cus) {
   BwdPlan pl{};
   pl.cpg = a->dim / a->ngroups;
@@ -688,6 +750,11 @@ BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a, int cus) {
   if (want > pl.nck) want = pl.nck;
   pl.segc = static_cast<int>((pl.nck + want - 1) / want);
   pl.nseg = static_cast<int>((pl.nck + pl.segc - 1) / pl.segc);   // every segment holds a chunk
+  pl.seg0 = pl.segc;
+  if (a->seq_segments <= 0 && pl.nseg == 2) {
+    pl.seg0 = pick_first_segment(pl.blocks, pl.nck, cus);
+    pl.segc = static_cast<int>(pl.nck - pl.seg0);
+  }
   const size_t ns = static_cast<size_t>(pl.nseg);
   const size_t bgn = static_cast<size_t>(a->batch * a->ngroups) * pl.nblk * a->dstate * a->seqlen;
   const size_t bdn = static_cast<size_t>(a->batch * a->dim * a->dstate);
@@ -750,7 +817,7 @@ extern "C" int ssm_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   p.n = static_cast<int>(a->dstate); p.ngroups = static_cast<int>(a->ngroups);
   p.nblk = static_cast<int>(pl.nblk); p.nck = static_cast<int>(pl.nck);
   p.softplus = a->delta_softplus;
-  p.segc = pl.segc; p.nseg = pl.nseg;
+  p.segc = pl.segc; p.nseg = pl.nseg; p.seg0 = pl.seg0;
 
   const bool hz = a->z != nullptr;
   hipError_t e = hipSuccess;
