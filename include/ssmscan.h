@@ -290,10 +290,15 @@ int ssm_scan_bwd(const ssm_scan_bwd_args_t *args, void *hip_stream);
  * as in ssm_scan_fwd_complex, and the phase of a_t to about one rounding
  * (Im(A) / (2 pi) held as two floats, the product's rounding error
  * recovered with an fma): ddelta weighs a phase error by |A|^2 delta'.
- * seq_segments must
- * be 0 or 1 (no sequence split; others return SSM_ERR_UNSUPPORTED); the
+ * seq_segments splits the sequence as in ssm_scan_bwd (0: the library's
+ * choice, k >= 1: at most k segments of whole chunks): a carry pass walks
+ * every segment after the first from a zero carry, and each segment starts
+ * from the carry of the later ones, the same recurrence reassociated (the
+ * decay over a segment is the product of its a_t, multiplied up step by
+ * step).  The
  * workspace (ssm_scan_bwd_complex_workspace_size) holds the partial sums and
- * is required.  Asynchronous on hip_stream; returns a status code. */
+ * the carries and is required.  Asynchronous on hip_stream; returns a status
+ * code. */
 int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *args, void *hip_stream);
 
 /* Host-only argument check of ssm_scan_bwd_complex (no HIP call). */

@@ -448,7 +448,7 @@ def ssm_scan_bwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, 
                          D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                          delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
                          want_dinitial_state: bool = False, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> dict:
+                         seq_segments: int = 0, stream=None) -> dict:
     """Enqueue ssm_scan_bwd_complex; returns the gradients in a dict.
 
     Inputs as for ``ssm_scan_fwd_complex`` (A complex64 or float32 pairs
@@ -458,7 +458,8 @@ def ssm_scan_bwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, 
     call wrote.  du, ddelta, dz come back in the io dtype; dD, ddelta_bias in
     float32; dA, dB, dC and dinitial_state as float32 (real, imaginary)
     pairs in A's, B's, C's and the state's layouts (``torch.view_as_complex``
-    turns them into complex64)."""
+    turns them into complex64).  ``seq_segments`` caps the sequence split
+    (0: the library's choice)."""
     delta = _dense(delta)
     io = _io_of(delta, "delta", 3)
     batch, dim, seqlen = delta.shape
@@ -510,6 +511,7 @@ def ssm_scan_bwd_complex(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, 
     args.D, args.delta_bias, args.z = _ptr(D), _ptr(delta_bias), _ptr(z)
     args.delta_softplus = int(bool(delta_softplus))
     args.checkpoints, args.dout = _ptr(checkpoints), _ptr(dout)
+    args.seq_segments = int(seq_segments)
     for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
         setattr(args, k, _ptr(g[k]))
     L = _lib.lib()

@@ -650,95 +650,14 @@ struct BwdPlan {
   size_t bytes;
 };
 
-// Segments of the sequence split.  One 768-thread workgroup fills a compute
-// unit, so a grid of few workgroups leaves units idle, and one that is not a
-// whole number of rounds leaves its last round part-empty.  Cutting the
-// sequence into ns segments multiplies the workgroups by ns and divides each
-// one's length by ns, at the price of the carry pass over the segments after
-// the first, which costs about a quarter of the main pass per (channel,
-// timestep) when it fills the chip (measured).  Modelled time, in units of
-// one workgroup walking one chunk:
-//   ceil(blocks * ns / cus) * segc  +  kCarryCost * (ns - 1) / ns * blocks * nck / cus
-// and the plan takes the segment count that minimises it.
-constexpr double kCarryCost = 0.25;
-
-int pick_segments(int64_t blocks, int64_t nck, int cus) {
-  const int64_t most = nck / kMinSegChunks < kMaxSeg ? nck / kMinSegChunks : kMaxSeg;
-  const double work = static_cast<double>(blocks) * static_cast<double>(nck) / cus;
-  int best = 1;
-  double best_t = 1e300;
-  for (int64_t k = 1; k <= (most > 1 ? most : 1); ++k) {
-    const int64_t segc = (nck + k - 1) / k;
-    const int64_t ns = (nck + segc - 1) / segc;
-    const double rounds = static_cast<double>((blocks * ns + cus - 1) / cus);
-    const double t = rounds * static_cast<double>(segc) + kCarryCost * static_cast<double>(ns - 1) / ns * work;
-    if (t < best_t * 0.99) {   // a split has to win by more than the model's noise
-      best_t = t;
-      best = static_cast<int>(ns);
-    }
-  }
-  return best;
-}
-
-// The time (in chunk walks) at which the last of n workgroups of la chunks
-// and then n of lb chunks ends when each goes to the first compute unit free,
-// in that order: the dispatch of a two-segment grid, segment 0 first.
-int64_t two_class_makespan(int64_t n, int64_t la, int64_t lb, int64_t units) {
-  struct Group { int64_t t, k; };   // k units free from time t
-  Group g[8];
-  int ng = 1;
-  g[0] = {0, units};
-  int64_t end = 0;
-  auto place = [&](int64_t cnt, int64_t len) -> bool {
-    while (cnt > 0) {
-      int i = 0;
-      for (int j = 1; j < ng; ++j)
-        if (g[j].t < g[i].t) i = j;
-      const int64_t k = cnt < g[i].k ? cnt : g[i].k;
-      const int64_t t = g[i].t + len;
-      cnt -= k;
-      g[i].k -= k;
-      if (g[i].k == 0) g[i] = g[--ng];
-      int m = -1;
-      for (int j = 0; j < ng; ++j)
-        if (g[j].t == t) m = j;
-      if (m >= 0) {
-        g[m].k += k;
-      } else {
-        if (ng == 8) return false;   // never reached: at most three free times coexist
-        g[ng++] = {t, k};
-      }
-      if (t > end) end = t;
-    }
-    return true;
-  };
-  if (!place(n, la) || !place(n, lb)) return INT64_MAX;
-  return end;
-}
-
-// When the library splits the sequence in two, segment 0 (dispatched first)
-// may be the longer one: the carry pass then covers only the short second
-// segment, and the second segment's workgroups fill the units the first
-// segment's last round leaves free.  The length of segment 0 minimises the
-// modelled time of the two passes, two_class_makespan + kCarryCost * (chunks
-// of segment 1) * blocks / cus, equal halves where a longer first segment
-// does not pay (a grid of one round).  Measured at mamba2p8b (864 workgroups,
-// 64 chunks; the model picks 55): first segment of 32 chunks 1.711 ms, 48:
+// Segments of the sequence split (host_util.h: split_segments,
+// split_first_segment).  One 768-thread workgroup fills a compute unit; the
+// carry pass over the segments after the first costs about a quarter of the
+// main pass per (channel, timestep) when it fills the chip (measured).  For
+// the uneven two-segment split, measured at mamba2p8b (864 workgroups, 64
+// chunks; the model picks 55): first segment of 32 chunks 1.711 ms, 48:
 // 1.641, 52: 1.587, 54: 1.606, 56: 1.593, 58: 1.634, 60: 1.675.
-int pick_first_segment(int64_t blocks, int64_t nck, int cus) {
-  const int64_t half = (nck + 1) / 2;
-  int64_t best = half;
-  double best_t = 1e300;
-  for (int64_t l0 = half; l0 < nck; ++l0) {
-    const double t = static_cast<double>(two_class_makespan(blocks, l0, nck - l0, cus)) +
-                     kCarryCost * static_cast<double>(nck - l0) * static_cast<double>(blocks) / cus;
-    if (t < best_t * 0.99) {
-      best_t = t;
-      best = l0;
-    }
-  }
-  return static_cast<int>(best);
-}
+constexpr double kCarryCost = 0.25;
 
 BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a, int cus) {
   BwdPlan pl{};
@@ -746,13 +665,14 @@ BwdPlan plan_bwd(const ssm_scan_bwd_args_t *a, int cus) {
   pl.nblk = (pl.cpg + kCPB - 1) / kCPB;
   pl.nck = (a->seqlen + kT - 1) / kT;
   pl.blocks = a->batch * a->ngroups * pl.nblk;
-  int64_t want = a->seq_segments > 0 ? a->seq_segments : pick_segments(pl.blocks, pl.nck, cus);
+  int64_t want = a->seq_segments > 0 ? a->seq_segments
+                                     : split_segments(pl.blocks, pl.nck, cus, kCarryCost, kMaxSeg, kMinSegChunks);
   if (want > pl.nck) want = pl.nck;
   pl.segc = static_cast<int>((pl.nck + want - 1) / want);
   pl.nseg = static_cast<int>((pl.nck + pl.segc - 1) / pl.segc);   // every segment holds a chunk
   pl.seg0 = pl.segc;
   if (a->seq_segments <= 0 && pl.nseg == 2) {
-    pl.seg0 = pick_first_segment(pl.blocks, pl.nck, cus);
+    pl.seg0 = split_first_segment(pl.blocks, pl.nck, cus, kCarryCost);
     pl.segc = static_cast<int>(pl.nck - pl.seg0);
   }
   const size_t ns = static_cast<size_t>(pl.nseg);

@@ -53,10 +53,14 @@ struct CbwdParams {
   void *du, *ddelta, *dz;
   float *dA, *dB, *dC, *dD, *ddbias, *dinit;
   float *ws_bc;               // time-varying dB/dC partials [b*g][blk][t][s][4]
-  float *ws_dA, *ws_fB, *ws_fC, *ws_dD, *ws_db;   // per-batch partials
+  float *ws_dA, *ws_fB, *ws_fC, *ws_dD, *ws_db;   // per-(segment, batch) partials
+  // sequence split: segment k >= 1's adjoint carry out of its first timestep
+  // with no carry coming in, and its decay prod_t a_t, both (nseg, b, d, n, 2)
+  float *loc, *pdec;
   int64_t batch, dim, seqlen, nck, cpg;
   int n, ngroups, groups_eff, nblk;
   int softplus;
+  int nseg, seg0, segc;       // segments; chunks of segment 0 and of the others
 };
 
 // sum over the 16 lanes of a row, in every lane (rotations within the row)
@@ -92,11 +96,18 @@ __device__ __forceinline__ float fold_rows4(float v0, float v1, float v2, float 
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int IO, bool BV, bool CV>
+// CARRY: the carry pass of the sequence split.  Workgroup (x, y) walks
+// segment y + 1 of its channels backwards from a zero carry, through the
+// same adjoint steps as the backward walk (h += dy conj(C_t), then
+// h <- conj(a_t) h), and stores the carry out of the segment's first
+// timestep and the segment's decay prod_t a_t, multiplied up step by step as
+// the walk applies it (its phase as accurate as the walk's); nothing else.
+template <int IO, bool BV, bool CV, bool CARRY>
 __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
   constexpr bool ANYV = BV || CV;
+  constexpr bool PART = ANYV && !CARRY;
   __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kCk : 1][16][2];       // [B, C][t][s][re, im]
-  __shared__ float s_part[ANYV ? kWavesPerWG : 1][ANYV ? kCk : 1][16][4];   // per-wave (dB, dC) sums
+  __shared__ float s_part[PART ? kWavesPerWG : 1][PART ? kCk : 1][16][4];   // per-wave (dB, dC) sums
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -126,12 +137,33 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
   const float Dd = p.D ? p.D[dl] : 0.0f;
   const int64_t bg = b * p.ngroups + g;
   const int64_t bc_base = bg * n * L * 2;   // element of (b, g, state 0, t 0, re) in a varying B/C
+  const int64_t BD = p.batch * p.dim;
+  const int seg = CARRY ? static_cast<int>(blockIdx.y) + 1 : static_cast<int>(blockIdx.y);
+  const int64_t cbeg = seg == 0 ? 0 : p.seg0 + static_cast<int64_t>(seg - 1) * p.segc;
+  const int64_t clen = seg == 0 ? p.seg0 : p.segc;
+  const int64_t cend = cbeg + clen < p.nck ? cbeg + clen : p.nck;   // this workgroup's chunks [cbeg, cend)
 
   float hr = 0.0f, hi = 0.0f;                                 // adjoint carry
+  if constexpr (!CARRY) {
+    // the carry entering from the later segments: each maps an incoming
+    // carry G to loc + conj(P) G, P its decay prod_t a_t
+    if (seg + 1 < p.nseg && sv) {
+      for (int k = p.nseg - 1; k > seg; --k) {
+        const float *lc = p.loc + ((k * BD + row) * n + s) * 2;
+        const float *pd = p.pdec + ((k * BD + row) * n + s) * 2;
+        const float er = pd[0], ei = pd[1];
+        const float nhr = fmaf(er, hr, fmaf(ei, hi, lc[0]));
+        const float nhi = fmaf(er, hi, fmaf(-ei, hr, lc[1]));
+        hr = nhr;
+        hi = nhi;
+      }
+    }
+  }
   float dAr = 0.0f, dAi = 0.0f, fBr = 0.0f, fBi = 0.0f, fCr = 0.0f, fCi = 0.0f;
   float accD = 0.0f, accBias = 0.0f;                           // owner lanes' sums over their timesteps
+  float Pr = 1.0f, Pi = 0.0f;                                  // the segment's decay prod_t a_t (CARRY)
 
-  for (int64_t ci = p.nck - 1; ci >= 0; --ci) {
+  for (int64_t ci = cend - 1; ci >= cbeg; --ci) {
     const int64_t c0 = ci * kCk;
     const int len = static_cast<int>((L - c0 < kCk) ? L - c0 : kCk);
 
@@ -169,12 +201,36 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         const int tensor = idx >> 10, r = idx & 1023;
         const int st = r >> 6, tc = r & 63, t = tc >> 1, comp = tc & 1;
         float v = 0.0f;
-        const bool want = tensor == 0 ? BV : CV;
+        const bool want = tensor == 0 ? (BV && !CARRY) : CV;
         if (want && st < n && t < len)
           v = load_io<IO>(tensor == 0 ? p.B : p.C, bc_base + (static_cast<int64_t>(st) * L + c0 + t) * 2 + comp);
         s_bc[tensor][t][st][comp] = v;
       }
       __syncthreads();
+    }
+    if constexpr (CARRY) {
+      static_for(std::make_integer_sequence<int, kCk>{}, [&](auto J) {
+        constexpr int t = kCk - 1 - decltype(J)::value;
+        if (t < len) {
+          const float dt = row_bc<t % 16>(o_dt[t / 16]);
+          const float dy = row_bc<t % 16>(o_dy[t / 16]);
+          float cr, cim, er, ei;
+          if constexpr (CV) { cr = s_bc[1][t][s][0]; cim = s_bc[1][t][s][1]; }
+          else { cr = Cfr; cim = Cfi; }
+          hr = fmaf(dy, cr, hr);
+          hi = fmaf(-dy, cim, hi);
+          cexp_turns(dt, Ar2, Atr.hi, Atr.lo, er, ei);
+          const float nhr = fmaf(er, hr, ei * hi);
+          const float nhi = fmaf(er, hi, -ei * hr);
+          hr = nhr;
+          hi = nhi;
+          const float nPr = fmaf(er, Pr, -ei * Pi);
+          const float nPi = fmaf(er, Pi, ei * Pr);
+          Pr = nPr;
+          Pi = nPi;
+        }
+      });
+      continue;
     }
     float xr = 0.0f, xi = 0.0f;
     if (sv) {
@@ -244,7 +300,7 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
         const float gBr = dtu * hr, gBi = dtu * hi;
         if constexpr (!BV) { fBr += gBr; fBi += gBi; }
         if constexpr (!CV) { fCr += gCr; fCi += gCi; }
-        if constexpr (ANYV) {
+        if constexpr (PART) {
           // row rw holds the wave's sum of component ((rw & 1) << 1) | (rw >> 1)
           // of (dB re, dB im, dC re, dC im)
           const float v = fold_rows4(BV ? gBr : 0.0f, BV ? gBi : 0.0f, CV ? gCr : 0.0f, CV ? gCi : 0.0f);
@@ -303,7 +359,7 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
     }
 
     // ---- the workgroup's partial sums of time-varying dB/dC for the chunk
-    if constexpr (ANYV) {
+    if constexpr (PART) {
       __syncthreads();
       static_assert(kCk * 16 == 512, "one (timestep, state) of the chunk per thread");
       const int t = tid >> 4, st = tid & 15;
@@ -318,10 +374,21 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
     }
   }
 
-  // ---- per-channel results
+  if constexpr (CARRY) {
+    if (valid && sv) {
+      float *lc = p.loc + ((seg * BD + row) * n + s) * 2;
+      float *pd = p.pdec + ((seg * BD + row) * n + s) * 2;
+      lc[0] = hr;
+      lc[1] = hi;
+      pd[0] = Pr;
+      pd[1] = Pi;
+    }
+    return;
+  }
+  // ---- per-channel results (partials per segment and batch)
   if (valid && sv) {
-    const int64_t e = (row * n + s) * 2;
-    if (p.dinit) { p.dinit[e] = hr; p.dinit[e + 1] = hi; }
+    const int64_t e = ((seg * BD + row) * n + s) * 2;
+    if (p.dinit && seg == 0) { p.dinit[(row * n + s) * 2] = hr; p.dinit[(row * n + s) * 2 + 1] = hi; }
     p.ws_dA[e] = dAr;
     p.ws_dA[e + 1] = dAi;
     if constexpr (!BV) { p.ws_fB[e] = fBr; p.ws_fB[e + 1] = fBi; }
@@ -329,8 +396,8 @@ __global__ void __launch_bounds__(512) cbwd_kernel(const CbwdParams p) {
   }
   const float sD = row_sum16(accD), sB = row_sum16(accBias);
   if (valid && s == 0) {
-    p.ws_dD[row] = sD;
-    p.ws_db[row] = sB;
+    p.ws_dD[seg * BD + row] = sD;
+    p.ws_db[seg * BD + row] = sB;
   }
 }
 
@@ -343,8 +410,8 @@ __global__ void __launch_bounds__(256) cbwd_sum_kernel(const CbwdParams p, int b
   const int64_t nds = p.dim * n;
   if (i < nds) {
     float ar = 0.0f, ai = 0.0f, br = 0.0f, bi = 0.0f, cr = 0.0f, cim = 0.0f;
-    for (int64_t b = 0; b < p.batch; ++b) {
-      const int64_t e = (b * nds + i) * 2;
+    for (int64_t sb = 0; sb < p.nseg * p.batch; ++sb) {   // (segment, batch) in order
+      const int64_t e = (sb * nds + i) * 2;
       ar += p.ws_dA[e]; ai += p.ws_dA[e + 1];
       if (!bv) { br += p.ws_fB[e]; bi += p.ws_fB[e + 1]; }
       if (!cv) { cr += p.ws_fC[e]; cim += p.ws_fC[e + 1]; }
@@ -355,9 +422,9 @@ __global__ void __launch_bounds__(256) cbwd_sum_kernel(const CbwdParams p, int b
   }
   if (i < p.dim) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < p.batch; ++b) {
-      sd += p.ws_dD[b * p.dim + i];
-      sb += p.ws_db[b * p.dim + i];
+    for (int64_t k = 0; k < p.nseg * p.batch; ++k) {
+      sd += p.ws_dD[k * p.dim + i];
+      sb += p.ws_db[k * p.dim + i];
     }
     if (p.dD) p.dD[i] = sd;
     if (p.ddbias) p.ddbias[i] = sb;
@@ -382,36 +449,77 @@ using CbwdFn = void (*)(const CbwdParams);
 
 template <int IO>
 CbwdFn pick_cbwd(bool bv, bool cv) {
-  if (bv && cv) return cbwd_kernel<IO, true, true>;
-  if (bv) return cbwd_kernel<IO, true, false>;
-  if (cv) return cbwd_kernel<IO, false, true>;
-  return cbwd_kernel<IO, false, false>;
+  if (bv && cv) return cbwd_kernel<IO, true, true, false>;
+  if (bv) return cbwd_kernel<IO, true, false, false>;
+  if (cv) return cbwd_kernel<IO, false, true, false>;
+  return cbwd_kernel<IO, false, false, false>;
+}
+
+template <int IO>
+CbwdFn pick_ccarry(bool cv) {
+  return cv ? cbwd_kernel<IO, false, true, true> : cbwd_kernel<IO, false, false, true>;
+}
+
+CbwdFn cbwd_fn(int32_t io, bool bv, bool cv) {
+  return io == SSM_BF16 ? pick_cbwd<1>(bv, cv) : io == SSM_F16 ? pick_cbwd<2>(bv, cv) : pick_cbwd<0>(bv, cv);
 }
 
 struct CbwdPlan {
   int groups_eff, nblk;
-  int64_t cpg;
-  size_t off_bc, off_dA, off_fB, off_fC, off_dD, off_db, ws_bytes;
+  int64_t cpg, nck, nwg;
+  int nseg, seg0, segc;
+  size_t off_bc, off_dA, off_fB, off_fC, off_dD, off_db, off_loc, off_pdec, ws_bytes;
 };
+
+// Sequence split (host_util.h: split_segments, split_first_segment).  The
+// carry pass walks a chunk with the exps and the h update of the backward
+// step alone, but as a chain of dependent steps behind each chunk's loads it
+// takes about 0.55 of the main walk's time per chunk (measured at
+// mamba2p8b_complex: 197 us for the carry of a 14-chunk segment).  There
+// the library therefore keeps one pass: a split saved 113 us of the main
+// kernel's 4.2 ms and its carry pass cost 197.
+constexpr double kCarryCostC = 0.6;
+constexpr int kMaxSegC = 64;        // most segments the library picks by itself
+constexpr int kMinSegChunksC = 4;   // and the fewest chunks it gives a segment
 
 size_t up256c(size_t v) { return (v + 255) / 256 * 256; }
 
-CbwdPlan cbwd_plan(const ssm_scan_bwd_args_t *a) {
+CbwdPlan cbwd_plan(const ssm_scan_bwd_args_t *a, int cus) {
   CbwdPlan pl{};
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
   pl.groups_eff = (bv || cv) ? static_cast<int>(a->ngroups) : 1;
   pl.cpg = a->dim / pl.groups_eff;
   pl.nblk = static_cast<int>((pl.cpg + kChPerWG - 1) / kChPerWG);
+  pl.nck = (a->seqlen + kCk - 1) / kCk;
+  pl.nwg = a->batch * pl.groups_eff * pl.nblk;
+  int per_cu = blocks_per_cu(reinterpret_cast<const void *>(cbwd_fn(a->io_dtype, bv, cv)), 512);
+  if (per_cu <= 0) per_cu = 2;
+  const int64_t slots = static_cast<int64_t>(per_cu) * cus;
+  int64_t want = a->seq_segments > 0 ? a->seq_segments
+                                     : split_segments(pl.nwg, pl.nck, slots, kCarryCostC, kMaxSegC, kMinSegChunksC);
+  if (want > pl.nck) want = pl.nck;
+  if (want < 1) want = 1;
+  pl.segc = static_cast<int>((pl.nck + want - 1) / want);
+  pl.nseg = static_cast<int>((pl.nck + pl.segc - 1) / pl.segc);   // every segment holds a chunk
+  pl.seg0 = pl.segc;
+  if (a->seq_segments <= 0 && pl.nseg == 2) {
+    pl.seg0 = split_first_segment(pl.nwg, pl.nck, slots, kCarryCostC);
+    pl.segc = static_cast<int>(pl.nck - pl.seg0);
+  }
+  const size_t ns = static_cast<size_t>(pl.nseg);
   const size_t f = sizeof(float);
-  const size_t per_batch = static_cast<size_t>(a->batch) * a->dim * a->dstate * 2 * f;
+  const size_t bd = static_cast<size_t>(a->batch) * a->dim;
+  const size_t per_seg = ns * bd * a->dstate * 2 * f;   // complex (segment, b, d, n)
   size_t off = 0;
   pl.off_bc = off;
   if (bv || cv) off += up256c(static_cast<size_t>(a->batch) * a->ngroups * pl.nblk * a->seqlen * a->dstate * 4 * f);
-  pl.off_dA = off; off += up256c(per_batch);
-  pl.off_fB = off; if (!bv) off += up256c(per_batch);
-  pl.off_fC = off; if (!cv) off += up256c(per_batch);
-  pl.off_dD = off; off += up256c(static_cast<size_t>(a->batch) * a->dim * f);
-  pl.off_db = off; off += up256c(static_cast<size_t>(a->batch) * a->dim * f);
+  pl.off_dA = off; off += up256c(per_seg);
+  pl.off_fB = off; if (!bv) off += up256c(per_seg);
+  pl.off_fC = off; if (!cv) off += up256c(per_seg);
+  pl.off_dD = off; off += up256c(ns * bd * f);
+  pl.off_db = off; off += up256c(ns * bd * f);
+  pl.off_loc = off; if (pl.nseg > 1) off += up256c(per_seg);
+  pl.off_pdec = off; if (pl.nseg > 1) off += up256c(per_seg);
   pl.ws_bytes = off;
   return pl;
 }
@@ -425,14 +533,14 @@ extern "C" int ssm_scan_bwd_complex_workspace_size(const ssm_scan_bwd_args_t *a,
   const int st = ssm_scan_bwd_complex_validate(a);
   if (st != SSM_OK) return st;
   if (!bytes) return SSM_ERR_NULL;
-  *bytes = cbwd_plan(a).ws_bytes;
+  *bytes = cbwd_plan(a, cu_count_cached()).ws_bytes;
   return SSM_OK;
 }
 
 extern "C" int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *a, void *stream_ptr) {
   const int st = ssm_scan_bwd_complex_validate(a);
   if (st != SSM_OK) return st;
-  const CbwdPlan pl = cbwd_plan(a);
+  const CbwdPlan pl = cbwd_plan(a, cu_count_cached());
   if (!a->workspace || a->workspace_bytes < pl.ws_bytes) return SSM_ERR_WORKSPACE;
   const bool bv = a->B_kind == SSM_BC_VARYING, cv = a->C_kind == SSM_BC_VARYING;
   CbwdParams p{};
@@ -448,13 +556,16 @@ extern "C" int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *a, void *stream_p
   p.ws_fC = reinterpret_cast<float *>(ws + pl.off_fC);
   p.ws_dD = reinterpret_cast<float *>(ws + pl.off_dD);
   p.ws_db = reinterpret_cast<float *>(ws + pl.off_db);
+  p.loc = pl.nseg > 1 ? reinterpret_cast<float *>(ws + pl.off_loc) : nullptr;
+  p.pdec = pl.nseg > 1 ? reinterpret_cast<float *>(ws + pl.off_pdec) : nullptr;
+  p.nseg = pl.nseg; p.seg0 = pl.seg0; p.segc = pl.segc;
   p.batch = a->batch; p.dim = a->dim; p.seqlen = a->seqlen;
-  p.nck = (a->seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
+  p.nck = pl.nck;
   p.cpg = pl.cpg;
   p.n = static_cast<int>(a->dstate); p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = pl.groups_eff; p.nblk = pl.nblk;
   p.softplus = a->delta_softplus;
-  const int64_t nwg = a->batch * pl.groups_eff * pl.nblk;
+  const int64_t nwg = pl.nwg;
   int64_t nsum = a->dim * a->dstate;
   if (bv || cv) {
     const int64_t v = a->batch * a->ngroups * a->seqlen * a->dstate;
@@ -462,13 +573,20 @@ extern "C" int ssm_scan_bwd_complex(const ssm_scan_bwd_args_t *a, void *stream_p
   }
   if (a->dim > nsum) nsum = a->dim;
   const int64_t sum_blocks = (nsum + 255) / 256;
-  if (nwg > 0x7fffffffLL || sum_blocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
+  if (nwg > 0x7fffffffLL || sum_blocks > 0x7fffffffLL || pl.nseg > 65535) return SSM_ERR_SHAPE;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  CbwdFn f = a->io_dtype == SSM_BF16 ? pick_cbwd<1>(bv, cv)
-           : a->io_dtype == SSM_F16  ? pick_cbwd<2>(bv, cv)
-                                     : pick_cbwd<0>(bv, cv);
-  hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(nwg)), dim3(512), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (pl.nseg > 1) {   // the carry pass over segments 1 .. nseg - 1
+    CbwdFn fc = a->io_dtype == SSM_BF16 ? pick_ccarry<1>(cv) : a->io_dtype == SSM_F16 ? pick_ccarry<2>(cv)
+                                                                                       : pick_ccarry<0>(cv);
+    hipLaunchKernelGGL(fc, dim3(static_cast<unsigned>(nwg), static_cast<unsigned>(pl.nseg - 1)), dim3(512), 0,
+                       stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipLaunchKernelGGL(cbwd_fn(a->io_dtype, bv, cv), dim3(static_cast<unsigned>(nwg), static_cast<unsigned>(pl.nseg)),
+                     dim3(512), 0, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   hipLaunchKernelGGL(cbwd_sum_kernel, dim3(static_cast<unsigned>(sum_blocks)), dim3(256), 0, stream, p,
                      static_cast<int>(bv), static_cast<int>(cv));

@@ -107,7 +107,6 @@ extern "C" int ssm_scan_bwd_complex_validate(const ssm_scan_bwd_args_t *a) {
   if (!product_fits(a->batch, 2 * a->ngroups * a->dstate, a->seqlen) ||
       !product_fits(a->batch * a->dim, 2 * a->dstate, a->seqlen))
     return SSM_ERR_SHAPE;
-  if (a->seq_segments > 1) return SSM_ERR_UNSUPPORTED;   // no sequence split
   return SSM_OK;
 }
 

@@ -517,13 +517,22 @@ def test_plan_query():
 
 
 def test_complex_bwd_validation():
-    """ssm_scan_bwd_complex: the real backward's checks, no sequence split,
-    and the workspace required before anything is enqueued."""
+    """ssm_scan_bwd_complex: the real backward's checks, any sequence split,
+    and the workspace required before anything is enqueued (more segments,
+    more partial sums)."""
     L = _lib.lib()
     v = lambda a: L.ssm_scan_bwd_complex_validate(ctypes.byref(a))  # noqa: E731
     assert v(_good_bwd()) == _lib.SSM_OK
     assert v(_good_bwd(seq_segments=1)) == _lib.SSM_OK
-    assert v(_good_bwd(seq_segments=2)) == _lib.SSM_ERR_UNSUPPORTED
+    assert v(_good_bwd(seq_segments=3)) == _lib.SSM_OK
+    assert v(_good_bwd(seq_segments=-1)) == _lib.SSM_ERR_SHAPE
+    sizes = []
+    for k in (1, 3):
+        need = ctypes.c_size_t(0)
+        assert L.ssm_scan_bwd_complex_workspace_size(ctypes.byref(_good_bwd(seq_segments=k)),
+                                                     ctypes.byref(need)) == _lib.SSM_OK
+        sizes.append(need.value)
+    assert sizes[1] > sizes[0]
     assert v(_good_bwd(checkpoints=None)) == _lib.SSM_ERR_NULL
     assert v(_good_bwd(dstate=17)) == _lib.SSM_ERR_UNSUPPORTED
     assert L.ssm_scan_bwd_complex_validate(None) == _lib.SSM_ERR_NULL

@@ -42,7 +42,7 @@ def _kinds(t):
     return bk, ck
 
 
-def _gpu(w, t, dout, want_dinit=True, ret_ckpt=False):
+def _gpu(w, t, dout, want_dinit=True, ret_ckpt=False, segments=0):
     import torch
     from state_space_model_scan_amd import binding
     io = w.io_dtype
@@ -57,7 +57,8 @@ def _gpu(w, t, dout, want_dinit=True, ret_ckpt=False):
     binding.ssm_scan_fwd_complex(u, delta, A, B, C, D, z, bias, w.softplus, initial_state=init_t,
                                  checkpoints=ck)
     g = binding.ssm_scan_bwd_complex(u, delta, A, B, C, dev(dout), ck, D=D, z=z, delta_bias=bias,
-                                     delta_softplus=w.softplus, want_dinitial_state=want_dinit)
+                                     delta_softplus=w.softplus, want_dinitial_state=want_dinit,
+                                     seq_segments=segments)
     torch.cuda.synchronize()
     res = {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
     if ret_ckpt:
@@ -108,13 +109,13 @@ def _compare(w, got, want, what, names=None, bars=None):
     return errs
 
 
-def _run(w, what, t=None):
+def _run(w, what, t=None, segments=0):
     log(f"[cbwd] {what}: b={w.batch} d={w.dim} l={w.seqlen} n={w.dstate} g={w.ngroups} io={w.io_dtype} "
         f"bc={w.bc_kind} z={w.has_z} D={w.has_D} bias={w.has_bias} sp={w.softplus} init={w.init_state} "
         f"Im A={w.A_imag}")
     t = make_complex_inputs(w) if t is None else t
     dout = make_dout(w)
-    got = _gpu(w, t, dout)
+    got = _gpu(w, t, dout, segments=segments)
     want = _oracle(w, t, dout)
     bars = _floor_bars(w, t, dout, want)
     errs = _compare(w, got, want, what, bars=bars)
@@ -205,6 +206,42 @@ def test_complex_bwd_deterministic():
     for k, v in a.items():
         if v is not None:
             np.testing.assert_array_equal(v, b[k])
+
+
+@pytest.mark.parametrize("segments", [2, 3, 7])
+@pytest.mark.parametrize("bc", ["varying", "fixed"])
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_complex_bwd_sequence_split(segments, bc, io):
+    """The sequence split forced to 2, 3 and 7 segments (10 chunks of 32 and
+    a ragged last chunk: segments of 5, 4 and 2 chunks), every gradient
+    against the oracle.  The carry that crosses a boundary still weighs
+    about exp(-0.3 * 20) of a gradient after a five-chunk segment, well above
+    the bar, so a wrong fold fails.  (Real parts of A near zero on the Im A
+    ladder put even the unsplit walk past the fp32 bar: du 3.0e-4 at
+    Re A = -0.02, the same with and without the split.)"""
+    w = BASE.scaled(batch=2, dim=64, seqlen=300, bc_kind=bc, io_dtype=io, init_state=True,
+                    seed=900 + segments + 10 * io + (bc == "fixed"))
+    _run(w, f"split segments={segments} bc={bc} io={io}", segments=segments)
+
+
+def test_complex_bwd_split_one_chunk_per_segment():
+    """Every chunk its own segment (9 segments over 270 timesteps), grouped
+    time-varying B/C, bf16."""
+    w = BASE.scaled(batch=2, dim=128, seqlen=270, ngroups=2, io_dtype=BF16, init_state=True, seed=930)
+    _run(w, "one chunk per segment", segments=9)
+
+
+def test_complex_bwd_split_agrees_with_unsplit():
+    """Split (4 segments) and unsplit runs agree to fp32 rounding on every
+    gradient: the same sums, reassociated."""
+    w = BASE.scaled(batch=2, dim=64, seqlen=512, io_dtype=F32, seed=935)
+    t = make_complex_inputs(w)
+    dout = make_dout(w)
+    a, b = _gpu(w, t, dout, segments=1), _gpu(w, t, dout, segments=4)
+    for k, v in a.items():
+        if v is not None:
+            e = max_err(b[k], v)
+            assert e <= 1e-4, f"{k}: split against unsplit {e:.3e}"
 
 
 def test_complex_bwd_mid_size():
