@@ -40,10 +40,22 @@
 namespace ssm {
 namespace {
 
-constexpr int kLPC = 4;                 // lanes per channel
-constexpr int kT = 8 * kLPC;            // timesteps per chunk
-constexpr int kCPW = 64 / kLPC;         // channels per wave
-static_assert(kT == SSM_CKPT_INTERVAL, "a checkpoint at every chunk start");
+constexpr int kBlockCh = 16;            // channels of a block: a four-lane wave's, or two eight-lane waves'
+constexpr int kT = SSM_CKPT_INTERVAL;   // timesteps per chunk
+static_assert(chunk_of(4) == kT && chunk_of(8) == kT, "a checkpoint at every chunk start");
+
+// LDS floats of one wave: the B/C tile ([B, C][t][state][re, im]) and the
+// delta' / delta'*u hand-off ([group of 4 timesteps][2][channel][4]).
+constexpr int cplx_lds_floats(int nsw, int lpc, bool anyv) {
+  return (anyv ? 2 * kT * nsw * lpc * 2 : 4) + (kT / 4) * 2 * (64 / lpc) * 4;
+}
+
+// The work of one wave: batch, B/C group and its first channel.
+struct CplxWork {
+  int64_t b;
+  int g;
+  int64_t d0;
+};
 
 struct CplxParams {
   const void *u, *delta, *B, *C, *z;
@@ -54,35 +66,35 @@ struct CplxParams {
   int64_t batch, dim, seqlen, cpg, nck;
   int n, ngroups, groups_eff, nblk, nblocks;
   int softplus, vec, xcd_swizzle;
+  int mix_whole, mix_small;   // mixed plan: four-lane waves, then eight-lane waves (0, 0: none)
 };
 
-template <int IO, int NSW, bool BV, bool CV>
-__global__ void __launch_bounds__(64)
-scan_complex_kernel(const CplxParams p) {
+// One wave's walk of its channels (LPC lanes per channel, NSW complex states
+// a lane) over the whole sequence; its LDS slice is `lds`
+// (cplx_lds_floats(NSW, LPC, BV || CV) floats, 16-byte aligned).
+template <int IO, int NSW, int LPC, bool BV, bool CV>
+__device__ __forceinline__ void cplx_body(const CplxParams &p, float *lds, const CplxWork wk) {
   constexpr bool ANYV = BV || CV;
-  constexpr int NP = NSW * kLPC;        // padded state count
+  constexpr int KP = kp_of(LPC);        // timesteps each lane owns per chunk
+  constexpr int CPW = 64 / LPC;         // channels per wave
+  constexpr int NP = NSW * LPC;         // padded state count
   constexpr int PIECES = NP * (kT / 8); // B/C staging pieces: 8 timesteps of one state
   static_assert(PIECES <= 64, "one B/C piece per lane");
 
   // [B or C][timestep][state][re, im]
-  __shared__ float s_bc[ANYV ? 2 : 1][ANYV ? kT : 1][ANYV ? NP : 1][2];
+  auto sbc = [&](int tensor, int t, int st) -> float * { return lds + ((tensor * kT + t) * NP + st) * 2; };
   // delta' and delta'*u of timesteps 4g..4g+3 as [channel][4] each, for
-  // every group g of the chunk (written by the owner, read by the quad)
-  __shared__ __attribute__((aligned(16))) float s_dd[(kT / 4) * 2 * kCPW * 4];
-  auto dd_at = [&](int g) -> float * { return &s_dd[g * 2 * kCPW * 4]; };
+  // every group g of the chunk (written by the owner, read by the channel's lanes)
+  float *s_dd = lds + (ANYV ? 2 * kT * NP * 2 : 4);
+  auto dd_at = [&](int g) -> float * { return &s_dd[g * 2 * CPW * 4]; };
 
   const int lane = threadIdx.x & 63;
-  const int q = lane % kLPC;
-  const int cw_idx = lane / kLPC;
-
-  int bid = blockIdx.x;
-  if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
-  const int blk = bid % p.nblk;
-  const int rest = bid / p.nblk;
-  const int g = rest % p.groups_eff;
-  const int64_t b = rest / p.groups_eff;
+  const int q = lane % LPC;
+  const int cw_idx = lane / LPC;
+  const int g = wk.g;
+  const int64_t b = wk.b;
   const int64_t d_end = (g + 1) * p.cpg;
-  const int64_t d = g * p.cpg + static_cast<int64_t>(blk) * kCPW + cw_idx;
+  const int64_t d = wk.d0 + cw_idx;
   const bool valid = d < d_end;
   const int64_t dl = valid ? d : d_end - 1;
   const int64_t row = b * p.dim + dl;
@@ -112,13 +124,13 @@ scan_complex_kernel(const CplxParams p) {
   // element index of (b, g, state 0, t 0, re) in a varying B/C
   const int64_t bc_base = ((b * p.ngroups + g) * n) * seqlen * 2;
 
-  const int own = q * kKP;
+  const int own = q * KP;
   auto count = [&](int64_t c) {
     const int64_t tp0 = c + own;
-    return static_cast<int>((seqlen - tp0 < kKP) ? seqlen - tp0 : kKP);
+    return static_cast<int>((seqlen - tp0 < KP) ? seqlen - tp0 : KP);
   };
 
-  RawV<IO, kKP> r_u, r_dl, r_z;
+  RawV<IO, KP> r_u, r_dl, r_z;
   r_u.zero(); r_dl.zero(); r_z.zero();
   auto fetch = [&](int64_t c) {
     const int64_t tp0 = c + own;
@@ -152,27 +164,27 @@ scan_complex_kernel(const CplxParams p) {
         const RawV<IO, 8> &sb = i < 4 ? rB0 : rB1;
         const RawV<IO, 8> &sc = i < 4 ? rC0 : rC1;
         if constexpr (BV) {
-          s_bc[0][bc_t0 + i][bc_s][0] = sb.get(2 * (i & 3));
-          s_bc[0][bc_t0 + i][bc_s][1] = sb.get(2 * (i & 3) + 1);
+          sbc(0, bc_t0 + i, bc_s)[0] = sb.get(2 * (i & 3));
+          sbc(0, bc_t0 + i, bc_s)[1] = sb.get(2 * (i & 3) + 1);
         }
         if constexpr (CV) {
-          s_bc[ANYV ? 1 : 0][bc_t0 + i][bc_s][0] = sc.get(2 * (i & 3));
-          s_bc[ANYV ? 1 : 0][bc_t0 + i][bc_s][1] = sc.get(2 * (i & 3) + 1);
+          sbc(ANYV ? 1 : 0, bc_t0 + i, bc_s)[0] = sc.get(2 * (i & 3));
+          sbc(ANYV ? 1 : 0, bc_t0 + i, bc_s)[1] = sc.get(2 * (i & 3) + 1);
         }
       }
     }
   };
 
-  float dtv[kKP], dtuv[kKP], duv[kKP], yv[kKP];
+  float dtv[KP], dtuv[KP], duv[KP], yv[KP];
 #pragma unroll
-  for (int i = 0; i < kKP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
+  for (int i = 0; i < KP; ++i) { dtv[i] = dtuv[i] = duv[i] = yv[i] = 0.0f; }
 
   // FCc: a whole chunk, so no lane owns timesteps past the end
   auto prep = [&](int64_t c, auto FCc) {
     constexpr bool FC = decltype(FCc)::value;
     const int cnt = count(c);
 #pragma unroll
-    for (int i = 0; i < kKP; ++i) {
+    for (int i = 0; i < KP; ++i) {
       const float uu = r_u.get(i);
       float dt = r_dl.get(i) + bias;
       if (p.softplus) dt = softplus_acc(dt);
@@ -192,16 +204,16 @@ scan_complex_kernel(const CplxParams p) {
     constexpr int gb = (t / 4) % 2;
     if constexpr (t % 4 == 0) {
       dtq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + cw_idx * 4);
-      dtuq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + kCPW * 4 + cw_idx * 4);
+      dtuq[gb] = *reinterpret_cast<const float4 *>(dd_at(t / 4) + CPW * 4 + cw_idx * 4);
     }
     constexpr int e = t % 4;
     in.dt = e == 0 ? dtq[gb].x : e == 1 ? dtq[gb].y : e == 2 ? dtq[gb].z : dtq[gb].w;
     in.dtu = e == 0 ? dtuq[gb].x : e == 1 ? dtuq[gb].y : e == 2 ? dtuq[gb].z : dtuq[gb].w;
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
-      if constexpr (BV) { in.Br[k] = s_bc[0][t][s0 + k][0]; in.Bi[k] = s_bc[0][t][s0 + k][1]; }
+      if constexpr (BV) { in.Br[k] = sbc(0, t, s0 + k)[0]; in.Bi[k] = sbc(0, t, s0 + k)[1]; }
       else { in.Br[k] = Bfr[k]; in.Bi[k] = Bfi[k]; }
-      if constexpr (CV) { in.Cr[k] = s_bc[ANYV ? 1 : 0][t][s0 + k][0]; in.Ci[k] = s_bc[ANYV ? 1 : 0][t][s0 + k][1]; }
+      if constexpr (CV) { in.Cr[k] = sbc(ANYV ? 1 : 0, t, s0 + k)[0]; in.Ci[k] = sbc(ANYV ? 1 : 0, t, s0 + k)[1]; }
       else { in.Cr[k] = Cfr[k]; in.Ci[k] = Cfi[k]; }
     }
   };
@@ -222,11 +234,14 @@ scan_complex_kernel(const CplxParams p) {
       y = fmaf(in.Cr[k], nr, y);
       y = fmaf(-in.Ci[k], ni, y);
     }
-    // Re(C.x) over the quad's states: lanes (0,1) and (2,3) first, then the
-    // pairs (DPP quad permutes); the owner of timestep t keeps it
+    // Re(C.x) over the channel's states: lanes (0,1) and (2,3) first, then
+    // the pairs (DPP quad permutes), then with eight lanes the two quads; the
+    // owner of timestep t keeps it
     y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, true));  // [1,0,3,2]
     y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, true));  // [2,3,0,1]
-    if (q == t / kKP) yv[t % kKP] = y;
+    if constexpr (LPC == 8)   // and the other quad of the eight lanes (row_half_mirror)
+      y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x141, 0xf, 0xf, true));
+    if (q == t / KP) yv[t % KP] = y;
   };
 
   fetch(0);
@@ -235,19 +250,19 @@ scan_complex_kernel(const CplxParams p) {
   for (int64_t c = 0; c < seqlen; c += kT) {
     const int len = static_cast<int>((seqlen - c < kT) ? seqlen - c : kT);
     if (len == kT) prep(c, std::true_type{}); else prep(c, std::false_type{});
-    // this lane's timesteps are groups 2q and 2q+1; the previous chunk's
+    // this lane's timesteps are groups own/4 .. own/4 + KP/4 - 1; the previous chunk's
     // reads of the rows are issued before these stores
     wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < KP / 4; ++j) {
       float *dp = dd_at((own >> 2) + j);
       *reinterpret_cast<float4 *>(dp + cw_idx * 4) = make_float4(dtv[4 * j], dtv[4 * j + 1], dtv[4 * j + 2], dtv[4 * j + 3]);
-      *reinterpret_cast<float4 *>(dp + kCPW * 4 + cw_idx * 4) =
+      *reinterpret_cast<float4 *>(dp + CPW * 4 + cw_idx * 4) =
           make_float4(dtuv[4 * j], dtuv[4 * j + 1], dtuv[4 * j + 2], dtuv[4 * j + 3]);
     }
     if constexpr (ANYV) stage_bc();
     wave_lds_sync();            // the slice is written before any lane reads it
-    const RawV<IO, kKP> z_cur = r_z;
+    const RawV<IO, KP> z_cur = r_z;
     if (p.ckpt && valid) {   // the state before timestep c (the backward starts its chunks there)
       float *dst = p.ckpt + ((row * p.nck + c / kT) * n) * 2;
 #pragma unroll
@@ -283,14 +298,14 @@ scan_complex_kernel(const CplxParams p) {
     }
     const int cnt = count(c);
     if (cnt > 0 && valid) {
-      float o[kKP];
+      float o[KP];
 #pragma unroll
-      for (int i = 0; i < kKP; ++i) {
+      for (int i = 0; i < KP; ++i) {
         float y = yv[i] + duv[i];
         if (p.z) y *= silu_f(z_cur.get(i));
         o[i] = y;
       }
-      store_n<IO, kKP>(p.out, rbase + c + own, o, cnt, vec);
+      store_n<IO, KP>(p.out, rbase + c + own, o, cnt, vec);
     }
   }
 
@@ -304,6 +319,53 @@ scan_complex_kernel(const CplxParams p) {
   }
 }
 
+// Three waves per SIMD (at most 168 VGPRs): the mixed plan needs q + 1 = 3,
+// and the plain plan at 2.5 waves per SIMD runs its third waves beside the others.
+template <int IO, int NSW, bool BV, bool CV>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) scan_complex_kernel(const CplxParams p) {
+  __shared__ __attribute__((aligned(16))) float lds[cplx_lds_floats(NSW, 4, BV || CV)];
+  int bid = blockIdx.x;
+  if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
+  const int blk = bid % p.nblk;
+  const int rest = bid / p.nblk;
+  CplxWork wk;
+  wk.g = rest % p.groups_eff;
+  wk.b = rest / p.groups_eff;
+  wk.d0 = wk.g * p.cpg + static_cast<int64_t>(blk) * kBlockCh;
+  cplx_body<IO, NSW, 4, BV, CV>(p, lds, wk);
+}
+
+// The mixed plan at dstate 13..16 (the real kernel's): workgroups below
+// mix_whole are four-lane waves over 16-channel blocks; each block left over
+// is covered by two eight-lane waves of 8 channels (two complex states per
+// lane), each with about half the work, so every SIMD holds its whole waves
+// and at most one half wave.
+template <int IO, bool BV, bool CV>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) scan_complex_mix_kernel(const CplxParams p) {
+  constexpr int L4 = cplx_lds_floats(4, 4, BV || CV), L8 = cplx_lds_floats(2, 8, BV || CV);
+  __shared__ __attribute__((aligned(16))) float lds[L4 > L8 ? L4 : L8];
+  const int nwhole = p.mix_whole;
+  const int bid = blockIdx.x;
+  const bool big = bid < nwhole;
+  int unit, half = 0;
+  if (big) {
+    unit = p.xcd_swizzle ? (bid & 7) * (nwhole >> 3) + (bid >> 3) : bid;
+  } else {
+    int j = bid - nwhole;
+    if (p.xcd_swizzle && p.mix_small % 8 == 0) j = (j & 7) * (p.mix_small >> 3) + (j >> 3);
+    unit = nwhole + j / 2;
+    half = j % 2;
+  }
+  const int blk = unit % p.nblk;
+  const int rest = unit / p.nblk;
+  CplxWork wk;
+  wk.g = rest % p.groups_eff;
+  wk.b = rest / p.groups_eff;
+  wk.d0 = wk.g * p.cpg + static_cast<int64_t>(blk) * kBlockCh + 8 * half;
+  if (big) cplx_body<IO, 4, 4, BV, CV>(p, lds, wk);
+  else cplx_body<IO, 2, 8, BV, CV>(p, lds, wk);
+}
+
 using CplxFn = void (*)(const CplxParams);
 
 template <int IO, int NSW>
@@ -312,6 +374,16 @@ CplxFn pick_cplx_bc(bool bv, bool cv) {
   if (bv) return scan_complex_kernel<IO, NSW, true, false>;
   if (cv) return scan_complex_kernel<IO, NSW, false, true>;
   return scan_complex_kernel<IO, NSW, false, false>;
+}
+template <int IO>
+CplxFn pick_cplx_mix(bool bv, bool cv) {
+  if (bv && cv) return scan_complex_mix_kernel<IO, true, true>;
+  if (bv) return scan_complex_mix_kernel<IO, true, false>;
+  if (cv) return scan_complex_mix_kernel<IO, false, true>;
+  return scan_complex_mix_kernel<IO, false, false>;
+}
+CplxFn cplx_mix_fn(int32_t io, bool bv, bool cv) {
+  return io == SSM_BF16 ? pick_cplx_mix<1>(bv, cv) : io == SSM_F16 ? pick_cplx_mix<2>(bv, cv) : pick_cplx_mix<0>(bv, cv);
 }
 template <int IO>
 CplxFn pick_cplx(int nsw, bool bv, bool cv) {
@@ -342,18 +414,32 @@ extern "C" int ssm_scan_fwd_complex(const ssm_scan_args_t *a, void *stream_ptr) 
   p.n = n; p.ngroups = static_cast<int>(a->ngroups);
   p.groups_eff = (bv || cv) ? p.ngroups : 1;
   p.cpg = a->dim / p.groups_eff;
-  p.nblk = static_cast<int>((p.cpg + kCPW - 1) / kCPW);
+  p.nblk = static_cast<int>((p.cpg + kBlockCh - 1) / kBlockCh);
   const int64_t nblocks = a->batch * p.groups_eff * p.nblk;
   if (nblocks > 0x7fffffffLL) return SSM_ERR_SHAPE;
   p.nblocks = static_cast<int>(nblocks);
   p.softplus = a->delta_softplus;
   p.vec = (a->seqlen % 8 == 0) && aligned16(a->u) && aligned16(a->delta) && aligned16(a->out) &&
           (!a->z || aligned16(a->z)) && (!bv || aligned16(a->B)) && (!cv || aligned16(a->C));
-  p.xcd_swizzle = (p.nblocks % 8 == 0);
-  CplxFn f = a->io_dtype == SSM_BF16 ? pick_cplx<1>(nsw, bv, cv)
+  // mixed plan (as the real forward's): q >= 2 whole waves per SIMD and r
+  // blocks over become 2r half waves, provided q + 1 waves fit a SIMD
+  p.mix_whole = p.mix_small = 0;
+  if (nsw == 4) {
+    const int simds = 4 * cu_count_cached();
+    const int q = p.nblocks / simds, r = p.nblocks % simds;
+    if (q >= 2 && r > 0 && 2 * r <= simds &&
+        4 * (q + 1) <= blocks_per_cu(reinterpret_cast<const void *>(cplx_mix_fn(a->io_dtype, bv, cv)), 64)) {
+      p.mix_whole = p.nblocks - r;
+      p.mix_small = 2 * r;
+    }
+  }
+  p.xcd_swizzle = p.mix_small ? (p.mix_whole % 8 == 0) : (p.nblocks % 8 == 0);
+  CplxFn f = p.mix_small ? cplx_mix_fn(a->io_dtype, bv, cv)
+           : a->io_dtype == SSM_BF16 ? pick_cplx<1>(nsw, bv, cv)
            : a->io_dtype == SSM_F16  ? pick_cplx<2>(nsw, bv, cv)
                                      : pick_cplx<0>(nsw, bv, cv);
-  hipLaunchKernelGGL(f, dim3(p.nblocks), dim3(64), 0, stream, p);
+  const int grid = p.mix_small ? p.mix_whole + p.mix_small : p.nblocks;
+  hipLaunchKernelGGL(f, dim3(grid), dim3(64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;

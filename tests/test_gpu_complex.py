@@ -178,6 +178,20 @@ def test_complex_full_size_sampled_rows():
     log(f"  max normalised error out {e:.2e} last_state {el:.2e}")
 
 
+@pytest.mark.parametrize("seqlen", [96, 100])
+def test_complex_mixed_plan_all_rows(seqlen):
+    """The Mamba-2.8B-shaped width (b=8 d=5120 g=4: 2560 blocks of 16
+    channels, 2048 whole waves and 1024 eight-lane waves of 8 channels) on a
+    short sequence, whole chunks (96, vector loads) and a ragged one (100,
+    element loads): every row of out and last_state against the oracle."""
+    w = COMPLEX_WORKLOADS["mamba2p8b_complex"].scaled(seqlen=seqlen, init_state=True, seed=1200 + seqlen)
+    t = make_complex_inputs(w)
+    log(f"complex mixed plan: b={w.batch} d={w.dim} l={w.seqlen}")
+    o, ls = _gpu(w, t)
+    e, el = _check(w, (o, ls), _oracle(w, t), f"mixed plan l={seqlen}")
+    log(f"  max normalised error out {e:.2e} last_state {el:.2e}")
+
+
 def test_complex_misaligned_pointers():
     """Every io tensor one element off 16-byte alignment at a sequence length
     divisible by 8: the element-wise loads and stores."""
