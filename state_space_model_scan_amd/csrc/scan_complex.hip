@@ -319,10 +319,15 @@ __device__ __forceinline__ void cplx_body(const CplxParams &p, float *lds, const
   }
 }
 
-// Three waves per SIMD (at most 168 VGPRs): the mixed plan needs q + 1 = 3,
-// and the plain plan at 2.5 waves per SIMD runs its third waves beside the others.
+// 16-bit io: three waves per SIMD (at most 168 VGPRs), since the mixed plan
+// needs q + 1 = 3 and the plain plan at 2.5 waves per SIMD runs its third
+// waves beside the others.  fp32 io keeps its registers: under that cap its
+// walk spills up to 55 dwords and the 2.8B-shaped layer ran 1235 us in the
+// mixed plan against 1013 us uncapped in the plain one, so it takes the plain
+// plan only.
 template <int IO, int NSW, bool BV, bool CV>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) scan_complex_kernel(const CplxParams p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(IO == SSM_F32 ? 1 : 3)))
+scan_complex_kernel(const CplxParams p) {
   __shared__ __attribute__((aligned(16))) float lds[cplx_lds_floats(NSW, 4, BV || CV)];
   int bid = blockIdx.x;
   if (p.xcd_swizzle) bid = (bid & 7) * (p.nblocks >> 3) + (bid >> 3);
@@ -383,7 +388,7 @@ CplxFn pick_cplx_mix(bool bv, bool cv) {
   return scan_complex_mix_kernel<IO, false, false>;
 }
 CplxFn cplx_mix_fn(int32_t io, bool bv, bool cv) {
-  return io == SSM_BF16 ? pick_cplx_mix<1>(bv, cv) : io == SSM_F16 ? pick_cplx_mix<2>(bv, cv) : pick_cplx_mix<0>(bv, cv);
+  return io == SSM_BF16 ? pick_cplx_mix<1>(bv, cv) : io == SSM_F16 ? pick_cplx_mix<2>(bv, cv) : nullptr;
 }
 template <int IO>
 CplxFn pick_cplx(int nsw, bool bv, bool cv) {
@@ -421,10 +426,10 @@ extern "C" int ssm_scan_fwd_complex(const ssm_scan_args_t *a, void *stream_ptr) 
   p.softplus = a->delta_softplus;
   p.vec = (a->seqlen % 8 == 0) && aligned16(a->u) && aligned16(a->delta) && aligned16(a->out) &&
           (!a->z || aligned16(a->z)) && (!bv || aligned16(a->B)) && (!cv || aligned16(a->C));
-  // mixed plan (as the real forward's): q >= 2 whole waves per SIMD and r
-  // blocks over become 2r half waves, provided q + 1 waves fit a SIMD
+  // mixed plan (as the real forward's), 16-bit io: q >= 2 whole waves per
+  // SIMD and r blocks over become 2r half waves, provided q + 1 waves fit a SIMD
   p.mix_whole = p.mix_small = 0;
-  if (nsw == 4) {
+  if (nsw == 4 && a->io_dtype != SSM_F32) {
     const int simds = 4 * cu_count_cached();
     const int q = p.nblocks / simds, r = p.nblocks % simds;
     if (q >= 2 && r > 0 && 2 * r <= simds &&

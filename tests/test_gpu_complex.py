@@ -178,15 +178,23 @@ def test_complex_full_size_sampled_rows():
     log(f"  max normalised error out {e:.2e} last_state {el:.2e}")
 
 
-@pytest.mark.parametrize("seqlen", [96, 100])
-def test_complex_mixed_plan_all_rows(seqlen):
+@pytest.mark.parametrize("seqlen,io,kind", [(96, None, "varying"), (100, None, "varying"), (64, F32, "varying"),
+                                            (70, F16, "varying"), (66, F32, "fixed")])
+def test_complex_mixed_plan_all_rows(seqlen, io, kind):
     """The Mamba-2.8B-shaped width (b=8 d=5120 g=4: 2560 blocks of 16
     channels, 2048 whole waves and 1024 eight-lane waves of 8 channels) on a
     short sequence, whole chunks (96, vector loads) and a ragged one (100,
-    element loads): every row of out and last_state against the oracle."""
+    element loads), with the layer's bf16 io and with fp16 io (the mixed
+    kernel's instances), and with fp32 io, which takes the plain plan, B/C
+    varying and fixed (one group: the same 2560 blocks): every row of out
+    and last_state against the oracle."""
     w = COMPLEX_WORKLOADS["mamba2p8b_complex"].scaled(seqlen=seqlen, init_state=True, seed=1200 + seqlen)
+    if io is not None:
+        w = w.scaled(io_dtype=io)
+    if kind != w.bc_kind:
+        w = w.scaled(bc_kind=kind)
     t = make_complex_inputs(w)
-    log(f"complex mixed plan: b={w.batch} d={w.dim} l={w.seqlen}")
+    log(f"complex mixed plan: b={w.batch} d={w.dim} l={w.seqlen} io={w.io_dtype} B/C {w.bc_kind}")
     o, ls = _gpu(w, t)
     e, el = _check(w, (o, ls), _oracle(w, t), f"mixed plan l={seqlen}")
     log(f"  max normalised error out {e:.2e} last_state {el:.2e}")
